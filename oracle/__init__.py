@@ -1,0 +1,227 @@
+"""fp64 CPU oracle for the diagonal affine recurrence scan (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls it, and this package never
+imports the product path.
+
+The arithmetic lives in ``oracle.c`` (plain C, double precision, one lane at a
+time; see the header of that file for the definitions and where they come
+from).  This module only compiles it with gcc when the shared object is
+missing or older than the source, and marshals numpy float64 arrays.
+
+Definitions (page "triton_training_scan.py", kernels ``_real_forward``,
+``_real_backward`` and the ``_real_chunk_*`` / ``_real_reverse_chunk_*``
+family):
+
+* forward   ``h_t = a_t h_{t-1} + b_t`` from ``h_{-1} = h0`` (zero by default),
+  ``out = h``, ``last = h_{T-1}``;
+* backward  ``lambda_t = g_t + a_{t+1} lambda_{t+1}`` seeded with
+  ``grad_last``, ``grad_b = lambda``, ``grad_a_t = lambda_t h_{t-1}``,
+  ``grad_h0 = a_0 lambda_0``;
+* chunk summary ``(P_k, Q_k)``, exclusive prefix ``chunk_in``, replay, and the
+  reverse-time trio.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-pthread"]
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (fp contraction off)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.c_int64
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            # The mutation tests point this at a deliberately broken copy of
+            # oracle.c, compiled elsewhere, to show that the pins catch it.
+            override = os.environ.get("ORACLE_LIBRARY_OVERRIDE")
+            if override:
+                path = override
+            else:
+                path = build()
+            lib = ctypes.CDLL(path)
+            sigs = {
+                "oracle_scan_fwd": [_I, _I, _I, _D, _D, _D, _D, _D],
+                "oracle_scan_bwd": [_I, _I, _I, _D, _D, _D, _D, _D, _D, _D, _D],
+                "oracle_chunk_summary": [_I, _I, _I, _I, _D, _D, _D, _D],
+                "oracle_chunk_prefix": [_I, _I, _I, _D, _D, _D, _D, _D],
+                "oracle_chunk_replay": [_I, _I, _I, _I, _D, _D, _D, _D, _D],
+                "oracle_reverse_chunk_summary": [_I, _I, _I, _I, _D, _D, _D, _D],
+                "oracle_reverse_chunk_prefix": [_I, _I, _I, _D, _D, _D, _D, _D],
+                "oracle_reverse_chunk_replay": [_I, _I, _I, _I, _D, _D, _D, _D, _D, _D, _D],
+                "oracle_parallel_fwd": [_I, _I, _I, _D, _D, _D, _D, _D, ctypes.c_int],
+                "oracle_parallel_bwd": [_I, _I, _I, _D, _D, _D, _D, _D, _D, _D, _D, ctypes.c_int],
+            }
+            for name, args in sigs.items():
+                fn = getattr(lib, name)
+                fn.argtypes = args
+                fn.restype = ctypes.c_int if name.startswith("oracle_parallel") else None
+            _lib = lib
+    return _lib
+
+
+def _f64(x, shape=None):
+    if x is None:
+        return None
+    arr = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    if shape is not None and arr.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {arr.shape}")
+    return arr
+
+
+def _p(arr):
+    return None if arr is None else arr.ctypes.data_as(_D)
+
+
+def _bdt(a):
+    if a.ndim != 3:
+        raise ValueError("expected a [B, T, D] array")
+    return a.shape
+
+
+def scan_fwd(a, b, h0=None, threads: int = 1):
+    """Forward scan in fp64.  Returns (out [B,T,D], last [B,D])."""
+    a = _f64(a)
+    B, T, D = _bdt(a)
+    b = _f64(b, a.shape)
+    h0 = _f64(h0, (B, D))
+    out = np.empty((B, T, D))
+    last = np.empty((B, D))
+    lib = _load()
+    if threads > 1:
+        rc = lib.oracle_parallel_fwd(B, T, D, _p(a), _p(b), _p(h0), _p(out), _p(last), threads)
+        if rc != 0:
+            raise RuntimeError("oracle thread start failed")
+    else:
+        lib.oracle_scan_fwd(B, T, D, _p(a), _p(b), _p(h0), _p(out), _p(last))
+    return out, last
+
+
+def scan_bwd(a, h, g, h0=None, grad_last=None, threads: int = 1):
+    """Backward scan in fp64.  ``h`` are the forward states.
+
+    Returns (grad_a, grad_b, grad_h0)."""
+    a = _f64(a)
+    B, T, D = _bdt(a)
+    h = _f64(h, a.shape)
+    g = _f64(g, a.shape)
+    h0 = _f64(h0, (B, D))
+    grad_last = _f64(grad_last, (B, D))
+    grad_a = np.empty((B, T, D))
+    grad_b = np.empty((B, T, D))
+    grad_h0 = np.empty((B, D))
+    lib = _load()
+    if threads > 1:
+        rc = lib.oracle_parallel_bwd(B, T, D, _p(a), _p(h), _p(g), _p(h0), _p(grad_last),
+                                     _p(grad_a), _p(grad_b), _p(grad_h0), threads)
+        if rc != 0:
+            raise RuntimeError("oracle thread start failed")
+    else:
+        lib.oracle_scan_bwd(B, T, D, _p(a), _p(h), _p(g), _p(h0), _p(grad_last),
+                            _p(grad_a), _p(grad_b), _p(grad_h0))
+    return grad_a, grad_b, grad_h0
+
+
+def n_chunks(T: int, C: int) -> int:
+    return (T + C - 1) // C
+
+
+def chunk_summary(a, b, C: int):
+    """Per-chunk affine maps (P, Q), each [B, NC, D]."""
+    a = _f64(a)
+    B, T, D = _bdt(a)
+    b = _f64(b, a.shape)
+    NC = n_chunks(T, C)
+    P = np.empty((B, NC, D))
+    Q = np.empty((B, NC, D))
+    _load().oracle_chunk_summary(B, T, D, C, _p(a), _p(b), _p(P), _p(Q))
+    return P, Q
+
+
+def chunk_prefix(P, Q, h0=None):
+    """Exclusive forward prefix over chunk maps.  Returns (chunk_in, last)."""
+    P = _f64(P)
+    B, NC, D = _bdt(P)
+    Q = _f64(Q, P.shape)
+    h0 = _f64(h0, (B, D))
+    chunk_in = np.empty((B, NC, D))
+    last = np.empty((B, D))
+    _load().oracle_chunk_prefix(B, NC, D, _p(P), _p(Q), _p(h0), _p(chunk_in), _p(last))
+    return chunk_in, last
+
+
+def chunk_replay(a, b, chunk_in, C: int):
+    """Replay every chunk from its entering state.  Returns (out, last)."""
+    a = _f64(a)
+    B, T, D = _bdt(a)
+    b = _f64(b, a.shape)
+    chunk_in = _f64(chunk_in, (B, n_chunks(T, C), D))
+    out = np.empty((B, T, D))
+    last = np.empty((B, D))
+    _load().oracle_chunk_replay(B, T, D, C, _p(a), _p(b), _p(chunk_in), _p(out), _p(last))
+    return out, last
+
+
+def reverse_chunk_summary(a, g, C: int):
+    """Per-chunk reverse adjoint maps (P, Q), each [B, NC, D]."""
+    a = _f64(a)
+    B, T, D = _bdt(a)
+    g = _f64(g, a.shape)
+    NC = n_chunks(T, C)
+    P = np.empty((B, NC, D))
+    Q = np.empty((B, NC, D))
+    _load().oracle_reverse_chunk_summary(B, T, D, C, _p(a), _p(g), _p(P), _p(Q))
+    return P, Q
+
+
+def reverse_chunk_prefix(P, Q, grad_last=None):
+    """Exclusive right-to-left prefix.  Returns (future, grad_h0)."""
+    P = _f64(P)
+    B, NC, D = _bdt(P)
+    Q = _f64(Q, P.shape)
+    grad_last = _f64(grad_last, (B, D))
+    future = np.empty((B, NC, D))
+    grad_h0 = np.empty((B, D))
+    _load().oracle_reverse_chunk_prefix(B, NC, D, _p(P), _p(Q), _p(grad_last), _p(future),
+                                        _p(grad_h0))
+    return future, grad_h0
+
+
+def reverse_chunk_replay(a, h, g, future, C: int, h0=None):
+    """Replay every chunk backwards from its future carry.  Returns (grad_a, grad_b)."""
+    a = _f64(a)
+    B, T, D = _bdt(a)
+    h = _f64(h, a.shape)
+    g = _f64(g, a.shape)
+    future = _f64(future, (B, n_chunks(T, C), D))
+    h0 = _f64(h0, (B, D))
+    grad_a = np.empty((B, T, D))
+    grad_b = np.empty((B, T, D))
+    _load().oracle_reverse_chunk_replay(B, T, D, C, _p(a), _p(h), _p(g), _p(future), _p(h0),
+                                        _p(grad_a), _p(grad_b))
+    return grad_a, grad_b

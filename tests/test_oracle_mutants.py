@@ -1,0 +1,69 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of oracle.c (a dropped term, a swapped
+operand, a shifted index, a wrong seed, an inclusive-for-exclusive scan),
+compiles it with gcc into a temporary directory, and runs the pin suite
+against it in a subprocess.  The suite must fail for every mutant; the clean
+source must pass.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+# (name, text in oracle.c, replacement, occurrence index or None for all)
+MUTANTS = [
+    ("fwd_drop_b", "h = a[i] * h + b[i];\n            if (out)", "h = a[i] * h;\n            if (out)"),
+    ("fwd_swap_ab", "h = a[i] * h + b[i];\n            if (out)", "h = b[i] * h + a[i];\n            if (out)"),
+    ("fwd_ignore_h0", "double h = h0 ? h0[lane] : 0.0;", "double h = 0.0;"),
+    ("bwd_drop_carry", "double lam = g[i] + carry;\n            double h_prev = (t > 0) ? h[idx3(bi, t - 1, d, T, D)] : (h0 ? h0[lane] : 0.0);",
+     "double lam = g[i];\n            double h_prev = (t > 0) ? h[idx3(bi, t - 1, d, T, D)] : (h0 ? h0[lane] : 0.0);"),
+    ("bwd_hprev_same_step", "double h_prev = (t > 0) ? h[idx3(bi, t - 1, d, T, D)] : (h0 ? h0[lane] : 0.0);",
+     "double h_prev = h[idx3(bi, t, d, T, D)];"),
+    ("bwd_carry_uses_g", "carry = a[i] * lam;\n        }\n        if (grad_h0)", "carry = a[i] * g[i];\n        }\n        if (grad_h0)"),
+    ("bwd_ignore_grad_last", "double carry = grad_last ? grad_last[lane] : 0.0;", "double carry = 0.0;"),
+    ("bwd_grad_h0_lambda", "if (grad_h0) grad_h0[lane] = carry;", "if (grad_h0) grad_h0[lane] = carry / 2;"),
+    ("summary_drop_decay", "q = a[i] * q + b[i];", "q = q + b[i];"),
+    ("prefix_inclusive", "chunk_in[i] = s;\n                s = P[i] * s + Q[i];", "s = P[i] * s + Q[i];\n                chunk_in[i] = s;"),
+    ("replay_zero_start", "double h = chunk_in[idx3(bi, k, d, NC, D)];", "double h = 0.0;"),
+    ("rsummary_drop_a_on_g", "q = a[i] * q + a[i] * g[i];", "q = a[i] * q + g[i];"),
+    ("rprefix_inclusive", "future[i] = s;\n                s = P[i] * s + Q[i];", "s = P[i] * s + Q[i];\n                future[i] = s;"),
+    ("rreplay_no_decay", "carry = a[i] * lam;\n                }", "carry = lam;\n                }"),
+]
+
+
+def _run_pins(lib_path):
+    env = dict(os.environ)
+    env["ORACLE_LIBRARY_OVERRIDE"] = lib_path
+    return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                           os.path.join(HERE, "test_oracle_pins.py")],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+
+
+def _compile(src_text, tmp_path, name):
+    c = tmp_path / f"{name}.c"
+    so = tmp_path / f"{name}.so"
+    c.write_text(src_text)
+    subprocess.check_call(["gcc", *oracle.GCC_FLAGS, str(c), "-o", str(so)])
+    return str(so)
+
+
+def test_clean_oracle_passes_pins(tmp_path):
+    src = open(SRC).read()
+    r = _run_pins(_compile(src, tmp_path, "clean"))
+    assert r.returncode == 0, r.stdout[-2000:]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, old, new, tmp_path):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique ({src.count(old)})"
+    r = _run_pins(_compile(src.replace(old, new), tmp_path, name))
+    assert r.returncode != 0, f"mutant {name} survived the pins"

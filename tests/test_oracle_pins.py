@@ -1,0 +1,376 @@
+"""Pins of the fp64 oracle against what the mathematics fixes (CPU only).
+
+Each test checks the oracle against something other than itself: a value
+derived by hand, a closed form, a library routine (numpy cumsum, torch
+autograd), exact rational arithmetic, finite differences, or an identity that
+a dropped term, a wrong sign or a shifted index would break.  The recurrence
+and its adjoint are the ones the page "triton_training_scan.py"
+(botwwt.github.io/SAMU_GPU/benchmark) defines in _real_forward and
+_real_backward; the chunk forms are its _real_chunk_* and
+_real_reverse_chunk_* kernels.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def rand(shape, seed, lo=-1.0, hi=1.0):
+    return np.random.default_rng(seed).uniform(lo, hi, size=shape)
+
+
+def dyadic(shape, seed, scale=8):
+    """Random dyadic rationals k/scale, exact in binary floating point."""
+    r = np.random.default_rng(seed)
+    return r.integers(-scale, scale + 1, size=shape) / float(scale)
+
+
+# ----------------------------------------------------------------------------
+# hand-worked example (tests/golden/hand_example.json, derivation inside)
+# ----------------------------------------------------------------------------
+def load_golden():
+    with open(os.path.join(HERE, "golden", "hand_example.json")) as f:
+        ex = json.load(f)
+    arr = lambda k: np.array(ex[k], dtype=np.float64)[None]  # [1, T, D]
+    return ex, arr
+
+
+def test_golden_forward_backward():
+    ex, arr = load_golden()
+    a, b, g = arr("a"), arr("b"), arr("g")
+    out, last = oracle.scan_fwd(a, b)
+    assert np.array_equal(out, arr("out"))
+    assert np.array_equal(last[0], np.array(ex["last"]))
+    ga, gb, gh0 = oracle.scan_bwd(a, out, g)
+    assert np.array_equal(gb, arr("grad_b"))
+    assert np.array_equal(ga, arr("grad_a"))
+    assert np.array_equal(gh0[0], np.array(ex["grad_h0"]))
+    gl = np.array(ex["grad_last"])[None]
+    ga, gb, gh0 = oracle.scan_bwd(a, out, g, grad_last=gl)
+    w = ex["with_grad_last"]
+    assert np.array_equal(gb[0], np.array(w["grad_b"]))
+    assert np.array_equal(ga[0], np.array(w["grad_a"]))
+    assert np.array_equal(gh0[0], np.array(w["grad_h0"]))
+
+
+def test_golden_chunks():
+    ex, arr = load_golden()
+    a, b, g = arr("a"), arr("b"), arr("g")
+    C = ex["chunk"]
+    P, Q = oracle.chunk_summary(a, b, C)
+    assert np.array_equal(P, arr("P")) and np.array_equal(Q, arr("Q"))
+    cin, last = oracle.chunk_prefix(P, Q)
+    assert np.array_equal(cin, arr("chunk_in"))
+    assert np.array_equal(last[0], np.array(ex["last"]))
+    out, last2 = oracle.chunk_replay(a, b, cin, C)
+    assert np.array_equal(out, arr("out")) and np.array_equal(last2, last)
+    rP, rQ = oracle.reverse_chunk_summary(a, g, C)
+    assert np.array_equal(rP, arr("reverse_P")) and np.array_equal(rQ, arr("reverse_Q"))
+    fut, gh0 = oracle.reverse_chunk_prefix(rP, rQ)
+    assert np.array_equal(fut, arr("future"))
+    assert np.array_equal(gh0[0], np.array(ex["grad_h0"]))
+    ga, gb = oracle.reverse_chunk_replay(a, out, g, fut, C)
+    assert np.array_equal(ga, arr("grad_a")) and np.array_equal(gb, arr("grad_b"))
+
+
+# ----------------------------------------------------------------------------
+# special cases that reduce to textbook results
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1])
+def test_a_one_is_cumulative_sum(seed):
+    B, T, D = 2, 37, 5
+    a = np.ones((B, T, D))
+    b = rand((B, T, D), seed)
+    g = rand((B, T, D), seed + 10)
+    gl = rand((B, D), seed + 20)
+    out, last = oracle.scan_fwd(a, b)
+    np.testing.assert_allclose(out, np.cumsum(b, axis=1), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(last, b.sum(axis=1), rtol=0, atol=1e-12)
+    ga, gb, gh0 = oracle.scan_bwd(a, out, g, grad_last=gl)
+    rev = np.flip(np.cumsum(np.flip(g, axis=1), axis=1), axis=1) + gl[:, None, :]
+    np.testing.assert_allclose(gb, rev, rtol=0, atol=1e-12)
+    prev = np.concatenate([np.zeros((B, 1, D)), out[:, :-1]], axis=1)
+    np.testing.assert_allclose(ga, rev * prev, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(gh0, rev[:, 0], rtol=0, atol=1e-12)
+
+
+def test_a_zero_returns_b():
+    B, T, D = 3, 20, 4
+    a = np.zeros((B, T, D))
+    b = rand((B, T, D), 3)
+    g = rand((B, T, D), 4)
+    out, last = oracle.scan_fwd(a, b, h0=rand((B, D), 5))
+    assert np.array_equal(out, b) and np.array_equal(last, b[:, -1])
+    ga, gb, gh0 = oracle.scan_bwd(a, out, g)
+    assert np.array_equal(gb, g)
+    assert np.array_equal(ga[:, 1:], g[:, 1:] * b[:, :-1])
+    assert np.array_equal(ga[:, 0], np.zeros((B, D)))
+    assert np.array_equal(gh0, np.zeros((B, D)))
+
+
+@pytest.mark.parametrize("alpha,beta,gamma", [(0.9, 1.0, 1.0), (0.5, -2.0, 0.25), (1.5, 0.5, -1.0),
+                                              (-0.7, 1.0, 2.0)])
+def test_constant_coefficients_geometric_sum(alpha, beta, gamma):
+    B, T, D = 1, 40, 3
+    a = np.full((B, T, D), alpha)
+    b = np.full((B, T, D), beta)
+    g = np.full((B, T, D), gamma)
+    t = np.arange(T)[None, :, None]
+    out, last = oracle.scan_fwd(a, b)
+    h = beta * (1 - alpha ** (t + 1)) / (1 - alpha)
+    np.testing.assert_allclose(out, np.broadcast_to(h, out.shape), rtol=1e-12, atol=1e-12)
+    ga, gb, _ = oracle.scan_bwd(a, out, g)
+    lam = gamma * (1 - alpha ** (T - t)) / (1 - alpha)
+    np.testing.assert_allclose(gb, np.broadcast_to(lam, gb.shape), rtol=1e-12, atol=1e-12)
+    hprev = np.where(t > 0, beta * (1 - alpha ** t) / (1 - alpha), 0.0)
+    np.testing.assert_allclose(ga, np.broadcast_to(lam * hprev, ga.shape), rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# brute force on tiny inputs
+# ----------------------------------------------------------------------------
+def test_forward_matches_explicit_sum_exactly():
+    """h_t = sum_{k<=t} (prod_{j=k+1..t} a_j) b_k + (prod_{j=0..t} a_j) h0,
+    evaluated in exact rational arithmetic on dyadic inputs."""
+    B, T, D = 2, 9, 3
+    a = dyadic((B, T, D), 7, scale=4)
+    b = dyadic((B, T, D), 8, scale=4)
+    h0 = dyadic((B, D), 9, scale=4)
+    out, last = oracle.scan_fwd(a, b, h0=h0)
+    for bi in range(B):
+        for d in range(D):
+            A = [Fraction(x) for x in a[bi, :, d]]
+            Bv = [Fraction(x) for x in b[bi, :, d]]
+            for t in range(T):
+                s = Fraction(h0[bi, d])
+                for j in range(0, t + 1):
+                    s *= A[j]
+                for k in range(t + 1):
+                    p = Bv[k]
+                    for j in range(k + 1, t + 1):
+                        p *= A[j]
+                    s += p
+                assert out[bi, t, d] == float(s)  # dyadic, few bits: exact in fp64
+            assert last[bi, d] == out[bi, T - 1, d]
+
+
+def test_forward_jacobian_in_b():
+    """d out_s / d b_t = prod_{j=t+1..s} a_j for t <= s, zero for t > s."""
+    T = 8
+    a = rand((1, T, 1), 11, 0.3, 1.2)
+    for t in range(T):
+        e = np.zeros((1, T, 1))
+        e[0, t, 0] = 1.0
+        col, _ = oracle.scan_fwd(a, e)
+        for s in range(T):
+            want = np.prod(a[0, t + 1:s + 1, 0]) if s >= t else 0.0
+            assert col[0, s, 0] == pytest.approx(want, rel=1e-14, abs=0)
+
+
+def _loss(a, b, g, gl, h0):
+    out, last = oracle.scan_fwd(a, b, h0=h0)
+    return float(np.sum(g * out) + np.sum(gl * last))
+
+
+def test_backward_matches_central_finite_differences():
+    B, T, D = 2, 6, 2
+    a = rand((B, T, D), 21, 0.2, 1.1)
+    b = rand((B, T, D), 22)
+    g = rand((B, T, D), 23)
+    gl = rand((B, D), 24)
+    h0 = rand((B, D), 25)
+    out, _ = oracle.scan_fwd(a, b, h0=h0)
+    ga, gb, gh0 = oracle.scan_bwd(a, out, g, h0=h0, grad_last=gl)
+    eps = 1e-6
+    for name, x, grad in (("a", a, ga), ("b", b, gb), ("h0", h0, gh0)):
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            ix = it.multi_index
+            args = {"a": a.copy(), "b": b.copy(), "h0": h0.copy()}
+            args[name][ix] += eps
+            up = _loss(args["a"], args["b"], g, gl, args["h0"])
+            args[name][ix] -= 2 * eps
+            dn = _loss(args["a"], args["b"], g, gl, args["h0"])
+            fd = (up - dn) / (2 * eps)
+            assert grad[ix] == pytest.approx(fd, rel=1e-7, abs=1e-8), (name, ix)
+
+
+def test_backward_matches_torch_autograd():
+    torch = pytest.importorskip("torch")
+    B, T, D = 2, 11, 3
+    a = rand((B, T, D), 31, -1.1, 1.1)
+    b = rand((B, T, D), 32)
+    g = rand((B, T, D), 33)
+    gl = rand((B, D), 34)
+    h0 = rand((B, D), 35)
+    ta = torch.tensor(a, requires_grad=True)
+    tb = torch.tensor(b, requires_grad=True)
+    th0 = torch.tensor(h0, requires_grad=True)
+    h = th0
+    outs = []
+    for t in range(T):
+        h = ta[:, t] * h + tb[:, t]
+        outs.append(h)
+    tout = torch.stack(outs, dim=1)
+    loss = (tout * torch.tensor(g)).sum() + (h * torch.tensor(gl)).sum()
+    loss.backward()
+    out, last = oracle.scan_fwd(a, b, h0=h0)
+    np.testing.assert_allclose(out, tout.detach().numpy(), rtol=1e-13, atol=1e-13)
+    ga, gb, gh0 = oracle.scan_bwd(a, out, g, h0=h0, grad_last=gl)
+    np.testing.assert_allclose(ga, ta.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(gb, tb.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(gh0, th0.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# identities at moderate size
+# ----------------------------------------------------------------------------
+def test_adjoint_identity():
+    """out is linear in (b, h0): <g,out> + <gl,last> = <grad_b,b> + <grad_h0,h0>."""
+    B, T, D = 3, 500, 7
+    a = rand((B, T, D), 41, 0.8, 1.0)
+    b = rand((B, T, D), 42)
+    g = rand((B, T, D), 43)
+    gl = rand((B, D), 44)
+    h0 = rand((B, D), 45)
+    out, last = oracle.scan_fwd(a, b, h0=h0)
+    ga, gb, gh0 = oracle.scan_bwd(a, out, g, h0=h0, grad_last=gl)
+    lhs = np.sum(g * out) + np.sum(gl * last)
+    rhs = np.sum(gb * b) + np.sum(gh0 * h0)
+    assert lhs == pytest.approx(rhs, rel=1e-11)
+
+
+def test_time_reversal_duality():
+    """grad_b is the forward scan run backwards in time: with
+    at_tau = a_{T-tau} (tau >= 1), at_0 = 1, bt_tau = g_{T-1-tau} and initial
+    state grad_last, flip(scan(at, bt)) = grad_b."""
+    B, T, D = 2, 64, 5
+    a = rand((B, T, D), 51, 0.5, 1.0)
+    b = rand((B, T, D), 52)
+    g = rand((B, T, D), 53)
+    gl = rand((B, D), 54)
+    out, _ = oracle.scan_fwd(a, b)
+    _, gb, gh0 = oracle.scan_bwd(a, out, g, grad_last=gl)
+    at = np.concatenate([np.ones((B, 1, D)), np.flip(a[:, 1:], axis=1)], axis=1)
+    bt = np.flip(g, axis=1)
+    dual, dual_last = oracle.scan_fwd(at, bt, h0=gl)
+    np.testing.assert_allclose(np.flip(dual, axis=1), gb, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a[:, 0] * dual_last, gh0, rtol=1e-12, atol=1e-12)
+
+
+def test_linearity_in_b():
+    B, T, D = 2, 100, 3
+    a = rand((B, T, D), 61, 0.5, 1.0)
+    b1 = rand((B, T, D), 62)
+    b2 = rand((B, T, D), 63)
+    o1, _ = oracle.scan_fwd(a, b1)
+    o2, _ = oracle.scan_fwd(a, b2)
+    o3, _ = oracle.scan_fwd(a, 2.0 * b1 - 3.0 * b2)
+    np.testing.assert_allclose(o3, 2.0 * o1 - 3.0 * o2, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# chunk forms: associativity against the sequential definition
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("T,C", [(64, 16), (100, 16), (65, 64), (1, 16), (256, 256), (300, 128)])
+def test_chunk_forms_equal_sequential(T, C):
+    B, D = 2, 3
+    a = rand((B, T, D), 71, 0.6, 1.05)
+    b = rand((B, T, D), 72)
+    g = rand((B, T, D), 73)
+    gl = rand((B, D), 74)
+    h0 = rand((B, D), 75)
+    out, last = oracle.scan_fwd(a, b, h0=h0)
+    P, Q = oracle.chunk_summary(a, b, C)
+    NC = oracle.n_chunks(T, C)
+    assert P.shape == (B, NC, D)
+    # P is a plain product over the chunk (numpy prod), Q the chunk scanned from zero
+    for k in range(NC):
+        sl = slice(k * C, min(k * C + C, T))
+        np.testing.assert_allclose(P[:, k], np.prod(a[:, sl], axis=1), rtol=1e-13)
+        q, _ = oracle.scan_fwd(a[:, sl], b[:, sl])
+        np.testing.assert_allclose(Q[:, k], q[:, -1], rtol=1e-13)
+    cin, plast = oracle.chunk_prefix(P, Q, h0=h0)
+    np.testing.assert_allclose(cin[:, 0], h0, rtol=0, atol=0)
+    np.testing.assert_allclose(plast, last, rtol=1e-12, atol=1e-12)
+    ro, rl = oracle.chunk_replay(a, b, cin, C)
+    np.testing.assert_allclose(ro, out, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(rl, last, rtol=1e-12, atol=1e-12)
+    for k in range(1, NC):
+        np.testing.assert_allclose(cin[:, k], out[:, k * C - 1], rtol=1e-12, atol=1e-12)
+
+    ga, gb, gh0 = oracle.scan_bwd(a, out, g, h0=h0, grad_last=gl)
+    rP, rQ = oracle.reverse_chunk_summary(a, g, C)
+    for k in range(NC):
+        sl = slice(k * C, min(k * C + C, T))
+        np.testing.assert_allclose(rP[:, k], np.prod(a[:, sl], axis=1), rtol=1e-13)
+    fut, rg0 = oracle.reverse_chunk_prefix(rP, rQ, grad_last=gl)
+    np.testing.assert_allclose(fut[:, NC - 1], gl, rtol=0, atol=0)
+    np.testing.assert_allclose(rg0, gh0, rtol=1e-12, atol=1e-12)
+    # the carry entering chunk k from the right is a_{t} lambda_{t} at its first row after it
+    for k in range(NC - 1):
+        t = (k + 1) * C
+        np.testing.assert_allclose(fut[:, k], a[:, t] * gb[:, t], rtol=1e-12, atol=1e-12)
+    rga, rgb = oracle.reverse_chunk_replay(a, out, g, fut, C, h0=h0)
+    np.testing.assert_allclose(rga, ga, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(rgb, gb, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# masked workload invariants: resets and padding
+# ----------------------------------------------------------------------------
+def test_reset_and_padding_invariants():
+    rng = np.random.default_rng(81)
+    B, T, D = 2, 60, 4
+    a = rng.uniform(0.5, 1.0, (B, T, D))
+    b = rng.standard_normal((B, T, D))
+    g = rng.standard_normal((B, T, D))
+    r = 23  # reset step in every batch row
+    pads = [5, 6, 40, 41, 42]
+    a[:, r] = 0.0
+    a[:, pads] = 1.0
+    b[:, pads] = 0.0
+    g[:, pads] = 0.0
+    out, _ = oracle.scan_fwd(a, b)
+    ga, gb, _ = oracle.scan_bwd(a, out, g)
+    # a reset restarts the scan: out_r = b_r, and the suffix equals a fresh scan
+    assert np.array_equal(out[:, r], b[:, r])
+    fresh, _ = oracle.scan_fwd(a[:, r:], b[:, r:])
+    np.testing.assert_allclose(out[:, r:], fresh, rtol=1e-13, atol=1e-13)
+    # gradients before the reset do not see grad_out after it
+    g2 = g.copy()
+    g2[:, r + 1:] = rng.standard_normal((B, T - r - 1, D))
+    ga2, gb2, _ = oracle.scan_bwd(a, out, g2)
+    assert np.array_equal(gb2[:, :r], gb[:, :r])
+    assert np.array_equal(ga2[:, :r], ga[:, :r])
+    # padding steps pass the state through
+    for p in pads:
+        np.testing.assert_allclose(out[:, p], out[:, p - 1], rtol=0, atol=0)
+    # compaction: dropping padding steps leaves every kept output unchanged
+    keep = [t for t in range(T) if t not in pads]
+    oc, _ = oracle.scan_fwd(a[:, keep], b[:, keep])
+    np.testing.assert_allclose(oc, out[:, keep], rtol=1e-13, atol=1e-13)
+    gac, gbc, _ = oracle.scan_bwd(a[:, keep], oc, g[:, keep])
+    np.testing.assert_allclose(gbc, gb[:, keep], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(gac, ga[:, keep], rtol=1e-12, atol=1e-12)
+
+
+def test_last_equals_final_state_and_threads_agree():
+    B, T, D = 3, 200, 33
+    a = rand((B, T, D), 91, 0.8, 1.0)
+    b = rand((B, T, D), 92)
+    g = rand((B, T, D), 93)
+    out, last = oracle.scan_fwd(a, b)
+    assert np.array_equal(last, out[:, -1])
+    out4, last4 = oracle.scan_fwd(a, b, threads=4)
+    assert np.array_equal(out4, out) and np.array_equal(last4, last)
+    r1 = oracle.scan_bwd(a, out, g)
+    r4 = oracle.scan_bwd(a, out, g, threads=5)
+    for x, y in zip(r1, r4):
+        assert np.array_equal(x, y)

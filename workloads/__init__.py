@@ -1,0 +1,216 @@
+"""Seeded synthetic inputs for the diagonal affine scan workloads.
+
+This module holds no arithmetic of the scan itself: it only draws random
+tensors and stores them in the I/O format (float32, or bfloat16 bit patterns
+rounded to nearest-even).  Both the oracle side (tests, CPU baseline) and the
+GPU side (tests, bench, smoke) take their inputs from here, so both see the
+same bits.
+
+Recipes (one per workload; the five named workloads below are the shapes the
+scan is specified on, with the value distributions stated for each):
+
+* ``small``   B=2  T=256    D=64   fp32  a~U(0.9,0.999)   b=N(0,1)*sqrt(1-a^2)
+* ``wide``    B=8  T=2048   D=2560 bf16  a=clip(sigmoid(N(4,1)),0.8,0.9999)
+                                         b=N(0,1)*sqrt(1-a^2)
+* ``long32``  B=4  T=8192   D=4096 fp32  a~U(0.95,0.9999)  b~N(0,1)
+* ``longseq`` B=1  T=131072 D=1024 bf16  a~U(0.99,0.99999) b~N(0, sd 0.1)
+* ``masked``  B=16 T=4096   D=2560 bf16  a~U(0.5,0.9999); per token (b,t)
+              10% padding steps (a=1, b=0, g=0) and 5% reset steps (a=0);
+              b=N(0,1)*sqrt(1-a^2) using the final a.
+
+In every recipe grad_out ~ N(0,1) (zero at padding tokens), the draws are
+i.i.d. per element, numpy ``default_rng(seed)`` (PCG64) is used in float64 in
+the order a, masks, b, grad_out, and the values are then cast to float32 and,
+for bf16 workloads, rounded to bfloat16 (nearest-even).  The draws are made
+one batch row at a time (a, masks, b, grad_out for row 0, then row 1, ...),
+which bounds host memory; that row order is part of the recipe.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int
+    D: int
+    dtype: str  # "f32" or "bf16"
+    recipe: str  # key into _RECIPES
+    chunk: int = 0  # chunk length the workload is specified with (0: unspecified)
+
+    @property
+    def N(self) -> int:
+        return self.B * self.T * self.D
+
+    @property
+    def itemsize(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    def with_shape(self, B=None, T=None, D=None, name=None) -> "Workload":
+        return dataclasses.replace(self, B=B or self.B, T=T or self.T, D=D or self.D,
+                                   name=name or self.name)
+
+
+WORKLOADS = {
+    "small": Workload("small", 2, 256, 64, "f32", "small", 64),
+    "wide": Workload("wide", 8, 2048, 2560, "bf16", "wide"),
+    "long32": Workload("long32", 4, 8192, 4096, "f32", "long32", 64),
+    "longseq": Workload("longseq", 1, 131072, 1024, "bf16", "longseq", 64),
+    "masked": Workload("masked", 16, 4096, 2560, "bf16", "masked"),
+}
+
+
+# ----------------------------------------------------------------------------
+# storage formats
+# ----------------------------------------------------------------------------
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even.
+
+    NaN inputs map to a quiet NaN."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint32)
+    nan = (u & np.uint64(0x7FFFFFFF)) > np.uint64(0x7F800000)
+    r = np.where(nan, ((u >> np.uint64(16)).astype(np.uint32) | np.uint32(0x40)), r)
+    return (r & np.uint32(0xFFFF)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float32 (exact)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_storage(x64: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 draw -> stored I/O representation (float32, or uint16 bf16 bits)."""
+    x32 = x64.astype(np.float32)
+    return x32 if dtype == "f32" else f32_to_bf16_bits(x32)
+
+
+def storage_to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored representation -> the exact values it holds, in float64."""
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    return bf16_bits_to_f32(x).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# recipes: each returns float64 (a, b, g) for one batch row of shape [T, D]
+# ----------------------------------------------------------------------------
+def _row_small(rng, T, D):
+    a = rng.uniform(0.9, 0.999, size=(T, D))
+    b = rng.standard_normal((T, D)) * np.sqrt(1.0 - a * a)
+    g = rng.standard_normal((T, D))
+    return a, b, g
+
+
+def _row_wide(rng, T, D):
+    z = rng.normal(4.0, 1.0, size=(T, D))
+    a = np.clip(1.0 / (1.0 + np.exp(-z)), 0.8, 0.9999)
+    b = rng.standard_normal((T, D)) * np.sqrt(1.0 - a * a)
+    g = rng.standard_normal((T, D))
+    return a, b, g
+
+
+def _row_long32(rng, T, D):
+    a = rng.uniform(0.95, 0.9999, size=(T, D))
+    b = rng.standard_normal((T, D))
+    g = rng.standard_normal((T, D))
+    return a, b, g
+
+
+def _row_longseq(rng, T, D):
+    a = rng.uniform(0.99, 0.99999, size=(T, D))
+    b = rng.normal(0.0, 0.1, size=(T, D))
+    g = rng.standard_normal((T, D))
+    return a, b, g
+
+
+PAD_FRACTION = 0.10
+RESET_FRACTION = 0.05
+
+
+def _row_masked(rng, T, D):
+    a = rng.uniform(0.5, 0.9999, size=(T, D))
+    # token masks, per (b, t) across all D: padding with p=0.10, then resets
+    # among the non-padding tokens so that 5% of all tokens are resets.
+    pad = rng.random(T) < PAD_FRACTION
+    reset = (rng.random(T) < RESET_FRACTION / (1.0 - PAD_FRACTION)) & ~pad
+    a[pad, :] = 1.0
+    a[reset, :] = 0.0
+    b = rng.standard_normal((T, D)) * np.sqrt(1.0 - a * a)
+    b[pad, :] = 0.0
+    g = rng.standard_normal((T, D))
+    g[pad, :] = 0.0
+    return a, b, g, pad, reset
+
+
+_RECIPES = {
+    "small": _row_small,
+    "wide": _row_wide,
+    "long32": _row_long32,
+    "longseq": _row_longseq,
+    "masked": _row_masked,
+}
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Stored inputs of one workload: float32 arrays, or uint16 bf16 bit arrays."""
+    workload: Workload
+    a: np.ndarray
+    b: np.ndarray
+    g: np.ndarray
+    pad: Optional[np.ndarray] = None  # [B, T] bool (masked workload only)
+    reset: Optional[np.ndarray] = None
+
+    def f64(self, name: str, lanes=None) -> np.ndarray:
+        """Exact stored values as float64, optionally restricted to lanes.
+
+        ``lanes`` is a list of (b, d) pairs; the result is then [1, T, len]."""
+        x = getattr(self, name)
+        if lanes is not None:
+            bs = np.array([l[0] for l in lanes])
+            ds = np.array([l[1] for l in lanes])
+            x = x[bs, :, ds].T[None]  # [1, T, L]
+        return storage_to_f64(x, self.workload.dtype)
+
+
+def generate(wl: Workload, seed: int = 0, need_grad: bool = True) -> Inputs:
+    """Draw the stored inputs of ``wl`` (row by row over the batch)."""
+    recipe = _RECIPES[wl.recipe]
+    st = np.float32 if wl.dtype == "f32" else np.uint16
+    a = np.empty((wl.B, wl.T, wl.D), st)
+    b = np.empty_like(a)
+    g = np.empty_like(a) if need_grad else None
+    pad = reset = None
+    if wl.recipe == "masked":
+        pad = np.zeros((wl.B, wl.T), bool)
+        reset = np.zeros((wl.B, wl.T), bool)
+    rng = np.random.default_rng(seed)
+    for bi in range(wl.B):
+        res = recipe(rng, wl.T, wl.D)
+        a[bi] = to_storage(res[0], wl.dtype)
+        b[bi] = to_storage(res[1], wl.dtype)
+        if need_grad:
+            g[bi] = to_storage(res[2], wl.dtype)
+        if pad is not None:
+            pad[bi], reset[bi] = res[3], res[4]
+    return Inputs(wl, a, b, g, pad, reset)
+
+
+def sample_lanes(wl: Workload, count: int, seed: int = 1):
+    """A reproducible set of distinct (b, d) lanes, always including the corners."""
+    rng = np.random.default_rng(seed)
+    lanes = {(0, 0), (wl.B - 1, wl.D - 1), (0, wl.D - 1), (wl.B - 1, 0)}
+    total = wl.B * wl.D
+    while len(lanes) < min(count, total):
+        k = int(rng.integers(total))
+        lanes.add((k // wl.D, k % wl.D))
+    return sorted(lanes)
