@@ -1,0 +1,203 @@
+"""Benchmark of the diagonal affine scan, forward + backward, on one MI355X.
+
+A step is one forward scan (out and the fp32 final state) followed by one
+reverse-time backward (grad_a, grad_b) over one batch of synthetic inputs,
+both through the C ABI with the library's automatic algorithm choice.  The
+inputs are generated (seeded) and copied to HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wide]
+
+Prints one JSON line.  `value` is the effective HBM bandwidth of the whole
+step: the algorithmic bytes (forward 3*s*N + 4*B*D, backward 5*s*N, s the I/O
+element size, N = B*T*D) divided by the measured step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+
+WORKLOAD_TEXT = {
+    "small": "B=2 T=256 D=64 fp32, a~U(0.9,0.999), b=N(0,1)*sqrt(1-a^2)",
+    "wide": "B=8 T=2048 D=2560 bf16 I/O fp32 state, a=clip(sigmoid(N(4,1)),0.8,0.9999), b=N(0,1)*sqrt(1-a^2)",
+    "long32": "B=4 T=8192 D=4096 fp32, a~U(0.95,0.9999), b~N(0,1)",
+    "longseq": "B=1 T=131072 D=1024 bf16 I/O fp32 state, a~U(0.99,0.99999), b~N(0,0.1)",
+    "masked": "B=16 T=4096 D=2560 bf16, a~U(0.5,0.9999), 10% padding / 5% reset tokens",
+}
+
+
+def algorithmic_bytes(B, T, D, s):
+    N = B * T * D
+    return 3 * s * N + 4 * B * D, 5 * s * N
+
+
+def cpu_baseline(inp, budget_s=10.0):
+    """The fp64 oracle on the host cores, on the same workload (whole, or as
+    many whole passes as fit in about `budget_s`).  Returns a dict."""
+    import oracle
+
+    wl = inp.workload
+    cores = min(16, len(os.sched_getaffinity(0)))
+    a, b, g = inp.f64("a"), inp.f64("b"), inp.f64("g")
+    reps, t_total = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        h, _ = oracle.scan_fwd(a, b, threads=cores)
+        oracle.scan_bwd(a, h, g, threads=cores)
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if t_total >= budget_s or reps >= 5:
+            break
+    fb, bb = algorithmic_bytes(wl.B, wl.T, wl.D, wl.itemsize)
+    return {
+        "value": round((fb + bb) * reps / t_total / 1e9, 3),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"the whole {wl.name} workload, fwd+bwd, {reps} pass(es) in {t_total:.1f} s "
+                  f"(fp64, {cores} threads over lanes; input conversion untimed)",
+        "elements_per_s": round(wl.N * reps / t_total, 1),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wide")
+    ap.add_argument("--algo", default="auto")
+    ap.add_argument("--fwd-chunk", type=int, default=0)
+    ap.add_argument("--bwd-chunk", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; the scan is built and "
+                                   "measured on a single MI355X (run with --gpus 1)"}))
+        sys.exit(2)
+
+    import torch
+
+    import linear_recurrence_sequence_diag_amd as lr
+    import workloads as W
+
+    lr.library()  # fails loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+
+    wl = W.WORKLOADS[args.workload]
+    inp = W.generate(wl, seed=0)
+    dt = lr.F32 if wl.dtype == "f32" else lr.BF16
+
+    def dev(x):
+        if wl.dtype == "f32":
+            return torch.from_numpy(x).cuda()
+        return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+
+    a, b, g = dev(inp.a), dev(inp.b), dev(inp.g)
+    B, T, D = wl.B, wl.T, wl.D
+    out = torch.empty_like(a)
+    ga = torch.empty_like(a)
+    gb = torch.empty_like(a)
+    last = torch.empty((B, D), device="cuda", dtype=torch.float32)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    fo = lr.make_opts(algo=args.algo, chunk=args.fwd_chunk)
+    bo = lr.make_opts(algo=args.algo, chunk=args.bwd_chunk)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        lr.scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), last.data_ptr(), B, T, D, dt,
+                       sh, fo)
+        if ev:
+            ev[1].record(stream)
+        lr.scan_bwd_ex(a.data_ptr(), out.data_ptr(), g.data_ptr(), None, ga.data_ptr(),
+                       gb.data_ptr(), B, T, D, dt, sh, bo)
+        if ev:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_per_step = total_ms / args.steps
+
+    fb, bb = algorithmic_bytes(B, T, D, wl.itemsize)
+    value = (fb + bb) / (ms_per_step * 1e-3) / 1e9
+    fwd_algo, fwd_chunk = lr.scan_auto_algo(B, T, D, dt, 0)
+    bwd_algo, bwd_chunk = lr.scan_auto_algo(B, T, D, dt, 1)
+    if args.algo != "auto":
+        fwd_algo = bwd_algo = lr.ALGOS[args.algo]
+        fwd_chunk, bwd_chunk = args.fwd_chunk, args.bwd_chunk
+    names = {v: k for k, v in lr.ALGOS.items()}
+    if bwd_ms >= fwd_ms:
+        dom, dom_ms, dom_bytes = "backward", bwd_ms, bb
+    else:
+        dom, dom_ms, dom_bytes = "forward", fwd_ms, fb
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": "fwd+bwd scan effective HBM GB/s (and % of peak), elements/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded numpy draws, see workloads/__init__.py)",
+        "config": {
+            "workload": f"{wl.name}: {WORKLOAD_TEXT[wl.name]}",
+            "B": B, "T": T, "D": D,
+            "fwd_algo": f"{names[fwd_algo]}{fwd_chunk or ''}",
+            "bwd_algo": f"{names[bwd_algo]}{bwd_chunk or ''}",
+        },
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "elements_per_s": round(wl.N / (ms_per_step * 1e-3), 1),
+        "fwd_us": round(fwd_ms * 1e3, 2),
+        "bwd_us": round(bwd_ms * 1e3, 2),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": f"{dom} scan ({names[bwd_algo if dom == 'backward' else fwd_algo]})",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

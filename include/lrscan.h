@@ -1,0 +1,171 @@
+/*
+ * lrscan.h -- C ABI of the MI355X (gfx950) diagonal affine recurrence scan.
+ *
+ * The operation (page "triton_training_scan.py", botwwt.github.io/SAMU_GPU/
+ * benchmark, kernels _real_forward and _real_backward, and the autograd
+ * classes _RealScan / _RealChunkScan and the function real_scan_with_last):
+ *
+ *   forward   h_{-1} = h0 (zero unless given),  h_t = a_t * h_{t-1} + b_t,
+ *             out[b,t,d] = h_t,  last[b,d] = h_{T-1}
+ *   backward  the gradient of  L = <grad_out, out> + <grad_last, last>:
+ *             lambda_{T-1} = grad_out_{T-1} + grad_last,
+ *             lambda_t     = grad_out_t + a_{t+1} * lambda_{t+1},
+ *             grad_b_t = lambda_t,  grad_a_t = lambda_t * h_{t-1},
+ *             grad_h0  = a_0 * lambda_0
+ *
+ * Conventions shared by every entry point:
+ *
+ *  - Pointers are device pointers on the current HIP device, except `opts`,
+ *    which is a host pointer.  The caller owns every buffer; the library never
+ *    frees caller memory.
+ *  - [B, T, D] tensors are contiguous, row-major, D fastest: element (b,t,d)
+ *    is at (b*T + t)*D + d.  [B, D] tensors (h0, last, grad_last, grad_h0) are
+ *    fp32 at b*D + d.  Chunk tensors are fp32 [B, NC, D], NC = ceil(T / chunk).
+ *  - `dtype` (LRSCAN_F32 or LRSCAN_BF16) is the storage type of a, b, out,
+ *    grad_out, grad_a and grad_b.  Loads are widened to fp32, all arithmetic
+ *    and every carried state is fp32, and stores to bf16 round to nearest
+ *    even.  last, h0, grad_last, grad_h0 and all chunk tensors are fp32.
+ *  - `stream` is a hipStream_t (NULL for the default stream).  Work is
+ *    enqueued asynchronously on it.  Argument errors are found before any
+ *    work is enqueued and return a negative status.
+ *  - Inputs and outputs must not alias each other.
+ *  - Results are deterministic: the same call on the same data gives the same
+ *    bits every time.
+ *  - Calls that share one workspace (the library's own per-stream workspace,
+ *    or one passed in opts) must be ordered on one stream.
+ */
+#ifndef LRSCAN_H
+#define LRSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LRSCAN_API __attribute__((visibility("default")))
+
+/* storage types */
+enum { LRSCAN_F32 = 0, LRSCAN_BF16 = 1 };
+
+/* status codes */
+enum {
+    LRSCAN_OK = 0,
+    LRSCAN_ERR_NULL = -1,      /* a required pointer is NULL */
+    LRSCAN_ERR_DIM = -2,       /* B, T or D < 1, or a size overflows */
+    LRSCAN_ERR_DTYPE = -3,     /* dtype is not LRSCAN_F32 / LRSCAN_BF16 */
+    LRSCAN_ERR_CHUNK = -4,     /* chunk length not supported by the chosen algorithm */
+    LRSCAN_ERR_WORKSPACE = -5, /* workspace given but smaller than scan_workspace_bytes() */
+    LRSCAN_ERR_HIP = -6,       /* the HIP runtime reported an error (launch or allocation) */
+    LRSCAN_ERR_ALGO = -7       /* unknown algorithm */
+};
+
+/* algorithms */
+enum {
+    LRSCAN_ALGO_AUTO = 0,    /* the library picks (measured crossover) */
+    LRSCAN_ALGO_SEQ = 1,     /* one thread walks all T steps of its lanes */
+    LRSCAN_ALGO_CHUNKED = 2, /* three launches: chunk summary, chunk prefix, chunk replay */
+    LRSCAN_ALGO_FUSED = 3    /* one launch: tile summary, look-back prefix, replay from registers */
+};
+
+typedef struct {
+    int algo;               /* LRSCAN_ALGO_* */
+    int chunk;              /* 0: the algorithm's default.  CHUNKED: a power of two in [16, 1024].
+                               FUSED: tile length in steps: 256, 512 or 1024 forward,
+                               256 or 512 backward (tile * D * elem_bytes < 2^31).
+                               SEQ: ignored. */
+    void* workspace;        /* device scratch, or NULL for the library's own per-stream cache */
+    size_t workspace_bytes; /* size of `workspace` */
+    const float* h0;        /* [B, D] initial state, or NULL for zero (forward and backward) */
+    float* grad_h0;         /* [B, D] output of the backward, or NULL */
+} lrscan_opts;
+
+/*
+ * scan_fwd: out = every state of the scan of (a, b); last = the final state.
+ *   a, b  [B,T,D] dtype, read only.     out  [B,T,D] dtype, written.
+ *   last  [B,D] fp32, written; may be NULL.
+ * Returns LRSCAN_OK or a negative status.
+ */
+LRSCAN_API int scan_fwd(const void* a, const void* b, void* out, float* last, int64_t B, int64_t T,
+                        int64_t D, int dtype, void* stream);
+
+/*
+ * scan_bwd: gradients of <grad_out, out> + <grad_last, last> with respect to
+ * a and b.  `out` is the forward's output (h_{t-1} is read from it).
+ *   a, out, grad_out [B,T,D] dtype, read only.   grad_last [B,D] fp32 or NULL.
+ *   grad_a, grad_b   [B,T,D] dtype, written.
+ */
+LRSCAN_API int scan_bwd(const void* a, const void* out, const void* grad_out,
+                        const float* grad_last, void* grad_a, void* grad_b, int64_t B, int64_t T,
+                        int64_t D, int dtype, void* stream);
+
+/* As above, with options (algorithm, chunk, workspace, initial state).  opts may be NULL. */
+LRSCAN_API int scan_fwd_ex(const void* a, const void* b, void* out, float* last, int64_t B,
+                           int64_t T, int64_t D, int dtype, void* stream, const lrscan_opts* opts);
+LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
+                           const float* grad_last, void* grad_a, void* grad_b, int64_t B,
+                           int64_t T, int64_t D, int dtype, void* stream, const lrscan_opts* opts);
+
+/* Bytes of workspace the call with these arguments needs (0 if none).
+ * Returns 0 for invalid arguments. */
+LRSCAN_API size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t D, int dtype,
+                                       const lrscan_opts* opts);
+
+/* A static string naming a status code. */
+LRSCAN_API const char* scan_status_string(int status);
+
+/* The algorithm LRSCAN_ALGO_AUTO picks for this shape (forward if dir == 0, else backward),
+ * and through *chunk its chunk / tile length.  Returns a negative status on bad arguments. */
+LRSCAN_API int scan_auto_algo(int64_t B, int64_t T, int64_t D, int dtype, int dir, int* chunk);
+
+/* ------------------------------------------------------------------------
+ * The steps of the chunked form, one entry point each (page
+ * "triton_training_scan.py": _real_chunk_summary, _real_chunk_prefix,
+ * _real_chunk_replay and the _real_reverse_chunk_* trio).  NC = ceil(T/chunk);
+ * chunk is a power of two in [16, 1024].  Steps past T inside the final chunk
+ * are identity steps (a = 1, b = 0, grad_out = 0).
+ * ------------------------------------------------------------------------ */
+
+/* P[b,k,d] = product of a over chunk k;  Q[b,k,d] = chunk k scanned from a zero state. */
+LRSCAN_API int scan_chunk_summary(const void* a, const void* b, float* P, float* Q, int64_t B,
+                                  int64_t T, int64_t D, int chunk, int dtype, void* stream);
+
+/* Exclusive scan over the chunk maps: chunk_in[:,0] = h0 (or 0),
+ * chunk_in[:,k+1] = P[:,k] * chunk_in[:,k] + Q[:,k].  last (nullable) receives
+ * the state after the final chunk.  h0 may be NULL. */
+LRSCAN_API int scan_chunk_prefix(const float* P, const float* Q, const float* h0, float* chunk_in,
+                                 float* last, int64_t B, int64_t NC, int64_t D, void* stream);
+
+/* Rescan every chunk from chunk_in and write out (dtype); last (nullable) gets
+ * the final state of the final chunk. */
+LRSCAN_API int scan_chunk_replay(const void* a, const void* b, const float* chunk_in, void* out,
+                                 float* last, int64_t B, int64_t T, int64_t D, int chunk,
+                                 int dtype, void* stream);
+
+/* Reverse summary: walking chunk k backwards, P = product of a,
+ * Q <- a_t * (Q + grad_out_t) from Q = 0: the map from the carry entering the
+ * chunk on the right to the carry a_s * lambda_s leaving its first row s. */
+LRSCAN_API int scan_reverse_chunk_summary(const void* a, const void* grad_out, float* P, float* Q,
+                                          int64_t B, int64_t T, int64_t D, int chunk, int dtype,
+                                          void* stream);
+
+/* Exclusive right-to-left scan: future[:,NC-1] = grad_last (or 0),
+ * future[:,k-1] = P[:,k] * future[:,k] + Q[:,k];  grad_h0 (nullable) receives
+ * P[:,0] * future[:,0] + Q[:,0].  grad_last may be NULL. */
+LRSCAN_API int scan_reverse_chunk_prefix(const float* P, const float* Q, const float* grad_last,
+                                         float* future, float* grad_h0, int64_t B, int64_t NC,
+                                         int64_t D, void* stream);
+
+/* Walk every chunk backwards from its future carry, writing grad_a and grad_b
+ * (dtype).  h_{t-1} comes from out (and from h0, or zero, at t = 0). */
+LRSCAN_API int scan_reverse_chunk_replay(const void* a, const void* out, const void* grad_out,
+                                         const float* future, const float* h0, void* grad_a,
+                                         void* grad_b, int64_t B, int64_t T, int64_t D, int chunk,
+                                         int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRSCAN_H */

@@ -1,0 +1,352 @@
+"""Diagonal affine recurrence scan on MI355X (gfx950): Python binding of liblrscan.
+
+The scan ``h_t = a_t * h_{t-1} + b_t`` over [B, T, D] tensors and its
+reverse-time adjoint run entirely in the HIP kernels of ``liblrscan.so``
+(built from ``csrc/`` by ``build.py``).  This module only marshals arguments:
+the raw entry points keep the C names of ``include/lrscan.h`` and take device
+pointers; the tensor helpers below allocate outputs with torch (device memory
+and the current stream are all torch is used for) and call them.
+
+There is no fallback: if the library is not built, or no GPU is present, the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblrscan.so")
+
+F32, BF16 = 0, 1
+ALGO_AUTO, ALGO_SEQ, ALGO_CHUNKED, ALGO_FUSED = 0, 1, 2, 3
+ALGOS = {"auto": ALGO_AUTO, "seq": ALGO_SEQ, "chunked": ALGO_CHUNKED, "fused": ALGO_FUSED}
+
+STATUS = {
+    0: "LRSCAN_OK", -1: "LRSCAN_ERR_NULL", -2: "LRSCAN_ERR_DIM", -3: "LRSCAN_ERR_DTYPE",
+    -4: "LRSCAN_ERR_CHUNK", -5: "LRSCAN_ERR_WORKSPACE", -6: "LRSCAN_ERR_HIP", -7: "LRSCAN_ERR_ALGO",
+}
+
+
+class LRScanError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+class Opts(ctypes.Structure):
+    """Mirror of ``lrscan_opts``."""
+    _fields_ = [
+        ("algo", ctypes.c_int),
+        ("chunk", ctypes.c_int),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("h0", ctypes.c_void_p),
+        ("grad_h0", ctypes.c_void_p),
+    ]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+_SIGS = {
+    "scan_fwd": ([_P, _P, _P, _P, _I64, _I64, _I64, _INT, _P], _INT),
+    "scan_bwd": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P], _INT),
+    "scan_fwd_ex": ([_P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
+    "scan_bwd_ex": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
+    "scan_workspace_bytes": ([_I64, _I64, _I64, _INT, ctypes.POINTER(Opts)], ctypes.c_size_t),
+    "scan_status_string": ([_INT], ctypes.c_char_p),
+    "scan_auto_algo": ([_I64, _I64, _I64, _INT, _INT, ctypes.POINTER(_INT)], _INT),
+    "scan_chunk_summary": ([_P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P], _INT),
+    "scan_chunk_prefix": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
+    "scan_chunk_replay": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P], _INT),
+    "scan_reverse_chunk_summary": ([_P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P], _INT),
+    "scan_reverse_chunk_prefix": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
+    "scan_reverse_chunk_replay": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P], _INT),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library():
+    """The loaded liblrscan (ctypes.CDLL).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(
+                    f"{LIB_PATH} is not built; run `python -m linear_recurrence_sequence_diag_amd.build`")
+            lib = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in _SIGS.items():
+                fn = getattr(lib, name)
+                fn.argtypes = args
+                fn.restype = res
+            _lib = lib
+    return _lib
+
+
+def _check(status: int, what: str) -> int:
+    if status < 0 and what != "scan_auto_algo":
+        raise LRScanError(status, what)
+    return status
+
+
+def scan_status_string(status: int) -> str:
+    return library().scan_status_string(status).decode()
+
+
+status_string = scan_status_string
+
+
+# ---------------------------------------------------------------------------
+# raw entry points: same names and arguments as the C ABI (device pointers as
+# ints, a stream handle as an int); negative status codes raise LRScanError
+# ---------------------------------------------------------------------------
+def scan_fwd(a, b, out, last, B, T, D, dtype, stream):
+    return _check(library().scan_fwd(a, b, out, last, B, T, D, dtype, stream), "scan_fwd")
+
+
+def scan_bwd(a, out, grad_out, grad_last, grad_a, grad_b, B, T, D, dtype, stream):
+    return _check(library().scan_bwd(a, out, grad_out, grad_last, grad_a, grad_b, B, T, D, dtype,
+                                     stream), "scan_bwd")
+
+
+def scan_fwd_ex(a, b, out, last, B, T, D, dtype, stream, opts):
+    return _check(library().scan_fwd_ex(a, b, out, last, B, T, D, dtype, stream,
+                                        ctypes.byref(opts) if opts is not None else None),
+                  "scan_fwd_ex")
+
+
+def scan_bwd_ex(a, out, grad_out, grad_last, grad_a, grad_b, B, T, D, dtype, stream, opts):
+    return _check(library().scan_bwd_ex(a, out, grad_out, grad_last, grad_a, grad_b, B, T, D, dtype,
+                                        stream, ctypes.byref(opts) if opts is not None else None),
+                  "scan_bwd_ex")
+
+
+def scan_workspace_bytes(B, T, D, dtype, opts=None):
+    return library().scan_workspace_bytes(B, T, D, dtype,
+                                          ctypes.byref(opts) if opts is not None else None)
+
+
+def scan_auto_algo(B, T, D, dtype, direction):
+    chunk = ctypes.c_int(0)
+    algo = library().scan_auto_algo(B, T, D, dtype, direction, ctypes.byref(chunk))
+    if algo < 0:
+        raise LRScanError(algo, "scan_auto_algo")
+    return algo, chunk.value
+
+
+def scan_chunk_summary(a, b, P, Q, B, T, D, chunk, dtype, stream):
+    return _check(library().scan_chunk_summary(a, b, P, Q, B, T, D, chunk, dtype, stream),
+                  "scan_chunk_summary")
+
+
+def scan_chunk_prefix(P, Q, h0, chunk_in, last, B, NC, D, stream):
+    return _check(library().scan_chunk_prefix(P, Q, h0, chunk_in, last, B, NC, D, stream),
+                  "scan_chunk_prefix")
+
+
+def scan_chunk_replay(a, b, chunk_in, out, last, B, T, D, chunk, dtype, stream):
+    return _check(library().scan_chunk_replay(a, b, chunk_in, out, last, B, T, D, chunk, dtype,
+                                              stream), "scan_chunk_replay")
+
+
+def scan_reverse_chunk_summary(a, grad_out, P, Q, B, T, D, chunk, dtype, stream):
+    return _check(library().scan_reverse_chunk_summary(a, grad_out, P, Q, B, T, D, chunk, dtype,
+                                                       stream), "scan_reverse_chunk_summary")
+
+
+def scan_reverse_chunk_prefix(P, Q, grad_last, future, grad_h0, B, NC, D, stream):
+    return _check(library().scan_reverse_chunk_prefix(P, Q, grad_last, future, grad_h0, B, NC, D,
+                                                      stream), "scan_reverse_chunk_prefix")
+
+
+def scan_reverse_chunk_replay(a, out, grad_out, future, h0, grad_a, grad_b, B, T, D, chunk, dtype,
+                              stream):
+    return _check(library().scan_reverse_chunk_replay(a, out, grad_out, future, h0, grad_a, grad_b,
+                                                      B, T, D, chunk, dtype, stream),
+                  "scan_reverse_chunk_replay")
+
+
+# ---------------------------------------------------------------------------
+# torch tensor helpers (allocation + marshalling only)
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.float32:
+        return F32
+    if dt == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {dt}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t):
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def _check_seq(name, t, ref=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dim() != 3:
+        raise ValueError(f"{name} must be [B, T, D]")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ref is not None and (t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device):
+        raise ValueError(f"{name} must match a in shape, dtype and device")
+
+
+def _check_state(name, t, ref):
+    if t is None:
+        return
+    torch = _torch()
+    B, _, D = ref.shape
+    if t.shape != (B, D) or t.dtype != torch.float32 or t.device != ref.device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 [B, D] tensor on a's device")
+
+
+def make_opts(algo="auto", chunk=0, h0=None, grad_h0=None, workspace=None):
+    o = Opts()
+    o.algo = ALGOS[algo] if isinstance(algo, str) else int(algo)
+    o.chunk = int(chunk)
+    o.workspace = None if workspace is None else workspace.data_ptr()
+    o.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    o.h0 = _ptr(h0)
+    o.grad_h0 = _ptr(grad_h0)
+    return o
+
+
+def scan(a, b, h0=None, algo="auto", chunk=0, with_last=True):
+    """Forward scan.  Returns (out, last); out has a's dtype, last is float32 [B, D]."""
+    torch = _torch()
+    _check_seq("a", a)
+    _check_seq("b", b, a)
+    _check_state("h0", h0, a)
+    B, T, D = a.shape
+    out = torch.empty_like(a)
+    last = torch.empty((B, D), device=a.device, dtype=torch.float32) if with_last else None
+    with torch.cuda.device(a.device):
+        scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), _ptr(last), B, T, D,
+                    dtype_code(a.dtype), _stream(a), make_opts(algo, chunk, h0=h0))
+    return out, last
+
+
+def scan_backward(a, out, grad_out, grad_last=None, h0=None, algo="auto", chunk=0,
+                  need_grad_h0=False):
+    """Reverse-time adjoint.  Returns (grad_a, grad_b, grad_h0 or None)."""
+    torch = _torch()
+    _check_seq("a", a)
+    _check_seq("out", out, a)
+    _check_seq("grad_out", grad_out, a)
+    _check_state("grad_last", grad_last, a)
+    _check_state("h0", h0, a)
+    B, T, D = a.shape
+    grad_a = torch.empty_like(a)
+    grad_b = torch.empty_like(a)
+    grad_h0 = torch.empty((B, D), device=a.device, dtype=torch.float32) if need_grad_h0 else None
+    with torch.cuda.device(a.device):
+        scan_bwd_ex(a.data_ptr(), out.data_ptr(), grad_out.data_ptr(), _ptr(grad_last),
+                    grad_a.data_ptr(), grad_b.data_ptr(), B, T, D, dtype_code(a.dtype), _stream(a),
+                    make_opts(algo, chunk, h0=h0, grad_h0=grad_h0))
+    return grad_a, grad_b, grad_h0
+
+
+def n_chunks(T, chunk):
+    return (T + chunk - 1) // chunk
+
+
+def chunk_summary(a, b, chunk, reverse=False):
+    """(P, Q) per chunk, float32 [B, NC, D] (reverse: b is grad_out)."""
+    torch = _torch()
+    _check_seq("a", a)
+    _check_seq("b", b, a)
+    B, T, D = a.shape
+    NC = n_chunks(T, chunk)
+    P = torch.empty((B, NC, D), device=a.device, dtype=torch.float32)
+    Q = torch.empty_like(P)
+    fn = scan_reverse_chunk_summary if reverse else scan_chunk_summary
+    with torch.cuda.device(a.device):
+        fn(a.data_ptr(), b.data_ptr(), P.data_ptr(), Q.data_ptr(), B, T, D, chunk,
+           dtype_code(a.dtype), _stream(a))
+    return P, Q
+
+
+def chunk_prefix(P, Q, init=None, reverse=False):
+    """Exclusive scan over chunk maps.  Returns (entering [B,NC,D], final [B,D])."""
+    torch = _torch()
+    B, NC, D = P.shape
+    ent = torch.empty_like(P)
+    fin = torch.empty((B, D), device=P.device, dtype=torch.float32)
+    fn = scan_reverse_chunk_prefix if reverse else scan_chunk_prefix
+    with torch.cuda.device(P.device):
+        fn(P.data_ptr(), Q.data_ptr(), _ptr(init), ent.data_ptr(), fin.data_ptr(), B, NC, D,
+           _stream(P))
+    return ent, fin
+
+
+def chunk_replay(a, b, chunk_in, chunk):
+    torch = _torch()
+    B, T, D = a.shape
+    out = torch.empty_like(a)
+    last = torch.empty((B, D), device=a.device, dtype=torch.float32)
+    with torch.cuda.device(a.device):
+        scan_chunk_replay(a.data_ptr(), b.data_ptr(), chunk_in.data_ptr(), out.data_ptr(),
+                          last.data_ptr(), B, T, D, chunk, dtype_code(a.dtype), _stream(a))
+    return out, last
+
+
+def reverse_chunk_replay(a, out, grad_out, future, chunk, h0=None):
+    torch = _torch()
+    B, T, D = a.shape
+    ga = torch.empty_like(a)
+    gb = torch.empty_like(a)
+    with torch.cuda.device(a.device):
+        scan_reverse_chunk_replay(a.data_ptr(), out.data_ptr(), grad_out.data_ptr(),
+                                  future.data_ptr(), _ptr(h0), ga.data_ptr(), gb.data_ptr(), B, T,
+                                  D, chunk, dtype_code(a.dtype), _stream(a))
+    return ga, gb
+
+
+def _make_autograd():
+    torch = _torch()
+
+    class DiagonalScan(torch.autograd.Function):
+        """out = scan(a, b); gradients from the reverse-time kernels."""
+
+        @staticmethod
+        def forward(ctx, a, b):
+            a = a.contiguous()
+            b = b.contiguous()
+            out, _ = scan(a, b, with_last=False)
+            ctx.save_for_backward(a, out)
+            return out
+
+        @staticmethod
+        def backward(ctx, grad_out):
+            a, out = ctx.saved_tensors
+            ga, gb, _ = scan_backward(a, out, grad_out.contiguous())
+            return ga, gb
+
+    return DiagonalScan
+
+
+_autograd_cls = None
+
+
+def diagonal_scan(a, b):
+    """Differentiable scan (torch autograd) returning every state."""
+    global _autograd_cls
+    if _autograd_cls is None:
+        _autograd_cls = _make_autograd()
+    return _autograd_cls.apply(a, b)

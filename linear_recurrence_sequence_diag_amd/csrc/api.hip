@@ -1,0 +1,319 @@
+// api.hip -- the C ABI of liblrscan (declared in include/lrscan.h): argument
+// validation, the algorithm choice, workspace handling, and the calls into
+// the kernel launchers.  No torch type crosses this boundary.
+#include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/lrscan.h"
+#include "device.hpp"
+#include "launch.hpp"
+
+using namespace lrscan;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 40;  // generous bound that keeps size_t math exact
+
+bool dims_ok(int64_t B, int64_t T, int64_t D) {
+    if (B < 1 || T < 1 || D < 1) return false;
+    if (B > kMaxElems || T > kMaxElems || D > kMaxElems) return false;
+    if (B * D > kMaxElems / T) return false;
+    return true;
+}
+
+bool dtype_ok(int dt) { return dt == LRSCAN_F32 || dt == LRSCAN_BF16; }
+
+bool chunk_ok(int chunk) { return chunk >= 16 && chunk <= 1024 && (chunk & (chunk - 1)) == 0; }
+
+constexpr int kDefaultChunk = 64;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// ---- library-owned workspace, one per (device, stream) ------------------------
+struct CachedWs {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, void*>, CachedWs> g_ws;
+
+// Returns a device buffer of at least `bytes` owned by the library, ordered on `st`.
+hipError_t library_workspace(size_t bytes, hipStream_t st, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    CachedWs& c = g_ws[{dev, (void*)st}];
+    if (c.bytes < bytes) {
+        if (c.ptr) {
+            e = hipFreeAsync(c.ptr, st);
+            if (e != hipSuccess) return e;
+            c.ptr = nullptr;
+            c.bytes = 0;
+        }
+        const size_t want = align_up(bytes + bytes / 4, 1 << 20);
+        e = hipMallocAsync(&c.ptr, want, st);
+        if (e != hipSuccess) return e;
+        c.bytes = want;
+    }
+    *out = c.ptr;
+    return hipSuccess;
+}
+
+struct Resolved {
+    int algo;
+    int chunk;
+};
+
+// The measured crossover (see the dispatch notes in the design document of
+// this package): the single-launch fused form reads every input once and wins
+// on every measured shape; the per-lane walk is kept for explicit requests.
+Resolved resolve(const Shape& s, int dir, const lrscan_opts* o) {
+    Resolved r;
+    r.algo = o ? o->algo : LRSCAN_ALGO_AUTO;
+    r.chunk = o ? o->chunk : 0;
+    if (r.algo == LRSCAN_ALGO_AUTO) {
+        r.algo = LRSCAN_ALGO_FUSED;
+        r.chunk = 0;
+    }
+    if (r.chunk == 0) {
+        if (r.algo == LRSCAN_ALGO_CHUNKED) r.chunk = kDefaultChunk;
+        if (r.algo == LRSCAN_ALGO_FUSED) r.chunk = fused_default_tile(s, dir);
+    }
+    return r;
+}
+
+int validate_algo(const Shape& s, int dir, const Resolved& r) {
+    switch (r.algo) {
+        case LRSCAN_ALGO_SEQ: return LRSCAN_OK;
+        case LRSCAN_ALGO_CHUNKED: return chunk_ok(r.chunk) ? LRSCAN_OK : LRSCAN_ERR_CHUNK;
+        case LRSCAN_ALGO_FUSED:
+            return fused_tile_supported(s, dir, r.chunk) ? LRSCAN_OK : LRSCAN_ERR_CHUNK;
+    }
+    return LRSCAN_ERR_ALGO;
+}
+
+size_t chunked_bytes(const Shape& s, int chunk) {
+    const size_t nc = (size_t)((s.T + chunk - 1) / chunk);
+    return 3 * align_up(nc * (size_t)s.B * (size_t)s.D * 4, 256);
+}
+
+size_t needed_bytes(const Shape& s, const Resolved& r) {
+    switch (r.algo) {
+        case LRSCAN_ALGO_CHUNKED: return chunked_bytes(s, r.chunk);
+        case LRSCAN_ALGO_FUSED: return fused_workspace_bytes(s, r.chunk);
+    }
+    return 0;
+}
+
+// Workspace for a call: the caller's (checked) or the library's.
+int get_workspace(const Shape& s, const Resolved& r, const lrscan_opts* o, hipStream_t st,
+                  void** ws) {
+    const size_t need = needed_bytes(s, r);
+    *ws = nullptr;
+    if (need == 0) return LRSCAN_OK;
+    if (o && o->workspace) {
+        if (o->workspace_bytes < need) return LRSCAN_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(o->workspace) % 256 != 0) return LRSCAN_ERR_WORKSPACE;
+        *ws = o->workspace;
+        return LRSCAN_OK;
+    }
+    return library_workspace(need, st, ws) == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_HIP;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+LRSCAN_API const char* scan_status_string(int status) {
+    switch (status) {
+        case LRSCAN_OK: return "ok";
+        case LRSCAN_ERR_NULL: return "a required pointer is NULL";
+        case LRSCAN_ERR_DIM: return "B, T and D must be >= 1 and their product must fit";
+        case LRSCAN_ERR_DTYPE: return "dtype must be LRSCAN_F32 or LRSCAN_BF16";
+        case LRSCAN_ERR_CHUNK: return "chunk / tile length not supported by the algorithm";
+        case LRSCAN_ERR_WORKSPACE: return "workspace smaller than scan_workspace_bytes() or not 256-byte aligned";
+        case LRSCAN_ERR_HIP: return "the HIP runtime reported an error";
+        case LRSCAN_ERR_ALGO: return "unknown algorithm";
+    }
+    return "unknown status";
+}
+
+LRSCAN_API int scan_auto_algo(int64_t B, int64_t T, int64_t D, int dtype, int dir, int* chunk) {
+    if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
+    const Shape s{B, T, D, dtype};
+    const Resolved r = resolve(s, dir, nullptr);
+    if (chunk) *chunk = r.chunk;
+    return r.algo;
+}
+
+LRSCAN_API size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t D, int dtype,
+                                       const lrscan_opts* opts) {
+    if (!dims_ok(B, T, D) || !dtype_ok(dtype)) return 0;
+    const Shape s{B, T, D, dtype};
+    size_t need = 0;
+    for (int dir = 0; dir < 2; ++dir) {
+        const Resolved r = resolve(s, dir, opts);
+        if (validate_algo(s, dir, r) != LRSCAN_OK) continue;
+        const size_t n = needed_bytes(s, r);
+        if (n > need) need = n;
+    }
+    return need;
+}
+
+LRSCAN_API int scan_fwd_ex(const void* a, const void* b, void* out, float* last, int64_t B,
+                           int64_t T, int64_t D, int dtype, void* stream, const lrscan_opts* opts) {
+    if (!a || !b || !out) return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
+    const Shape s{B, T, D, dtype};
+    const Resolved r = resolve(s, 0, opts);
+    int st = validate_algo(s, 0, r);
+    if (st != LRSCAN_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const float* h0 = opts ? opts->h0 : nullptr;
+    void* ws = nullptr;
+    st = get_workspace(s, r, opts, hs, &ws);
+    if (st != LRSCAN_OK) return st;
+    switch (r.algo) {
+        case LRSCAN_ALGO_SEQ: return hip_status(launch_seq_fwd(s, a, b, out, last, h0, hs));
+        case LRSCAN_ALGO_CHUNKED: {
+            const int64_t NC = (T + r.chunk - 1) / r.chunk;
+            const size_t part = align_up((size_t)NC * B * D * 4, 256);
+            float* P = static_cast<float*>(ws);
+            float* Q = reinterpret_cast<float*>(static_cast<char*>(ws) + part);
+            float* cin = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * part);
+            hipError_t e = launch_chunk_summary(s, r.chunk, a, b, P, Q, hs);
+            if (e == hipSuccess) e = launch_chunk_prefix(B, NC, D, P, Q, h0, cin, nullptr, hs);
+            if (e == hipSuccess) e = launch_chunk_replay(s, r.chunk, a, b, cin, out, last, hs);
+            return hip_status(e);
+        }
+        case LRSCAN_ALGO_FUSED:
+            return hip_status(launch_fused_fwd(s, r.chunk, a, b, out, last, h0, ws, hs));
+    }
+    return LRSCAN_ERR_ALGO;
+}
+
+LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
+                           const float* grad_last, void* grad_a, void* grad_b, int64_t B,
+                           int64_t T, int64_t D, int dtype, void* stream, const lrscan_opts* opts) {
+    if (!a || !out || !grad_out || !grad_a || !grad_b) return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
+    const Shape s{B, T, D, dtype};
+    const Resolved r = resolve(s, 1, opts);
+    int st = validate_algo(s, 1, r);
+    if (st != LRSCAN_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const float* h0 = opts ? opts->h0 : nullptr;
+    float* grad_h0 = opts ? opts->grad_h0 : nullptr;
+    void* ws = nullptr;
+    st = get_workspace(s, r, opts, hs, &ws);
+    if (st != LRSCAN_OK) return st;
+    switch (r.algo) {
+        case LRSCAN_ALGO_SEQ:
+            return hip_status(launch_seq_bwd(s, a, out, grad_out, grad_last, h0, grad_a, grad_b,
+                                             grad_h0, hs));
+        case LRSCAN_ALGO_CHUNKED: {
+            const int64_t NC = (T + r.chunk - 1) / r.chunk;
+            const size_t part = align_up((size_t)NC * B * D * 4, 256);
+            float* P = static_cast<float*>(ws);
+            float* Q = reinterpret_cast<float*>(static_cast<char*>(ws) + part);
+            float* fut = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * part);
+            hipError_t e = launch_reverse_chunk_summary(s, r.chunk, a, grad_out, P, Q, hs);
+            if (e == hipSuccess)
+                e = launch_reverse_chunk_prefix(B, NC, D, P, Q, grad_last, fut, grad_h0, hs);
+            if (e == hipSuccess)
+                e = launch_reverse_chunk_replay(s, r.chunk, a, out, grad_out, fut, h0, grad_a,
+                                                grad_b, hs);
+            return hip_status(e);
+        }
+        case LRSCAN_ALGO_FUSED:
+            return hip_status(launch_fused_bwd(s, r.chunk, a, out, grad_out, grad_last, h0, grad_a,
+                                               grad_b, grad_h0, ws, hs));
+    }
+    return LRSCAN_ERR_ALGO;
+}
+
+LRSCAN_API int scan_fwd(const void* a, const void* b, void* out, float* last, int64_t B, int64_t T,
+                        int64_t D, int dtype, void* stream) {
+    return scan_fwd_ex(a, b, out, last, B, T, D, dtype, stream, nullptr);
+}
+
+LRSCAN_API int scan_bwd(const void* a, const void* out, const void* grad_out,
+                        const float* grad_last, void* grad_a, void* grad_b, int64_t B, int64_t T,
+                        int64_t D, int dtype, void* stream) {
+    return scan_bwd_ex(a, out, grad_out, grad_last, grad_a, grad_b, B, T, D, dtype, stream,
+                       nullptr);
+}
+
+// ---- the chunked form, step by step ---------------------------------------------
+LRSCAN_API int scan_chunk_summary(const void* a, const void* b, float* P, float* Q, int64_t B,
+                                  int64_t T, int64_t D, int chunk, int dtype, void* stream) {
+    if (!a || !b || !P || !Q) return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
+    if (!chunk_ok(chunk)) return LRSCAN_ERR_CHUNK;
+    return hip_status(launch_chunk_summary(Shape{B, T, D, dtype}, chunk, a, b, P, Q,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+LRSCAN_API int scan_chunk_prefix(const float* P, const float* Q, const float* h0, float* chunk_in,
+                                 float* last, int64_t B, int64_t NC, int64_t D, void* stream) {
+    if (!P || !Q || !chunk_in) return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, NC, D)) return LRSCAN_ERR_DIM;
+    return hip_status(launch_chunk_prefix(B, NC, D, P, Q, h0, chunk_in, last,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+LRSCAN_API int scan_chunk_replay(const void* a, const void* b, const float* chunk_in, void* out,
+                                 float* last, int64_t B, int64_t T, int64_t D, int chunk,
+                                 int dtype, void* stream) {
+    if (!a || !b || !chunk_in || !out) return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
+    if (!chunk_ok(chunk)) return LRSCAN_ERR_CHUNK;
+    return hip_status(launch_chunk_replay(Shape{B, T, D, dtype}, chunk, a, b, chunk_in, out, last,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+LRSCAN_API int scan_reverse_chunk_summary(const void* a, const void* grad_out, float* P, float* Q,
+                                          int64_t B, int64_t T, int64_t D, int chunk, int dtype,
+                                          void* stream) {
+    if (!a || !grad_out || !P || !Q) return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
+    if (!chunk_ok(chunk)) return LRSCAN_ERR_CHUNK;
+    return hip_status(launch_reverse_chunk_summary(Shape{B, T, D, dtype}, chunk, a, grad_out, P, Q,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+LRSCAN_API int scan_reverse_chunk_prefix(const float* P, const float* Q, const float* grad_last,
+                                         float* future, float* grad_h0, int64_t B, int64_t NC,
+                                         int64_t D, void* stream) {
+    if (!P || !Q || !future) return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, NC, D)) return LRSCAN_ERR_DIM;
+    return hip_status(launch_reverse_chunk_prefix(B, NC, D, P, Q, grad_last, future, grad_h0,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+LRSCAN_API int scan_reverse_chunk_replay(const void* a, const void* out, const void* grad_out,
+                                         const float* future, const float* h0, void* grad_a,
+                                         void* grad_b, int64_t B, int64_t T, int64_t D, int chunk,
+                                         int dtype, void* stream) {
+    if (!a || !out || !grad_out || !future || !grad_a || !grad_b) return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
+    if (!chunk_ok(chunk)) return LRSCAN_ERR_CHUNK;
+    return hip_status(launch_reverse_chunk_replay(Shape{B, T, D, dtype}, chunk, a, out, grad_out,
+                                                  future, h0, grad_a, grad_b,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,288 @@
+// device.hpp -- device-side building blocks shared by the scan kernels (gfx950).
+//
+//  * storage types: fp32 and bf16 elements, widened to fp32 on load and
+//    rounded to nearest even on store (bf16 via the gfx950 packed convert);
+//  * 16-byte row vectors: one thread owns V = 16 / sizeof(elem) adjacent lanes
+//    of a [B, T, D] row (4 fp32 or 8 bf16), loaded and stored with one
+//    dwordx4 access when the row is 16-byte aligned, element by element
+//    otherwise;
+//  * the affine map h -> p*h + q that summarises a run of steps, and its
+//    composition "later after earlier" (associative, not commutative; page
+//    "triton_training_scan.py", the affine prefix kernels that compose the
+//    current map with the accumulated one);
+//  * cross-lane scans of such maps inside one 64-lane wavefront.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lrscan {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1 };
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// storage element conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Two floats -> two bf16 packed in one dword (lo in bits 0..15), RNE.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    __bf16 l = (__bf16)lo;
+    __bf16 h = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    __bf16 v = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, v);
+}
+
+template <int DT>
+struct Elem;
+
+template <>
+struct Elem<DT_F32> {
+    using raw = float;
+    static constexpr int bytes = 4;
+    static constexpr int V = 4;  // lanes per 16-byte vector
+    __device__ static float load1(const void* base, size_t i) {
+        return reinterpret_cast<const float*>(base)[i];
+    }
+    __device__ static void store1(void* base, size_t i, float x) { reinterpret_cast<float*>(base)[i] = x; }
+};
+
+template <>
+struct Elem<DT_BF16> {
+    using raw = uint16_t;
+    static constexpr int bytes = 2;
+    static constexpr int V = 8;
+    __device__ static float load1(const void* base, size_t i) {
+        return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[i]);
+    }
+    __device__ static void store1(void* base, size_t i, float x) {
+        reinterpret_cast<uint16_t*>(base)[i] = f32_to_bf16_bits(x);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// 16-byte row vectors (raw storage kept packed in 4 dwords)
+// ---------------------------------------------------------------------------
+template <int DT>
+struct RowVec {
+    static constexpr int V = Elem<DT>::V;
+    uint4 w;
+
+    __device__ __forceinline__ float get(int j) const {
+        if constexpr (DT == DT_F32) {
+            const uint32_t x = (j == 0) ? w.x : (j == 1) ? w.y : (j == 2) ? w.z : w.w;
+            return __uint_as_float(x);
+        } else {
+            const uint32_t x = (j >> 1 == 0) ? w.x : (j >> 1 == 1) ? w.y : (j >> 1 == 2) ? w.z : w.w;
+            return (j & 1) ? __uint_as_float(x & 0xffff0000u) : __uint_as_float(x << 16);
+        }
+    }
+
+    // identity row: every lane holds `v` (exact in both storage types for 0 and 1)
+    __device__ __forceinline__ static RowVec splat(float v) {
+        RowVec r;
+        uint32_t x;
+        if constexpr (DT == DT_F32) {
+            x = __float_as_uint(v);
+        } else {
+            const uint32_t h = __float_as_uint(v) >> 16;
+            x = h | (h << 16);
+        }
+        r.w = make_uint4(x, x, x, x);
+        return r;
+    }
+};
+
+// Output staging: V floats rounded into the storage type and written as one vector.
+template <int DT>
+struct RowOut {
+    static constexpr int V = Elem<DT>::V;
+    float v[V];
+    __device__ __forceinline__ uint4 pack() const {
+        if constexpr (DT == DT_F32) {
+            return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                              __float_as_uint(v[3]));
+        } else {
+            return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                              pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+        }
+    }
+};
+
+// Load V lanes starting at element offset `off` (lane d0 of a row).
+// ALIGNED: the whole vector is in range and 16-byte aligned.
+// Otherwise `nvalid` (0..V) lanes are loaded one by one and the rest are `fill`.
+template <int DT, bool ALIGNED>
+__device__ __forceinline__ RowVec<DT> load_row(const void* base, size_t off, int nvalid, float fill) {
+    if constexpr (ALIGNED) {
+        RowVec<DT> r;
+        r.w = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + off * Elem<DT>::bytes);
+        return r;
+    } else {
+        RowVec<DT> r = RowVec<DT>::splat(fill);
+        uint32_t ws[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
+        const typename Elem<DT>::raw* p = reinterpret_cast<const typename Elem<DT>::raw*>(base) + off;
+#pragma unroll
+        for (int j = 0; j < RowVec<DT>::V; ++j) {
+            if (j < nvalid) {
+                if constexpr (DT == DT_F32) {
+                    ws[j] = __float_as_uint(p[j]);
+                } else {
+                    const uint32_t h = p[j];
+                    ws[j >> 1] = (j & 1) ? ((ws[j >> 1] & 0x0000ffffu) | (h << 16))
+                                         : ((ws[j >> 1] & 0xffff0000u) | h);
+                }
+            }
+        }
+        r.w = make_uint4(ws[0], ws[1], ws[2], ws[3]);
+        return r;
+    }
+}
+
+template <int DT, bool ALIGNED>
+__device__ __forceinline__ void store_row(void* base, size_t off, int nvalid, const RowOut<DT>& o) {
+    if constexpr (ALIGNED) {
+        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(base) + off * Elem<DT>::bytes) = o.pack();
+    } else {
+#pragma unroll
+        for (int j = 0; j < RowOut<DT>::V; ++j)
+            if (j < nvalid) Elem<DT>::store1(base, off + j, o.v[j]);
+    }
+}
+
+// Row vectors addressed as (wave-uniform row pointer) + (per-lane byte offset),
+// so the compiler can keep the pointer in SGPRs and one 32-bit offset per lane
+// in a VGPR for every row of a tile.
+template <int DT, bool ALIGNED>
+__device__ __forceinline__ RowVec<DT> load_vec(const char* row, uint32_t lane_off, int nvalid,
+                                               float fill) {
+    if constexpr (ALIGNED) {
+        RowVec<DT> r;
+        r.w = *reinterpret_cast<const uint4*>(row + lane_off);
+        return r;
+    } else {
+        return load_row<DT, false>(row + lane_off, 0, nvalid, fill);
+    }
+}
+
+template <int DT, bool ALIGNED>
+__device__ __forceinline__ void store_vec(char* row, uint32_t lane_off, int nvalid,
+                                          const RowOut<DT>& o) {
+    if constexpr (ALIGNED) {
+        *reinterpret_cast<uint4*>(row + lane_off) = o.pack();
+    } else {
+        store_row<DT, false>(row + lane_off, 0, nvalid, o);
+    }
+}
+
+// Make the compiler forget what it knows about a register-resident row, so it
+// re-widens packed bf16 values where they are used again instead of keeping
+// the widened copies alive (which would double the registers a tile needs).
+template <int DT>
+__device__ __forceinline__ void opaque(RowVec<DT>& r) {
+    asm volatile("" : "+v"(r.w.x), "+v"(r.w.y), "+v"(r.w.z), "+v"(r.w.w));
+}
+
+template <typename T>
+__device__ __forceinline__ T uniform(T x) {
+    return __builtin_amdgcn_readfirstlane(x);
+}
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// ---------------------------------------------------------------------------
+// affine maps h -> p*h + q
+// ---------------------------------------------------------------------------
+struct Aff {
+    float p, q;
+};
+
+__device__ __forceinline__ Aff aff_identity() { return Aff{1.0f, 0.0f}; }
+
+// "later after earlier": h -> later.p*(earlier.p*h + earlier.q) + later.q
+__device__ __forceinline__ Aff aff_then(Aff earlier, Aff later) {
+    return Aff{later.p * earlier.p, fmaf(later.p, earlier.q, later.q)};
+}
+
+__device__ __forceinline__ float aff_apply(Aff m, float h) { return fmaf(m.p, h, m.q); }
+
+// ---------------------------------------------------------------------------
+// in-wavefront scans of affine maps
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ float shfl_up_f(float x, int delta) { return __shfl_up(x, delta, kWave); }
+__device__ __forceinline__ float shfl_down_f(float x, int delta) { return __shfl_down(x, delta, kWave); }
+
+// Inclusive scan over the "group" index g = lane / STRIDE (groups of STRIDE
+// adjacent lanes, G = 64 / STRIDE groups), in increasing g: on return lane
+// (g, c) holds  m_g after m_{g-1} after ... after m_0  for its column c.
+// Hillis-Steele: log2(G) steps, each a cross-lane move through the LDS
+// crossbar (ds_bpermute; the offsets are multiples of STRIDE and cross the
+// 16-lane DPP rows) and one compose.  The association order is fixed, so the
+// result is deterministic.
+template <int STRIDE>
+__device__ __forceinline__ Aff wave_scan_up(Aff m) {
+    const int g = lane_id() / STRIDE;
+#pragma unroll
+    for (int s = 1; s < kWave / STRIDE; s <<= 1) {
+        Aff e;
+        e.p = shfl_up_f(m.p, s * STRIDE);
+        e.q = shfl_up_f(m.q, s * STRIDE);
+        if (g >= s) m = aff_then(e, m);
+    }
+    return m;
+}
+
+// Inclusive scan in decreasing g: lane g holds m_g after m_{g+1} after ... after m_{G-1}
+// (used by the reverse-time pass, whose carries flow from later rows to earlier ones).
+template <int STRIDE>
+__device__ __forceinline__ Aff wave_scan_down(Aff m) {
+    constexpr int G = kWave / STRIDE;
+    const int g = lane_id() / STRIDE;
+#pragma unroll
+    for (int s = 1; s < G; s <<= 1) {
+        Aff e;
+        e.p = shfl_down_f(m.p, s * STRIDE);
+        e.q = shfl_down_f(m.q, s * STRIDE);
+        if (g + s < G) m = aff_then(e, m);
+    }
+    return m;
+}
+
+// ---------------------------------------------------------------------------
+// device-coherent single-word publication (look-back flags + values)
+// ---------------------------------------------------------------------------
+// A published float is never the all-ones pattern; scratch words start as it.
+constexpr uint32_t kEmpty = 0xffffffffu;
+
+__device__ __forceinline__ uint32_t publishable(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return u == kEmpty ? 0x7fc00000u : u;  // an input NaN with that payload becomes the canonical NaN
+}
+
+__device__ __forceinline__ void publish_u32(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish_u64(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t peek_u32(const uint32_t* p) {
+    return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long peek_u64(const unsigned long long* p) {
+    return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace lrscan

@@ -1,0 +1,57 @@
+// launch.hpp -- host-side launchers of the scan kernels (internal to liblrscan).
+//
+// Every launcher enqueues on `stream` and returns hipSuccess or the error the
+// runtime reported for the launch.  Arguments have been validated by the
+// C-ABI layer; the launchers only check what the kernels themselves assume.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lrscan {
+
+struct Shape {
+    int64_t B, T, D;
+    int dtype;  // DT_F32 / DT_BF16
+};
+
+// True when every [B,T,D] row starts 16-byte aligned for these base pointers
+// (D * elem_bytes % 16 == 0 and each pointer 16-byte aligned).
+bool rows_aligned(const Shape& s, const void* const* ptrs, int n);
+
+// ---- per-lane sequential walk ---------------------------------------------
+hipError_t launch_seq_fwd(const Shape& s, const void* a, const void* b, void* out, float* last,
+                          const float* h0, hipStream_t st);
+hipError_t launch_seq_bwd(const Shape& s, const void* a, const void* out, const void* g,
+                          const float* grad_last, const float* h0, void* grad_a, void* grad_b,
+                          float* grad_h0, hipStream_t st);
+
+// ---- three-launch chunked form ----------------------------------------------
+hipError_t launch_chunk_summary(const Shape& s, int chunk, const void* a, const void* b, float* P,
+                                float* Q, hipStream_t st);
+hipError_t launch_chunk_prefix(int64_t B, int64_t NC, int64_t D, const float* P, const float* Q,
+                               const float* h0, float* chunk_in, float* last, hipStream_t st);
+hipError_t launch_chunk_replay(const Shape& s, int chunk, const void* a, const void* b,
+                               const float* chunk_in, void* out, float* last, hipStream_t st);
+hipError_t launch_reverse_chunk_summary(const Shape& s, int chunk, const void* a, const void* g,
+                                        float* P, float* Q, hipStream_t st);
+hipError_t launch_reverse_chunk_prefix(int64_t B, int64_t NC, int64_t D, const float* P,
+                                       const float* Q, const float* grad_last, float* future,
+                                       float* grad_h0, hipStream_t st);
+hipError_t launch_reverse_chunk_replay(const Shape& s, int chunk, const void* a, const void* out,
+                                       const void* g, const float* future, const float* h0,
+                                       void* grad_a, void* grad_b, hipStream_t st);
+
+// ---- single-launch fused form ----------------------------------------------
+// Tile lengths (steps per workgroup) with a compiled kernel.
+bool fused_tile_supported(const Shape& s, int dir, int tile);
+int fused_default_tile(const Shape& s, int dir);
+size_t fused_workspace_bytes(const Shape& s, int tile);
+hipError_t launch_fused_fwd(const Shape& s, int tile, const void* a, const void* b, void* out,
+                            float* last, const float* h0, void* ws, hipStream_t st);
+hipError_t launch_fused_bwd(const Shape& s, int tile, const void* a, const void* out,
+                            const void* g, const float* grad_last, const float* h0, void* grad_a,
+                            void* grad_b, float* grad_h0, void* ws, hipStream_t st);
+
+}  // namespace lrscan

@@ -1,0 +1,214 @@
+// seq.hip -- the per-lane sequential scan (forward and backward).
+//
+// One thread owns V adjacent lanes (one 16-byte vector: 4 fp32 or 8 bf16) of
+// one batch row and walks all T steps, keeping the fp32 state (forward) or the
+// fp32 adjoint (backward) in registers, as the page "triton_training_scan.py"
+// does in _real_forward and _real_backward.  On MI355X the walk is bound by
+// memory latency unless B*D/V threads are many times the 256 CUs x 64 lanes:
+// each thread keeps U rows of every input in flight (a register double
+// buffer) to raise the bytes in flight per lane.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace lrscan {
+
+namespace {
+
+constexpr int kSeqBlock = 256;
+constexpr int kSeqU = 8;  // rows in flight per buffer
+
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kSeqBlock) void seq_fwd_kernel(const void* __restrict__ a,
+                                                            const void* __restrict__ b,
+                                                            void* __restrict__ out,
+                                                            float* __restrict__ last,
+                                                            const float* __restrict__ h0,
+                                                            int64_t B, int64_t T, int64_t D,
+                                                            int64_t vpr) {
+    constexpr int V = Elem<DT>::V;
+    constexpr int U = kSeqU;
+    const int64_t gid = (int64_t)blockIdx.x * kSeqBlock + threadIdx.x;
+    const int64_t bi = gid / vpr;
+    if (bi >= B) return;
+    const int64_t d0 = (gid - bi * vpr) * V;
+    const int nvalid = (int)((D - d0) < V ? (D - d0) : V);
+    const size_t base = (size_t)bi * (size_t)T * (size_t)D + (size_t)d0;
+
+    float h[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) h[j] = (h0 && j < nvalid) ? h0[bi * D + d0 + j] : 0.0f;
+
+    RowVec<DT> ca[U], cb[U], na[U], nb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (u < T) {
+            ca[u] = load_row<DT, ALIGNED>(a, base + (size_t)u * D, nvalid, 1.0f);
+            cb[u] = load_row<DT, ALIGNED>(b, base + (size_t)u * D, nvalid, 0.0f);
+        }
+    }
+    for (int64_t t0 = 0; t0 < T; t0 += U) {
+        const int64_t tn = t0 + U;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (tn + u < T) {
+                na[u] = load_row<DT, ALIGNED>(a, base + (size_t)(tn + u) * D, nvalid, 1.0f);
+                nb[u] = load_row<DT, ALIGNED>(b, base + (size_t)(tn + u) * D, nvalid, 0.0f);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (t0 + u < T) {
+                RowOut<DT> o;
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    h[j] = fmaf(ca[u].get(j), h[j], cb[u].get(j));
+                    o.v[j] = h[j];
+                }
+                store_row<DT, ALIGNED>(out, base + (size_t)(t0 + u) * D, nvalid, o);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            ca[u] = na[u];
+            cb[u] = nb[u];
+        }
+    }
+    if (last) {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            if (j < nvalid) last[bi * D + d0 + j] = h[j];
+    }
+}
+
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kSeqBlock) void seq_bwd_kernel(
+    const void* __restrict__ a, const void* __restrict__ out, const void* __restrict__ g,
+    const float* __restrict__ grad_last, const float* __restrict__ h0, void* __restrict__ grad_a,
+    void* __restrict__ grad_b, float* __restrict__ grad_h0, int64_t B, int64_t T, int64_t D,
+    int64_t vpr) {
+    constexpr int V = Elem<DT>::V;
+    constexpr int U = kSeqU;
+    const int64_t gid = (int64_t)blockIdx.x * kSeqBlock + threadIdx.x;
+    const int64_t bi = gid / vpr;
+    if (bi >= B) return;
+    const int64_t d0 = (gid - bi * vpr) * V;
+    const int nvalid = (int)((D - d0) < V ? (D - d0) : V);
+    const size_t base = (size_t)bi * (size_t)T * (size_t)D + (size_t)d0;
+
+    float carry[V], hinit[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        carry[j] = (grad_last && j < nvalid) ? grad_last[bi * D + d0 + j] : 0.0f;
+        hinit[j] = (h0 && j < nvalid) ? h0[bi * D + d0 + j] : 0.0f;
+    }
+
+    // block u of a buffer holds row t0 - u (walking down)
+    RowVec<DT> ca[U], cg[U], ch[U], na[U], ng[U], nh[U];
+    auto load_block = [&](int64_t top, RowVec<DT>* ra, RowVec<DT>* rg, RowVec<DT>* rh) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = top - u;
+            if (t >= 0) {
+                ra[u] = load_row<DT, ALIGNED>(a, base + (size_t)t * D, nvalid, 1.0f);
+                rg[u] = load_row<DT, ALIGNED>(g, base + (size_t)t * D, nvalid, 0.0f);
+                if (t >= 1) rh[u] = load_row<DT, ALIGNED>(out, base + (size_t)(t - 1) * D, nvalid, 0.0f);
+            }
+        }
+    };
+    load_block(T - 1, ca, cg, ch);
+    for (int64_t top = T - 1; top >= 0; top -= U) {
+        if (top - U >= 0) load_block(top - U, na, ng, nh);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = top - u;
+            if (t >= 0) {
+                RowOut<DT> oa, ob;
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    const float lam = cg[u].get(j) + carry[j];
+                    const float hp = (t >= 1) ? ch[u].get(j) : hinit[j];
+                    ob.v[j] = lam;
+                    oa.v[j] = lam * hp;
+                    carry[j] = ca[u].get(j) * lam;
+                }
+                store_row<DT, ALIGNED>(grad_a, base + (size_t)t * D, nvalid, oa);
+                store_row<DT, ALIGNED>(grad_b, base + (size_t)t * D, nvalid, ob);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            ca[u] = na[u];
+            cg[u] = ng[u];
+            ch[u] = nh[u];
+        }
+    }
+    if (grad_h0) {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            if (j < nvalid) grad_h0[bi * D + d0 + j] = carry[j];
+    }
+}
+
+template <int DT>
+int64_t vecs_per_row(int64_t D) {
+    return (D + Elem<DT>::V - 1) / Elem<DT>::V;
+}
+
+template <int DT>
+hipError_t seq_fwd_t(const Shape& s, const void* a, const void* b, void* out, float* last,
+                     const float* h0, hipStream_t st) {
+    const void* ptrs[3] = {a, b, out};
+    const int64_t vpr = vecs_per_row<DT>(s.D);
+    const int64_t threads = s.B * vpr;
+    const dim3 grid((unsigned)((threads + kSeqBlock - 1) / kSeqBlock));
+    if (rows_aligned(s, ptrs, 3))
+        hipLaunchKernelGGL((seq_fwd_kernel<DT, true>), grid, dim3(kSeqBlock), 0, st, a, b, out,
+                           last, h0, s.B, s.T, s.D, vpr);
+    else
+        hipLaunchKernelGGL((seq_fwd_kernel<DT, false>), grid, dim3(kSeqBlock), 0, st, a, b, out,
+                           last, h0, s.B, s.T, s.D, vpr);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t seq_bwd_t(const Shape& s, const void* a, const void* out, const void* g,
+                     const float* grad_last, const float* h0, void* grad_a, void* grad_b,
+                     float* grad_h0, hipStream_t st) {
+    const void* ptrs[5] = {a, out, g, grad_a, grad_b};
+    const int64_t vpr = vecs_per_row<DT>(s.D);
+    const int64_t threads = s.B * vpr;
+    const dim3 grid((unsigned)((threads + kSeqBlock - 1) / kSeqBlock));
+    if (rows_aligned(s, ptrs, 5))
+        hipLaunchKernelGGL((seq_bwd_kernel<DT, true>), grid, dim3(kSeqBlock), 0, st, a, out, g,
+                           grad_last, h0, grad_a, grad_b, grad_h0, s.B, s.T, s.D, vpr);
+    else
+        hipLaunchKernelGGL((seq_bwd_kernel<DT, false>), grid, dim3(kSeqBlock), 0, st, a, out, g,
+                           grad_last, h0, grad_a, grad_b, grad_h0, s.B, s.T, s.D, vpr);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool rows_aligned(const Shape& s, const void* const* ptrs, int n) {
+    const int eb = s.dtype == DT_F32 ? 4 : 2;
+    if ((s.D * eb) % 16 != 0) return false;
+    for (int i = 0; i < n; ++i)
+        if (reinterpret_cast<uintptr_t>(ptrs[i]) % 16 != 0) return false;
+    return true;
+}
+
+hipError_t launch_seq_fwd(const Shape& s, const void* a, const void* b, void* out, float* last,
+                          const float* h0, hipStream_t st) {
+    return s.dtype == DT_F32 ? seq_fwd_t<DT_F32>(s, a, b, out, last, h0, st)
+                             : seq_fwd_t<DT_BF16>(s, a, b, out, last, h0, st);
+}
+
+hipError_t launch_seq_bwd(const Shape& s, const void* a, const void* out, const void* g,
+                          const float* grad_last, const float* h0, void* grad_a, void* grad_b,
+                          float* grad_h0, hipStream_t st) {
+    return s.dtype == DT_F32
+               ? seq_bwd_t<DT_F32>(s, a, out, g, grad_last, h0, grad_a, grad_b, grad_h0, st)
+               : seq_bwd_t<DT_BF16>(s, a, out, g, grad_last, h0, grad_a, grad_b, grad_h0, st);
+}
+
+}  // namespace lrscan

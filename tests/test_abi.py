@@ -1,0 +1,104 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments before touching the GPU (CPU only: no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lrscan.h")
+
+
+def _lib():
+    import linear_recurrence_sequence_diag_amd as lr
+    if not os.path.exists(lr.LIB_PATH):
+        from linear_recurrence_sequence_diag_amd import build
+        build.build()
+    return lr
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return re.findall(r"LRSCAN_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_symbols())
+    for n in ("scan_fwd", "scan_bwd", "scan_fwd_ex", "scan_bwd_ex", "scan_workspace_bytes",
+              "scan_status_string", "scan_chunk_summary", "scan_chunk_prefix", "scan_chunk_replay",
+              "scan_reverse_chunk_summary", "scan_reverse_chunk_prefix",
+              "scan_reverse_chunk_replay"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lr = _lib()
+    lib = ctypes.CDLL(lr.LIB_PATH)
+    for n in declared_symbols():
+        assert hasattr(lib, n), f"{n} declared in lrscan.h but not exported"
+    # nothing else with C linkage leaks out besides the declared entry points
+    out = os.popen(f"nm -D --defined-only {lr.LIB_PATH}").read()
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    c_names = {n for n in exported if not n.startswith("_Z") and not n.startswith("_")}
+    assert c_names <= set(declared_symbols()) | {"_init", "_fini"}, c_names - set(declared_symbols())
+
+
+def test_binding_names_match_the_abi():
+    lr = _lib()
+    for n in declared_symbols():
+        assert callable(getattr(lr, n)), f"binding lacks {n}"
+
+
+def test_status_strings():
+    lr = _lib()
+    for code in range(-7, 1):
+        s = lr.status_string(code)
+        assert isinstance(s, str) and s and s != "unknown status"
+    assert lr.status_string(-99) == "unknown status"
+
+
+def test_argument_errors_return_status_without_work():
+    lr = _lib()
+    lib = lr.library()
+    fake = 0x10000  # never dereferenced: validation fails first
+    assert lib.scan_fwd(None, fake, fake, None, 2, 8, 4, lr.F32, None) == -1
+    assert lib.scan_fwd(fake, fake, fake, None, 0, 8, 4, lr.F32, None) == -2
+    assert lib.scan_fwd(fake, fake, fake, None, 2, -1, 4, lr.F32, None) == -2
+    assert lib.scan_fwd(fake, fake, fake, None, 2, 8, 4, 7, None) == -3
+    assert lib.scan_bwd(fake, fake, None, None, fake, fake, 2, 8, 4, lr.F32, None) == -1
+    assert lib.scan_bwd(fake, fake, fake, None, fake, fake, 1 << 30, 1 << 30, 1 << 30, lr.F32,
+                        None) == -2
+    o = lr.make_opts(algo="chunked", chunk=24)
+    assert lib.scan_fwd_ex(fake, fake, fake, None, 2, 8, 4, lr.F32, None, ctypes.byref(o)) == -4
+    o = lr.make_opts(algo="fused", chunk=100)
+    assert lib.scan_bwd_ex(fake, fake, fake, None, fake, fake, 2, 8, 4, lr.BF16, None,
+                           ctypes.byref(o)) == -4
+    o = lr.make_opts(algo=9)
+    assert lib.scan_fwd_ex(fake, fake, fake, None, 2, 8, 4, lr.F32, None, ctypes.byref(o)) == -7
+    o = lr.make_opts(algo="chunked", chunk=64)
+    o.workspace = fake
+    o.workspace_bytes = 16
+    assert lib.scan_fwd_ex(fake, fake, fake, None, 2, 8, 4, lr.F32, None, ctypes.byref(o)) == -5
+    assert lib.scan_chunk_summary(fake, fake, fake, fake, 2, 8, 4, 17, lr.F32, None) == -4
+    assert lib.scan_chunk_prefix(fake, None, None, fake, None, 2, 3, 4, None) == -1
+    assert lib.scan_reverse_chunk_replay(fake, fake, fake, fake, None, fake, fake, 2, 8, 0, 64,
+                                         lr.F32, None) == -2
+    with pytest.raises(lr.LRScanError):
+        lr.scan_fwd(None, fake, fake, None, 2, 8, 4, lr.F32, None)
+
+
+def test_workspace_sizes_and_auto_choice():
+    lr = _lib()
+    assert lr.scan_workspace_bytes(0, 8, 4, lr.F32) == 0
+    o = lr.make_opts(algo="seq")
+    assert lr.scan_workspace_bytes(2, 8, 4, lr.F32, o) == 0
+    o = lr.make_opts(algo="chunked", chunk=64)
+    n = lr.scan_workspace_bytes(4, 8192, 4096, lr.F32, o)
+    assert n >= 3 * 4 * 128 * 4096 * 4
+    for dt in (lr.F32, lr.BF16):
+        for direction in (0, 1):
+            algo, chunk = lr.scan_auto_algo(8, 2048, 2560, dt, direction)
+            assert algo in (lr.ALGO_SEQ, lr.ALGO_CHUNKED, lr.ALGO_FUSED)
+            o = lr.make_opts(algo=algo, chunk=chunk)
+            assert lr.scan_workspace_bytes(8, 2048, 2560, dt, o) >= 0

@@ -214,3 +214,21 @@ def sample_lanes(wl: Workload, count: int, seed: int = 1):
         k = int(rng.integers(total))
         lanes.add((k // wl.D, k % wl.D))
     return sorted(lanes)
+
+
+def random_inputs(B: int, T: int, D: int, dtype: str, seed: int = 0, a_lo: float = 0.5,
+                  a_hi: float = 1.0, with_state: bool = False):
+    """Ad-hoc inputs for edge shapes: a ~ U(a_lo, a_hi), b, g ~ N(0,1), and
+    (optionally) h0, grad_last ~ N(0,1) as float32 [B, D].  Drawn in float64 in
+    the order a, b, g, h0, grad_last, then stored like the named workloads."""
+    rng = np.random.default_rng(seed)
+    a = rng.uniform(a_lo, a_hi, size=(B, T, D))
+    b = rng.standard_normal((B, T, D))
+    g = rng.standard_normal((B, T, D))
+    wl = Workload(f"random_B{B}_T{T}_D{D}_{dtype}", B, T, D, dtype, "random")
+    inp = Inputs(wl, to_storage(a, dtype), to_storage(b, dtype), to_storage(g, dtype))
+    if with_state:
+        h0 = rng.standard_normal((B, D)).astype(np.float32)
+        gl = rng.standard_normal((B, D)).astype(np.float32)
+        return inp, h0, gl
+    return inp
