@@ -56,7 +56,7 @@ def cpu_baseline(inp, budget_s=10.0):
         oracle.scan_bwd(a, h, g, threads=cores)
         t_total += time.perf_counter() - t0
         reps += 1
-        if t_total >= budget_s or reps >= 5:
+        if t_total >= budget_s or reps >= 200:
             break
     fb, bb = algorithmic_bytes(wl.B, wl.T, wl.D, wl.itemsize)
     return {

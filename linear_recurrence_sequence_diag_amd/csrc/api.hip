@@ -5,6 +5,7 @@
 
 #include <map>
 #include <mutex>
+#include <tuple>
 #include <utility>
 
 #include "../../include/lrscan.h"
@@ -32,21 +33,31 @@ constexpr int kDefaultChunk = 64;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// ---- library-owned workspace, one per (device, stream) ------------------------
+// ---- library-owned workspaces, one per (device, stream, kind) ----------------
+// Kind 0 holds the chunked form's P, Q and entering states; kind 1 holds the
+// fused form's self-cleaning scratch, which must not be shared with anything
+// else and is initialised once per allocation.
 struct CachedWs {
     void* ptr = nullptr;
     size_t bytes = 0;
+    bool fresh = false;  // not yet initialised for the fused form
 };
 std::mutex g_ws_mutex;
-std::map<std::pair<int, void*>, CachedWs> g_ws;
+std::map<std::tuple<int, void*, int>, CachedWs> g_ws;
 
-// Returns a device buffer of at least `bytes` owned by the library, ordered on `st`.
-hipError_t library_workspace(size_t bytes, hipStream_t st, void** out) {
+struct Workspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+    bool init = false;  // the fused form must initialise it before use
+};
+
+// A device buffer of at least `bytes` owned by the library, ordered on `st`.
+hipError_t library_workspace(size_t bytes, int kind, hipStream_t st, Workspace* out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
-    CachedWs& c = g_ws[{dev, (void*)st}];
+    CachedWs& c = g_ws[std::make_tuple(dev, (void*)st, kind)];
     if (c.bytes < bytes) {
         if (c.ptr) {
             e = hipFreeAsync(c.ptr, st);
@@ -58,9 +69,28 @@ hipError_t library_workspace(size_t bytes, hipStream_t st, void** out) {
         e = hipMallocAsync(&c.ptr, want, st);
         if (e != hipSuccess) return e;
         c.bytes = want;
+        c.fresh = true;
     }
-    *out = c.ptr;
+    out->ptr = c.ptr;
+    out->bytes = c.bytes;
+    out->init = c.fresh;
     return hipSuccess;
+}
+
+// Called after a launch that initialised the library's fused workspace was
+// enqueued successfully.
+void workspace_initialised(hipStream_t st) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto it = g_ws.find(std::make_tuple(dev, (void*)st, 1));
+    if (it != g_ws.end()) it->second.fresh = false;
+}
+
+int fused_status(hipError_t e, const Workspace& ws, const lrscan_opts* o, hipStream_t st) {
+    if (e != hipSuccess) return LRSCAN_ERR_HIP;
+    if (ws.init && !(o && o->workspace)) workspace_initialised(st);
+    return LRSCAN_OK;
 }
 
 struct Resolved {
@@ -109,19 +139,24 @@ size_t needed_bytes(const Shape& s, const Resolved& r) {
     return 0;
 }
 
-// Workspace for a call: the caller's (checked) or the library's.
+// Workspace for a call: the caller's (checked; the fused form initialises it
+// on every call, since the library cannot know what the caller did with it
+// in between) or the library's.
 int get_workspace(const Shape& s, const Resolved& r, const lrscan_opts* o, hipStream_t st,
-                  void** ws) {
+                  Workspace* ws) {
     const size_t need = needed_bytes(s, r);
-    *ws = nullptr;
+    *ws = Workspace{};
     if (need == 0) return LRSCAN_OK;
     if (o && o->workspace) {
         if (o->workspace_bytes < need) return LRSCAN_ERR_WORKSPACE;
         if (reinterpret_cast<uintptr_t>(o->workspace) % 256 != 0) return LRSCAN_ERR_WORKSPACE;
-        *ws = o->workspace;
+        ws->ptr = o->workspace;
+        ws->bytes = need;  // initialised on every call: only what this call uses
+        ws->init = true;
         return LRSCAN_OK;
     }
-    return library_workspace(need, st, ws) == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_HIP;
+    const int kind = r.algo == LRSCAN_ALGO_FUSED ? 1 : 0;
+    return library_workspace(need, kind, st, ws) == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_HIP;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_HIP; }
@@ -178,7 +213,7 @@ LRSCAN_API int scan_fwd_ex(const void* a, const void* b, void* out, float* last,
     if (st != LRSCAN_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const float* h0 = opts ? opts->h0 : nullptr;
-    void* ws = nullptr;
+    Workspace ws;
     st = get_workspace(s, r, opts, hs, &ws);
     if (st != LRSCAN_OK) return st;
     switch (r.algo) {
@@ -186,16 +221,18 @@ LRSCAN_API int scan_fwd_ex(const void* a, const void* b, void* out, float* last,
         case LRSCAN_ALGO_CHUNKED: {
             const int64_t NC = (T + r.chunk - 1) / r.chunk;
             const size_t part = align_up((size_t)NC * B * D * 4, 256);
-            float* P = static_cast<float*>(ws);
-            float* Q = reinterpret_cast<float*>(static_cast<char*>(ws) + part);
-            float* cin = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * part);
+            float* P = static_cast<float*>(ws.ptr);
+            float* Q = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + part);
+            float* cin = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + 2 * part);
             hipError_t e = launch_chunk_summary(s, r.chunk, a, b, P, Q, hs);
             if (e == hipSuccess) e = launch_chunk_prefix(B, NC, D, P, Q, h0, cin, nullptr, hs);
             if (e == hipSuccess) e = launch_chunk_replay(s, r.chunk, a, b, cin, out, last, hs);
             return hip_status(e);
         }
         case LRSCAN_ALGO_FUSED:
-            return hip_status(launch_fused_fwd(s, r.chunk, a, b, out, last, h0, ws, hs));
+            return fused_status(launch_fused_fwd(s, r.chunk, a, b, out, last, h0, ws.ptr, ws.bytes,
+                                                 ws.init, hs),
+                                ws, opts, hs);
     }
     return LRSCAN_ERR_ALGO;
 }
@@ -213,7 +250,7 @@ LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const float* h0 = opts ? opts->h0 : nullptr;
     float* grad_h0 = opts ? opts->grad_h0 : nullptr;
-    void* ws = nullptr;
+    Workspace ws;
     st = get_workspace(s, r, opts, hs, &ws);
     if (st != LRSCAN_OK) return st;
     switch (r.algo) {
@@ -223,9 +260,9 @@ LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
         case LRSCAN_ALGO_CHUNKED: {
             const int64_t NC = (T + r.chunk - 1) / r.chunk;
             const size_t part = align_up((size_t)NC * B * D * 4, 256);
-            float* P = static_cast<float*>(ws);
-            float* Q = reinterpret_cast<float*>(static_cast<char*>(ws) + part);
-            float* fut = reinterpret_cast<float*>(static_cast<char*>(ws) + 2 * part);
+            float* P = static_cast<float*>(ws.ptr);
+            float* Q = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + part);
+            float* fut = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + 2 * part);
             hipError_t e = launch_reverse_chunk_summary(s, r.chunk, a, grad_out, P, Q, hs);
             if (e == hipSuccess)
                 e = launch_reverse_chunk_prefix(B, NC, D, P, Q, grad_last, fut, grad_h0, hs);
@@ -235,8 +272,10 @@ LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
             return hip_status(e);
         }
         case LRSCAN_ALGO_FUSED:
-            return hip_status(launch_fused_bwd(s, r.chunk, a, out, grad_out, grad_last, h0, grad_a,
-                                               grad_b, grad_h0, ws, hs));
+            return fused_status(launch_fused_bwd(s, r.chunk, a, out, grad_out, grad_last, h0,
+                                                 grad_a, grad_b, grad_h0, ws.ptr, ws.bytes,
+                                                 ws.init, hs),
+                                ws, opts, hs);
     }
     return LRSCAN_ERR_ALGO;
 }

@@ -34,6 +34,7 @@
 // mirror image: tickets run from the last chunk to the first and carries flow
 // from later rows to earlier ones.
 #include <algorithm>
+#include <cstddef>
 
 #include "device.hpp"
 #include "launch.hpp"
@@ -45,13 +46,59 @@ namespace {
 constexpr int kCG = 8;           // threads per row (8 x 16 B = 128 B)
 constexpr int kRG = kWave / kCG;  // row groups (segments) per wavefront
 constexpr int kLB = 8;           // look-back window
-constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint32_t kSpinLimit = 1u << 20;
+
+// Workspace of the fused form.  A 256-byte header, then two regions of equal
+// size.  A launch publishes into region `phase`, which is all-ones wherever it
+// will write; it clears the words the previous launch dirtied in the other
+// region, and the workgroup that takes the last ticket resets the other
+// region's ticket counter, records how many words this launch dirties and
+// flips the phase.  Every workgroup has read the phase before the last ticket
+// is taken, so back-to-back launches on one stream need no separate
+// initialisation step.
+// The ticket counters live in their own 128-byte line: every workgroup reads
+// the phase word, and sharing its line with the atomically updated counters
+// slowed the launch down several-fold on MI355X.
+struct Header {
+    uint32_t phase;
+    uint32_t reserved;
+    unsigned long long dirty[2];  // words the last user of each region wrote
+    uint32_t pad[26];
+    uint32_t ctr[2];              // ticket counters (all-ones: no ticket taken yet)
+};
+static_assert(offsetof(Header, ctr) == 128, "ticket counters start a new cache line");
 
 struct Scratch {
-    uint32_t* counter;
-    unsigned long long* pq;  // [NK][nS][W] packed (P bits, Q bits)
-    uint32_t* h;             // [NK][nS][W] inclusive state
+    Header* hdr;
+    uint32_t* region[2];
+    unsigned long long entries;  // NK * nS * W published entries (3 words each)
+    uint32_t total_tiles;
 };
+
+constexpr int kHeaderBytes = 256;
+
+struct TileTicket {
+    uint32_t ticket;
+    uint32_t phase;
+    unsigned long long nclear;
+};
+
+__device__ __forceinline__ void header_update(const Scratch& sc, uint32_t p) {
+    publish_u32(&sc.hdr->ctr[p ^ 1u], kEmpty);
+    publish_u64(&sc.hdr->dirty[p], 3ull * sc.entries);
+    publish_u32(&sc.hdr->phase, p ^ 1u);
+}
+
+// Restore the all-ones state of the words the previous launch wrote in the
+// region this launch does not use (spread over all workgroups).
+__device__ __forceinline__ void clear_other_region(const Scratch& sc, const TileTicket& tt,
+                                                   int nthreads) {
+    uint32_t* other = sc.region[tt.phase ^ 1u];
+    const unsigned long long stride = (unsigned long long)sc.total_tiles * nthreads;
+    for (unsigned long long i = (unsigned long long)tt.ticket * nthreads + threadIdx.x; i < tt.nclear;
+         i += stride)
+        other[i] = kEmpty;
+}
 
 __device__ __forceinline__ unsigned long long pack_aff(Aff m) {
     return (unsigned long long)publishable(m.p) | ((unsigned long long)publishable(m.q) << 32);
@@ -65,8 +112,8 @@ __device__ __forceinline__ Aff unpack_aff(unsigned long long w) {
 // chain (h0 forward, grad_last reverse).  Returns the chained value; NaN if
 // the wait ever exceeded the spin limit (then every output of the tile is NaN).
 template <int DIR>
-__device__ float look_back(const Scratch& sc, int64_t k, int64_t NK, int64_t nS, int64_t s, int W,
-                           int c, float base0) {
+__device__ float look_back(const unsigned long long* pqs, const uint32_t* hs, int64_t k, int64_t NK,
+                           int64_t nS, int64_t s, int W, int c, float base0) {
     const int64_t span = DIR < 0 ? k : (NK - 1 - k);  // predecessors in the chain
     if (span == 0) return base0;
     for (uint32_t spin = 0;; ++spin) {
@@ -77,8 +124,8 @@ __device__ float look_back(const Scratch& sc, int64_t k, int64_t NK, int64_t nS,
             const int64_t j = k + DIR * (1 + i);
             if (i < span) {
                 const size_t o = ((size_t)j * nS + s) * W + c;
-                hw[i] = peek_u32(sc.h + o);
-                pq[i] = peek_u64(sc.pq + o);
+                hw[i] = peek_u32(hs + o);
+                pq[i] = peek_u64(pqs + o);
             } else {
                 hw[i] = kEmpty;
                 pq[i] = ~0ull;
@@ -127,7 +174,7 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_fwd_kernel(
     constexpr int SEGS = WAVES * kRG;
     constexpr int64_t CT = (int64_t)SEGS * NR;
 
-    __shared__ uint32_t s_ticket;
+    __shared__ TileTicket s_tt;
     __shared__ Aff s_excl[WAVES][V][kWave];
     __shared__ Aff s_wtot[WAVES][W];
     __shared__ float s_hin[W];
@@ -137,9 +184,19 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_fwd_kernel(
     const int l = tid % kWave;
     const int rg = l / kCG;
     const int cg = l % kCG;
-    if (tid == 0) s_ticket = atomicAdd(sc.counter, 1u) + 1u;
+    if (tid == 0) {
+        const uint32_t p = peek_u32(&sc.hdr->phase);
+        s_tt.phase = p;
+        s_tt.ticket = atomicAdd(&sc.hdr->ctr[p], 1u) + 1u;
+        s_tt.nclear = sc.hdr->dirty[p ^ 1u];
+        if (s_tt.ticket == sc.total_tiles - 1) header_update(sc, p);
+    }
     __syncthreads();
-    const int64_t ticket = uniform(s_ticket);
+    const TileTicket tt = s_tt;
+    const int64_t ticket = uniform(tt.ticket);
+    const uint32_t phase = uniform(tt.phase);
+    const unsigned long long* pqs = reinterpret_cast<const unsigned long long*>(sc.region[phase]);
+    const uint32_t* hs = sc.region[phase] + 2 * sc.entries;
     const int64_t k = ticket / nS;
     const int64_t s = ticket - k * nS;
     const int64_t bi = s / nW;
@@ -170,6 +227,7 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_fwd_kernel(
         ra[i] = ok ? xa : RowVec<DT>::splat(1.0f);
         rb[i] = ok ? xb : RowVec<DT>::splat(0.0f);
     }
+    clear_other_region(sc, tt, WAVES * kWave);
 
     // summary of this thread's segment, per lane, then the wavefront scan
 #pragma unroll
@@ -204,11 +262,11 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_fwd_kernel(
         for (int w = 0; w < WAVES; ++w) A = aff_then(A, s_wtot[w][c]);
         const size_t o = ((size_t)k * nS + s) * W + c;
         const bool more = k + 1 < NK;
-        if (more) publish_u64(sc.pq + o, pack_aff(A));
+        if (more) publish_u64(const_cast<unsigned long long*>(pqs) + o, pack_aff(A));
         const int64_t dl = dcol0 + c;
         const float base0 = (h0 && dl < D) ? h0[bi * D + dl] : 0.0f;
-        const float hin = look_back<-1>(sc, k, NK, nS, s, W, c, base0);
-        if (more) publish_u32(sc.h + o, publishable(aff_apply(A, hin)));
+        const float hin = look_back<-1>(pqs, hs, k, NK, nS, s, W, c, base0);
+        if (more) publish_u32(const_cast<uint32_t*>(hs) + o, publishable(aff_apply(A, hin)));
         s_hin[c] = hin;
     }
     __syncthreads();
@@ -259,7 +317,7 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_bwd_kernel(
     constexpr int SEGS = WAVES * kRG;
     constexpr int64_t CT = (int64_t)SEGS * NR;
 
-    __shared__ uint32_t s_ticket;
+    __shared__ TileTicket s_tt;
     __shared__ Aff s_excl[WAVES][V][kWave];
     __shared__ Aff s_wtot[WAVES][W];
     __shared__ float s_cin[W];
@@ -269,9 +327,19 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_bwd_kernel(
     const int l = tid % kWave;
     const int rg = l / kCG;
     const int cg = l % kCG;
-    if (tid == 0) s_ticket = atomicAdd(sc.counter, 1u) + 1u;
+    if (tid == 0) {
+        const uint32_t p = peek_u32(&sc.hdr->phase);
+        s_tt.phase = p;
+        s_tt.ticket = atomicAdd(&sc.hdr->ctr[p], 1u) + 1u;
+        s_tt.nclear = sc.hdr->dirty[p ^ 1u];
+        if (s_tt.ticket == sc.total_tiles - 1) header_update(sc, p);
+    }
     __syncthreads();
-    const int64_t ticket = uniform(s_ticket);
+    const TileTicket tt = s_tt;
+    const int64_t ticket = uniform(tt.ticket);
+    const uint32_t phase = uniform(tt.phase);
+    const unsigned long long* pqs = reinterpret_cast<const unsigned long long*>(sc.region[phase]);
+    const uint32_t* hs = sc.region[phase] + 2 * sc.entries;
     const int64_t kr = ticket / nS;
     const int64_t s = ticket - kr * nS;
     const int64_t k = NK - 1 - kr;
@@ -308,6 +376,7 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_bwd_kernel(
         rg_[i] = ok ? xg : RowVec<DT>::splat(0.0f);
         rh[i] = (ok && row >= 1) ? xh : RowVec<DT>::splat(0.0f);
     }
+    clear_other_region(sc, tt, WAVES * kWave);
 
     // reverse summary: the map from the carry entering the segment on the
     // right to the carry a_s*lambda_s leaving its first row s
@@ -342,11 +411,11 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_bwd_kernel(
         for (int w = WAVES - 1; w >= 0; --w) A = aff_then(A, s_wtot[w][c]);
         const size_t o = ((size_t)k * nS + s) * W + c;
         const bool more = k > 0;
-        if (more) publish_u64(sc.pq + o, pack_aff(A));
+        if (more) publish_u64(const_cast<unsigned long long*>(pqs) + o, pack_aff(A));
         const int64_t dl = dcol0 + c;
         const float base0 = (grad_last && dl < D) ? grad_last[bi * D + dl] : 0.0f;
-        const float cin = look_back<+1>(sc, k, NK, nS, s, W, c, base0);
-        if (more) publish_u32(sc.h + o, publishable(aff_apply(A, cin)));
+        const float cin = look_back<+1>(pqs, hs, k, NK, nS, s, W, c, base0);
+        if (more) publish_u32(const_cast<uint32_t*>(hs) + o, publishable(aff_apply(A, cin)));
         s_cin[c] = cin;
     }
     __syncthreads();
@@ -387,10 +456,15 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_bwd_kernel(
     }
 }
 
-__global__ void fill_ones_kernel(uint32_t* __restrict__ p, size_t n) {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (size_t)gridDim.x * blockDim.x)
-        p[i] = 0xffffffffu;
+// Workspace initialisation: header (phase 0, both counters unused, nothing
+// dirty) and both regions all-ones.
+__global__ void scratch_init_kernel(uint32_t* __restrict__ p, size_t words) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+         i += (size_t)gridDim.x * blockDim.x) {
+        uint32_t v = kEmpty;
+        if (i < kHeaderBytes / 4) v = (i == 32 || i == 33) ? kEmpty : 0u;  // Header::ctr
+        p[i] = v;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -402,16 +476,13 @@ struct TileCfg {
 constexpr TileCfg kFwdTiles[] = {{256, 8, 4}, {512, 16, 4}, {1024, 16, 8}};
 constexpr TileCfg kBwdTiles[] = {{256, 8, 4}, {512, 8, 8}};
 
-template <int DT>
-constexpr int lanes_per_series() {
-    return kCG * Elem<DT>::V;
+int64_t series_width(int dtype) {
+    return kCG * (dtype == DT_F32 ? Elem<DT_F32>::V : Elem<DT_BF16>::V);
 }
-
-int64_t series_width(int dtype) { return dtype == DT_F32 ? lanes_per_series<DT_F32>() : lanes_per_series<DT_BF16>(); }
 
 struct Layout {
     int64_t nW, nS, NK, W;
-    size_t words_pq, words_h;
+    unsigned long long entries;
 };
 
 Layout layout_of(const Shape& s, int tile) {
@@ -420,33 +491,42 @@ Layout layout_of(const Shape& s, int tile) {
     L.nW = (s.D + L.W - 1) / L.W;
     L.nS = s.B * L.nW;
     L.NK = (s.T + tile - 1) / tile;
-    L.words_pq = (size_t)L.NK * L.nS * L.W;
-    L.words_h = (size_t)L.NK * L.nS * L.W;
+    L.entries = (unsigned long long)L.NK * L.nS * L.W;
     return L;
 }
 
-constexpr size_t kHeader = 256;  // counter, padded
+size_t region_bytes_for(const Layout& L) { return (L.entries * 12 + 255) / 256 * 256; }
 
-Scratch carve(void* ws, const Layout& L) {
-    char* p = static_cast<char*>(ws);
-    Scratch sc;
-    sc.counter = reinterpret_cast<uint32_t*>(p);
-    sc.pq = reinterpret_cast<unsigned long long*>(p + kHeader);
-    sc.h = reinterpret_cast<uint32_t*>(p + kHeader + L.words_pq * 8);
-    return sc;
+// Region size implied by a workspace size (the same for every call on one buffer).
+size_t region_bytes_of(size_t ws_bytes) {
+    return ws_bytes < (size_t)kHeaderBytes ? 0 : (ws_bytes - kHeaderBytes) / 2 / 256 * 256;
 }
 
-hipError_t init_scratch(void* ws, const Layout& L, hipStream_t st) {
-    const size_t words = kHeader / 4 + L.words_pq * 2 + L.words_h;
-    const unsigned blocks = (unsigned)std::min<size_t>((words + 255) / 256, 4096);
-    hipLaunchKernelGGL(fill_ones_kernel, dim3(blocks), dim3(256), 0, st,
-                       static_cast<uint32_t*>(ws), words);
-    return hipGetLastError();
+hipError_t prepare(void* ws, size_t ws_bytes, bool init, const Layout& L, hipStream_t st,
+                   Scratch* sc) {
+    const size_t rb = region_bytes_of(ws_bytes);
+    if (rb < region_bytes_for(L)) return hipErrorInvalidValue;
+    if ((unsigned long long)L.NK * L.nS >= 0xffffffffull) return hipErrorInvalidValue;
+    char* base = static_cast<char*>(ws);
+    if (init) {
+        const size_t words = (kHeaderBytes + 2 * rb) / 4;
+        const unsigned blocks = (unsigned)std::min<size_t>((words + 255) / 256, 8192);
+        hipLaunchKernelGGL(scratch_init_kernel, dim3(blocks), dim3(256), 0, st,
+                           reinterpret_cast<uint32_t*>(base), words);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    sc->hdr = reinterpret_cast<Header*>(base);
+    sc->region[0] = reinterpret_cast<uint32_t*>(base + kHeaderBytes);
+    sc->region[1] = reinterpret_cast<uint32_t*>(base + kHeaderBytes + rb);
+    sc->entries = L.entries;
+    sc->total_tiles = (uint32_t)(L.NK * L.nS);
+    return hipSuccess;
 }
 
 template <int DT, bool AL, int NR, int WAVES>
 void fwd_launch(const Shape& s, const Layout& L, const void* a, const void* b, void* out,
-                float* last, const float* h0, Scratch sc, hipStream_t st) {
+                float* last, const float* h0, const Scratch& sc, hipStream_t st) {
     const dim3 grid((unsigned)(L.NK * L.nS));
     hipLaunchKernelGGL((fused_fwd_kernel<DT, AL, NR, WAVES>), grid, dim3(WAVES * kWave), 0, st, a,
                        b, out, last, h0, sc, s.T, s.D, L.nW, L.nS, L.NK);
@@ -454,8 +534,8 @@ void fwd_launch(const Shape& s, const Layout& L, const void* a, const void* b, v
 
 template <int DT, bool AL, int NR, int WAVES>
 void bwd_launch(const Shape& s, const Layout& L, const void* a, const void* out, const void* g,
-                const float* gl, const float* h0, void* ga, void* gb, float* gh0, Scratch sc,
-                hipStream_t st) {
+                const float* gl, const float* h0, void* ga, void* gb, float* gh0,
+                const Scratch& sc, hipStream_t st) {
     const dim3 grid((unsigned)(L.NK * L.nS));
     hipLaunchKernelGGL((fused_bwd_kernel<DT, AL, NR, WAVES>), grid, dim3(WAVES * kWave), 0, st, a,
                        out, g, gl, h0, ga, gb, gh0, sc, s.T, s.D, L.nW, L.nS, L.NK);
@@ -463,7 +543,7 @@ void bwd_launch(const Shape& s, const Layout& L, const void* a, const void* out,
 
 template <int DT, bool AL>
 bool fwd_dispatch(int tile, const Shape& s, const Layout& L, const void* a, const void* b,
-                  void* out, float* last, const float* h0, Scratch sc, hipStream_t st) {
+                  void* out, float* last, const float* h0, const Scratch& sc, hipStream_t st) {
     switch (tile) {
         case 256: fwd_launch<DT, AL, 8, 4>(s, L, a, b, out, last, h0, sc, st); return true;
         case 512: fwd_launch<DT, AL, 16, 4>(s, L, a, b, out, last, h0, sc, st); return true;
@@ -475,7 +555,7 @@ bool fwd_dispatch(int tile, const Shape& s, const Layout& L, const void* a, cons
 template <int DT, bool AL>
 bool bwd_dispatch(int tile, const Shape& s, const Layout& L, const void* a, const void* out,
                   const void* g, const float* gl, const float* h0, void* ga, void* gb, float* gh0,
-                  Scratch sc, hipStream_t st) {
+                  const Scratch& sc, hipStream_t st) {
     switch (tile) {
         case 256: bwd_launch<DT, AL, 8, 4>(s, L, a, out, g, gl, h0, ga, gb, gh0, sc, st); return true;
         case 512: bwd_launch<DT, AL, 8, 8>(s, L, a, out, g, gl, h0, ga, gb, gh0, sc, st); return true;
@@ -505,16 +585,16 @@ int fused_default_tile(const Shape& s, int dir) {
 }
 
 size_t fused_workspace_bytes(const Shape& s, int tile) {
-    const Layout L = layout_of(s, tile);
-    return kHeader + L.words_pq * 8 + L.words_h * 4;
+    return kHeaderBytes + 2 * region_bytes_for(layout_of(s, tile));
 }
 
 hipError_t launch_fused_fwd(const Shape& s, int tile, const void* a, const void* b, void* out,
-                            float* last, const float* h0, void* ws, hipStream_t st) {
+                            float* last, const float* h0, void* ws, size_t ws_bytes, bool init,
+                            hipStream_t st) {
     const Layout L = layout_of(s, tile);
-    hipError_t e = init_scratch(ws, L, st);
+    Scratch sc;
+    hipError_t e = prepare(ws, ws_bytes, init, L, st, &sc);
     if (e != hipSuccess) return e;
-    const Scratch sc = carve(ws, L);
     const void* ptrs[3] = {a, b, out};
     const bool al = rows_aligned(s, ptrs, 3);
     bool ok;
@@ -530,11 +610,12 @@ hipError_t launch_fused_fwd(const Shape& s, int tile, const void* a, const void*
 
 hipError_t launch_fused_bwd(const Shape& s, int tile, const void* a, const void* out,
                             const void* g, const float* grad_last, const float* h0, void* grad_a,
-                            void* grad_b, float* grad_h0, void* ws, hipStream_t st) {
+                            void* grad_b, float* grad_h0, void* ws, size_t ws_bytes, bool init,
+                            hipStream_t st) {
     const Layout L = layout_of(s, tile);
-    hipError_t e = init_scratch(ws, L, st);
+    Scratch sc;
+    hipError_t e = prepare(ws, ws_bytes, init, L, st, &sc);
     if (e != hipSuccess) return e;
-    const Scratch sc = carve(ws, L);
     const void* ptrs[5] = {a, out, g, grad_a, grad_b};
     const bool al = rows_aligned(s, ptrs, 5);
     bool ok;

@@ -48,10 +48,16 @@ hipError_t launch_reverse_chunk_replay(const Shape& s, int chunk, const void* a,
 bool fused_tile_supported(const Shape& s, int dir, int tile);
 int fused_default_tile(const Shape& s, int dir);
 size_t fused_workspace_bytes(const Shape& s, int tile);
+// `ws` holds the fused form's header and two scratch regions; `init` must be
+// true the first time a buffer is used (and whenever its contents were
+// disturbed): the launcher then enqueues one initialisation kernel first.
+// Every launch on a buffer must use the same `ws_bytes`.
 hipError_t launch_fused_fwd(const Shape& s, int tile, const void* a, const void* b, void* out,
-                            float* last, const float* h0, void* ws, hipStream_t st);
+                            float* last, const float* h0, void* ws, size_t ws_bytes, bool init,
+                            hipStream_t st);
 hipError_t launch_fused_bwd(const Shape& s, int tile, const void* a, const void* out,
                             const void* g, const float* grad_last, const float* h0, void* grad_a,
-                            void* grad_b, float* grad_h0, void* ws, hipStream_t st);
+                            void* grad_b, float* grad_h0, void* ws, size_t ws_bytes, bool init,
+                            hipStream_t st);
 
 }  // namespace lrscan
