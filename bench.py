@@ -79,6 +79,8 @@ def main():
     ap.add_argument("--algo", default="auto")
     ap.add_argument("--fwd-chunk", type=int, default=0)
     ap.add_argument("--bwd-chunk", type=int, default=0)
+    ap.add_argument("--fwd-width", type=int, default=0)
+    ap.add_argument("--bwd-width", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
@@ -114,8 +116,8 @@ def main():
     last = torch.empty((B, D), device="cuda", dtype=torch.float32)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-    fo = lr.make_opts(algo=args.algo, chunk=args.fwd_chunk)
-    bo = lr.make_opts(algo=args.algo, chunk=args.bwd_chunk)
+    fo = lr.make_opts(algo=args.algo, chunk=args.fwd_chunk, width=args.fwd_width)
+    bo = lr.make_opts(algo=args.algo, chunk=args.bwd_chunk, width=args.bwd_width)
 
     def step(ev=None):
         if ev:
@@ -149,12 +151,20 @@ def main():
 
     fb, bb = algorithmic_bytes(B, T, D, wl.itemsize)
     value = (fb + bb) / (ms_per_step * 1e-3) / 1e9
-    fwd_algo, fwd_chunk = lr.scan_auto_algo(B, T, D, dt, 0)
-    bwd_algo, bwd_chunk = lr.scan_auto_algo(B, T, D, dt, 1)
+    fwd_algo, fwd_chunk, fwd_width = lr.scan_auto_algo(B, T, D, dt, 0)
+    bwd_algo, bwd_chunk, bwd_width = lr.scan_auto_algo(B, T, D, dt, 1)
     if args.algo != "auto":
         fwd_algo = bwd_algo = lr.ALGOS[args.algo]
         fwd_chunk, bwd_chunk = args.fwd_chunk, args.bwd_chunk
+        fwd_width, bwd_width = args.fwd_width, args.bwd_width
     names = {v: k for k, v in lr.ALGOS.items()}
+
+    def algo_name(algo, chunk, width):
+        if names[algo] == "fused":
+            return f"fused(width {width * 16} B, tile {chunk} rows)"
+        if names[algo] == "chunked":
+            return f"chunked(chunk {chunk})"
+        return names[algo]
     if bwd_ms >= fwd_ms:
         dom, dom_ms, dom_bytes = "backward", bwd_ms, bb
     else:
@@ -177,8 +187,8 @@ def main():
         "config": {
             "workload": f"{wl.name}: {WORKLOAD_TEXT[wl.name]}",
             "B": B, "T": T, "D": D,
-            "fwd_algo": f"{names[fwd_algo]}{fwd_chunk or ''}",
-            "bwd_algo": f"{names[bwd_algo]}{bwd_chunk or ''}",
+            "fwd_algo": algo_name(fwd_algo, fwd_chunk, fwd_width),
+            "bwd_algo": algo_name(bwd_algo, bwd_chunk, bwd_width),
         },
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "elements_per_s": round(wl.N / (ms_per_step * 1e-3), 1),

@@ -72,9 +72,14 @@ enum {
 typedef struct {
     int algo;               /* LRSCAN_ALGO_* */
     int chunk;              /* 0: the algorithm's default.  CHUNKED: a power of two in [16, 1024].
-                               FUSED: tile length in steps: 256, 512 or 1024 forward,
-                               256 or 512 backward (tile * D * elem_bytes < 2^31).
-                               SEQ: ignored. */
+                               FUSED: rows per tile (see `width`).  SEQ: ignored. */
+    int width;              /* FUSED only: threads of 16 bytes per tile row (8, 16 or 32; a
+                               tile row is 128, 256 or 512 contiguous bytes); 0: default.
+                               Supported (width, chunk): forward (8,256) (8,512) (16,128)
+                               (16,256) (32,64) (32,128); backward (8,256) (8,128) (16,128)
+                               (32,64) (32,32).  Rows that are not 16-byte aligned
+                               (D * elem_bytes % 16 != 0 or an unaligned pointer) support
+                               only (8,256). */
     void* workspace;        /* device scratch, or NULL for the library's own per-stream cache */
     size_t workspace_bytes; /* size of `workspace` */
     const float* h0;        /* [B, D] initial state, or NULL for zero (forward and backward) */
@@ -115,9 +120,11 @@ LRSCAN_API size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t D, int dtyp
 /* A static string naming a status code. */
 LRSCAN_API const char* scan_status_string(int status);
 
-/* The algorithm LRSCAN_ALGO_AUTO picks for this shape (forward if dir == 0, else backward),
- * and through *chunk its chunk / tile length.  Returns a negative status on bad arguments. */
-LRSCAN_API int scan_auto_algo(int64_t B, int64_t T, int64_t D, int dtype, int dir, int* chunk);
+/* The algorithm LRSCAN_ALGO_AUTO picks for this shape with 16-byte aligned pointers (forward
+ * if dir == 0, else backward), and through *chunk and *width (both nullable) its chunk or tile
+ * length and tile width.  Returns the algorithm, or a negative status on bad arguments. */
+LRSCAN_API int scan_auto_algo(int64_t B, int64_t T, int64_t D, int dtype, int dir, int* chunk,
+                              int* width);
 
 /* ------------------------------------------------------------------------
  * The steps of the chunked form, one entry point each (page

@@ -40,6 +40,7 @@ class Opts(ctypes.Structure):
     _fields_ = [
         ("algo", ctypes.c_int),
         ("chunk", ctypes.c_int),
+        ("width", ctypes.c_int),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("h0", ctypes.c_void_p),
@@ -57,7 +58,8 @@ _SIGS = {
     "scan_bwd_ex": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
     "scan_workspace_bytes": ([_I64, _I64, _I64, _INT, ctypes.POINTER(Opts)], ctypes.c_size_t),
     "scan_status_string": ([_INT], ctypes.c_char_p),
-    "scan_auto_algo": ([_I64, _I64, _I64, _INT, _INT, ctypes.POINTER(_INT)], _INT),
+    "scan_auto_algo": ([_I64, _I64, _I64, _INT, _INT, ctypes.POINTER(_INT), ctypes.POINTER(_INT)],
+                       _INT),
     "scan_chunk_summary": ([_P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P], _INT),
     "scan_chunk_prefix": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
     "scan_chunk_replay": ([_P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P], _INT),
@@ -131,11 +133,14 @@ def scan_workspace_bytes(B, T, D, dtype, opts=None):
 
 
 def scan_auto_algo(B, T, D, dtype, direction):
+    """(algo, chunk, width) the library picks for this shape."""
     chunk = ctypes.c_int(0)
-    algo = library().scan_auto_algo(B, T, D, dtype, direction, ctypes.byref(chunk))
+    width = ctypes.c_int(0)
+    algo = library().scan_auto_algo(B, T, D, dtype, direction, ctypes.byref(chunk),
+                                    ctypes.byref(width))
     if algo < 0:
         raise LRScanError(algo, "scan_auto_algo")
-    return algo, chunk.value
+    return algo, chunk.value, width.value
 
 
 def scan_chunk_summary(a, b, P, Q, B, T, D, chunk, dtype, stream):
@@ -216,10 +221,11 @@ def _check_state(name, t, ref):
         raise ValueError(f"{name} must be a contiguous float32 [B, D] tensor on a's device")
 
 
-def make_opts(algo="auto", chunk=0, h0=None, grad_h0=None, workspace=None):
+def make_opts(algo="auto", chunk=0, h0=None, grad_h0=None, workspace=None, width=0):
     o = Opts()
     o.algo = ALGOS[algo] if isinstance(algo, str) else int(algo)
     o.chunk = int(chunk)
+    o.width = int(width)
     o.workspace = None if workspace is None else workspace.data_ptr()
     o.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     o.h0 = _ptr(h0)
@@ -227,7 +233,7 @@ def make_opts(algo="auto", chunk=0, h0=None, grad_h0=None, workspace=None):
     return o
 
 
-def scan(a, b, h0=None, algo="auto", chunk=0, with_last=True):
+def scan(a, b, h0=None, algo="auto", chunk=0, with_last=True, width=0):
     """Forward scan.  Returns (out, last); out has a's dtype, last is float32 [B, D]."""
     torch = _torch()
     _check_seq("a", a)
@@ -238,12 +244,12 @@ def scan(a, b, h0=None, algo="auto", chunk=0, with_last=True):
     last = torch.empty((B, D), device=a.device, dtype=torch.float32) if with_last else None
     with torch.cuda.device(a.device):
         scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), _ptr(last), B, T, D,
-                    dtype_code(a.dtype), _stream(a), make_opts(algo, chunk, h0=h0))
+                    dtype_code(a.dtype), _stream(a), make_opts(algo, chunk, h0=h0, width=width))
     return out, last
 
 
 def scan_backward(a, out, grad_out, grad_last=None, h0=None, algo="auto", chunk=0,
-                  need_grad_h0=False):
+                  need_grad_h0=False, width=0):
     """Reverse-time adjoint.  Returns (grad_a, grad_b, grad_h0 or None)."""
     torch = _torch()
     _check_seq("a", a)
@@ -258,7 +264,7 @@ def scan_backward(a, out, grad_out, grad_last=None, h0=None, algo="auto", chunk=
     with torch.cuda.device(a.device):
         scan_bwd_ex(a.data_ptr(), out.data_ptr(), grad_out.data_ptr(), _ptr(grad_last),
                     grad_a.data_ptr(), grad_b.data_ptr(), B, T, D, dtype_code(a.dtype), _stream(a),
-                    make_opts(algo, chunk, h0=h0, grad_h0=grad_h0))
+                    make_opts(algo, chunk, h0=h0, grad_h0=grad_h0, width=width))
     return grad_a, grad_b, grad_h0
 
 

@@ -96,32 +96,44 @@ int fused_status(hipError_t e, const Workspace& ws, const lrscan_opts* o, hipStr
 struct Resolved {
     int algo;
     int chunk;
+    int width;
 };
 
-// The measured crossover (see the dispatch notes in the design document of
-// this package): the single-launch fused form reads every input once and wins
-// on every measured shape; the per-lane walk is kept for explicit requests.
-Resolved resolve(const Shape& s, int dir, const lrscan_opts* o) {
+// Whether rows of this shape can be 16-byte aligned at all (pointers are
+// checked separately at launch time).
+bool shape_aligned(const Shape& s) { return (s.D * (s.dtype == LRSCAN_F32 ? 4 : 2)) % 16 == 0; }
+
+// The automatic choice: the single-launch fused form reads every input once
+// and was the fastest form on every measured shape; its tile shape comes from
+// fused_default_cfg.  The per-lane walk and the three-launch form are kept
+// for explicit requests.
+Resolved resolve(const Shape& s, int dir, const lrscan_opts* o, bool aligned) {
     Resolved r;
     r.algo = o ? o->algo : LRSCAN_ALGO_AUTO;
     r.chunk = o ? o->chunk : 0;
+    r.width = o ? o->width : 0;
     if (r.algo == LRSCAN_ALGO_AUTO) {
         r.algo = LRSCAN_ALGO_FUSED;
         r.chunk = 0;
+        r.width = 0;
     }
-    if (r.chunk == 0) {
-        if (r.algo == LRSCAN_ALGO_CHUNKED) r.chunk = kDefaultChunk;
-        if (r.algo == LRSCAN_ALGO_FUSED) r.chunk = fused_default_tile(s, dir);
+    if (r.algo == LRSCAN_ALGO_CHUNKED && r.chunk == 0) r.chunk = kDefaultChunk;
+    if (r.algo == LRSCAN_ALGO_FUSED && (r.chunk == 0 || r.width == 0)) {
+        int w = 0, t = 0;
+        fused_default_cfg(s, dir, aligned, &w, &t);
+        if (r.width == 0) r.width = w;
+        if (r.chunk == 0) r.chunk = t;
     }
     return r;
 }
 
-int validate_algo(const Shape& s, int dir, const Resolved& r) {
+int validate_algo(const Shape& s, int dir, const Resolved& r, bool aligned) {
     switch (r.algo) {
         case LRSCAN_ALGO_SEQ: return LRSCAN_OK;
         case LRSCAN_ALGO_CHUNKED: return chunk_ok(r.chunk) ? LRSCAN_OK : LRSCAN_ERR_CHUNK;
         case LRSCAN_ALGO_FUSED:
-            return fused_tile_supported(s, dir, r.chunk) ? LRSCAN_OK : LRSCAN_ERR_CHUNK;
+            return fused_cfg_supported(s, dir, r.width, r.chunk, aligned) ? LRSCAN_OK
+                                                                            : LRSCAN_ERR_CHUNK;
     }
     return LRSCAN_ERR_ALGO;
 }
@@ -134,7 +146,7 @@ size_t chunked_bytes(const Shape& s, int chunk) {
 size_t needed_bytes(const Shape& s, const Resolved& r) {
     switch (r.algo) {
         case LRSCAN_ALGO_CHUNKED: return chunked_bytes(s, r.chunk);
-        case LRSCAN_ALGO_FUSED: return fused_workspace_bytes(s, r.chunk);
+        case LRSCAN_ALGO_FUSED: return fused_workspace_bytes(s, r.width, r.chunk);
     }
     return 0;
 }
@@ -179,26 +191,32 @@ LRSCAN_API const char* scan_status_string(int status) {
     return "unknown status";
 }
 
-LRSCAN_API int scan_auto_algo(int64_t B, int64_t T, int64_t D, int dtype, int dir, int* chunk) {
+LRSCAN_API int scan_auto_algo(int64_t B, int64_t T, int64_t D, int dtype, int dir, int* chunk,
+                              int* width) {
     if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
     const Shape s{B, T, D, dtype};
-    const Resolved r = resolve(s, dir, nullptr);
+    const Resolved r = resolve(s, dir, nullptr, shape_aligned(s));
     if (chunk) *chunk = r.chunk;
+    if (width) *width = r.width;
     return r.algo;
 }
 
+// The largest need over both directions and both pointer alignments (a call
+// with unaligned pointers falls back to the narrowest fused tile).
 LRSCAN_API size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t D, int dtype,
                                        const lrscan_opts* opts) {
     if (!dims_ok(B, T, D) || !dtype_ok(dtype)) return 0;
     const Shape s{B, T, D, dtype};
     size_t need = 0;
-    for (int dir = 0; dir < 2; ++dir) {
-        const Resolved r = resolve(s, dir, opts);
-        if (validate_algo(s, dir, r) != LRSCAN_OK) continue;
-        const size_t n = needed_bytes(s, r);
-        if (n > need) need = n;
-    }
+    for (int dir = 0; dir < 2; ++dir)
+        for (int al = 0; al < 2; ++al) {
+            if (al && !shape_aligned(s)) continue;
+            const Resolved r = resolve(s, dir, opts, al != 0);
+            if (validate_algo(s, dir, r, al != 0) != LRSCAN_OK) continue;
+            const size_t n = needed_bytes(s, r);
+            if (n > need) need = n;
+        }
     return need;
 }
 
@@ -208,8 +226,10 @@ LRSCAN_API int scan_fwd_ex(const void* a, const void* b, void* out, float* last,
     if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
     const Shape s{B, T, D, dtype};
-    const Resolved r = resolve(s, 0, opts);
-    int st = validate_algo(s, 0, r);
+    const void* ptrs[3] = {a, b, out};
+    const bool aligned = rows_aligned(s, ptrs, 3);
+    const Resolved r = resolve(s, 0, opts, aligned);
+    int st = validate_algo(s, 0, r, aligned);
     if (st != LRSCAN_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const float* h0 = opts ? opts->h0 : nullptr;
@@ -230,8 +250,8 @@ LRSCAN_API int scan_fwd_ex(const void* a, const void* b, void* out, float* last,
             return hip_status(e);
         }
         case LRSCAN_ALGO_FUSED:
-            return fused_status(launch_fused_fwd(s, r.chunk, a, b, out, last, h0, ws.ptr, ws.bytes,
-                                                 ws.init, hs),
+            return fused_status(launch_fused_fwd(s, r.width, r.chunk, a, b, out, last, h0,
+                                                 ws.ptr, ws.bytes, ws.init, hs),
                                 ws, opts, hs);
     }
     return LRSCAN_ERR_ALGO;
@@ -244,8 +264,10 @@ LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
     if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
     const Shape s{B, T, D, dtype};
-    const Resolved r = resolve(s, 1, opts);
-    int st = validate_algo(s, 1, r);
+    const void* ptrs[5] = {a, out, grad_out, grad_a, grad_b};
+    const bool aligned = rows_aligned(s, ptrs, 5);
+    const Resolved r = resolve(s, 1, opts, aligned);
+    int st = validate_algo(s, 1, r, aligned);
     if (st != LRSCAN_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const float* h0 = opts ? opts->h0 : nullptr;
@@ -272,8 +294,8 @@ LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
             return hip_status(e);
         }
         case LRSCAN_ALGO_FUSED:
-            return fused_status(launch_fused_bwd(s, r.chunk, a, out, grad_out, grad_last, h0,
-                                                 grad_a, grad_b, grad_h0, ws.ptr, ws.bytes,
+            return fused_status(launch_fused_bwd(s, r.width, r.chunk, a, out, grad_out, grad_last,
+                                                 h0, grad_a, grad_b, grad_h0, ws.ptr, ws.bytes,
                                                  ws.init, hs),
                                 ws, opts, hs);
     }

@@ -43,61 +43,57 @@ namespace lrscan {
 
 namespace {
 
-constexpr int kCG = 8;           // threads per row (8 x 16 B = 128 B)
-constexpr int kRG = kWave / kCG;  // row groups (segments) per wavefront
-constexpr int kLB = 8;           // look-back window
 constexpr uint32_t kSpinLimit = 1u << 20;
 
-// Workspace of the fused form.  A 256-byte header, then two regions of equal
-// size.  A launch publishes into region `phase`, which is all-ones wherever it
-// will write; it clears the words the previous launch dirtied in the other
-// region, and the workgroup that takes the last ticket resets the other
-// region's ticket counter, records how many words this launch dirties and
-// flips the phase.  Every workgroup has read the phase before the last ticket
-// is taken, so back-to-back launches on one stream need no separate
-// initialisation step.
-// The ticket counters live in their own 128-byte line: every workgroup reads
-// the phase word, and sharing its line with the atomically updated counters
-// slowed the launch down several-fold on MI355X.
+// Workspace of the fused form: a 256-byte header, then two regions of equal
+// size.  A region holds nC ticket counters (each in its own 128-byte line),
+// then the published (P, Q) words, then the published inclusive states H.  A
+// launch uses region `phase`, which is all-ones wherever it will write; it
+// clears the words the previous launch dirtied in the other region, counters
+// included.  The workgroup that takes the last ticket of the last counter to
+// run out records how many words this launch dirties, resets the other
+// phase's count of exhausted counters and flips the phase.  By then every
+// workgroup has read the phase, so back-to-back launches on one stream (or
+// replays of a captured graph) need no separate initialisation step.
+//
+// Tickets.  Same-address atomics serialise (about 11.5 ns each on MI355X: one
+// counter for 2560 workgroups costs 30 us), so tickets come from nC counters,
+// nC a divisor of the number of series nS.  Counter c hands out local indices
+// i = 0, 1, ... in arrival order, and the tile is t = i*nC + c, taken in the
+// chain-major order k = t / nS, s = t % nS.  Because nC divides nS, every
+// predecessor t - j*nS of a tile comes from the same counter with a smaller
+// index, so it was taken by a workgroup that is already running: the chain
+// always drains.  Workgroups are spread over counters so that each counter is
+// fed from all XCDs and the counters advance together, which keeps the rows
+// in flight close to each other (this matters for DRAM locality).
 struct Header {
     uint32_t phase;
     uint32_t reserved;
     unsigned long long dirty[2];  // words the last user of each region wrote
     uint32_t pad[26];
-    uint32_t ctr[2];              // ticket counters (all-ones: no ticket taken yet)
+    uint32_t done[2];             // per phase: counters run out (all-ones: none)
 };
-static_assert(offsetof(Header, ctr) == 128, "ticket counters start a new cache line");
+static_assert(offsetof(Header, done) == 128, "the counter tally starts a new cache line");
+
+constexpr int kCtrStride = 32;  // words between ticket counters (one 128-byte line each)
+constexpr int kMaxCounters = 64;
 
 struct Scratch {
     Header* hdr;
     uint32_t* region[2];
-    unsigned long long entries;  // NK * nS * W published entries (3 words each)
+    unsigned long long entries;    // NK * nS * W published entries (3 words each)
+    unsigned long long ctr_words;  // nC * kCtrStride
     uint32_t total_tiles;
+    uint32_t nC;                   // ticket counters (divides nS)
+    uint32_t quota;                // tickets per counter = total_tiles / nC
 };
 
 constexpr int kHeaderBytes = 256;
 
-struct TileTicket {
-    uint32_t ticket;
-    uint32_t phase;
-    unsigned long long nclear;
-};
-
 __device__ __forceinline__ void header_update(const Scratch& sc, uint32_t p) {
-    publish_u32(&sc.hdr->ctr[p ^ 1u], kEmpty);
-    publish_u64(&sc.hdr->dirty[p], 3ull * sc.entries);
+    publish_u32(&sc.hdr->done[p ^ 1u], kEmpty);
+    publish_u64(&sc.hdr->dirty[p], sc.ctr_words + 3ull * sc.entries);
     publish_u32(&sc.hdr->phase, p ^ 1u);
-}
-
-// Restore the all-ones state of the words the previous launch wrote in the
-// region this launch does not use (spread over all workgroups).
-__device__ __forceinline__ void clear_other_region(const Scratch& sc, const TileTicket& tt,
-                                                   int nthreads) {
-    uint32_t* other = sc.region[tt.phase ^ 1u];
-    const unsigned long long stride = (unsigned long long)sc.total_tiles * nthreads;
-    for (unsigned long long i = (unsigned long long)tt.ticket * nthreads + threadIdx.x; i < tt.nclear;
-         i += stride)
-        other[i] = kEmpty;
 }
 
 __device__ __forceinline__ unsigned long long pack_aff(Aff m) {
@@ -107,25 +103,126 @@ __device__ __forceinline__ Aff unpack_aff(unsigned long long w) {
     return Aff{__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32))};
 }
 
+// ---------------------------------------------------------------------------
+// tile configuration
+//
+// TPR threads (16-byte vectors) cover one row of a tile: W = TPR*V lanes,
+// TPR*16 contiguous bytes per row.  A wavefront holds RG = 64/TPR row groups,
+// each thread NR consecutive rows; a workgroup of WAVES wavefronts covers
+// CT = WAVES*RG*NR rows.  LB is the look-back window.
+// ---------------------------------------------------------------------------
+template <int DT_, int TPR_, int NR_, int WAVES_, int LB_>
+struct Cfg {
+    static constexpr int DT = DT_, TPR = TPR_, NR = NR_, WAVES = WAVES_, LB = LB_;
+    static constexpr int V = Elem<DT>::V;
+    static constexpr int EB = Elem<DT>::bytes;
+    static constexpr int RG = kWave / TPR;
+    static constexpr int W = TPR * V;
+    static constexpr int NT = WAVES * kWave;
+    static constexpr int CT = WAVES * RG * NR;
+    static_assert(TPR == 8 || TPR == 16 || TPR == 32, "row width");
+    static_assert(W <= NT, "one look-back column per thread");
+};
+
+struct Dims {
+    int T, D, nW, nS, NK;
+};
+
+// One thread's view of its tile.
+struct Geo {
+    int k, s, bi, dcol0, d0, trow0, row0;
+    int nvalid;     // lanes of this thread's vector that exist (0..V)
+    int nrows;      // rows of this thread's segment that exist (0..NR)
+    size_t tbase;   // byte offset of (batch bi, row trow0, lane dcol0)
+    uint32_t coff;  // this thread's byte offset inside a row
+};
+
+template <class C, bool REV>
+__device__ __forceinline__ Geo tile_geo(uint32_t ticket, const Dims& d, int wave, int rg, int cg) {
+    Geo g;
+    const int kk = (int)(ticket / (uint32_t)d.nS);
+    g.s = (int)ticket - kk * d.nS;
+    g.k = REV ? d.NK - 1 - kk : kk;
+    g.bi = g.s / d.nW;
+    g.dcol0 = (g.s - g.bi * d.nW) * C::W;
+    g.d0 = g.dcol0 + cg * C::V;
+    g.nvalid = g.d0 >= d.D ? 0 : ((d.D - g.d0) < C::V ? (d.D - g.d0) : C::V);
+    g.trow0 = g.k * C::CT;
+    g.row0 = g.trow0 + (wave * C::RG + rg) * C::NR;
+    const int left = d.T - g.row0;
+    g.nrows = g.nvalid == 0 ? 0 : (left <= 0 ? 0 : (left < C::NR ? left : C::NR));
+    g.tbase = (((size_t)g.bi * d.T + g.trow0) * d.D + g.dcol0) * C::EB;
+    // lanes past D read a valid column (their values are never used)
+    g.coff = (uint32_t)((g.nvalid > 0 ? cg * C::V : 0) * C::EB);
+    return g;
+}
+
+// Byte offset, from the tile base, of row `row` of this thread's column,
+// clamped to a row that exists (rows past T are read but never used).
+__device__ __forceinline__ uint32_t row_off(const Geo& g, int row, int T, uint32_t rowbytes) {
+    const int rc = row < T ? row : T - 1;
+    return (uint32_t)(rc - g.trow0) * rowbytes + g.coff;
+}
+
+// Ticket, phase and the number of words to clear, read once per workgroup.
+struct Ticket {
+    uint32_t ticket, phase;
+    unsigned long long nclear;
+};
+
+__device__ __forceinline__ Ticket take_ticket(const Scratch& sc) {
+    __shared__ Ticket s_t;
+    if (threadIdx.x == 0) {
+        const uint32_t p = peek_u32(&sc.hdr->phase);
+        const uint32_t b = blockIdx.x;
+        const uint32_t c = (b % sc.nC + b / sc.nC) % sc.nC;  // a permutation within each row of nC
+        const uint32_t i = atomicAdd(sc.region[p] + (size_t)c * kCtrStride, 1u) + 1u;
+        s_t.phase = p;
+        s_t.ticket = i * sc.nC + c;
+        s_t.nclear = sc.hdr->dirty[p ^ 1u];
+        if (i == sc.quota - 1 && atomicAdd(&sc.hdr->done[p], 1u) + 1u == sc.nC - 1)
+            header_update(sc, p);
+    }
+    __syncthreads();
+    Ticket t;
+    t.ticket = uniform(s_t.ticket);
+    t.phase = uniform(s_t.phase);
+    t.nclear = (unsigned long long)uniform64((int64_t)s_t.nclear);
+    return t;
+}
+
+// Restore the all-ones state of this ticket's share of the words the
+// previous launch wrote in the region this launch does not use.
+__device__ __forceinline__ void clear_share(const Scratch& sc, const Ticket& t, int nthreads) {
+    uint32_t* other = sc.region[t.phase ^ 1u];
+    const unsigned long long stride = (unsigned long long)sc.total_tiles * nthreads;
+    for (unsigned long long i = (unsigned long long)t.ticket * nthreads + threadIdx.x; i < t.nclear;
+         i += stride)
+        other[i] = kEmpty;
+}
+
 // Carry entering tile k of a chain (forward: DIR = -1 looks at k-1, k-2, ...;
 // reverse: DIR = +1 looks at k+1, k+2, ...).  `base0` is the carry entering the
-// chain (h0 forward, grad_last reverse).  Returns the chained value; NaN if
-// the wait ever exceeded the spin limit (then every output of the tile is NaN).
-template <int DIR>
-__device__ float look_back(const unsigned long long* pqs, const uint32_t* hs, int64_t k, int64_t NK,
-                           int64_t nS, int64_t s, int W, int c, float base0) {
-    const int64_t span = DIR < 0 ? k : (NK - 1 - k);  // predecessors in the chain
+// chain (h0 forward, grad_last reverse).  The nearest published inclusive
+// state within the window is taken and the maps of the tiles in between are
+// applied to it oldest first, so the result is the plain chained value.
+// Returns NaN if a wait ever exceeded the spin limit.
+template <int DIR, int LB>
+__device__ float look_back(const unsigned long long* pqs, const uint32_t* hs, int k, int NK, int nS,
+                           int s, int W, int c, float base0) {
+    const int span = DIR < 0 ? k : (NK - 1 - k);  // predecessors in the chain
     if (span == 0) return base0;
     for (uint32_t spin = 0;; ++spin) {
-        uint32_t hw[kLB];
-        unsigned long long pq[kLB];
+        uint32_t hw[LB];
+        unsigned long long pq[LB];
 #pragma unroll
-        for (int i = 0; i < kLB; ++i) {
-            const int64_t j = k + DIR * (1 + i);
+        for (int i = 0; i < LB; ++i) {
+            const int j = k + DIR * (1 + i);
             if (i < span) {
-                const size_t o = ((size_t)j * nS + s) * W + c;
-                hw[i] = peek_u32(hs + o);
-                pq[i] = peek_u64(pqs + o);
+                // wave-uniform entry base + per-lane column
+                const size_t e = ((size_t)j * (size_t)nS + (size_t)s) * W;
+                hw[i] = peek_u32(hs + e + c);
+                pq[i] = peek_u64(pqs + e + c);
             } else {
                 hw[i] = kEmpty;
                 pq[i] = ~0ull;
@@ -135,7 +232,7 @@ __device__ float look_back(const unsigned long long* pqs, const uint32_t* hs, in
         bool stop = false;
         float base = base0;
 #pragma unroll
-        for (int i = 0; i < kLB; ++i) {
+        for (int i = 0; i < LB; ++i) {
             if (depth < 0 && !stop) {
                 if (i >= span) {
                     depth = i;  // reached the start of the chain
@@ -147,11 +244,11 @@ __device__ float look_back(const unsigned long long* pqs, const uint32_t* hs, in
                 }
             }
         }
-        if (depth < 0 && !stop && span == kLB) depth = kLB;  // chain start just past the window
+        if (depth < 0 && !stop && span == LB) depth = LB;  // chain start just past the window
         if (depth >= 0) {
             float x = base;
 #pragma unroll
-            for (int i = kLB - 1; i >= 0; --i)
+            for (int i = LB - 1; i >= 0; --i)
                 if (i < depth) x = aff_apply(unpack_aff(pq[i]), x);
             return x;
         }
@@ -160,92 +257,89 @@ __device__ float look_back(const unsigned long long* pqs, const uint32_t* hs, in
     }
 }
 
+struct FwdArgs {
+    const void* a;
+    const void* b;
+    void* out;
+    float* last;
+    const float* h0;
+    Scratch sc;
+    Dims d;
+};
+
+struct BwdArgs {
+    const void* a;
+    const void* out;
+    const void* g;
+    const float* grad_last;
+    const float* h0;
+    void* grad_a;
+    void* grad_b;
+    float* grad_h0;
+    Scratch sc;
+    Dims d;
+};
+
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <int DT, bool ALIGNED, int NR, int WAVES>
-__global__ __launch_bounds__(WAVES* kWave) void fused_fwd_kernel(
-    const void* __restrict__ a, const void* __restrict__ b, void* __restrict__ out,
-    float* __restrict__ last, const float* __restrict__ h0, Scratch sc, int64_t T, int64_t D,
-    int64_t nW, int64_t nS, int64_t NK) {
-    constexpr int V = Elem<DT>::V;
-    constexpr int EB = Elem<DT>::bytes;
-    constexpr int W = kCG * V;
-    constexpr int SEGS = WAVES * kRG;
-    constexpr int64_t CT = (int64_t)SEGS * NR;
-
-    __shared__ TileTicket s_tt;
+template <class C, bool ALIGNED>
+__global__ __launch_bounds__(C::NT) void fused_fwd_kernel(FwdArgs x) {
+    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
     __shared__ Aff s_excl[WAVES][V][kWave];
     __shared__ Aff s_wtot[WAVES][W];
     __shared__ float s_hin[W];
 
+    const Dims d = x.d;
     const int tid = threadIdx.x;
     const int wave = uniform((int)(threadIdx.x / kWave));
     const int l = tid % kWave;
-    const int rg = l / kCG;
-    const int cg = l % kCG;
-    if (tid == 0) {
-        const uint32_t p = peek_u32(&sc.hdr->phase);
-        s_tt.phase = p;
-        s_tt.ticket = atomicAdd(&sc.hdr->ctr[p], 1u) + 1u;
-        s_tt.nclear = sc.hdr->dirty[p ^ 1u];
-        if (s_tt.ticket == sc.total_tiles - 1) header_update(sc, p);
-    }
-    __syncthreads();
-    const TileTicket tt = s_tt;
-    const int64_t ticket = uniform(tt.ticket);
-    const uint32_t phase = uniform(tt.phase);
-    const unsigned long long* pqs = reinterpret_cast<const unsigned long long*>(sc.region[phase]);
-    const uint32_t* hs = sc.region[phase] + 2 * sc.entries;
-    const int64_t k = ticket / nS;
-    const int64_t s = ticket - k * nS;
-    const int64_t bi = s / nW;
-    const int64_t dcol0 = (s - bi * nW) * W;
-    const int64_t d0 = dcol0 + cg * V;
-    const int nvalid = d0 >= D ? 0 : (int)((D - d0) < V ? (D - d0) : V);
-    const int64_t trow0 = k * CT;                                         // first row of the tile
-    const int64_t row0 = trow0 + (int64_t)(wave * kRG + rg) * NR;          // first row of this thread
-    const int64_t rowbytes = D * EB;
-    const size_t tbase = (((size_t)bi * T + trow0) * D + dcol0) * EB;     // wave-uniform
-    // lanes past D read a valid column and are then replaced by identity steps
-    const uint32_t coff = (uint32_t)((nvalid > 0 ? cg * V : 0) * EB);
-    const char* pa = static_cast<const char*>(a) + tbase;
-    const char* pb = static_cast<const char*>(b) + tbase;
-    char* po = static_cast<char*>(out) + tbase;
+    const int rg = l / TPR;
+    const int cg = l % TPR;
+    const Ticket tk = take_ticket(x.sc);
+    const Geo g = tile_geo<C, false>(tk.ticket, d, wave, rg, cg);
+    const uint32_t rowbytes = (uint32_t)d.D * C::EB;
+    const char* pa = static_cast<const char*>(x.a) + g.tbase;
+    const char* pb = static_cast<const char*>(x.b) + g.tbase;
+    char* po = static_cast<char*>(x.out) + g.tbase;
 
-    // every load is issued unconditionally (rows past T read row T-1) so that
-    // all of them are in flight together; invalid rows become identity steps
-    RowVec<DT> ra[NR], rb[NR];
+    // every load is issued before any is used; rows past T and lanes past D
+    // are read from valid addresses and replaced by identity steps below
+    RowVec<C::DT> ra[NR], rb[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const int64_t row = row0 + i;
-        const int64_t rc = row < T ? row : T - 1;
-        const uint32_t off = (uint32_t)(rc - trow0) * (uint32_t)rowbytes + coff;
-        const RowVec<DT> xa = load_vec<DT, ALIGNED>(pa, off, nvalid, 1.0f);
-        const RowVec<DT> xb = load_vec<DT, ALIGNED>(pb, off, nvalid, 0.0f);
-        const bool ok = row < T && nvalid > 0;
-        ra[i] = ok ? xa : RowVec<DT>::splat(1.0f);
-        rb[i] = ok ? xb : RowVec<DT>::splat(0.0f);
+        const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
+        ra[i] = load_vec<C::DT, ALIGNED>(pa, off, g.nvalid, 1.0f);
+        rb[i] = load_vec<C::DT, ALIGNED>(pb, off, g.nvalid, 0.0f);
     }
-    clear_other_region(sc, tt, WAVES * kWave);
+    clear_share(x.sc, tk, C::NT);
 
-    // summary of this thread's segment, per lane, then the wavefront scan
+    // summary of this thread's rows, per lane (rows outer, so only one row
+    // is widened to fp32 at a time), then the wavefront scan over its RG
+    // row groups
+    Aff m[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) m[j] = aff_identity();
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const bool ok = i < g.nrows;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const float at = ok ? ra[i].get(j) : 1.0f;
+            const float bt = ok ? rb[i].get(j) : 0.0f;
+            m[j].p = at * m[j].p;
+            m[j].q = fmaf(at, m[j].q, bt);
+        }
+    }
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        Aff m = aff_identity();
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const float at = ra[i].get(j);
-            m.p = at * m.p;
-            m.q = fmaf(at, m.q, rb[i].get(j));
-        }
-        const Aff inc = wave_scan_up<kCG>(m);
+        const Aff inc = wave_scan_up<TPR>(m[j]);
         Aff ex;
-        ex.p = shfl_up_f(inc.p, kCG);
-        ex.q = shfl_up_f(inc.q, kCG);
+        ex.p = shfl_up_f(inc.p, TPR);
+        ex.q = shfl_up_f(inc.q, TPR);
         if (rg == 0) ex = aff_identity();
         s_excl[wave][j][l] = ex;
-        if (rg == kRG - 1) s_wtot[wave][cg * V + j] = inc;
+        if (rg == RG - 1) s_wtot[wave][cg * V + j] = inc;
     }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -254,18 +348,21 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_fwd_kernel(
     }
     __syncthreads();
 
-    // tile map, publication, look-back (one lane per column in wavefront 0)
-    if (wave == 0 && l < W) {
-        const int c = l;
+    // tile map, publication, look-back: one column per thread
+    if (tid < W) {
+        const int c = tid;
+        const unsigned long long* pqs =
+            reinterpret_cast<const unsigned long long*>(x.sc.region[tk.phase] + x.sc.ctr_words);
+        const uint32_t* hs = x.sc.region[tk.phase] + x.sc.ctr_words + 2 * x.sc.entries;
         Aff A = aff_identity();
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) A = aff_then(A, s_wtot[w][c]);
-        const size_t o = ((size_t)k * nS + s) * W + c;
-        const bool more = k + 1 < NK;
+        const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
+        const bool more = g.k + 1 < d.NK;
         if (more) publish_u64(const_cast<unsigned long long*>(pqs) + o, pack_aff(A));
-        const int64_t dl = dcol0 + c;
-        const float base0 = (h0 && dl < D) ? h0[bi * D + dl] : 0.0f;
-        const float hin = look_back<-1>(pqs, hs, k, NK, nS, s, W, c, base0);
+        const int dl = g.dcol0 + c;
+        const float base0 = (x.h0 && dl < d.D) ? x.h0[(size_t)g.bi * d.D + dl] : 0.0f;
+        const float hin = look_back<-1, C::LB>(pqs, hs, g.k, d.NK, d.nS, g.s, W, c, base0);
         if (more) publish_u32(const_cast<uint32_t*>(hs) + o, publishable(aff_apply(A, hin)));
         s_hin[c] = hin;
     }
@@ -276,124 +373,94 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_fwd_kernel(
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         const int col = cg * V + j;
-        float x = s_hin[col];
-        for (int w = 0; w < wave; ++w) x = aff_apply(s_wtot[w][col], x);
-        h[j] = aff_apply(s_excl[wave][j][l], x);
+        float xv = s_hin[col];
+        for (int w = 0; w < wave; ++w) xv = aff_apply(s_wtot[w][col], xv);
+        h[j] = aff_apply(s_excl[wave][j][l], xv);
     }
-    if (nvalid > 0) {
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            if (row0 + i < T) {
-                RowOut<DT> o;
+    for (int i = 0; i < NR; ++i) {
+        if (i < g.nrows) {
+            RowOut<C::DT> o;
 #pragma unroll
-                for (int j = 0; j < V; ++j) {
-                    h[j] = fmaf(ra[i].get(j), h[j], rb[i].get(j));
-                    o.v[j] = h[j];
-                }
-                store_vec<DT, ALIGNED>(po, (uint32_t)(row0 + i - trow0) * (uint32_t)rowbytes + coff,
-                                       nvalid, o);
+            for (int j = 0; j < V; ++j) {
+                h[j] = fmaf(ra[i].get(j), h[j], rb[i].get(j));
+                o.v[j] = h[j];
             }
+            store_vec<C::DT, ALIGNED>(po, row_off(g, g.row0 + i, d.T, rowbytes), g.nvalid, o);
         }
-        if (last && row0 <= T - 1 && T - 1 < row0 + NR) {
+    }
+    if (x.last && g.nrows > 0 && g.row0 + g.nrows == d.T) {
 #pragma unroll
-            for (int j = 0; j < V; ++j)
-                if (j < nvalid) last[bi * D + d0 + j] = h[j];
-        }
+        for (int j = 0; j < V; ++j)
+            if (j < g.nvalid) x.last[(size_t)g.bi * d.D + g.d0 + j] = h[j];
     }
 }
 
 // ---------------------------------------------------------------------------
 // reverse time (backward)
 // ---------------------------------------------------------------------------
-template <int DT, bool ALIGNED, int NR, int WAVES>
-__global__ __launch_bounds__(WAVES* kWave) void fused_bwd_kernel(
-    const void* __restrict__ a, const void* __restrict__ out, const void* __restrict__ g,
-    const float* __restrict__ grad_last, const float* __restrict__ h0, void* __restrict__ grad_a,
-    void* __restrict__ grad_b, float* __restrict__ grad_h0, Scratch sc, int64_t T, int64_t D,
-    int64_t nW, int64_t nS, int64_t NK) {
-    constexpr int V = Elem<DT>::V;
-    constexpr int EB = Elem<DT>::bytes;
-    constexpr int W = kCG * V;
-    constexpr int SEGS = WAVES * kRG;
-    constexpr int64_t CT = (int64_t)SEGS * NR;
-
-    __shared__ TileTicket s_tt;
+template <class C, bool ALIGNED>
+__global__ __launch_bounds__(C::NT) void fused_bwd_kernel(BwdArgs x) {
+    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
     __shared__ Aff s_excl[WAVES][V][kWave];
     __shared__ Aff s_wtot[WAVES][W];
     __shared__ float s_cin[W];
 
+    const Dims d = x.d;
     const int tid = threadIdx.x;
     const int wave = uniform((int)(threadIdx.x / kWave));
     const int l = tid % kWave;
-    const int rg = l / kCG;
-    const int cg = l % kCG;
-    if (tid == 0) {
-        const uint32_t p = peek_u32(&sc.hdr->phase);
-        s_tt.phase = p;
-        s_tt.ticket = atomicAdd(&sc.hdr->ctr[p], 1u) + 1u;
-        s_tt.nclear = sc.hdr->dirty[p ^ 1u];
-        if (s_tt.ticket == sc.total_tiles - 1) header_update(sc, p);
-    }
-    __syncthreads();
-    const TileTicket tt = s_tt;
-    const int64_t ticket = uniform(tt.ticket);
-    const uint32_t phase = uniform(tt.phase);
-    const unsigned long long* pqs = reinterpret_cast<const unsigned long long*>(sc.region[phase]);
-    const uint32_t* hs = sc.region[phase] + 2 * sc.entries;
-    const int64_t kr = ticket / nS;
-    const int64_t s = ticket - kr * nS;
-    const int64_t k = NK - 1 - kr;
-    const int64_t bi = s / nW;
-    const int64_t dcol0 = (s - bi * nW) * W;
-    const int64_t d0 = dcol0 + cg * V;
-    const int nvalid = d0 >= D ? 0 : (int)((D - d0) < V ? (D - d0) : V);
-    const int64_t trow0 = k * CT;
-    const int64_t row0 = trow0 + (int64_t)(wave * kRG + rg) * NR;
-    const int64_t rowbytes = D * EB;
-    const size_t tbase = (((size_t)bi * T + trow0) * D + dcol0) * EB;
-    const int64_t hrow0 = trow0 > 0 ? trow0 - 1 : 0;  // first row of `out` the tile reads
-    const size_t hbase = (((size_t)bi * T + hrow0) * D + dcol0) * EB;
-    const uint32_t coff = (uint32_t)((nvalid > 0 ? cg * V : 0) * EB);
-    const char* pa = static_cast<const char*>(a) + tbase;
-    const char* pg = static_cast<const char*>(g) + tbase;
-    const char* ph = static_cast<const char*>(out) + hbase;
-    char* pga = static_cast<char*>(grad_a) + tbase;
-    char* pgb = static_cast<char*>(grad_b) + tbase;
+    const int rg = l / TPR;
+    const int cg = l % TPR;
+    const Ticket tk = take_ticket(x.sc);
+    const Geo g = tile_geo<C, true>(tk.ticket, d, wave, rg, cg);
+    const uint32_t rowbytes = (uint32_t)d.D * C::EB;
+    const char* pa = static_cast<const char*>(x.a) + g.tbase;
+    const char* pg = static_cast<const char*>(x.g) + g.tbase;
+    // h_{t-1} lives in row t-1 of `out`: its offsets count from the row the
+    // tile's reads of `out` start at (one before the tile, or row 0)
+    const int hrow0 = g.trow0 > 0 ? g.trow0 - 1 : 0;
+    const char* ph = static_cast<const char*>(x.out) + g.tbase - (size_t)(g.trow0 - hrow0) * rowbytes;
+    char* pga = static_cast<char*>(x.grad_a) + g.tbase;
+    char* pgb = static_cast<char*>(x.grad_b) + g.tbase;
 
-    RowVec<DT> ra[NR], rg_[NR], rh[NR];
+    RowVec<C::DT> ra[NR], rg_[NR], rh[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const int64_t row = row0 + i;
-        const int64_t rc = row < T ? row : T - 1;
-        const int64_t hr = rc >= 1 ? rc - 1 : 0;  // h_{t-1} lives in row t-1 of out
-        const uint32_t off = (uint32_t)(rc - trow0) * (uint32_t)rowbytes + coff;
-        const uint32_t hoff = (uint32_t)(hr - hrow0) * (uint32_t)rowbytes + coff;
-        const RowVec<DT> xa = load_vec<DT, ALIGNED>(pa, off, nvalid, 1.0f);
-        const RowVec<DT> xg = load_vec<DT, ALIGNED>(pg, off, nvalid, 0.0f);
-        const RowVec<DT> xh = load_vec<DT, ALIGNED>(ph, hoff, nvalid, 0.0f);
-        const bool ok = row < T && nvalid > 0;
-        ra[i] = ok ? xa : RowVec<DT>::splat(1.0f);
-        rg_[i] = ok ? xg : RowVec<DT>::splat(0.0f);
-        rh[i] = (ok && row >= 1) ? xh : RowVec<DT>::splat(0.0f);
+        const int row = g.row0 + i;
+        const int rc = row < d.T ? row : d.T - 1;
+        const int hr = rc >= 1 ? rc - 1 : 0;
+        const uint32_t off = (uint32_t)(rc - g.trow0) * rowbytes + g.coff;
+        const uint32_t hoff = (uint32_t)(hr - hrow0) * rowbytes + g.coff;
+        ra[i] = load_vec<C::DT, ALIGNED>(pa, off, g.nvalid, 1.0f);
+        rg_[i] = load_vec<C::DT, ALIGNED>(pg, off, g.nvalid, 0.0f);
+        rh[i] = load_vec<C::DT, ALIGNED>(ph, hoff, g.nvalid, 0.0f);
     }
-    clear_other_region(sc, tt, WAVES * kWave);
+    clear_share(x.sc, tk, C::NT);
 
     // reverse summary: the map from the carry entering the segment on the
     // right to the carry a_s*lambda_s leaving its first row s
+    Aff m[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) m[j] = aff_identity();
+#pragma unroll
+    for (int i = NR - 1; i >= 0; --i) {
+        const bool ok = i < g.nrows;
+#pragma unroll
+        for (int j = 0; j < V; ++j) {
+            const float at = ok ? ra[i].get(j) : 1.0f;
+            const float gt = ok ? rg_[i].get(j) : 0.0f;
+            m[j].p = at * m[j].p;
+            m[j].q = at * (m[j].q + gt);
+        }
+    }
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        Aff m = aff_identity();
-#pragma unroll
-        for (int i = NR - 1; i >= 0; --i) {
-            const float at = ra[i].get(j);
-            m.p = at * m.p;
-            m.q = at * (m.q + rg_[i].get(j));
-        }
-        const Aff inc = wave_scan_down<kCG>(m);
+        const Aff inc = wave_scan_down<TPR>(m[j]);
         Aff ex;
-        ex.p = shfl_down_f(inc.p, kCG);
-        ex.q = shfl_down_f(inc.q, kCG);
-        if (rg == kRG - 1) ex = aff_identity();
+        ex.p = shfl_down_f(inc.p, TPR);
+        ex.q = shfl_down_f(inc.q, TPR);
+        if (rg == RG - 1) ex = aff_identity();
         s_excl[wave][j][l] = ex;
         if (rg == 0) s_wtot[wave][cg * V + j] = inc;
     }
@@ -404,17 +471,20 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_bwd_kernel(
     }
     __syncthreads();
 
-    if (wave == 0 && l < W) {
-        const int c = l;
+    if (tid < W) {
+        const int c = tid;
+        const unsigned long long* pqs =
+            reinterpret_cast<const unsigned long long*>(x.sc.region[tk.phase] + x.sc.ctr_words);
+        const uint32_t* hs = x.sc.region[tk.phase] + x.sc.ctr_words + 2 * x.sc.entries;
         Aff A = aff_identity();
 #pragma unroll
         for (int w = WAVES - 1; w >= 0; --w) A = aff_then(A, s_wtot[w][c]);
-        const size_t o = ((size_t)k * nS + s) * W + c;
-        const bool more = k > 0;
+        const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
+        const bool more = g.k > 0;
         if (more) publish_u64(const_cast<unsigned long long*>(pqs) + o, pack_aff(A));
-        const int64_t dl = dcol0 + c;
-        const float base0 = (grad_last && dl < D) ? grad_last[bi * D + dl] : 0.0f;
-        const float cin = look_back<+1>(pqs, hs, k, NK, nS, s, W, c, base0);
+        const int dl = g.dcol0 + c;
+        const float base0 = (x.grad_last && dl < d.D) ? x.grad_last[(size_t)g.bi * d.D + dl] : 0.0f;
+        const float cin = look_back<+1, C::LB>(pqs, hs, g.k, d.NK, d.nS, g.s, W, c, base0);
         if (more) publish_u32(const_cast<uint32_t*>(hs) + o, publishable(aff_apply(A, cin)));
         s_cin[c] = cin;
     }
@@ -424,35 +494,33 @@ __global__ __launch_bounds__(WAVES* kWave) void fused_bwd_kernel(
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         const int col = cg * V + j;
-        float x = s_cin[col];
-        for (int w = WAVES - 1; w > wave; --w) x = aff_apply(s_wtot[w][col], x);
-        carry[j] = aff_apply(s_excl[wave][j][l], x);
+        float xv = s_cin[col];
+        for (int w = WAVES - 1; w > wave; --w) xv = aff_apply(s_wtot[w][col], xv);
+        carry[j] = aff_apply(s_excl[wave][j][l], xv);
     }
-    if (nvalid > 0) {
 #pragma unroll
-        for (int i = NR - 1; i >= 0; --i) {
-            const int64_t row = row0 + i;
-            if (row < T) {
-                RowOut<DT> oa, ob;
+    for (int i = NR - 1; i >= 0; --i) {
+        if (i < g.nrows) {
+            const int row = g.row0 + i;
+            RowOut<C::DT> oa, ob;
 #pragma unroll
-                for (int j = 0; j < V; ++j) {
-                    const float lam = rg_[i].get(j) + carry[j];
-                    float hp = rh[i].get(j);
-                    if (row == 0) hp = (h0 && j < nvalid) ? h0[bi * D + d0 + j] : 0.0f;
-                    ob.v[j] = lam;
-                    oa.v[j] = lam * hp;
-                    carry[j] = ra[i].get(j) * lam;
-                }
-                const uint32_t off = (uint32_t)(row - trow0) * (uint32_t)rowbytes + coff;
-                store_vec<DT, ALIGNED>(pga, off, nvalid, oa);
-                store_vec<DT, ALIGNED>(pgb, off, nvalid, ob);
+            for (int j = 0; j < V; ++j) {
+                const float lam = rg_[i].get(j) + carry[j];
+                float hp = rh[i].get(j);
+                if (row == 0) hp = (x.h0 && j < g.nvalid) ? x.h0[(size_t)g.bi * d.D + g.d0 + j] : 0.0f;
+                ob.v[j] = lam;
+                oa.v[j] = lam * hp;
+                carry[j] = ra[i].get(j) * lam;
             }
+            const uint32_t off = row_off(g, row, d.T, rowbytes);
+            store_vec<C::DT, ALIGNED>(pga, off, g.nvalid, oa);
+            store_vec<C::DT, ALIGNED>(pgb, off, g.nvalid, ob);
         }
-        if (grad_h0 && row0 == 0) {
+    }
+    if (x.grad_h0 && g.nrows > 0 && g.row0 == 0) {
 #pragma unroll
-            for (int j = 0; j < V; ++j)
-                if (j < nvalid) grad_h0[bi * D + d0 + j] = carry[j];
-        }
+        for (int j = 0; j < V; ++j)
+            if (j < g.nvalid) x.grad_h0[(size_t)g.bi * d.D + g.d0 + j] = carry[j];
     }
 }
 
@@ -462,40 +530,67 @@ __global__ void scratch_init_kernel(uint32_t* __restrict__ p, size_t words) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
          i += (size_t)gridDim.x * blockDim.x) {
         uint32_t v = kEmpty;
-        if (i < kHeaderBytes / 4) v = (i == 32 || i == 33) ? kEmpty : 0u;  // Header::ctr
+        if (i < kHeaderBytes / 4) v = (i == 32 || i == 33) ? kEmpty : 0u;  // Header::done
         p[i] = v;
     }
 }
 
 // ---------------------------------------------------------------------------
-// tile configurations: tile length -> (rows per thread, wavefronts)
+// host side: configurations, layout, launch
 // ---------------------------------------------------------------------------
+// (width = threads per row, tile = rows per tile) -> kernel parameters
 struct TileCfg {
-    int tile, nr, waves;
+    int width, tile, nr, waves, lb;
 };
-constexpr TileCfg kFwdTiles[] = {{256, 8, 4}, {512, 16, 4}, {1024, 16, 8}};
-constexpr TileCfg kBwdTiles[] = {{256, 8, 4}, {512, 8, 8}};
+constexpr TileCfg kFwdCfgs[] = {
+    {8, 256, 8, 4, 8}, {8, 512, 16, 4, 8}, {16, 128, 8, 4, 4},
+    {16, 256, 16, 4, 4}, {32, 64, 8, 4, 4}, {32, 128, 16, 4, 4},
+};
+constexpr TileCfg kBwdCfgs[] = {
+    {8, 256, 8, 4, 8}, {8, 128, 4, 4, 8}, {16, 128, 8, 4, 4},
+    {32, 64, 8, 4, 4}, {32, 32, 4, 4, 4},
+};
 
-int64_t series_width(int dtype) {
-    return kCG * (dtype == DT_F32 ? Elem<DT_F32>::V : Elem<DT_BF16>::V);
+const TileCfg* find_cfg(int dir, int width, int tile) {
+    if (dir == 0) {
+        for (const auto& c : kFwdCfgs)
+            if (c.width == width && c.tile == tile) return &c;
+    } else {
+        for (const auto& c : kBwdCfgs)
+            if (c.width == width && c.tile == tile) return &c;
+    }
+    return nullptr;
 }
 
 struct Layout {
-    int64_t nW, nS, NK, W;
+    int nW, nS, NK, W;
     unsigned long long entries;
 };
 
-Layout layout_of(const Shape& s, int tile) {
+Layout layout_of(const Shape& s, int width, int tile) {
     Layout L;
-    L.W = series_width(s.dtype);
-    L.nW = (s.D + L.W - 1) / L.W;
-    L.nS = s.B * L.nW;
-    L.NK = (s.T + tile - 1) / tile;
+    L.W = width * (s.dtype == DT_F32 ? Elem<DT_F32>::V : Elem<DT_BF16>::V);
+    L.nW = (int)((s.D + L.W - 1) / L.W);
+    L.nS = (int)(s.B * L.nW);
+    L.NK = (int)((s.T + tile - 1) / tile);
     L.entries = (unsigned long long)L.NK * L.nS * L.W;
     return L;
 }
 
-size_t region_bytes_for(const Layout& L) { return (L.entries * 12 + 255) / 256 * 256; }
+// Ticket counters: the largest power of two up to kMaxCounters dividing nS.
+int counters_of(const Layout& L) {
+    int c = 1;
+    while (c < kMaxCounters && L.nS % (2 * c) == 0) c *= 2;
+    return c;
+}
+
+unsigned long long ctr_words_of(const Layout& L) {
+    return (unsigned long long)counters_of(L) * kCtrStride;
+}
+
+size_t region_bytes_for(const Layout& L) {
+    return ((ctr_words_of(L) + 3 * L.entries) * 4 + 255) / 256 * 256;
+}
 
 // Region size implied by a workspace size (the same for every call on one buffer).
 size_t region_bytes_of(size_t ws_bytes) {
@@ -506,7 +601,6 @@ hipError_t prepare(void* ws, size_t ws_bytes, bool init, const Layout& L, hipStr
                    Scratch* sc) {
     const size_t rb = region_bytes_of(ws_bytes);
     if (rb < region_bytes_for(L)) return hipErrorInvalidValue;
-    if ((unsigned long long)L.NK * L.nS >= 0xffffffffull) return hipErrorInvalidValue;
     char* base = static_cast<char*>(ws);
     if (init) {
         const size_t words = (kHeaderBytes + 2 * rb) / 4;
@@ -520,115 +614,144 @@ hipError_t prepare(void* ws, size_t ws_bytes, bool init, const Layout& L, hipStr
     sc->region[0] = reinterpret_cast<uint32_t*>(base + kHeaderBytes);
     sc->region[1] = reinterpret_cast<uint32_t*>(base + kHeaderBytes + rb);
     sc->entries = L.entries;
-    sc->total_tiles = (uint32_t)(L.NK * L.nS);
+    sc->ctr_words = ctr_words_of(L);
+    sc->total_tiles = (uint32_t)((unsigned long long)L.NK * L.nS);
+    sc->nC = (uint32_t)counters_of(L);
+    sc->quota = sc->total_tiles / sc->nC;
     return hipSuccess;
 }
 
-template <int DT, bool AL, int NR, int WAVES>
-void fwd_launch(const Shape& s, const Layout& L, const void* a, const void* b, void* out,
-                float* last, const float* h0, const Scratch& sc, hipStream_t st) {
-    const dim3 grid((unsigned)(L.NK * L.nS));
-    hipLaunchKernelGGL((fused_fwd_kernel<DT, AL, NR, WAVES>), grid, dim3(WAVES * kWave), 0, st, a,
-                       b, out, last, h0, sc, s.T, s.D, L.nW, L.nS, L.NK);
+template <int DT, int TPR, int NR, int WAVES, int LB, bool AL>
+void launch_fwd_cfg(const FwdArgs& x, hipStream_t st) {
+    using C = Cfg<DT, TPR, NR, WAVES, LB>;
+    hipLaunchKernelGGL((fused_fwd_kernel<C, AL>), dim3(x.sc.total_tiles), dim3(C::NT), 0, st, x);
 }
 
-template <int DT, bool AL, int NR, int WAVES>
-void bwd_launch(const Shape& s, const Layout& L, const void* a, const void* out, const void* g,
-                const float* gl, const float* h0, void* ga, void* gb, float* gh0,
-                const Scratch& sc, hipStream_t st) {
-    const dim3 grid((unsigned)(L.NK * L.nS));
-    hipLaunchKernelGGL((fused_bwd_kernel<DT, AL, NR, WAVES>), grid, dim3(WAVES * kWave), 0, st, a,
-                       out, g, gl, h0, ga, gb, gh0, sc, s.T, s.D, L.nW, L.nS, L.NK);
+template <int DT, int TPR, int NR, int WAVES, int LB, bool AL>
+void launch_bwd_cfg(const BwdArgs& x, hipStream_t st) {
+    using C = Cfg<DT, TPR, NR, WAVES, LB>;
+    hipLaunchKernelGGL((fused_bwd_kernel<C, AL>), dim3(x.sc.total_tiles), dim3(C::NT), 0, st, x);
 }
 
-template <int DT, bool AL>
-bool fwd_dispatch(int tile, const Shape& s, const Layout& L, const void* a, const void* b,
-                  void* out, float* last, const float* h0, const Scratch& sc, hipStream_t st) {
-    switch (tile) {
-        case 256: fwd_launch<DT, AL, 8, 4>(s, L, a, b, out, last, h0, sc, st); return true;
-        case 512: fwd_launch<DT, AL, 16, 4>(s, L, a, b, out, last, h0, sc, st); return true;
-        case 1024: fwd_launch<DT, AL, 16, 8>(s, L, a, b, out, last, h0, sc, st); return true;
+// Unaligned rows (D * elem_bytes not a multiple of 16, or unaligned pointers)
+// use element-wise accesses and only the narrowest configuration.
+template <int DT>
+bool fwd_dispatch(const TileCfg& c, bool al, const FwdArgs& x, hipStream_t st) {
+    if (!al) {
+        if (c.width != 8 || c.tile != 256) return false;
+        launch_fwd_cfg<DT, 8, 8, 4, 8, false>(x, st);
+        return true;
     }
-    return false;
+    if (c.width == 8 && c.tile == 256) launch_fwd_cfg<DT, 8, 8, 4, 8, true>(x, st);
+    else if (c.width == 8 && c.tile == 512) launch_fwd_cfg<DT, 8, 16, 4, 8, true>(x, st);
+    else if (c.width == 16 && c.tile == 128) launch_fwd_cfg<DT, 16, 8, 4, 4, true>(x, st);
+    else if (c.width == 16 && c.tile == 256) launch_fwd_cfg<DT, 16, 16, 4, 4, true>(x, st);
+    else if (c.width == 32 && c.tile == 64) launch_fwd_cfg<DT, 32, 8, 4, 4, true>(x, st);
+    else if (c.width == 32 && c.tile == 128) launch_fwd_cfg<DT, 32, 16, 4, 4, true>(x, st);
+    else return false;
+    return true;
 }
 
-template <int DT, bool AL>
-bool bwd_dispatch(int tile, const Shape& s, const Layout& L, const void* a, const void* out,
-                  const void* g, const float* gl, const float* h0, void* ga, void* gb, float* gh0,
-                  const Scratch& sc, hipStream_t st) {
-    switch (tile) {
-        case 256: bwd_launch<DT, AL, 8, 4>(s, L, a, out, g, gl, h0, ga, gb, gh0, sc, st); return true;
-        case 512: bwd_launch<DT, AL, 8, 8>(s, L, a, out, g, gl, h0, ga, gb, gh0, sc, st); return true;
+template <int DT>
+bool bwd_dispatch(const TileCfg& c, bool al, const BwdArgs& x, hipStream_t st) {
+    if (!al) {
+        if (c.width != 8 || c.tile != 256) return false;
+        launch_bwd_cfg<DT, 8, 8, 4, 8, false>(x, st);
+        return true;
     }
-    return false;
+    if (c.width == 8 && c.tile == 256) launch_bwd_cfg<DT, 8, 8, 4, 8, true>(x, st);
+    else if (c.width == 8 && c.tile == 128) launch_bwd_cfg<DT, 8, 4, 4, 8, true>(x, st);
+    else if (c.width == 16 && c.tile == 128) launch_bwd_cfg<DT, 16, 8, 4, 4, true>(x, st);
+    else if (c.width == 32 && c.tile == 64) launch_bwd_cfg<DT, 32, 8, 4, 4, true>(x, st);
+    else if (c.width == 32 && c.tile == 32) launch_bwd_cfg<DT, 32, 4, 4, 4, true>(x, st);
+    else return false;
+    return true;
 }
 
 }  // namespace
 
-bool fused_tile_supported(const Shape& s, int dir, int tile) {
-    // per-lane row offsets inside a tile are 32-bit
+bool fused_cfg_supported(const Shape& s, int dir, int width, int tile, bool aligned) {
+    if (!find_cfg(dir, width, tile)) return false;
+    if (!aligned && (width != 8 || tile != 256)) return false;
+    // 32-bit row offsets inside a tile, 32-bit lane and row indices, 32-bit tickets
     const int64_t eb = s.dtype == DT_F32 ? 4 : 2;
-    if ((int64_t)tile * s.D * eb >= ((int64_t)1 << 31)) return false;
-    if (dir == 0) {
-        for (const auto& c : kFwdTiles)
-            if (c.tile == tile) return true;
-    } else {
-        for (const auto& c : kBwdTiles)
-            if (c.tile == tile) return true;
+    if ((int64_t)(tile + 1) * s.D * eb >= ((int64_t)1 << 31)) return false;
+    if (s.T >= ((int64_t)1 << 31) - tile || s.D >= ((int64_t)1 << 30)) return false;
+    const Layout L = layout_of(s, width, tile);
+    if ((unsigned long long)L.NK * L.nS >= 0xffffffffull) return false;
+    if (s.B * (int64_t)L.nW >= ((int64_t)1 << 31)) return false;
+    return true;
+}
+
+// Default tile shape, from measurements on MI355X (bf16 [8,2048,2560] and
+// [16,4096,2560], fp32 [4,8192,4096], bf16 [1,131072,1024]): 256-byte rows
+// when there are enough lane blocks to keep every tile chain short (bf16 with
+// at least 128 such blocks), else 128-byte rows, which give long single-batch
+// sequences 4x as many chains.  fp32 was fastest with 128-byte rows.
+void fused_default_cfg(const Shape& s, int dir, bool aligned, int* width, int* tile) {
+    *width = 8;
+    *tile = 256;
+    if (!aligned) return;
+    if (s.dtype == DT_BF16) {
+        const int64_t lanes16 = 16 * Elem<DT_BF16>::V;
+        const int64_t blocks16 = s.B * ((s.D + lanes16 - 1) / lanes16);
+        if (blocks16 >= 128) {
+            *width = 16;
+            *tile = dir == 0 ? 256 : 128;
+        }
     }
-    return false;
 }
 
-int fused_default_tile(const Shape& s, int dir) {
-    (void)s;
-    return dir == 0 ? 512 : 256;
+size_t fused_workspace_bytes(const Shape& s, int width, int tile) {
+    return kHeaderBytes + 2 * region_bytes_for(layout_of(s, width, tile));
 }
 
-size_t fused_workspace_bytes(const Shape& s, int tile) {
-    return kHeaderBytes + 2 * region_bytes_for(layout_of(s, tile));
-}
-
-hipError_t launch_fused_fwd(const Shape& s, int tile, const void* a, const void* b, void* out,
-                            float* last, const float* h0, void* ws, size_t ws_bytes, bool init,
-                            hipStream_t st) {
-    const Layout L = layout_of(s, tile);
-    Scratch sc;
-    hipError_t e = prepare(ws, ws_bytes, init, L, st, &sc);
+hipError_t launch_fused_fwd(const Shape& s, int width, int tile, const void* a, const void* b,
+                            void* out, float* last, const float* h0, void* ws, size_t ws_bytes,
+                            bool init, hipStream_t st) {
+    const TileCfg* c = find_cfg(0, width, tile);
+    if (!c) return hipErrorInvalidValue;
+    const Layout L = layout_of(s, width, tile);
+    FwdArgs x;
+    hipError_t e = prepare(ws, ws_bytes, init, L, st, &x.sc);
     if (e != hipSuccess) return e;
+    x.a = a;
+    x.b = b;
+    x.out = out;
+    x.last = last;
+    x.h0 = h0;
+    x.d = Dims{(int)s.T, (int)s.D, L.nW, L.nS, L.NK};
     const void* ptrs[3] = {a, b, out};
     const bool al = rows_aligned(s, ptrs, 3);
-    bool ok;
-    if (s.dtype == DT_F32)
-        ok = al ? fwd_dispatch<DT_F32, true>(tile, s, L, a, b, out, last, h0, sc, st)
-                : fwd_dispatch<DT_F32, false>(tile, s, L, a, b, out, last, h0, sc, st);
-    else
-        ok = al ? fwd_dispatch<DT_BF16, true>(tile, s, L, a, b, out, last, h0, sc, st)
-                : fwd_dispatch<DT_BF16, false>(tile, s, L, a, b, out, last, h0, sc, st);
+    const bool ok = s.dtype == DT_F32 ? fwd_dispatch<DT_F32>(*c, al, x, st)
+                                      : fwd_dispatch<DT_BF16>(*c, al, x, st);
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-hipError_t launch_fused_bwd(const Shape& s, int tile, const void* a, const void* out,
+hipError_t launch_fused_bwd(const Shape& s, int width, int tile, const void* a, const void* out,
                             const void* g, const float* grad_last, const float* h0, void* grad_a,
                             void* grad_b, float* grad_h0, void* ws, size_t ws_bytes, bool init,
                             hipStream_t st) {
-    const Layout L = layout_of(s, tile);
-    Scratch sc;
-    hipError_t e = prepare(ws, ws_bytes, init, L, st, &sc);
+    const TileCfg* c = find_cfg(1, width, tile);
+    if (!c) return hipErrorInvalidValue;
+    const Layout L = layout_of(s, width, tile);
+    BwdArgs x;
+    hipError_t e = prepare(ws, ws_bytes, init, L, st, &x.sc);
     if (e != hipSuccess) return e;
+    x.a = a;
+    x.out = out;
+    x.g = g;
+    x.grad_last = grad_last;
+    x.h0 = h0;
+    x.grad_a = grad_a;
+    x.grad_b = grad_b;
+    x.grad_h0 = grad_h0;
+    x.d = Dims{(int)s.T, (int)s.D, L.nW, L.nS, L.NK};
     const void* ptrs[5] = {a, out, g, grad_a, grad_b};
     const bool al = rows_aligned(s, ptrs, 5);
-    bool ok;
-    if (s.dtype == DT_F32)
-        ok = al ? bwd_dispatch<DT_F32, true>(tile, s, L, a, out, g, grad_last, h0, grad_a, grad_b,
-                                             grad_h0, sc, st)
-                : bwd_dispatch<DT_F32, false>(tile, s, L, a, out, g, grad_last, h0, grad_a,
-                                              grad_b, grad_h0, sc, st);
-    else
-        ok = al ? bwd_dispatch<DT_BF16, true>(tile, s, L, a, out, g, grad_last, h0, grad_a, grad_b,
-                                              grad_h0, sc, st)
-                : bwd_dispatch<DT_BF16, false>(tile, s, L, a, out, g, grad_last, h0, grad_a,
-                                               grad_b, grad_h0, sc, st);
+    const bool ok = s.dtype == DT_F32 ? bwd_dispatch<DT_F32>(*c, al, x, st)
+                                      : bwd_dispatch<DT_BF16>(*c, al, x, st);
     if (!ok) return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -44,18 +44,20 @@ hipError_t launch_reverse_chunk_replay(const Shape& s, int chunk, const void* a,
                                        void* grad_a, void* grad_b, hipStream_t st);
 
 // ---- single-launch fused form ----------------------------------------------
-// Tile lengths (steps per workgroup) with a compiled kernel.
-bool fused_tile_supported(const Shape& s, int dir, int tile);
-int fused_default_tile(const Shape& s, int dir);
-size_t fused_workspace_bytes(const Shape& s, int tile);
+// A configuration is (width, tile): width threads of 16 bytes cover one row of
+// a tile (8, 16 or 32) and a tile spans `tile` rows.  Unaligned rows support
+// only width 8, tile 256.
+bool fused_cfg_supported(const Shape& s, int dir, int width, int tile, bool aligned);
+void fused_default_cfg(const Shape& s, int dir, bool aligned, int* width, int* tile);
+size_t fused_workspace_bytes(const Shape& s, int width, int tile);
 // `ws` holds the fused form's header and two scratch regions; `init` must be
 // true the first time a buffer is used (and whenever its contents were
 // disturbed): the launcher then enqueues one initialisation kernel first.
 // Every launch on a buffer must use the same `ws_bytes`.
-hipError_t launch_fused_fwd(const Shape& s, int tile, const void* a, const void* b, void* out,
-                            float* last, const float* h0, void* ws, size_t ws_bytes, bool init,
-                            hipStream_t st);
-hipError_t launch_fused_bwd(const Shape& s, int tile, const void* a, const void* out,
+hipError_t launch_fused_fwd(const Shape& s, int width, int tile, const void* a, const void* b,
+                            void* out, float* last, const float* h0, void* ws, size_t ws_bytes,
+                            bool init, hipStream_t st);
+hipError_t launch_fused_bwd(const Shape& s, int width, int tile, const void* a, const void* out,
                             const void* g, const float* grad_last, const float* h0, void* grad_a,
                             void* grad_b, float* grad_h0, void* ws, size_t ws_bytes, bool init,
                             hipStream_t st);

@@ -74,6 +74,8 @@ def test_argument_errors_return_status_without_work():
     o = lr.make_opts(algo="fused", chunk=100)
     assert lib.scan_bwd_ex(fake, fake, fake, None, fake, fake, 2, 8, 4, lr.BF16, None,
                            ctypes.byref(o)) == -4
+    o = lr.make_opts(algo="fused", chunk=64, width=32)  # wide tiles need aligned rows (D=3)
+    assert lib.scan_fwd_ex(fake, fake, fake, None, 2, 8, 3, lr.BF16, None, ctypes.byref(o)) == -4
     o = lr.make_opts(algo=9)
     assert lib.scan_fwd_ex(fake, fake, fake, None, 2, 8, 4, lr.F32, None, ctypes.byref(o)) == -7
     o = lr.make_opts(algo="chunked", chunk=64)
@@ -98,7 +100,7 @@ def test_workspace_sizes_and_auto_choice():
     assert n >= 3 * 4 * 128 * 4096 * 4
     for dt in (lr.F32, lr.BF16):
         for direction in (0, 1):
-            algo, chunk = lr.scan_auto_algo(8, 2048, 2560, dt, direction)
+            algo, chunk, width = lr.scan_auto_algo(8, 2048, 2560, dt, direction)
             assert algo in (lr.ALGO_SEQ, lr.ALGO_CHUNKED, lr.ALGO_FUSED)
-            o = lr.make_opts(algo=algo, chunk=chunk)
+            o = lr.make_opts(algo=algo, chunk=chunk, width=width)
             assert lr.scan_workspace_bytes(8, 2048, 2560, dt, o) >= 0

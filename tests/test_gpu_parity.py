@@ -18,11 +18,19 @@ import linear_recurrence_sequence_diag_amd as lr  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 
-# (name, forward chunk/tile, backward chunk/tile)
-ALGOS = [("seq", 0, 0), ("chunked", 16, 16), ("chunked", 64, 64), ("chunked", 256, 256),
-         ("chunked", 1024, 1024), ("fused", 256, 256), ("fused", 512, 512), ("fused", 1024, 512),
-         ("auto", 0, 0)]
-ALGO_IDS = [f"{a}{c}" if c else a for a, c, _ in ALGOS]
+# (name, forward chunk/tile, backward chunk/tile, forward width, backward width)
+ALGOS = [("seq", 0, 0, 0, 0), ("chunked", 16, 16, 0, 0), ("chunked", 64, 64, 0, 0),
+         ("chunked", 256, 256, 0, 0), ("chunked", 1024, 1024, 0, 0),
+         ("fused", 256, 256, 8, 8), ("fused", 512, 128, 8, 8), ("fused", 128, 128, 16, 16),
+         ("fused", 256, 128, 16, 16), ("fused", 64, 64, 32, 32), ("fused", 128, 32, 32, 32),
+         ("auto", 0, 0, 0, 0)]
+ALGO_IDS = [f"{a}{c}w{w}" if c else a for a, c, _, w, _ in ALGOS]
+
+
+def aligned_only(algo, cf, cb, wf, wb, D, dt):
+    """Wider fused tiles need 16-byte aligned rows."""
+    rows_aligned = (D * (4 if dt == "f32" else 2)) % 16 == 0
+    return algo == "fused" and not rows_aligned and (wf, cf, wb, cb) != (8, 256, 8, 256)
 
 
 @pytest.fixture(autouse=True, scope="module")
@@ -32,15 +40,15 @@ def _need_gpu():
     lr.library()
 
 
-def run_pair(inp, algo, cf, cb, h0=None, gl=None):
+def run_pair(inp, algo, cf, cb, wf=0, wb=0, h0=None, gl=None):
     """GPU forward then backward (the backward reads the GPU's own out)."""
     dt = inp.workload.dtype
     a, b, g = dev(inp.a, dt), dev(inp.b, dt), dev(inp.g, dt)
     th0 = None if h0 is None else dev_f32(h0)
     tgl = None if gl is None else dev_f32(gl)
-    out, last = lr.scan(a, b, h0=th0, algo=algo, chunk=cf)
+    out, last = lr.scan(a, b, h0=th0, algo=algo, chunk=cf, width=wf)
     ga, gb, gh0 = lr.scan_backward(a, out, g, grad_last=tgl, h0=th0, algo=algo, chunk=cb,
-                                   need_grad_h0=True)
+                                   need_grad_h0=True, width=wb)
     torch.cuda.synchronize()
     return out, last, ga, gb, gh0
 
@@ -76,27 +84,29 @@ def test_golden_hand_example_exact():
         inp = W.Inputs(W.Workload("hand", 1, 4, 2, dt, "hand"), W.to_storage(arr("a"), dt),
                        W.to_storage(arr("b"), dt), W.to_storage(arr("g"), dt))
         gl = np.array(ex["grad_last"], np.float32)[None]
-        for algo, cf, cb in ALGOS:
-            log(f"golden {dt} {algo}{cf}")
-            out, last, ga, gb, gh0 = run_pair(inp, algo, cf, cb)
+        for algo, cf, cb, wf, wb in ALGOS:
+            if aligned_only(algo, cf, cb, wf, wb, 2, dt):
+                continue
+            log(f"golden {dt} {algo}{cf} w{wf}")
+            out, last, ga, gb, gh0 = run_pair(inp, algo, cf, cb, wf, wb)
             assert np.array_equal(host(out), arr("out")), (dt, algo)
             assert np.array_equal(host(last)[0], np.array(ex["last"])), (dt, algo)
             assert np.array_equal(host(ga), arr("grad_a")), (dt, algo)
             assert np.array_equal(host(gb), arr("grad_b")), (dt, algo)
             assert np.array_equal(host(gh0)[0], np.array(ex["grad_h0"])), (dt, algo)
-            out, last, ga, gb, gh0 = run_pair(inp, algo, cf, cb, gl=gl)
+            out, last, ga, gb, gh0 = run_pair(inp, algo, cf, cb, wf, wb, gl=gl)
             w = ex["with_grad_last"]
             assert np.array_equal(host(ga)[0], np.array(w["grad_a"])), (dt, algo)
             assert np.array_equal(host(gb)[0], np.array(w["grad_b"])), (dt, algo)
             assert np.array_equal(host(gh0)[0], np.array(w["grad_h0"])), (dt, algo)
 
 
-@pytest.mark.parametrize("algo,cf,cb", ALGOS, ids=ALGO_IDS)
-def test_small_workload(algo, cf, cb):
+@pytest.mark.parametrize("algo,cf,cb,wf,wb", ALGOS, ids=ALGO_IDS)
+def test_small_workload(algo, cf, cb, wf, wb):
     """The B=2, T=256, D=64 fp32 workload, whole tensors, every algorithm."""
     inp = W.generate(W.WORKLOADS["small"], seed=0)
-    log(f"small {algo}{cf}")
-    check_against_oracle(inp, run_pair(inp, algo, cf, cb))
+    log(f"small {algo}{cf} w{wf}")
+    check_against_oracle(inp, run_pair(inp, algo, cf, cb, wf, wb))
 
 
 SHAPES = [(1, 1, 1), (1, 2, 3), (2, 63, 7), (2, 64, 8), (1, 65, 9), (3, 257, 64), (2, 300, 65),
@@ -109,9 +119,11 @@ def test_ragged_shapes_all_algos(B, T, D, dt):
     """Tails in T (partial chunks and tiles) and in D (partial vectors and
     lane blocks, unaligned rows), with an initial state and grad_last."""
     inp, h0, gl = W.random_inputs(B, T, D, dt, seed=B * 1000 + T * 10 + D, with_state=True)
-    for algo, cf, cb in ALGOS:
-        log(f"ragged B{B} T{T} D{D} {dt} {algo}{cf}")
-        check_against_oracle(inp, run_pair(inp, algo, cf, cb, h0=h0, gl=gl), h0=h0, gl=gl)
+    for algo, cf, cb, wf, wb in ALGOS:
+        if aligned_only(algo, cf, cb, wf, wb, D, dt):
+            continue
+        log(f"ragged B{B} T{T} D{D} {dt} {algo}{cf} w{wf}")
+        check_against_oracle(inp, run_pair(inp, algo, cf, cb, wf, wb, h0=h0, gl=gl), h0=h0, gl=gl)
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -163,13 +175,13 @@ def test_deterministic_and_paths_agree(dt):
     B, T, D = 2, 4096, 256
     inp = W.random_inputs(B, T, D, dt, seed=5, a_lo=0.9)
     runs = {}
-    for algo, cf, cb in ALGOS:
-        r1 = run_pair(inp, algo, cf, cb)
-        r2 = run_pair(inp, algo, cf, cb)
+    for algo, cf, cb, wf, wb in ALGOS:
+        r1 = run_pair(inp, algo, cf, cb, wf, wb)
+        r2 = run_pair(inp, algo, cf, cb, wf, wb)
         for x, y in zip(r1, r2):
-            assert torch.equal(x, y), f"{algo}{cf} not bitwise repeatable"
-        runs[(algo, cf)] = [host(x) for x in r1]
-    ref = runs[("seq", 0)]
+            assert torch.equal(x, y), f"{algo}{cf} w{wf} not bitwise repeatable"
+        runs[(algo, cf, wf)] = [host(x) for x in r1]
+    ref = runs[("seq", 0, 0)]
     worst = 0.0
     for key, r in runs.items():
         for x, y in zip(r, ref):
@@ -194,8 +206,8 @@ def test_identity_and_reset_steps():
         b = inp.f64("b")
         b[:, pads] = 0.0
         inp = W.Inputs(inp.workload, W.to_storage(a, dt), W.to_storage(b, dt), inp.g)
-        for algo, cf, cb in ALGOS:
-            out, last, ga, gb, _ = run_pair(inp, algo, cf, cb)
+        for algo, cf, cb, wf, wb in ALGOS:
+            out, last, ga, gb, _ = run_pair(inp, algo, cf, cb, wf, wb)
             o = host(out)
             assert np.array_equal(o[:, resets], W.storage_to_f64(inp.b, dt)[:, resets]), (dt, algo)
             if algo == "seq":
@@ -222,19 +234,19 @@ def test_caller_workspace_and_errors():
     B, T, D = 2, 700, 40
     inp = W.random_inputs(B, T, D, "bf16", seed=9)
     a, b = dev(inp.a, "bf16"), dev(inp.b, "bf16")
-    for algo, chunk in (("chunked", 64), ("fused", 256)):
-        o = lr.make_opts(algo=algo, chunk=chunk)
+    for algo, chunk, width in (("chunked", 64, 0), ("fused", 256, 8), ("fused", 64, 32)):
+        o = lr.make_opts(algo=algo, chunk=chunk, width=width)
         n = lr.scan_workspace_bytes(B, T, D, lr.BF16, o)
         ws = torch.empty(n, dtype=torch.uint8, device="cuda")
         out = torch.empty_like(a)
         last = torch.empty((B, D), device="cuda")
-        opts = lr.make_opts(algo=algo, chunk=chunk, workspace=ws)
+        opts = lr.make_opts(algo=algo, chunk=chunk, workspace=ws, width=width)
         lr.scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), last.data_ptr(), B, T, D,
                        lr.BF16, torch.cuda.current_stream().cuda_stream, opts)
         torch.cuda.synchronize()
         h, hl = oracle.scan_fwd(inp.f64("a"), inp.f64("b"))
         check_close("out", host(out), h, "bf16")
-        small = lr.make_opts(algo=algo, chunk=chunk, workspace=ws[: n // 2])
+        small = lr.make_opts(algo=algo, chunk=chunk, workspace=ws[: n // 2], width=width)
         with pytest.raises(lr.LRScanError):
             lr.scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), None, B, T, D, lr.BF16,
                            torch.cuda.current_stream().cuda_stream, small)
