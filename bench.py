@@ -41,6 +41,38 @@ def algorithmic_bytes(B, T, D, s):
     return 3 * s * N + 4 * B * D, 5 * s * N
 
 
+def kernel_sources_sha256():
+    """Hash of the fused kernels' sources: counter readings are only valid for them."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_recurrence_sequence_diag_amd", "csrc")
+    for f in ("fused.hip", "device.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, direction, algo):
+    """HBM bytes per launch of the dominant kernel from the rocprofv3 counter
+    runs recorded in profiles/hbm_traffic.json (FETCH_SIZE and WRITE_SIZE in
+    KiB per dispatch, each scaled by what the counter reads for a plain copy of
+    known size).  None when no reading exists for this kernel or its sources
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if algo != "fused" or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != kernel_sources_sha256():
+        return None
+    e = rec.get("workloads", {}).get(workload, {}).get(direction)
+    if not e:
+        return None
+    cf = rec["copy_factor"]
+    kib = e["fetch_kib"] * cf["FETCH_SIZE"] + e["write_kib"] * cf["WRITE_SIZE"]
+    return round(kib * 1024)
+
+
 def cpu_baseline(inp, budget_s=10.0):
     """The fp64 oracle on the host cores, on the same workload (whole, or as
     many whole passes as fit in about `budget_s`).  Returns a dict."""
@@ -82,6 +114,8 @@ def main():
     ap.add_argument("--fwd-width", type=int, default=0)
     ap.add_argument("--bwd-width", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (the reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -98,6 +132,19 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(2)
+
+    if args.calibrate_copy:
+        # A plain copy of known size: its HBM byte counters (FETCH_SIZE, WRITE_SIZE)
+        # give the factor that turns counter readings into bytes.
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read_per_copy": 4 * n,
+                          "bytes_written_per_copy": 4 * n, "copies": args.steps}))
+        return
 
     wl = W.WORKLOADS[args.workload]
     inp = W.generate(wl, seed=0)
@@ -119,35 +166,44 @@ def main():
     fo = lr.make_opts(algo=args.algo, chunk=args.fwd_chunk, width=args.fwd_width)
     bo = lr.make_opts(algo=args.algo, chunk=args.bwd_chunk, width=args.bwd_width)
 
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
+    def fwd():
         lr.scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), last.data_ptr(), B, T, D, dt,
                        sh, fo)
-        if ev:
-            ev[1].record(stream)
+
+    def bwd():
         lr.scan_bwd_ex(a.data_ptr(), out.data_ptr(), g.data_ptr(), None, ga.data_ptr(),
                        gb.data_ptr(), B, T, D, dt, sh, bo)
-        if ev:
-            ev[2].record(stream)
 
     for _ in range(args.warmup):
-        step()
+        fwd()
+        bwd()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # timed region: K whole steps back to back, HIP events on the launch stream
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
+    for _ in range(args.steps):
+        fwd()
+        bwd()
     t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    ms_per_step = total_ms / args.steps
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+
+    # per-kernel average launch duration: K launches of one direction back to
+    # back between two events (each call is one kernel launch)
+    def kernel_ms(fn):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    fwd_ms = kernel_ms(fwd)
+    bwd_ms = kernel_ms(bwd)
 
     fb, bb = algorithmic_bytes(B, T, D, wl.itemsize)
     value = (fb + bb) / (ms_per_step * 1e-3) / 1e9
@@ -204,6 +260,7 @@ def main():
             "traffic": None,
         },
     }
+    res["roofline"]["traffic"] = measured_traffic(wl.name, dom, names[bwd_algo if dom == "backward" else fwd_algo])
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(res), flush=True)
