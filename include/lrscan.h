@@ -84,6 +84,11 @@ typedef struct {
     size_t workspace_bytes; /* size of `workspace` */
     const float* h0;        /* [B, D] initial state, or NULL for zero (forward and backward) */
     float* grad_h0;         /* [B, D] output of the backward, or NULL */
+    int polls;              /* FUSED only: times a tile polls for its predecessors' published
+                               results before it stops waiting and derives the missing ones
+                               from the inputs itself; <= 0: the library default.  Results
+                               are bitwise the same for every value (1 exercises the
+                               derivation path). */
 } lrscan_opts;
 
 /*

@@ -45,6 +45,7 @@ class Opts(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("h0", ctypes.c_void_p),
         ("grad_h0", ctypes.c_void_p),
+        ("polls", ctypes.c_int),
     ]
 
 
@@ -221,7 +222,7 @@ def _check_state(name, t, ref):
         raise ValueError(f"{name} must be a contiguous float32 [B, D] tensor on a's device")
 
 
-def make_opts(algo="auto", chunk=0, h0=None, grad_h0=None, workspace=None, width=0):
+def make_opts(algo="auto", chunk=0, h0=None, grad_h0=None, workspace=None, width=0, polls=0):
     o = Opts()
     o.algo = ALGOS[algo] if isinstance(algo, str) else int(algo)
     o.chunk = int(chunk)
@@ -230,10 +231,11 @@ def make_opts(algo="auto", chunk=0, h0=None, grad_h0=None, workspace=None, width
     o.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     o.h0 = _ptr(h0)
     o.grad_h0 = _ptr(grad_h0)
+    o.polls = int(polls)
     return o
 
 
-def scan(a, b, h0=None, algo="auto", chunk=0, with_last=True, width=0):
+def scan(a, b, h0=None, algo="auto", chunk=0, with_last=True, width=0, polls=0):
     """Forward scan.  Returns (out, last); out has a's dtype, last is float32 [B, D]."""
     torch = _torch()
     _check_seq("a", a)
@@ -244,12 +246,13 @@ def scan(a, b, h0=None, algo="auto", chunk=0, with_last=True, width=0):
     last = torch.empty((B, D), device=a.device, dtype=torch.float32) if with_last else None
     with torch.cuda.device(a.device):
         scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), _ptr(last), B, T, D,
-                    dtype_code(a.dtype), _stream(a), make_opts(algo, chunk, h0=h0, width=width))
+                    dtype_code(a.dtype), _stream(a),
+                    make_opts(algo, chunk, h0=h0, width=width, polls=polls))
     return out, last
 
 
 def scan_backward(a, out, grad_out, grad_last=None, h0=None, algo="auto", chunk=0,
-                  need_grad_h0=False, width=0):
+                  need_grad_h0=False, width=0, polls=0):
     """Reverse-time adjoint.  Returns (grad_a, grad_b, grad_h0 or None)."""
     torch = _torch()
     _check_seq("a", a)
@@ -264,7 +267,7 @@ def scan_backward(a, out, grad_out, grad_last=None, h0=None, algo="auto", chunk=
     with torch.cuda.device(a.device):
         scan_bwd_ex(a.data_ptr(), out.data_ptr(), grad_out.data_ptr(), _ptr(grad_last),
                     grad_a.data_ptr(), grad_b.data_ptr(), B, T, D, dtype_code(a.dtype), _stream(a),
-                    make_opts(algo, chunk, h0=h0, grad_h0=grad_h0, width=width))
+                    make_opts(algo, chunk, h0=h0, grad_h0=grad_h0, width=width, polls=polls))
     return grad_a, grad_b, grad_h0
 
 

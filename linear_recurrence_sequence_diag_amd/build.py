@@ -24,6 +24,9 @@ HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
     # no packed-fp32 instructions in any generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # arithmetic exactly as written: no implicit multiply-add contraction, so
+    # two code paths that spell out the same operations round identically
+    "-ffp-contract=off",
     "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -251,7 +251,7 @@ LRSCAN_API int scan_fwd_ex(const void* a, const void* b, void* out, float* last,
         }
         case LRSCAN_ALGO_FUSED:
             return fused_status(launch_fused_fwd(s, r.width, r.chunk, a, b, out, last, h0,
-                                                 ws.ptr, ws.bytes, ws.init, hs),
+                                                 ws.ptr, ws.bytes, ws.init, opts ? opts->polls : 0, hs),
                                 ws, opts, hs);
     }
     return LRSCAN_ERR_ALGO;
@@ -296,7 +296,7 @@ LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
         case LRSCAN_ALGO_FUSED:
             return fused_status(launch_fused_bwd(s, r.width, r.chunk, a, out, grad_out, grad_last,
                                                  h0, grad_a, grad_b, grad_h0, ws.ptr, ws.bytes,
-                                                 ws.init, hs),
+                                                 ws.init, opts ? opts->polls : 0, hs),
                                 ws, opts, hs);
     }
     return LRSCAN_ERR_ALGO;

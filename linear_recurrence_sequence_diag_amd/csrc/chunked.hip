@@ -241,9 +241,12 @@ __global__ __launch_bounds__(kBlk) void reverse_chunk_replay_kernel(
             const int64_t t = top - u;
             if (t >= t_begin) {
                 RowOut<DT> oa, ob;
+                // lambda_t = g_t + a_{t+1}*lambda_{t+1} as one fma inside a
+                // block of rows; across blocks carry[] holds the product
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
-                    const float lam = rg[u].get(j) + carry[j];
+                    const float an = u > 0 ? ra[u > 0 ? u - 1 : 0].get(j) : 1.0f;
+                    const float lam = fmaf(an, carry[j], rg[u].get(j));
                     float hp;
                     if (t >= 1)
                         hp = rh[u].get(j);
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(kBlk) void reverse_chunk_replay_kernel(
                         hp = (h0 && j < ci.nvalid) ? h0[ci.bi * D + ci.d0 + j] : 0.0f;
                     ob.v[j] = lam;
                     oa.v[j] = lam * hp;
-                    carry[j] = ra[u].get(j) * lam;
+                    carry[j] = (u == kU - 1 || t == t_begin) ? ra[u].get(j) * lam : lam;
                 }
                 store_row<DT, ALIGNED>(grad_a, base + (size_t)t * D, ci.nvalid, oa);
                 store_row<DT, ALIGNED>(grad_b, base + (size_t)t * D, ci.nvalid, ob);

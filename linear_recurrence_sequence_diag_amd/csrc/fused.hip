@@ -24,7 +24,10 @@
 //    made deterministic: every H equals the plain chained value
 //    H_k = fma(P_k, H_{k-1}, Q_k) whatever the timing, so results do not
 //    depend on scheduling.  A tile only waits on tiles with smaller tickets,
-//    which are already resident or finished, so the chain always drains.
+//    which are already resident or finished, so the chain always drains; and
+//    a tile that has polled long enough derives the maps it is missing from
+//    the inputs itself (bitwise the values their owners publish), so no wait
+//    is unbounded and no result depends on which path was taken.
 //  * Replay: each thread rescans its rows from registers, starting from the
 //    state entering its segment, and writes the outputs once.
 //
@@ -43,7 +46,11 @@ namespace lrscan {
 
 namespace {
 
-constexpr uint32_t kSpinLimit = 1u << 20;
+// Look-back polls before a tile stops waiting and derives the predecessor
+// maps it is missing (normal waits take a few polls; this bound only matters
+// when a predecessor's workgroup is descheduled for a long time).
+constexpr uint32_t kDefaultPolls = 1024;
+
 
 // Workspace of the fused form: a 256-byte header, then two regions of equal
 // size.  A region holds nC ticket counters (each in its own 128-byte line),
@@ -122,6 +129,11 @@ struct Cfg {
     static constexpr int CT = WAVES * RG * NR;
     static_assert(TPR == 8 || TPR == 16 || TPR == 32, "row width");
     static_assert(W <= NT, "one look-back column per thread");
+    // waves per SIMD the register budget is held to (the forward keeps two
+    // input arrays of NR rows in registers through the look-back, the
+    // backward three)
+    static constexpr int OCC_F = NR <= 8 ? 3 : 2;
+    static constexpr int OCC_B = NR <= 4 ? (TPR > 8 ? 4 : 3) : (NR <= 8 && TPR > 8 ? 3 : 2);
 };
 
 struct Dims {
@@ -193,36 +205,61 @@ __device__ __forceinline__ Ticket take_ticket(const Scratch& sc) {
 
 // Restore the all-ones state of this ticket's share of the words the
 // previous launch wrote in the region this launch does not use.
-__device__ __forceinline__ void clear_share(const Scratch& sc, const Ticket& t, int nthreads) {
-    uint32_t* other = sc.region[t.phase ^ 1u];
+__device__ __forceinline__ void clear_share(const Scratch& sc, uint32_t phase,
+                                            unsigned long long nclear, int nthreads, uint32_t ticket) {
+    uint32_t* other = sc.region[phase ^ 1u];
     const unsigned long long stride = (unsigned long long)sc.total_tiles * nthreads;
-    for (unsigned long long i = (unsigned long long)t.ticket * nthreads + threadIdx.x; i < t.nclear;
+    for (unsigned long long i = (unsigned long long)ticket * nthreads + threadIdx.x; i < nclear;
          i += stride)
         other[i] = kEmpty;
+}
+
+// Largest `v` over the active lanes of the wavefront (wave-uniform result).
+__device__ __forceinline__ int wave_max_active(int v) {
+    unsigned long long act = __ballot(1);
+    int r = 0;
+    while (act) {
+        const int lane = __builtin_ctzll(act);
+        const int u = __shfl(v, lane, kWave);
+        r = u > r ? u : r;
+        act &= act - 1;
+    }
+    return uniform(r);
 }
 
 // Carry entering tile k of a chain (forward: DIR = -1 looks at k-1, k-2, ...;
 // reverse: DIR = +1 looks at k+1, k+2, ...).  `base0` is the carry entering the
 // chain (h0 forward, grad_last reverse).  The nearest published inclusive
-// state within the window is taken and the maps of the tiles in between are
-// applied to it oldest first, so the result is the plain chained value.
-// Returns NaN if a wait ever exceeded the spin limit.
-template <int DIR, int LB>
+// state within a window of LB predecessors is taken and the maps of the tiles
+// in between are applied to it oldest first, so the result is the plain
+// chained value.
+//
+// The window is polled up to `polls` times.  After that the tile stops
+// waiting: it finds the nearest published state at any distance, and derives
+// every map in between that is not yet published itself, with `map_of(j)`,
+// from the inputs and bitwise equal to what tile j publishes.  So no tile
+// ever waits on a workgroup that has not started, whatever order the
+// hardware starts workgroups in, and results do not depend on which path
+// was taken.
+template <int DIR, int LB, class MapOf>
 __device__ float look_back(const unsigned long long* pqs, const uint32_t* hs, int k, int NK, int nS,
-                           int s, int W, int c, float base0) {
+                           int s, int W, int c, float base0, uint32_t polls, MapOf&& map_of) {
     const int span = DIR < 0 ? k : (NK - 1 - k);  // predecessors in the chain
     if (span == 0) return base0;
-    for (uint32_t spin = 0;; ++spin) {
+    // entry of predecessor i (0: the nearest): wave-uniform base + per-lane column
+    auto entry = [&](int i) -> size_t {
+        const int j = k + DIR * (1 + i);
+        return ((size_t)j * (size_t)nS + (size_t)s) * W + c;
+    };
+    for (uint32_t spin = 0; spin < polls; ++spin) {
         uint32_t hw[LB];
         unsigned long long pq[LB];
 #pragma unroll
         for (int i = 0; i < LB; ++i) {
-            const int j = k + DIR * (1 + i);
             if (i < span) {
-                // wave-uniform entry base + per-lane column
-                const size_t e = ((size_t)j * (size_t)nS + (size_t)s) * W;
-                hw[i] = peek_u32(hs + e + c);
-                pq[i] = peek_u64(pqs + e + c);
+                const size_t e = entry(i);
+                hw[i] = peek_u32(hs + e);
+                pq[i] = peek_u64(pqs + e);
             } else {
                 hw[i] = kEmpty;
                 pq[i] = ~0ull;
@@ -252,10 +289,72 @@ __device__ float look_back(const unsigned long long* pqs, const uint32_t* hs, in
                 if (i < depth) x = aff_apply(unpack_aff(pq[i]), x);
             return x;
         }
-        if (spin >= kSpinLimit) return __uint_as_float(0x7fc00000u);
         __builtin_amdgcn_s_sleep(1);
     }
+    // nearest published state at any distance (or the chain start) ...
+    int m = span;
+    float base = base0;
+    for (int i0 = 0; i0 < span && m == span; i0 += LB) {
+        uint32_t hw[LB];
+#pragma unroll
+        for (int i = 0; i < LB; ++i) hw[i] = i0 + i < span ? peek_u32(hs + entry(i0 + i)) : kEmpty;
+#pragma unroll
+        for (int i = 0; i < LB; ++i) {
+            if (m == span && hw[i] != kEmpty) {
+                m = i0 + i;
+                base = __uint_as_float(hw[i]);
+            }
+        }
+    }
+    // ... then the m maps in between, oldest first, published or derived
+    // The walk is wave-uniform, so a map that some lane has to derive is
+    // derived for the same tile in every lane at once (each for its own lane
+    // of the block), with wave-uniform row addresses.
+    float x = base;
+    const int m_max = wave_max_active(m);
+#pragma unroll 1
+    for (int i = m_max - 1; i >= 0; --i) {
+        const bool mine = i < m;
+        const unsigned long long w = mine ? peek_u64(pqs + entry(i)) : 0ull;
+        const bool need = mine && (uint32_t)w == kEmpty;
+        Aff a = unpack_aff(w);
+        if (__any(need)) {
+            const Aff dm = map_of(k + DIR * (1 + i));
+            if (need) a = dm;
+        }
+        if (mine) x = aff_apply(a, x);
+    }
+    return x;
 }
+
+// Pairwise reduction, in a fixed association, of the RG maps a wavefront's
+// row groups produce, fed one at a time in scan order: for RG a power of two
+// this is the balanced tree that the in-wavefront Hillis-Steele scan forms
+// for its last group, so the total is bitwise the same.
+template <int RG>
+struct TreeFold {
+    static constexpr int L = RG == 1 ? 1 : (RG == 2 ? 1 : (RG == 4 ? 2 : 3));  // pending levels
+    Aff st[L];
+    Aff top;
+    // g-th leaf (0-based): merge it with the pending left node of every level
+    // the leaf completes; the root lands in `top`
+    __device__ __forceinline__ void push(int g, Aff node) {
+        if (RG == 1) {
+            top = node;
+            return;
+        }
+#pragma unroll
+        for (int lvl = 0; lvl < L; ++lvl) {
+            if (((g >> lvl) & 1) == 0) {
+                st[lvl] = node;
+                return;
+            }
+            node = aff_then(st[lvl], node);
+        }
+        top = node;
+    }
+    __device__ __forceinline__ Aff total() const { return top; }
+};
 
 struct FwdArgs {
     const void* a;
@@ -265,6 +364,7 @@ struct FwdArgs {
     const float* h0;
     Scratch sc;
     Dims d;
+    uint32_t polls;
 };
 
 struct BwdArgs {
@@ -278,13 +378,92 @@ struct BwdArgs {
     float* grad_h0;
     Scratch sc;
     Dims d;
+    uint32_t polls;
 };
+
+// Map of tile j of series (bi, lane block) for lane `col`, derived from the
+// inputs in exactly the order the workgroup owning tile j computes it: NR
+// rows per thread, the in-wavefront scan over the RG row groups of each
+// wavefront, then the wavefronts in order.  Lanes past D are the identity.
+template <class C>
+__device__ Aff fwd_tile_map(const FwdArgs& x, int j, int bi, int col) {
+    constexpr int RG = C::RG, NR = C::NR;
+    Aff A = aff_identity();
+    if (col >= x.d.D) return A;
+    // wave-uniform row addresses, one 32-bit lane offset
+    const size_t rowbytes = (size_t)x.d.D * C::EB;
+    const char* a0 = static_cast<const char*>(x.a) + (size_t)bi * x.d.T * rowbytes;
+    const char* b0 = static_cast<const char*>(x.b) + (size_t)bi * x.d.T * rowbytes;
+    const uint32_t coff = (uint32_t)col * C::EB;
+#pragma unroll 1
+    for (int w = 0; w < C::WAVES; ++w) {
+        TreeFold<RG> tree;
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            Aff t = aff_identity();
+            const int r0 = j * C::CT + (w * RG + g) * NR;
+#pragma unroll 1
+            for (int i = 0; i < NR; ++i) {
+                const int r = r0 + i;
+                float at = 1.0f, bt = 0.0f;
+                if (r < x.d.T) {
+                    const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes);  // same tile in every lane
+                    at = Elem<C::DT>::load1(a0 + ro + coff, 0);
+                    bt = Elem<C::DT>::load1(b0 + ro + coff, 0);
+                }
+                t.p = at * t.p;
+                t.q = fmaf(at, t.q, bt);
+            }
+            tree.push(g, t);
+        }
+        A = aff_then(A, tree.total());
+    }
+    return unpack_aff(pack_aff(A));
+}
+
+// Reverse-time counterpart: rows in decreasing order, row groups from the
+// last to the first, wavefronts from the last to the first.
+template <class C>
+__device__ Aff bwd_tile_map(const BwdArgs& x, int j, int bi, int col) {
+    constexpr int RG = C::RG, NR = C::NR;
+    Aff A = aff_identity();
+    if (col >= x.d.D) return A;
+    const size_t rowbytes = (size_t)x.d.D * C::EB;
+    const char* a0 = static_cast<const char*>(x.a) + (size_t)bi * x.d.T * rowbytes;
+    const char* g0 = static_cast<const char*>(x.g) + (size_t)bi * x.d.T * rowbytes;
+    const uint32_t coff = (uint32_t)col * C::EB;
+#pragma unroll 1
+    for (int w = C::WAVES - 1; w >= 0; --w) {
+        TreeFold<RG> tree;
+#pragma unroll
+        for (int g = RG - 1; g >= 0; --g) {
+            Aff t = aff_identity();
+            const int r0 = j * C::CT + (w * RG + g) * NR;
+#pragma unroll 1
+            for (int i = NR - 1; i >= 0; --i) {
+                const int r = r0 + i;
+                float at = 1.0f, gt = 0.0f;
+                if (r < x.d.T) {
+                    const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes);  // same tile in every lane
+                    at = Elem<C::DT>::load1(a0 + ro + coff, 0);
+                    gt = Elem<C::DT>::load1(g0 + ro + coff, 0);
+                }
+                t.p = at * t.p;
+                t.q = at * (t.q + gt);
+            }
+            tree.push(RG - 1 - g, t);
+        }
+        A = aff_then(A, tree.total());
+    }
+    return unpack_aff(pack_aff(A));
+}
 
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
 template <class C, bool ALIGNED>
-__global__ __launch_bounds__(C::NT) void fused_fwd_kernel(FwdArgs x) {
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC_F)))
+void fused_fwd_kernel(FwdArgs x) {
     constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
     __shared__ Aff s_excl[WAVES][V][kWave];
     __shared__ Aff s_wtot[WAVES][W];
@@ -312,7 +491,7 @@ __global__ __launch_bounds__(C::NT) void fused_fwd_kernel(FwdArgs x) {
         ra[i] = load_vec<C::DT, ALIGNED>(pa, off, g.nvalid, 1.0f);
         rb[i] = load_vec<C::DT, ALIGNED>(pb, off, g.nvalid, 0.0f);
     }
-    clear_share(x.sc, tk, C::NT);
+    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
 
     // summary of this thread's rows, per lane (rows outer, so only one row
     // is widened to fp32 at a time), then the wavefront scan over its RG
@@ -347,13 +526,14 @@ __global__ __launch_bounds__(C::NT) void fused_fwd_kernel(FwdArgs x) {
         opaque(rb[i]);
     }
     __syncthreads();
+    const uint32_t phase = tk.phase;
 
     // tile map, publication, look-back: one column per thread
     if (tid < W) {
         const int c = tid;
         const unsigned long long* pqs =
-            reinterpret_cast<const unsigned long long*>(x.sc.region[tk.phase] + x.sc.ctr_words);
-        const uint32_t* hs = x.sc.region[tk.phase] + x.sc.ctr_words + 2 * x.sc.entries;
+            reinterpret_cast<const unsigned long long*>(x.sc.region[phase] + x.sc.ctr_words);
+        const uint32_t* hs = x.sc.region[phase] + x.sc.ctr_words + 2 * x.sc.entries;
         Aff A = aff_identity();
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) A = aff_then(A, s_wtot[w][c]);
@@ -362,7 +542,8 @@ __global__ __launch_bounds__(C::NT) void fused_fwd_kernel(FwdArgs x) {
         if (more) publish_u64(const_cast<unsigned long long*>(pqs) + o, pack_aff(A));
         const int dl = g.dcol0 + c;
         const float base0 = (x.h0 && dl < d.D) ? x.h0[(size_t)g.bi * d.D + dl] : 0.0f;
-        const float hin = look_back<-1, C::LB>(pqs, hs, g.k, d.NK, d.nS, g.s, W, c, base0);
+        const float hin = look_back<-1, C::LB>(pqs, hs, g.k, d.NK, d.nS, g.s, W, c, base0, x.polls,
+                                               [&](int j) { return fwd_tile_map<C>(x, j, g.bi, dl); });
         if (more) publish_u32(const_cast<uint32_t*>(hs) + o, publishable(aff_apply(A, hin)));
         s_hin[c] = hin;
     }
@@ -400,7 +581,8 @@ __global__ __launch_bounds__(C::NT) void fused_fwd_kernel(FwdArgs x) {
 // reverse time (backward)
 // ---------------------------------------------------------------------------
 template <class C, bool ALIGNED>
-__global__ __launch_bounds__(C::NT) void fused_bwd_kernel(BwdArgs x) {
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC_B)))
+void fused_bwd_kernel(BwdArgs x) {
     constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
     __shared__ Aff s_excl[WAVES][V][kWave];
     __shared__ Aff s_wtot[WAVES][W];
@@ -436,7 +618,7 @@ __global__ __launch_bounds__(C::NT) void fused_bwd_kernel(BwdArgs x) {
         rg_[i] = load_vec<C::DT, ALIGNED>(pg, off, g.nvalid, 0.0f);
         rh[i] = load_vec<C::DT, ALIGNED>(ph, hoff, g.nvalid, 0.0f);
     }
-    clear_share(x.sc, tk, C::NT);
+    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
 
     // reverse summary: the map from the carry entering the segment on the
     // right to the carry a_s*lambda_s leaving its first row s
@@ -470,12 +652,13 @@ __global__ __launch_bounds__(C::NT) void fused_bwd_kernel(BwdArgs x) {
         opaque(rg_[i]);
     }
     __syncthreads();
+    const uint32_t phase = tk.phase;
 
     if (tid < W) {
         const int c = tid;
         const unsigned long long* pqs =
-            reinterpret_cast<const unsigned long long*>(x.sc.region[tk.phase] + x.sc.ctr_words);
-        const uint32_t* hs = x.sc.region[tk.phase] + x.sc.ctr_words + 2 * x.sc.entries;
+            reinterpret_cast<const unsigned long long*>(x.sc.region[phase] + x.sc.ctr_words);
+        const uint32_t* hs = x.sc.region[phase] + x.sc.ctr_words + 2 * x.sc.entries;
         Aff A = aff_identity();
 #pragma unroll
         for (int w = WAVES - 1; w >= 0; --w) A = aff_then(A, s_wtot[w][c]);
@@ -484,33 +667,39 @@ __global__ __launch_bounds__(C::NT) void fused_bwd_kernel(BwdArgs x) {
         if (more) publish_u64(const_cast<unsigned long long*>(pqs) + o, pack_aff(A));
         const int dl = g.dcol0 + c;
         const float base0 = (x.grad_last && dl < d.D) ? x.grad_last[(size_t)g.bi * d.D + dl] : 0.0f;
-        const float cin = look_back<+1, C::LB>(pqs, hs, g.k, d.NK, d.nS, g.s, W, c, base0);
+        const float cin = look_back<+1, C::LB>(pqs, hs, g.k, d.NK, d.nS, g.s, W, c, base0, x.polls,
+                                               [&](int j) { return bwd_tile_map<C>(x, j, g.bi, dl); });
         if (more) publish_u32(const_cast<uint32_t*>(hs) + o, publishable(aff_apply(A, cin)));
         s_cin[c] = cin;
     }
     __syncthreads();
 
-    float carry[V];
+    // lam[j] starts as the carry a_{s+1}*lambda_{s+1} entering this thread's
+    // last row from the right; each row then takes
+    // lambda_t = g_t + a_{t+1}*lambda_{t+1} as one fma with the a of the row
+    // after it (the carry itself for the first row processed)
+    float lam[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         const int col = cg * V + j;
         float xv = s_cin[col];
         for (int w = WAVES - 1; w > wave; --w) xv = aff_apply(s_wtot[w][col], xv);
-        carry[j] = aff_apply(s_excl[wave][j][l], xv);
+        lam[j] = aff_apply(s_excl[wave][j][l], xv);
     }
 #pragma unroll
     for (int i = NR - 1; i >= 0; --i) {
         if (i < g.nrows) {
             const int row = g.row0 + i;
+            const bool after = i + 1 < NR && i + 1 < g.nrows;  // row t+1 is in this segment
             RowOut<C::DT> oa, ob;
 #pragma unroll
             for (int j = 0; j < V; ++j) {
-                const float lam = rg_[i].get(j) + carry[j];
+                const float an = (i + 1 < NR && after) ? ra[i + 1 < NR ? i + 1 : i].get(j) : 1.0f;
+                lam[j] = fmaf(an, lam[j], rg_[i].get(j));
                 float hp = rh[i].get(j);
                 if (row == 0) hp = (x.h0 && j < g.nvalid) ? x.h0[(size_t)g.bi * d.D + g.d0 + j] : 0.0f;
-                ob.v[j] = lam;
-                oa.v[j] = lam * hp;
-                carry[j] = ra[i].get(j) * lam;
+                ob.v[j] = lam[j];
+                oa.v[j] = lam[j] * hp;
             }
             const uint32_t off = row_off(g, row, d.T, rowbytes);
             store_vec<C::DT, ALIGNED>(pga, off, g.nvalid, oa);
@@ -520,7 +709,7 @@ __global__ __launch_bounds__(C::NT) void fused_bwd_kernel(BwdArgs x) {
     if (x.grad_h0 && g.nrows > 0 && g.row0 == 0) {
 #pragma unroll
         for (int j = 0; j < V; ++j)
-            if (j < g.nvalid) x.grad_h0[(size_t)g.bi * d.D + g.d0 + j] = carry[j];
+            if (j < g.nvalid) x.grad_h0[(size_t)g.bi * d.D + g.d0 + j] = ra[0].get(j) * lam[j];
     }
 }
 
@@ -622,9 +811,9 @@ hipError_t prepare(void* ws, size_t ws_bytes, bool init, const Layout& L, hipStr
 }
 
 template <int DT, int TPR, int NR, int WAVES, int LB, bool AL>
-void launch_fwd_cfg(const FwdArgs& x, hipStream_t st) {
+void launch_fwd_cfg(const FwdArgs& x0, hipStream_t st) {
     using C = Cfg<DT, TPR, NR, WAVES, LB>;
-    hipLaunchKernelGGL((fused_fwd_kernel<C, AL>), dim3(x.sc.total_tiles), dim3(C::NT), 0, st, x);
+    hipLaunchKernelGGL((fused_fwd_kernel<C, AL>), dim3(x0.sc.total_tiles), dim3(C::NT), 0, st, x0);
 }
 
 template <int DT, int TPR, int NR, int WAVES, int LB, bool AL>
@@ -708,7 +897,7 @@ size_t fused_workspace_bytes(const Shape& s, int width, int tile) {
 
 hipError_t launch_fused_fwd(const Shape& s, int width, int tile, const void* a, const void* b,
                             void* out, float* last, const float* h0, void* ws, size_t ws_bytes,
-                            bool init, hipStream_t st) {
+                            bool init, int polls, hipStream_t st) {
     const TileCfg* c = find_cfg(0, width, tile);
     if (!c) return hipErrorInvalidValue;
     const Layout L = layout_of(s, width, tile);
@@ -721,6 +910,7 @@ hipError_t launch_fused_fwd(const Shape& s, int width, int tile, const void* a, 
     x.last = last;
     x.h0 = h0;
     x.d = Dims{(int)s.T, (int)s.D, L.nW, L.nS, L.NK};
+    x.polls = polls > 0 ? (uint32_t)polls : kDefaultPolls;
     const void* ptrs[3] = {a, b, out};
     const bool al = rows_aligned(s, ptrs, 3);
     const bool ok = s.dtype == DT_F32 ? fwd_dispatch<DT_F32>(*c, al, x, st)
@@ -732,7 +922,7 @@ hipError_t launch_fused_fwd(const Shape& s, int width, int tile, const void* a, 
 hipError_t launch_fused_bwd(const Shape& s, int width, int tile, const void* a, const void* out,
                             const void* g, const float* grad_last, const float* h0, void* grad_a,
                             void* grad_b, float* grad_h0, void* ws, size_t ws_bytes, bool init,
-                            hipStream_t st) {
+                            int polls, hipStream_t st) {
     const TileCfg* c = find_cfg(1, width, tile);
     if (!c) return hipErrorInvalidValue;
     const Layout L = layout_of(s, width, tile);
@@ -748,6 +938,7 @@ hipError_t launch_fused_bwd(const Shape& s, int width, int tile, const void* a, 
     x.grad_b = grad_b;
     x.grad_h0 = grad_h0;
     x.d = Dims{(int)s.T, (int)s.D, L.nW, L.nS, L.NK};
+    x.polls = polls > 0 ? (uint32_t)polls : kDefaultPolls;
     const void* ptrs[5] = {a, out, g, grad_a, grad_b};
     const bool al = rows_aligned(s, ptrs, 5);
     const bool ok = s.dtype == DT_F32 ? bwd_dispatch<DT_F32>(*c, al, x, st)

@@ -53,13 +53,15 @@ size_t fused_workspace_bytes(const Shape& s, int width, int tile);
 // `ws` holds the fused form's header and two scratch regions; `init` must be
 // true the first time a buffer is used (and whenever its contents were
 // disturbed): the launcher then enqueues one initialisation kernel first.
-// Every launch on a buffer must use the same `ws_bytes`.
+// Every launch on a buffer must use the same `ws_bytes`.  `polls` (<= 0: the
+// default) bounds how often a tile polls for its predecessors before it
+// derives their missing maps itself; results are bitwise the same either way.
 hipError_t launch_fused_fwd(const Shape& s, int width, int tile, const void* a, const void* b,
                             void* out, float* last, const float* h0, void* ws, size_t ws_bytes,
-                            bool init, hipStream_t st);
+                            bool init, int polls, hipStream_t st);
 hipError_t launch_fused_bwd(const Shape& s, int width, int tile, const void* a, const void* out,
                             const void* g, const float* grad_last, const float* h0, void* grad_a,
                             void* grad_b, float* grad_h0, void* ws, size_t ws_bytes, bool init,
-                            hipStream_t st);
+                            int polls, hipStream_t st);
 
 }  // namespace lrscan

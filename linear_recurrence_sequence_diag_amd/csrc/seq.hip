@@ -123,13 +123,17 @@ __global__ __launch_bounds__(kSeqBlock) void seq_bwd_kernel(
             const int64_t t = top - u;
             if (t >= 0) {
                 RowOut<DT> oa, ob;
+                // lambda_t = g_t + a_{t+1}*lambda_{t+1}: one fma with the a of
+                // row t+1 inside a block; across blocks carry[] holds the
+                // product a_{t+1}*lambda_{t+1}
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
-                    const float lam = cg[u].get(j) + carry[j];
+                    const float an = u > 0 ? ca[u > 0 ? u - 1 : 0].get(j) : 1.0f;
+                    const float lam = fmaf(an, carry[j], cg[u].get(j));
                     const float hp = (t >= 1) ? ch[u].get(j) : hinit[j];
                     ob.v[j] = lam;
                     oa.v[j] = lam * hp;
-                    carry[j] = ca[u].get(j) * lam;
+                    carry[j] = (u == U - 1 || t == 0) ? ca[u].get(j) * lam : lam;
                 }
                 store_row<DT, ALIGNED>(grad_a, base + (size_t)t * D, nvalid, oa);
                 store_row<DT, ALIGNED>(grad_b, base + (size_t)t * D, nvalid, ob);

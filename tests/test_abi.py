@@ -104,3 +104,28 @@ def test_workspace_sizes_and_auto_choice():
             assert algo in (lr.ALGO_SEQ, lr.ALGO_CHUNKED, lr.ALGO_FUSED)
             o = lr.make_opts(algo=algo, chunk=chunk, width=width)
             assert lr.scan_workspace_bytes(8, 2048, 2560, dt, o) >= 0
+
+
+def test_options_struct_layout_matches_the_header(tmp_path):
+    """The binding's mirror of lrscan_opts has the C struct's size and field
+    offsets (checked by compiling the header with the host C compiler)."""
+    import shutil
+    import subprocess
+    lr = _lib()
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    names = [f[0] for f in lr.Opts._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"lrscan.h\"\n"
+                   "int main(void) {\n  printf(\"%zu\\n\", sizeof(lrscan_opts));\n" +
+                   "".join(f"  printf(\"%zu\\n\", offsetof(lrscan_opts, {n}));\n" for n in names) +
+                   "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(lr.Opts)
+    for n, off in zip(names, vals[1:]):
+        assert getattr(lr.Opts, n).offset == off, n

@@ -190,6 +190,35 @@ def test_deterministic_and_paths_agree(dt):
     assert worst < (1e-4 if dt == "f32" else 2e-2)
 
 
+FUSED = [c for c in ALGOS if c[0] == "fused"]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,D", [(2, 4096, 256), (3, 1000, 201), (1, 20000, 64)],
+                         ids=["B2T4096D256", "B3T1000D201", "B1T20000D64"])
+def test_lookback_derivation_is_bitwise_identical(B, T, D, dt):
+    """With a single poll, a fused tile whose predecessors have not published
+    yet derives their maps from the inputs (the path taken when a
+    predecessor's workgroup stays descheduled).  Every output must be bitwise
+    the one the default, waiting, path gives, with h0 and grad_last set."""
+    inp, h0n, gln = W.random_inputs(B, T, D, dt, seed=11, a_lo=0.9, with_state=True)
+    a, b, g = dev(inp.a, dt), dev(inp.b, dt), dev(inp.g, dt)
+    h0, gl = dev_f32(h0n), dev_f32(gln)
+    for algo, cf, cb, wf, wb in FUSED:
+        if aligned_only(algo, cf, cb, wf, wb, D, dt):
+            continue
+        res = []
+        for polls in (0, 1):
+            out, last = lr.scan(a, b, h0=h0, algo=algo, chunk=cf, width=wf, polls=polls)
+            ga, gb, gh0 = lr.scan_backward(a, out, g, grad_last=gl, h0=h0, algo=algo, chunk=cb,
+                                           need_grad_h0=True, width=wb, polls=polls)
+            torch.cuda.synchronize()
+            res.append((out, last, ga, gb, gh0))
+        for name, x, y in zip(("out", "last", "grad_a", "grad_b", "grad_h0"), *res):
+            assert torch.equal(x, y), f"fused f{cf}w{wf} b{cb}w{wb}: {name} differs with polls=1"
+    log(f"{dt} B{B} T{T} D{D}: derived look-back maps bitwise equal on {len(FUSED)} configs")
+
+
 def test_identity_and_reset_steps():
     """a = 0 steps restart the scan bit for bit on every path; a = 1 steps
     carry the state unchanged bit for bit on the sequential path (chunked
