@@ -50,6 +50,7 @@ def build(force: bool = False) -> str:
 
 
 _D = ctypes.POINTER(ctypes.c_double)
+_U8 = ctypes.POINTER(ctypes.c_uint8)
 _I = ctypes.c_int64
 
 
@@ -66,16 +67,17 @@ def _load():
                 path = build()
             lib = ctypes.CDLL(path)
             sigs = {
-                "oracle_scan_fwd": [_I, _I, _I, _D, _D, _D, _D, _D],
-                "oracle_scan_bwd": [_I, _I, _I, _D, _D, _D, _D, _D, _D, _D, _D],
+                "oracle_scan_fwd": [_I, _I, _I, _D, _D, _D, _U8, _D, _D],
+                "oracle_scan_bwd": [_I, _I, _I, _D, _D, _D, _D, _D, _U8, _D, _D, _D],
                 "oracle_chunk_summary": [_I, _I, _I, _I, _D, _D, _D, _D],
                 "oracle_chunk_prefix": [_I, _I, _I, _D, _D, _D, _D, _D],
                 "oracle_chunk_replay": [_I, _I, _I, _I, _D, _D, _D, _D, _D],
                 "oracle_reverse_chunk_summary": [_I, _I, _I, _I, _D, _D, _D, _D],
                 "oracle_reverse_chunk_prefix": [_I, _I, _I, _D, _D, _D, _D, _D],
                 "oracle_reverse_chunk_replay": [_I, _I, _I, _I, _D, _D, _D, _D, _D, _D, _D],
-                "oracle_parallel_fwd": [_I, _I, _I, _D, _D, _D, _D, _D, ctypes.c_int],
-                "oracle_parallel_bwd": [_I, _I, _I, _D, _D, _D, _D, _D, _D, _D, _D, ctypes.c_int],
+                "oracle_parallel_fwd": [_I, _I, _I, _D, _D, _D, _U8, _D, _D, ctypes.c_int],
+                "oracle_parallel_bwd": [_I, _I, _I, _D, _D, _D, _D, _D, _U8, _D, _D, _D,
+                                        ctypes.c_int],
             }
             for name, args in sigs.items():
                 fn = getattr(lib, name)
@@ -95,7 +97,9 @@ def _f64(x, shape=None):
 
 
 def _p(arr):
-    return None if arr is None else arr.ctypes.data_as(_D)
+    if arr is None:
+        return None
+    return arr.ctypes.data_as(_U8 if arr.dtype == np.uint8 else _D)
 
 
 def _bdt(a):
@@ -104,26 +108,40 @@ def _bdt(a):
     return a.shape
 
 
-def scan_fwd(a, b, h0=None, threads: int = 1):
-    """Forward scan in fp64.  Returns (out [B,T,D], last [B,D])."""
+def _mask(reset, B, T):
+    """[B, T] segment-start mask as contiguous uint8 (None stays None)."""
+    if reset is None:
+        return None
+    m = np.ascontiguousarray(np.asarray(reset), dtype=np.uint8)
+    if m.shape != (B, T):
+        raise ValueError(f"reset mask has shape {m.shape}, expected {(B, T)}")
+    return m
+
+
+def scan_fwd(a, b, h0=None, threads: int = 1, reset=None):
+    """Forward scan in fp64.  Returns (out [B,T,D], last [B,D]).  ``reset``
+    ([B, T], nonzero = a segment starts there) drops the entering state."""
     a = _f64(a)
     B, T, D = _bdt(a)
     b = _f64(b, a.shape)
     h0 = _f64(h0, (B, D))
+    rm = _mask(reset, B, T)
     out = np.empty((B, T, D))
     last = np.empty((B, D))
     lib = _load()
     if threads > 1:
-        rc = lib.oracle_parallel_fwd(B, T, D, _p(a), _p(b), _p(h0), _p(out), _p(last), threads)
+        rc = lib.oracle_parallel_fwd(B, T, D, _p(a), _p(b), _p(h0), _p(rm), _p(out), _p(last),
+                                     threads)
         if rc != 0:
             raise RuntimeError("oracle thread start failed")
     else:
-        lib.oracle_scan_fwd(B, T, D, _p(a), _p(b), _p(h0), _p(out), _p(last))
+        lib.oracle_scan_fwd(B, T, D, _p(a), _p(b), _p(h0), _p(rm), _p(out), _p(last))
     return out, last
 
 
-def scan_bwd(a, h, g, h0=None, grad_last=None, threads: int = 1):
-    """Backward scan in fp64.  ``h`` are the forward states.
+def scan_bwd(a, h, g, h0=None, grad_last=None, threads: int = 1, reset=None):
+    """Backward scan in fp64.  ``h`` are the forward states (of the same
+    ``reset`` mask).
 
     Returns (grad_a, grad_b, grad_h0)."""
     a = _f64(a)
@@ -132,17 +150,18 @@ def scan_bwd(a, h, g, h0=None, grad_last=None, threads: int = 1):
     g = _f64(g, a.shape)
     h0 = _f64(h0, (B, D))
     grad_last = _f64(grad_last, (B, D))
+    rm = _mask(reset, B, T)
     grad_a = np.empty((B, T, D))
     grad_b = np.empty((B, T, D))
     grad_h0 = np.empty((B, D))
     lib = _load()
     if threads > 1:
         rc = lib.oracle_parallel_bwd(B, T, D, _p(a), _p(h), _p(g), _p(h0), _p(grad_last),
-                                     _p(grad_a), _p(grad_b), _p(grad_h0), threads)
+                                     _p(rm), _p(grad_a), _p(grad_b), _p(grad_h0), threads)
         if rc != 0:
             raise RuntimeError("oracle thread start failed")
     else:
-        lib.oracle_scan_bwd(B, T, D, _p(a), _p(h), _p(g), _p(h0), _p(grad_last),
+        lib.oracle_scan_bwd(B, T, D, _p(a), _p(h), _p(g), _p(h0), _p(grad_last), _p(rm),
                             _p(grad_a), _p(grad_b), _p(grad_h0))
     return grad_a, grad_b, grad_h0
 

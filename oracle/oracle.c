@@ -36,6 +36,21 @@ static size_t idx3(int64_t b, int64_t t, int64_t d, int64_t T, int64_t D) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* Segment resets (optional).  reset is a [B, T] byte mask, element (b, t) at */
+/* b*T + t; a nonzero byte marks step t of batch row b as the first step of a */
+/* new segment.  The state entering that step is dropped: the step's          */
+/* transition is taken as 0 in place of a_t, so h_t = b_t.  (Page            */
+/* "triton_training_scan.py", _samu_tiled_serial_forward: a step whose        */
+/* segment position is 0 forces the decay to 0; the same page's token mask   */
+/* is per (b, t) across all D.)  In the backward, a_t does not enter a reset  */
+/* step, so grad_a_t = 0 there, and the adjoint carried to earlier steps is   */
+/* 0 * lambda_t = 0.                                                          */
+/* ------------------------------------------------------------------------ */
+static int is_reset(const uint8_t* reset, int64_t bi, int64_t t, int64_t T) {
+    return reset != NULL && reset[(size_t)bi * (size_t)T + (size_t)t] != 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Forward: h_{-1} = h0 (zero when h0 is NULL); h_t = a_t h_{t-1} + b_t.      */
 /* out[b,t,d] = h_t; last[b,d] = h_{T-1}.                                    */
 /* (_real_forward: zero state, one multiply-add per step, every state stored, */
@@ -43,14 +58,15 @@ static size_t idx3(int64_t b, int64_t t, int64_t d, int64_t T, int64_t D) {
 /* ------------------------------------------------------------------------ */
 static void fwd_lanes(int64_t B, int64_t T, int64_t D, int64_t lane0, int64_t lane1,
                       const double* a, const double* b, const double* h0,
-                      double* out, double* last) {
+                      const uint8_t* reset, double* out, double* last) {
     (void)B;
     for (int64_t lane = lane0; lane < lane1; ++lane) {
         int64_t bi = lane / D, d = lane % D;
         double h = h0 ? h0[lane] : 0.0;
         for (int64_t t = 0; t < T; ++t) {
             size_t i = idx3(bi, t, d, T, D);
-            h = a[i] * h + b[i];
+            double at = is_reset(reset, bi, t, T) ? 0.0 : a[i];
+            h = at * h + b[i];
             if (out) out[i] = h;
         }
         if (last) last[lane] = h;
@@ -58,8 +74,8 @@ static void fwd_lanes(int64_t B, int64_t T, int64_t D, int64_t lane0, int64_t la
 }
 
 void oracle_scan_fwd(int64_t B, int64_t T, int64_t D, const double* a, const double* b,
-                     const double* h0, double* out, double* last) {
-    fwd_lanes(B, T, D, 0, B * D, a, b, h0, out, last);
+                     const double* h0, const uint8_t* reset, double* out, double* last) {
+    fwd_lanes(B, T, D, 0, B * D, a, b, h0, reset, out, last);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -76,7 +92,7 @@ void oracle_scan_fwd(int64_t B, int64_t T, int64_t D, const double* a, const dou
 /* ------------------------------------------------------------------------ */
 static void bwd_lanes(int64_t B, int64_t T, int64_t D, int64_t lane0, int64_t lane1,
                       const double* a, const double* h, const double* g,
-                      const double* h0, const double* grad_last,
+                      const double* h0, const double* grad_last, const uint8_t* reset,
                       double* grad_a, double* grad_b, double* grad_h0) {
     (void)B;
     for (int64_t lane = lane0; lane < lane1; ++lane) {
@@ -84,11 +100,12 @@ static void bwd_lanes(int64_t B, int64_t T, int64_t D, int64_t lane0, int64_t la
         double carry = grad_last ? grad_last[lane] : 0.0; /* a_{t+1} lambda_{t+1} */
         for (int64_t t = T - 1; t >= 0; --t) {
             size_t i = idx3(bi, t, d, T, D);
+            int r = is_reset(reset, bi, t, T);
             double lam = g[i] + carry;
             double h_prev = (t > 0) ? h[idx3(bi, t - 1, d, T, D)] : (h0 ? h0[lane] : 0.0);
             grad_b[i] = lam;
-            grad_a[i] = lam * h_prev;
-            carry = a[i] * lam;
+            grad_a[i] = r ? 0.0 : lam * h_prev;
+            carry = (r ? 0.0 : a[i]) * lam;
         }
         if (grad_h0) grad_h0[lane] = carry;
     }
@@ -96,8 +113,8 @@ static void bwd_lanes(int64_t B, int64_t T, int64_t D, int64_t lane0, int64_t la
 
 void oracle_scan_bwd(int64_t B, int64_t T, int64_t D, const double* a, const double* h,
                      const double* g, const double* h0, const double* grad_last,
-                     double* grad_a, double* grad_b, double* grad_h0) {
-    bwd_lanes(B, T, D, 0, B * D, a, h, g, h0, grad_last, grad_a, grad_b, grad_h0);
+                     const uint8_t* reset, double* grad_a, double* grad_b, double* grad_h0) {
+    bwd_lanes(B, T, D, 0, B * D, a, h, g, h0, grad_last, reset, grad_a, grad_b, grad_h0);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -236,16 +253,18 @@ typedef struct {
     int dir; /* 0 forward, 1 backward */
     int64_t B, T, D, lane0, lane1;
     const double *a, *b, *h, *g, *h0, *grad_last;
+    const uint8_t* reset;
     double *out, *last, *grad_a, *grad_b, *grad_h0;
 } job_t;
 
 static void* run_job(void* p) {
     job_t* j = (job_t*)p;
     if (j->dir == 0)
-        fwd_lanes(j->B, j->T, j->D, j->lane0, j->lane1, j->a, j->b, j->h0, j->out, j->last);
+        fwd_lanes(j->B, j->T, j->D, j->lane0, j->lane1, j->a, j->b, j->h0, j->reset, j->out,
+                  j->last);
     else
         bwd_lanes(j->B, j->T, j->D, j->lane0, j->lane1, j->a, j->h, j->g, j->h0, j->grad_last,
-                  j->grad_a, j->grad_b, j->grad_h0);
+                  j->reset, j->grad_a, j->grad_b, j->grad_h0);
     return NULL;
 }
 
@@ -272,17 +291,20 @@ static int run_parallel(job_t proto, int threads) {
 }
 
 int oracle_parallel_fwd(int64_t B, int64_t T, int64_t D, const double* a, const double* b,
-                        const double* h0, double* out, double* last, int threads) {
+                        const double* h0, const uint8_t* reset, double* out, double* last,
+                        int threads) {
     job_t j = {0};
-    j.dir = 0; j.B = B; j.T = T; j.D = D; j.a = a; j.b = b; j.h0 = h0; j.out = out; j.last = last;
+    j.dir = 0; j.B = B; j.T = T; j.D = D; j.a = a; j.b = b; j.h0 = h0; j.reset = reset;
+    j.out = out; j.last = last;
     return run_parallel(j, threads);
 }
 
 int oracle_parallel_bwd(int64_t B, int64_t T, int64_t D, const double* a, const double* h,
                         const double* g, const double* h0, const double* grad_last,
-                        double* grad_a, double* grad_b, double* grad_h0, int threads) {
+                        const uint8_t* reset, double* grad_a, double* grad_b, double* grad_h0,
+                        int threads) {
     job_t j = {0};
-    j.dir = 1; j.B = B; j.T = T; j.D = D; j.a = a; j.h = h; j.g = g; j.h0 = h0;
+    j.dir = 1; j.B = B; j.T = T; j.D = D; j.a = a; j.h = h; j.g = g; j.h0 = h0; j.reset = reset;
     j.grad_last = grad_last; j.grad_a = grad_a; j.grad_b = grad_b; j.grad_h0 = grad_h0;
     return run_parallel(j, threads);
 }

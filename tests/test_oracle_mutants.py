@@ -20,14 +20,14 @@ SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
 # (name, text in oracle.c, replacement, occurrence index or None for all)
 MUTANTS = [
-    ("fwd_drop_b", "h = a[i] * h + b[i];\n            if (out)", "h = a[i] * h;\n            if (out)"),
-    ("fwd_swap_ab", "h = a[i] * h + b[i];\n            if (out)", "h = b[i] * h + a[i];\n            if (out)"),
+    ("fwd_drop_b", "h = at * h + b[i];\n            if (out)", "h = at * h;\n            if (out)"),
+    ("fwd_swap_ab", "h = at * h + b[i];\n            if (out)", "h = b[i] * h + at;\n            if (out)"),
     ("fwd_ignore_h0", "double h = h0 ? h0[lane] : 0.0;", "double h = 0.0;"),
     ("bwd_drop_carry", "double lam = g[i] + carry;\n            double h_prev = (t > 0) ? h[idx3(bi, t - 1, d, T, D)] : (h0 ? h0[lane] : 0.0);",
      "double lam = g[i];\n            double h_prev = (t > 0) ? h[idx3(bi, t - 1, d, T, D)] : (h0 ? h0[lane] : 0.0);"),
     ("bwd_hprev_same_step", "double h_prev = (t > 0) ? h[idx3(bi, t - 1, d, T, D)] : (h0 ? h0[lane] : 0.0);",
      "double h_prev = h[idx3(bi, t, d, T, D)];"),
-    ("bwd_carry_uses_g", "carry = a[i] * lam;\n        }\n        if (grad_h0)", "carry = a[i] * g[i];\n        }\n        if (grad_h0)"),
+    ("bwd_carry_uses_g", "carry = (r ? 0.0 : a[i]) * lam;", "carry = (r ? 0.0 : a[i]) * g[i];"),
     ("bwd_ignore_grad_last", "double carry = grad_last ? grad_last[lane] : 0.0;", "double carry = 0.0;"),
     ("bwd_grad_h0_lambda", "if (grad_h0) grad_h0[lane] = carry;", "if (grad_h0) grad_h0[lane] = carry / 2;"),
     ("summary_drop_decay", "q = a[i] * q + b[i];", "q = q + b[i];"),
@@ -36,6 +36,15 @@ MUTANTS = [
     ("rsummary_drop_a_on_g", "q = a[i] * q + a[i] * g[i];", "q = a[i] * q + g[i];"),
     ("rprefix_inclusive", "future[i] = s;\n                s = P[i] * s + Q[i];", "s = P[i] * s + Q[i];\n                future[i] = s;"),
     ("rreplay_no_decay", "carry = a[i] * lam;\n                }", "carry = lam;\n                }"),
+    ("reset_ignored_fwd", "double at = is_reset(reset, bi, t, T) ? 0.0 : a[i];", "double at = a[i];"),
+    ("reset_zeroes_b", "double at = is_reset(reset, bi, t, T) ? 0.0 : a[i];\n            h = at * h + b[i];",
+     "double at = a[i];\n            h = at * h + (is_reset(reset, bi, t, T) ? 0.0 : b[i]);"),
+    ("reset_shifted", "double at = is_reset(reset, bi, t, T) ? 0.0 : a[i];",
+     "double at = is_reset(reset, bi, t > 0 ? t - 1 : 0, T) ? 0.0 : a[i];"),
+    ("reset_keeps_grad_a", "grad_a[i] = r ? 0.0 : lam * h_prev;", "grad_a[i] = lam * h_prev;"),
+    ("reset_keeps_carry", "carry = (r ? 0.0 : a[i]) * lam;", "carry = a[i] * lam;"),
+    ("reset_mask_transposed", "return reset != NULL && reset[(size_t)bi * (size_t)T + (size_t)t] != 0;",
+     "return reset != NULL && reset[(size_t)bi * (size_t)T + (size_t)(T - 1 - t)] != 0;"),
 ]
 
 

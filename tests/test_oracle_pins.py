@@ -374,3 +374,91 @@ def test_last_equals_final_state_and_threads_agree():
     r4 = oracle.scan_bwd(a, out, g, threads=5)
     for x, y in zip(r1, r4):
         assert np.array_equal(x, y)
+
+
+# ----------------------------------------------------------------------------
+# segment resets: a [B, T] mask whose nonzero entries start a new segment
+# (the state entering that step is dropped, as a forced a = 0)
+# ----------------------------------------------------------------------------
+def _segments(mask_row):
+    """[start, end) of every segment of one batch row."""
+    T = mask_row.shape[0]
+    starts = [0] + [t for t in range(1, T) if mask_row[t]]
+    return list(zip(starts, starts[1:] + [T]))
+
+
+def _reset_case(B=3, T=40, D=5, seed=21):
+    a, b, g = rand((B, T, D), seed, 0.3, 1.2), rand((B, T, D), seed + 1), rand((B, T, D), seed + 2)
+    h0, gl = rand((B, D), seed + 3), rand((B, D), seed + 4)
+    mask = np.random.default_rng(seed + 5).random((B, T)) < 0.15
+    mask[0, 0] = True       # a reset on the very first step drops h0
+    mask[1, 0] = False
+    mask[1, T - 1] = True   # and one on the very last step
+    return a, b, g, h0, gl, mask
+
+
+def test_reset_mask_splits_into_independent_segments():
+    """Forward and backward with a reset mask equal the plain scan run on
+    each segment on its own: zero entering state (h0 only for a first segment
+    that is not reset), grad_last only for the final segment, no gradient
+    reaching a reset step's a, and none crossing a reset."""
+    a, b, g, h0, gl, mask = _reset_case()
+    B, T, D = a.shape
+    out, last = oracle.scan_fwd(a, b, h0=h0, reset=mask)
+    ga, gb, gh0 = oracle.scan_bwd(a, out, g, h0=h0, grad_last=gl, reset=mask)
+    for bi in range(B):
+        for s, e in _segments(mask[bi]):
+            first = s == 0 and not mask[bi, 0]
+            sh0 = h0[bi:bi + 1] if first else None
+            so, sl = oracle.scan_fwd(a[bi:bi + 1, s:e], b[bi:bi + 1, s:e], h0=sh0)
+            assert np.array_equal(out[bi, s:e], so[0]), (bi, s, e)
+            sgl = gl[bi:bi + 1] if e == T else None
+            sga, sgb, sgh0 = oracle.scan_bwd(a[bi:bi + 1, s:e], so, g[bi:bi + 1, s:e], h0=sh0,
+                                             grad_last=sgl)
+            assert np.array_equal(gb[bi, s:e], sgb[0]), (bi, s, e)
+            assert np.array_equal(ga[bi, s:e], sga[0]), (bi, s, e)
+            if s == 0:
+                expect = sgh0[0] if first else np.zeros(D)
+                assert np.array_equal(gh0[bi], expect), bi
+            else:
+                assert np.all(ga[bi, s] == 0.0)
+        assert np.array_equal(last[bi], out[bi, T - 1])
+
+
+def test_reset_gradients_match_finite_differences():
+    """dL/da, dL/db and dL/dh0 of L = <g, out> + <grad_last, last> under a
+    reset mask, by central differences in fp64 (a is not used at a reset
+    step, so its derivative there is exactly 0)."""
+    a, b, g, h0, gl, mask = _reset_case(B=2, T=9, D=2, seed=33)
+    mask[0, 4] = True
+
+    def loss(a_, b_, h0_):
+        o, l = oracle.scan_fwd(a_, b_, h0=h0_, reset=mask)
+        return float(np.sum(g * o) + np.sum(gl * l))
+
+    out, _ = oracle.scan_fwd(a, b, h0=h0, reset=mask)
+    ga, gb, gh0 = oracle.scan_bwd(a, out, g, h0=h0, grad_last=gl, reset=mask)
+    eps = 1e-6
+    for arr, grad, which in ((a, ga, 0), (b, gb, 1), (h0, gh0, 2)):
+        for idx in np.ndindex(arr.shape):
+            up, dn = arr.copy(), arr.copy()
+            up[idx] += eps
+            dn[idx] -= eps
+            args_up = [a, b, h0]
+            args_dn = [a, b, h0]
+            args_up[which], args_dn[which] = up, dn
+            fd = (loss(*args_up) - loss(*args_dn)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-7 * (1 + abs(fd)), (which, idx, fd, grad[idx])
+    assert np.all(ga[mask[:, :, None].repeat(a.shape[2], 2)] == 0.0)
+
+
+def test_reset_all_clear_mask_is_the_plain_scan():
+    a, b, g, h0, gl, _ = _reset_case(seed=41)
+    mask = np.zeros(a.shape[:2], dtype=bool)
+    o1, l1 = oracle.scan_fwd(a, b, h0=h0, reset=mask)
+    o2, l2 = oracle.scan_fwd(a, b, h0=h0)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    r1 = oracle.scan_bwd(a, o1, g, h0=h0, grad_last=gl, reset=mask)
+    r2 = oracle.scan_bwd(a, o2, g, h0=h0, grad_last=gl)
+    for x, y in zip(r1, r2):
+        assert np.array_equal(x, y)
