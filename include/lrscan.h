@@ -89,6 +89,15 @@ typedef struct {
                                from the inputs itself; <= 0: the library default.  Results
                                are bitwise the same for every value (1 exercises the
                                derivation path). */
+    const uint8_t* reset;   /* [B, T] bytes (b*T + t), or NULL.  Nonzero marks step t of batch
+                               row b as the first step of a new segment: the state entering it
+                               is dropped (the step's transition is taken as 0, so
+                               h_t = b_t).  Forward and backward take the same mask; the
+                               backward then gives grad_a_t = 0 at such a step (a_t is not
+                               used), carries no adjoint past it, and grad_h0 = 0 for a row
+                               whose step 0 is marked (page "triton_training_scan.py",
+                               _samu_tiled_serial_forward/_backward: a step at segment
+                               position 0 forces the decay to 0).  Every algorithm. */
 } lrscan_opts;
 
 /*

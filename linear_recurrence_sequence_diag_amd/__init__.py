@@ -46,6 +46,7 @@ class Opts(ctypes.Structure):
         ("h0", ctypes.c_void_p),
         ("grad_h0", ctypes.c_void_p),
         ("polls", ctypes.c_int),
+        ("reset", ctypes.c_void_p),
     ]
 
 
@@ -222,7 +223,19 @@ def _check_state(name, t, ref):
         raise ValueError(f"{name} must be a contiguous float32 [B, D] tensor on a's device")
 
 
-def make_opts(algo="auto", chunk=0, h0=None, grad_h0=None, workspace=None, width=0, polls=0):
+def _check_mask(t, ref):
+    """Segment-start mask: a contiguous bool or uint8 [B, T] tensor on a's device."""
+    if t is None:
+        return
+    torch = _torch()
+    B, T, _ = ref.shape
+    if (t.shape != (B, T) or t.dtype not in (torch.bool, torch.uint8) or t.device != ref.device
+            or not t.is_contiguous()):
+        raise ValueError("reset must be a contiguous bool or uint8 [B, T] tensor on a's device")
+
+
+def make_opts(algo="auto", chunk=0, h0=None, grad_h0=None, workspace=None, width=0, polls=0,
+              reset=None):
     o = Opts()
     o.algo = ALGOS[algo] if isinstance(algo, str) else int(algo)
     o.chunk = int(chunk)
@@ -232,13 +245,16 @@ def make_opts(algo="auto", chunk=0, h0=None, grad_h0=None, workspace=None, width
     o.h0 = _ptr(h0)
     o.grad_h0 = _ptr(grad_h0)
     o.polls = int(polls)
+    o.reset = _ptr(reset)
     return o
 
 
-def scan(a, b, h0=None, algo="auto", chunk=0, with_last=True, width=0, polls=0):
-    """Forward scan.  Returns (out, last); out has a's dtype, last is float32 [B, D]."""
+def scan(a, b, h0=None, algo="auto", chunk=0, with_last=True, width=0, polls=0, reset=None):
+    """Forward scan.  Returns (out, last); out has a's dtype, last is float32 [B, D].
+    ``reset`` ([B, T] bool/uint8) starts a new segment wherever it is set."""
     torch = _torch()
     _check_seq("a", a)
+    _check_mask(reset, a)
     _check_seq("b", b, a)
     _check_state("h0", h0, a)
     B, T, D = a.shape
@@ -247,15 +263,17 @@ def scan(a, b, h0=None, algo="auto", chunk=0, with_last=True, width=0, polls=0):
     with torch.cuda.device(a.device):
         scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), _ptr(last), B, T, D,
                     dtype_code(a.dtype), _stream(a),
-                    make_opts(algo, chunk, h0=h0, width=width, polls=polls))
+                    make_opts(algo, chunk, h0=h0, width=width, polls=polls, reset=reset))
     return out, last
 
 
 def scan_backward(a, out, grad_out, grad_last=None, h0=None, algo="auto", chunk=0,
-                  need_grad_h0=False, width=0, polls=0):
-    """Reverse-time adjoint.  Returns (grad_a, grad_b, grad_h0 or None)."""
+                  need_grad_h0=False, width=0, polls=0, reset=None):
+    """Reverse-time adjoint.  Returns (grad_a, grad_b, grad_h0 or None).  ``reset``
+    must be the mask the forward used."""
     torch = _torch()
     _check_seq("a", a)
+    _check_mask(reset, a)
     _check_seq("out", out, a)
     _check_seq("grad_out", grad_out, a)
     _check_state("grad_last", grad_last, a)
@@ -267,7 +285,8 @@ def scan_backward(a, out, grad_out, grad_last=None, h0=None, algo="auto", chunk=
     with torch.cuda.device(a.device):
         scan_bwd_ex(a.data_ptr(), out.data_ptr(), grad_out.data_ptr(), _ptr(grad_last),
                     grad_a.data_ptr(), grad_b.data_ptr(), B, T, D, dtype_code(a.dtype), _stream(a),
-                    make_opts(algo, chunk, h0=h0, grad_h0=grad_h0, width=width, polls=polls))
+                    make_opts(algo, chunk, h0=h0, grad_h0=grad_h0, width=width, polls=polls,
+                              reset=reset))
     return grad_a, grad_b, grad_h0
 
 
@@ -334,18 +353,19 @@ def _make_autograd():
         """out = scan(a, b); gradients from the reverse-time kernels."""
 
         @staticmethod
-        def forward(ctx, a, b):
+        def forward(ctx, a, b, reset):
             a = a.contiguous()
             b = b.contiguous()
-            out, _ = scan(a, b, with_last=False)
+            out, _ = scan(a, b, with_last=False, reset=reset)
             ctx.save_for_backward(a, out)
+            ctx.reset = reset
             return out
 
         @staticmethod
         def backward(ctx, grad_out):
             a, out = ctx.saved_tensors
-            ga, gb, _ = scan_backward(a, out, grad_out.contiguous())
-            return ga, gb
+            ga, gb, _ = scan_backward(a, out, grad_out.contiguous(), reset=ctx.reset)
+            return ga, gb, None
 
     return DiagonalScan
 
@@ -353,9 +373,10 @@ def _make_autograd():
 _autograd_cls = None
 
 
-def diagonal_scan(a, b):
-    """Differentiable scan (torch autograd) returning every state."""
+def diagonal_scan(a, b, reset=None):
+    """Differentiable scan (torch autograd) returning every state; ``reset``
+    ([B, T] bool/uint8, not differentiated) starts new segments."""
     global _autograd_cls
     if _autograd_cls is None:
         _autograd_cls = _make_autograd()
-    return _autograd_cls.apply(a, b)
+    return _autograd_cls.apply(a, b, reset)

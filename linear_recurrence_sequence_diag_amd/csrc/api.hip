@@ -233,24 +233,25 @@ LRSCAN_API int scan_fwd_ex(const void* a, const void* b, void* out, float* last,
     if (st != LRSCAN_OK) return st;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const float* h0 = opts ? opts->h0 : nullptr;
+    const uint8_t* reset = opts ? opts->reset : nullptr;
     Workspace ws;
     st = get_workspace(s, r, opts, hs, &ws);
     if (st != LRSCAN_OK) return st;
     switch (r.algo) {
-        case LRSCAN_ALGO_SEQ: return hip_status(launch_seq_fwd(s, a, b, out, last, h0, hs));
+        case LRSCAN_ALGO_SEQ: return hip_status(launch_seq_fwd(s, a, b, out, last, h0, reset, hs));
         case LRSCAN_ALGO_CHUNKED: {
             const int64_t NC = (T + r.chunk - 1) / r.chunk;
             const size_t part = align_up((size_t)NC * B * D * 4, 256);
             float* P = static_cast<float*>(ws.ptr);
             float* Q = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + part);
             float* cin = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + 2 * part);
-            hipError_t e = launch_chunk_summary(s, r.chunk, a, b, P, Q, hs);
+            hipError_t e = launch_chunk_summary(s, r.chunk, a, b, reset, P, Q, hs);
             if (e == hipSuccess) e = launch_chunk_prefix(B, NC, D, P, Q, h0, cin, nullptr, hs);
-            if (e == hipSuccess) e = launch_chunk_replay(s, r.chunk, a, b, cin, out, last, hs);
+            if (e == hipSuccess) e = launch_chunk_replay(s, r.chunk, a, b, reset, cin, out, last, hs);
             return hip_status(e);
         }
         case LRSCAN_ALGO_FUSED:
-            return fused_status(launch_fused_fwd(s, r.width, r.chunk, a, b, out, last, h0,
+            return fused_status(launch_fused_fwd(s, r.width, r.chunk, a, b, out, last, h0, reset,
                                                  ws.ptr, ws.bytes, ws.init, opts ? opts->polls : 0, hs),
                                 ws, opts, hs);
     }
@@ -272,12 +273,13 @@ LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const float* h0 = opts ? opts->h0 : nullptr;
     float* grad_h0 = opts ? opts->grad_h0 : nullptr;
+    const uint8_t* reset = opts ? opts->reset : nullptr;
     Workspace ws;
     st = get_workspace(s, r, opts, hs, &ws);
     if (st != LRSCAN_OK) return st;
     switch (r.algo) {
         case LRSCAN_ALGO_SEQ:
-            return hip_status(launch_seq_bwd(s, a, out, grad_out, grad_last, h0, grad_a, grad_b,
+            return hip_status(launch_seq_bwd(s, a, out, grad_out, grad_last, h0, reset, grad_a, grad_b,
                                              grad_h0, hs));
         case LRSCAN_ALGO_CHUNKED: {
             const int64_t NC = (T + r.chunk - 1) / r.chunk;
@@ -285,17 +287,17 @@ LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
             float* P = static_cast<float*>(ws.ptr);
             float* Q = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + part);
             float* fut = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + 2 * part);
-            hipError_t e = launch_reverse_chunk_summary(s, r.chunk, a, grad_out, P, Q, hs);
+            hipError_t e = launch_reverse_chunk_summary(s, r.chunk, a, grad_out, reset, P, Q, hs);
             if (e == hipSuccess)
                 e = launch_reverse_chunk_prefix(B, NC, D, P, Q, grad_last, fut, grad_h0, hs);
             if (e == hipSuccess)
-                e = launch_reverse_chunk_replay(s, r.chunk, a, out, grad_out, fut, h0, grad_a,
+                e = launch_reverse_chunk_replay(s, r.chunk, a, out, grad_out, reset, fut, h0, grad_a,
                                                 grad_b, hs);
             return hip_status(e);
         }
         case LRSCAN_ALGO_FUSED:
             return fused_status(launch_fused_bwd(s, r.width, r.chunk, a, out, grad_out, grad_last,
-                                                 h0, grad_a, grad_b, grad_h0, ws.ptr, ws.bytes,
+                                                 h0, reset, grad_a, grad_b, grad_h0, ws.ptr, ws.bytes,
                                                  ws.init, opts ? opts->polls : 0, hs),
                                 ws, opts, hs);
     }
@@ -321,7 +323,7 @@ LRSCAN_API int scan_chunk_summary(const void* a, const void* b, float* P, float*
     if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
     if (!chunk_ok(chunk)) return LRSCAN_ERR_CHUNK;
-    return hip_status(launch_chunk_summary(Shape{B, T, D, dtype}, chunk, a, b, P, Q,
+    return hip_status(launch_chunk_summary(Shape{B, T, D, dtype}, chunk, a, b, nullptr, P, Q,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -340,7 +342,7 @@ LRSCAN_API int scan_chunk_replay(const void* a, const void* b, const float* chun
     if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
     if (!chunk_ok(chunk)) return LRSCAN_ERR_CHUNK;
-    return hip_status(launch_chunk_replay(Shape{B, T, D, dtype}, chunk, a, b, chunk_in, out, last,
+    return hip_status(launch_chunk_replay(Shape{B, T, D, dtype}, chunk, a, b, nullptr, chunk_in, out, last,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -351,7 +353,7 @@ LRSCAN_API int scan_reverse_chunk_summary(const void* a, const void* grad_out, f
     if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
     if (!chunk_ok(chunk)) return LRSCAN_ERR_CHUNK;
-    return hip_status(launch_reverse_chunk_summary(Shape{B, T, D, dtype}, chunk, a, grad_out, P, Q,
+    return hip_status(launch_reverse_chunk_summary(Shape{B, T, D, dtype}, chunk, a, grad_out, nullptr, P, Q,
                                                    static_cast<hipStream_t>(stream)));
 }
 
@@ -372,7 +374,7 @@ LRSCAN_API int scan_reverse_chunk_replay(const void* a, const void* out, const v
     if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
     if (!chunk_ok(chunk)) return LRSCAN_ERR_CHUNK;
-    return hip_status(launch_reverse_chunk_replay(Shape{B, T, D, dtype}, chunk, a, out, grad_out,
+    return hip_status(launch_reverse_chunk_replay(Shape{B, T, D, dtype}, chunk, a, out, grad_out, nullptr,
                                                   future, h0, grad_a, grad_b,
                                                   static_cast<hipStream_t>(stream)));
 }

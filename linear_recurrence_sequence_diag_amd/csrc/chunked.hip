@@ -17,6 +17,8 @@
 // segments of a wavefront are combined with an in-wavefront scan, the
 // wavefronts through LDS, and every thread then rewalks its segment from the
 // state entering it.
+#include <type_traits>
+
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -78,9 +80,12 @@ __device__ __forceinline__ ChunkIdx chunk_index(int64_t B, int64_t NC, int64_t D
 // ---------------------------------------------------------------------------
 // forward summary: P = prod a, Q = chunk scanned from zero
 // ---------------------------------------------------------------------------
-template <int DT, bool ALIGNED>
+// RST (every kernel below): `reset` ([B, T] bytes) marks segment starts,
+// where the step's transition is taken as 0.
+template <int DT, bool ALIGNED, bool RST>
 __global__ __launch_bounds__(kBlk) void chunk_summary_kernel(const void* __restrict__ a,
                                                              const void* __restrict__ b,
+                                                             const uint8_t* __restrict__ reset,
                                                              float* __restrict__ P,
                                                              float* __restrict__ Q, int64_t B,
                                                              int64_t T, int64_t D, int C) {
@@ -97,20 +102,23 @@ __global__ __launch_bounds__(kBlk) void chunk_summary_kernel(const void* __restr
     }
     const int64_t t_begin = ci.k * C;
     const int64_t t_end = (t_begin + C < T) ? t_begin + C : T;
+    const uint8_t* rrow = RST ? reset + (size_t)ci.bi * T : nullptr;
     for (int64_t t0 = t_begin; t0 < t_end; t0 += kU) {
         RowVec<DT> ra[kU], rb[kU];
+        uint32_t rr[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u)
             if (t0 + u < t_end) {
                 ra[u] = load_row<DT, ALIGNED>(a, base + (size_t)(t0 + u) * D, ci.nvalid, 1.0f);
                 rb[u] = load_row<DT, ALIGNED>(b, base + (size_t)(t0 + u) * D, ci.nvalid, 0.0f);
+                if (RST) rr[u] = rrow[t0 + u];
             }
 #pragma unroll
         for (int u = 0; u < kU; ++u)
             if (t0 + u < t_end) {
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
-                    const float at = ra[u].get(j);
+                    const float at = (RST && rr[u]) ? 0.0f : ra[u].get(j);
                     p[j] = at * p[j];
                     q[j] = fmaf(at, q[j], rb[u].get(j));
                 }
@@ -124,10 +132,11 @@ __global__ __launch_bounds__(kBlk) void chunk_summary_kernel(const void* __restr
 // ---------------------------------------------------------------------------
 // forward replay: rescan each chunk from chunk_in
 // ---------------------------------------------------------------------------
-template <int DT, bool ALIGNED>
+template <int DT, bool ALIGNED, bool RST>
 __global__ __launch_bounds__(kBlk) void chunk_replay_kernel(
-    const void* __restrict__ a, const void* __restrict__ b, const float* __restrict__ chunk_in,
-    void* __restrict__ out, float* __restrict__ last, int64_t B, int64_t T, int64_t D, int C) {
+    const void* __restrict__ a, const void* __restrict__ b, const uint8_t* __restrict__ reset,
+    const float* __restrict__ chunk_in, void* __restrict__ out, float* __restrict__ last,
+    int64_t B, int64_t T, int64_t D, int C) {
     constexpr int V = Elem<DT>::V;
     const int64_t NC = (T + C - 1) / C;
     const ChunkIdx ci = chunk_index<DT>(B, NC, D);
@@ -137,13 +146,16 @@ __global__ __launch_bounds__(kBlk) void chunk_replay_kernel(
     load_vecf(chunk_in, ((size_t)ci.bi * NC + ci.k) * D + ci.d0, ci.nvalid, h, V, ALIGNED, 0.0f);
     const int64_t t_begin = ci.k * C;
     const int64_t t_end = (t_begin + C < T) ? t_begin + C : T;
+    const uint8_t* rrow = RST ? reset + (size_t)ci.bi * T : nullptr;
     for (int64_t t0 = t_begin; t0 < t_end; t0 += kU) {
         RowVec<DT> ra[kU], rb[kU];
+        uint32_t rr[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u)
             if (t0 + u < t_end) {
                 ra[u] = load_row<DT, ALIGNED>(a, base + (size_t)(t0 + u) * D, ci.nvalid, 1.0f);
                 rb[u] = load_row<DT, ALIGNED>(b, base + (size_t)(t0 + u) * D, ci.nvalid, 0.0f);
+                if (RST) rr[u] = rrow[t0 + u];
             }
 #pragma unroll
         for (int u = 0; u < kU; ++u)
@@ -151,7 +163,8 @@ __global__ __launch_bounds__(kBlk) void chunk_replay_kernel(
                 RowOut<DT> o;
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
-                    h[j] = fmaf(ra[u].get(j), h[j], rb[u].get(j));
+                    const float at = (RST && rr[u]) ? 0.0f : ra[u].get(j);
+                    h[j] = fmaf(at, h[j], rb[u].get(j));
                     o.v[j] = h[j];
                 }
                 store_row<DT, ALIGNED>(out, base + (size_t)(t0 + u) * D, ci.nvalid, o);
@@ -167,10 +180,10 @@ __global__ __launch_bounds__(kBlk) void chunk_replay_kernel(
 // ---------------------------------------------------------------------------
 // reverse summary: walking the chunk backwards, P = prod a, Q <- a (Q + g)
 // ---------------------------------------------------------------------------
-template <int DT, bool ALIGNED>
+template <int DT, bool ALIGNED, bool RST>
 __global__ __launch_bounds__(kBlk) void reverse_chunk_summary_kernel(
-    const void* __restrict__ a, const void* __restrict__ g, float* __restrict__ P,
-    float* __restrict__ Q, int64_t B, int64_t T, int64_t D, int C) {
+    const void* __restrict__ a, const void* __restrict__ g, const uint8_t* __restrict__ reset,
+    float* __restrict__ P, float* __restrict__ Q, int64_t B, int64_t T, int64_t D, int C) {
     constexpr int V = Elem<DT>::V;
     const int64_t NC = (T + C - 1) / C;
     const ChunkIdx ci = chunk_index<DT>(B, NC, D);
@@ -184,20 +197,23 @@ __global__ __launch_bounds__(kBlk) void reverse_chunk_summary_kernel(
     }
     const int64_t t_begin = ci.k * C;
     const int64_t t_end = (t_begin + C < T) ? t_begin + C : T;
+    const uint8_t* rrow = RST ? reset + (size_t)ci.bi * T : nullptr;
     for (int64_t top = t_end - 1; top >= t_begin; top -= kU) {
         RowVec<DT> ra[kU], rg[kU];
+        uint32_t rr[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u)
             if (top - u >= t_begin) {
                 ra[u] = load_row<DT, ALIGNED>(a, base + (size_t)(top - u) * D, ci.nvalid, 1.0f);
                 rg[u] = load_row<DT, ALIGNED>(g, base + (size_t)(top - u) * D, ci.nvalid, 0.0f);
+                if (RST) rr[u] = rrow[top - u];
             }
 #pragma unroll
         for (int u = 0; u < kU; ++u)
             if (top - u >= t_begin) {
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
-                    const float at = ra[u].get(j);
+                    const float at = (RST && rr[u]) ? 0.0f : ra[u].get(j);
                     p[j] = at * p[j];
                     q[j] = at * (q[j] + rg[u].get(j));
                 }
@@ -211,11 +227,12 @@ __global__ __launch_bounds__(kBlk) void reverse_chunk_summary_kernel(
 // ---------------------------------------------------------------------------
 // reverse replay: from the future carry, walk the chunk backwards
 // ---------------------------------------------------------------------------
-template <int DT, bool ALIGNED>
+template <int DT, bool ALIGNED, bool RST>
 __global__ __launch_bounds__(kBlk) void reverse_chunk_replay_kernel(
     const void* __restrict__ a, const void* __restrict__ out, const void* __restrict__ g,
-    const float* __restrict__ future, const float* __restrict__ h0, void* __restrict__ grad_a,
-    void* __restrict__ grad_b, int64_t B, int64_t T, int64_t D, int C) {
+    const uint8_t* __restrict__ reset, const float* __restrict__ future,
+    const float* __restrict__ h0, void* __restrict__ grad_a, void* __restrict__ grad_b, int64_t B,
+    int64_t T, int64_t D, int C) {
     constexpr int V = Elem<DT>::V;
     const int64_t NC = (T + C - 1) / C;
     const ChunkIdx ci = chunk_index<DT>(B, NC, D);
@@ -225,8 +242,10 @@ __global__ __launch_bounds__(kBlk) void reverse_chunk_replay_kernel(
     load_vecf(future, ((size_t)ci.bi * NC + ci.k) * D + ci.d0, ci.nvalid, carry, V, ALIGNED, 0.0f);
     const int64_t t_begin = ci.k * C;
     const int64_t t_end = (t_begin + C < T) ? t_begin + C : T;
+    const uint8_t* rrow = RST ? reset + (size_t)ci.bi * T : nullptr;
     for (int64_t top = t_end - 1; top >= t_begin; top -= kU) {
         RowVec<DT> ra[kU], rg[kU], rh[kU];
+        uint32_t rr[kU];
 #pragma unroll
         for (int u = 0; u < kU; ++u) {
             const int64_t t = top - u;
@@ -234,6 +253,7 @@ __global__ __launch_bounds__(kBlk) void reverse_chunk_replay_kernel(
                 ra[u] = load_row<DT, ALIGNED>(a, base + (size_t)t * D, ci.nvalid, 1.0f);
                 rg[u] = load_row<DT, ALIGNED>(g, base + (size_t)t * D, ci.nvalid, 0.0f);
                 if (t >= 1) rh[u] = load_row<DT, ALIGNED>(out, base + (size_t)(t - 1) * D, ci.nvalid, 0.0f);
+                if (RST) rr[u] = rrow[t];
             }
         }
 #pragma unroll
@@ -243,18 +263,24 @@ __global__ __launch_bounds__(kBlk) void reverse_chunk_replay_kernel(
                 RowOut<DT> oa, ob;
                 // lambda_t = g_t + a_{t+1}*lambda_{t+1} as one fma inside a
                 // block of rows; across blocks carry[] holds the product
+                // a segment start uses no a_t: transition 0, grad_a_t = 0
+                const int up = u > 0 ? u - 1 : 0;
+                const bool rs = RST && rr[u];
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
-                    const float an = u > 0 ? ra[u > 0 ? u - 1 : 0].get(j) : 1.0f;
+                    const float an = u > 0 ? ((RST && rr[up]) ? 0.0f : ra[up].get(j)) : 1.0f;
                     const float lam = fmaf(an, carry[j], rg[u].get(j));
                     float hp;
-                    if (t >= 1)
+                    if (rs)
+                        hp = 0.0f;
+                    else if (t >= 1)
                         hp = rh[u].get(j);
                     else
                         hp = (h0 && j < ci.nvalid) ? h0[ci.bi * D + ci.d0 + j] : 0.0f;
                     ob.v[j] = lam;
                     oa.v[j] = lam * hp;
-                    carry[j] = (u == kU - 1 || t == t_begin) ? ra[u].get(j) * lam : lam;
+                    const float at = rs ? 0.0f : ra[u].get(j);
+                    carry[j] = (u == kU - 1 || t == t_begin) ? at * lam : lam;
                 }
                 store_row<DT, ALIGNED>(grad_a, base + (size_t)t * D, ci.nvalid, oa);
                 store_row<DT, ALIGNED>(grad_b, base + (size_t)t * D, ci.nvalid, ob);
@@ -325,9 +351,18 @@ __global__ __launch_bounds__(kPxWaves* kWave) void chunk_prefix_kernel(
     }
 }
 
+// Calls f(AL, RS) with both flags as std::integral_constant<bool>.
+template <class F>
+void dispatch2(bool al, bool rst, F&& f) {
+    if (al && rst) f(std::true_type{}, std::true_type{});
+    else if (al) f(std::true_type{}, std::false_type{});
+    else if (rst) f(std::false_type{}, std::true_type{});
+    else f(std::false_type{}, std::false_type{});
+}
+
 template <int DT>
-hipError_t summary_t(const Shape& s, int C, const void* a, const void* b, float* P, float* Q,
-                     bool reverse, hipStream_t st) {
+hipError_t summary_t(const Shape& s, int C, const void* a, const void* b, const uint8_t* reset,
+                     float* P, float* Q, bool reverse, hipStream_t st) {
     const int64_t NC = (s.T + C - 1) / C;
     const int64_t vpr = (s.D + Elem<DT>::V - 1) / Elem<DT>::V;
     const int64_t threads = s.B * NC * vpr;
@@ -335,58 +370,48 @@ hipError_t summary_t(const Shape& s, int C, const void* a, const void* b, float*
     const void* ptrs[2] = {a, b};
     const bool al = rows_aligned(s, ptrs, 2) && reinterpret_cast<uintptr_t>(P) % 16 == 0 &&
                     reinterpret_cast<uintptr_t>(Q) % 16 == 0;
-    if (reverse) {
-        if (al)
-            hipLaunchKernelGGL((reverse_chunk_summary_kernel<DT, true>), grid, dim3(kBlk), 0, st, a,
-                               b, P, Q, s.B, s.T, s.D, C);
+    dispatch2(al, reset != nullptr, [&](auto AL, auto RS) {
+        if (reverse)
+            hipLaunchKernelGGL((reverse_chunk_summary_kernel<DT, decltype(AL)::value, decltype(RS)::value>),
+                               grid, dim3(kBlk), 0, st, a, b, reset, P, Q, s.B, s.T, s.D, C);
         else
-            hipLaunchKernelGGL((reverse_chunk_summary_kernel<DT, false>), grid, dim3(kBlk), 0, st,
-                               a, b, P, Q, s.B, s.T, s.D, C);
-    } else {
-        if (al)
-            hipLaunchKernelGGL((chunk_summary_kernel<DT, true>), grid, dim3(kBlk), 0, st, a, b, P,
-                               Q, s.B, s.T, s.D, C);
-        else
-            hipLaunchKernelGGL((chunk_summary_kernel<DT, false>), grid, dim3(kBlk), 0, st, a, b, P,
-                               Q, s.B, s.T, s.D, C);
-    }
+            hipLaunchKernelGGL((chunk_summary_kernel<DT, decltype(AL)::value, decltype(RS)::value>),
+                               grid, dim3(kBlk), 0, st, a, b, reset, P, Q, s.B, s.T, s.D, C);
+    });
     return hipGetLastError();
 }
 
 template <int DT>
-hipError_t replay_t(const Shape& s, int C, const void* a, const void* b, const float* cin,
-                    void* out, float* last, hipStream_t st) {
+hipError_t replay_t(const Shape& s, int C, const void* a, const void* b, const uint8_t* reset,
+                    const float* cin, void* out, float* last, hipStream_t st) {
     const int64_t NC = (s.T + C - 1) / C;
     const int64_t vpr = (s.D + Elem<DT>::V - 1) / Elem<DT>::V;
     const int64_t threads = s.B * NC * vpr;
     const dim3 grid((unsigned)((threads + kBlk - 1) / kBlk));
     const void* ptrs[3] = {a, b, out};
     const bool al = rows_aligned(s, ptrs, 3) && reinterpret_cast<uintptr_t>(cin) % 16 == 0;
-    if (al)
-        hipLaunchKernelGGL((chunk_replay_kernel<DT, true>), grid, dim3(kBlk), 0, st, a, b, cin, out,
-                           last, s.B, s.T, s.D, C);
-    else
-        hipLaunchKernelGGL((chunk_replay_kernel<DT, false>), grid, dim3(kBlk), 0, st, a, b, cin,
-                           out, last, s.B, s.T, s.D, C);
+    dispatch2(al, reset != nullptr, [&](auto AL, auto RS) {
+        hipLaunchKernelGGL((chunk_replay_kernel<DT, decltype(AL)::value, decltype(RS)::value>), grid,
+                           dim3(kBlk), 0, st, a, b, reset, cin, out, last, s.B, s.T, s.D, C);
+    });
     return hipGetLastError();
 }
 
 template <int DT>
 hipError_t reverse_replay_t(const Shape& s, int C, const void* a, const void* out, const void* g,
-                            const float* fut, const float* h0, void* ga, void* gb,
-                            hipStream_t st) {
+                            const uint8_t* reset, const float* fut, const float* h0, void* ga,
+                            void* gb, hipStream_t st) {
     const int64_t NC = (s.T + C - 1) / C;
     const int64_t vpr = (s.D + Elem<DT>::V - 1) / Elem<DT>::V;
     const int64_t threads = s.B * NC * vpr;
     const dim3 grid((unsigned)((threads + kBlk - 1) / kBlk));
     const void* ptrs[5] = {a, out, g, ga, gb};
     const bool al = rows_aligned(s, ptrs, 5) && reinterpret_cast<uintptr_t>(fut) % 16 == 0;
-    if (al)
-        hipLaunchKernelGGL((reverse_chunk_replay_kernel<DT, true>), grid, dim3(kBlk), 0, st, a, out,
-                           g, fut, h0, ga, gb, s.B, s.T, s.D, C);
-    else
-        hipLaunchKernelGGL((reverse_chunk_replay_kernel<DT, false>), grid, dim3(kBlk), 0, st, a,
-                           out, g, fut, h0, ga, gb, s.B, s.T, s.D, C);
+    dispatch2(al, reset != nullptr, [&](auto AL, auto RS) {
+        hipLaunchKernelGGL((reverse_chunk_replay_kernel<DT, decltype(AL)::value, decltype(RS)::value>),
+                           grid, dim3(kBlk), 0, st, a, out, g, reset, fut, h0, ga, gb, s.B, s.T,
+                           s.D, C);
+    });
     return hipGetLastError();
 }
 
@@ -405,10 +430,10 @@ hipError_t prefix_t(bool rev, int64_t B, int64_t NC, int64_t D, const float* P, 
 
 }  // namespace
 
-hipError_t launch_chunk_summary(const Shape& s, int chunk, const void* a, const void* b, float* P,
-                                float* Q, hipStream_t st) {
-    return s.dtype == DT_F32 ? summary_t<DT_F32>(s, chunk, a, b, P, Q, false, st)
-                             : summary_t<DT_BF16>(s, chunk, a, b, P, Q, false, st);
+hipError_t launch_chunk_summary(const Shape& s, int chunk, const void* a, const void* b,
+                                const uint8_t* reset, float* P, float* Q, hipStream_t st) {
+    return s.dtype == DT_F32 ? summary_t<DT_F32>(s, chunk, a, b, reset, P, Q, false, st)
+                             : summary_t<DT_BF16>(s, chunk, a, b, reset, P, Q, false, st);
 }
 
 hipError_t launch_chunk_prefix(int64_t B, int64_t NC, int64_t D, const float* P, const float* Q,
@@ -417,15 +442,16 @@ hipError_t launch_chunk_prefix(int64_t B, int64_t NC, int64_t D, const float* P,
 }
 
 hipError_t launch_chunk_replay(const Shape& s, int chunk, const void* a, const void* b,
-                               const float* chunk_in, void* out, float* last, hipStream_t st) {
-    return s.dtype == DT_F32 ? replay_t<DT_F32>(s, chunk, a, b, chunk_in, out, last, st)
-                             : replay_t<DT_BF16>(s, chunk, a, b, chunk_in, out, last, st);
+                               const uint8_t* reset, const float* chunk_in, void* out, float* last,
+                               hipStream_t st) {
+    return s.dtype == DT_F32 ? replay_t<DT_F32>(s, chunk, a, b, reset, chunk_in, out, last, st)
+                             : replay_t<DT_BF16>(s, chunk, a, b, reset, chunk_in, out, last, st);
 }
 
 hipError_t launch_reverse_chunk_summary(const Shape& s, int chunk, const void* a, const void* g,
-                                        float* P, float* Q, hipStream_t st) {
-    return s.dtype == DT_F32 ? summary_t<DT_F32>(s, chunk, a, g, P, Q, true, st)
-                             : summary_t<DT_BF16>(s, chunk, a, g, P, Q, true, st);
+                                        const uint8_t* reset, float* P, float* Q, hipStream_t st) {
+    return s.dtype == DT_F32 ? summary_t<DT_F32>(s, chunk, a, g, reset, P, Q, true, st)
+                             : summary_t<DT_BF16>(s, chunk, a, g, reset, P, Q, true, st);
 }
 
 hipError_t launch_reverse_chunk_prefix(int64_t B, int64_t NC, int64_t D, const float* P,
@@ -435,11 +461,12 @@ hipError_t launch_reverse_chunk_prefix(int64_t B, int64_t NC, int64_t D, const f
 }
 
 hipError_t launch_reverse_chunk_replay(const Shape& s, int chunk, const void* a, const void* out,
-                                       const void* g, const float* future, const float* h0,
-                                       void* grad_a, void* grad_b, hipStream_t st) {
+                                       const void* g, const uint8_t* reset, const float* future,
+                                       const float* h0, void* grad_a, void* grad_b,
+                                       hipStream_t st) {
     return s.dtype == DT_F32
-               ? reverse_replay_t<DT_F32>(s, chunk, a, out, g, future, h0, grad_a, grad_b, st)
-               : reverse_replay_t<DT_BF16>(s, chunk, a, out, g, future, h0, grad_a, grad_b, st);
+               ? reverse_replay_t<DT_F32>(s, chunk, a, out, g, reset, future, h0, grad_a, grad_b, st)
+               : reverse_replay_t<DT_BF16>(s, chunk, a, out, g, reset, future, h0, grad_a, grad_b, st);
 }
 
 }  // namespace lrscan

@@ -176,6 +176,14 @@ __device__ __forceinline__ uint32_t row_off(const Geo& g, int row, int T, uint32
     return (uint32_t)(rc - g.trow0) * rowbytes + g.coff;
 }
 
+// Segment-start byte of row i of this thread's segment (rows past T read the
+// last row; their steps are identity steps anyway).
+__device__ __forceinline__ uint32_t reset_byte(const uint8_t* reset, const Geo& g, int i, int T) {
+    const int row = g.row0 + i;
+    const int rc = row < T ? row : T - 1;
+    return reset[(size_t)g.bi * T + rc];
+}
+
 // Ticket, phase and the number of words to clear, read once per workgroup.
 struct Ticket {
     uint32_t ticket, phase;
@@ -362,6 +370,7 @@ struct FwdArgs {
     void* out;
     float* last;
     const float* h0;
+    const uint8_t* reset;  // [B, T] segment starts, or NULL
     Scratch sc;
     Dims d;
     uint32_t polls;
@@ -373,6 +382,7 @@ struct BwdArgs {
     const void* g;
     const float* grad_last;
     const float* h0;
+    const uint8_t* reset;  // [B, T] segment starts, or NULL
     void* grad_a;
     void* grad_b;
     float* grad_h0;
@@ -410,6 +420,7 @@ __device__ Aff fwd_tile_map(const FwdArgs& x, int j, int bi, int col) {
                     const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes);  // same tile in every lane
                     at = Elem<C::DT>::load1(a0 + ro + coff, 0);
                     bt = Elem<C::DT>::load1(b0 + ro + coff, 0);
+                    if (x.reset && x.reset[(size_t)bi * x.d.T + r]) at = 0.0f;
                 }
                 t.p = at * t.p;
                 t.q = fmaf(at, t.q, bt);
@@ -447,6 +458,7 @@ __device__ Aff bwd_tile_map(const BwdArgs& x, int j, int bi, int col) {
                     const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes);  // same tile in every lane
                     at = Elem<C::DT>::load1(a0 + ro + coff, 0);
                     gt = Elem<C::DT>::load1(g0 + ro + coff, 0);
+                    if (x.reset && x.reset[(size_t)bi * x.d.T + r]) at = 0.0f;
                 }
                 t.p = at * t.p;
                 t.q = at * (t.q + gt);
@@ -461,7 +473,7 @@ __device__ Aff bwd_tile_map(const BwdArgs& x, int j, int bi, int col) {
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <class C, bool ALIGNED>
+template <class C, bool ALIGNED, bool RST>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC_F)))
 void fused_fwd_kernel(FwdArgs x) {
     constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
@@ -484,6 +496,11 @@ void fused_fwd_kernel(FwdArgs x) {
 
     // every load is issued before any is used; rows past T and lanes past D
     // are read from valid addresses and replaced by identity steps below
+    uint32_t rs[NR];
+    if constexpr (RST) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) rs[i] = reset_byte(x.reset, g, i, d.T);
+    }
     RowVec<C::DT> ra[NR], rb[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -492,6 +509,12 @@ void fused_fwd_kernel(FwdArgs x) {
         rb[i] = load_vec<C::DT, ALIGNED>(pb, off, g.nvalid, 0.0f);
     }
     clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
+    if constexpr (RST) {
+        // a segment start drops the entering state: its transition becomes 0
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+            if (rs[i]) ra[i] = RowVec<C::DT>::splat(0.0f);
+    }
 
     // summary of this thread's rows, per lane (rows outer, so only one row
     // is widened to fp32 at a time), then the wavefront scan over its RG
@@ -580,7 +603,7 @@ void fused_fwd_kernel(FwdArgs x) {
 // ---------------------------------------------------------------------------
 // reverse time (backward)
 // ---------------------------------------------------------------------------
-template <class C, bool ALIGNED>
+template <class C, bool ALIGNED, bool RST>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC_B)))
 void fused_bwd_kernel(BwdArgs x) {
     constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
@@ -606,6 +629,11 @@ void fused_bwd_kernel(BwdArgs x) {
     char* pga = static_cast<char*>(x.grad_a) + g.tbase;
     char* pgb = static_cast<char*>(x.grad_b) + g.tbase;
 
+    uint32_t rs[NR];
+    if constexpr (RST) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) rs[i] = reset_byte(x.reset, g, i, d.T);
+    }
     RowVec<C::DT> ra[NR], rg_[NR], rh[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -619,6 +647,19 @@ void fused_bwd_kernel(BwdArgs x) {
         rh[i] = load_vec<C::DT, ALIGNED>(ph, hoff, g.nvalid, 0.0f);
     }
     clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
+    // at a segment start a_t is not used: its transition is 0 (no adjoint
+    // crosses it) and grad_a_t = 0 (the previous state is taken as 0)
+    uint32_t rbits = 0;
+    if constexpr (RST) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            if (rs[i]) {
+                ra[i] = RowVec<C::DT>::splat(0.0f);
+                rh[i] = RowVec<C::DT>::splat(0.0f);
+                rbits |= 1u << i;
+            }
+        }
+    }
 
     // reverse summary: the map from the carry entering the segment on the
     // right to the carry a_s*lambda_s leaving its first row s
@@ -697,7 +738,8 @@ void fused_bwd_kernel(BwdArgs x) {
                 const float an = (i + 1 < NR && after) ? ra[i + 1 < NR ? i + 1 : i].get(j) : 1.0f;
                 lam[j] = fmaf(an, lam[j], rg_[i].get(j));
                 float hp = rh[i].get(j);
-                if (row == 0) hp = (x.h0 && j < g.nvalid) ? x.h0[(size_t)g.bi * d.D + g.d0 + j] : 0.0f;
+                if (row == 0 && !((rbits >> i) & 1u))
+                    hp = (x.h0 && j < g.nvalid) ? x.h0[(size_t)g.bi * d.D + g.d0 + j] : 0.0f;
                 ob.v[j] = lam[j];
                 oa.v[j] = lam[j] * hp;
             }
@@ -813,13 +855,19 @@ hipError_t prepare(void* ws, size_t ws_bytes, bool init, const Layout& L, hipStr
 template <int DT, int TPR, int NR, int WAVES, int LB, bool AL>
 void launch_fwd_cfg(const FwdArgs& x0, hipStream_t st) {
     using C = Cfg<DT, TPR, NR, WAVES, LB>;
-    hipLaunchKernelGGL((fused_fwd_kernel<C, AL>), dim3(x0.sc.total_tiles), dim3(C::NT), 0, st, x0);
+    if (x0.reset)
+        hipLaunchKernelGGL((fused_fwd_kernel<C, AL, true>), dim3(x0.sc.total_tiles), dim3(C::NT), 0, st, x0);
+    else
+        hipLaunchKernelGGL((fused_fwd_kernel<C, AL, false>), dim3(x0.sc.total_tiles), dim3(C::NT), 0, st, x0);
 }
 
 template <int DT, int TPR, int NR, int WAVES, int LB, bool AL>
 void launch_bwd_cfg(const BwdArgs& x, hipStream_t st) {
     using C = Cfg<DT, TPR, NR, WAVES, LB>;
-    hipLaunchKernelGGL((fused_bwd_kernel<C, AL>), dim3(x.sc.total_tiles), dim3(C::NT), 0, st, x);
+    if (x.reset)
+        hipLaunchKernelGGL((fused_bwd_kernel<C, AL, true>), dim3(x.sc.total_tiles), dim3(C::NT), 0, st, x);
+    else
+        hipLaunchKernelGGL((fused_bwd_kernel<C, AL, false>), dim3(x.sc.total_tiles), dim3(C::NT), 0, st, x);
 }
 
 // Unaligned rows (D * elem_bytes not a multiple of 16, or unaligned pointers)
@@ -896,8 +944,8 @@ size_t fused_workspace_bytes(const Shape& s, int width, int tile) {
 }
 
 hipError_t launch_fused_fwd(const Shape& s, int width, int tile, const void* a, const void* b,
-                            void* out, float* last, const float* h0, void* ws, size_t ws_bytes,
-                            bool init, int polls, hipStream_t st) {
+                            void* out, float* last, const float* h0, const uint8_t* reset,
+                            void* ws, size_t ws_bytes, bool init, int polls, hipStream_t st) {
     const TileCfg* c = find_cfg(0, width, tile);
     if (!c) return hipErrorInvalidValue;
     const Layout L = layout_of(s, width, tile);
@@ -909,6 +957,7 @@ hipError_t launch_fused_fwd(const Shape& s, int width, int tile, const void* a, 
     x.out = out;
     x.last = last;
     x.h0 = h0;
+    x.reset = reset;
     x.d = Dims{(int)s.T, (int)s.D, L.nW, L.nS, L.NK};
     x.polls = polls > 0 ? (uint32_t)polls : kDefaultPolls;
     const void* ptrs[3] = {a, b, out};
@@ -920,9 +969,9 @@ hipError_t launch_fused_fwd(const Shape& s, int width, int tile, const void* a, 
 }
 
 hipError_t launch_fused_bwd(const Shape& s, int width, int tile, const void* a, const void* out,
-                            const void* g, const float* grad_last, const float* h0, void* grad_a,
-                            void* grad_b, float* grad_h0, void* ws, size_t ws_bytes, bool init,
-                            int polls, hipStream_t st) {
+                            const void* g, const float* grad_last, const float* h0,
+                            const uint8_t* reset, void* grad_a, void* grad_b, float* grad_h0,
+                            void* ws, size_t ws_bytes, bool init, int polls, hipStream_t st) {
     const TileCfg* c = find_cfg(1, width, tile);
     if (!c) return hipErrorInvalidValue;
     const Layout L = layout_of(s, width, tile);
@@ -934,6 +983,7 @@ hipError_t launch_fused_bwd(const Shape& s, int width, int tile, const void* a, 
     x.g = g;
     x.grad_last = grad_last;
     x.h0 = h0;
+    x.reset = reset;
     x.grad_a = grad_a;
     x.grad_b = grad_b;
     x.grad_h0 = grad_h0;

@@ -21,27 +21,31 @@ struct Shape {
 bool rows_aligned(const Shape& s, const void* const* ptrs, int n);
 
 // ---- per-lane sequential walk ---------------------------------------------
+// `reset` ([B, T] bytes, or NULL) marks segment starts, where the step's
+// transition is taken as 0 (every launcher below that takes it).
 hipError_t launch_seq_fwd(const Shape& s, const void* a, const void* b, void* out, float* last,
-                          const float* h0, hipStream_t st);
+                          const float* h0, const uint8_t* reset, hipStream_t st);
 hipError_t launch_seq_bwd(const Shape& s, const void* a, const void* out, const void* g,
-                          const float* grad_last, const float* h0, void* grad_a, void* grad_b,
-                          float* grad_h0, hipStream_t st);
+                          const float* grad_last, const float* h0, const uint8_t* reset,
+                          void* grad_a, void* grad_b, float* grad_h0, hipStream_t st);
 
 // ---- three-launch chunked form ----------------------------------------------
-hipError_t launch_chunk_summary(const Shape& s, int chunk, const void* a, const void* b, float* P,
-                                float* Q, hipStream_t st);
+hipError_t launch_chunk_summary(const Shape& s, int chunk, const void* a, const void* b,
+                                const uint8_t* reset, float* P, float* Q, hipStream_t st);
 hipError_t launch_chunk_prefix(int64_t B, int64_t NC, int64_t D, const float* P, const float* Q,
                                const float* h0, float* chunk_in, float* last, hipStream_t st);
 hipError_t launch_chunk_replay(const Shape& s, int chunk, const void* a, const void* b,
-                               const float* chunk_in, void* out, float* last, hipStream_t st);
+                               const uint8_t* reset, const float* chunk_in, void* out, float* last,
+                               hipStream_t st);
 hipError_t launch_reverse_chunk_summary(const Shape& s, int chunk, const void* a, const void* g,
-                                        float* P, float* Q, hipStream_t st);
+                                        const uint8_t* reset, float* P, float* Q, hipStream_t st);
 hipError_t launch_reverse_chunk_prefix(int64_t B, int64_t NC, int64_t D, const float* P,
                                        const float* Q, const float* grad_last, float* future,
                                        float* grad_h0, hipStream_t st);
 hipError_t launch_reverse_chunk_replay(const Shape& s, int chunk, const void* a, const void* out,
-                                       const void* g, const float* future, const float* h0,
-                                       void* grad_a, void* grad_b, hipStream_t st);
+                                       const void* g, const uint8_t* reset, const float* future,
+                                       const float* h0, void* grad_a, void* grad_b,
+                                       hipStream_t st);
 
 // ---- single-launch fused form ----------------------------------------------
 // A configuration is (width, tile): width threads of 16 bytes cover one row of
@@ -57,11 +61,11 @@ size_t fused_workspace_bytes(const Shape& s, int width, int tile);
 // default) bounds how often a tile polls for its predecessors before it
 // derives their missing maps itself; results are bitwise the same either way.
 hipError_t launch_fused_fwd(const Shape& s, int width, int tile, const void* a, const void* b,
-                            void* out, float* last, const float* h0, void* ws, size_t ws_bytes,
-                            bool init, int polls, hipStream_t st);
+                            void* out, float* last, const float* h0, const uint8_t* reset,
+                            void* ws, size_t ws_bytes, bool init, int polls, hipStream_t st);
 hipError_t launch_fused_bwd(const Shape& s, int width, int tile, const void* a, const void* out,
-                            const void* g, const float* grad_last, const float* h0, void* grad_a,
-                            void* grad_b, float* grad_h0, void* ws, size_t ws_bytes, bool init,
-                            int polls, hipStream_t st);
+                            const void* g, const float* grad_last, const float* h0,
+                            const uint8_t* reset, void* grad_a, void* grad_b, float* grad_h0,
+                            void* ws, size_t ws_bytes, bool init, int polls, hipStream_t st);
 
 }  // namespace lrscan

@@ -17,12 +17,15 @@ namespace {
 constexpr int kSeqBlock = 256;
 constexpr int kSeqU = 8;  // rows in flight per buffer
 
-template <int DT, bool ALIGNED>
+// RST: `reset` ([B, T] bytes) marks segment starts, where the step's
+// transition is taken as 0 (the entering state is dropped).
+template <int DT, bool ALIGNED, bool RST>
 __global__ __launch_bounds__(kSeqBlock) void seq_fwd_kernel(const void* __restrict__ a,
                                                             const void* __restrict__ b,
                                                             void* __restrict__ out,
                                                             float* __restrict__ last,
                                                             const float* __restrict__ h0,
+                                                            const uint8_t* __restrict__ reset,
                                                             int64_t B, int64_t T, int64_t D,
                                                             int64_t vpr) {
     constexpr int V = Elem<DT>::V;
@@ -38,12 +41,15 @@ __global__ __launch_bounds__(kSeqBlock) void seq_fwd_kernel(const void* __restri
 #pragma unroll
     for (int j = 0; j < V; ++j) h[j] = (h0 && j < nvalid) ? h0[bi * D + d0 + j] : 0.0f;
 
+    const uint8_t* rrow = RST ? reset + (size_t)bi * (size_t)T : nullptr;
     RowVec<DT> ca[U], cb[U], na[U], nb[U];
+    uint32_t cr[U], nr[U];  // segment-start bytes of the buffered rows (RST)
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (u < T) {
             ca[u] = load_row<DT, ALIGNED>(a, base + (size_t)u * D, nvalid, 1.0f);
             cb[u] = load_row<DT, ALIGNED>(b, base + (size_t)u * D, nvalid, 0.0f);
+            if (RST) cr[u] = rrow[u];
         }
     }
     for (int64_t t0 = 0; t0 < T; t0 += U) {
@@ -53,6 +59,7 @@ __global__ __launch_bounds__(kSeqBlock) void seq_fwd_kernel(const void* __restri
             if (tn + u < T) {
                 na[u] = load_row<DT, ALIGNED>(a, base + (size_t)(tn + u) * D, nvalid, 1.0f);
                 nb[u] = load_row<DT, ALIGNED>(b, base + (size_t)(tn + u) * D, nvalid, 0.0f);
+                if (RST) nr[u] = rrow[tn + u];
             }
         }
 #pragma unroll
@@ -61,7 +68,8 @@ __global__ __launch_bounds__(kSeqBlock) void seq_fwd_kernel(const void* __restri
                 RowOut<DT> o;
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
-                    h[j] = fmaf(ca[u].get(j), h[j], cb[u].get(j));
+                    const float at = (RST && cr[u]) ? 0.0f : ca[u].get(j);
+                    h[j] = fmaf(at, h[j], cb[u].get(j));
                     o.v[j] = h[j];
                 }
                 store_row<DT, ALIGNED>(out, base + (size_t)(t0 + u) * D, nvalid, o);
@@ -71,6 +79,7 @@ __global__ __launch_bounds__(kSeqBlock) void seq_fwd_kernel(const void* __restri
         for (int u = 0; u < U; ++u) {
             ca[u] = na[u];
             cb[u] = nb[u];
+            if (RST) cr[u] = nr[u];
         }
     }
     if (last) {
@@ -80,12 +89,14 @@ __global__ __launch_bounds__(kSeqBlock) void seq_fwd_kernel(const void* __restri
     }
 }
 
-template <int DT, bool ALIGNED>
+// RST: at a segment start a_t is not used (its transition is 0), so no
+// adjoint crosses it and grad_a_t = 0.
+template <int DT, bool ALIGNED, bool RST>
 __global__ __launch_bounds__(kSeqBlock) void seq_bwd_kernel(
     const void* __restrict__ a, const void* __restrict__ out, const void* __restrict__ g,
-    const float* __restrict__ grad_last, const float* __restrict__ h0, void* __restrict__ grad_a,
-    void* __restrict__ grad_b, float* __restrict__ grad_h0, int64_t B, int64_t T, int64_t D,
-    int64_t vpr) {
+    const float* __restrict__ grad_last, const float* __restrict__ h0,
+    const uint8_t* __restrict__ reset, void* __restrict__ grad_a, void* __restrict__ grad_b,
+    float* __restrict__ grad_h0, int64_t B, int64_t T, int64_t D, int64_t vpr) {
     constexpr int V = Elem<DT>::V;
     constexpr int U = kSeqU;
     const int64_t gid = (int64_t)blockIdx.x * kSeqBlock + threadIdx.x;
@@ -103,8 +114,11 @@ __global__ __launch_bounds__(kSeqBlock) void seq_bwd_kernel(
     }
 
     // block u of a buffer holds row t0 - u (walking down)
+    const uint8_t* rrow = RST ? reset + (size_t)bi * (size_t)T : nullptr;
     RowVec<DT> ca[U], cg[U], ch[U], na[U], ng[U], nh[U];
-    auto load_block = [&](int64_t top, RowVec<DT>* ra, RowVec<DT>* rg, RowVec<DT>* rh) {
+    uint32_t cr[U], nr[U];  // segment-start bytes of the buffered rows (RST)
+    auto load_block = [&](int64_t top, RowVec<DT>* ra, RowVec<DT>* rg, RowVec<DT>* rh,
+                          uint32_t* rr) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t t = top - u;
@@ -112,12 +126,13 @@ __global__ __launch_bounds__(kSeqBlock) void seq_bwd_kernel(
                 ra[u] = load_row<DT, ALIGNED>(a, base + (size_t)t * D, nvalid, 1.0f);
                 rg[u] = load_row<DT, ALIGNED>(g, base + (size_t)t * D, nvalid, 0.0f);
                 if (t >= 1) rh[u] = load_row<DT, ALIGNED>(out, base + (size_t)(t - 1) * D, nvalid, 0.0f);
+                if (RST) rr[u] = rrow[t];
             }
         }
     };
-    load_block(T - 1, ca, cg, ch);
+    load_block(T - 1, ca, cg, ch, cr);
     for (int64_t top = T - 1; top >= 0; top -= U) {
-        if (top - U >= 0) load_block(top - U, na, ng, nh);
+        if (top - U >= 0) load_block(top - U, na, ng, nh, nr);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t t = top - u;
@@ -126,14 +141,17 @@ __global__ __launch_bounds__(kSeqBlock) void seq_bwd_kernel(
                 // lambda_t = g_t + a_{t+1}*lambda_{t+1}: one fma with the a of
                 // row t+1 inside a block; across blocks carry[] holds the
                 // product a_{t+1}*lambda_{t+1}
+                const int up = u > 0 ? u - 1 : 0;
+                const bool rs = RST && cr[u];
 #pragma unroll
                 for (int j = 0; j < V; ++j) {
-                    const float an = u > 0 ? ca[u > 0 ? u - 1 : 0].get(j) : 1.0f;
+                    const float an = u > 0 ? ((RST && cr[up]) ? 0.0f : ca[up].get(j)) : 1.0f;
                     const float lam = fmaf(an, carry[j], cg[u].get(j));
-                    const float hp = (t >= 1) ? ch[u].get(j) : hinit[j];
+                    const float hp = rs ? 0.0f : ((t >= 1) ? ch[u].get(j) : hinit[j]);
                     ob.v[j] = lam;
                     oa.v[j] = lam * hp;
-                    carry[j] = (u == U - 1 || t == 0) ? ca[u].get(j) * lam : lam;
+                    const float at = rs ? 0.0f : ca[u].get(j);
+                    carry[j] = (u == U - 1 || t == 0) ? at * lam : lam;
                 }
                 store_row<DT, ALIGNED>(grad_a, base + (size_t)t * D, nvalid, oa);
                 store_row<DT, ALIGNED>(grad_b, base + (size_t)t * D, nvalid, ob);
@@ -144,6 +162,7 @@ __global__ __launch_bounds__(kSeqBlock) void seq_bwd_kernel(
             ca[u] = na[u];
             cg[u] = ng[u];
             ch[u] = nh[u];
+            if (RST) cr[u] = nr[u];
         }
     }
     if (grad_h0) {
@@ -158,36 +177,54 @@ int64_t vecs_per_row(int64_t D) {
     return (D + Elem<DT>::V - 1) / Elem<DT>::V;
 }
 
+template <int DT, bool AL, bool RST>
+void seq_fwd_launch(const Shape& s, dim3 grid, const void* a, const void* b, void* out,
+                    float* last, const float* h0, const uint8_t* reset, int64_t vpr,
+                    hipStream_t st) {
+    hipLaunchKernelGGL((seq_fwd_kernel<DT, AL, RST>), grid, dim3(kSeqBlock), 0, st, a, b, out,
+                       last, h0, reset, s.B, s.T, s.D, vpr);
+}
+
 template <int DT>
 hipError_t seq_fwd_t(const Shape& s, const void* a, const void* b, void* out, float* last,
-                     const float* h0, hipStream_t st) {
+                     const float* h0, const uint8_t* reset, hipStream_t st) {
     const void* ptrs[3] = {a, b, out};
     const int64_t vpr = vecs_per_row<DT>(s.D);
     const int64_t threads = s.B * vpr;
     const dim3 grid((unsigned)((threads + kSeqBlock - 1) / kSeqBlock));
-    if (rows_aligned(s, ptrs, 3))
-        hipLaunchKernelGGL((seq_fwd_kernel<DT, true>), grid, dim3(kSeqBlock), 0, st, a, b, out,
-                           last, h0, s.B, s.T, s.D, vpr);
-    else
-        hipLaunchKernelGGL((seq_fwd_kernel<DT, false>), grid, dim3(kSeqBlock), 0, st, a, b, out,
-                           last, h0, s.B, s.T, s.D, vpr);
+    const bool al = rows_aligned(s, ptrs, 3);
+    if (al && reset) seq_fwd_launch<DT, true, true>(s, grid, a, b, out, last, h0, reset, vpr, st);
+    else if (al) seq_fwd_launch<DT, true, false>(s, grid, a, b, out, last, h0, reset, vpr, st);
+    else if (reset) seq_fwd_launch<DT, false, true>(s, grid, a, b, out, last, h0, reset, vpr, st);
+    else seq_fwd_launch<DT, false, false>(s, grid, a, b, out, last, h0, reset, vpr, st);
     return hipGetLastError();
+}
+
+template <int DT, bool AL, bool RST>
+void seq_bwd_launch(const Shape& s, dim3 grid, const void* a, const void* out, const void* g,
+                    const float* grad_last, const float* h0, const uint8_t* reset, void* grad_a,
+                    void* grad_b, float* grad_h0, int64_t vpr, hipStream_t st) {
+    hipLaunchKernelGGL((seq_bwd_kernel<DT, AL, RST>), grid, dim3(kSeqBlock), 0, st, a, out, g,
+                       grad_last, h0, reset, grad_a, grad_b, grad_h0, s.B, s.T, s.D, vpr);
 }
 
 template <int DT>
 hipError_t seq_bwd_t(const Shape& s, const void* a, const void* out, const void* g,
-                     const float* grad_last, const float* h0, void* grad_a, void* grad_b,
-                     float* grad_h0, hipStream_t st) {
+                     const float* grad_last, const float* h0, const uint8_t* reset, void* grad_a,
+                     void* grad_b, float* grad_h0, hipStream_t st) {
     const void* ptrs[5] = {a, out, g, grad_a, grad_b};
     const int64_t vpr = vecs_per_row<DT>(s.D);
     const int64_t threads = s.B * vpr;
     const dim3 grid((unsigned)((threads + kSeqBlock - 1) / kSeqBlock));
-    if (rows_aligned(s, ptrs, 5))
-        hipLaunchKernelGGL((seq_bwd_kernel<DT, true>), grid, dim3(kSeqBlock), 0, st, a, out, g,
-                           grad_last, h0, grad_a, grad_b, grad_h0, s.B, s.T, s.D, vpr);
+    const bool al = rows_aligned(s, ptrs, 5);
+    if (al && reset)
+        seq_bwd_launch<DT, true, true>(s, grid, a, out, g, grad_last, h0, reset, grad_a, grad_b, grad_h0, vpr, st);
+    else if (al)
+        seq_bwd_launch<DT, true, false>(s, grid, a, out, g, grad_last, h0, reset, grad_a, grad_b, grad_h0, vpr, st);
+    else if (reset)
+        seq_bwd_launch<DT, false, true>(s, grid, a, out, g, grad_last, h0, reset, grad_a, grad_b, grad_h0, vpr, st);
     else
-        hipLaunchKernelGGL((seq_bwd_kernel<DT, false>), grid, dim3(kSeqBlock), 0, st, a, out, g,
-                           grad_last, h0, grad_a, grad_b, grad_h0, s.B, s.T, s.D, vpr);
+        seq_bwd_launch<DT, false, false>(s, grid, a, out, g, grad_last, h0, reset, grad_a, grad_b, grad_h0, vpr, st);
     return hipGetLastError();
 }
 
@@ -202,17 +239,17 @@ bool rows_aligned(const Shape& s, const void* const* ptrs, int n) {
 }
 
 hipError_t launch_seq_fwd(const Shape& s, const void* a, const void* b, void* out, float* last,
-                          const float* h0, hipStream_t st) {
-    return s.dtype == DT_F32 ? seq_fwd_t<DT_F32>(s, a, b, out, last, h0, st)
-                             : seq_fwd_t<DT_BF16>(s, a, b, out, last, h0, st);
+                          const float* h0, const uint8_t* reset, hipStream_t st) {
+    return s.dtype == DT_F32 ? seq_fwd_t<DT_F32>(s, a, b, out, last, h0, reset, st)
+                             : seq_fwd_t<DT_BF16>(s, a, b, out, last, h0, reset, st);
 }
 
 hipError_t launch_seq_bwd(const Shape& s, const void* a, const void* out, const void* g,
-                          const float* grad_last, const float* h0, void* grad_a, void* grad_b,
-                          float* grad_h0, hipStream_t st) {
+                          const float* grad_last, const float* h0, const uint8_t* reset,
+                          void* grad_a, void* grad_b, float* grad_h0, hipStream_t st) {
     return s.dtype == DT_F32
-               ? seq_bwd_t<DT_F32>(s, a, out, g, grad_last, h0, grad_a, grad_b, grad_h0, st)
-               : seq_bwd_t<DT_BF16>(s, a, out, g, grad_last, h0, grad_a, grad_b, grad_h0, st);
+               ? seq_bwd_t<DT_F32>(s, a, out, g, grad_last, h0, reset, grad_a, grad_b, grad_h0, st)
+               : seq_bwd_t<DT_BF16>(s, a, out, g, grad_last, h0, reset, grad_a, grad_b, grad_h0, st);
 }
 
 }  // namespace lrscan
