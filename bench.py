@@ -102,6 +102,57 @@ def cpu_baseline(inp, budget_s=10.0):
     }
 
 
+def inference_line(args, wl, lr, torch, a, b, dt):
+    """JSON line of the state-only forward (prefill) or of the decode step."""
+    B, T, D = wl.B, wl.T, wl.D
+    s = wl.itemsize
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    last = torch.empty((B, D), device="cuda", dtype=torch.float32)
+    if args.mode == "prefill":
+        o = lr.make_opts(algo=args.algo, chunk=args.fwd_chunk, width=args.fwd_width)
+
+        def fn():
+            lr.scan_fwd_ex(a.data_ptr(), b.data_ptr(), None, last.data_ptr(), B, T, D, dt, sh, o)
+        nbytes = 2 * s * B * T * D + 4 * B * D
+        unit_note = "state-only forward: reads a and b, writes the fp32 last state"
+    else:
+        # one token: a[:, t], b[:, t] as [B, D] (a strided view is made contiguous once)
+        at = a[:, T // 2].contiguous()
+        bt = b[:, T // 2].contiguous()
+        state = torch.zeros((B, D), device="cuda", dtype=torch.float32)
+        out = torch.empty_like(at)
+
+        def fn():
+            lr.scan_step(at.data_ptr(), bt.data_ptr(), state.data_ptr(), None, out.data_ptr(),
+                         state.data_ptr(), B, D, dt, sh)
+        nbytes = (3 * s + 8) * B * D
+        unit_note = "one decode step: reads a, b and the fp32 state, writes out and the state"
+    for _ in range(args.warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": f"{args.mode}: effective HBM GB/s",
+        "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded numpy draws, see workloads/__init__.py)",
+        "config": {"workload": f"{wl.name}: {WORKLOAD_TEXT[wl.name]}", "B": B, "T": T, "D": D,
+                   "mode": unit_note},
+        "us_per_call": round(ms * 1e3, 2),
+        "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +164,10 @@ def main():
     ap.add_argument("--bwd-chunk", type=int, default=0)
     ap.add_argument("--fwd-width", type=int, default=0)
     ap.add_argument("--bwd-width", type=int, default=0)
+    ap.add_argument("--mode", default="train", choices=["train", "prefill", "decode"],
+                    help="train: forward + backward (the default line); prefill: the state-only "
+                         "forward (reads a and b, writes last); decode: one scan_step per token "
+                         "on the workload's [B, D] lanes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (the reference for HBM byte counters)")
@@ -157,6 +212,9 @@ def main():
 
     a, b, g = dev(inp.a), dev(inp.b), dev(inp.g)
     B, T, D = wl.B, wl.T, wl.D
+    if args.mode != "train":
+        print(json.dumps(inference_line(args, wl, lr, torch, a, b, dt)), flush=True)
+        return
     out = torch.empty_like(a)
     ga = torch.empty_like(a)
     gb = torch.empty_like(a)

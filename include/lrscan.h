@@ -102,9 +102,12 @@ typedef struct {
 
 /*
  * scan_fwd: out = every state of the scan of (a, b); last = the final state.
- *   a, b  [B,T,D] dtype, read only.     out  [B,T,D] dtype, written.
- *   last  [B,D] fp32, written; may be NULL.
- * Returns LRSCAN_OK or a negative status.
+ *   a, b  [B,T,D] dtype, read only.     out  [B,T,D] dtype, written; may be NULL
+ *   when last is given (a state-only forward, e.g. a prefill that keeps only
+ *   the final state: no [B,T,D] output is written, and last is bitwise the
+ *   one the full forward gives).
+ *   last  [B,D] fp32, written; may be NULL when out is given.
+ * Returns LRSCAN_OK or a negative status (LRSCAN_ERR_NULL if both are NULL).
  */
 LRSCAN_API int scan_fwd(const void* a, const void* b, void* out, float* last, int64_t B, int64_t T,
                         int64_t D, int dtype, void* stream);
@@ -125,6 +128,25 @@ LRSCAN_API int scan_fwd_ex(const void* a, const void* b, void* out, float* last,
 LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
                            const float* grad_last, void* grad_a, void* grad_b, int64_t B,
                            int64_t T, int64_t D, int dtype, void* stream, const lrscan_opts* opts);
+
+/*
+ * scan_step: one time step of the recurrence on [B, D] lanes, for decoding
+ * token by token from a carried fp32 state (page "triton_training_scan.py",
+ * real_scan_with_last returns that fp32 final state for inference, and
+ * _samu_decode updates the state one token at a time in one launch):
+ *   h = a * state_in + b   (state_in NULL: zero;  reset[b] != 0: the state is
+ *                            dropped for batch row b, so h = b)
+ *   a, b       [B, D] dtype, read only (one step of the [B,T,D] inputs).
+ *   state_in   [B, D] fp32 or NULL.       reset  [B] bytes or NULL.
+ *   out        [B, D] dtype, written (h rounded to dtype); may be NULL.
+ *   state_out  [B, D] fp32, written (h); may be NULL; may equal state_in
+ *              (an in-place update).  At least one of out, state_out.
+ * Chaining T calls from a zero state gives bitwise the states and outputs of
+ * scan_fwd with LRSCAN_ALGO_SEQ.  Returns LRSCAN_OK or a negative status.
+ */
+LRSCAN_API int scan_step(const void* a, const void* b, const float* state_in,
+                         const uint8_t* reset, void* out, float* state_out, int64_t B, int64_t D,
+                         int dtype, void* stream);
 
 /* Bytes of workspace the call with these arguments needs (0 if none).
  * Returns 0 for invalid arguments. */

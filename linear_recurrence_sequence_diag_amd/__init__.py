@@ -60,6 +60,7 @@ _SIGS = {
     "scan_bwd_ex": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
     "scan_workspace_bytes": ([_I64, _I64, _I64, _INT, ctypes.POINTER(Opts)], ctypes.c_size_t),
     "scan_status_string": ([_INT], ctypes.c_char_p),
+    "scan_step": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P], _INT),
     "scan_auto_algo": ([_I64, _I64, _I64, _INT, _INT, ctypes.POINTER(_INT), ctypes.POINTER(_INT)],
                        _INT),
     "scan_chunk_summary": ([_P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P], _INT),
@@ -127,6 +128,11 @@ def scan_bwd_ex(a, out, grad_out, grad_last, grad_a, grad_b, B, T, D, dtype, str
     return _check(library().scan_bwd_ex(a, out, grad_out, grad_last, grad_a, grad_b, B, T, D, dtype,
                                         stream, ctypes.byref(opts) if opts is not None else None),
                   "scan_bwd_ex")
+
+
+def scan_step(a, b, state_in, reset, out, state_out, B, D, dtype, stream):
+    return _check(library().scan_step(a, b, state_in, reset, out, state_out, B, D, dtype, stream),
+                  "scan_step")
 
 
 def scan_workspace_bytes(B, T, D, dtype, opts=None):
@@ -249,19 +255,23 @@ def make_opts(algo="auto", chunk=0, h0=None, grad_h0=None, workspace=None, width
     return o
 
 
-def scan(a, b, h0=None, algo="auto", chunk=0, with_last=True, width=0, polls=0, reset=None):
+def scan(a, b, h0=None, algo="auto", chunk=0, with_last=True, width=0, polls=0, reset=None,
+         with_out=True):
     """Forward scan.  Returns (out, last); out has a's dtype, last is float32 [B, D].
-    ``reset`` ([B, T] bool/uint8) starts a new segment wherever it is set."""
+    ``reset`` ([B, T] bool/uint8) starts a new segment wherever it is set.
+    ``with_out=False`` runs the state-only forward (out is None)."""
     torch = _torch()
     _check_seq("a", a)
     _check_mask(reset, a)
     _check_seq("b", b, a)
     _check_state("h0", h0, a)
     B, T, D = a.shape
-    out = torch.empty_like(a)
+    if not (with_out or with_last):
+        raise ValueError("a forward needs out or last")
+    out = torch.empty_like(a) if with_out else None
     last = torch.empty((B, D), device=a.device, dtype=torch.float32) if with_last else None
     with torch.cuda.device(a.device):
-        scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), _ptr(last), B, T, D,
+        scan_fwd_ex(a.data_ptr(), b.data_ptr(), _ptr(out), _ptr(last), B, T, D,
                     dtype_code(a.dtype), _stream(a),
                     make_opts(algo, chunk, h0=h0, width=width, polls=polls, reset=reset))
     return out, last
@@ -288,6 +298,33 @@ def scan_backward(a, out, grad_out, grad_last=None, h0=None, algo="auto", chunk=
                     make_opts(algo, chunk, h0=h0, grad_h0=grad_h0, width=width, polls=polls,
                               reset=reset))
     return grad_a, grad_b, grad_h0
+
+
+def step(a, b, state=None, reset=None, with_out=True, out_state=None):
+    """One decoding step on [B, D]: h = a*state + b (state None: zero; rows
+    with reset set start from zero).  Returns (out in a's dtype or None,
+    the new float32 state).  ``out_state`` may be ``state`` (in place)."""
+    torch = _torch()
+    if not isinstance(a, torch.Tensor) or not a.is_cuda or a.dim() != 2 or not a.is_contiguous():
+        raise ValueError("a must be a contiguous CUDA (HIP) [B, D] tensor")
+    if not isinstance(b, torch.Tensor) or b.shape != a.shape or b.dtype != a.dtype or \
+            b.device != a.device or not b.is_contiguous():
+        raise ValueError("b must match a in shape, dtype and device")
+    B, D = a.shape
+    for name, t in (("state", state), ("out_state", out_state)):
+        if t is not None and (t.shape != (B, D) or t.dtype != torch.float32 or t.device != a.device
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [B, D] tensor on a's device")
+    if reset is not None and (reset.shape != (B,) or reset.dtype not in (torch.bool, torch.uint8)
+                              or reset.device != a.device or not reset.is_contiguous()):
+        raise ValueError("reset must be a contiguous bool or uint8 [B] tensor on a's device")
+    out = torch.empty_like(a) if with_out else None
+    new = out_state if out_state is not None else torch.empty((B, D), device=a.device,
+                                                              dtype=torch.float32)
+    with torch.cuda.device(a.device):
+        scan_step(a.data_ptr(), b.data_ptr(), _ptr(state), _ptr(reset), _ptr(out), new.data_ptr(),
+                  B, D, dtype_code(a.dtype), _stream(a))
+    return out, new
 
 
 def n_chunks(T, chunk):

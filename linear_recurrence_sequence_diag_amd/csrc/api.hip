@@ -222,7 +222,7 @@ LRSCAN_API size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t D, int dtyp
 
 LRSCAN_API int scan_fwd_ex(const void* a, const void* b, void* out, float* last, int64_t B,
                            int64_t T, int64_t D, int dtype, void* stream, const lrscan_opts* opts) {
-    if (!a || !b || !out) return LRSCAN_ERR_NULL;
+    if (!a || !b || (!out && !last)) return LRSCAN_ERR_NULL;
     if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
     const Shape s{B, T, D, dtype};
@@ -314,6 +314,16 @@ LRSCAN_API int scan_bwd(const void* a, const void* out, const void* grad_out,
                         int64_t D, int dtype, void* stream) {
     return scan_bwd_ex(a, out, grad_out, grad_last, grad_a, grad_b, B, T, D, dtype, stream,
                        nullptr);
+}
+
+LRSCAN_API int scan_step(const void* a, const void* b, const float* state_in,
+                         const uint8_t* reset, void* out, float* state_out, int64_t B, int64_t D,
+                         int dtype, void* stream) {
+    if (!a || !b || (!out && !state_out)) return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, 1, D)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
+    return hip_status(launch_step(B, D, dtype, a, b, state_in, reset, out, state_out,
+                                  static_cast<hipStream_t>(stream)));
 }
 
 // ---- the chunked form, step by step ---------------------------------------------

@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kBlk) void chunk_replay_kernel(
                     h[j] = fmaf(at, h[j], rb[u].get(j));
                     o.v[j] = h[j];
                 }
-                store_row<DT, ALIGNED>(out, base + (size_t)(t0 + u) * D, ci.nvalid, o);
+                if (out) store_row<DT, ALIGNED>(out, base + (size_t)(t0 + u) * D, ci.nvalid, o);
             }
     }
     if (last && ci.k == NC - 1) {

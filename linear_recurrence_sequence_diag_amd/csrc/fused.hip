@@ -473,7 +473,9 @@ __device__ Aff bwd_tile_map(const BwdArgs& x, int j, int bi, int col) {
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <class C, bool ALIGNED, bool RST>
+// OUT = false: state-only forward (no `out`): only the thread holding row T-1
+// of a lane replays, to write `last` exactly as the full forward does.
+template <class C, bool ALIGNED, bool RST, bool OUT>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC_F)))
 void fused_fwd_kernel(FwdArgs x) {
     constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
@@ -572,6 +574,11 @@ void fused_fwd_kernel(FwdArgs x) {
     }
     __syncthreads();
 
+    const bool ends = g.nrows > 0 && g.row0 + g.nrows == d.T;  // holds row T-1
+    if constexpr (!OUT) {
+        if (!(x.last && ends)) return;
+    }
+
     // replay from registers
     float h[V];
 #pragma unroll
@@ -590,10 +597,11 @@ void fused_fwd_kernel(FwdArgs x) {
                 h[j] = fmaf(ra[i].get(j), h[j], rb[i].get(j));
                 o.v[j] = h[j];
             }
-            store_vec<C::DT, ALIGNED>(po, row_off(g, g.row0 + i, d.T, rowbytes), g.nvalid, o);
+            if constexpr (OUT)
+                store_vec<C::DT, ALIGNED>(po, row_off(g, g.row0 + i, d.T, rowbytes), g.nvalid, o);
         }
     }
-    if (x.last && g.nrows > 0 && g.row0 + g.nrows == d.T) {
+    if (x.last && ends) {
 #pragma unroll
         for (int j = 0; j < V; ++j)
             if (j < g.nvalid) x.last[(size_t)g.bi * d.D + g.d0 + j] = h[j];
@@ -855,10 +863,14 @@ hipError_t prepare(void* ws, size_t ws_bytes, bool init, const Layout& L, hipStr
 template <int DT, int TPR, int NR, int WAVES, int LB, bool AL>
 void launch_fwd_cfg(const FwdArgs& x0, hipStream_t st) {
     using C = Cfg<DT, TPR, NR, WAVES, LB>;
-    if (x0.reset)
-        hipLaunchKernelGGL((fused_fwd_kernel<C, AL, true>), dim3(x0.sc.total_tiles), dim3(C::NT), 0, st, x0);
-    else
-        hipLaunchKernelGGL((fused_fwd_kernel<C, AL, false>), dim3(x0.sc.total_tiles), dim3(C::NT), 0, st, x0);
+    const dim3 grid(x0.sc.total_tiles), block(C::NT);
+    if (x0.out) {
+        if (x0.reset) hipLaunchKernelGGL((fused_fwd_kernel<C, AL, true, true>), grid, block, 0, st, x0);
+        else hipLaunchKernelGGL((fused_fwd_kernel<C, AL, false, true>), grid, block, 0, st, x0);
+    } else {
+        if (x0.reset) hipLaunchKernelGGL((fused_fwd_kernel<C, AL, true, false>), grid, block, 0, st, x0);
+        else hipLaunchKernelGGL((fused_fwd_kernel<C, AL, false, false>), grid, block, 0, st, x0);
+    }
 }
 
 template <int DT, int TPR, int NR, int WAVES, int LB, bool AL>

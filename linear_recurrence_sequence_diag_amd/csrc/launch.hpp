@@ -47,6 +47,11 @@ hipError_t launch_reverse_chunk_replay(const Shape& s, int chunk, const void* a,
                                        const float* h0, void* grad_a, void* grad_b,
                                        hipStream_t st);
 
+// ---- one time step on [B, D] lanes (decoding) --------------------------------
+hipError_t launch_step(int64_t B, int64_t D, int dtype, const void* a, const void* b,
+                       const float* state_in, const uint8_t* reset, void* out, float* state_out,
+                       hipStream_t st);
+
 // ---- single-launch fused form ----------------------------------------------
 // A configuration is (width, tile): width threads of 16 bytes cover one row of
 // a tile (8, 16 or 32) and a tile spans `tile` rows.  Unaligned rows support

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kSeqBlock) void seq_fwd_kernel(const void* __restri
                     h[j] = fmaf(at, h[j], cb[u].get(j));
                     o.v[j] = h[j];
                 }
-                store_row<DT, ALIGNED>(out, base + (size_t)(t0 + u) * D, nvalid, o);
+                if (out) store_row<DT, ALIGNED>(out, base + (size_t)(t0 + u) * D, nvalid, o);
             }
         }
 #pragma unroll

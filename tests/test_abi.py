@@ -25,7 +25,7 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     names = set(declared_symbols())
-    for n in ("scan_fwd", "scan_bwd", "scan_fwd_ex", "scan_bwd_ex", "scan_workspace_bytes",
+    for n in ("scan_fwd", "scan_bwd", "scan_fwd_ex", "scan_bwd_ex", "scan_step", "scan_workspace_bytes",
               "scan_status_string", "scan_chunk_summary", "scan_chunk_prefix", "scan_chunk_replay",
               "scan_reverse_chunk_summary", "scan_reverse_chunk_prefix",
               "scan_reverse_chunk_replay"):
@@ -88,6 +88,12 @@ def test_argument_errors_return_status_without_work():
                                          lr.F32, None) == -2
     with pytest.raises(lr.LRScanError):
         lr.scan_fwd(None, fake, fake, None, 2, 8, 4, lr.F32, None)
+    # a forward needs out or last; a step needs out or the new state
+    assert lib.scan_fwd(fake, fake, None, None, 2, 8, 4, lr.F32, None) == -1
+    assert lib.scan_step(None, fake, None, None, fake, fake, 2, 4, lr.F32, None) == -1
+    assert lib.scan_step(fake, fake, fake, None, None, None, 2, 4, lr.F32, None) == -1
+    assert lib.scan_step(fake, fake, None, None, fake, None, 0, 4, lr.F32, None) == -2
+    assert lib.scan_step(fake, fake, None, None, fake, None, 2, 4, 5, None) == -3
 
 
 def test_workspace_sizes_and_auto_choice():
