@@ -5,9 +5,9 @@ Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 its Python binding) never imports, links or calls it, and this package never
 imports the product path.
 
-The arithmetic lives in ``oracle.c`` (plain C, double precision, one lane at a
-time; see the header of that file for the definitions and where they come
-from).  This module only compiles it with gcc when the shared object is
+The arithmetic lives in ``oracle.c`` and ``oracle_complex.c`` (plain C,
+double precision, one lane at a time; see the headers of those files for the
+definitions and where they come from).  This module only compiles it with gcc when the shared object is
 missing or older than the source, and marshals numpy float64 arrays.
 
 Definitions (page "triton_training_scan.py", kernels ``_real_forward``,
@@ -33,6 +33,8 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
+_SRC_COMPLEX = os.path.join(_HERE, "oracle_complex.c")
+SOURCES = (_SRC, _SRC_COMPLEX)
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
@@ -42,9 +44,11 @@ GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-pthre
 
 def build(force: bool = False) -> str:
     """Compile oracle.c into liboracle.so with gcc (fp contraction off)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    stale = not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(f)
+                                             for f in SOURCES)
+    if force or stale:
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp])
+        subprocess.check_call(["gcc", *GCC_FLAGS, *SOURCES, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -78,6 +82,9 @@ def _load():
                 "oracle_parallel_fwd": [_I, _I, _I, _D, _D, _D, _U8, _D, _D, ctypes.c_int],
                 "oracle_parallel_bwd": [_I, _I, _I, _D, _D, _D, _D, _D, _U8, _D, _D, _D,
                                         ctypes.c_int],
+                "oracle_complex_fwd": [_I, _I, _I, _D, _D, _D, _D, _D, _D, _U8, _D, _D, _D, _D],
+                "oracle_complex_bwd": [_I, _I, _I, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _U8,
+                                       _D, _D, _D, _D, _D, _D],
             }
             for name, args in sigs.items():
                 fn = getattr(lib, name)
@@ -244,3 +251,55 @@ def reverse_chunk_replay(a, h, g, future, C: int, h0=None):
     _load().oracle_reverse_chunk_replay(B, T, D, C, _p(a), _p(h), _p(g), _p(future), _p(h0),
                                         _p(grad_a), _p(grad_b))
     return grad_a, grad_b
+
+
+# ----------------------------------------------------------------------------
+# complex diagonal scan (planar storage in the C oracle; complex128 here)
+# ----------------------------------------------------------------------------
+def _planar(z, shape):
+    """(real, imag) contiguous float64 arrays of a complex array (None -> None)."""
+    if z is None:
+        return None, None
+    z = np.asarray(z)
+    if tuple(z.shape) != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {z.shape}")
+    return (np.ascontiguousarray(z.real, dtype=np.float64),
+            np.ascontiguousarray(z.imag, dtype=np.float64))
+
+
+def complex_fwd(a, b, h0=None, reset=None):
+    """Complex scan h_t = a_t h_{t-1} + b_t in fp64.  a, b: complex [B, T, M];
+    h0: complex [B, M] or None; reset: [B, T] mask or None.
+    Returns (out [B, T, M], last [B, M]) as complex128."""
+    a = np.asarray(a)
+    if a.ndim != 3:
+        raise ValueError("expected a [B, T, M] array")
+    B, T, M = a.shape
+    ar, ai = _planar(a, (B, T, M))
+    br, bi = _planar(b, (B, T, M))
+    h0r, h0i = _planar(h0, (B, M))
+    rm = _mask(reset, B, T)
+    out_r, out_i = np.empty((B, T, M)), np.empty((B, T, M))
+    last_r, last_i = np.empty((B, M)), np.empty((B, M))
+    _load().oracle_complex_fwd(B, T, M, _p(ar), _p(ai), _p(br), _p(bi), _p(h0r), _p(h0i), _p(rm),
+                               _p(out_r), _p(out_i), _p(last_r), _p(last_i))
+    return out_r + 1j * out_i, last_r + 1j * last_i
+
+
+def complex_bwd(a, h, g, h0=None, grad_last=None, reset=None):
+    """Adjoint of the complex scan for L = sum Re(conj(g) h) + Re(conj(grad_last) h_{T-1}):
+    gradients as dL/dRe + i dL/dIm.  Returns (grad_a, grad_b, grad_h0) complex128."""
+    a = np.asarray(a)
+    B, T, M = a.shape
+    ar, ai = _planar(a, (B, T, M))
+    hr, hi = _planar(h, (B, T, M))
+    gr, gi = _planar(g, (B, T, M))
+    h0r, h0i = _planar(h0, (B, M))
+    glr, gli = _planar(grad_last, (B, M))
+    rm = _mask(reset, B, T)
+    gar, gai, gbr, gbi = (np.empty((B, T, M)) for _ in range(4))
+    gh0r, gh0i = np.empty((B, M)), np.empty((B, M))
+    _load().oracle_complex_bwd(B, T, M, _p(ar), _p(ai), _p(hr), _p(hi), _p(gr), _p(gi), _p(h0r),
+                               _p(h0i), _p(glr), _p(gli), _p(rm), _p(gar), _p(gai), _p(gbr),
+                               _p(gbi), _p(gh0r), _p(gh0i))
+    return gar + 1j * gai, gbr + 1j * gbi, gh0r + 1j * gh0i

@@ -17,6 +17,7 @@ import oracle
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
+SRC_COMPLEX = os.path.join(ROOT, "oracle", "oracle_complex.c")
 
 # (name, text in oracle.c, replacement, occurrence index or None for all)
 MUTANTS = [
@@ -43,6 +44,16 @@ MUTANTS = [
      "double at = is_reset(reset, bi, t > 0 ? t - 1 : 0, T) ? 0.0 : a[i];"),
     ("reset_keeps_grad_a", "grad_a[i] = r ? 0.0 : lam * h_prev;", "grad_a[i] = lam * h_prev;"),
     ("reset_keeps_carry", "carry = (r ? 0.0 : a[i]) * lam;", "carry = a[i] * lam;"),
+    # complex oracle (the mutation applies to oracle_complex.c)
+    ("c:fwd_conj_a", "h = at * h + CMPLX(br[i], bi[i]);", "h = conj(at) * h + CMPLX(br[i], bi[i]);"),
+    ("c:fwd_swap_re_im_b", "h = at * h + CMPLX(br[i], bi[i]);", "h = at * h + CMPLX(bi[i], br[i]);"),
+    ("c:bwd_carry_no_conj", "carry = conj(at) * lam;", "carry = at * lam;"),
+    ("c:bwd_grad_a_no_conj", "lam * conj(prev);", "lam * prev;"),
+    ("c:bwd_grad_a_conj_lam", "lam * conj(prev);", "conj(lam) * prev;"),
+    ("c:reset_ignored", "double complex at = c_reset(reset, b, t, T) ? CMPLX(0.0, 0.0) : CMPLX(ar[i], ai[i]);",
+     "double complex at = CMPLX(ar[i], ai[i]);"),
+    ("c:h0_imag_dropped", "double complex h = h0r ? CMPLX(h0r[lane], h0i[lane]) : CMPLX(0.0, 0.0);",
+     "double complex h = h0r ? CMPLX(h0r[lane], 0.0) : CMPLX(0.0, 0.0);"),
     ("reset_mask_transposed", "return reset != NULL && reset[(size_t)bi * (size_t)T + (size_t)t] != 0;",
      "return reset != NULL && reset[(size_t)bi * (size_t)T + (size_t)(T - 1 - t)] != 0;"),
 ]
@@ -56,11 +67,13 @@ def _run_pins(lib_path):
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
 
 
-def _compile(src_text, tmp_path, name):
+def _compile(src_text, tmp_path, name, complex_text=None):
     c = tmp_path / f"{name}.c"
+    cc = tmp_path / f"{name}_complex.c"
     so = tmp_path / f"{name}.so"
     c.write_text(src_text)
-    subprocess.check_call(["gcc", *oracle.GCC_FLAGS, str(c), "-o", str(so)])
+    cc.write_text(complex_text if complex_text is not None else open(SRC_COMPLEX).read())
+    subprocess.check_call(["gcc", *oracle.GCC_FLAGS, str(c), str(cc), "-o", str(so), "-lm"])
     return str(so)
 
 
@@ -72,7 +85,13 @@ def test_clean_oracle_passes_pins(tmp_path):
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(name, old, new, tmp_path):
-    src = open(SRC).read()
+    path = SRC_COMPLEX if name.startswith("c:") else SRC
+    src = open(path).read()
     assert src.count(old) == 1, f"mutation site for {name} not unique ({src.count(old)})"
-    r = _run_pins(_compile(src.replace(old, new), tmp_path, name))
+    tag = name.replace(":", "_")
+    if path == SRC_COMPLEX:
+        so = _compile(open(SRC).read(), tmp_path, tag, complex_text=src.replace(old, new))
+    else:
+        so = _compile(src.replace(old, new), tmp_path, tag)
+    r = _run_pins(so)
     assert r.returncode != 0, f"mutant {name} survived the pins"

@@ -462,3 +462,89 @@ def test_reset_all_clear_mask_is_the_plain_scan():
     r2 = oracle.scan_bwd(a, o2, g, h0=h0, grad_last=gl)
     for x, y in zip(r1, r2):
         assert np.array_equal(x, y)
+
+
+# ----------------------------------------------------------------------------
+# complex diagonal scan (page "triton_training_scan.py", _complex_forward /
+# _complex_backward): h_t = a_t h_{t-1} + b_t over complex values, adjoint
+# through conj(a)
+# ----------------------------------------------------------------------------
+def crand(shape, seed, scale=1.0):
+    r = np.random.default_rng(seed)
+    return scale * (r.uniform(-1, 1, shape) + 1j * r.uniform(-1, 1, shape))
+
+
+def test_complex_with_real_values_is_the_real_scan():
+    """Real a, b, g, h0, grad_last: every complex result has a zero imaginary
+    part and a real part bitwise equal to the real oracle's."""
+    B, T, D = 2, 37, 5
+    a, b, g = rand((B, T, D), 50, 0.2, 1.1), rand((B, T, D), 51), rand((B, T, D), 52)
+    h0, gl = rand((B, D), 53), rand((B, D), 54)
+    mask = np.random.default_rng(55).random((B, T)) < 0.1
+    o, l = oracle.complex_fwd(a + 0j, b + 0j, h0=h0 + 0j, reset=mask)
+    ro, rl = oracle.scan_fwd(a, b, h0=h0, reset=mask)
+    assert np.array_equal(o.real, ro) and not np.any(o.imag)
+    assert np.array_equal(l.real, rl) and not np.any(l.imag)
+    ga, gb, gh0 = oracle.complex_bwd(a + 0j, o, g + 0j, h0=h0 + 0j, grad_last=gl + 0j, reset=mask)
+    rga, rgb, rgh0 = oracle.scan_bwd(a, ro, g, h0=h0, grad_last=gl, reset=mask)
+    for z, r in ((ga, rga), (gb, rgb), (gh0, rgh0)):
+        assert np.array_equal(z.real, r) and not np.any(z.imag)
+
+
+def test_complex_real_transition_splits_into_two_real_scans():
+    """With real a, the real and imaginary parts of b scan independently."""
+    B, T, D = 3, 29, 4
+    a = rand((B, T, D), 60, 0.1, 1.0)
+    b, g = crand((B, T, D), 61), crand((B, T, D), 62)
+    o, _ = oracle.complex_fwd(a + 0j, b)
+    assert np.array_equal(o.real, oracle.scan_fwd(a, b.real)[0])
+    assert np.array_equal(o.imag, oracle.scan_fwd(a, b.imag)[0])
+    ga, gb, _ = oracle.complex_bwd(a + 0j, o, g)
+    assert np.array_equal(gb.real, oracle.scan_bwd(a, o.real, g.real)[1])
+    assert np.array_equal(gb.imag, oracle.scan_bwd(a, o.imag, g.imag)[1])
+
+
+def test_complex_rotation_closed_form():
+    """a_t = r e^{i theta} for every t and b = (b0, 0, 0, ...): h_t = a^t b0."""
+    T = 400
+    r_, th = 0.999, 0.3
+    a = np.full((1, T, 1), r_ * np.exp(1j * th))
+    b = np.zeros((1, T, 1), complex)
+    b[0, 0, 0] = 0.7 - 0.2j
+    o, _ = oracle.complex_fwd(a, b)
+    t = np.arange(T)
+    expect = (r_ ** t) * np.exp(1j * th * t) * b[0, 0, 0]
+    assert np.allclose(o[0, :, 0], expect, rtol=1e-12 * T, atol=1e-15)
+    # |a| = 1: the modulus is preserved
+    o1, _ = oracle.complex_fwd(np.full((1, T, 1), np.exp(1j * th)), b)
+    assert np.allclose(np.abs(o1[0, :, 0]), abs(b[0, 0, 0]), rtol=1e-12 * T)
+
+
+def test_complex_gradients_match_finite_differences():
+    """dL/dRe + i dL/dIm of L = sum Re(conj(g) h) + Re(conj(grad_last) h_{T-1})
+    for a, b and h0, by central differences in fp64, with a reset mask."""
+    B, T, M = 2, 7, 2
+    a, b, g = crand((B, T, M), 70, 0.8), crand((B, T, M), 71), crand((B, T, M), 72)
+    h0, gl = crand((B, M), 73), crand((B, M), 74)
+    mask = np.zeros((B, T), bool)
+    mask[1, 3] = True
+
+    def loss(a_, b_, h0_):
+        o, l = oracle.complex_fwd(a_, b_, h0=h0_, reset=mask)
+        return float(np.sum((np.conj(g) * o).real) + np.sum((np.conj(gl) * l).real))
+
+    o, _ = oracle.complex_fwd(a, b, h0=h0, reset=mask)
+    ga, gb, gh0 = oracle.complex_bwd(a, o, g, h0=h0, grad_last=gl, reset=mask)
+    eps = 1e-6
+    for which, (arr, grad) in enumerate(((a, ga), (b, gb), (h0, gh0))):
+        for idx in np.ndindex(arr.shape):
+            for unit, part in ((1.0, "re"), (1j, "im")):
+                up, dn = arr.copy(), arr.copy()
+                up[idx] += eps * unit
+                dn[idx] -= eps * unit
+                args_up, args_dn = [a, b, h0], [a, b, h0]
+                args_up[which], args_dn[which] = up, dn
+                fd = (loss(*args_up) - loss(*args_dn)) / (2 * eps)
+                got = grad[idx].real if part == "re" else grad[idx].imag
+                assert abs(fd - got) <= 1e-7 * (1 + abs(fd)), (which, idx, part, fd, got)
+    assert ga[1, 3, 0] == 0 and ga[1, 3, 1] == 0
