@@ -33,6 +33,9 @@ WORKLOAD_TEXT = {
     "long32": "B=4 T=8192 D=4096 fp32, a~U(0.95,0.9999), b~N(0,1)",
     "longseq": "B=1 T=131072 D=1024 bf16 I/O fp32 state, a~U(0.99,0.99999), b~N(0,0.1)",
     "masked": "B=16 T=4096 D=2560 bf16, a~U(0.5,0.9999), 10% padding / 5% reset tokens",
+    "cwide": "complex, planar re/im: B=8 T=2048 M=2560 bf16 I/O fp32 state, a=r*exp(i*theta), "
+             "r=clip(sigmoid(N(4,1)),0.8,0.9999), theta~U(-pi/8,pi/8), b=CN(0,1)*sqrt((1-r^2)/2)",
+    "csmall": "complex, planar re/im: B=2 T=256 M=64 fp32, the cwide recipe",
 }
 
 
@@ -100,6 +103,81 @@ def cpu_baseline(inp, budget_s=10.0):
                   f"(fp64, {cores} threads over lanes; input conversion untimed)",
         "elements_per_s": round(wl.N * reps / t_total, 1),
     }
+
+
+def complex_line(args, wl, lr, torch, W):
+    """JSON line of the complex scan (planar re/im arrays): train = forward +
+    backward through AUTO; prefill = the state-only forward."""
+    inp = W.generate_complex(wl, seed=0)
+    B, T, M = wl.B, wl.T, wl.D
+    s = wl.itemsize
+    N = B * T * M
+
+    def dev(x):
+        if wl.dtype == "f32":
+            return torch.from_numpy(x).cuda()
+        return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+
+    ar, ai, br, bi, gr, gi = (dev(getattr(inp, n)) for n in ("ar", "ai", "br", "bi", "gr", "gi"))
+    dt = lr.F32 if wl.dtype == "f32" else lr.BF16
+    out_r, out_i = torch.empty_like(ar), torch.empty_like(ar)
+    g4 = [torch.empty_like(ar) for _ in range(4)]
+    last = [torch.empty((B, M), device="cuda", dtype=torch.float32) for _ in range(2)]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    o = lr.make_opts(algo=args.algo)
+    P = lambda t: t.data_ptr()
+
+    def fwd(with_out=True):
+        lr.scan_complex_fwd(P(ar), P(ai), P(br), P(bi), P(out_r) if with_out else None,
+                            P(out_i) if with_out else None, P(last[0]), P(last[1]), None, None,
+                            B, T, M, dt, sh, o)
+
+    def bwd():
+        lr.scan_complex_bwd(P(ar), P(ai), P(out_r), P(out_i), P(gr), P(gi), None, None, None,
+                            None, P(g4[0]), P(g4[1]), P(g4[2]), P(g4[3]), None, None, B, T, M, dt,
+                            sh, o)
+
+    if args.mode == "prefill":
+        step = [lambda: fwd(False)]
+        nbytes = 4 * s * N + 8 * B * M
+    else:
+        step = [fwd, bwd]
+        nbytes = (6 * s * N + 8 * B * M) + 10 * s * N
+    for _ in range(args.warmup):
+        for f in step:
+            f()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        for f in step:
+            f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    res = {"metric": f"complex {args.mode}: effective HBM GB/s",
+           "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+           "data": "synthetic (seeded numpy draws, see workloads/__init__.py)",
+           "config": {"workload": f"{wl.name}: {WORKLOAD_TEXT[wl.name]}", "B": B, "T": T, "M": M}}
+    res["pct_of_peak"] = round(100 * res["value"] / HBM_PEAK_GBPS, 2)
+    if args.mode != "prefill":
+        # per-direction averages over back-to-back launches
+        for name, f, nb in (("fwd", fwd, 6 * s * N + 8 * B * M), ("bwd", bwd, 10 * s * N)):
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            for _ in range(args.steps):
+                f()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            kms = a0.elapsed_time(a1) / args.steps
+            res[f"{name}_us"] = round(kms * 1e3, 2)
+            res[f"{name}_GBps"] = round(nb / (kms * 1e-3) / 1e9, 1)
+    return res
 
 
 def inference_line(args, wl, lr, torch, a, b, dt):
@@ -201,6 +279,10 @@ def main():
                           "bytes_written_per_copy": 4 * n, "copies": args.steps}))
         return
 
+    if args.workload in W.COMPLEX_WORKLOADS:
+        print(json.dumps(complex_line(args, W.COMPLEX_WORKLOADS[args.workload], lr, torch, W)),
+              flush=True)
+        return
     wl = W.WORKLOADS[args.workload]
     inp = W.generate(wl, seed=0)
     dt = lr.F32 if wl.dtype == "f32" else lr.BF16

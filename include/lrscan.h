@@ -148,6 +148,45 @@ LRSCAN_API int scan_step(const void* a, const void* b, const float* state_in,
                          const uint8_t* reset, void* out, float* state_out, int64_t B, int64_t D,
                          int dtype, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Complex diagonal scan, planar storage (page "triton_training_scan.py":
+ * _complex_forward, _complex_backward, complex_scan, complex_scan_with_last):
+ *   h_{-1} = h0 (zero unless given),  h_t = a_t * h_{t-1} + b_t  (complex).
+ * Real and imaginary parts are separate [B, T, M] arrays of `dtype` (M modes,
+ * layout as above); states are pairs of fp32 [B, M] arrays.  Every (re, im)
+ * pair of pointers is given whole or NULL whole (else LRSCAN_ERR_NULL).
+ * The backward is the gradient of the real loss
+ *   L = sum Re(conj(grad_out) * out) + Re(conj(grad_last) * last),
+ * written as dL/dRe + i dL/dIm:
+ *   lambda_{T-1} = grad_out_{T-1} + grad_last,
+ *   lambda_t = grad_out_t + conj(a_{t+1}) * lambda_{t+1},
+ *   grad_b_t = lambda_t,  grad_a_t = lambda_t * conj(h_{t-1}),
+ *   grad_h0 = conj(a_0) * lambda_0.
+ * opts: algo AUTO, FUSED (one tile shape: width 8, 128 rows; chunk and width
+ * must be 0 or those) or SEQ (CHUNKED returns LRSCAN_ERR_ALGO); workspace,
+ * polls and reset as for the real scan; opts->h0 and opts->grad_h0 are not
+ * used (the states are the explicit arguments).
+ * ------------------------------------------------------------------------ */
+/*   ar, ai, br, bi  read.   out_r, out_i written (NULL pair: state-only
+ *   forward, then last is required).   last_r, last_i written (nullable pair).
+ *   h0_r, h0_i (nullable pair). */
+LRSCAN_API int scan_complex_fwd(const void* ar, const void* ai, const void* br, const void* bi,
+                                void* out_r, void* out_i, float* last_r, float* last_i,
+                                const float* h0_r, const float* h0_i, int64_t B, int64_t T,
+                                int64_t M, int dtype, void* stream, const lrscan_opts* opts);
+/*   out_r, out_i: the forward's outputs (h_{t-1} is read from them).
+ *   grad_last_*, h0_*, grad_h0_*: nullable pairs.  grad_ar .. grad_bi written. */
+LRSCAN_API int scan_complex_bwd(const void* ar, const void* ai, const void* out_r,
+                                const void* out_i, const void* grad_out_r, const void* grad_out_i,
+                                const float* grad_last_r, const float* grad_last_i,
+                                const float* h0_r, const float* h0_i, void* grad_ar,
+                                void* grad_ai, void* grad_br, void* grad_bi, float* grad_h0_r,
+                                float* grad_h0_i, int64_t B, int64_t T, int64_t M, int dtype,
+                                void* stream, const lrscan_opts* opts);
+/* Bytes of caller workspace a complex call with these arguments needs (0 if none). */
+LRSCAN_API size_t scan_complex_workspace_bytes(int64_t B, int64_t T, int64_t M, int dtype,
+                                               const lrscan_opts* opts);
+
 /* Bytes of workspace the call with these arguments needs (0 if none).
  * Returns 0 for invalid arguments. */
 LRSCAN_API size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t D, int dtype,

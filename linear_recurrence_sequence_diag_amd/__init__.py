@@ -61,6 +61,10 @@ _SIGS = {
     "scan_workspace_bytes": ([_I64, _I64, _I64, _INT, ctypes.POINTER(Opts)], ctypes.c_size_t),
     "scan_status_string": ([_INT], ctypes.c_char_p),
     "scan_step": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P], _INT),
+    "scan_complex_fwd": ([_P] * 10 + [_I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
+    "scan_complex_bwd": ([_P] * 16 + [_I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
+    "scan_complex_workspace_bytes": ([_I64, _I64, _I64, _INT, ctypes.POINTER(Opts)],
+                                     ctypes.c_size_t),
     "scan_auto_algo": ([_I64, _I64, _I64, _INT, _INT, ctypes.POINTER(_INT), ctypes.POINTER(_INT)],
                        _INT),
     "scan_chunk_summary": ([_P, _P, _P, _P, _I64, _I64, _I64, _INT, _INT, _P], _INT),
@@ -133,6 +137,30 @@ def scan_bwd_ex(a, out, grad_out, grad_last, grad_a, grad_b, B, T, D, dtype, str
 def scan_step(a, b, state_in, reset, out, state_out, B, D, dtype, stream):
     return _check(library().scan_step(a, b, state_in, reset, out, state_out, B, D, dtype, stream),
                   "scan_step")
+
+
+def scan_complex_fwd(ar, ai, br, bi, out_r, out_i, last_r, last_i, h0_r, h0_i, B, T, M, dtype,
+                     stream, opts):
+    return _check(library().scan_complex_fwd(ar, ai, br, bi, out_r, out_i, last_r, last_i, h0_r,
+                                             h0_i, B, T, M, dtype, stream,
+                                             ctypes.byref(opts) if opts is not None else None),
+                  "scan_complex_fwd")
+
+
+def scan_complex_bwd(ar, ai, out_r, out_i, grad_out_r, grad_out_i, grad_last_r, grad_last_i, h0_r,
+                     h0_i, grad_ar, grad_ai, grad_br, grad_bi, grad_h0_r, grad_h0_i, B, T, M,
+                     dtype, stream, opts):
+    return _check(library().scan_complex_bwd(ar, ai, out_r, out_i, grad_out_r, grad_out_i,
+                                             grad_last_r, grad_last_i, h0_r, h0_i, grad_ar,
+                                             grad_ai, grad_br, grad_bi, grad_h0_r, grad_h0_i, B,
+                                             T, M, dtype, stream,
+                                             ctypes.byref(opts) if opts is not None else None),
+                  "scan_complex_bwd")
+
+
+def scan_complex_workspace_bytes(B, T, M, dtype, opts=None):
+    return library().scan_complex_workspace_bytes(B, T, M, dtype,
+                                                  ctypes.byref(opts) if opts is not None else None)
 
 
 def scan_workspace_bytes(B, T, D, dtype, opts=None):
@@ -327,6 +355,66 @@ def step(a, b, state=None, reset=None, with_out=True, out_state=None):
     return out, new
 
 
+def _pair(x):
+    return (None, None) if x is None else (x[0], x[1])
+
+
+def complex_scan(ar, ai, br, bi, h0=None, algo="auto", with_last=True, with_out=True, polls=0,
+                 reset=None):
+    """Complex scan h_t = a_t h_{t-1} + b_t on planar [B, T, M] tensors (real
+    and imaginary parts separate).  h0: (re, im) float32 [B, M] pair or None.
+    Returns (out_r, out_i, last_r, last_i); parts not asked for are None."""
+    torch = _torch()
+    _check_seq("ar", ar)
+    for name, t in (("ai", ai), ("br", br), ("bi", bi)):
+        _check_seq(name, t, ar)
+    _check_mask(reset, ar)
+    h0r, h0i = _pair(h0)
+    _check_state("h0 (real part)", h0r, ar)
+    _check_state("h0 (imaginary part)", h0i, ar)
+    if not (with_out or with_last):
+        raise ValueError("a forward needs out or last")
+    B, T, M = ar.shape
+    out_r = torch.empty_like(ar) if with_out else None
+    out_i = torch.empty_like(ar) if with_out else None
+    mk = (lambda: torch.empty((B, M), device=ar.device, dtype=torch.float32))
+    last_r, last_i = (mk(), mk()) if with_last else (None, None)
+    with torch.cuda.device(ar.device):
+        scan_complex_fwd(ar.data_ptr(), ai.data_ptr(), br.data_ptr(), bi.data_ptr(), _ptr(out_r),
+                         _ptr(out_i), _ptr(last_r), _ptr(last_i), _ptr(h0r), _ptr(h0i), B, T, M,
+                         dtype_code(ar.dtype), _stream(ar),
+                         make_opts(algo, polls=polls, reset=reset))
+    return out_r, out_i, last_r, last_i
+
+
+def complex_scan_backward(ar, ai, out_r, out_i, grad_out_r, grad_out_i, grad_last=None, h0=None,
+                          algo="auto", need_grad_h0=False, polls=0, reset=None):
+    """Adjoint of complex_scan for L = sum Re(conj(g) out) + Re(conj(grad_last) last).
+    Returns (grad_ar, grad_ai, grad_br, grad_bi, (grad_h0_r, grad_h0_i) or None)."""
+    torch = _torch()
+    _check_seq("ar", ar)
+    for name, t in (("ai", ai), ("out_r", out_r), ("out_i", out_i), ("grad_out_r", grad_out_r),
+                    ("grad_out_i", grad_out_i)):
+        _check_seq(name, t, ar)
+    _check_mask(reset, ar)
+    glr, gli = _pair(grad_last)
+    h0r, h0i = _pair(h0)
+    for name, t in (("grad_last", glr), ("grad_last", gli), ("h0", h0r), ("h0", h0i)):
+        _check_state(name, t, ar)
+    B, T, M = ar.shape
+    g = [torch.empty_like(ar) for _ in range(4)]
+    gh0 = ((torch.empty((B, M), device=ar.device, dtype=torch.float32),
+            torch.empty((B, M), device=ar.device, dtype=torch.float32)) if need_grad_h0 else None)
+    gh0r, gh0i = _pair(gh0)
+    with torch.cuda.device(ar.device):
+        scan_complex_bwd(ar.data_ptr(), ai.data_ptr(), out_r.data_ptr(), out_i.data_ptr(),
+                         grad_out_r.data_ptr(), grad_out_i.data_ptr(), _ptr(glr), _ptr(gli),
+                         _ptr(h0r), _ptr(h0i), g[0].data_ptr(), g[1].data_ptr(), g[2].data_ptr(),
+                         g[3].data_ptr(), _ptr(gh0r), _ptr(gh0i), B, T, M, dtype_code(ar.dtype),
+                         _stream(ar), make_opts(algo, polls=polls, reset=reset))
+    return g[0], g[1], g[2], g[3], gh0
+
+
 def n_chunks(T, chunk):
     return (T + chunk - 1) // chunk
 
@@ -408,6 +496,40 @@ def _make_autograd():
 
 
 _autograd_cls = None
+_complex_autograd_cls = None
+
+
+def _make_complex_autograd():
+    torch = _torch()
+
+    class ComplexDiagonalScan(torch.autograd.Function):
+        """(out_r, out_i) = complex scan of (a, b); gradients from the reverse-time kernels."""
+
+        @staticmethod
+        def forward(ctx, ar, ai, br, bi, reset):
+            ar, ai, br, bi = (t.contiguous() for t in (ar, ai, br, bi))
+            out_r, out_i, _, _ = complex_scan(ar, ai, br, bi, with_last=False, reset=reset)
+            ctx.save_for_backward(ar, ai, out_r, out_i)
+            ctx.reset = reset
+            return out_r, out_i
+
+        @staticmethod
+        def backward(ctx, grad_out_r, grad_out_i):
+            ar, ai, out_r, out_i = ctx.saved_tensors
+            gar, gai, gbr, gbi, _ = complex_scan_backward(
+                ar, ai, out_r, out_i, grad_out_r.contiguous(), grad_out_i.contiguous(),
+                reset=ctx.reset)
+            return gar, gai, gbr, gbi, None
+
+    return ComplexDiagonalScan
+
+
+def complex_diagonal_scan(ar, ai, br, bi, reset=None):
+    """Differentiable complex scan (torch autograd) on planar tensors; returns (out_r, out_i)."""
+    global _complex_autograd_cls
+    if _complex_autograd_cls is None:
+        _complex_autograd_cls = _make_complex_autograd()
+    return _complex_autograd_cls.apply(ar, ai, br, bi, reset)
 
 
 def diagonal_scan(a, b, reset=None):

@@ -173,6 +173,43 @@ int get_workspace(const Shape& s, const Resolved& r, const lrscan_opts* o, hipSt
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_HIP; }
 
+// ---- complex scan helpers ----
+
+bool pair_ok(const void* re, const void* im) { return (re == nullptr) == (im == nullptr); }
+
+// AUTO -> FUSED; FUSED accepts only its one tile shape; CHUNKED is not provided.
+int complex_algo(const lrscan_opts* o, int* algo) {
+    const int a = o ? o->algo : LRSCAN_ALGO_AUTO;
+    if (a == LRSCAN_ALGO_AUTO || a == LRSCAN_ALGO_FUSED) {
+        const int c = o ? o->chunk : 0, w = o ? o->width : 0;
+        if ((c != 0 && c != kComplexTile) || (w != 0 && w != kComplexWidth)) return LRSCAN_ERR_CHUNK;
+        *algo = LRSCAN_ALGO_FUSED;
+        return LRSCAN_OK;
+    }
+    if (a == LRSCAN_ALGO_SEQ) {
+        *algo = a;
+        return LRSCAN_OK;
+    }
+    return LRSCAN_ERR_ALGO;
+}
+
+int complex_workspace(const Shape& s, int algo, const lrscan_opts* o, hipStream_t st,
+                      Workspace* ws) {
+    *ws = Workspace{};
+    if (algo != LRSCAN_ALGO_FUSED) return LRSCAN_OK;
+    if (!complex_fused_supported(s)) return LRSCAN_ERR_DIM;
+    const size_t need = complex_fused_workspace_bytes(s);
+    if (o && o->workspace) {
+        if (o->workspace_bytes < need) return LRSCAN_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(o->workspace) % 256 != 0) return LRSCAN_ERR_WORKSPACE;
+        ws->ptr = o->workspace;
+        ws->bytes = need;
+        ws->init = true;
+        return LRSCAN_OK;
+    }
+    return library_workspace(need, 1, st, ws) == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -324,6 +361,75 @@ LRSCAN_API int scan_step(const void* a, const void* b, const float* state_in,
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
     return hip_status(launch_step(B, D, dtype, a, b, state_in, reset, out, state_out,
                                   static_cast<hipStream_t>(stream)));
+}
+
+// ---- complex diagonal scan --------------------------------------------------------
+
+LRSCAN_API int scan_complex_fwd(const void* ar, const void* ai, const void* br, const void* bi,
+                                void* out_r, void* out_i, float* last_r, float* last_i,
+                                const float* h0_r, const float* h0_i, int64_t B, int64_t T,
+                                int64_t M, int dtype, void* stream, const lrscan_opts* opts) {
+    if (!ar || !ai || !br || !bi) return LRSCAN_ERR_NULL;
+    if (!pair_ok(out_r, out_i) || !pair_ok(last_r, last_i) || !pair_ok(h0_r, h0_i))
+        return LRSCAN_ERR_NULL;
+    if (!out_r && !last_r) return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, T, M)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
+    int algo = 0;
+    int st = complex_algo(opts, &algo);
+    if (st != LRSCAN_OK) return st;
+    const Shape s{B, T, M, dtype};
+    const CxFwdPtrs p{ar, ai, br, bi, out_r, out_i, last_r, last_i, h0_r, h0_i,
+                      opts ? opts->reset : nullptr};
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (algo == LRSCAN_ALGO_SEQ) return hip_status(launch_complex_seq_fwd(s, p, hs));
+    Workspace ws;
+    st = complex_workspace(s, algo, opts, hs, &ws);
+    if (st != LRSCAN_OK) return st;
+    return fused_status(launch_complex_fused_fwd(s, p, ws.ptr, ws.bytes, ws.init,
+                                                 opts ? opts->polls : 0, hs),
+                        ws, opts, hs);
+}
+
+LRSCAN_API int scan_complex_bwd(const void* ar, const void* ai, const void* out_r,
+                                const void* out_i, const void* grad_out_r, const void* grad_out_i,
+                                const float* grad_last_r, const float* grad_last_i,
+                                const float* h0_r, const float* h0_i, void* grad_ar,
+                                void* grad_ai, void* grad_br, void* grad_bi, float* grad_h0_r,
+                                float* grad_h0_i, int64_t B, int64_t T, int64_t M, int dtype,
+                                void* stream, const lrscan_opts* opts) {
+    if (!ar || !ai || !out_r || !out_i || !grad_out_r || !grad_out_i || !grad_ar || !grad_ai ||
+        !grad_br || !grad_bi)
+        return LRSCAN_ERR_NULL;
+    if (!pair_ok(grad_last_r, grad_last_i) || !pair_ok(h0_r, h0_i) ||
+        !pair_ok(grad_h0_r, grad_h0_i))
+        return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, T, M)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
+    int algo = 0;
+    int st = complex_algo(opts, &algo);
+    if (st != LRSCAN_OK) return st;
+    const Shape s{B, T, M, dtype};
+    const CxBwdPtrs p{ar, ai, out_r, out_i, grad_out_r, grad_out_i, grad_last_r, grad_last_i,
+                      h0_r, h0_i, opts ? opts->reset : nullptr, grad_ar, grad_ai, grad_br,
+                      grad_bi, grad_h0_r, grad_h0_i};
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (algo == LRSCAN_ALGO_SEQ) return hip_status(launch_complex_seq_bwd(s, p, hs));
+    Workspace ws;
+    st = complex_workspace(s, algo, opts, hs, &ws);
+    if (st != LRSCAN_OK) return st;
+    return fused_status(launch_complex_fused_bwd(s, p, ws.ptr, ws.bytes, ws.init,
+                                                 opts ? opts->polls : 0, hs),
+                        ws, opts, hs);
+}
+
+LRSCAN_API size_t scan_complex_workspace_bytes(int64_t B, int64_t T, int64_t M, int dtype,
+                                               const lrscan_opts* opts) {
+    if (!dims_ok(B, T, M) || !dtype_ok(dtype)) return 0;
+    int algo = 0;
+    if (complex_algo(opts, &algo) != LRSCAN_OK || algo != LRSCAN_ALGO_FUSED) return 0;
+    const Shape s{B, T, M, dtype};
+    return complex_fused_supported(s) ? complex_fused_workspace_bytes(s) : 0;
 }
 
 // ---- the chunked form, step by step ---------------------------------------------

@@ -36,72 +36,11 @@
 // so readers need no separate flag or fence.  The reverse-time kernel is the
 // mirror image: tickets run from the last chunk to the first and carries flow
 // from later rows to earlier ones.
-#include <algorithm>
-#include <cstddef>
-
-#include "device.hpp"
-#include "launch.hpp"
+#include "fused_common.hpp"
 
 namespace lrscan {
 
 namespace {
-
-// Look-back polls before a tile stops waiting and derives the predecessor
-// maps it is missing (normal waits take a few polls; this bound only matters
-// when a predecessor's workgroup is descheduled for a long time).
-constexpr uint32_t kDefaultPolls = 1024;
-
-
-// Workspace of the fused form: a 256-byte header, then two regions of equal
-// size.  A region holds nC ticket counters (each in its own 128-byte line),
-// then the published (P, Q) words, then the published inclusive states H.  A
-// launch uses region `phase`, which is all-ones wherever it will write; it
-// clears the words the previous launch dirtied in the other region, counters
-// included.  The workgroup that takes the last ticket of the last counter to
-// run out records how many words this launch dirties, resets the other
-// phase's count of exhausted counters and flips the phase.  By then every
-// workgroup has read the phase, so back-to-back launches on one stream (or
-// replays of a captured graph) need no separate initialisation step.
-//
-// Tickets.  Same-address atomics serialise (about 11.5 ns each on MI355X: one
-// counter for 2560 workgroups costs 30 us), so tickets come from nC counters,
-// nC a divisor of the number of series nS.  Counter c hands out local indices
-// i = 0, 1, ... in arrival order, and the tile is t = i*nC + c, taken in the
-// chain-major order k = t / nS, s = t % nS.  Because nC divides nS, every
-// predecessor t - j*nS of a tile comes from the same counter with a smaller
-// index, so it was taken by a workgroup that is already running: the chain
-// always drains.  Workgroups are spread over counters so that each counter is
-// fed from all XCDs and the counters advance together, which keeps the rows
-// in flight close to each other (this matters for DRAM locality).
-struct Header {
-    uint32_t phase;
-    uint32_t reserved;
-    unsigned long long dirty[2];  // words the last user of each region wrote
-    uint32_t pad[26];
-    uint32_t done[2];             // per phase: counters run out (all-ones: none)
-};
-static_assert(offsetof(Header, done) == 128, "the counter tally starts a new cache line");
-
-constexpr int kCtrStride = 32;  // words between ticket counters (one 128-byte line each)
-constexpr int kMaxCounters = 64;
-
-struct Scratch {
-    Header* hdr;
-    uint32_t* region[2];
-    unsigned long long entries;    // NK * nS * W published entries (3 words each)
-    unsigned long long ctr_words;  // nC * kCtrStride
-    uint32_t total_tiles;
-    uint32_t nC;                   // ticket counters (divides nS)
-    uint32_t quota;                // tickets per counter = total_tiles / nC
-};
-
-constexpr int kHeaderBytes = 256;
-
-__device__ __forceinline__ void header_update(const Scratch& sc, uint32_t p) {
-    publish_u32(&sc.hdr->done[p ^ 1u], kEmpty);
-    publish_u64(&sc.hdr->dirty[p], sc.ctr_words + 3ull * sc.entries);
-    publish_u32(&sc.hdr->phase, p ^ 1u);
-}
 
 __device__ __forceinline__ unsigned long long pack_aff(Aff m) {
     return (unsigned long long)publishable(m.p) | ((unsigned long long)publishable(m.q) << 32);
@@ -110,258 +49,32 @@ __device__ __forceinline__ Aff unpack_aff(unsigned long long w) {
     return Aff{__uint_as_float((uint32_t)w), __uint_as_float((uint32_t)(w >> 32))};
 }
 
-// ---------------------------------------------------------------------------
-// tile configuration
-//
-// TPR threads (16-byte vectors) cover one row of a tile: W = TPR*V lanes,
-// TPR*16 contiguous bytes per row.  A wavefront holds RG = 64/TPR row groups,
-// each thread NR consecutive rows; a workgroup of WAVES wavefronts covers
-// CT = WAVES*RG*NR rows.  LB is the look-back window.
-// ---------------------------------------------------------------------------
-template <int DT_, int TPR_, int NR_, int WAVES_, int LB_>
-struct Cfg {
-    static constexpr int DT = DT_, TPR = TPR_, NR = NR_, WAVES = WAVES_, LB = LB_;
-    static constexpr int V = Elem<DT>::V;
-    static constexpr int EB = Elem<DT>::bytes;
-    static constexpr int RG = kWave / TPR;
-    static constexpr int W = TPR * V;
-    static constexpr int NT = WAVES * kWave;
-    static constexpr int CT = WAVES * RG * NR;
-    static_assert(TPR == 8 || TPR == 16 || TPR == 32, "row width");
-    static_assert(W <= NT, "one look-back column per thread");
-    // waves per SIMD the register budget is held to (the forward keeps two
-    // input arrays of NR rows in registers through the look-back, the
-    // backward three)
-    static constexpr int OCC_F = NR <= 8 ? 3 : 2;
-    static constexpr int OCC_B = NR <= 4 ? (TPR > 8 ? 4 : 3) : (NR <= 8 && TPR > 8 ? 3 : 2);
+// A real entry: (P, Q) in one 64-bit word, H in one 32-bit word.
+struct RealLink {
+    using S = float;
+    using M = Aff;
+    using HRaw = uint32_t;
+    using MRaw = unsigned long long;
+    const uint32_t* hs;
+    const unsigned long long* pqs;
+    int nS, s, W, c;
+    __device__ size_t entry(int j) const { return ((size_t)j * (size_t)nS + (size_t)s) * W + c; }
+    __device__ HRaw load_h(int j) const { return peek_u32(hs + entry(j)); }
+    __device__ MRaw load_m(int j) const { return peek_u64(pqs + entry(j)); }
+    __device__ static HRaw empty_h() { return kEmpty; }
+    __device__ static MRaw empty_m() { return ~0ull; }
+    __device__ static bool ready_h(HRaw w) { return w != kEmpty; }
+    __device__ static bool ready_m(MRaw w) { return (uint32_t)w != kEmpty; }
+    __device__ static S state(HRaw w) { return __uint_as_float(w); }
+    __device__ static M map(MRaw w) { return unpack_aff(w); }
+    __device__ static S apply(M m, S x) { return aff_apply(m, x); }
 };
 
-struct Dims {
-    int T, D, nW, nS, NK;
-};
+// Words per published entry: (P, Q) and H.
+constexpr int kRealWords = 3;
 
-// One thread's view of its tile.
-struct Geo {
-    int k, s, bi, dcol0, d0, trow0, row0;
-    int nvalid;     // lanes of this thread's vector that exist (0..V)
-    int nrows;      // rows of this thread's segment that exist (0..NR)
-    size_t tbase;   // byte offset of (batch bi, row trow0, lane dcol0)
-    uint32_t coff;  // this thread's byte offset inside a row
-};
-
-template <class C, bool REV>
-__device__ __forceinline__ Geo tile_geo(uint32_t ticket, const Dims& d, int wave, int rg, int cg) {
-    Geo g;
-    const int kk = (int)(ticket / (uint32_t)d.nS);
-    g.s = (int)ticket - kk * d.nS;
-    g.k = REV ? d.NK - 1 - kk : kk;
-    g.bi = g.s / d.nW;
-    g.dcol0 = (g.s - g.bi * d.nW) * C::W;
-    g.d0 = g.dcol0 + cg * C::V;
-    g.nvalid = g.d0 >= d.D ? 0 : ((d.D - g.d0) < C::V ? (d.D - g.d0) : C::V);
-    g.trow0 = g.k * C::CT;
-    g.row0 = g.trow0 + (wave * C::RG + rg) * C::NR;
-    const int left = d.T - g.row0;
-    g.nrows = g.nvalid == 0 ? 0 : (left <= 0 ? 0 : (left < C::NR ? left : C::NR));
-    g.tbase = (((size_t)g.bi * d.T + g.trow0) * d.D + g.dcol0) * C::EB;
-    // lanes past D read a valid column (their values are never used)
-    g.coff = (uint32_t)((g.nvalid > 0 ? cg * C::V : 0) * C::EB);
-    return g;
-}
-
-// Byte offset, from the tile base, of row `row` of this thread's column,
-// clamped to a row that exists (rows past T are read but never used).
-__device__ __forceinline__ uint32_t row_off(const Geo& g, int row, int T, uint32_t rowbytes) {
-    const int rc = row < T ? row : T - 1;
-    return (uint32_t)(rc - g.trow0) * rowbytes + g.coff;
-}
-
-// Segment-start byte of row i of this thread's segment (rows past T read the
-// last row; their steps are identity steps anyway).
-__device__ __forceinline__ uint32_t reset_byte(const uint8_t* reset, const Geo& g, int i, int T) {
-    const int row = g.row0 + i;
-    const int rc = row < T ? row : T - 1;
-    return reset[(size_t)g.bi * T + rc];
-}
-
-// Ticket, phase and the number of words to clear, read once per workgroup.
-struct Ticket {
-    uint32_t ticket, phase;
-    unsigned long long nclear;
-};
-
-__device__ __forceinline__ Ticket take_ticket(const Scratch& sc) {
-    __shared__ Ticket s_t;
-    if (threadIdx.x == 0) {
-        const uint32_t p = peek_u32(&sc.hdr->phase);
-        const uint32_t b = blockIdx.x;
-        const uint32_t c = (b % sc.nC + b / sc.nC) % sc.nC;  // a permutation within each row of nC
-        const uint32_t i = atomicAdd(sc.region[p] + (size_t)c * kCtrStride, 1u) + 1u;
-        s_t.phase = p;
-        s_t.ticket = i * sc.nC + c;
-        s_t.nclear = sc.hdr->dirty[p ^ 1u];
-        if (i == sc.quota - 1 && atomicAdd(&sc.hdr->done[p], 1u) + 1u == sc.nC - 1)
-            header_update(sc, p);
-    }
-    __syncthreads();
-    Ticket t;
-    t.ticket = uniform(s_t.ticket);
-    t.phase = uniform(s_t.phase);
-    t.nclear = (unsigned long long)uniform64((int64_t)s_t.nclear);
-    return t;
-}
-
-// Restore the all-ones state of this ticket's share of the words the
-// previous launch wrote in the region this launch does not use.
-__device__ __forceinline__ void clear_share(const Scratch& sc, uint32_t phase,
-                                            unsigned long long nclear, int nthreads, uint32_t ticket) {
-    uint32_t* other = sc.region[phase ^ 1u];
-    const unsigned long long stride = (unsigned long long)sc.total_tiles * nthreads;
-    for (unsigned long long i = (unsigned long long)ticket * nthreads + threadIdx.x; i < nclear;
-         i += stride)
-        other[i] = kEmpty;
-}
-
-// Largest `v` over the active lanes of the wavefront (wave-uniform result).
-__device__ __forceinline__ int wave_max_active(int v) {
-    unsigned long long act = __ballot(1);
-    int r = 0;
-    while (act) {
-        const int lane = __builtin_ctzll(act);
-        const int u = __shfl(v, lane, kWave);
-        r = u > r ? u : r;
-        act &= act - 1;
-    }
-    return uniform(r);
-}
-
-// Carry entering tile k of a chain (forward: DIR = -1 looks at k-1, k-2, ...;
-// reverse: DIR = +1 looks at k+1, k+2, ...).  `base0` is the carry entering the
-// chain (h0 forward, grad_last reverse).  The nearest published inclusive
-// state within a window of LB predecessors is taken and the maps of the tiles
-// in between are applied to it oldest first, so the result is the plain
-// chained value.
-//
-// The window is polled up to `polls` times.  After that the tile stops
-// waiting: it finds the nearest published state at any distance, and derives
-// every map in between that is not yet published itself, with `map_of(j)`,
-// from the inputs and bitwise equal to what tile j publishes.  So no tile
-// ever waits on a workgroup that has not started, whatever order the
-// hardware starts workgroups in, and results do not depend on which path
-// was taken.
-template <int DIR, int LB, class MapOf>
-__device__ float look_back(const unsigned long long* pqs, const uint32_t* hs, int k, int NK, int nS,
-                           int s, int W, int c, float base0, uint32_t polls, MapOf&& map_of) {
-    const int span = DIR < 0 ? k : (NK - 1 - k);  // predecessors in the chain
-    if (span == 0) return base0;
-    // entry of predecessor i (0: the nearest): wave-uniform base + per-lane column
-    auto entry = [&](int i) -> size_t {
-        const int j = k + DIR * (1 + i);
-        return ((size_t)j * (size_t)nS + (size_t)s) * W + c;
-    };
-    for (uint32_t spin = 0; spin < polls; ++spin) {
-        uint32_t hw[LB];
-        unsigned long long pq[LB];
-#pragma unroll
-        for (int i = 0; i < LB; ++i) {
-            if (i < span) {
-                const size_t e = entry(i);
-                hw[i] = peek_u32(hs + e);
-                pq[i] = peek_u64(pqs + e);
-            } else {
-                hw[i] = kEmpty;
-                pq[i] = ~0ull;
-            }
-        }
-        int depth = -1;
-        bool stop = false;
-        float base = base0;
-#pragma unroll
-        for (int i = 0; i < LB; ++i) {
-            if (depth < 0 && !stop) {
-                if (i >= span) {
-                    depth = i;  // reached the start of the chain
-                } else if (hw[i] != kEmpty) {
-                    depth = i;
-                    base = __uint_as_float(hw[i]);
-                } else if ((uint32_t)pq[i] == kEmpty) {
-                    stop = true;
-                }
-            }
-        }
-        if (depth < 0 && !stop && span == LB) depth = LB;  // chain start just past the window
-        if (depth >= 0) {
-            float x = base;
-#pragma unroll
-            for (int i = LB - 1; i >= 0; --i)
-                if (i < depth) x = aff_apply(unpack_aff(pq[i]), x);
-            return x;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    // nearest published state at any distance (or the chain start) ...
-    int m = span;
-    float base = base0;
-    for (int i0 = 0; i0 < span && m == span; i0 += LB) {
-        uint32_t hw[LB];
-#pragma unroll
-        for (int i = 0; i < LB; ++i) hw[i] = i0 + i < span ? peek_u32(hs + entry(i0 + i)) : kEmpty;
-#pragma unroll
-        for (int i = 0; i < LB; ++i) {
-            if (m == span && hw[i] != kEmpty) {
-                m = i0 + i;
-                base = __uint_as_float(hw[i]);
-            }
-        }
-    }
-    // ... then the m maps in between, oldest first, published or derived
-    // The walk is wave-uniform, so a map that some lane has to derive is
-    // derived for the same tile in every lane at once (each for its own lane
-    // of the block), with wave-uniform row addresses.
-    float x = base;
-    const int m_max = wave_max_active(m);
-#pragma unroll 1
-    for (int i = m_max - 1; i >= 0; --i) {
-        const bool mine = i < m;
-        const unsigned long long w = mine ? peek_u64(pqs + entry(i)) : 0ull;
-        const bool need = mine && (uint32_t)w == kEmpty;
-        Aff a = unpack_aff(w);
-        if (__any(need)) {
-            const Aff dm = map_of(k + DIR * (1 + i));
-            if (need) a = dm;
-        }
-        if (mine) x = aff_apply(a, x);
-    }
-    return x;
-}
-
-// Pairwise reduction, in a fixed association, of the RG maps a wavefront's
-// row groups produce, fed one at a time in scan order: for RG a power of two
-// this is the balanced tree that the in-wavefront Hillis-Steele scan forms
-// for its last group, so the total is bitwise the same.
-template <int RG>
-struct TreeFold {
-    static constexpr int L = RG == 1 ? 1 : (RG == 2 ? 1 : (RG == 4 ? 2 : 3));  // pending levels
-    Aff st[L];
-    Aff top;
-    // g-th leaf (0-based): merge it with the pending left node of every level
-    // the leaf completes; the root lands in `top`
-    __device__ __forceinline__ void push(int g, Aff node) {
-        if (RG == 1) {
-            top = node;
-            return;
-        }
-#pragma unroll
-        for (int lvl = 0; lvl < L; ++lvl) {
-            if (((g >> lvl) & 1) == 0) {
-                st[lvl] = node;
-                return;
-            }
-            node = aff_then(st[lvl], node);
-        }
-        top = node;
-    }
-    __device__ __forceinline__ Aff total() const { return top; }
+struct AffThen {
+    __device__ static Aff then(Aff earlier, Aff later) { return aff_then(earlier, later); }
 };
 
 struct FwdArgs {
@@ -407,7 +120,7 @@ __device__ Aff fwd_tile_map(const FwdArgs& x, int j, int bi, int col) {
     const uint32_t coff = (uint32_t)col * C::EB;
 #pragma unroll 1
     for (int w = 0; w < C::WAVES; ++w) {
-        TreeFold<RG> tree;
+        TreeFold<RG, Aff, AffThen> tree;
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
             Aff t = aff_identity();
@@ -445,7 +158,7 @@ __device__ Aff bwd_tile_map(const BwdArgs& x, int j, int bi, int col) {
     const uint32_t coff = (uint32_t)col * C::EB;
 #pragma unroll 1
     for (int w = C::WAVES - 1; w >= 0; --w) {
-        TreeFold<RG> tree;
+        TreeFold<RG, Aff, AffThen> tree;
 #pragma unroll
         for (int g = RG - 1; g >= 0; --g) {
             Aff t = aff_identity();
@@ -567,8 +280,9 @@ void fused_fwd_kernel(FwdArgs x) {
         if (more) publish_u64(const_cast<unsigned long long*>(pqs) + o, pack_aff(A));
         const int dl = g.dcol0 + c;
         const float base0 = (x.h0 && dl < d.D) ? x.h0[(size_t)g.bi * d.D + dl] : 0.0f;
-        const float hin = look_back<-1, C::LB>(pqs, hs, g.k, d.NK, d.nS, g.s, W, c, base0, x.polls,
-                                               [&](int j) { return fwd_tile_map<C>(x, j, g.bi, dl); });
+        const RealLink lk{hs, pqs, d.nS, g.s, W, c};
+        const float hin = look_back<RealLink, -1, C::LB>(
+            lk, g.k, d.NK, base0, x.polls, [&](int j) { return fwd_tile_map<C>(x, j, g.bi, dl); });
         if (more) publish_u32(const_cast<uint32_t*>(hs) + o, publishable(aff_apply(A, hin)));
         s_hin[c] = hin;
     }
@@ -716,8 +430,9 @@ void fused_bwd_kernel(BwdArgs x) {
         if (more) publish_u64(const_cast<unsigned long long*>(pqs) + o, pack_aff(A));
         const int dl = g.dcol0 + c;
         const float base0 = (x.grad_last && dl < d.D) ? x.grad_last[(size_t)g.bi * d.D + dl] : 0.0f;
-        const float cin = look_back<+1, C::LB>(pqs, hs, g.k, d.NK, d.nS, g.s, W, c, base0, x.polls,
-                                               [&](int j) { return bwd_tile_map<C>(x, j, g.bi, dl); });
+        const RealLink lk{hs, pqs, d.nS, g.s, W, c};
+        const float cin = look_back<RealLink, +1, C::LB>(
+            lk, g.k, d.NK, base0, x.polls, [&](int j) { return bwd_tile_map<C>(x, j, g.bi, dl); });
         if (more) publish_u32(const_cast<uint32_t*>(hs) + o, publishable(aff_apply(A, cin)));
         s_cin[c] = cin;
     }
@@ -763,17 +478,6 @@ void fused_bwd_kernel(BwdArgs x) {
     }
 }
 
-// Workspace initialisation: header (phase 0, both counters unused, nothing
-// dirty) and both regions all-ones.
-__global__ void scratch_init_kernel(uint32_t* __restrict__ p, size_t words) {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
-         i += (size_t)gridDim.x * blockDim.x) {
-        uint32_t v = kEmpty;
-        if (i < kHeaderBytes / 4) v = (i == 32 || i == 33) ? kEmpty : 0u;  // Header::done
-        p[i] = v;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // host side: configurations, layout, launch
 // ---------------------------------------------------------------------------
@@ -799,65 +503,6 @@ const TileCfg* find_cfg(int dir, int width, int tile) {
             if (c.width == width && c.tile == tile) return &c;
     }
     return nullptr;
-}
-
-struct Layout {
-    int nW, nS, NK, W;
-    unsigned long long entries;
-};
-
-Layout layout_of(const Shape& s, int width, int tile) {
-    Layout L;
-    L.W = width * (s.dtype == DT_F32 ? Elem<DT_F32>::V : Elem<DT_BF16>::V);
-    L.nW = (int)((s.D + L.W - 1) / L.W);
-    L.nS = (int)(s.B * L.nW);
-    L.NK = (int)((s.T + tile - 1) / tile);
-    L.entries = (unsigned long long)L.NK * L.nS * L.W;
-    return L;
-}
-
-// Ticket counters: the largest power of two up to kMaxCounters dividing nS.
-int counters_of(const Layout& L) {
-    int c = 1;
-    while (c < kMaxCounters && L.nS % (2 * c) == 0) c *= 2;
-    return c;
-}
-
-unsigned long long ctr_words_of(const Layout& L) {
-    return (unsigned long long)counters_of(L) * kCtrStride;
-}
-
-size_t region_bytes_for(const Layout& L) {
-    return ((ctr_words_of(L) + 3 * L.entries) * 4 + 255) / 256 * 256;
-}
-
-// Region size implied by a workspace size (the same for every call on one buffer).
-size_t region_bytes_of(size_t ws_bytes) {
-    return ws_bytes < (size_t)kHeaderBytes ? 0 : (ws_bytes - kHeaderBytes) / 2 / 256 * 256;
-}
-
-hipError_t prepare(void* ws, size_t ws_bytes, bool init, const Layout& L, hipStream_t st,
-                   Scratch* sc) {
-    const size_t rb = region_bytes_of(ws_bytes);
-    if (rb < region_bytes_for(L)) return hipErrorInvalidValue;
-    char* base = static_cast<char*>(ws);
-    if (init) {
-        const size_t words = (kHeaderBytes + 2 * rb) / 4;
-        const unsigned blocks = (unsigned)std::min<size_t>((words + 255) / 256, 8192);
-        hipLaunchKernelGGL(scratch_init_kernel, dim3(blocks), dim3(256), 0, st,
-                           reinterpret_cast<uint32_t*>(base), words);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    sc->hdr = reinterpret_cast<Header*>(base);
-    sc->region[0] = reinterpret_cast<uint32_t*>(base + kHeaderBytes);
-    sc->region[1] = reinterpret_cast<uint32_t*>(base + kHeaderBytes + rb);
-    sc->entries = L.entries;
-    sc->ctr_words = ctr_words_of(L);
-    sc->total_tiles = (uint32_t)((unsigned long long)L.NK * L.nS);
-    sc->nC = (uint32_t)counters_of(L);
-    sc->quota = sc->total_tiles / sc->nC;
-    return hipSuccess;
 }
 
 template <int DT, int TPR, int NR, int WAVES, int LB, bool AL>
@@ -952,7 +597,7 @@ void fused_default_cfg(const Shape& s, int dir, bool aligned, int* width, int* t
 }
 
 size_t fused_workspace_bytes(const Shape& s, int width, int tile) {
-    return kHeaderBytes + 2 * region_bytes_for(layout_of(s, width, tile));
+    return kHeaderBytes + 2 * region_bytes_for(layout_of(s, width, tile), kRealWords);
 }
 
 hipError_t launch_fused_fwd(const Shape& s, int width, int tile, const void* a, const void* b,
@@ -962,7 +607,7 @@ hipError_t launch_fused_fwd(const Shape& s, int width, int tile, const void* a, 
     if (!c) return hipErrorInvalidValue;
     const Layout L = layout_of(s, width, tile);
     FwdArgs x;
-    hipError_t e = prepare(ws, ws_bytes, init, L, st, &x.sc);
+    hipError_t e = prepare(ws, ws_bytes, init, L, kRealWords, st, &x.sc);
     if (e != hipSuccess) return e;
     x.a = a;
     x.b = b;
@@ -988,7 +633,7 @@ hipError_t launch_fused_bwd(const Shape& s, int width, int tile, const void* a, 
     if (!c) return hipErrorInvalidValue;
     const Layout L = layout_of(s, width, tile);
     BwdArgs x;
-    hipError_t e = prepare(ws, ws_bytes, init, L, st, &x.sc);
+    hipError_t e = prepare(ws, ws_bytes, init, L, kRealWords, st, &x.sc);
     if (e != hipSuccess) return e;
     x.a = a;
     x.out = out;

@@ -73,4 +73,34 @@ hipError_t launch_fused_bwd(const Shape& s, int width, int tile, const void* a, 
                             const uint8_t* reset, void* grad_a, void* grad_b, float* grad_h0,
                             void* ws, size_t ws_bytes, bool init, int polls, hipStream_t st);
 
+// ---- complex diagonal scan (planar real / imaginary arrays) ----------------
+// [B, T, M] arrays of one storage type; states [B, M] fp32.  NULL h0 / last /
+// grad_last / grad_h0 pairs mean "zero" / "not wanted".
+struct CxFwdPtrs {
+    const void *ar, *ai, *br, *bi;
+    void *out_r, *out_i;         // NULL pair: state-only forward
+    float *last_r, *last_i;
+    const float *h0r, *h0i;
+    const uint8_t* reset;
+};
+struct CxBwdPtrs {
+    const void *ar, *ai, *hr, *hi, *gr, *gi;  // h = the forward's out
+    const float *glr, *gli, *h0r, *h0i;
+    const uint8_t* reset;
+    void *gar, *gai, *gbr, *gbi;
+    float *gh0r, *gh0i;
+};
+hipError_t launch_complex_seq_fwd(const Shape& s, const CxFwdPtrs& p, hipStream_t st);
+hipError_t launch_complex_seq_bwd(const Shape& s, const CxBwdPtrs& p, hipStream_t st);
+// The fused complex form has one tile shape (8 threads of 16 bytes per row
+// of each array, 128 rows); its workspace follows the fused conventions.
+constexpr int kComplexWidth = 8;
+constexpr int kComplexTile = 128;
+bool complex_fused_supported(const Shape& s);
+size_t complex_fused_workspace_bytes(const Shape& s);
+hipError_t launch_complex_fused_fwd(const Shape& s, const CxFwdPtrs& p, void* ws, size_t ws_bytes,
+                                    bool init, int polls, hipStream_t st);
+hipError_t launch_complex_fused_bwd(const Shape& s, const CxBwdPtrs& p, void* ws, size_t ws_bytes,
+                                    bool init, int polls, hipStream_t st);
+
 }  // namespace lrscan

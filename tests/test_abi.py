@@ -25,7 +25,8 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     names = set(declared_symbols())
-    for n in ("scan_fwd", "scan_bwd", "scan_fwd_ex", "scan_bwd_ex", "scan_step", "scan_workspace_bytes",
+    for n in ("scan_fwd", "scan_bwd", "scan_fwd_ex", "scan_bwd_ex", "scan_step", "scan_complex_fwd",
+              "scan_complex_bwd", "scan_complex_workspace_bytes", "scan_workspace_bytes",
               "scan_status_string", "scan_chunk_summary", "scan_chunk_prefix", "scan_chunk_replay",
               "scan_reverse_chunk_summary", "scan_reverse_chunk_prefix",
               "scan_reverse_chunk_replay"):
@@ -88,6 +89,23 @@ def test_argument_errors_return_status_without_work():
                                          lr.F32, None) == -2
     with pytest.raises(lr.LRScanError):
         lr.scan_fwd(None, fake, fake, None, 2, 8, 4, lr.F32, None)
+    # complex: pairs whole or NULL whole; no chunked form; one fused tile shape
+    assert lib.scan_complex_fwd(fake, fake, fake, fake, fake, None, None, None, None, None, 2, 8,
+                                4, lr.F32, None, None) == -1
+    assert lib.scan_complex_fwd(fake, fake, fake, fake, None, None, None, None, None, None, 2, 8,
+                                4, lr.F32, None, None) == -1
+    assert lib.scan_complex_fwd(fake, fake, fake, fake, fake, fake, None, None, None, None, 2, 0,
+                                4, lr.F32, None, None) == -2
+    o = lr.make_opts(algo="chunked")
+    assert lib.scan_complex_fwd(fake, fake, fake, fake, fake, fake, None, None, None, None, 2, 8,
+                                4, lr.F32, None, ctypes.byref(o)) == -7
+    o = lr.make_opts(algo="fused", chunk=256)
+    assert lib.scan_complex_bwd(*([fake] * 6), None, None, None, None, *([fake] * 4), None, None,
+                                2, 8, 4, lr.BF16, None, ctypes.byref(o)) == -4
+    assert lib.scan_complex_bwd(*([fake] * 6), fake, None, None, None, *([fake] * 4), None, None,
+                                2, 8, 4, lr.BF16, None, None) == -1
+    assert lr.scan_complex_workspace_bytes(2, 1000, 64, lr.F32) > 0
+    assert lr.scan_complex_workspace_bytes(2, 1000, 64, lr.F32, lr.make_opts(algo="seq")) == 0
     # a forward needs out or last; a step needs out or the new state
     assert lib.scan_fwd(fake, fake, None, None, 2, 8, 4, lr.F32, None) == -1
     assert lib.scan_step(None, fake, None, None, fake, fake, 2, 4, lr.F32, None) == -1

@@ -232,3 +232,68 @@ def random_inputs(B: int, T: int, D: int, dtype: str, seed: int = 0, a_lo: float
         gl = rng.standard_normal((B, D)).astype(np.float32)
         return inp, h0, gl
     return inp
+
+
+# ----------------------------------------------------------------------------
+# complex workloads (planar storage: separate real / imaginary arrays)
+# ----------------------------------------------------------------------------
+# ``cwide``  B=8 T=2048 M=2560 bf16: the wide workload with complex values.
+#            a = r e^{i theta}, r = clip(sigmoid(N(4,1)), 0.8, 0.9999),
+#            theta ~ U(-pi/8, pi/8); b = (N(0,1) + i N(0,1)) sqrt((1-r^2)/2);
+#            grad_out = N(0,1) + i N(0,1).  Drawn one batch row at a time in
+#            the order r, theta, b (re, im), grad_out (re, im).
+COMPLEX_WORKLOADS = {
+    "cwide": Workload("cwide", 8, 2048, 2560, "bf16", "cwide"),
+    "csmall": Workload("csmall", 2, 256, 64, "f32", "cwide"),
+}
+
+
+@dataclasses.dataclass
+class ComplexInputs:
+    """Stored planar inputs: float32 arrays, or uint16 bf16 bit arrays."""
+    workload: Workload
+    ar: np.ndarray
+    ai: np.ndarray
+    br: np.ndarray
+    bi: np.ndarray
+    gr: np.ndarray
+    gi: np.ndarray
+
+    def c128(self, name: str, lanes=None) -> np.ndarray:
+        """Exact stored values of "a", "b" or "g" as complex128 (optionally
+        restricted to a list of (b, m) lanes: [1, T, len])."""
+        re, im = getattr(self, name + "r"), getattr(self, name + "i")
+        if lanes is not None:
+            bs = np.array([l[0] for l in lanes])
+            ms = np.array([l[1] for l in lanes])
+            re, im = re[bs, :, ms].T[None], im[bs, :, ms].T[None]
+        dt = self.workload.dtype
+        return storage_to_f64(re, dt) + 1j * storage_to_f64(im, dt)
+
+
+def complex_inputs(B: int, T: int, M: int, dtype: str, seed: int = 0, r_lo: float = 0.8,
+                   r_hi: float = 0.9999, theta: float = np.pi / 8,
+                   name: str = "complex") -> ComplexInputs:
+    """Complex planar inputs with the cwide recipe (|a| = r clipped to
+    [r_lo, r_hi] from sigmoid(N(4,1)), phase ~ U(-theta, theta))."""
+    st = np.float32 if dtype == "f32" else np.uint16
+    arrs = [np.empty((B, T, M), st) for _ in range(6)]
+    rng = np.random.default_rng(seed)
+    for bi in range(B):
+        z = rng.normal(4.0, 1.0, size=(T, M))
+        r = np.clip(1.0 / (1.0 + np.exp(-z)), r_lo, r_hi)
+        th = rng.uniform(-theta, theta, size=(T, M))
+        scale = np.sqrt((1.0 - r * r) / 2.0)
+        b_re = rng.standard_normal((T, M)) * scale
+        b_im = rng.standard_normal((T, M)) * scale
+        g_re = rng.standard_normal((T, M))
+        g_im = rng.standard_normal((T, M))
+        vals = (r * np.cos(th), r * np.sin(th), b_re, b_im, g_re, g_im)
+        for dst, v in zip(arrs, vals):
+            dst[bi] = to_storage(v, dtype)
+    wl = Workload(name, B, T, M, dtype, "cwide")
+    return ComplexInputs(wl, *arrs)
+
+
+def generate_complex(wl: Workload, seed: int = 0) -> ComplexInputs:
+    return complex_inputs(wl.B, wl.T, wl.D, wl.dtype, seed, name=wl.name)
