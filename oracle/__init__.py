@@ -85,6 +85,8 @@ def _load():
                 "oracle_complex_fwd": [_I, _I, _I, _D, _D, _D, _D, _D, _D, _U8, _D, _D, _D, _D],
                 "oracle_complex_bwd": [_I, _I, _I, _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, _U8,
                                        _D, _D, _D, _D, _D, _D],
+                "oracle_samu_fwd": [_I, _I, _I] + [_D] * 8 + [_U8] + [_D] * 4,
+                "oracle_samu_bwd": [_I, _I, _I] + [_D] * 12 + [_U8] + [_D] * 8,
             }
             for name, args in sigs.items():
                 fn = getattr(lib, name)
@@ -303,3 +305,53 @@ def complex_bwd(a, h, g, h0=None, grad_last=None, reset=None):
                                _p(h0i), _p(glr), _p(gli), _p(rm), _p(gar), _p(gai), _p(gbr),
                                _p(gbi), _p(gh0r), _p(gh0i))
     return gar + 1j * gai, gbr + 1j * gbi, gh0r + 1j * gh0i
+
+
+# ----------------------------------------------------------------------------
+# fused-transition (SAMU-form) complex scan
+# ----------------------------------------------------------------------------
+def _f64v(x, shape):
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {x.shape}")
+    return x
+
+
+def samu_fwd(eta, delta, nu_log, theta_log, b, h0=None, reset=None):
+    """Scan with transitions rebuilt from controls: eta, delta [B, T];
+    nu_log, theta_log [M]; b complex [B, T, M].  Returns (out, last) complex."""
+    b = np.asarray(b)
+    B, T, M = b.shape
+    e, dl = _f64v(eta, (B, T)), _f64v(delta, (B, T))
+    nl, tl = _f64v(nu_log, (M,)), _f64v(theta_log, (M,))
+    br, bi = _planar(b, (B, T, M))
+    h0r, h0i = _planar(h0, (B, M))
+    rm = _mask(reset, B, T)
+    out_r, out_i = np.empty((B, T, M)), np.empty((B, T, M))
+    last_r, last_i = np.empty((B, M)), np.empty((B, M))
+    _load().oracle_samu_fwd(B, T, M, _p(e), _p(dl), _p(nl), _p(tl), _p(br), _p(bi), _p(h0r),
+                            _p(h0i), _p(rm), _p(out_r), _p(out_i), _p(last_r), _p(last_i))
+    return out_r + 1j * out_i, last_r + 1j * last_i
+
+
+def samu_bwd(eta, delta, nu_log, theta_log, h, g, h0=None, grad_last=None, reset=None):
+    """Gradients of L = sum Re(conj(g) h) + Re(conj(grad_last) h_{T-1}).
+    Returns (grad_eta [B,T], grad_delta [B,T], grad_nu_log [M],
+    grad_theta_log [M], grad_b complex [B,T,M], grad_h0 complex [B,M])."""
+    h = np.asarray(h)
+    B, T, M = h.shape
+    e, dl = _f64v(eta, (B, T)), _f64v(delta, (B, T))
+    nl, tl = _f64v(nu_log, (M,)), _f64v(theta_log, (M,))
+    hr, hi = _planar(h, (B, T, M))
+    gr, gi = _planar(g, (B, T, M))
+    h0r, h0i = _planar(h0, (B, M))
+    glr, gli = _planar(grad_last, (B, M))
+    rm = _mask(reset, B, T)
+    ge, gd = np.empty((B, T)), np.empty((B, T))
+    gn, gt = np.empty(M), np.empty(M)
+    gbr, gbi = np.empty((B, T, M)), np.empty((B, T, M))
+    gh0r, gh0i = np.empty((B, M)), np.empty((B, M))
+    _load().oracle_samu_bwd(B, T, M, _p(e), _p(dl), _p(nl), _p(tl), _p(hr), _p(hi), _p(gr),
+                            _p(gi), _p(h0r), _p(h0i), _p(glr), _p(gli), _p(rm), _p(ge), _p(gd),
+                            _p(gn), _p(gt), _p(gbr), _p(gbi), _p(gh0r), _p(gh0i))
+    return ge, gd, gn, gt, gbr + 1j * gbi, gh0r + 1j * gh0i

@@ -54,6 +54,15 @@ MUTANTS = [
      "double complex at = CMPLX(ar[i], ai[i]);"),
     ("c:h0_imag_dropped", "double complex h = h0r ? CMPLX(h0r[lane], h0i[lane]) : CMPLX(0.0, 0.0);",
      "double complex h = h0r ? CMPLX(h0r[lane], 0.0) : CMPLX(0.0, 0.0);"),
+    ("c:samu_nu_not_exp", "double nu = exp(nu_log), theta = exp(theta_log);",
+     "double nu = nu_log, theta = exp(theta_log);"),
+    ("c:samu_phase_sign", "return rho * cexp(CMPLX(0.0, theta + delta));",
+     "return rho * cexp(CMPLX(0.0, theta - delta));"),
+    ("c:samu_radial_no_nu", "double radial = -nu * exp(eta[tok]) * creal(w);",
+     "double radial = -exp(eta[tok]) * creal(w);"),
+    ("c:samu_theta_grad_no_theta", "grad_theta_log[m] += theta * phase;",
+     "grad_theta_log[m] += phase;"),
+    ("c:samu_phase_real_part", "double phase = cimag(w);", "double phase = creal(w);"),
     ("reset_mask_transposed", "return reset != NULL && reset[(size_t)bi * (size_t)T + (size_t)t] != 0;",
      "return reset != NULL && reset[(size_t)bi * (size_t)T + (size_t)(T - 1 - t)] != 0;"),
 ]

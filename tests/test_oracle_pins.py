@@ -548,3 +548,71 @@ def test_complex_gradients_match_finite_differences():
                 got = grad[idx].real if part == "re" else grad[idx].imag
                 assert abs(fd - got) <= 1e-7 * (1 + abs(fd)), (which, idx, part, fd, got)
     assert ga[1, 3, 0] == 0 and ga[1, 3, 1] == 0
+
+
+# ----------------------------------------------------------------------------
+# fused-transition (SAMU-form) scan (page "triton_training_scan.py",
+# _samu_forward / _samu_backward): a = exp(-nu e^eta) e^{i(theta + delta)},
+# nu = e^{nu_log}, theta = e^{theta_log}
+# ----------------------------------------------------------------------------
+def test_samu_hand_values_closed_form():
+    """nu_log = 0, eta = ln ln 2 gives rho = 1/2; theta = delta = pi/2 gives a
+    phase of pi: a = -1/2 on every step.  With b = 1 the scan is the geometric
+    sum h_t = (1 - (-1/2)^(t+1)) / (3/2); with b = i it is i times that."""
+    T = 60
+    eta = np.full((1, T), np.log(np.log(2.0)))
+    delta = np.full((1, T), np.pi / 2)
+    nu_log, theta_log = np.zeros(2), np.full(2, np.log(np.pi / 2))
+    b = np.zeros((1, T, 2), complex)
+    b[..., 0] = 1.0
+    b[..., 1] = 1j
+    out, last = oracle.samu_fwd(eta, delta, nu_log, theta_log, b)
+    t = np.arange(T)
+    geo = (1 - (-0.5) ** (t + 1)) / 1.5
+    assert np.allclose(out[0, :, 0], geo, rtol=0, atol=1e-14)
+    assert np.allclose(out[0, :, 1], 1j * geo, rtol=0, atol=1e-14)
+    assert np.allclose(last[0], [geo[-1], 1j * geo[-1]], atol=1e-14)
+
+
+def test_samu_gradients_match_finite_differences():
+    """grad_eta, grad_delta (per token), grad_nu_log, grad_theta_log (per
+    mode), grad_b and grad_h0 of L = sum Re(conj(g) h) + Re(conj(g_last) h_{T-1})
+    by central differences in fp64, with a reset mask."""
+    B, T, M = 2, 6, 3
+    r = np.random.default_rng(80)
+    eta, delta = r.uniform(-2.0, 0.5, (B, T)), r.uniform(-1.0, 1.0, (B, T))
+    nu_log, theta_log = r.uniform(-1.0, 0.5, M), r.uniform(-1.0, 1.0, M)
+    b, g = crand((B, T, M), 81), crand((B, T, M), 82)
+    h0, gl = crand((B, M), 83), crand((B, M), 84)
+    mask = np.zeros((B, T), bool)
+    mask[0, 2] = True
+
+    def loss(e, d, nl, tl, bb, hh0):
+        o, l = oracle.samu_fwd(e, d, nl, tl, bb, h0=hh0, reset=mask)
+        return float(np.sum((np.conj(g) * o).real) + np.sum((np.conj(gl) * l).real))
+
+    out, _ = oracle.samu_fwd(eta, delta, nu_log, theta_log, b, h0=h0, reset=mask)
+    ge, gd, gn, gt, gb, gh0 = oracle.samu_bwd(eta, delta, nu_log, theta_log, out, g, h0=h0,
+                                             grad_last=gl, reset=mask)
+    args = [eta, delta, nu_log, theta_log, b, h0]
+    eps = 1e-6
+    for which, grad in ((0, ge), (1, gd), (2, gn), (3, gt)):
+        for idx in np.ndindex(args[which].shape):
+            up = [x.copy() for x in args]
+            dn = [x.copy() for x in args]
+            up[which][idx] += eps
+            dn[which][idx] -= eps
+            fd = (loss(*up) - loss(*dn)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-7 * (1 + abs(fd)), (which, idx, fd, grad[idx])
+    for which, grad in ((4, gb), (5, gh0)):
+        for idx in np.ndindex(args[which].shape):
+            for unit in (1.0, 1j):
+                up = [x.copy() for x in args]
+                dn = [x.copy() for x in args]
+                up[which][idx] += eps * unit
+                dn[which][idx] -= eps * unit
+                fd = (loss(*up) - loss(*dn)) / (2 * eps)
+                got = grad[idx].real if unit == 1.0 else grad[idx].imag
+                assert abs(fd - got) <= 1e-7 * (1 + abs(fd)), (which, idx, unit, fd, got)
+    # a reset step's transition does not depend on its controls
+    assert ge[0, 2] == 0.0 and gd[0, 2] == 0.0
