@@ -36,6 +36,10 @@ WORKLOAD_TEXT = {
     "cwide": "complex, planar re/im: B=8 T=2048 M=2560 bf16 I/O fp32 state, a=r*exp(i*theta), "
              "r=clip(sigmoid(N(4,1)),0.8,0.9999), theta~U(-pi/8,pi/8), b=CN(0,1)*sqrt((1-r^2)/2)",
     "csmall": "complex, planar re/im: B=2 T=256 M=64 fp32, the cwide recipe",
+    "swide": "fused transition (SAMU form), planar re/im: B=8 T=2048 M=2560 bf16 I/O fp32 state, "
+             "a=exp(-e^nu_log e^eta) exp(i(e^theta_log+delta)) rebuilt in the kernel, "
+             "nu~U(0.005,0.5), theta~U(0.001,pi), eta~N(0,0.5^2), delta~N(0,0.1^2), b=0.3 CN(0,1)",
+    "ssmall": "fused transition (SAMU form): B=2 T=256 M=64 fp32, the swide recipe",
 }
 
 
@@ -180,6 +184,94 @@ def complex_line(args, wl, lr, torch, W):
     return res
 
 
+def samu_line(args, wl, lr, torch, W):
+    """JSON line of the fused-transition scan: train = forward + backward
+    (all four parameter gradients and grad_b); prefill = the state-only
+    forward.  Algorithmic bytes count the arrays of the interface only: the
+    forward reads b (re, im), eta, delta, nu_log, theta_log and writes out
+    (re, im) and last; the backward reads out, grad_out (re, im each), the
+    controls and parameters and writes grad_b (re, im) and the four
+    parameter gradients."""
+    inp = W.generate_samu(wl, seed=0)
+    B, T, M = wl.B, wl.T, wl.D
+    s = wl.itemsize
+    N = B * T * M
+
+    def dev(x):
+        if wl.dtype == "f32":
+            return torch.from_numpy(x).cuda()
+        return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+
+    eta, delta, br, bi, gr, gi = (dev(getattr(inp, n))
+                                  for n in ("eta", "delta", "br", "bi", "gr", "gi"))
+    nu_log = torch.from_numpy(inp.nu_log).cuda()
+    theta_log = torch.from_numpy(inp.theta_log).cuda()
+    dt = lr.F32 if wl.dtype == "f32" else lr.BF16
+    out_r, out_i = torch.empty_like(br), torch.empty_like(br)
+    gbr, gbi = torch.empty_like(br), torch.empty_like(br)
+    f32 = dict(device="cuda", dtype=torch.float32)
+    last = [torch.empty((B, M), **f32) for _ in range(2)]
+    ge, gd = torch.empty((B, T), **f32), torch.empty((B, T), **f32)
+    gn, gt = torch.empty((M,), **f32), torch.empty((M,), **f32)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    o = lr.make_opts(algo=args.algo)
+    P = lambda t: t.data_ptr()
+    ctl = (P(eta), P(delta), P(nu_log), P(theta_log))
+
+    def fwd(with_out=True):
+        lr.scan_samu_fwd(*ctl, P(br), P(bi), P(out_r) if with_out else None,
+                         P(out_i) if with_out else None, P(last[0]), P(last[1]), None, None,
+                         B, T, M, dt, sh, o)
+
+    def bwd():
+        lr.scan_samu_bwd(*ctl, P(out_r), P(out_i), P(gr), P(gi), None, None, None, None, P(ge),
+                         P(gd), P(gn), P(gt), P(gbr), P(gbi), None, None, B, T, M, dt, sh, o)
+
+    ctl_bytes = 2 * s * B * T + 8 * M
+    fwd_bytes = 4 * s * N + 8 * B * M + ctl_bytes
+    bwd_bytes = 6 * s * N + ctl_bytes + 8 * B * T + 8 * M
+    if args.mode == "prefill":
+        step = [lambda: fwd(False)]
+        nbytes = 2 * s * N + 8 * B * M + ctl_bytes
+    else:
+        step = [fwd, bwd]
+        nbytes = fwd_bytes + bwd_bytes
+    for _ in range(args.warmup):
+        for f in step:
+            f()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        for f in step:
+            f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    res = {"metric": f"fused-transition {args.mode}: effective HBM GB/s",
+           "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+           "data": "synthetic (seeded numpy draws, see workloads/__init__.py)",
+           "config": {"workload": f"{wl.name}: {WORKLOAD_TEXT[wl.name]}", "B": B, "T": T, "M": M}}
+    res["pct_of_peak"] = round(100 * res["value"] / HBM_PEAK_GBPS, 2)
+    if args.mode != "prefill":
+        for name, f, nb in (("fwd", fwd, fwd_bytes), ("bwd", bwd, bwd_bytes)):
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            for _ in range(args.steps):
+                f()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            kms = a0.elapsed_time(a1) / args.steps
+            res[f"{name}_us"] = round(kms * 1e3, 2)
+            res[f"{name}_GBps"] = round(nb / (kms * 1e-3) / 1e9, 1)
+    return res
+
+
 def inference_line(args, wl, lr, torch, a, b, dt):
     """JSON line of the state-only forward (prefill) or of the decode step."""
     B, T, D = wl.B, wl.T, wl.D
@@ -281,6 +373,10 @@ def main():
 
     if args.workload in W.COMPLEX_WORKLOADS:
         print(json.dumps(complex_line(args, W.COMPLEX_WORKLOADS[args.workload], lr, torch, W)),
+              flush=True)
+        return
+    if args.workload in W.SAMU_WORKLOADS:
+        print(json.dumps(samu_line(args, W.SAMU_WORKLOADS[args.workload], lr, torch, W)),
               flush=True)
         return
     wl = W.WORKLOADS[args.workload]

@@ -187,6 +187,54 @@ LRSCAN_API int scan_complex_bwd(const void* ar, const void* ai, const void* out_
 LRSCAN_API size_t scan_complex_workspace_bytes(int64_t B, int64_t T, int64_t M, int dtype,
                                                const lrscan_opts* opts);
 
+/* ------------------------------------------------------------------------
+ * Fused-transition complex scan, SAMU form (page "triton_training_scan.py":
+ * _samu_forward, _samu_backward, _SAMUScan).  The transition is not an input:
+ * for batch b, step t and mode m it is rebuilt inside the kernels from
+ * per-token controls eta, delta ([B, T], `dtype`) and per-mode parameters
+ * nu_log, theta_log ([M], fp32):
+ *   a = exp(-e^{nu_log[m]} * e^{eta[b,t]}) * exp(i (e^{theta_log[m]} + delta[b,t])),
+ *   h_t = a_t * h_{t-1} + b_t   (complex, planar b / out as for scan_complex_*).
+ * The backward is the gradient of the same real loss as scan_complex_bwd;
+ * with grad_a_t = lambda_t * conj(h_{t-1}), w = conj(a) * grad_a:
+ *   grad_eta[b,t]     = sum_m -e^{nu_log} e^{eta} Re(w),
+ *   grad_delta[b,t]   = sum_m Im(w),
+ *   grad_nu_log[m]    = sum_{b,t} -e^{nu_log} e^{eta} Re(w),
+ *   grad_theta_log[m] = sum_{b,t} e^{theta_log} Im(w),
+ * all fp32; grad_b and grad_h0 as for scan_complex_bwd.  The sums are taken in
+ * a fixed order (results do not depend on scheduling).  At a reset step
+ * (opts->reset) the transition is 0 and contributes nothing to the four
+ * parameter gradients.
+ * opts: algo AUTO or FUSED only (width 8, 128 rows: chunk and width 0 or
+ * those; anything else LRSCAN_ERR_ALGO / LRSCAN_ERR_CHUNK); workspace, polls
+ * and reset as for the real scan.  A caller workspace must hold
+ * scan_samu_workspace_bytes(); its contents are overwritten by every call.
+ * ------------------------------------------------------------------------ */
+/*   eta, delta, nu_log, theta_log, br, bi read.  out_r, out_i written (NULL
+ *   pair: state-only forward, then last is required).  last_r, last_i written
+ *   (nullable pair).  h0_r, h0_i (nullable pair). */
+LRSCAN_API int scan_samu_fwd(const void* eta, const void* delta, const float* nu_log,
+                             const float* theta_log, const void* br, const void* bi, void* out_r,
+                             void* out_i, float* last_r, float* last_i, const float* h0_r,
+                             const float* h0_i, int64_t B, int64_t T, int64_t M, int dtype,
+                             void* stream, const lrscan_opts* opts);
+/*   out_r, out_i: the forward's outputs.  grad_last_*, h0_*, grad_h0_*:
+ *   nullable pairs.  grad_eta, grad_delta ([B, T]), grad_nu_log,
+ *   grad_theta_log ([M]): each nullable (not computed when NULL).
+ *   grad_br, grad_bi ([B, T, M], dtype) written. */
+LRSCAN_API int scan_samu_bwd(const void* eta, const void* delta, const float* nu_log,
+                             const float* theta_log, const void* out_r, const void* out_i,
+                             const void* grad_out_r, const void* grad_out_i,
+                             const float* grad_last_r, const float* grad_last_i,
+                             const float* h0_r, const float* h0_i, float* grad_eta,
+                             float* grad_delta, float* grad_nu_log, float* grad_theta_log,
+                             void* grad_br, void* grad_bi, float* grad_h0_r, float* grad_h0_i,
+                             int64_t B, int64_t T, int64_t M, int dtype, void* stream,
+                             const lrscan_opts* opts);
+/* Bytes of caller workspace a fused-transition call needs (0 for invalid arguments). */
+LRSCAN_API size_t scan_samu_workspace_bytes(int64_t B, int64_t T, int64_t M, int dtype,
+                                            const lrscan_opts* opts);
+
 /* Bytes of workspace the call with these arguments needs (0 if none).
  * Returns 0 for invalid arguments. */
 LRSCAN_API size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t D, int dtype,

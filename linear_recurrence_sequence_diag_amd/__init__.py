@@ -63,6 +63,10 @@ _SIGS = {
     "scan_step": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P], _INT),
     "scan_complex_fwd": ([_P] * 10 + [_I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
     "scan_complex_bwd": ([_P] * 16 + [_I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
+    "scan_samu_fwd": ([_P] * 12 + [_I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
+    "scan_samu_bwd": ([_P] * 20 + [_I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
+    "scan_samu_workspace_bytes": ([_I64, _I64, _I64, _INT, ctypes.POINTER(Opts)],
+                                  ctypes.c_size_t),
     "scan_complex_workspace_bytes": ([_I64, _I64, _I64, _INT, ctypes.POINTER(Opts)],
                                      ctypes.c_size_t),
     "scan_auto_algo": ([_I64, _I64, _I64, _INT, _INT, ctypes.POINTER(_INT), ctypes.POINTER(_INT)],
@@ -161,6 +165,32 @@ def scan_complex_bwd(ar, ai, out_r, out_i, grad_out_r, grad_out_i, grad_last_r, 
 def scan_complex_workspace_bytes(B, T, M, dtype, opts=None):
     return library().scan_complex_workspace_bytes(B, T, M, dtype,
                                                   ctypes.byref(opts) if opts is not None else None)
+
+
+def scan_samu_fwd(eta, delta, nu_log, theta_log, br, bi, out_r, out_i, last_r, last_i, h0_r, h0_i,
+                  B, T, M, dtype, stream, opts):
+    return _check(library().scan_samu_fwd(eta, delta, nu_log, theta_log, br, bi, out_r, out_i,
+                                          last_r, last_i, h0_r, h0_i, B, T, M, dtype, stream,
+                                          ctypes.byref(opts) if opts is not None else None),
+                  "scan_samu_fwd")
+
+
+def scan_samu_bwd(eta, delta, nu_log, theta_log, out_r, out_i, grad_out_r, grad_out_i,
+                  grad_last_r, grad_last_i, h0_r, h0_i, grad_eta, grad_delta, grad_nu_log,
+                  grad_theta_log, grad_br, grad_bi, grad_h0_r, grad_h0_i, B, T, M, dtype, stream,
+                  opts):
+    return _check(library().scan_samu_bwd(eta, delta, nu_log, theta_log, out_r, out_i,
+                                          grad_out_r, grad_out_i, grad_last_r, grad_last_i, h0_r,
+                                          h0_i, grad_eta, grad_delta, grad_nu_log,
+                                          grad_theta_log, grad_br, grad_bi, grad_h0_r, grad_h0_i,
+                                          B, T, M, dtype, stream,
+                                          ctypes.byref(opts) if opts is not None else None),
+                  "scan_samu_bwd")
+
+
+def scan_samu_workspace_bytes(B, T, M, dtype, opts=None):
+    return library().scan_samu_workspace_bytes(B, T, M, dtype,
+                                               ctypes.byref(opts) if opts is not None else None)
 
 
 def scan_workspace_bytes(B, T, D, dtype, opts=None):
@@ -415,6 +445,85 @@ def complex_scan_backward(ar, ai, out_r, out_i, grad_out_r, grad_out_i, grad_las
     return g[0], g[1], g[2], g[3], gh0
 
 
+def _check_controls(eta, delta, nu_log, theta_log, ref):
+    """eta, delta: contiguous [B, T] tensors of b's dtype; nu_log, theta_log:
+    contiguous float32 [M] tensors, all on b's device."""
+    torch = _torch()
+    B, T, M = ref.shape
+    for name, t in (("eta", eta), ("delta", delta)):
+        if (not isinstance(t, torch.Tensor) or t.shape != (B, T) or t.dtype != ref.dtype
+                or t.device != ref.device or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous [B, T] tensor of b's dtype and device")
+    for name, t in (("nu_log", nu_log), ("theta_log", theta_log)):
+        if (not isinstance(t, torch.Tensor) or t.shape != (M,) or t.dtype != torch.float32
+                or t.device != ref.device or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [M] tensor on b's device")
+
+
+def samu_scan(eta, delta, nu_log, theta_log, br, bi, h0=None, with_last=True, with_out=True,
+              polls=0, reset=None, workspace=None):
+    """Fused-transition complex scan: a_t = exp(-e^nu_log e^eta) exp(i (e^theta_log + delta))
+    is rebuilt in the kernel; h_t = a_t h_{t-1} + b_t on planar [B, T, M] b.
+    Returns (out_r, out_i, last_r, last_i); parts not asked for are None."""
+    torch = _torch()
+    _check_seq("br", br)
+    _check_seq("bi", bi, br)
+    _check_controls(eta, delta, nu_log, theta_log, br)
+    _check_mask(reset, br)
+    h0r, h0i = _pair(h0)
+    _check_state("h0 (real part)", h0r, br)
+    _check_state("h0 (imaginary part)", h0i, br)
+    if not (with_out or with_last):
+        raise ValueError("a forward needs out or last")
+    B, T, M = br.shape
+    out_r = torch.empty_like(br) if with_out else None
+    out_i = torch.empty_like(br) if with_out else None
+    mk = (lambda: torch.empty((B, M), device=br.device, dtype=torch.float32))
+    last_r, last_i = (mk(), mk()) if with_last else (None, None)
+    with torch.cuda.device(br.device):
+        scan_samu_fwd(eta.data_ptr(), delta.data_ptr(), nu_log.data_ptr(), theta_log.data_ptr(),
+                      br.data_ptr(), bi.data_ptr(), _ptr(out_r), _ptr(out_i), _ptr(last_r),
+                      _ptr(last_i), _ptr(h0r), _ptr(h0i), B, T, M, dtype_code(br.dtype),
+                      _stream(br), make_opts(polls=polls, reset=reset, workspace=workspace))
+    return out_r, out_i, last_r, last_i
+
+
+def samu_scan_backward(eta, delta, nu_log, theta_log, out_r, out_i, grad_out_r, grad_out_i,
+                       grad_last=None, h0=None, need_grad_h0=False, polls=0, reset=None,
+                       workspace=None):
+    """Adjoint of samu_scan for L = sum Re(conj(g) out) + Re(conj(grad_last) last).
+    Returns (grad_eta [B,T], grad_delta [B,T], grad_nu_log [M], grad_theta_log [M]
+    (all float32), grad_br, grad_bi, (grad_h0_r, grad_h0_i) or None)."""
+    torch = _torch()
+    _check_seq("out_r", out_r)
+    for name, t in (("out_i", out_i), ("grad_out_r", grad_out_r), ("grad_out_i", grad_out_i)):
+        _check_seq(name, t, out_r)
+    _check_controls(eta, delta, nu_log, theta_log, out_r)
+    _check_mask(reset, out_r)
+    glr, gli = _pair(grad_last)
+    h0r, h0i = _pair(h0)
+    for name, t in (("grad_last", glr), ("grad_last", gli), ("h0", h0r), ("h0", h0i)):
+        _check_state(name, t, out_r)
+    B, T, M = out_r.shape
+    dev = out_r.device
+    ge = torch.empty((B, T), device=dev, dtype=torch.float32)
+    gd = torch.empty((B, T), device=dev, dtype=torch.float32)
+    gn = torch.empty((M,), device=dev, dtype=torch.float32)
+    gt = torch.empty((M,), device=dev, dtype=torch.float32)
+    gbr, gbi = torch.empty_like(out_r), torch.empty_like(out_r)
+    gh0 = ((torch.empty((B, M), device=dev, dtype=torch.float32),
+            torch.empty((B, M), device=dev, dtype=torch.float32)) if need_grad_h0 else None)
+    gh0r, gh0i = _pair(gh0)
+    with torch.cuda.device(dev):
+        scan_samu_bwd(eta.data_ptr(), delta.data_ptr(), nu_log.data_ptr(), theta_log.data_ptr(),
+                      out_r.data_ptr(), out_i.data_ptr(), grad_out_r.data_ptr(),
+                      grad_out_i.data_ptr(), _ptr(glr), _ptr(gli), _ptr(h0r), _ptr(h0i),
+                      ge.data_ptr(), gd.data_ptr(), gn.data_ptr(), gt.data_ptr(), gbr.data_ptr(),
+                      gbi.data_ptr(), _ptr(gh0r), _ptr(gh0i), B, T, M, dtype_code(out_r.dtype),
+                      _stream(out_r), make_opts(polls=polls, reset=reset, workspace=workspace))
+    return ge, gd, gn, gt, gbr, gbi, gh0
+
+
 def n_chunks(T, chunk):
     return (T + chunk - 1) // chunk
 
@@ -530,6 +639,45 @@ def complex_diagonal_scan(ar, ai, br, bi, reset=None):
     if _complex_autograd_cls is None:
         _complex_autograd_cls = _make_complex_autograd()
     return _complex_autograd_cls.apply(ar, ai, br, bi, reset)
+
+
+_samu_autograd_cls = None
+
+
+def _make_samu_autograd():
+    torch = _torch()
+
+    class SAMUScan(torch.autograd.Function):
+        """(out_r, out_i) of the fused-transition scan; the backward rebuilds the
+        transitions and returns gradients for eta, delta, nu_log, theta_log, br, bi."""
+
+        @staticmethod
+        def forward(ctx, eta, delta, nu_log, theta_log, br, bi, reset):
+            eta, delta, nu_log, theta_log, br, bi = (
+                t.contiguous() for t in (eta, delta, nu_log, theta_log, br, bi))
+            out_r, out_i, _, _ = samu_scan(eta, delta, nu_log, theta_log, br, bi,
+                                           with_last=False, reset=reset)
+            ctx.save_for_backward(eta, delta, nu_log, theta_log, out_r, out_i)
+            ctx.reset = reset
+            return out_r, out_i
+
+        @staticmethod
+        def backward(ctx, grad_out_r, grad_out_i):
+            eta, delta, nu_log, theta_log, out_r, out_i = ctx.saved_tensors
+            ge, gd, gn, gt, gbr, gbi, _ = samu_scan_backward(
+                eta, delta, nu_log, theta_log, out_r, out_i, grad_out_r.contiguous(),
+                grad_out_i.contiguous(), reset=ctx.reset)
+            return (ge.to(eta.dtype), gd.to(delta.dtype), gn, gt, gbr, gbi, None)
+
+    return SAMUScan
+
+
+def samu_diagonal_scan(eta, delta, nu_log, theta_log, br, bi, reset=None):
+    """Differentiable fused-transition scan (torch autograd); returns (out_r, out_i)."""
+    global _samu_autograd_cls
+    if _samu_autograd_cls is None:
+        _samu_autograd_cls = _make_samu_autograd()
+    return _samu_autograd_cls.apply(eta, delta, nu_log, theta_log, br, bi, reset)
 
 
 def diagonal_scan(a, b, reset=None):

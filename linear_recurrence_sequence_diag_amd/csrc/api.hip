@@ -36,7 +36,8 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // ---- library-owned workspaces, one per (device, stream, kind) ----------------
 // Kind 0 holds the chunked form's P, Q and entering states; kind 1 holds the
 // fused form's self-cleaning scratch, which must not be shared with anything
-// else and is initialised once per allocation.
+// else and is initialised once per allocation; kind 2 holds the
+// fused-transition scan's factor tables and partial sums.
 struct CachedWs {
     void* ptr = nullptr;
     size_t bytes = 0;
@@ -208,6 +209,41 @@ int complex_workspace(const Shape& s, int algo, const lrscan_opts* o, hipStream_
         return LRSCAN_OK;
     }
     return library_workspace(need, 1, st, ws) == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_HIP;
+}
+
+// ---- fused-transition scan helpers ----
+
+// AUTO or FUSED with the one tile shape; other algorithms are not provided.
+int samu_algo(const lrscan_opts* o) {
+    const int a = o ? o->algo : LRSCAN_ALGO_AUTO;
+    if (a != LRSCAN_ALGO_AUTO && a != LRSCAN_ALGO_FUSED) return LRSCAN_ERR_ALGO;
+    const int c = o ? o->chunk : 0, w = o ? o->width : 0;
+    if ((c != 0 && c != kComplexTile) || (w != 0 && w != kComplexWidth)) return LRSCAN_ERR_CHUNK;
+    return LRSCAN_OK;
+}
+
+size_t samu_need(const Shape& s) { return align_up(samu_scratch_bytes(s), 256) + samu_aux_bytes(s); }
+
+// The fused scratch (library kind 1, or the head of the caller's buffer) and
+// the auxiliary tables (library kind 2, or the caller's buffer after it).
+int samu_workspace(const Shape& s, const lrscan_opts* o, hipStream_t st, Workspace* ws,
+                   void** aux) {
+    *ws = Workspace{};
+    if (!samu_supported(s)) return LRSCAN_ERR_DIM;
+    if (o && o->workspace) {
+        if (o->workspace_bytes < samu_need(s)) return LRSCAN_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(o->workspace) % 256 != 0) return LRSCAN_ERR_WORKSPACE;
+        ws->ptr = o->workspace;
+        ws->bytes = samu_scratch_bytes(s);
+        ws->init = true;
+        *aux = static_cast<char*>(o->workspace) + align_up(samu_scratch_bytes(s), 256);
+        return LRSCAN_OK;
+    }
+    if (library_workspace(samu_scratch_bytes(s), 1, st, ws) != hipSuccess) return LRSCAN_ERR_HIP;
+    Workspace a;
+    if (library_workspace(samu_aux_bytes(s), 2, st, &a) != hipSuccess) return LRSCAN_ERR_HIP;
+    *aux = a.ptr;
+    return LRSCAN_OK;
 }
 
 }  // namespace
@@ -430,6 +466,93 @@ LRSCAN_API size_t scan_complex_workspace_bytes(int64_t B, int64_t T, int64_t M, 
     if (complex_algo(opts, &algo) != LRSCAN_OK || algo != LRSCAN_ALGO_FUSED) return 0;
     const Shape s{B, T, M, dtype};
     return complex_fused_supported(s) ? complex_fused_workspace_bytes(s) : 0;
+}
+
+// ---- fused-transition (SAMU-form) complex scan ---------------------------------------
+
+LRSCAN_API int scan_samu_fwd(const void* eta, const void* delta, const float* nu_log,
+                             const float* theta_log, const void* br, const void* bi, void* out_r,
+                             void* out_i, float* last_r, float* last_i, const float* h0_r,
+                             const float* h0_i, int64_t B, int64_t T, int64_t M, int dtype,
+                             void* stream, const lrscan_opts* opts) {
+    if (!eta || !delta || !nu_log || !theta_log || !br || !bi) return LRSCAN_ERR_NULL;
+    if (!pair_ok(out_r, out_i) || !pair_ok(last_r, last_i) || !pair_ok(h0_r, h0_i))
+        return LRSCAN_ERR_NULL;
+    if (!out_r && !last_r) return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, T, M)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
+    int st = samu_algo(opts);
+    if (st != LRSCAN_OK) return st;
+    const Shape s{B, T, M, dtype};
+    const SamuFwdPtrs p{eta,    delta,  nu_log, theta_log, br,   bi,  out_r,
+                        out_i,  last_r, last_i, h0_r,      h0_i, opts ? opts->reset : nullptr};
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    Workspace ws;
+    void* aux = nullptr;
+    st = samu_workspace(s, opts, hs, &ws, &aux);
+    if (st != LRSCAN_OK) return st;
+    return fused_status(
+        launch_samu_fwd(s, p, ws.ptr, ws.bytes, ws.init, aux, opts ? opts->polls : 0, hs), ws,
+        opts, hs);
+}
+
+LRSCAN_API int scan_samu_bwd(const void* eta, const void* delta, const float* nu_log,
+                             const float* theta_log, const void* out_r, const void* out_i,
+                             const void* grad_out_r, const void* grad_out_i,
+                             const float* grad_last_r, const float* grad_last_i,
+                             const float* h0_r, const float* h0_i, float* grad_eta,
+                             float* grad_delta, float* grad_nu_log, float* grad_theta_log,
+                             void* grad_br, void* grad_bi, float* grad_h0_r, float* grad_h0_i,
+                             int64_t B, int64_t T, int64_t M, int dtype, void* stream,
+                             const lrscan_opts* opts) {
+    if (!eta || !delta || !nu_log || !theta_log || !out_r || !out_i || !grad_out_r ||
+        !grad_out_i || !grad_br || !grad_bi)
+        return LRSCAN_ERR_NULL;
+    if (!pair_ok(grad_last_r, grad_last_i) || !pair_ok(h0_r, h0_i) ||
+        !pair_ok(grad_h0_r, grad_h0_i))
+        return LRSCAN_ERR_NULL;
+    if (!dims_ok(B, T, M)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
+    int st = samu_algo(opts);
+    if (st != LRSCAN_OK) return st;
+    const Shape s{B, T, M, dtype};
+    SamuBwdPtrs p;
+    p.eta = eta;
+    p.delta = delta;
+    p.nu_log = nu_log;
+    p.theta_log = theta_log;
+    p.hr = out_r;
+    p.hi = out_i;
+    p.gr = grad_out_r;
+    p.gi = grad_out_i;
+    p.glr = grad_last_r;
+    p.gli = grad_last_i;
+    p.h0r = h0_r;
+    p.h0i = h0_i;
+    p.reset = opts ? opts->reset : nullptr;
+    p.grad_eta = grad_eta;
+    p.grad_delta = grad_delta;
+    p.grad_nu_log = grad_nu_log;
+    p.grad_theta_log = grad_theta_log;
+    p.gbr = grad_br;
+    p.gbi = grad_bi;
+    p.gh0r = grad_h0_r;
+    p.gh0i = grad_h0_i;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    Workspace ws;
+    void* aux = nullptr;
+    st = samu_workspace(s, opts, hs, &ws, &aux);
+    if (st != LRSCAN_OK) return st;
+    return fused_status(
+        launch_samu_bwd(s, p, ws.ptr, ws.bytes, ws.init, aux, opts ? opts->polls : 0, hs), ws,
+        opts, hs);
+}
+
+LRSCAN_API size_t scan_samu_workspace_bytes(int64_t B, int64_t T, int64_t M, int dtype,
+                                            const lrscan_opts* opts) {
+    if (!dims_ok(B, T, M) || !dtype_ok(dtype) || samu_algo(opts) != LRSCAN_OK) return 0;
+    const Shape s{B, T, M, dtype};
+    return samu_supported(s) ? samu_need(s) : 0;
 }
 
 // ---- the chunked form, step by step ---------------------------------------------

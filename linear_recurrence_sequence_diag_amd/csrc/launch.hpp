@@ -103,4 +103,38 @@ hipError_t launch_complex_fused_fwd(const Shape& s, const CxFwdPtrs& p, void* ws
 hipError_t launch_complex_fused_bwd(const Shape& s, const CxBwdPtrs& p, void* ws, size_t ws_bytes,
                                     bool init, int polls, hipStream_t st);
 
+// ---- fused-transition (SAMU-form) complex scan ------------------------------
+// The transition is rebuilt from per-token controls eta, delta ([B, T], I/O
+// type) and per-mode parameters nu_log, theta_log ([M], fp32).
+struct SamuFwdPtrs {
+    const void *eta, *delta;
+    const float *nu_log, *theta_log;
+    const void *br, *bi;
+    void *out_r, *out_i;  // NULL pair: state-only forward
+    float *last_r, *last_i;
+    const float *h0r, *h0i;
+    const uint8_t* reset;
+};
+struct SamuBwdPtrs {
+    const void *eta, *delta;
+    const float *nu_log, *theta_log;
+    const void *hr, *hi, *gr, *gi;  // h = the forward's out
+    const float *glr, *gli, *h0r, *h0i;
+    const uint8_t* reset;
+    float *grad_eta, *grad_delta, *grad_nu_log, *grad_theta_log;
+    void *gbr, *gbi;
+    float *gh0r, *gh0i;
+};
+bool samu_supported(const Shape& s);
+// Two buffers: `ws` is the fused scratch (conventions of the fused form,
+// samu_scratch_bytes); `aux` (256-byte aligned, samu_aux_bytes) holds the
+// per-call transition factor tables and the backward's partial sums, and is
+// overwritten by every call.
+size_t samu_scratch_bytes(const Shape& s);
+size_t samu_aux_bytes(const Shape& s);
+hipError_t launch_samu_fwd(const Shape& s, const SamuFwdPtrs& p, void* ws, size_t ws_bytes,
+                           bool init, void* aux, int polls, hipStream_t st);
+hipError_t launch_samu_bwd(const Shape& s, const SamuBwdPtrs& p, void* ws, size_t ws_bytes,
+                           bool init, void* aux, int polls, hipStream_t st);
+
 }  // namespace lrscan

@@ -27,6 +27,7 @@ def test_header_declares_the_boundary():
     names = set(declared_symbols())
     for n in ("scan_fwd", "scan_bwd", "scan_fwd_ex", "scan_bwd_ex", "scan_step", "scan_complex_fwd",
               "scan_complex_bwd", "scan_complex_workspace_bytes", "scan_workspace_bytes",
+              "scan_samu_fwd", "scan_samu_bwd", "scan_samu_workspace_bytes",
               "scan_status_string", "scan_chunk_summary", "scan_chunk_prefix", "scan_chunk_replay",
               "scan_reverse_chunk_summary", "scan_reverse_chunk_prefix",
               "scan_reverse_chunk_replay"):
@@ -106,6 +107,34 @@ def test_argument_errors_return_status_without_work():
                                 2, 8, 4, lr.BF16, None, None) == -1
     assert lr.scan_complex_workspace_bytes(2, 1000, 64, lr.F32) > 0
     assert lr.scan_complex_workspace_bytes(2, 1000, 64, lr.F32, lr.make_opts(algo="seq")) == 0
+    # fused-transition scan: controls required, pairs whole, AUTO/FUSED only
+    assert lib.scan_samu_fwd(None, *([fake] * 7), None, None, None, None, 2, 8, 4, lr.F32, None,
+                             None) == -1
+    assert lib.scan_samu_fwd(*([fake] * 7), None, None, None, None, None, 2, 8, 4, lr.F32, None,
+                             None) == -1
+    assert lib.scan_samu_fwd(*([fake] * 8), None, None, None, None, 2, 8, 0, lr.F32, None,
+                             None) == -2
+    assert lib.scan_samu_fwd(*([fake] * 8), None, None, None, None, 2, 8, 4, 3, None, None) == -3
+    for algo, code in (("seq", -7), ("chunked", -7)):
+        o = lr.make_opts(algo=algo)
+        assert lib.scan_samu_fwd(*([fake] * 8), None, None, None, None, 2, 8, 4, lr.F32, None,
+                                 ctypes.byref(o)) == code
+    o = lr.make_opts(algo="fused", chunk=64)
+    assert lib.scan_samu_bwd(*([fake] * 8), None, None, None, None, None, None, None, None,
+                             fake, fake, None, None, 2, 8, 4, lr.BF16, None,
+                             ctypes.byref(o)) == -4
+    assert lib.scan_samu_bwd(*([fake] * 8), fake, None, None, None, None, None, None, None,
+                             fake, fake, None, None, 2, 8, 4, lr.BF16, None, None) == -1
+    assert lib.scan_samu_bwd(*([fake] * 8), None, None, None, None, None, None, None, None,
+                             None, fake, None, None, 2, 8, 4, lr.BF16, None, None) == -1
+    assert lr.scan_samu_workspace_bytes(2, 1000, 64, lr.F32) > lr.scan_complex_workspace_bytes(
+        2, 1000, 64, lr.F32)
+    assert lr.scan_samu_workspace_bytes(2, 1000, 64, lr.F32, lr.make_opts(algo="seq")) == 0
+    o = lr.make_opts()
+    o.workspace = fake
+    o.workspace_bytes = 16
+    assert lib.scan_samu_fwd(*([fake] * 8), None, None, None, None, 2, 8, 4, lr.F32, None,
+                             ctypes.byref(o)) == -5
     # a forward needs out or last; a step needs out or the new state
     assert lib.scan_fwd(fake, fake, None, None, 2, 8, 4, lr.F32, None) == -1
     assert lib.scan_step(None, fake, None, None, fake, fake, 2, 4, lr.F32, None) == -1

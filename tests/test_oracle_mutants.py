@@ -54,6 +54,15 @@ MUTANTS = [
      "double complex at = CMPLX(ar[i], ai[i]);"),
     ("c:h0_imag_dropped", "double complex h = h0r ? CMPLX(h0r[lane], h0i[lane]) : CMPLX(0.0, 0.0);",
      "double complex h = h0r ? CMPLX(h0r[lane], 0.0) : CMPLX(0.0, 0.0);"),
+    # the same slips in the fused-transition oracle, which spells these lines
+    # identically ("c2:" mutates the second occurrence)
+    ("c2:fwd_conj_a", "h = at * h + CMPLX(br[i], bi[i]);", "h = conj(at) * h + CMPLX(br[i], bi[i]);"),
+    ("c2:fwd_swap_re_im_b", "h = at * h + CMPLX(br[i], bi[i]);", "h = at * h + CMPLX(bi[i], br[i]);"),
+    ("c2:bwd_carry_no_conj", "carry = conj(at) * lam;", "carry = at * lam;"),
+    ("c2:bwd_grad_a_no_conj", "lam * conj(prev);", "lam * prev;"),
+    ("c2:bwd_grad_a_conj_lam", "lam * conj(prev);", "conj(lam) * prev;"),
+    ("c2:h0_imag_dropped", "double complex h = h0r ? CMPLX(h0r[lane], h0i[lane]) : CMPLX(0.0, 0.0);",
+     "double complex h = h0r ? CMPLX(h0r[lane], 0.0) : CMPLX(0.0, 0.0);"),
     ("c:samu_nu_not_exp", "double nu = exp(nu_log), theta = exp(theta_log);",
      "double nu = nu_log, theta = exp(theta_log);"),
     ("c:samu_phase_sign", "return rho * cexp(CMPLX(0.0, theta + delta));",
@@ -92,15 +101,28 @@ def test_clean_oracle_passes_pins(tmp_path):
     assert r.returncode == 0, r.stdout[-2000:]
 
 
+def _mutate(src, old, new, nth):
+    """Replace the nth occurrence of old (1-based)."""
+    at = -1
+    for _ in range(nth):
+        at = src.index(old, at + 1)
+    return src[:at] + new + src[at + len(old):]
+
+
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(name, old, new, tmp_path):
-    path = SRC_COMPLEX if name.startswith("c:") else SRC
+    path = SRC_COMPLEX if name.startswith(("c:", "c2:")) else SRC
     src = open(path).read()
-    assert src.count(old) == 1, f"mutation site for {name} not unique ({src.count(old)})"
+    # a site is either unique or spelled once in each complex oracle (two)
+    nth = 2 if name.startswith("c2:") else 1
+    assert src.count(old) in ((1, 2) if path == SRC_COMPLEX else (1,)), \
+        f"mutation site for {name} appears {src.count(old)} times"
+    assert src.count(old) >= nth, f"{name}: no occurrence {nth}"
+    mutated = _mutate(src, old, new, nth)
     tag = name.replace(":", "_")
     if path == SRC_COMPLEX:
-        so = _compile(open(SRC).read(), tmp_path, tag, complex_text=src.replace(old, new))
+        so = _compile(open(SRC).read(), tmp_path, tag, complex_text=mutated)
     else:
-        so = _compile(src.replace(old, new), tmp_path, tag)
+        so = _compile(mutated, tmp_path, tag)
     r = _run_pins(so)
     assert r.returncode != 0, f"mutant {name} survived the pins"

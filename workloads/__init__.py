@@ -297,3 +297,80 @@ def complex_inputs(B: int, T: int, M: int, dtype: str, seed: int = 0, r_lo: floa
 
 def generate_complex(wl: Workload, seed: int = 0) -> ComplexInputs:
     return complex_inputs(wl.B, wl.T, wl.D, wl.dtype, seed, name=wl.name)
+
+
+# ----------------------------------------------------------------------------
+# fused-transition (SAMU-form) workloads: the transition is not stored; it is
+# rebuilt from per-token controls eta, delta [B, T] (I/O type) and per-mode
+# parameters nu_log, theta_log [M] (float32).
+# ----------------------------------------------------------------------------
+# ``swide``  B=8 T=2048 M=2560 bf16: the wide shape with rebuilt transitions.
+#            Per mode (drawn first, in this order): nu = U(0.005, 0.5),
+#            theta = U(0.001, pi), stored as nu_log = ln nu, theta_log =
+#            ln theta.  Then per batch row: eta ~ N(0, 0.5^2),
+#            delta ~ N(0, 0.1^2) per token, b = 0.3 (N(0,1) + i N(0,1)),
+#            grad_out = N(0,1) + i N(0,1).  The decay exp(-nu e^eta) then
+#            spans about 0.25 .. 0.998.
+SAMU_WORKLOADS = {
+    "swide": Workload("swide", 8, 2048, 2560, "bf16", "swide"),
+    "ssmall": Workload("ssmall", 2, 256, 64, "f32", "swide"),
+}
+
+
+@dataclasses.dataclass
+class SamuInputs:
+    """Stored inputs: eta, delta [B, T] and planar b, grad_out [B, T, M] in the
+    I/O format (float32 or bf16 bits); nu_log, theta_log float32 [M]."""
+    workload: Workload
+    eta: np.ndarray
+    delta: np.ndarray
+    nu_log: np.ndarray
+    theta_log: np.ndarray
+    br: np.ndarray
+    bi: np.ndarray
+    gr: np.ndarray
+    gi: np.ndarray
+
+    def controls(self, rows=None):
+        """Exact stored (eta, delta, nu_log, theta_log) as float64 (eta and
+        delta optionally restricted to a list of batch rows)."""
+        dt = self.workload.dtype
+        e, d = self.eta, self.delta
+        if rows is not None:
+            e, d = e[rows], d[rows]
+        return (storage_to_f64(e, dt), storage_to_f64(d, dt),
+                self.nu_log.astype(np.float64), self.theta_log.astype(np.float64))
+
+    def c128(self, name: str, rows=None) -> np.ndarray:
+        """Exact stored "b" or "g" as complex128 (optionally only some batch rows)."""
+        re, im = getattr(self, name + "r"), getattr(self, name + "i")
+        if rows is not None:
+            re, im = re[rows], im[rows]
+        dt = self.workload.dtype
+        return storage_to_f64(re, dt) + 1j * storage_to_f64(im, dt)
+
+
+def samu_inputs(B: int, T: int, M: int, dtype: str, seed: int = 0, nu_hi: float = 0.5,
+                eta_sd: float = 0.5, name: str = "samu") -> SamuInputs:
+    """Inputs with the swide recipe (``nu_hi`` and ``eta_sd`` adjustable)."""
+    st = np.float32 if dtype == "f32" else np.uint16
+    rng = np.random.default_rng(seed)
+    nu = rng.uniform(0.005, nu_hi, size=M)
+    theta = rng.uniform(0.001, np.pi, size=M)
+    eta = np.empty((B, T), st)
+    delta = np.empty((B, T), st)
+    arrs = [np.empty((B, T, M), st) for _ in range(4)]
+    for bi in range(B):
+        eta[bi] = to_storage(rng.normal(0.0, eta_sd, size=T), dtype)
+        delta[bi] = to_storage(rng.normal(0.0, 0.1, size=T), dtype)
+        vals = (0.3 * rng.standard_normal((T, M)), 0.3 * rng.standard_normal((T, M)),
+                rng.standard_normal((T, M)), rng.standard_normal((T, M)))
+        for dst, v in zip(arrs, vals):
+            dst[bi] = to_storage(v, dtype)
+    wl = Workload(name, B, T, M, dtype, "swide")
+    return SamuInputs(wl, eta, delta, np.log(nu).astype(np.float32),
+                      np.log(theta).astype(np.float32), *arrs)
+
+
+def generate_samu(wl: Workload, seed: int = 0) -> SamuInputs:
+    return samu_inputs(wl.B, wl.T, wl.D, wl.dtype, seed, name=wl.name)
