@@ -53,7 +53,7 @@ def kernel_sources_sha256():
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_recurrence_sequence_diag_amd", "csrc")
-    for f in ("fused.hip", "device.hpp"):
+    for f in ("fused.hip", "fused_common.hpp", "device.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()

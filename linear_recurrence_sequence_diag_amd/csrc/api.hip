@@ -213,12 +213,12 @@ int complex_workspace(const Shape& s, int algo, const lrscan_opts* o, hipStream_
 
 // ---- fused-transition scan helpers ----
 
-// AUTO or FUSED with the one tile shape; other algorithms are not provided.
+// AUTO or FUSED with the library's tile shapes (chunk and width 0); other
+// algorithms are not provided.
 int samu_algo(const lrscan_opts* o) {
     const int a = o ? o->algo : LRSCAN_ALGO_AUTO;
     if (a != LRSCAN_ALGO_AUTO && a != LRSCAN_ALGO_FUSED) return LRSCAN_ERR_ALGO;
-    const int c = o ? o->chunk : 0, w = o ? o->width : 0;
-    if ((c != 0 && c != kComplexTile) || (w != 0 && w != kComplexWidth)) return LRSCAN_ERR_CHUNK;
+    if (o && (o->chunk != 0 || o->width != 0)) return LRSCAN_ERR_CHUNK;
     return LRSCAN_OK;
 }
 

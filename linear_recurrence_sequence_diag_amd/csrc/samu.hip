@@ -28,7 +28,7 @@ namespace {
 // Per-mode and per-token factors of the transition, computed once per call by
 // samu_factor_kernel into two small tables that every tile reads.
 struct SamuLane {
-    float nu, th, ct, st;  // nu, theta, cos theta, sin theta
+    float nu2, th, ct, st;  // nu log2(e), theta, cos theta, sin theta
 };
 struct SamuTok {
     float e, cd, sd;  // e^eta, cos delta, sin delta
@@ -43,6 +43,9 @@ __device__ __forceinline__ SamuTok samu_tok(const float4* tok_tab, size_t t) {
     const float4 v = tok_tab[t];
     return SamuTok{v.x, v.y, v.z};
 }
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.693147180559945309417f;
 
 template <int DT>
 __global__ void samu_factor_kernel(const void* __restrict__ eta, const void* __restrict__ delta,
@@ -59,16 +62,21 @@ __global__ void samu_factor_kernel(const void* __restrict__ eta, const void* __r
         const float th = expf(theta_log[i]);
         float st, ct;
         sincosf(th, &st, &ct);
-        mode_tab[i] = make_float4(expf(nu_log[i]), th, ct, st);
+        mode_tab[i] = make_float4(expf(nu_log[i]) * kLog2e, th, ct, st);
     }
 }
 
-// a = exp(-nu e^eta) e^{i (theta + delta)}, by angle addition.
-__device__ __forceinline__ Cx samu_a(const SamuLane& L, const SamuTok& k) {
+// a = exp(-nu e^eta) e^{i (theta + delta)}: the decay as 2^{-x2} with
+// x2 = nu log2(e) e^eta (one hardware exp2), the rotation by angle addition.
+__device__ __forceinline__ float samu_x2(const SamuLane& L, const SamuTok& k) { return L.nu2 * k.e; }
+__device__ __forceinline__ Cx samu_a_of(const SamuLane& L, const SamuTok& k, float x2) {
     const float cosine = fmaf(L.ct, k.cd, -(L.st * k.sd));
     const float sine = fmaf(L.st, k.cd, L.ct * k.sd);
-    const float rho = expf(-(L.nu * k.e));
+    const float rho = __builtin_amdgcn_exp2f(-x2);
     return Cx{rho * cosine, rho * sine};
+}
+__device__ __forceinline__ Cx samu_a(const SamuLane& L, const SamuTok& k) {
+    return samu_a_of(L, k, samu_x2(L, k));
 }
 
 struct SamuFwdArgs {
@@ -309,20 +317,33 @@ void samu_fwd_kernel(SamuFwdArgs x) {
     }
 }
 
-// Sum over the TPR lanes of one row group (every lane gets the total; the
-// butterfly has the same association in every lane).
-template <int TPR>
-__device__ __forceinline__ float row_sum(float v) {
+// Transposing sum of N values per lane over the lanes {l ^ o}, o running
+// over the powers of two from O down to LAST.  While a lane holds more than
+// one value, each stage halves them: the lane whose offset bit is clear keeps
+// the lower half, its partner the upper half, and each adds the partner's
+// copy of the half it keeps; once one value is left the remaining stages are
+// plain butterfly sums.  Afterwards a lane holds K = max(1, N / G) values (G
+// the number of lanes in the group), value q being the total of index
+//   q + K * (g / max(1, G / N)),   g = the lane's position in its group,
+// and lanes with the same g / max(1, G / N) hold the same totals.  The order of
+// the additions is fixed, so the sums are deterministic, and a stage costs
+// max(1, N / 2^k) shuffles instead of N.
+template <int N, int O, int LAST>
+__device__ __forceinline__ void tsum(float* v, int lane) {
+    if constexpr (N >= 2) {
+        constexpr int H = N / 2;
+        const bool up = (lane & O) != 0;
 #pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) v += __shfl_xor(v, o, kWave);
-    return v;
-}
-// Sum over the row groups of a wavefront (lanes with the same column).
-template <int TPR>
-__device__ __forceinline__ float col_sum(float v) {
-#pragma unroll
-    for (int o = TPR; o < kWave; o <<= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+        for (int q = 0; q < H; ++q) {
+            const float mine = up ? v[H + q] : v[q];
+            const float give = up ? v[q] : v[H + q];
+            v[q] = mine + __shfl_xor(give, O, kWave);
+        }
+        if constexpr (O > LAST) tsum<H, O / 2, LAST>(v, lane);
+    } else {
+        v[0] += __shfl_xor(v[0], O, kWave);
+        if constexpr (O > LAST) tsum<1, O / 2, LAST>(v, lane);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -439,25 +460,31 @@ void samu_bwd_kernel(SamuBwdArgs x) {
     char* pgbr = static_cast<char*>(x.p.gbr) + g.tbase;
     char* pgbi = static_cast<char*>(x.p.gbi) + g.tbase;
     Cx carry[V];
-    float acc_nu[V], acc_th[V];
+    // acc[2j], acc[2j+1]: this thread's sums over its rows of lane j's radial
+    // and phase terms (theta is applied once per tile and lane); tsum_[2i], [2i+1]: row i's sums over
+    // this thread's lanes of the radial and phase terms
+    float acc[2 * V], tsum_[2 * NR];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         const int col = cg * V + j;
         Cx xv = s_cin[col];
         for (int w = WAVES - 1; w > wave; --w) xv = caff_apply(s_wtot[w][col], xv);
         carry[j] = caff_apply(s_excl[wave][j][l], xv);
-        acc_nu[j] = 0.0f;
-        acc_th[j] = 0.0f;
+        acc[2 * j] = 0.0f;
+        acc[2 * j + 1] = 0.0f;
     }
     const int lb = g.s - g.bi * d.nW;  // lane block of this tile
 #pragma unroll
     for (int i = NR - 1; i >= 0; --i) {
         const int row = g.row0 + i;
+        tsum_[2 * i] = 0.0f;
+        tsum_[2 * i + 1] = 0.0f;
         if (row < d.T) {  // the same for every lane of a row group
             RowOut<C::DT> obr, obi;
             float rsum = 0.0f, psum = 0.0f;
 #pragma unroll
             for (int j = 0; j < V; ++j) {
+                const float x2 = samu_x2(ln[j], tok[i]);
                 const Cx at = trans(i, j);
                 const Cx lam = cadd(vget(gr[i], gi[i], j), carry[j]);
                 Cx hp = vget(hr[i], hi[i], j);
@@ -471,12 +498,12 @@ void samu_bwd_kernel(SamuBwdArgs x) {
                 const Cx ga = rs ? Cx{0.0f, 0.0f} : cmul(lam, cconj(hp));
                 const Cx w = cmul(cconj(at), ga);
                 const bool live = j < g.nvalid;
-                const float radial = live ? -(ln[j].nu * tok[i].e) * w.r : 0.0f;
+                const float radial = live ? -(x2 * kLn2) * w.r : 0.0f;
                 const float phase = live ? w.i : 0.0f;
                 rsum += radial;
                 psum += phase;
-                acc_nu[j] += radial;
-                acc_th[j] += ln[j].th * phase;
+                acc[2 * j] += radial;
+                acc[2 * j + 1] += phase;
                 obr.v[j] = lam.r;
                 obi.v[j] = lam.i;
                 carry[j] = cmul(cconj(at), lam);
@@ -486,12 +513,26 @@ void samu_bwd_kernel(SamuBwdArgs x) {
                 store_vec<C::DT, ALIGNED>(pgbr, off, g.nvalid, obr);
                 store_vec<C::DT, ALIGNED>(pgbi, off, g.nvalid, obi);
             }
-            rsum = row_sum<TPR>(rsum);
-            psum = row_sum<TPR>(psum);
-            if (cg == 0) {
-                const size_t tp = (size_t)lb * x.tokens + (size_t)g.bi * d.T + row;
-                x.tok_eta[tp] = rsum;
-                x.tok_delta[tp] = psum;
+            tsum_[2 * i] = rsum;
+            tsum_[2 * i + 1] = psum;
+        }
+    }
+    // per-token partials over the row group's TPR lanes; value index 2i is
+    // row i's radial sum, 2i + 1 its phase sum
+    {
+        constexpr int NV = 2 * NR;
+        constexpr int KT = NV >= TPR ? NV / TPR : 1;
+        constexpr int SP = NV >= TPR ? 1 : TPR / NV;
+        tsum<NV, TPR / 2, 1>(tsum_, cg);
+        if (cg % SP == 0) {
+#pragma unroll
+            for (int q = 0; q < KT; ++q) {
+                const int idx = q + KT * (cg / SP);
+                const int row = g.row0 + idx / 2;
+                if (row < d.T) {
+                    const size_t tp = (size_t)lb * x.tokens + (size_t)g.bi * d.T + row;
+                    ((idx & 1) ? x.tok_delta : x.tok_eta)[tp] = tsum_[q];
+                }
             }
         }
     }
@@ -503,14 +544,19 @@ void samu_bwd_kernel(SamuBwdArgs x) {
                 x.p.gh0i[(size_t)g.bi * d.D + g.d0 + j] = carry[j].i;
             }
     }
-    // per-mode partials of this tile: over the row groups, then the waves
+    // per-mode partials of this tile: over the RG row groups, then over the
+    // waves; value index 2j of acc is lane j's radial sum, 2j + 1 its phase sum
+    {
+        constexpr int NV = 2 * V;
+        constexpr int KM = NV >= RG ? NV / RG : 1;
+        constexpr int SP = NV >= RG ? 1 : RG / NV;
+        tsum<NV, kWave / 2, TPR>(acc, l);
+        if (rg % SP == 0) {
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-        const float nu = col_sum<TPR>(acc_nu[j]);
-        const float th = col_sum<TPR>(acc_th[j]);
-        if (rg == 0) {
-            s_acc[0][wave][cg * V + j] = nu;
-            s_acc[1][wave][cg * V + j] = th;
+            for (int q = 0; q < KM; ++q) {
+                const int idx = q + KM * (rg / SP);
+                s_acc[idx & 1][wave][cg * V + idx / 2] = acc[q];
+            }
         }
     }
     __syncthreads();
@@ -525,37 +571,52 @@ void samu_bwd_kernel(SamuBwdArgs x) {
             }
             const size_t mp = ((size_t)g.k * (d.nS / d.nW) + g.bi) * d.D + dl;
             x.mode_nu[mp] = nu;
-            x.mode_theta[mp] = th;
+            x.mode_theta[mp] = th * x.mode_tab[dl].y;  // d/dtheta_log = theta d/dtheta
         }
     }
 }
 
-// grad_eta / grad_delta: sum of a token's nW lane-block partials in order;
-// grad_nu_log / grad_theta_log: sum of a mode's NK*B tile partials in order.
-__global__ void samu_reduce_kernel(const float* __restrict__ tok_eta,
-                                   const float* __restrict__ tok_delta,
-                                   const float* __restrict__ mode_nu,
-                                   const float* __restrict__ mode_theta, float* grad_eta,
-                                   float* grad_delta, float* grad_nu_log, float* grad_theta_log,
-                                   int64_t tokens, int nW, int64_t tiles, int64_t M) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < tokens) {
-        float e = 0.0f, dl = 0.0f;
-        for (int w = 0; w < nW; ++w) {
-            e += tok_eta[(int64_t)w * tokens + i];
-            dl += tok_delta[(int64_t)w * tokens + i];
+// The second pass: dst[i] = sum_k src[k n + i] over k < count, for two arrays
+// at once.  A workgroup covers 64 consecutive i; its four wavefronts take the
+// k of one residue mod 4 each, in increasing order, and the four partial sums
+// are added in wavefront order: a fixed order, so results are deterministic.
+struct SumJob {
+    const float *src0, *src1;
+    float *dst0, *dst1;
+    int64_t n, count;
+};
+constexpr int kSumLanes = 64;
+constexpr int kSumSlices = 4;
+
+__global__ __launch_bounds__(kSumLanes* kSumSlices) void samu_reduce_kernel(SumJob a, SumJob b,
+                                                                            unsigned blocks_a) {
+    __shared__ float s_part[2][kSumSlices][kSumLanes];
+    const bool first = blockIdx.x < blocks_a;
+    const SumJob& j = first ? a : b;
+    const int64_t blk = first ? blockIdx.x : blockIdx.x - blocks_a;
+    const int lane = threadIdx.x % kSumLanes;
+    const int slice = threadIdx.x / kSumLanes;
+    const int64_t i = blk * kSumLanes + lane;
+    float s0 = 0.0f, s1 = 0.0f;
+    if (i < j.n) {
+#pragma unroll 4
+        for (int64_t k = slice; k < j.count; k += kSumSlices) {
+            s0 += j.src0[k * j.n + i];
+            s1 += j.src1[k * j.n + i];
         }
-        if (grad_eta) grad_eta[i] = e;
-        if (grad_delta) grad_delta[i] = dl;
     }
-    if (i < M) {
-        float n = 0.0f, t = 0.0f;
-        for (int64_t k = 0; k < tiles; ++k) {
-            n += mode_nu[k * M + i];
-            t += mode_theta[k * M + i];
+    s_part[0][slice][lane] = s0;
+    s_part[1][slice][lane] = s1;
+    __syncthreads();
+    if (slice == 0 && i < j.n) {
+        float t0 = s_part[0][0][lane], t1 = s_part[1][0][lane];
+#pragma unroll
+        for (int q = 1; q < kSumSlices; ++q) {
+            t0 += s_part[0][q][lane];
+            t1 += s_part[1][q][lane];
         }
-        if (grad_nu_log) grad_nu_log[i] = n;
-        if (grad_theta_log) grad_theta_log[i] = t;
+        if (j.dst0) j.dst0[i] = t0;
+        if (j.dst1) j.dst1[i] = t1;
     }
 }
 
@@ -567,10 +628,24 @@ void dispatch2(bool al, bool rst, F&& f) {
     else f(std::false_type{}, std::false_type{});
 }
 
+// Tile shapes of the two directions: Cfg<type, threads of 16 bytes per row,
+// rows per thread, wavefronts, look-back window>.  256 rows of 128-byte rows
+// per array: measured on MI355X (bf16 B8 T2048 M2560) against 128 rows and
+// 256-byte rows (8 or 4 rows per thread, 4 or 8 wavefronts), this shape was
+// the fastest in both directions; the tile's fixed costs (ticket, look-back,
+// barriers) dominate smaller tiles, whose bytes per tile are fewer than the
+// real scan's because the transitions are not read.
 template <int DT>
-using SamuCfg = Cfg<DT, kComplexWidth, 4, 4, 4>;  // 128 rows, as the complex form
+using SamuFwdCfg = Cfg<DT, 8, 8, 4, 4>;
+template <int DT>
+using SamuBwdCfg = Cfg<DT, 8, 8, 4, 4>;
 
-Layout samu_layout(const Shape& s) { return layout_of(s, kComplexWidth, kComplexTile); }
+Layout samu_fwd_layout(const Shape& s) {
+    return layout_of(s, SamuFwdCfg<DT_F32>::TPR, SamuFwdCfg<DT_F32>::CT);
+}
+Layout samu_bwd_layout(const Shape& s) {
+    return layout_of(s, SamuBwdCfg<DT_F32>::TPR, SamuBwdCfg<DT_F32>::CT);
+}
 
 // The auxiliary buffer: the mode table [M] and token table [B*T] (float4
 // each), then, for the backward, the partial sums.
@@ -579,7 +654,7 @@ struct AuxLayout {
 };
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 AuxLayout aux_layout(const Shape& s) {
-    const Layout L = samu_layout(s);
+    const Layout L = samu_bwd_layout(s);
     const size_t tokens = (size_t)s.B * s.T;
     AuxLayout a;
     a.mode = 0;
@@ -606,8 +681,8 @@ hipError_t samu_factors(const Shape& s, const void* eta, const void* delta, cons
 template <int DT>
 hipError_t samu_fwd_t(const Shape& s, const SamuFwdPtrs& p, void* ws, size_t ws_bytes, bool init,
                       void* auxp, int polls, hipStream_t st) {
-    using C = SamuCfg<DT>;
-    const Layout L = samu_layout(s);
+    using C = SamuFwdCfg<DT>;
+    const Layout L = samu_fwd_layout(s);
     char* aux = static_cast<char*>(auxp);
     const AuxLayout a = aux_layout(s);
     SamuFwdArgs x;
@@ -635,8 +710,8 @@ hipError_t samu_fwd_t(const Shape& s, const SamuFwdPtrs& p, void* ws, size_t ws_
 template <int DT>
 hipError_t samu_bwd_t(const Shape& s, const SamuBwdPtrs& p, void* ws, size_t ws_bytes, bool init,
                       void* auxp, int polls, hipStream_t st) {
-    using C = SamuCfg<DT>;
-    const Layout L = samu_layout(s);
+    using C = SamuBwdCfg<DT>;
+    const Layout L = samu_bwd_layout(s);
     char* aux = static_cast<char*>(auxp);
     const AuxLayout a = aux_layout(s);
     SamuBwdArgs x;
@@ -664,20 +739,40 @@ hipError_t samu_bwd_t(const Shape& s, const SamuBwdPtrs& p, void* ws, size_t ws_
     });
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t n = std::max<int64_t>((int64_t)tokens, s.D);
-    hipLaunchKernelGGL(samu_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       x.tok_eta, x.tok_delta, x.mode_nu, x.mode_theta, p.grad_eta, p.grad_delta,
-                       p.grad_nu_log, p.grad_theta_log, (int64_t)tokens, L.nW,
-                       (int64_t)L.NK * s.B, s.D);
+    // grad_eta / grad_delta: a token's nW lane-block partials; grad_nu_log /
+    // grad_theta_log: a mode's NK*B tile partials
+    const SumJob jt{x.tok_eta, x.tok_delta, p.grad_eta, p.grad_delta, (int64_t)tokens,
+                    (int64_t)L.nW};
+    const SumJob jm{x.mode_nu, x.mode_theta, p.grad_nu_log, p.grad_theta_log, s.D,
+                    (int64_t)L.NK * s.B};
+    const unsigned bt = (unsigned)((tokens + kSumLanes - 1) / kSumLanes);
+    const unsigned bm = (unsigned)((s.D + kSumLanes - 1) / kSumLanes);
+    hipLaunchKernelGGL(samu_reduce_kernel, dim3(bt + bm), dim3(kSumLanes * kSumSlices), 0, st, jt,
+                       jm, bt);
     return hipGetLastError();
 }
 
 }  // namespace
 
-bool samu_supported(const Shape& s) { return complex_fused_supported(s); }
+// The index limits of the tiled form (32-bit tile offsets, ticket and series
+// counts) for one direction's tile shape.
+bool samu_layout_ok(const Shape& s, int tile, const Layout& L) {
+    const int64_t eb = s.dtype == DT_F32 ? 4 : 2;
+    if ((int64_t)(tile + 1) * s.D * eb >= ((int64_t)1 << 31)) return false;
+    if (s.T >= ((int64_t)1 << 31) - tile || s.D >= ((int64_t)1 << 30)) return false;
+    if ((unsigned long long)L.NK * L.nS >= 0xffffffffull) return false;
+    if (s.B * (int64_t)L.nW >= ((int64_t)1 << 31)) return false;
+    return true;
+}
+
+bool samu_supported(const Shape& s) {
+    return samu_layout_ok(s, SamuFwdCfg<DT_F32>::CT, samu_fwd_layout(s)) &&
+           samu_layout_ok(s, SamuBwdCfg<DT_F32>::CT, samu_bwd_layout(s));
+}
 
 size_t samu_scratch_bytes(const Shape& s) {
-    return kHeaderBytes + 2 * region_bytes_for(samu_layout(s), kComplexWords);
+    return kHeaderBytes + 2 * std::max(region_bytes_for(samu_fwd_layout(s), kComplexWords),
+                                       region_bytes_for(samu_bwd_layout(s), kComplexWords));
 }
 
 size_t samu_aux_bytes(const Shape& s) { return aux_layout(s).total; }
