@@ -162,8 +162,8 @@ LRSCAN_API int scan_step(const void* a, const void* b, const float* state_in,
  *   lambda_t = grad_out_t + conj(a_{t+1}) * lambda_{t+1},
  *   grad_b_t = lambda_t,  grad_a_t = lambda_t * conj(h_{t-1}),
  *   grad_h0 = conj(a_0) * lambda_0.
- * opts: algo AUTO, FUSED (one tile shape: width 8, 128 rows; chunk and width
- * must be 0 or those) or SEQ (CHUNKED returns LRSCAN_ERR_ALGO); workspace,
+ * opts: algo AUTO, FUSED (the library's tile shapes: chunk and width must be
+ * 0, else LRSCAN_ERR_CHUNK) or SEQ (CHUNKED returns LRSCAN_ERR_ALGO); workspace,
  * polls and reset as for the real scan; opts->h0 and opts->grad_h0 are not
  * used (the states are the explicit arguments).
  * ------------------------------------------------------------------------ */

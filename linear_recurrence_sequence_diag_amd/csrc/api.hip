@@ -178,12 +178,12 @@ int hip_status(hipError_t e) { return e == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_H
 
 bool pair_ok(const void* re, const void* im) { return (re == nullptr) == (im == nullptr); }
 
-// AUTO -> FUSED; FUSED accepts only its one tile shape; CHUNKED is not provided.
+// AUTO -> FUSED; FUSED takes the library's tile shapes (chunk and width 0);
+// CHUNKED is not provided.
 int complex_algo(const lrscan_opts* o, int* algo) {
     const int a = o ? o->algo : LRSCAN_ALGO_AUTO;
     if (a == LRSCAN_ALGO_AUTO || a == LRSCAN_ALGO_FUSED) {
-        const int c = o ? o->chunk : 0, w = o ? o->width : 0;
-        if ((c != 0 && c != kComplexTile) || (w != 0 && w != kComplexWidth)) return LRSCAN_ERR_CHUNK;
+        if (o && (o->chunk != 0 || o->width != 0)) return LRSCAN_ERR_CHUNK;
         *algo = LRSCAN_ALGO_FUSED;
         return LRSCAN_OK;
     }

@@ -583,8 +583,22 @@ void dispatch2(bool al, bool rst, F&& f) {
     else f(std::false_type{}, std::false_type{});
 }
 
+// Tile shapes of the two directions: Cfg<type, threads of 16 bytes per row,
+// rows per thread, wavefronts, look-back window>.  128 rows of 128-byte rows
+// per array; measured on MI355X (bf16 B8 T2048 M2560), 256-row tiles (8 rows
+// per thread, or 8 wavefronts) were no faster forward and 14-17% slower
+// backward, where six arrays of 8 rows no longer fit in registers.
 template <int DT>
-using CxCfg = Cfg<DT, kComplexWidth, 4, 4, 4>;  // 128 rows: 4 waves x 8 row groups x 4 rows
+using CxFwdCfg = Cfg<DT, 8, 4, 4, 4>;
+template <int DT>
+using CxBwdCfg = Cfg<DT, 8, 4, 4, 4>;
+
+Layout cx_fwd_layout(const Shape& s) {
+    return layout_of(s, CxFwdCfg<DT_F32>::TPR, CxFwdCfg<DT_F32>::CT);
+}
+Layout cx_bwd_layout(const Shape& s) {
+    return layout_of(s, CxBwdCfg<DT_F32>::TPR, CxBwdCfg<DT_F32>::CT);
+}
 
 bool fwd_aligned(const Shape& s, const CxFwdPtrs& p) {
     const void* ptrs[6] = {p.ar, p.ai, p.br, p.bi, p.out_r, p.out_i};
@@ -620,8 +634,8 @@ hipError_t cx_seq_bwd_t(const Shape& s, const CxBwdPtrs& p, hipStream_t st) {
 template <int DT>
 hipError_t cx_fused_fwd_t(const Shape& s, const CxFwdPtrs& p, void* ws, size_t ws_bytes, bool init,
                           int polls, hipStream_t st) {
-    using C = CxCfg<DT>;
-    const Layout L = layout_of(s, kComplexWidth, kComplexTile);
+    using C = CxFwdCfg<DT>;
+    const Layout L = cx_fwd_layout(s);
     CxFwdArgs x;
     x.p = p;
     hipError_t e = prepare(ws, ws_bytes, init, L, kComplexWords, st, &x.sc);
@@ -641,8 +655,8 @@ hipError_t cx_fused_fwd_t(const Shape& s, const CxFwdPtrs& p, void* ws, size_t w
 template <int DT>
 hipError_t cx_fused_bwd_t(const Shape& s, const CxBwdPtrs& p, void* ws, size_t ws_bytes, bool init,
                           int polls, hipStream_t st) {
-    using C = CxCfg<DT>;
-    const Layout L = layout_of(s, kComplexWidth, kComplexTile);
+    using C = CxBwdCfg<DT>;
+    const Layout L = cx_bwd_layout(s);
     CxBwdArgs x;
     x.p = p;
     hipError_t e = prepare(ws, ws_bytes, init, L, kComplexWords, st, &x.sc);
@@ -668,19 +682,13 @@ hipError_t launch_complex_seq_bwd(const Shape& s, const CxBwdPtrs& p, hipStream_
 }
 
 bool complex_fused_supported(const Shape& s) {
-    // the same index limits as the real fused form at its (8, 128) shape
-    const int64_t eb = s.dtype == DT_F32 ? 4 : 2;
-    if ((int64_t)(kComplexTile + 1) * s.D * eb >= ((int64_t)1 << 31)) return false;
-    if (s.T >= ((int64_t)1 << 31) - kComplexTile || s.D >= ((int64_t)1 << 30)) return false;
-    const Layout L = layout_of(s, kComplexWidth, kComplexTile);
-    if ((unsigned long long)L.NK * L.nS >= 0xffffffffull) return false;
-    if (s.B * (int64_t)L.nW >= ((int64_t)1 << 31)) return false;
-    return true;
+    return tiled_layout_ok(s, CxFwdCfg<DT_F32>::CT, cx_fwd_layout(s)) &&
+           tiled_layout_ok(s, CxBwdCfg<DT_F32>::CT, cx_bwd_layout(s));
 }
 
 size_t complex_fused_workspace_bytes(const Shape& s) {
-    return kHeaderBytes +
-           2 * region_bytes_for(layout_of(s, kComplexWidth, kComplexTile), kComplexWords);
+    return kHeaderBytes + 2 * std::max(region_bytes_for(cx_fwd_layout(s), kComplexWords),
+                                       region_bytes_for(cx_bwd_layout(s), kComplexWords));
 }
 
 hipError_t launch_complex_fused_fwd(const Shape& s, const CxFwdPtrs& p, void* ws, size_t ws_bytes,

@@ -92,10 +92,8 @@ struct CxBwdPtrs {
 };
 hipError_t launch_complex_seq_fwd(const Shape& s, const CxFwdPtrs& p, hipStream_t st);
 hipError_t launch_complex_seq_bwd(const Shape& s, const CxBwdPtrs& p, hipStream_t st);
-// The fused complex form has one tile shape (8 threads of 16 bytes per row
-// of each array, 128 rows); its workspace follows the fused conventions.
-constexpr int kComplexWidth = 8;
-constexpr int kComplexTile = 128;
+// The fused complex form has fixed tile shapes per direction; its workspace
+// follows the fused conventions.
 bool complex_fused_supported(const Shape& s);
 size_t complex_fused_workspace_bytes(const Shape& s);
 hipError_t launch_complex_fused_fwd(const Shape& s, const CxFwdPtrs& p, void* ws, size_t ws_bytes,

@@ -754,20 +754,9 @@ hipError_t samu_bwd_t(const Shape& s, const SamuBwdPtrs& p, void* ws, size_t ws_
 
 }  // namespace
 
-// The index limits of the tiled form (32-bit tile offsets, ticket and series
-// counts) for one direction's tile shape.
-bool samu_layout_ok(const Shape& s, int tile, const Layout& L) {
-    const int64_t eb = s.dtype == DT_F32 ? 4 : 2;
-    if ((int64_t)(tile + 1) * s.D * eb >= ((int64_t)1 << 31)) return false;
-    if (s.T >= ((int64_t)1 << 31) - tile || s.D >= ((int64_t)1 << 30)) return false;
-    if ((unsigned long long)L.NK * L.nS >= 0xffffffffull) return false;
-    if (s.B * (int64_t)L.nW >= ((int64_t)1 << 31)) return false;
-    return true;
-}
-
 bool samu_supported(const Shape& s) {
-    return samu_layout_ok(s, SamuFwdCfg<DT_F32>::CT, samu_fwd_layout(s)) &&
-           samu_layout_ok(s, SamuBwdCfg<DT_F32>::CT, samu_bwd_layout(s));
+    return tiled_layout_ok(s, SamuFwdCfg<DT_F32>::CT, samu_fwd_layout(s)) &&
+           tiled_layout_ok(s, SamuBwdCfg<DT_F32>::CT, samu_bwd_layout(s));
 }
 
 size_t samu_scratch_bytes(const Shape& s) {
