@@ -9,7 +9,11 @@ inputs are generated (seeded) and copied to HBM before the timed region.
 
 Prints one JSON line.  `value` is the effective HBM bandwidth of the whole
 step: the algorithmic bytes (forward 3*s*N + 4*B*D, backward 5*s*N, s the I/O
-element size, N = B*T*D) divided by the measured step time.
+element size, N = B*T*D) divided by the measured step time (K steps back to
+back).  Beside it: per-launch median and minimum, a "cold" step time with the
+Infinity Cache flushed before each step, the achievable streaming ceiling of a
+1 GiB device copy, the dominant kernel's roofline, and the fp64 oracle's rate
+on the host (all cores and one core).
 """
 from __future__ import annotations
 
@@ -97,7 +101,21 @@ def cpu_baseline(inp, budget_s=10.0):
         reps += 1
         if t_total >= budget_s or reps >= 200:
             break
+    # one pass on a single core beside it
+    t0 = time.perf_counter()
+    h, _ = oracle.scan_fwd(a, b, threads=1)
+    oracle.scan_bwd(a, h, g, threads=1)
+    t_one = time.perf_counter() - t0
     fb, bb = algorithmic_bytes(wl.B, wl.T, wl.D, wl.itemsize)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round((fb + bb) * reps / t_total / 1e9, 3),
         "unit": "GB/s",
@@ -106,6 +124,9 @@ def cpu_baseline(inp, budget_s=10.0):
         "sample": f"the whole {wl.name} workload, fwd+bwd, {reps} pass(es) in {t_total:.1f} s "
                   f"(fp64, {cores} threads over lanes; input conversion untimed)",
         "elements_per_s": round(wl.N * reps / t_total, 1),
+        "single_core": {"value": round((fb + bb) / t_one / 1e9, 3), "unit": "GB/s",
+                        "sample": f"one fwd+bwd pass in {t_one:.1f} s on 1 thread"},
+        "host": {"cpu_model": model, "hardware_threads": os.cpu_count()},
     }
 
 
@@ -441,6 +462,38 @@ def main():
     fwd_ms = kernel_ms(fwd)
     bwd_ms = kernel_ms(bwd)
 
+    # each launch timed on its own (median and min over K), and whole steps
+    # with the Infinity Cache flushed before each ("cold": a 1 GiB read between
+    # steps, outside the timed events; a read leaves clean lines, so the step
+    # pays no write-back of the flush)
+    def per_launch(fn, flush=None):
+        ts = []
+        for _ in range(args.steps):
+            if flush is not None:
+                flush()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        return ts[len(ts) // 2], ts[0]
+
+    scrub = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
+    scrub_sum = torch.empty((), device="cuda", dtype=torch.float32)
+    fwd_med, fwd_min = per_launch(fwd)
+    bwd_med, bwd_min = per_launch(bwd)
+    cold_med, cold_min = per_launch(lambda: (fwd(), bwd()),
+                                    flush=lambda: torch.sum(scrub, dim=0, out=scrub_sum))
+    # achievable streaming ceiling: a 1 GiB device copy (read + write), the
+    # runtime's copy kernel, larger than the Infinity Cache
+    src_c = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
+    copy_ms = min(kernel_ms(lambda: scrub.copy_(src_c)) for _ in range(2))
+    copy_gbps = 2 * src_c.numel() * 4 / (copy_ms * 1e-3) / 1e9
+    del scrub, scrub_sum, src_c
+
     fb, bb = algorithmic_bytes(B, T, D, wl.itemsize)
     value = (fb + bb) / (ms_per_step * 1e-3) / 1e9
     fwd_algo, fwd_chunk, fwd_width = lr.scan_auto_algo(B, T, D, dt, 0)
@@ -486,6 +539,13 @@ def main():
         "elements_per_s": round(wl.N / (ms_per_step * 1e-3), 1),
         "fwd_us": round(fwd_ms * 1e3, 2),
         "bwd_us": round(bwd_ms * 1e3, 2),
+        "per_launch_us": {"fwd_median": round(fwd_med * 1e3, 2), "fwd_min": round(fwd_min * 1e3, 2),
+                          "bwd_median": round(bwd_med * 1e3, 2), "bwd_min": round(bwd_min * 1e3, 2)},
+        "cold": {"ms_per_step_median": round(cold_med, 5), "ms_per_step_min": round(cold_min, 5),
+                 "value": round((fb + bb) / (cold_med * 1e-3) / 1e9, 2),
+                 "note": "1 GiB read before each step, outside the timed events"},
+        "ceiling": {"kernel": "device copy of 1 GiB (read + write)",
+                    "GB/s": round(copy_gbps, 1), "value_frac": round(value / copy_gbps, 4)},
         "roofline": {
             "bound": "hbm",
             "kernel": f"{dom} scan ({names[bwd_algo if dom == 'backward' else fwd_algo]})",
