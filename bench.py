@@ -52,18 +52,27 @@ def algorithmic_bytes(B, T, D, s):
     return 3 * s * N + 4 * B * D, 5 * s * N
 
 
-def kernel_sources_sha256():
-    """Hash of the fused kernels' sources: counter readings are only valid for them."""
+# The sources each family of tiled kernels is built from: counter readings are
+# only valid for the sources they were taken on.
+KERNEL_SOURCES = {
+    "real": ("fused.hip", "fused_common.hpp", "device.hpp"),
+    "complex": ("complex.hip", "complex_math.hpp", "fused_common.hpp", "device.hpp"),
+    "samu": ("samu.hip", "complex_math.hpp", "fused_common.hpp", "device.hpp"),
+}
+
+
+def kernel_sources_sha256(family="real"):
+    """Hash of one kernel family's sources."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_recurrence_sequence_diag_amd", "csrc")
-    for f in ("fused.hip", "fused_common.hpp", "device.hpp"):
+    for f in KERNEL_SOURCES[family]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload, direction, algo):
+def measured_traffic(workload, direction, algo, family="real"):
     """HBM bytes per launch of the dominant kernel from the rocprofv3 counter
     runs recorded in profiles/hbm_traffic.json (FETCH_SIZE and WRITE_SIZE in
     KiB per dispatch, each scaled by what the counter reads for a plain copy of
@@ -74,14 +83,35 @@ def measured_traffic(workload, direction, algo):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256") != kernel_sources_sha256():
+    w = rec.get("workloads", {}).get(workload, {})
+    if w.get("source_sha256", rec.get("source_sha256")) != kernel_sources_sha256(family):
         return None
-    e = rec.get("workloads", {}).get(workload, {}).get(direction)
+    e = w.get(direction)
     if not e:
         return None
     cf = rec["copy_factor"]
     kib = e["fetch_kib"] * cf["FETCH_SIZE"] + e["write_kib"] * cf["WRITE_SIZE"]
     return round(kib * 1024)
+
+
+def roofline(kernel, nbytes, ms, traffic=None):
+    """The dominant kernel's HBM roofline entry: algorithmic bytes per launch
+    over its average launch interval, against MI355X's 8 TB/s."""
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic}
+
+
+def timed_sample(fn, budget_s):
+    """Run fn() repeatedly for about budget_s; returns (passes, seconds)."""
+    reps, t_total = 0, 0.0
+    while True:
+        t0 = time.perf_counter()
+        fn()
+        t_total += time.perf_counter() - t0
+        reps += 1
+        if t_total >= budget_s or reps >= 200:
+            return reps, t_total
 
 
 def cpu_baseline(inp, budget_s=10.0):
@@ -202,7 +232,38 @@ def complex_line(args, wl, lr, torch, W):
             kms = a0.elapsed_time(a1) / args.steps
             res[f"{name}_us"] = round(kms * 1e3, 2)
             res[f"{name}_GBps"] = round(nb / (kms * 1e-3) / 1e9, 1)
+        res["roofline"] = roofline("complex backward scan (fused)", 10 * s * N,
+                                   res["bwd_us"] * 1e-3,
+                                   measured_traffic(wl.name, "backward", "fused", "complex"))
+    else:
+        res["roofline"] = roofline("complex state-only forward (fused)", nbytes, ms,
+                                   measured_traffic(wl.name, "forward", "fused", "complex"))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = complex_cpu_baseline(inp, args.mode)
     return res
+
+
+def complex_cpu_baseline(inp, mode, budget_s=8.0):
+    """The fp64 complex oracle (one host thread) on batch row 0 of the
+    workload, fwd+bwd (or the forward alone for prefill), scaled to GB/s with
+    the same algorithmic bytes per element."""
+    import oracle
+
+    wl = inp.workload
+    lanes = [(0, m) for m in range(wl.D)]
+    a, b, g = inp.c128("a", lanes), inp.c128("b", lanes), inp.c128("g", lanes)
+    s, N1 = wl.itemsize, wl.T * wl.D
+
+    def run():
+        h, _ = oracle.complex_fwd(a, b)
+        if mode != "prefill":
+            oracle.complex_bwd(a, h, g)
+    reps, t = timed_sample(run, budget_s)
+    nb = (4 * s * N1 + 8 * wl.D) if mode == "prefill" else (6 * s * N1 + 8 * wl.D + 10 * s * N1)
+    return {"value": round(nb * reps / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch row 0 of {wl.name} ([1, {wl.T}, {wl.D}]), "
+                      f"{'forward' if mode == 'prefill' else 'fwd+bwd'}, {reps} pass(es) in {t:.1f} s "
+                      f"(fp64 C99 complex, one thread; input conversion untimed)"}
 
 
 def samu_line(args, wl, lr, torch, W):
@@ -290,10 +351,45 @@ def samu_line(args, wl, lr, torch, W):
             kms = a0.elapsed_time(a1) / args.steps
             res[f"{name}_us"] = round(kms * 1e3, 2)
             res[f"{name}_GBps"] = round(nb / (kms * 1e-3) / 1e9, 1)
+        # the backward call is three launches (factor tables, the tiled
+        # kernel, the fixed-order reduction); its interval is charged whole
+        res["roofline"] = roofline("fused-transition backward call (fused)", bwd_bytes,
+                                   res["bwd_us"] * 1e-3,
+                                   measured_traffic(wl.name, "backward", "fused", "samu"))
+    else:
+        res["roofline"] = roofline("fused-transition state-only forward call (fused)", nbytes, ms,
+                                   measured_traffic(wl.name, "forward", "fused", "samu"))
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = samu_cpu_baseline(inp, args.mode)
     return res
 
 
-def inference_line(args, wl, lr, torch, a, b, dt):
+def samu_cpu_baseline(inp, mode, budget_s=8.0):
+    """The fp64 fused-transition oracle (one host thread) on batch row 0,
+    fwd+bwd (or the forward alone for prefill), in the same GB/s."""
+    import oracle
+
+    wl = inp.workload
+    rows = [0]
+    eta, delta, nu_log, theta_log = inp.controls(rows)
+    b, g = inp.c128("b", rows), inp.c128("g", rows)
+    s, N1, T, M = wl.itemsize, wl.T * wl.D, wl.T, wl.D
+
+    def run():
+        h, _ = oracle.samu_fwd(eta, delta, nu_log, theta_log, b)
+        if mode != "prefill":
+            oracle.samu_bwd(eta, delta, nu_log, theta_log, h, g)
+    reps, t = timed_sample(run, budget_s)
+    ctl = 2 * s * T + 8 * M
+    nb = (2 * s * N1 + 8 * M + ctl) if mode == "prefill" else (
+        4 * s * N1 + 8 * M + ctl + 6 * s * N1 + ctl + 8 * T + 8 * M)
+    return {"value": round(nb * reps / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch row 0 of {wl.name} ([1, {T}, {M}]), "
+                      f"{'forward' if mode == 'prefill' else 'fwd+bwd'}, {reps} pass(es) in {t:.1f} s "
+                      f"(fp64 C99 complex, one thread; input conversion untimed)"}
+
+
+def inference_line(args, wl, lr, torch, a, b, dt, inp=None):
     """JSON line of the state-only forward (prefill) or of the decode step."""
     B, T, D = wl.B, wl.T, wl.D
     s = wl.itemsize
@@ -341,7 +437,34 @@ def inference_line(args, wl, lr, torch, a, b, dt):
                    "mode": unit_note},
         "us_per_call": round(ms * 1e3, 2),
         "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": roofline("state-only forward (fused)" if args.mode == "prefill"
+                             else "decode step (one launch; launch-latency bound at this size)",
+                             nbytes, ms),
+        **({"cpu_baseline": inference_cpu_baseline(inp, args.mode)}
+           if inp is not None and not args.no_cpu_baseline else {}),
     }
+
+
+def inference_cpu_baseline(inp, mode, budget_s=8.0):
+    """The fp64 oracle beside the inference modes: the forward over the whole
+    workload (prefill), or one time step on the [B, D] lanes from a carried
+    state (decode), in the same GB/s."""
+    import oracle
+
+    wl = inp.workload
+    cores = min(16, len(os.sched_getaffinity(0)))
+    s, B, T, D = wl.itemsize, wl.B, wl.T, wl.D
+    if mode == "prefill":
+        a, b = inp.f64("a"), inp.f64("b")
+        reps, t = timed_sample(lambda: oracle.scan_fwd(a, b, threads=cores), budget_s)
+        nb, what = 2 * s * B * T * D + 4 * B * D, f"the whole {wl.name} forward"
+    else:
+        a, b = inp.f64("a")[:, T // 2:T // 2 + 1], inp.f64("b")[:, T // 2:T // 2 + 1]
+        state = np.zeros((B, D))
+        reps, t = timed_sample(lambda: oracle.scan_fwd(a, b, h0=state, threads=cores), budget_s / 4)
+        nb, what = (3 * s + 8) * B * D, f"one {wl.name} time step on [B, D] lanes"
+    return {"value": round(nb * reps / t / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what}, {reps} pass(es) in {t:.1f} s (fp64, {cores} threads over lanes)"}
 
 
 def main():
@@ -412,7 +535,7 @@ def main():
     a, b, g = dev(inp.a), dev(inp.b), dev(inp.g)
     B, T, D = wl.B, wl.T, wl.D
     if args.mode != "train":
-        print(json.dumps(inference_line(args, wl, lr, torch, a, b, dt)), flush=True)
+        print(json.dumps(inference_line(args, wl, lr, torch, a, b, dt, inp)), flush=True)
         return
     out = torch.empty_like(a)
     ga = torch.empty_like(a)
