@@ -495,8 +495,10 @@ void samu_bwd_kernel(SamuBwdArgs x) {
                                 x.p.h0i[(size_t)g.bi * d.D + g.d0 + j]};
                 }
                 const bool rs = RST && ((rbits >> i) & 1u);
-                const Cx ga = rs ? Cx{0.0f, 0.0f} : cmul(lam, cconj(hp));
-                const Cx w = cmul(cconj(at), ga);
+                // w = conj(a) grad_a = conj(a) lambda conj(h_{t-1}): the new
+                // carry conj(a) lambda times conj(h_{t-1}), one product fewer
+                carry[j] = cmul(cconj(at), lam);
+                const Cx w = rs ? Cx{0.0f, 0.0f} : cmul(carry[j], cconj(hp));
                 const bool live = j < g.nvalid;
                 const float radial = live ? -(x2 * kLn2) * w.r : 0.0f;
                 const float phase = live ? w.i : 0.0f;
@@ -506,7 +508,6 @@ void samu_bwd_kernel(SamuBwdArgs x) {
                 acc[2 * j + 1] += phase;
                 obr.v[j] = lam.r;
                 obi.v[j] = lam.i;
-                carry[j] = cmul(cconj(at), lam);
             }
             if (g.nvalid > 0) {
                 const uint32_t off = row_off(g, row, d.T, rowbytes);

@@ -87,7 +87,7 @@ def state_pair(B, M, seed):
     return (z.real.astype(np.float32) + 1j * z.imag.astype(np.float32))
 
 
-SHAPES = [(2, 300, 72), (3, 1000, 130), (1, 4096, 256), (2, 333, 13)]
+SHAPES = [(2, 300, 72), (3, 1000, 130), (1, 4096, 256), (2, 333, 13), (1, 1, 1), (2, 129, 1)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
