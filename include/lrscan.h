@@ -63,7 +63,9 @@ enum {
 
 /* algorithms */
 enum {
-    LRSCAN_ALGO_AUTO = 0,    /* the library picks (measured crossover) */
+    LRSCAN_ALGO_AUTO = 0,    /* the library picks: FUSED with a measured tile shape, or CHUNKED
+                                (complex scan: SEQ) where a tile would exceed the fused form's
+                                32-bit in-tile offsets (rows of hundreds of MB) */
     LRSCAN_ALGO_SEQ = 1,     /* one thread walks all T steps of its lanes */
     LRSCAN_ALGO_CHUNKED = 2, /* three launches: chunk summary, chunk prefix, chunk replay */
     LRSCAN_ALGO_FUSED = 3    /* one launch: tile summary, look-back prefix, replay from registers */

@@ -114,9 +114,20 @@ Resolved resolve(const Shape& s, int dir, const lrscan_opts* o, bool aligned) {
     r.chunk = o ? o->chunk : 0;
     r.width = o ? o->width : 0;
     if (r.algo == LRSCAN_ALGO_AUTO) {
-        r.algo = LRSCAN_ALGO_FUSED;
-        r.chunk = 0;
-        r.width = 0;
+        int w = 0, t = 0;
+        fused_default_cfg(s, dir, aligned, &w, &t);
+        if (fused_cfg_supported(s, dir, w, t, aligned)) {
+            r.algo = LRSCAN_ALGO_FUSED;
+            r.width = w;
+            r.chunk = t;
+        } else {
+            // past the tiled form's 32-bit in-tile offsets (a tile of rows of
+            // more than about 2 GB / tile bytes): the three-launch form
+            r.algo = LRSCAN_ALGO_CHUNKED;
+            r.chunk = kDefaultChunk;
+            r.width = 0;
+        }
+        return r;
     }
     if (r.algo == LRSCAN_ALGO_CHUNKED && r.chunk == 0) r.chunk = kDefaultChunk;
     if (r.algo == LRSCAN_ALGO_FUSED && (r.chunk == 0 || r.width == 0)) {
@@ -178,13 +189,14 @@ int hip_status(hipError_t e) { return e == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_H
 
 bool pair_ok(const void* re, const void* im) { return (re == nullptr) == (im == nullptr); }
 
-// AUTO -> FUSED; FUSED takes the library's tile shapes (chunk and width 0);
-// CHUNKED is not provided.
-int complex_algo(const lrscan_opts* o, int* algo) {
+// AUTO -> FUSED, or SEQ past the tiled form's index limits; FUSED takes the
+// library's tile shapes (chunk and width 0); CHUNKED is not provided.
+int complex_algo(const Shape& s, const lrscan_opts* o, int* algo) {
     const int a = o ? o->algo : LRSCAN_ALGO_AUTO;
     if (a == LRSCAN_ALGO_AUTO || a == LRSCAN_ALGO_FUSED) {
         if (o && (o->chunk != 0 || o->width != 0)) return LRSCAN_ERR_CHUNK;
-        *algo = LRSCAN_ALGO_FUSED;
+        *algo = (a == LRSCAN_ALGO_AUTO && !complex_fused_supported(s)) ? LRSCAN_ALGO_SEQ
+                                                                         : LRSCAN_ALGO_FUSED;
         return LRSCAN_OK;
     }
     if (a == LRSCAN_ALGO_SEQ) {
@@ -412,9 +424,9 @@ LRSCAN_API int scan_complex_fwd(const void* ar, const void* ai, const void* br, 
     if (!dims_ok(B, T, M)) return LRSCAN_ERR_DIM;
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
     int algo = 0;
-    int st = complex_algo(opts, &algo);
-    if (st != LRSCAN_OK) return st;
     const Shape s{B, T, M, dtype};
+    int st = complex_algo(s, opts, &algo);
+    if (st != LRSCAN_OK) return st;
     const CxFwdPtrs p{ar, ai, br, bi, out_r, out_i, last_r, last_i, h0_r, h0_i,
                       opts ? opts->reset : nullptr};
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -443,9 +455,9 @@ LRSCAN_API int scan_complex_bwd(const void* ar, const void* ai, const void* out_
     if (!dims_ok(B, T, M)) return LRSCAN_ERR_DIM;
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
     int algo = 0;
-    int st = complex_algo(opts, &algo);
-    if (st != LRSCAN_OK) return st;
     const Shape s{B, T, M, dtype};
+    int st = complex_algo(s, opts, &algo);
+    if (st != LRSCAN_OK) return st;
     const CxBwdPtrs p{ar, ai, out_r, out_i, grad_out_r, grad_out_i, grad_last_r, grad_last_i,
                       h0_r, h0_i, opts ? opts->reset : nullptr, grad_ar, grad_ai, grad_br,
                       grad_bi, grad_h0_r, grad_h0_i};
@@ -463,8 +475,8 @@ LRSCAN_API size_t scan_complex_workspace_bytes(int64_t B, int64_t T, int64_t M, 
                                                const lrscan_opts* opts) {
     if (!dims_ok(B, T, M) || !dtype_ok(dtype)) return 0;
     int algo = 0;
-    if (complex_algo(opts, &algo) != LRSCAN_OK || algo != LRSCAN_ALGO_FUSED) return 0;
     const Shape s{B, T, M, dtype};
+    if (complex_algo(s, opts, &algo) != LRSCAN_OK || algo != LRSCAN_ALGO_FUSED) return 0;
     return complex_fused_supported(s) ? complex_fused_workspace_bytes(s) : 0;
 }
 

@@ -1,0 +1,73 @@
+"""Extreme shapes against the fp64 oracle: one very long chain (a single lane
+block walking about a million steps, so every tile's look-back waits on the
+one before it), a single time step across four million lanes, and the
+complex and fused-transition forms on long single-lane chains.  Transitions
+are drawn in U(0.5, 0.99) so that no lane's memory spans the whole chain."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from _gpu import log
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import linear_recurrence_sequence_diag_amd as lr  # noqa: E402
+from test_gpu_parity import check_against_oracle, run_pair  # noqa: E402
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lr.library()
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,D", [(1, (1 << 20) + 3, 1), (1, (1 << 18) + 7, 8), (2, 100003, 3)],
+                         ids=["T1M_D1", "T256k_D8", "B2_T100k_D3"])
+@pytest.mark.parametrize("algo,chunk", [("auto", 0), ("chunked", 1024), ("seq", 0)],
+                         ids=["auto", "chunked1024", "seq"])
+def test_long_single_chain(B, T, D, dt, algo, chunk):
+    inp = W.random_inputs(B, T, D, dt, seed=51, a_lo=0.5, a_hi=0.99)
+    res = run_pair(inp, algo, chunk, chunk)
+    check_against_oracle(inp, res)
+    log(f"{algo} {dt} B{B} T{T} D{D}: within tolerance")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("algo,chunk", [("auto", 0), ("chunked", 16), ("seq", 0)],
+                         ids=["auto", "chunked16", "seq"])
+def test_single_step_many_lanes(dt, algo, chunk):
+    inp = W.random_inputs(1, 1, (1 << 22) + 5, dt, seed=52, a_lo=0.5, a_hi=0.99)
+    res = run_pair(inp, algo, chunk, chunk)
+    check_against_oracle(inp, res)
+    # one step from a zero state: out = b exactly, grad_b = grad_out exactly
+    assert torch.equal(res[0], torch.from_numpy(np.ascontiguousarray(inp.b).view(
+        np.int16 if dt == "bf16" else np.float32)).cuda().view(res[0].dtype))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_complex_long_single_lane(dt):
+    from test_gpu_complex import check_c, check_c_grad_a, chost, cprev, run
+    inp = W.complex_inputs(1, (1 << 18) + 5, 1, dt, seed=53, r_lo=0.5, r_hi=0.99, theta=np.pi)
+    a, b, g = inp.c128("a"), inp.c128("b"), inp.c128("g")
+    h, hl = oracle.complex_fwd(a, b)
+    oga, ogb, _ = oracle.complex_bwd(a, h, g)
+    for algo in ("fused", "seq"):
+        res = run(inp, algo, need_grad_h0=False)
+        check_c(f"{algo} out", chost(res[0], res[1]), h, dt)
+        check_c(f"{algo} grad_b", chost(res[6], res[7]), ogb, dt)
+        check_c_grad_a(chost(res[4], res[5]), oga, ogb, cprev(h, None), dt)
+    log(f"complex {dt} T{(1 << 18) + 5} M1: within tolerance")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_fused_transition_long_single_lane(dt):
+    from test_gpu_samu import Bounds, check_all, run
+    inp = W.samu_inputs(1, (1 << 17) + 5, 1, dt, seed=54)
+    eta, delta, nu_log, theta_log = inp.controls()
+    bd = Bounds(eta, delta, nu_log, theta_log, inp.c128("b"), inp.c128("g"), dt)
+    check_all(f"samu {dt} long", run(inp, need_grad_h0=False), bd)
+    log(f"fused-transition {dt} T{(1 << 17) + 5} M1: within the derived bounds")
