@@ -43,6 +43,11 @@ def test_single_step_many_lanes(dt, algo, chunk):
     inp = W.random_inputs(1, 1, (1 << 22) + 5, dt, seed=52, a_lo=0.5, a_hi=0.99)
     res = run_pair(inp, algo, chunk, chunk)
     check_against_oracle(inp, res)
+    rng = np.random.default_rng(55)
+    h0 = rng.standard_normal((1, (1 << 22) + 5)).astype(np.float32)
+    gl = rng.standard_normal((1, (1 << 22) + 5)).astype(np.float32)
+    check_against_oracle(inp, run_pair(inp, algo, chunk, chunk, h0=h0, gl=gl), h0=h0, gl=gl)
+    res = run_pair(inp, algo, chunk, chunk)
     # one step from a zero state: out = b exactly, grad_b = grad_out exactly
     assert torch.equal(res[0], torch.from_numpy(np.ascontiguousarray(inp.b).view(
         np.int16 if dt == "bf16" else np.float32)).cuda().view(res[0].dtype))
@@ -71,3 +76,40 @@ def test_fused_transition_long_single_lane(dt):
     bd = Bounds(eta, delta, nu_log, theta_log, inp.c128("b"), inp.c128("g"), dt)
     check_all(f"samu {dt} long", run(inp, need_grad_h0=False), bd)
     log(f"fused-transition {dt} T{(1 << 17) + 5} M1: within the derived bounds")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,D", [(100000, 3, 1), (4099, 5, 9), (1, 2, (1 << 21) + 1)],
+                         ids=["B100k_T3_D1", "B4099_T5_D9", "T2_D2M"])
+def test_many_short_series(B, T, D, dt):
+    """Very many series of a few steps (one tile per series, tens of thousands
+    of ticket holders per counter), and a two-step scan over two million lanes."""
+    inp = W.random_inputs(B, T, D, dt, seed=56, a_lo=0.5, a_hi=0.99)
+    for algo, chunk in (("auto", 0), ("chunked", 16)):
+        check_against_oracle(inp, run_pair(inp, algo, chunk, chunk))
+    log(f"{dt} B{B} T{T} D{D}: within tolerance")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_complex_many_short_series(dt):
+    from test_gpu_complex import check_c, chost, run
+    inp = W.complex_inputs(30000, 3, 3, dt, seed=57, r_lo=0.5, r_hi=0.99, theta=np.pi)
+    a, b, g = inp.c128("a"), inp.c128("b"), inp.c128("g")
+    h, _ = oracle.complex_fwd(a, b)
+    _, ogb, _ = oracle.complex_bwd(a, h, g)
+    for algo in ("fused", "seq"):
+        res = run(inp, algo, need_grad_h0=False)
+        check_c(f"{algo} out", chost(res[0], res[1]), h, dt)
+        check_c(f"{algo} grad_b", chost(res[6], res[7]), ogb, dt)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,M", [(2, 1, (1 << 20) + 3), (20000, 2, 3)], ids=["T1_M1M", "B20k_T2_M3"])
+def test_fused_transition_wide_and_many(B, T, M, dt):
+    """Many modes in one step (per-mode partials over a single tile row) and
+    many short series (per-token partials over a single lane block)."""
+    from test_gpu_samu import Bounds, check_all, run
+    inp = W.samu_inputs(B, T, M, dt, seed=58)
+    eta, delta, nu_log, theta_log = inp.controls()
+    bd = Bounds(eta, delta, nu_log, theta_log, inp.c128("b"), inp.c128("g"), dt)
+    check_all(f"samu {dt} B{B} T{T} M{M}", run(inp, need_grad_h0=False), bd)
