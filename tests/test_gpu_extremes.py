@@ -113,3 +113,79 @@ def test_fused_transition_wide_and_many(B, T, M, dt):
     eta, delta, nu_log, theta_log = inp.controls()
     bd = Bounds(eta, delta, nu_log, theta_log, inp.c128("b"), inp.c128("g"), dt)
     check_all(f"samu {dt} B{B} T{T} M{M}", run(inp, need_grad_h0=False), bd)
+
+
+def offset_copy(t, elems=1):
+    """The same values in a buffer whose data pointer is `elems` elements past
+    a 16-byte boundary (a contiguous view with a storage offset)."""
+    buf = torch.empty(t.numel() + elems, dtype=t.dtype, device=t.device)
+    v = buf[elems:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("algo,chunk,width", [("auto", 0, 0), ("fused", 256, 8), ("chunked", 64, 0),
+                                              ("seq", 0, 0)],
+                         ids=["auto", "fused256w8", "chunked64", "seq"])
+def test_misaligned_pointers_with_aligned_rows(dt, algo, chunk, width):
+    """D a multiple of the vector width but every array starting one element
+    past a 16-byte boundary: the element-wise paths, through the raw C ABI
+    (inputs and outputs misaligned)."""
+    from _gpu import dev, host
+    B, T, D = 2, 777, 128
+    inp = W.random_inputs(B, T, D, dt, seed=59, a_lo=0.5, a_hi=0.99)
+    a, b, g = (offset_copy(dev(x, dt)) for x in (inp.a, inp.b, inp.g))
+    out, ga, gb = (offset_copy(torch.zeros_like(a)) for _ in range(3))
+    last = torch.empty((B, D), device="cuda", dtype=torch.float32)
+    assert a.data_ptr() % 16 != 0 and out.data_ptr() % 16 != 0
+    code = lr.F32 if dt == "f32" else lr.BF16
+    st = torch.cuda.current_stream().cuda_stream
+    o = lr.make_opts(algo=algo, chunk=chunk, width=width)
+    lr.scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), last.data_ptr(), B, T, D, code, st, o)
+    lr.scan_bwd_ex(a.data_ptr(), out.data_ptr(), g.data_ptr(), None, ga.data_ptr(), gb.data_ptr(),
+                   B, T, D, code, st, o)
+    torch.cuda.synchronize()
+    from _gpu import check_close, check_grad_a, prev_state
+    h, hl = oracle.scan_fwd(inp.f64("a"), inp.f64("b"))
+    oga, ogb, _ = oracle.scan_bwd(inp.f64("a"), h, inp.f64("g"))
+    check_close("out", host(out), h, dt)
+    check_close("last", host(last), hl, "f32")
+    check_close("grad_b", host(gb), ogb, dt)
+    check_grad_a(host(ga), oga, ogb, prev_state(h), dt)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_misaligned_pointers_complex_and_fused_transition(dt):
+    """The complex and fused-transition forms on inputs that start one element
+    past a 16-byte boundary (their outputs are allocated aligned)."""
+    from _gpu import dev, dev_f32, host
+    from test_gpu_complex import check_c, chost
+    B, T, M = 2, 600, 64
+    c = W.complex_inputs(B, T, M, dt, seed=60, r_lo=0.5, r_hi=0.99, theta=np.pi)
+    t = {n: offset_copy(dev(getattr(c, n), dt)) for n in ("ar", "ai", "br", "bi", "gr", "gi")}
+    o = lr.complex_scan(t["ar"], t["ai"], t["br"], t["bi"])
+    g = lr.complex_scan_backward(t["ar"], t["ai"], offset_copy(o[0]), offset_copy(o[1]),
+                                 t["gr"], t["gi"])
+    torch.cuda.synchronize()
+    a, b, gg = c.c128("a"), c.c128("b"), c.c128("g")
+    h, _ = oracle.complex_fwd(a, b)
+    _, ogb, _ = oracle.complex_bwd(a, h, gg)
+    check_c("complex out", chost(o[0], o[1]), h, dt)
+    check_c("complex grad_b", chost(g[2], g[3]), ogb, dt)
+
+    from test_gpu_samu import Bounds, check
+    from _gpu import TOL
+    s = W.samu_inputs(B, T, M, dt, seed=61)
+    ts = {n: offset_copy(dev(getattr(s, n), dt)) for n in ("eta", "delta", "br", "bi", "gr", "gi")}
+    nl, tl = offset_copy(dev_f32(s.nu_log)), offset_copy(dev_f32(s.theta_log))
+    ctl = (ts["eta"], ts["delta"], nl, tl)
+    so = lr.samu_scan(*ctl, ts["br"], ts["bi"])
+    sg = lr.samu_scan_backward(*ctl, offset_copy(so[0]), offset_copy(so[1]), ts["gr"], ts["gi"])
+    torch.cuda.synchronize()
+    eta, delta, nu_log, theta_log = s.controls()
+    bd = Bounds(eta, delta, nu_log, theta_log, s.c128("b"), s.c128("g"), dt)
+    rtol, atol = TOL[dt]
+    check("samu out", host(so[0]) + 1j * host(so[1]), bd.h, atol + rtol * np.abs(bd.h) + bd.E_h)
+    check("samu grad_eta", host(sg[0]), bd.ge, bd.tol_ge)
+    check("samu grad_nu_log", host(sg[2]), bd.gn, bd.tol_gn)
