@@ -1,0 +1,102 @@
+"""The single-launch forms under HIP graph capture and on concurrent streams.
+
+Graphs: fused forward + backward captured on a stream whose library
+workspace is already set up, replayed several times with eager calls on the
+same stream (and so the same workspace) in between; every replay must equal
+the eager result bit for bit (the workspace cleans itself on the device, so
+replays need no initialisation step and capture no memset).
+
+Streams: two streams run different scans at the same time, each on its own
+library workspace; the results equal those of the same calls made alone."""
+import numpy as np
+import pytest
+
+import workloads as W
+from _gpu import dev, dev_f32, log
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import linear_recurrence_sequence_diag_amd as lr  # noqa: E402
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    lr.library()
+
+
+def real_step(a, b, g):
+    out, last = lr.scan(a, b)
+    ga, gb, _ = lr.scan_backward(a, out, g)
+    return [out, last, ga, gb]
+
+
+def samu_step(t):
+    ctl = (t["eta"], t["delta"], t["nu_log"], t["theta_log"])
+    o = lr.samu_scan(*ctl, t["br"], t["bi"])
+    gr = lr.samu_scan_backward(*ctl, o[0], o[1], t["gr"], t["gi"])
+    return list(o) + list(gr[:6])
+
+
+def samu_tensors(s):
+    dt = s.workload.dtype
+    t = {n: dev(getattr(s, n), dt) for n in ("eta", "delta", "br", "bi", "gr", "gi")}
+    t["nu_log"], t["theta_log"] = dev_f32(s.nu_log), dev_f32(s.theta_log)
+    return t
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_graph_replays_equal_eager(dt):
+    r = W.random_inputs(2, 3000, 256, dt, seed=71, a_lo=0.5, a_hi=0.99)
+    a, b, g = dev(r.a, dt), dev(r.b, dt), dev(r.g, dt)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        ref = [x.clone() for x in real_step(a, b, g)]   # also sets up this stream's workspace
+        sm = samu_tensors(W.samu_inputs(2, 700, 64, dt, seed=72))
+        sref = [x.clone() for x in samu_step(sm)]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        res = real_step(a, b, g)
+        sres = samu_step(sm)
+    for rep in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, (x, y) in enumerate(zip(res, ref)):
+            assert torch.equal(x, y), f"replay {rep}: real output {k} differs from eager"
+        for k, (x, y) in enumerate(zip(sres, sref)):
+            assert torch.equal(x, y), f"replay {rep}: fused-transition output {k} differs from eager"
+        with torch.cuda.stream(st):   # eager work on the same workspace between replays
+            again = real_step(a, b, g)
+        torch.cuda.synchronize()
+        assert all(torch.equal(x, y) for x, y in zip(again, ref)), f"eager call after replay {rep}"
+    log(f"graph {dt}: 4 replays bitwise equal to eager")
+
+
+def test_concurrent_streams_equal_solo():
+    r1 = W.random_inputs(4, 2048, 1024, "bf16", seed=73, a_lo=0.5, a_hi=0.99)
+    r2 = W.random_inputs(1, 20000, 512, "f32", seed=74, a_lo=0.5, a_hi=0.99)
+    x1 = [dev(v, "bf16") for v in (r1.a, r1.b, r1.g)]
+    x2 = [dev(v, "f32") for v in (r2.a, r2.b, r2.g)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        solo1 = [t.clone() for t in real_step(*x1)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s2):
+        solo2 = [t.clone() for t in real_step(*x2)]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        outs1, outs2 = [], []
+        for _ in range(3):   # interleave launches on the two streams
+            with torch.cuda.stream(s1):
+                outs1.append(real_step(*x1))
+            with torch.cuda.stream(s2):
+                outs2.append(real_step(*x2))
+        torch.cuda.synchronize()
+        for o in outs1:
+            assert all(torch.equal(x, y) for x, y in zip(o, solo1)), "stream 1 differs"
+        for o in outs2:
+            assert all(torch.equal(x, y) for x, y in zip(o, solo2)), "stream 2 differs"
+    log("two concurrent streams: bitwise equal to solo runs")
