@@ -100,3 +100,37 @@ def test_concurrent_streams_equal_solo():
         for o in outs2:
             assert all(torch.equal(x, y) for x, y in zip(o, solo2)), "stream 2 differs"
     log("two concurrent streams: bitwise equal to solo runs")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_captured_decode_loop(dt):
+    """Sixteen decode steps captured in one graph (state updated in place,
+    one token's a and b per step) replay to the eager chain bit for bit, and
+    the last state equals the state-only forward over the same tokens."""
+    B, T, D = 4, 16, 1000
+    r = W.random_inputs(B, T, D, dt, seed=75, a_lo=0.5, a_hi=0.99)
+    a, b = dev(r.a, dt), dev(r.b, dt)
+    at = [a[:, t].contiguous() for t in range(T)]
+    bt = [b[:, t].contiguous() for t in range(T)]
+    st = torch.cuda.Stream()
+    state = torch.zeros((B, D), device="cuda", dtype=torch.float32)
+    with torch.cuda.stream(st):
+        eager = []
+        for t in range(T):
+            o, _ = lr.step(at[t], bt[t], state=state, out_state=state)
+            eager.append(o.clone())
+        eager_state = state.clone()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    gstate = torch.zeros((B, D), device="cuda", dtype=torch.float32)
+    with torch.cuda.graph(graph, stream=st):
+        outs = [lr.step(at[t], bt[t], state=gstate, out_state=gstate)[0] for t in range(T)]
+    for rep in range(3):
+        gstate.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(x, y) for x, y in zip(outs, eager)), f"replay {rep} outputs"
+        assert torch.equal(gstate, eager_state), f"replay {rep} state"
+    _, last = lr.scan(a, b, algo="seq")
+    torch.cuda.synchronize()
+    assert torch.equal(last, eager_state)
