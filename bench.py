@@ -410,9 +410,9 @@ def inference_line(args, wl, lr, torch, a, b, dt, inp=None):
         state = torch.zeros((B, D), device="cuda", dtype=torch.float32)
         out = torch.empty_like(at)
 
-        def fn():
+        def fn(on=sh):
             lr.scan_step(at.data_ptr(), bt.data_ptr(), state.data_ptr(), None, out.data_ptr(),
-                         state.data_ptr(), B, D, dt, sh)
+                         state.data_ptr(), B, D, dt, on)
         nbytes = (3 * s + 8) * B * D
         unit_note = "one decode step: reads a, b and the fp32 state, writes out and the state"
     for _ in range(args.warmup):
@@ -436,6 +436,8 @@ def inference_line(args, wl, lr, torch, a, b, dt, inp=None):
         "config": {"workload": f"{wl.name}: {WORKLOAD_TEXT[wl.name]}", "B": B, "T": T, "D": D,
                    "mode": unit_note},
         "us_per_call": round(ms * 1e3, 2),
+        **({"graph_us_per_step": round(graph_decode_us(torch, fn, stream, args.steps), 2)}
+           if args.mode == "decode" else {}),
         "pct_of_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": roofline("state-only forward (fused)" if args.mode == "prefill"
                              else "decode step (one launch; launch-latency bound at this size)",
@@ -443,6 +445,30 @@ def inference_line(args, wl, lr, torch, a, b, dt, inp=None):
         **({"cpu_baseline": inference_cpu_baseline(inp, args.mode)}
            if inp is not None and not args.no_cpu_baseline else {}),
     }
+
+
+def graph_decode_us(torch, fn, stream, steps):
+    """Per-step time of `steps` decode steps captured in one HIP graph and
+    replayed (the launch interval of eager back-to-back calls removed);
+    fn(stream_handle) enqueues one step."""
+    s = torch.cuda.Stream()
+    s.wait_stream(stream)
+    fn(s.cuda_stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(steps):
+            fn(s.cuda_stream)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(5):
+        g.replay()
+    e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (5 * steps)
 
 
 def inference_cpu_baseline(inp, mode, budget_s=8.0):
