@@ -236,8 +236,8 @@ def complex_line(args, wl, lr, torch, W):
                                    res["bwd_us"] * 1e-3,
                                    measured_traffic(wl.name, "backward", "fused", "complex"))
     else:
-        res["roofline"] = roofline("complex state-only forward (fused)", nbytes, ms,
-                                   measured_traffic(wl.name, "forward", "fused", "complex"))
+        # no counter run covers the state-only kernel (it stores only `last`)
+        res["roofline"] = roofline("complex state-only forward (fused)", nbytes, ms)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = complex_cpu_baseline(inp, args.mode)
     return res
@@ -357,8 +357,7 @@ def samu_line(args, wl, lr, torch, W):
                                    res["bwd_us"] * 1e-3,
                                    measured_traffic(wl.name, "backward", "fused", "samu"))
     else:
-        res["roofline"] = roofline("fused-transition state-only forward call (fused)", nbytes, ms,
-                                   measured_traffic(wl.name, "forward", "fused", "samu"))
+        res["roofline"] = roofline("fused-transition state-only forward call (fused)", nbytes, ms)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = samu_cpu_baseline(inp, args.mode)
     return res

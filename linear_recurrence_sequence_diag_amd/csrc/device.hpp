@@ -52,7 +52,9 @@ struct Elem<DT_F32> {
     __device__ static float load1(const void* base, size_t i) {
         return reinterpret_cast<const float*>(base)[i];
     }
-    __device__ static void store1(void* base, size_t i, float x) { reinterpret_cast<float*>(base)[i] = x; }
+    __device__ static void store1(void* base, size_t i, float x) {
+        __builtin_nontemporal_store(x, reinterpret_cast<float*>(base) + i);
+    }
 };
 
 template <>
@@ -64,7 +66,7 @@ struct Elem<DT_BF16> {
         return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[i]);
     }
     __device__ static void store1(void* base, size_t i, float x) {
-        reinterpret_cast<uint16_t*>(base)[i] = f32_to_bf16_bits(x);
+        __builtin_nontemporal_store(f32_to_bf16_bits(x), reinterpret_cast<uint16_t*>(base) + i);
     }
 };
 
@@ -100,6 +102,17 @@ struct RowVec {
         return r;
     }
 };
+
+// Outputs are written once and read by later launches only, so every output
+// store is non-temporal: it does not displace data this launch still reads
+// from the caches, and leaves fewer dirty lines for the end-of-launch
+// write-back.  (Measured on MI355X: the backward on [8,2048,2560] bf16 went
+// from 94 to 78 us; every other form gained 0-14%.)
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16_nt(void* p, uint4 v) {
+    const u32x4_nt w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_nt*>(p));
+}
 
 // Output staging: V floats rounded into the storage type and written as one vector.
 template <int DT>
@@ -150,7 +163,7 @@ __device__ __forceinline__ RowVec<DT> load_row(const void* base, size_t off, int
 template <int DT, bool ALIGNED>
 __device__ __forceinline__ void store_row(void* base, size_t off, int nvalid, const RowOut<DT>& o) {
     if constexpr (ALIGNED) {
-        *reinterpret_cast<uint4*>(reinterpret_cast<char*>(base) + off * Elem<DT>::bytes) = o.pack();
+        store16_nt(reinterpret_cast<char*>(base) + off * Elem<DT>::bytes, o.pack());
     } else {
 #pragma unroll
         for (int j = 0; j < RowOut<DT>::V; ++j)
@@ -177,7 +190,7 @@ template <int DT, bool ALIGNED>
 __device__ __forceinline__ void store_vec(char* row, uint32_t lane_off, int nvalid,
                                           const RowOut<DT>& o) {
     if constexpr (ALIGNED) {
-        *reinterpret_cast<uint4*>(row + lane_off) = o.pack();
+        store16_nt(row + lane_off, o.pack());
     } else {
         store_row<DT, false>(row + lane_off, 0, nvalid, o);
     }
