@@ -204,6 +204,23 @@ __device__ __forceinline__ void opaque(RowVec<DT>& r) {
     asm volatile("" : "+v"(r.w.x), "+v"(r.w.y), "+v"(r.w.z), "+v"(r.w.w));
 }
 
+// Zero that the compiler cannot see through and that depends on a row loaded
+// into registers: loads addressed with it are issued after that row arrived.
+template <int DT>
+__device__ __forceinline__ int zero_after_row(const RowVec<DT>& r) {
+    int z;
+    asm volatile("" : "=v"(z) : "0"(0), "v"(r.w.x));
+    return z;
+}
+
+// Zero that the compiler cannot see through and that depends on `v`: an
+// address offset by it cannot be formed, nor its load issued, before `v` is.
+__device__ __forceinline__ int zero_after(float v) {
+    int z;
+    asm volatile("" : "=v"(z) : "0"(0), "v"(v));
+    return z;
+}
+
 template <typename T>
 __device__ __forceinline__ T uniform(T x) {
     return __builtin_amdgcn_readfirstlane(x);

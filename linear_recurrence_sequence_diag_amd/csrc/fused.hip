@@ -23,7 +23,10 @@
 //    ("Single-pass Parallel Prefix Scan with Decoupled Look-back", 2016),
 //    made deterministic: every H equals the plain chained value
 //    H_k = fma(P_k, H_{k-1}, Q_k) whatever the timing, so results do not
-//    depend on scheduling.  A tile only waits on tiles with smaller tickets,
+//    depend on scheduling.  The nearest predecessor's words are read once
+//    already before the summary barrier (as soon as the tile's own rows have
+//    arrived), so a tile whose predecessor has published by then needs no
+//    further round trip.  A tile only waits on tiles with smaller tickets,
 //    which are already resident or finished, so the chain always drains; and
 //    a tile that has polled long enough derives the maps it is missing from
 //    the inputs itself (bitwise the values their owners publish), so no wait
@@ -248,6 +251,10 @@ void fused_fwd_kernel(FwdArgs x) {
             m[j].q = fmaf(at, m[j].q, bt);
         }
     }
+    const uint32_t phase = tk.phase;
+    const unsigned long long* pqs =
+        reinterpret_cast<const unsigned long long*>(x.sc.region[phase] + x.sc.ctr_words);
+    const uint32_t* hs = x.sc.region[phase] + x.sc.ctr_words + 2 * x.sc.entries;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         const Aff inc = wave_scan_up<TPR>(m[j]);
@@ -263,15 +270,20 @@ void fused_fwd_kernel(FwdArgs x) {
         opaque(ra[i]);
         opaque(rb[i]);
     }
+    // early reading of the look-back window, issued once this thread's rows
+    // have arrived (the summary above consumed them)
+    EarlyWindow<RealLink, C::EW> early;
+    if (tid < W) {
+        int z = 0;
+#pragma unroll
+        for (int j = 0; j < V; ++j) z += zero_after(m[j].q);
+        early.template take<-1>(RealLink{hs, pqs, d.nS, g.s, W, tid + z}, g.k, d.NK);
+    }
     __syncthreads();
-    const uint32_t phase = tk.phase;
 
     // tile map, publication, look-back: one column per thread
     if (tid < W) {
         const int c = tid;
-        const unsigned long long* pqs =
-            reinterpret_cast<const unsigned long long*>(x.sc.region[phase] + x.sc.ctr_words);
-        const uint32_t* hs = x.sc.region[phase] + x.sc.ctr_words + 2 * x.sc.entries;
         Aff A = aff_identity();
 #pragma unroll
         for (int w = 0; w < WAVES; ++w) A = aff_then(A, s_wtot[w][c]);
@@ -281,8 +293,10 @@ void fused_fwd_kernel(FwdArgs x) {
         const int dl = g.dcol0 + c;
         const float base0 = (x.h0 && dl < d.D) ? x.h0[(size_t)g.bi * d.D + dl] : 0.0f;
         const RealLink lk{hs, pqs, d.nS, g.s, W, c};
-        const float hin = look_back<RealLink, -1, C::LB>(
-            lk, g.k, d.NK, base0, x.polls, [&](int j) { return fwd_tile_map<C>(x, j, g.bi, dl); });
+        float hin;
+        if (!early.template resolve<-1>(g.k, d.NK, base0, &hin))
+            hin = look_back<RealLink, -1, C::LB>(
+                lk, g.k, d.NK, base0, x.polls, [&](int j) { return fwd_tile_map<C>(x, j, g.bi, dl); });
         if (more) publish_u32(const_cast<uint32_t*>(hs) + o, publishable(aff_apply(A, hin)));
         s_hin[c] = hin;
     }
@@ -399,6 +413,10 @@ void fused_bwd_kernel(BwdArgs x) {
             m[j].q = at * (m[j].q + gt);
         }
     }
+    const uint32_t phase = tk.phase;
+    const unsigned long long* pqs =
+        reinterpret_cast<const unsigned long long*>(x.sc.region[phase] + x.sc.ctr_words);
+    const uint32_t* hs = x.sc.region[phase] + x.sc.ctr_words + 2 * x.sc.entries;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         const Aff inc = wave_scan_down<TPR>(m[j]);
@@ -414,14 +432,17 @@ void fused_bwd_kernel(BwdArgs x) {
         opaque(ra[i]);
         opaque(rg_[i]);
     }
+    EarlyWindow<RealLink, C::EW> early;
+    if (tid < W) {
+        int z = 0;
+#pragma unroll
+        for (int j = 0; j < V; ++j) z += zero_after(m[j].q);
+        early.template take<+1>(RealLink{hs, pqs, d.nS, g.s, W, tid + z}, g.k, d.NK);
+    }
     __syncthreads();
-    const uint32_t phase = tk.phase;
 
     if (tid < W) {
         const int c = tid;
-        const unsigned long long* pqs =
-            reinterpret_cast<const unsigned long long*>(x.sc.region[phase] + x.sc.ctr_words);
-        const uint32_t* hs = x.sc.region[phase] + x.sc.ctr_words + 2 * x.sc.entries;
         Aff A = aff_identity();
 #pragma unroll
         for (int w = WAVES - 1; w >= 0; --w) A = aff_then(A, s_wtot[w][c]);
@@ -431,8 +452,10 @@ void fused_bwd_kernel(BwdArgs x) {
         const int dl = g.dcol0 + c;
         const float base0 = (x.grad_last && dl < d.D) ? x.grad_last[(size_t)g.bi * d.D + dl] : 0.0f;
         const RealLink lk{hs, pqs, d.nS, g.s, W, c};
-        const float cin = look_back<RealLink, +1, C::LB>(
-            lk, g.k, d.NK, base0, x.polls, [&](int j) { return bwd_tile_map<C>(x, j, g.bi, dl); });
+        float cin;
+        if (!early.template resolve<+1>(g.k, d.NK, base0, &cin))
+            cin = look_back<RealLink, +1, C::LB>(
+                lk, g.k, d.NK, base0, x.polls, [&](int j) { return bwd_tile_map<C>(x, j, g.bi, dl); });
         if (more) publish_u32(const_cast<uint32_t*>(hs) + o, publishable(aff_apply(A, cin)));
         s_cin[c] = cin;
     }
@@ -578,20 +601,23 @@ bool fused_cfg_supported(const Shape& s, int dir, int width, int tile, bool alig
 }
 
 // Default tile shape, from measurements on MI355X (bf16 [8,2048,2560] and
-// [16,4096,2560], fp32 [4,8192,4096], bf16 [1,131072,1024]): 256-byte rows
-// when there are enough lane blocks to keep every tile chain short (bf16 with
-// at least 128 such blocks), else 128-byte rows, which give long single-batch
-// sequences 4x as many chains.  fp32 was fastest with 128-byte rows.
+// [16,4096,2560], fp32 [4,8192,4096], bf16 [1,131072,1024]).  Forward:
+// 128-byte rows of 256 steps everywhere (with the early look-back reading,
+// wider rows were no faster, and slower on [8,2048,2560]).  Backward:
+// 256-byte rows of 128 steps when there are enough lane blocks to keep every
+// tile chain short (bf16 with at least 128 such blocks), else 128-byte rows,
+// which give long single-batch sequences 4x as many chains; fp32 was fastest
+// with 128-byte rows.
 void fused_default_cfg(const Shape& s, int dir, bool aligned, int* width, int* tile) {
     *width = 8;
     *tile = 256;
-    if (!aligned) return;
+    if (!aligned || dir == 0) return;
     if (s.dtype == DT_BF16) {
         const int64_t lanes16 = 16 * Elem<DT_BF16>::V;
         const int64_t blocks16 = s.B * ((s.D + lanes16 - 1) / lanes16);
         if (blocks16 >= 128) {
             *width = 16;
-            *tile = dir == 0 ? 256 : 128;
+            *tile = 128;
         }
     }
 }

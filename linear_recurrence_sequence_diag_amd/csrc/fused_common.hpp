@@ -91,6 +91,7 @@ struct Cfg {
     static constexpr int W = TPR * V;
     static constexpr int NT = WAVES * kWave;
     static constexpr int CT = WAVES * RG * NR;
+    static constexpr int EW = 1;  // predecessors the look-back reads early (measured: 1 beats 2 and 4)
     static_assert(TPR == 8 || TPR == 16 || TPR == 32, "row width");
     static_assert(W <= NT, "one look-back column per thread");
     // waves per SIMD the register budget is held to (the forward keeps two
@@ -218,6 +219,85 @@ __device__ __forceinline__ int wave_max_active(int v) {
 // a single atomic load per word), says whether they are published
 // (ready_h / ready_m), decodes them (state / map) and applies a map to a
 // state; it fixes the value types (real or complex).
+// One reading of N predecessors' words (index 0 the nearest), `rem` of which
+// exist before the chain start: the depth of the nearest published state (its
+// value in *base) or of the chain start (base0), N + 1 when every map of the
+// window is published and neither lies within it, or -1 when a map is missing
+// first.
+template <class Link, int N>
+__device__ __forceinline__ int scan_window(const typename Link::HRaw (&hw)[N],
+                                           const typename Link::MRaw (&mw)[N], int rem,
+                                           typename Link::S base0, typename Link::S* base) {
+    int depth = -1;
+    bool stop = false;
+    *base = base0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if (depth < 0 && !stop) {
+            if (i >= rem) {
+                depth = i;  // reached the start of the chain
+            } else if (Link::ready_h(hw[i])) {
+                depth = i;
+                *base = Link::state(hw[i]);
+            } else if (!Link::ready_m(mw[i])) {
+                stop = true;
+            }
+        }
+    }
+    if (depth < 0 && !stop) depth = rem == N ? N : N + 1;  // chain start just past the window
+    return depth;
+}
+
+// Carry from one reading of the N nearest predecessors' words (index 0 the
+// nearest): the nearest published inclusive state, with the maps of the tiles
+// in between applied to it oldest first, or the chain start when it lies
+// within reach and every map up to it is published.  False if the reading
+// does not decide the carry yet.
+template <class Link, int N>
+__device__ __forceinline__ bool resolve_window(const typename Link::HRaw (&hw)[N],
+                                               const typename Link::MRaw (&mw)[N], int span,
+                                               typename Link::S base0, typename Link::S* out) {
+    using S = typename Link::S;
+    S base;
+    const int depth = scan_window<Link, N>(hw, mw, span, base0, &base);
+    if (depth < 0 || depth > N) return false;
+    S x = base;
+#pragma unroll
+    for (int i = N - 1; i >= 0; --i)
+        if (i < depth) x = Link::apply(Link::map(mw[i]), x);
+    *out = x;
+    return true;
+}
+
+// An early reading of the N nearest predecessors' words, taken while the
+// tile's own summary is still being combined, so that the look-back can
+// often finish without a further round trip.
+template <class Link, int N>
+struct EarlyWindow {
+    typename Link::HRaw hw[N];
+    typename Link::MRaw mw[N];
+    template <int DIR>
+    __device__ __forceinline__ void take(const Link& lk, int k, int NK) {
+        const int span = DIR < 0 ? k : (NK - 1 - k);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const bool have = i < span;
+            hw[i] = have ? lk.load_h(k + DIR * (1 + i)) : Link::empty_h();
+            mw[i] = have ? lk.load_m(k + DIR * (1 + i)) : Link::empty_m();
+        }
+    }
+    template <int DIR>
+    __device__ __forceinline__ bool resolve(int k, int NK, typename Link::S base0,
+                                            typename Link::S* out) const {
+        const int span = DIR < 0 ? k : (NK - 1 - k);
+        if (span == 0) {
+            *out = base0;
+            return true;
+        }
+        return resolve_window<Link, N>(hw, mw, span, base0, out);
+    }
+};
+
 template <class Link, int DIR, int LB, class MapOf>
 __device__ typename Link::S look_back(const Link& lk, int k, int NK, typename Link::S base0,
                                       uint32_t polls, MapOf&& map_of) {
@@ -239,30 +319,8 @@ __device__ typename Link::S look_back(const Link& lk, int k, int NK, typename Li
                 mw[i] = Link::empty_m();
             }
         }
-        int depth = -1;
-        bool stop = false;
-        S base = base0;
-#pragma unroll
-        for (int i = 0; i < LB; ++i) {
-            if (depth < 0 && !stop) {
-                if (i >= span) {
-                    depth = i;  // reached the start of the chain
-                } else if (Link::ready_h(hw[i])) {
-                    depth = i;
-                    base = Link::state(hw[i]);
-                } else if (!Link::ready_m(mw[i])) {
-                    stop = true;
-                }
-            }
-        }
-        if (depth < 0 && !stop && span == LB) depth = LB;  // chain start just past the window
-        if (depth >= 0) {
-            S x = base;
-#pragma unroll
-            for (int i = LB - 1; i >= 0; --i)
-                if (i < depth) x = Link::apply(Link::map(mw[i]), x);
-            return x;
-        }
+        S x;
+        if (resolve_window<Link, LB>(hw, mw, span, base0, &x)) return x;
         __builtin_amdgcn_s_sleep(1);
     }
     // nearest published state at any distance (or the chain start) ...

@@ -250,6 +250,14 @@ void samu_fwd_kernel(SamuFwdArgs x) {
         opaque(br[i]);
         opaque(bi[i]);
     }
+    // early reading of the look-back window, issued once this thread's last
+    // row has arrived
+    EarlyWindow<ComplexLink, C::EW> early;
+    if (tid < W) {
+        const CxWords we = cx_words(x.sc, tk.phase);
+        const int z = zero_after_row(bi[NR - 1]);
+        early.template take<-1>(ComplexLink{we.ps, we.qs, we.hs, d.nS, g.s, W, tid + z}, g.k, d.NK);
+    }
     __syncthreads();
 
     if (tid < W) {
@@ -269,8 +277,10 @@ void samu_fwd_kernel(SamuFwdArgs x) {
         if (x.p.h0r && dl < d.D)
             base0 = Cx{x.p.h0r[(size_t)g.bi * d.D + dl], x.p.h0i[(size_t)g.bi * d.D + dl]};
         const ComplexLink lk{wd.ps, wd.qs, wd.hs, d.nS, g.s, W, c};
-        const Cx hin = look_back<ComplexLink, -1, C::LB>(
-            lk, g.k, d.NK, base0, x.polls, [&](int j) { return samu_fwd_tile_map<C>(x, j, g.bi, dl); });
+        Cx hin;
+        if (!early.template resolve<-1>(g.k, d.NK, base0, &hin))
+            hin = look_back<ComplexLink, -1, C::LB>(
+                lk, g.k, d.NK, base0, x.polls, [&](int j) { return samu_fwd_tile_map<C>(x, j, g.bi, dl); });
         if (more) publish_u64(wd.hs + o, pack_cx(caff_apply(A, hin)));
         s_hin[c] = hin;
     }
@@ -431,6 +441,14 @@ void samu_bwd_kernel(SamuBwdArgs x) {
         opaque(gr[i]);
         opaque(gi[i]);
     }
+    // early reading of the look-back window, issued once this thread's last
+    // row has arrived
+    EarlyWindow<ComplexLink, C::EW> early;
+    if (tid < W) {
+        const CxWords we = cx_words(x.sc, tk.phase);
+        const int z = zero_after_row(gi[NR - 1]);
+        early.template take<+1>(ComplexLink{we.ps, we.qs, we.hs, d.nS, g.s, W, tid + z}, g.k, d.NK);
+    }
     __syncthreads();
 
     if (tid < W) {
@@ -450,8 +468,10 @@ void samu_bwd_kernel(SamuBwdArgs x) {
         if (x.p.glr && dl < d.D)
             base0 = Cx{x.p.glr[(size_t)g.bi * d.D + dl], x.p.gli[(size_t)g.bi * d.D + dl]};
         const ComplexLink lk{wd.ps, wd.qs, wd.hs, d.nS, g.s, W, c};
-        const Cx cin = look_back<ComplexLink, +1, C::LB>(
-            lk, g.k, d.NK, base0, x.polls, [&](int j) { return samu_bwd_tile_map<C>(x, j, g.bi, dl); });
+        Cx cin;
+        if (!early.template resolve<+1>(g.k, d.NK, base0, &cin))
+            cin = look_back<ComplexLink, +1, C::LB>(
+                lk, g.k, d.NK, base0, x.polls, [&](int j) { return samu_bwd_tile_map<C>(x, j, g.bi, dl); });
         if (more) publish_u64(wd.hs + o, pack_cx(caff_apply(A, cin)));
         s_cin[c] = cin;
     }
