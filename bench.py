@@ -30,6 +30,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+# every kernel computes in fp32 (state, maps, gradients); bf16 is only the storage type
+ARITH_DTYPE = "f32"
 
 WORKLOAD_TEXT = {
     "small": "B=2 T=256 D=64 fp32, a~U(0.9,0.999), b=N(0,1)*sqrt(1-a^2)",
@@ -215,9 +217,10 @@ def complex_line(args, wl, lr, torch, W):
     res = {"metric": f"complex {args.mode}: effective HBM GB/s",
            "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": ARITH_DTYPE,
            "data": "synthetic (seeded numpy draws, see workloads/__init__.py)",
-           "config": {"workload": f"{wl.name}: {WORKLOAD_TEXT[wl.name]}", "B": B, "T": T, "M": M}}
+           "config": {"workload": f"{wl.name}: {WORKLOAD_TEXT[wl.name]}", "B": B, "T": T, "M": M,
+                      "io_dtype": wl.dtype}}
     res["pct_of_peak"] = round(100 * res["value"] / HBM_PEAK_GBPS, 2)
     if args.mode != "prefill":
         # per-direction averages over back-to-back launches
@@ -335,9 +338,10 @@ def samu_line(args, wl, lr, torch, W):
     res = {"metric": f"fused-transition {args.mode}: effective HBM GB/s",
            "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": ARITH_DTYPE,
            "data": "synthetic (seeded numpy draws, see workloads/__init__.py)",
-           "config": {"workload": f"{wl.name}: {WORKLOAD_TEXT[wl.name]}", "B": B, "T": T, "M": M}}
+           "config": {"workload": f"{wl.name}: {WORKLOAD_TEXT[wl.name]}", "B": B, "T": T, "M": M,
+                      "io_dtype": wl.dtype}}
     res["pct_of_peak"] = round(100 * res["value"] / HBM_PEAK_GBPS, 2)
     if args.mode != "prefill":
         for name, f, nb in (("fwd", fwd, fwd_bytes), ("bwd", bwd, bwd_bytes)):
@@ -430,9 +434,10 @@ def inference_line(args, wl, lr, torch, a, b, dt, inp=None):
         "metric": f"{args.mode}: effective HBM GB/s",
         "value": round(gbps, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "scaling": "weak", "vs_baseline": None, "dtype": ARITH_DTYPE,
         "data": "synthetic (seeded numpy draws, see workloads/__init__.py)",
         "config": {"workload": f"{wl.name}: {WORKLOAD_TEXT[wl.name]}", "B": B, "T": T, "D": D,
+                   "io_dtype": wl.dtype,
                    "mode": unit_note},
         "us_per_call": round(ms * 1e3, 2),
         **({"graph_us_per_step": round(graph_decode_us(torch, fn, stream, args.steps), 2)}
@@ -675,11 +680,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": ARITH_DTYPE,
         "data": "synthetic (seeded numpy draws, see workloads/__init__.py)",
         "config": {
             "workload": f"{wl.name}: {WORKLOAD_TEXT[wl.name]}",
             "B": B, "T": T, "D": D,
+            "io_dtype": wl.dtype,
             "fwd_algo": algo_name(fwd_algo, fwd_chunk, fwd_width),
             "bwd_algo": algo_name(bwd_algo, bwd_chunk, bwd_width),
         },
