@@ -163,7 +163,6 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
         br[i] = load_vec<C::DT, ALIGNED>(pbr, off, g.nvalid, 0.0f);
         bi[i] = load_vec<C::DT, ALIGNED>(pbi, off, g.nvalid, 0.0f);
     }
-    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
     if constexpr (RST) {
 #pragma unroll
         for (int i = 0; i < NR; ++i)
@@ -232,6 +231,9 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
         s_hin[c] = hin;
     }
     __syncthreads();
+    // this tile's share of clearing the other region (here, not before the
+    // summary: a loop of stores there would make the summary wait for every load)
+    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
 
     const bool ends = g.nrows > 0 && g.row0 + g.nrows == d.T;
     if constexpr (!OUT) {
@@ -313,19 +315,22 @@ void cx_fused_bwd_kernel(CxBwdArgs x) {
     RowVec<C::DT> ar[NR], ai[NR], gr[NR], gi[NR], hr[NR], hi[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const int row = g.row0 + i;
-        const int rc = row < d.T ? row : d.T - 1;
-        const int hrw = rc >= 1 ? rc - 1 : 0;
-        const uint32_t off = (uint32_t)(rc - g.trow0) * rowbytes + g.coff;
-        const uint32_t hoff = (uint32_t)(hrw - hrow0) * rowbytes + g.coff;
+        const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
         ar[i] = load_vec<C::DT, ALIGNED>(par, off, g.nvalid, 1.0f);
         ai[i] = load_vec<C::DT, ALIGNED>(pai, off, g.nvalid, 0.0f);
         gr[i] = load_vec<C::DT, ALIGNED>(pgr, off, g.nvalid, 0.0f);
         gi[i] = load_vec<C::DT, ALIGNED>(pgi, off, g.nvalid, 0.0f);
+    }
+    // the rows of `out` last: only the replay uses them
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int row = g.row0 + i;
+        const int rc = row < d.T ? row : d.T - 1;
+        const int hrw = rc >= 1 ? rc - 1 : 0;
+        const uint32_t hoff = (uint32_t)(hrw - hrow0) * rowbytes + g.coff;
         hr[i] = load_vec<C::DT, ALIGNED>(phr, hoff, g.nvalid, 0.0f);
         hi[i] = load_vec<C::DT, ALIGNED>(phi, hoff, g.nvalid, 0.0f);
     }
-    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
     // at a segment start a_t is not used: transition 0, grad_a_t = 0
     uint32_t rbits = 0;
     if constexpr (RST) {
@@ -400,6 +405,9 @@ void cx_fused_bwd_kernel(CxBwdArgs x) {
         s_cin[c] = cin;
     }
     __syncthreads();
+    // this tile's share of clearing the other region (here, not before the
+    // summary: a loop of stores there would make the summary wait for every load)
+    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
 
     char* pgar = static_cast<char*>(x.p.gar) + g.tbase;
     char* pgai = static_cast<char*>(x.p.gai) + g.tbase;

@@ -226,7 +226,6 @@ void fused_fwd_kernel(FwdArgs x) {
         ra[i] = load_vec<C::DT, ALIGNED>(pa, off, g.nvalid, 1.0f);
         rb[i] = load_vec<C::DT, ALIGNED>(pb, off, g.nvalid, 0.0f);
     }
-    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
     if constexpr (RST) {
         // a segment start drops the entering state: its transition becomes 0
 #pragma unroll
@@ -301,6 +300,9 @@ void fused_fwd_kernel(FwdArgs x) {
         s_hin[c] = hin;
     }
     __syncthreads();
+    // this tile's share of clearing the other region (here, not before the
+    // summary: a loop of stores there would make the summary wait for every load)
+    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
 
     const bool ends = g.nrows > 0 && g.row0 + g.nrows == d.T;  // holds row T-1
     if constexpr (!OUT) {
@@ -370,19 +372,23 @@ void fused_bwd_kernel(BwdArgs x) {
 #pragma unroll
         for (int i = 0; i < NR; ++i) rs[i] = reset_byte(x.reset, g, i, d.T);
     }
+    // a and grad_out first: the summary and the look-back need only those, so
+    // they can proceed while the rows of `out` (used by the replay) arrive
     RowVec<C::DT> ra[NR], rg_[NR], rh[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
+        ra[i] = load_vec<C::DT, ALIGNED>(pa, off, g.nvalid, 1.0f);
+        rg_[i] = load_vec<C::DT, ALIGNED>(pg, off, g.nvalid, 0.0f);
+    }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const int row = g.row0 + i;
         const int rc = row < d.T ? row : d.T - 1;
         const int hr = rc >= 1 ? rc - 1 : 0;
-        const uint32_t off = (uint32_t)(rc - g.trow0) * rowbytes + g.coff;
         const uint32_t hoff = (uint32_t)(hr - hrow0) * rowbytes + g.coff;
-        ra[i] = load_vec<C::DT, ALIGNED>(pa, off, g.nvalid, 1.0f);
-        rg_[i] = load_vec<C::DT, ALIGNED>(pg, off, g.nvalid, 0.0f);
         rh[i] = load_vec<C::DT, ALIGNED>(ph, hoff, g.nvalid, 0.0f);
     }
-    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
     // at a segment start a_t is not used: its transition is 0 (no adjoint
     // crosses it) and grad_a_t = 0 (the previous state is taken as 0)
     uint32_t rbits = 0;
@@ -460,6 +466,9 @@ void fused_bwd_kernel(BwdArgs x) {
         s_cin[c] = cin;
     }
     __syncthreads();
+    // this tile's share of clearing the other region (here, not before the
+    // summary: a loop of stores there would make the summary wait for every load)
+    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
 
     // lam[j] starts as the carry a_{s+1}*lambda_{s+1} entering this thread's
     // last row from the right; each row then takes

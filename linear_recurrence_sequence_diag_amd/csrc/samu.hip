@@ -221,7 +221,6 @@ void samu_fwd_kernel(SamuFwdArgs x) {
         const int m = g.d0 + j < d.D ? g.d0 + j : d.D - 1;
         ln[j] = samu_lane(x.mode_tab, m);
     }
-    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
     // lanes past M step with the identity, as the derived maps assume
     auto trans = [&](int i, int j) -> Cx {
         if (j >= g.nvalid) return Cx{1.0f, 0.0f};
@@ -285,6 +284,9 @@ void samu_fwd_kernel(SamuFwdArgs x) {
         s_hin[c] = hin;
     }
     __syncthreads();
+    // this tile's share of clearing the other region (here, not before the
+    // summary: a loop of stores there would make the summary wait for every load)
+    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
 
     const bool ends = g.nrows > 0 && g.row0 + g.nrows == d.T;
     if constexpr (!OUT) {
@@ -387,13 +389,17 @@ void samu_bwd_kernel(SamuBwdArgs x) {
     RowVec<C::DT> gr[NR], gi[NR], hr[NR], hi[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
+        const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
+        gr[i] = load_vec<C::DT, ALIGNED>(pgr, off, g.nvalid, 0.0f);
+        gi[i] = load_vec<C::DT, ALIGNED>(pgi, off, g.nvalid, 0.0f);
+    }
+    // the rows of `out` last: only the replay uses them
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
         const int row = g.row0 + i;
         const int rc = row < d.T ? row : d.T - 1;
         const int hrw = rc >= 1 ? rc - 1 : 0;
-        const uint32_t off = (uint32_t)(rc - g.trow0) * rowbytes + g.coff;
         const uint32_t hoff = (uint32_t)(hrw - hrow0) * rowbytes + g.coff;
-        gr[i] = load_vec<C::DT, ALIGNED>(pgr, off, g.nvalid, 0.0f);
-        gi[i] = load_vec<C::DT, ALIGNED>(pgi, off, g.nvalid, 0.0f);
         hr[i] = load_vec<C::DT, ALIGNED>(phr, hoff, g.nvalid, 0.0f);
         hi[i] = load_vec<C::DT, ALIGNED>(phi, hoff, g.nvalid, 0.0f);
     }
@@ -412,7 +418,6 @@ void samu_bwd_kernel(SamuBwdArgs x) {
         const int m = g.d0 + j < d.D ? g.d0 + j : d.D - 1;
         ln[j] = samu_lane(x.mode_tab, m);
     }
-    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
     // lanes past M step with the identity, as the derived maps assume
     auto trans = [&](int i, int j) -> Cx {
         if (j >= g.nvalid) return Cx{1.0f, 0.0f};
@@ -476,6 +481,9 @@ void samu_bwd_kernel(SamuBwdArgs x) {
         s_cin[c] = cin;
     }
     __syncthreads();
+    // this tile's share of clearing the other region (here, not before the
+    // summary: a loop of stores there would make the summary wait for every load)
+    clear_share(x.sc, tk.phase, tk.nclear, C::NT, tk.ticket);
 
     char* pgbr = static_cast<char*>(x.p.gbr) + g.tbase;
     char* pgbi = static_cast<char*>(x.p.gbi) + g.tbase;
