@@ -314,13 +314,14 @@ void cx_fused_bwd_kernel(CxBwdArgs x) {
     }
     RowVec<C::DT> ar[NR], ai[NR], gr[NR], gi[NR], hr[NR], hi[NR];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
+    for (int i = NR - 1; i >= 0; --i) {  // last row first: the reverse summary's order
         const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
         ar[i] = load_vec<C::DT, ALIGNED>(par, off, g.nvalid, 1.0f);
         ai[i] = load_vec<C::DT, ALIGNED>(pai, off, g.nvalid, 0.0f);
         gr[i] = load_vec<C::DT, ALIGNED>(pgr, off, g.nvalid, 0.0f);
         gi[i] = load_vec<C::DT, ALIGNED>(pgi, off, g.nvalid, 0.0f);
     }
+    __builtin_amdgcn_sched_barrier(0);  // keep the load order as written
     // the rows of `out` last: only the replay uses them
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -331,6 +332,7 @@ void cx_fused_bwd_kernel(CxBwdArgs x) {
         hr[i] = load_vec<C::DT, ALIGNED>(phr, hoff, g.nvalid, 0.0f);
         hi[i] = load_vec<C::DT, ALIGNED>(phi, hoff, g.nvalid, 0.0f);
     }
+    __builtin_amdgcn_sched_barrier(0);
     // at a segment start a_t is not used: transition 0, grad_a_t = 0
     uint32_t rbits = 0;
     if constexpr (RST) {

@@ -372,15 +372,18 @@ void fused_bwd_kernel(BwdArgs x) {
 #pragma unroll
         for (int i = 0; i < NR; ++i) rs[i] = reset_byte(x.reset, g, i, d.T);
     }
-    // a and grad_out first: the summary and the look-back need only those, so
-    // they can proceed while the rows of `out` (used by the replay) arrive
+    // a and grad_out first, last row first (the order the reverse summary
+    // uses them), then `out`: the summary and the look-back proceed while the
+    // rows of `out` (used only by the replay) arrive.  The scheduling
+    // barriers keep the compiler from reordering or sinking the loads.
     RowVec<C::DT> ra[NR], rg_[NR], rh[NR];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
+    for (int i = NR - 1; i >= 0; --i) {
         const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
         ra[i] = load_vec<C::DT, ALIGNED>(pa, off, g.nvalid, 1.0f);
         rg_[i] = load_vec<C::DT, ALIGNED>(pg, off, g.nvalid, 0.0f);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const int row = g.row0 + i;
@@ -389,6 +392,7 @@ void fused_bwd_kernel(BwdArgs x) {
         const uint32_t hoff = (uint32_t)(hr - hrow0) * rowbytes + g.coff;
         rh[i] = load_vec<C::DT, ALIGNED>(ph, hoff, g.nvalid, 0.0f);
     }
+    __builtin_amdgcn_sched_barrier(0);
     // at a segment start a_t is not used: its transition is 0 (no adjoint
     // crosses it) and grad_a_t = 0 (the previous state is taken as 0)
     uint32_t rbits = 0;
