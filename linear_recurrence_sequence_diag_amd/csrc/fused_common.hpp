@@ -200,25 +200,6 @@ __device__ __forceinline__ int wave_max_active(int v) {
     return uniform(r);
 }
 
-// Carry entering tile k of a chain (forward: DIR = -1 looks at k-1, k-2, ...;
-// reverse: DIR = +1 looks at k+1, k+2, ...).  `base0` is the carry entering the
-// chain (h0 forward, grad_last reverse).  The nearest published inclusive
-// state within a window of LB predecessors is taken and the maps of the tiles
-// in between are applied to it oldest first, so the result is the plain
-// chained value.
-//
-// The window is polled up to `polls` times.  After that the tile stops
-// waiting: it finds the nearest published state at any distance, and derives
-// every map in between that is not yet published itself, with `map_of(j)`,
-// from the inputs and bitwise equal to what tile j publishes.  So no tile
-// ever waits on a workgroup that has not started, whatever order the
-// hardware starts workgroups in, and results do not depend on which path
-// was taken.
-//
-// `Link` reads one lane's published words of chunk j (load_h / load_m, each
-// a single atomic load per word), says whether they are published
-// (ready_h / ready_m), decodes them (state / map) and applies a map to a
-// state; it fixes the value types (real or complex).
 // One reading of N predecessors' words (index 0 the nearest), `rem` of which
 // exist before the chain start: the depth of the nearest published state (its
 // value in *base) or of the chain start (base0), N + 1 when every map of the
@@ -298,6 +279,25 @@ struct EarlyWindow {
     }
 };
 
+// Carry entering tile k of a chain (forward: DIR = -1 looks at k-1, k-2, ...;
+// reverse: DIR = +1 looks at k+1, k+2, ...).  `base0` is the carry entering the
+// chain (h0 forward, grad_last reverse).  The nearest published inclusive
+// state within a window of LB predecessors is taken and the maps of the tiles
+// in between are applied to it oldest first, so the result is the plain
+// chained value.
+//
+// The window is polled up to `polls` times.  After that the tile stops
+// waiting: it finds the nearest published state at any distance, and derives
+// every map in between that is not yet published itself, with `map_of(j)`,
+// from the inputs and bitwise equal to what tile j publishes.  So no tile
+// ever waits on a workgroup that has not started, whatever order the
+// hardware starts workgroups in, and results do not depend on which path
+// was taken.
+//
+// `Link` reads one lane's published words of chunk j (load_h / load_m, each
+// a single atomic load per word), says whether they are published
+// (ready_h / ready_m), decodes them (state / map) and applies a map to a
+// state; it fixes the value types (real or complex).
 template <class Link, int DIR, int LB, class MapOf>
 __device__ typename Link::S look_back(const Link& lk, int k, int NK, typename Link::S base0,
                                       uint32_t polls, MapOf&& map_of) {
