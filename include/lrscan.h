@@ -33,6 +33,16 @@
  *    bits every time.
  *  - Calls that share one workspace (the library's own per-stream workspace,
  *    or one passed in opts) must be ordered on one stream.
+ *  - Graph capture.  While `stream` is capturing a HIP graph, the library
+ *    allocates, frees and initialises nothing.  A call that needs the
+ *    library's workspace (opts->workspace NULL) then uses the one this stream
+ *    already has, which an eager call of at least the same size on the same
+ *    stream must have set up first; otherwise it returns LRSCAN_ERR_CAPTURE
+ *    and enqueues nothing.  The captured graph keeps using that buffer on
+ *    every replay: the library never frees a buffer a capture was given (a
+ *    later, larger eager call on the stream gets a new one), and replays must
+ *    be ordered with the other calls on that stream.  A caller workspace
+ *    (opts->workspace) is initialised inside each captured call instead.
  */
 #ifndef LRSCAN_H
 #define LRSCAN_H
@@ -58,7 +68,9 @@ enum {
     LRSCAN_ERR_CHUNK = -4,     /* chunk length not supported by the chosen algorithm */
     LRSCAN_ERR_WORKSPACE = -5, /* workspace given but smaller than scan_workspace_bytes() */
     LRSCAN_ERR_HIP = -6,       /* the HIP runtime reported an error (launch or allocation) */
-    LRSCAN_ERR_ALGO = -7       /* unknown algorithm */
+    LRSCAN_ERR_ALGO = -7,      /* unknown algorithm */
+    LRSCAN_ERR_CAPTURE = -8    /* the stream is capturing a graph and its library workspace is
+                                  missing or too small (see "Graph capture" above) */
 };
 
 /* algorithms */

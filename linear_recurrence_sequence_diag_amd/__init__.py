@@ -26,6 +26,7 @@ ALGOS = {"auto": ALGO_AUTO, "seq": ALGO_SEQ, "chunked": ALGO_CHUNKED, "fused": A
 STATUS = {
     0: "LRSCAN_OK", -1: "LRSCAN_ERR_NULL", -2: "LRSCAN_ERR_DIM", -3: "LRSCAN_ERR_DTYPE",
     -4: "LRSCAN_ERR_CHUNK", -5: "LRSCAN_ERR_WORKSPACE", -6: "LRSCAN_ERR_HIP", -7: "LRSCAN_ERR_ALGO",
+    -8: "LRSCAN_ERR_CAPTURE",
 }
 
 

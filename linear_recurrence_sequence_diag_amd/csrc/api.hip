@@ -7,6 +7,7 @@
 #include <mutex>
 #include <tuple>
 #include <utility>
+#include <vector>
 
 #include "../../include/lrscan.h"
 #include "device.hpp"
@@ -38,44 +39,73 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // fused form's self-cleaning scratch, which must not be shared with anything
 // else and is initialised once per allocation; kind 2 holds the
 // fused-transition scan's factor tables and partial sums.
+//
+// Graph capture.  A call captured into a HIP graph bakes the workspace
+// address into the graph's kernel arguments, and every replay uses it.  So
+// while a stream is capturing, the library neither allocates, frees nor
+// initialises: it hands out the stream's buffer only if that buffer is
+// already big enough and initialised (an eager call of at least this size
+// ran on the stream before), and marks it as captured.  A captured buffer is
+// never freed: when a later eager call needs a bigger one, it is retired
+// (kept for the life of the process) and a new one is allocated.
 struct CachedWs {
     void* ptr = nullptr;
     size_t bytes = 0;
-    bool fresh = false;  // not yet initialised for the fused form
+    bool fresh = false;     // not yet initialised for the fused form
+    bool captured = false;  // handed to a call under capture: a graph may hold it
 };
 std::mutex g_ws_mutex;
 std::map<std::tuple<int, void*, int>, CachedWs> g_ws;
+std::vector<void*> g_retired;  // superseded captured buffers (never freed)
 
 struct Workspace {
     void* ptr = nullptr;
     size_t bytes = 0;
-    bool init = false;  // the fused form must initialise it before use
+    bool init = false;     // the fused form must initialise it before use
+    bool library = false;  // one of the library's per-stream buffers
 };
 
+// Whether `st` is capturing into a graph (an invalidated capture counts).
+hipError_t stream_capturing(hipStream_t st, bool* capturing) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(st, &cs);
+    *capturing = cs != hipStreamCaptureStatusNone;
+    return e;
+}
+
 // A device buffer of at least `bytes` owned by the library, ordered on `st`.
-hipError_t library_workspace(size_t bytes, int kind, hipStream_t st, Workspace* out) {
+int library_workspace(size_t bytes, int kind, hipStream_t st, Workspace* out) {
     int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
+    if (hipGetDevice(&dev) != hipSuccess) return LRSCAN_ERR_HIP;
+    bool capturing = false;
+    if (stream_capturing(st, &capturing) != hipSuccess) return LRSCAN_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     CachedWs& c = g_ws[std::make_tuple(dev, (void*)st, kind)];
-    if (c.bytes < bytes) {
+    if (capturing) {
+        if (!c.ptr || c.bytes < bytes || c.fresh) return LRSCAN_ERR_CAPTURE;
+        c.captured = true;
+    } else if (c.bytes < bytes) {
         if (c.ptr) {
-            e = hipFreeAsync(c.ptr, st);
-            if (e != hipSuccess) return e;
-            c.ptr = nullptr;
-            c.bytes = 0;
+            if (c.captured) {
+                g_retired.push_back(c.ptr);
+            } else if (hipFreeAsync(c.ptr, st) != hipSuccess) {
+                return LRSCAN_ERR_HIP;
+            }
+            c = CachedWs{};
         }
         const size_t want = align_up(bytes + bytes / 4, 1 << 20);
-        e = hipMallocAsync(&c.ptr, want, st);
-        if (e != hipSuccess) return e;
+        if (hipMallocAsync(&c.ptr, want, st) != hipSuccess) {
+            c = CachedWs{};
+            return LRSCAN_ERR_HIP;
+        }
         c.bytes = want;
-        c.fresh = true;
+        c.fresh = kind == 1;  // only the fused scratch has an initial state
     }
     out->ptr = c.ptr;
     out->bytes = c.bytes;
     out->init = c.fresh;
-    return hipSuccess;
+    out->library = true;
+    return LRSCAN_OK;
 }
 
 // Called after a launch that initialised the library's fused workspace was
@@ -88,9 +118,9 @@ void workspace_initialised(hipStream_t st) {
     if (it != g_ws.end()) it->second.fresh = false;
 }
 
-int fused_status(hipError_t e, const Workspace& ws, const lrscan_opts* o, hipStream_t st) {
+int fused_status(hipError_t e, const Workspace& ws, hipStream_t st) {
     if (e != hipSuccess) return LRSCAN_ERR_HIP;
-    if (ws.init && !(o && o->workspace)) workspace_initialised(st);
+    if (ws.init && ws.library) workspace_initialised(st);
     return LRSCAN_OK;
 }
 
@@ -180,7 +210,7 @@ int get_workspace(const Shape& s, const Resolved& r, const lrscan_opts* o, hipSt
         return LRSCAN_OK;
     }
     const int kind = r.algo == LRSCAN_ALGO_FUSED ? 1 : 0;
-    return library_workspace(need, kind, st, ws) == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_HIP;
+    return library_workspace(need, kind, st, ws);
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_HIP; }
@@ -220,7 +250,7 @@ int complex_workspace(const Shape& s, int algo, const lrscan_opts* o, hipStream_
         ws->init = true;
         return LRSCAN_OK;
     }
-    return library_workspace(need, 1, st, ws) == hipSuccess ? LRSCAN_OK : LRSCAN_ERR_HIP;
+    return library_workspace(need, 1, st, ws);
 }
 
 // ---- fused-transition scan helpers ----
@@ -251,11 +281,65 @@ int samu_workspace(const Shape& s, const lrscan_opts* o, hipStream_t st, Workspa
         *aux = static_cast<char*>(o->workspace) + align_up(samu_scratch_bytes(s), 256);
         return LRSCAN_OK;
     }
-    if (library_workspace(samu_scratch_bytes(s), 1, st, ws) != hipSuccess) return LRSCAN_ERR_HIP;
+    int rc = library_workspace(samu_scratch_bytes(s), 1, st, ws);
+    if (rc != LRSCAN_OK) return rc;
     Workspace a;
-    if (library_workspace(samu_aux_bytes(s), 2, st, &a) != hipSuccess) return LRSCAN_ERR_HIP;
+    rc = library_workspace(samu_aux_bytes(s), 2, st, &a);
+    if (rc != LRSCAN_OK) return rc;
     *aux = a.ptr;
     return LRSCAN_OK;
+}
+
+// ---- the forward, shared by scan_fwd_ex and scan_fwd_noalloc ----
+
+struct FwdCall {
+    const void* a;
+    const void* b;
+    void* out;
+    float* last;
+    Shape s;
+    hipStream_t hs;
+    const lrscan_opts* o;
+};
+
+// Argument checks and the algorithm choice of a forward call.
+int check_fwd(const FwdCall& c, Resolved* r) {
+    if (!c.a || !c.b || (!c.out && !c.last)) return LRSCAN_ERR_NULL;
+    if (!dims_ok(c.s.B, c.s.T, c.s.D)) return LRSCAN_ERR_DIM;
+    if (!dtype_ok(c.s.dtype)) return LRSCAN_ERR_DTYPE;
+    const void* ptrs[3] = {c.a, c.b, c.out};
+    const bool aligned = rows_aligned(c.s, ptrs, 3);
+    *r = resolve(c.s, 0, c.o, aligned);
+    return validate_algo(c.s, 0, *r, aligned);
+}
+
+// Enqueue a checked forward call on workspace `ws`.
+int run_fwd(const FwdCall& c, const Resolved& r, const Workspace& ws) {
+    const Shape& s = c.s;
+    const float* h0 = c.o ? c.o->h0 : nullptr;
+    const uint8_t* reset = c.o ? c.o->reset : nullptr;
+    switch (r.algo) {
+        case LRSCAN_ALGO_SEQ:
+            return hip_status(launch_seq_fwd(s, c.a, c.b, c.out, c.last, h0, reset, c.hs));
+        case LRSCAN_ALGO_CHUNKED: {
+            const int64_t NC = (s.T + r.chunk - 1) / r.chunk;
+            const size_t part = align_up((size_t)NC * s.B * s.D * 4, 256);
+            float* P = static_cast<float*>(ws.ptr);
+            float* Q = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + part);
+            float* cin = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + 2 * part);
+            hipError_t e = launch_chunk_summary(s, r.chunk, c.a, c.b, reset, P, Q, c.hs);
+            if (e == hipSuccess) e = launch_chunk_prefix(s.B, NC, s.D, P, Q, h0, cin, nullptr, c.hs);
+            if (e == hipSuccess)
+                e = launch_chunk_replay(s, r.chunk, c.a, c.b, reset, cin, c.out, c.last, c.hs);
+            return hip_status(e);
+        }
+        case LRSCAN_ALGO_FUSED:
+            return fused_status(launch_fused_fwd(s, r.width, r.chunk, c.a, c.b, c.out, c.last, h0,
+                                                 reset, ws.ptr, ws.bytes, ws.init,
+                                                 c.o ? c.o->polls : 0, c.hs),
+                                ws, c.hs);
+    }
+    return LRSCAN_ERR_ALGO;
 }
 
 }  // namespace
@@ -272,6 +356,10 @@ LRSCAN_API const char* scan_status_string(int status) {
         case LRSCAN_ERR_WORKSPACE: return "workspace smaller than scan_workspace_bytes() or not 256-byte aligned";
         case LRSCAN_ERR_HIP: return "the HIP runtime reported an error";
         case LRSCAN_ERR_ALGO: return "unknown algorithm";
+        case LRSCAN_ERR_CAPTURE:
+            return "the stream is capturing a graph and has no library workspace of this size yet "
+                   "(make one eager call of at least this size on the stream first, or pass "
+                   "opts->workspace)";
     }
     return "unknown status";
 }
@@ -307,40 +395,14 @@ LRSCAN_API size_t scan_workspace_bytes(int64_t B, int64_t T, int64_t D, int dtyp
 
 LRSCAN_API int scan_fwd_ex(const void* a, const void* b, void* out, float* last, int64_t B,
                            int64_t T, int64_t D, int dtype, void* stream, const lrscan_opts* opts) {
-    if (!a || !b || (!out && !last)) return LRSCAN_ERR_NULL;
-    if (!dims_ok(B, T, D)) return LRSCAN_ERR_DIM;
-    if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
-    const Shape s{B, T, D, dtype};
-    const void* ptrs[3] = {a, b, out};
-    const bool aligned = rows_aligned(s, ptrs, 3);
-    const Resolved r = resolve(s, 0, opts, aligned);
-    int st = validate_algo(s, 0, r, aligned);
+    const FwdCall c{a, b, out, last, Shape{B, T, D, dtype}, static_cast<hipStream_t>(stream), opts};
+    Resolved r;
+    int st = check_fwd(c, &r);
     if (st != LRSCAN_OK) return st;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    const float* h0 = opts ? opts->h0 : nullptr;
-    const uint8_t* reset = opts ? opts->reset : nullptr;
     Workspace ws;
-    st = get_workspace(s, r, opts, hs, &ws);
+    st = get_workspace(c.s, r, opts, c.hs, &ws);
     if (st != LRSCAN_OK) return st;
-    switch (r.algo) {
-        case LRSCAN_ALGO_SEQ: return hip_status(launch_seq_fwd(s, a, b, out, last, h0, reset, hs));
-        case LRSCAN_ALGO_CHUNKED: {
-            const int64_t NC = (T + r.chunk - 1) / r.chunk;
-            const size_t part = align_up((size_t)NC * B * D * 4, 256);
-            float* P = static_cast<float*>(ws.ptr);
-            float* Q = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + part);
-            float* cin = reinterpret_cast<float*>(static_cast<char*>(ws.ptr) + 2 * part);
-            hipError_t e = launch_chunk_summary(s, r.chunk, a, b, reset, P, Q, hs);
-            if (e == hipSuccess) e = launch_chunk_prefix(B, NC, D, P, Q, h0, cin, nullptr, hs);
-            if (e == hipSuccess) e = launch_chunk_replay(s, r.chunk, a, b, reset, cin, out, last, hs);
-            return hip_status(e);
-        }
-        case LRSCAN_ALGO_FUSED:
-            return fused_status(launch_fused_fwd(s, r.width, r.chunk, a, b, out, last, h0, reset,
-                                                 ws.ptr, ws.bytes, ws.init, opts ? opts->polls : 0, hs),
-                                ws, opts, hs);
-    }
-    return LRSCAN_ERR_ALGO;
+    return run_fwd(c, r, ws);
 }
 
 LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
@@ -384,7 +446,7 @@ LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
             return fused_status(launch_fused_bwd(s, r.width, r.chunk, a, out, grad_out, grad_last,
                                                  h0, reset, grad_a, grad_b, grad_h0, ws.ptr, ws.bytes,
                                                  ws.init, opts ? opts->polls : 0, hs),
-                                ws, opts, hs);
+                                ws, hs);
     }
     return LRSCAN_ERR_ALGO;
 }
@@ -436,7 +498,7 @@ LRSCAN_API int scan_complex_fwd(const void* ar, const void* ai, const void* br, 
     if (st != LRSCAN_OK) return st;
     return fused_status(launch_complex_fused_fwd(s, p, ws.ptr, ws.bytes, ws.init,
                                                  opts ? opts->polls : 0, hs),
-                        ws, opts, hs);
+                        ws, hs);
 }
 
 LRSCAN_API int scan_complex_bwd(const void* ar, const void* ai, const void* out_r,
@@ -468,7 +530,7 @@ LRSCAN_API int scan_complex_bwd(const void* ar, const void* ai, const void* out_
     if (st != LRSCAN_OK) return st;
     return fused_status(launch_complex_fused_bwd(s, p, ws.ptr, ws.bytes, ws.init,
                                                  opts ? opts->polls : 0, hs),
-                        ws, opts, hs);
+                        ws, hs);
 }
 
 LRSCAN_API size_t scan_complex_workspace_bytes(int64_t B, int64_t T, int64_t M, int dtype,
@@ -504,8 +566,8 @@ LRSCAN_API int scan_samu_fwd(const void* eta, const void* delta, const float* nu
     st = samu_workspace(s, opts, hs, &ws, &aux);
     if (st != LRSCAN_OK) return st;
     return fused_status(
-        launch_samu_fwd(s, p, ws.ptr, ws.bytes, ws.init, aux, opts ? opts->polls : 0, hs), ws,
-        opts, hs);
+        launch_samu_fwd(s, p, ws.ptr, ws.bytes, ws.init, aux, opts ? opts->polls : 0, hs),
+        ws, hs);
 }
 
 LRSCAN_API int scan_samu_bwd(const void* eta, const void* delta, const float* nu_log,
@@ -556,8 +618,8 @@ LRSCAN_API int scan_samu_bwd(const void* eta, const void* delta, const float* nu
     st = samu_workspace(s, opts, hs, &ws, &aux);
     if (st != LRSCAN_OK) return st;
     return fused_status(
-        launch_samu_bwd(s, p, ws.ptr, ws.bytes, ws.init, aux, opts ? opts->polls : 0, hs), ws,
-        opts, hs);
+        launch_samu_bwd(s, p, ws.ptr, ws.bytes, ws.init, aux, opts ? opts->polls : 0, hs),
+        ws, hs);
 }
 
 LRSCAN_API size_t scan_samu_workspace_bytes(int64_t B, int64_t T, int64_t M, int dtype,

@@ -712,8 +712,8 @@ hipError_t launch_complex_seq_bwd(const Shape& s, const CxBwdPtrs& p, hipStream_
 }
 
 bool complex_fused_supported(const Shape& s) {
-    return tiled_layout_ok(s, CxFwdCfg<DT_F32>::CT, cx_fwd_layout(s)) &&
-           tiled_layout_ok(s, CxBwdCfg<DT_F32>::CT, cx_bwd_layout(s));
+    return tiled_layout_ok(s, CxFwdCfg<DT_F32>::CT, CxFwdCfg<DT_F32>::NT, cx_fwd_layout(s)) &&
+           tiled_layout_ok(s, CxBwdCfg<DT_F32>::CT, CxBwdCfg<DT_F32>::NT, cx_bwd_layout(s));
 }
 
 size_t complex_fused_workspace_bytes(const Shape& s) {

@@ -12,11 +12,12 @@ namespace {
 
 // The index limits of a tiled kernel (32-bit row offsets inside a tile,
 // 32-bit lane and row indices, 32-bit tickets) for a tile of `tile` rows.
-bool tiled_layout_ok(const Shape& s, int tile, const Layout& L) {
+bool tiled_layout_ok(const Shape& s, int tile, int nt, const Layout& L) {
     const int64_t eb = s.dtype == DT_F32 ? 4 : 2;
     if ((int64_t)(tile + 1) * s.D * eb >= ((int64_t)1 << 31)) return false;
     if (s.T >= ((int64_t)1 << 31) - tile || s.D >= ((int64_t)1 << 30)) return false;
     if ((unsigned long long)L.NK * L.nS >= 0xffffffffull) return false;
+    if (!grid_fits(L, nt)) return false;
     if (s.B * (int64_t)L.nW >= ((int64_t)1 << 31)) return false;
     return true;
 }

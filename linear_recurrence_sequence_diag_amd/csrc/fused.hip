@@ -609,6 +609,7 @@ bool fused_cfg_supported(const Shape& s, int dir, int width, int tile, bool alig
     if (s.T >= ((int64_t)1 << 31) - tile || s.D >= ((int64_t)1 << 30)) return false;
     const Layout L = layout_of(s, width, tile);
     if ((unsigned long long)L.NK * L.nS >= 0xffffffffull) return false;
+    if (!grid_fits(L, find_cfg(dir, width, tile)->waves * kWave)) return false;
     if (s.B * (int64_t)L.nW >= ((int64_t)1 << 31)) return false;
     return true;
 }

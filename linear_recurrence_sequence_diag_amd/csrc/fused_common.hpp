@@ -416,6 +416,13 @@ Layout layout_of(const Shape& s, int width, int tile) {
     return L;
 }
 
+// A launch of one workgroup of `nt` threads per tile stays within the 32-bit
+// count of work-items of a grid dimension.
+bool grid_fits(const Layout& L, int nt) {
+    return (unsigned long long)L.NK * (unsigned long long)L.nS * (unsigned long long)nt <
+           (1ull << 32);
+}
+
 // Ticket counters: the largest power of two up to kMaxCounters dividing nS.
 int counters_of(const Layout& L) {
     int c = 1;

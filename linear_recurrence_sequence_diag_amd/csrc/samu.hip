@@ -784,8 +784,8 @@ hipError_t samu_bwd_t(const Shape& s, const SamuBwdPtrs& p, void* ws, size_t ws_
 }  // namespace
 
 bool samu_supported(const Shape& s) {
-    return tiled_layout_ok(s, SamuFwdCfg<DT_F32>::CT, samu_fwd_layout(s)) &&
-           tiled_layout_ok(s, SamuBwdCfg<DT_F32>::CT, samu_bwd_layout(s));
+    return tiled_layout_ok(s, SamuFwdCfg<DT_F32>::CT, SamuFwdCfg<DT_F32>::NT, samu_fwd_layout(s)) &&
+           tiled_layout_ok(s, SamuBwdCfg<DT_F32>::CT, SamuBwdCfg<DT_F32>::NT, samu_bwd_layout(s));
 }
 
 size_t samu_scratch_bytes(const Shape& s) {

@@ -6,8 +6,16 @@ same stream (and so the same workspace) in between; every replay must equal
 the eager result bit for bit (the workspace cleans itself on the device, so
 replays need no initialisation step and capture no memset).
 
+Capture without a set-up workspace: a capturing stream gets no library
+allocation, so a first call under capture is refused (LRSCAN_ERR_CAPTURE)
+with nothing enqueued.  A larger eager call after a capture gets a new
+workspace while the captured graph keeps replaying on the old one, which the
+library never frees.
+
 Streams: two streams run different scans at the same time, each on its own
 library workspace; the results equal those of the same calls made alone."""
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -73,6 +81,86 @@ def test_graph_replays_equal_eager(dt):
         torch.cuda.synchronize()
         assert all(torch.equal(x, y) for x, y in zip(again, ref)), f"eager call after replay {rep}"
     log(f"graph {dt}: 4 replays bitwise equal to eager")
+
+
+def fresh_stream():
+    """A new HIP stream (never handed out before, so the library has no
+    workspace for it), wrapped for torch.  Not destroyed: the library keeps
+    its workspaces keyed by the handle."""
+    hip = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+    h = ctypes.c_void_p()
+    assert hip.hipStreamCreate(ctypes.byref(h)) == 0
+    return torch.cuda.ExternalStream(h.value)
+
+
+def test_capture_first_call_is_refused():
+    r = W.random_inputs(2, 700, 256, "f32", seed=76, a_lo=0.5, a_hi=0.99)
+    a, b = dev(r.a, "f32"), dev(r.b, "f32")
+    st = fresh_stream()
+    x = torch.arange(4096, device="cuda", dtype=torch.float32)
+    y = torch.zeros_like(x)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        y.copy_(x)
+        with pytest.raises(lr.LRScanError) as err:
+            lr.scan(a, b)
+    assert err.value.status == -8, err.value
+    for _ in range(2):
+        y.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, x)
+    # an eager call sets the stream up; then the same call captures and replays
+    with torch.cuda.stream(st):
+        ref = [t.clone() for t in lr.scan(a, b)]
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=st):
+        res = lr.scan(a, b)
+    for rep in range(3):
+        g2.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(u, v) for u, v in zip(res, ref)), f"replay {rep}"
+    log("capture: a first call is refused; after an eager call it captures and replays")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_capture_survives_a_larger_eager_call(dt):
+    """Capture at one size, then make a much larger eager call on the same
+    stream (the stream's workspace is replaced): the graph's replays still
+    equal eager results bit for bit."""
+    small = W.random_inputs(2, 3000, 256, dt, seed=77, a_lo=0.5, a_hi=0.99)
+    big = W.random_inputs(4, 4096, 2560, dt, seed=78, a_lo=0.5, a_hi=0.99)
+    a, b, g = dev(small.a, dt), dev(small.b, dt), dev(small.g, dt)
+    A, Bv, G = dev(big.a, dt), dev(big.b, dt), dev(big.g, dt)
+    st = fresh_stream()
+    with torch.cuda.stream(st):
+        ref = [x.clone() for x in real_step(a, b, g)]
+        big_ref = [x.clone() for x in real_step(A, Bv, G)]
+        small_again = [x.clone() for x in real_step(a, b, g)]
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(ref, small_again))
+    st2 = fresh_stream()
+    with torch.cuda.stream(st2):
+        real_step(a, b, g)   # sets st2's workspace up at the small size only
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st2):
+        res = real_step(a, b, g)
+    for rep in range(3):
+        with torch.cuda.stream(st2):   # needs a bigger workspace than the captured one
+            out_big = real_step(A, Bv, G)
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, (x, y) in enumerate(zip(res, ref)):
+            assert torch.equal(x, y), f"replay {rep}: output {k} differs from eager"
+        assert all(torch.equal(x, y) for x, y in zip(out_big, big_ref)), f"large call {rep}"
+        with torch.cuda.stream(st2):
+            again = real_step(a, b, g)
+        torch.cuda.synchronize()
+        assert all(torch.equal(x, y) for x, y in zip(again, ref)), f"eager after replay {rep}"
+    log(f"capture {dt}: replays unaffected by a larger eager call on the capture stream")
 
 
 def test_concurrent_streams_equal_solo():
