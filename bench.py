@@ -5,15 +5,20 @@ reverse-time backward (grad_a, grad_b) over one batch of synthetic inputs,
 both through the C ABI with the library's automatic algorithm choice.  The
 inputs are generated (seeded) and copied to HBM before the timed region.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wide]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Prints one JSON line.  `value` is the effective HBM bandwidth of the whole
-step: the algorithmic bytes (forward 3*s*N + 4*B*D, backward 5*s*N, s the I/O
-element size, N = B*T*D) divided by the measured step time (K steps back to
-back).  Beside it: per-launch median and minimum, a "cold" step time with the
-Infinity Cache flushed before each step, the achievable streaming ceiling of a
-1 GiB device copy, the dominant kernel's roofline, and the fp64 oracle's rate
-on the host (all cores and one core).
+With no --workload, one JSON line per large workload is printed: wide
+(B8 T2048 D2560 bf16), long32 (B4 T8192 D4096 fp32), longseq (B1 T131072
+D1024 bf16) and, last, masked (B16 T4096 D2560 bf16, padding and reset
+steps), the largest by elements.  Each line's `value` is the effective HBM
+bandwidth of the whole step: the algorithmic bytes (forward 3*s*N + 4*B*D,
+backward 5*s*N, s the I/O element size, N = B*T*D) divided by the mean step
+time over K steps, each timed with HIP events with the Infinity Cache flushed
+before it (a 1 GiB read outside the events).  Beside it: the same steps back
+to back ("warm"), the forward and backward kernels' mean durations inside the
+timed steps (the dominant one's roofline), the achievable ceiling of plain
+streaming kernels with the step's access pattern on the same arrays, timed
+the same way, and the fp64 oracle's rate on a bounded sample on the host.
 """
 from __future__ import annotations
 
@@ -117,28 +122,30 @@ def timed_sample(fn, budget_s):
 
 
 def cpu_baseline(inp, budget_s=10.0):
-    """The fp64 oracle on the host cores, on the same workload (whole, or as
-    many whole passes as fit in about `budget_s`).  Returns a dict."""
+    """The fp64 oracle on the host cores, on a bounded sample of the same
+    workload: batch row 0 (every step and lane of it), fwd+bwd, repeated for
+    about `budget_s`; one pass on a single thread over the first lanes of row
+    0 beside it.  Returns a dict."""
     import oracle
+
+    import workloads as W
 
     wl = inp.workload
     cores = min(16, len(os.sched_getaffinity(0)))
-    a, b, g = inp.f64("a"), inp.f64("b"), inp.f64("g")
-    reps, t_total = 0, 0.0
-    while True:
-        t0 = time.perf_counter()
-        h, _ = oracle.scan_fwd(a, b, threads=cores)
-        oracle.scan_bwd(a, h, g, threads=cores)
-        t_total += time.perf_counter() - t0
-        reps += 1
-        if t_total >= budget_s or reps >= 200:
-            break
-    # one pass on a single core beside it
+    a, b, g = (W.storage_to_f64(getattr(inp, n)[:1], wl.dtype) for n in ("a", "b", "g"))
+
+    def run(x, y, z, threads):
+        h, _ = oracle.scan_fwd(x, y, threads=threads)
+        oracle.scan_bwd(x, h, z, threads=threads)
+    reps, t_total = timed_sample(lambda: run(a, b, g, cores), budget_s)
+    # one pass on a single core over the first lanes of row 0
+    d1 = min(wl.D, 256)
+    a1, b1, g1 = (np.ascontiguousarray(x[:, :, :d1]) for x in (a, b, g))
     t0 = time.perf_counter()
-    h, _ = oracle.scan_fwd(a, b, threads=1)
-    oracle.scan_bwd(a, h, g, threads=1)
+    run(a1, b1, g1, 1)
     t_one = time.perf_counter() - t0
-    fb, bb = algorithmic_bytes(wl.B, wl.T, wl.D, wl.itemsize)
+    fb, bb = algorithmic_bytes(1, wl.T, wl.D, wl.itemsize)
+    f1, b1b = algorithmic_bytes(1, wl.T, d1, wl.itemsize)
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -153,11 +160,13 @@ def cpu_baseline(inp, budget_s=10.0):
         "unit": "GB/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"the whole {wl.name} workload, fwd+bwd, {reps} pass(es) in {t_total:.1f} s "
-                  f"(fp64, {cores} threads over lanes; input conversion untimed)",
-        "elements_per_s": round(wl.N * reps / t_total, 1),
-        "single_core": {"value": round((fb + bb) / t_one / 1e9, 3), "unit": "GB/s",
-                        "sample": f"one fwd+bwd pass in {t_one:.1f} s on 1 thread"},
+        "sample": f"batch row 0 of the {wl.name} workload ([1, {wl.T}, {wl.D}]), fwd+bwd, "
+                  f"{reps} pass(es) in {t_total:.1f} s (fp64, {cores} threads over lanes; "
+                  f"input conversion untimed)",
+        "elements_per_s": round(wl.T * wl.D * reps / t_total, 1),
+        "single_core": {"value": round((f1 + b1b) / t_one / 1e9, 3), "unit": "GB/s",
+                        "sample": f"lanes 0..{d1 - 1} of batch row 0, one fwd+bwd pass in "
+                                  f"{t_one:.2f} s on 1 thread"},
         "host": {"cpu_model": model, "hardware_threads": os.cpu_count()},
     }
 
@@ -497,63 +506,55 @@ def inference_cpu_baseline(inp, mode, budget_s=8.0):
             "sample": f"{what}, {reps} pass(es) in {t:.1f} s (fp64, {cores} threads over lanes)"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="wide")
-    ap.add_argument("--algo", default="auto")
-    ap.add_argument("--fwd-chunk", type=int, default=0)
-    ap.add_argument("--bwd-chunk", type=int, default=0)
-    ap.add_argument("--fwd-width", type=int, default=0)
-    ap.add_argument("--bwd-width", type=int, default=0)
-    ap.add_argument("--mode", default="train", choices=["train", "prefill", "decode"],
-                    help="train: forward + backward (the default line); prefill: the state-only "
-                         "forward (reads a and b, writes last); decode: one scan_step per token "
-                         "on the workload's [B, D] lanes")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain 1 GiB device copy (the reference for HBM byte counters)")
-    args = ap.parse_args()
+class StreamCeiling:
+    """Plain streaming kernels (libstreamceil.so, built beside liblrscan.so)
+    with the scan's access patterns: read 2 / write 1 and read 3 / write 2."""
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this benchmark measures one GPU; the scan is built and "
-                                   "measured on a single MI355X (run with --gpus 1)"}))
-        sys.exit(2)
+    def __init__(self):
+        import ctypes
 
-    import torch
+        import linear_recurrence_sequence_diag_amd as lr
+        path = os.path.join(os.path.dirname(lr.LIB_PATH), "libstreamceil.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built; run "
+                              "`python -m linear_recurrence_sequence_diag_amd.build`")
+        self.lib = ctypes.CDLL(path)
+        P = ctypes.c_void_p
+        self.lib.stream_ceiling_run.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, P,
+                                                ctypes.c_size_t, P]
+        self.lib.stream_ceiling_run.restype = ctypes.c_int
 
-    import linear_recurrence_sequence_diag_amd as lr
-    import workloads as W
+    def run(self, pattern, unroll, ins, outs, nbytes, stream):
+        p = [t.data_ptr() for t in ins] + [None] * (3 - len(ins))
+        q = [t.data_ptr() for t in outs] + [None] * (2 - len(outs))
+        rc = self.lib.stream_ceiling_run(pattern, unroll, p[0], p[1], p[2], q[0], q[1], nbytes,
+                                         stream)
+        if rc != 0:
+            raise RuntimeError(f"stream_ceiling_run failed ({rc})")
 
-    lr.library()  # fails loudly if the HIP library is not built
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
-        sys.exit(2)
 
-    if args.calibrate_copy:
-        # A plain copy of known size: its HBM byte counters (FETCH_SIZE, WRITE_SIZE)
-        # give the factor that turns counter readings into bytes.
-        n = 1 << 28
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibration": "copy", "bytes_read_per_copy": 4 * n,
-                          "bytes_written_per_copy": 4 * n, "copies": args.steps}))
-        return
+def cold_times(torch, stream, fns, steps, flush):
+    """Each of `steps` repetitions: flush the caches (outside the events),
+    then run fns in order with a HIP event before, between and after them on
+    `stream`.  Returns one list of durations (ms) per fn."""
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+          for _ in range(steps)]
+    for k in range(steps):
+        flush()
+        ev[k][0].record(stream)
+        for i, f in enumerate(fns):
+            f()
+            ev[k][i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [[ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)] for i in range(len(fns))]
 
-    if args.workload in W.COMPLEX_WORKLOADS:
-        print(json.dumps(complex_line(args, W.COMPLEX_WORKLOADS[args.workload], lr, torch, W)),
-              flush=True)
-        return
-    if args.workload in W.SAMU_WORKLOADS:
-        print(json.dumps(samu_line(args, W.SAMU_WORKLOADS[args.workload], lr, torch, W)),
-              flush=True)
-        return
-    wl = W.WORKLOADS[args.workload]
+
+DEFAULT_WORKLOADS = ("wide", "long32", "longseq", "masked")
+
+
+def train_line(args, name, lr, torch, W, cpu_budget):
+    """JSON line of the fwd+bwd step on one of the named real workloads."""
+    wl = W.WORKLOADS[name]
     inp = W.generate(wl, seed=0)
     dt = lr.F32 if wl.dtype == "f32" else lr.BF16
 
@@ -565,8 +566,7 @@ def main():
     a, b, g = dev(inp.a), dev(inp.b), dev(inp.g)
     B, T, D = wl.B, wl.T, wl.D
     if args.mode != "train":
-        print(json.dumps(inference_line(args, wl, lr, torch, a, b, dt, inp)), flush=True)
-        return
+        return inference_line(args, wl, lr, torch, a, b, dt, inp)
     out = torch.empty_like(a)
     ga = torch.empty_like(a)
     gb = torch.empty_like(a)
@@ -584,71 +584,59 @@ def main():
         lr.scan_bwd_ex(a.data_ptr(), out.data_ptr(), g.data_ptr(), None, ga.data_ptr(),
                        gb.data_ptr(), B, T, D, dt, sh, bo)
 
+    # the cache flush: a 1 GiB read, four times the 256 MB Infinity Cache (a
+    # read leaves clean lines, so the timed step pays no write-back for it)
+    scrub = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
+    scrub_sum = torch.empty((), device="cuda", dtype=torch.float32)
+
+    def flush():
+        torch.sum(scrub, dim=0, out=scrub_sum)
+
     for _ in range(args.warmup):
         fwd()
         bwd()
     torch.cuda.synchronize()
 
-    # timed region: K whole steps back to back, HIP events on the launch stream
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
+    # timed region: K steps, the caches flushed before each, HIP events on the
+    # launch stream before, between and after the two calls (each call is
+    # one kernel launch with the automatic choice)
+    fwd_t, bwd_t = cold_times(torch, stream, [fwd, bwd], args.steps, flush)
+    step_t = [x + y for x, y in zip(fwd_t, bwd_t)]
+    ms_per_step = sum(step_t) / len(step_t)
+    fwd_ms = sum(fwd_t) / len(fwd_t)
+    bwd_ms = sum(bwd_t) / len(bwd_t)
+
+    # the same steps back to back (inputs partly left in the Infinity Cache)
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
     for _ in range(args.steps):
         fwd()
         bwd()
-    t_end.record(stream)
+    w1.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-
-    # per-kernel average launch duration: K launches of one direction back to
-    # back between two events (each call is one kernel launch)
-    def kernel_ms(fn):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / args.steps
-
-    fwd_ms = kernel_ms(fwd)
-    bwd_ms = kernel_ms(bwd)
-
-    # each launch timed on its own (median and min over K), and whole steps
-    # with the Infinity Cache flushed before each ("cold": a 1 GiB read between
-    # steps, outside the timed events; a read leaves clean lines, so the step
-    # pays no write-back of the flush)
-    def per_launch(fn, flush=None):
-        ts = []
-        for _ in range(args.steps):
-            if flush is not None:
-                flush()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        ts.sort()
-        return ts[len(ts) // 2], ts[0]
-
-    scrub = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
-    scrub_sum = torch.empty((), device="cuda", dtype=torch.float32)
-    fwd_med, fwd_min = per_launch(fwd)
-    bwd_med, bwd_min = per_launch(bwd)
-    cold_med, cold_min = per_launch(lambda: (fwd(), bwd()),
-                                    flush=lambda: torch.sum(scrub, dim=0, out=scrub_sum))
-    # achievable streaming ceiling: a 1 GiB device copy (read + write), the
-    # runtime's copy kernel, larger than the Infinity Cache
-    src_c = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
-    copy_ms = min(kernel_ms(lambda: scrub.copy_(src_c)) for _ in range(2))
-    copy_gbps = 2 * src_c.numel() * 4 / (copy_ms * 1e-3) / 1e9
-    del scrub, scrub_sum, src_c
+    warm_ms = w0.elapsed_time(w1) / args.steps
 
     fb, bb = algorithmic_bytes(B, T, D, wl.itemsize)
     value = (fb + bb) / (ms_per_step * 1e-3) / 1e9
+
+    # achievable ceiling: streaming kernels with the step's access pattern on
+    # the same arrays (forward: a, b -> out; backward: a, out, grad_out ->
+    # grad_a, grad_b), timed like the step; the best of three unroll depths
+    ceil = StreamCeiling()
+    nb = a.numel() * a.element_size()
+    best = None
+    for u in (2, 4, 8):
+        tf, tb = cold_times(torch, stream,
+                            [lambda: ceil.run(1, u, [a, b], [out], nb, sh),
+                             lambda: ceil.run(2, u, [a, out, g], [ga, gb], nb, sh)],
+                            args.steps, flush)
+        c = (sum(tf) / len(tf), sum(tb) / len(tb), u)
+        if best is None or c[0] + c[1] < best[0] + best[1]:
+            best = c
+    ceil_gbps = (fb + bb) / ((best[0] + best[1]) * 1e-3) / 1e9
+    del scrub, scrub_sum
+
     fwd_algo, fwd_chunk, fwd_width = lr.scan_auto_algo(B, T, D, dt, 0)
     bwd_algo, bwd_chunk, bwd_width = lr.scan_auto_algo(B, T, D, dt, 1)
     if args.algo != "auto":
@@ -664,9 +652,9 @@ def main():
             return f"chunked(chunk {chunk})"
         return names[algo]
     if bwd_ms >= fwd_ms:
-        dom, dom_ms, dom_bytes = "backward", bwd_ms, bb
+        dom, dom_ms, dom_bytes, dom_algo = "backward", bwd_ms, bb, names[bwd_algo]
     else:
-        dom, dom_ms, dom_bytes = "forward", fwd_ms, fb
+        dom, dom_ms, dom_bytes, dom_algo = "forward", fwd_ms, fb, names[fwd_algo]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
 
     res = {
@@ -691,29 +679,113 @@ def main():
         },
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "elements_per_s": round(wl.N / (ms_per_step * 1e-3), 1),
+        "timing": "mean over K steps, each with the Infinity Cache flushed before it "
+                  "(a 1 GiB read outside the events)",
         "fwd_us": round(fwd_ms * 1e3, 2),
         "bwd_us": round(bwd_ms * 1e3, 2),
-        "per_launch_us": {"fwd_median": round(fwd_med * 1e3, 2), "fwd_min": round(fwd_min * 1e3, 2),
-                          "bwd_median": round(bwd_med * 1e3, 2), "bwd_min": round(bwd_min * 1e3, 2)},
-        "cold": {"ms_per_step_median": round(cold_med, 5), "ms_per_step_min": round(cold_min, 5),
-                 "value": round((fb + bb) / (cold_med * 1e-3) / 1e9, 2),
-                 "note": "1 GiB read before each step, outside the timed events"},
-        "ceiling": {"kernel": "device copy of 1 GiB (read + write)",
-                    "GB/s": round(copy_gbps, 1), "value_frac": round(value / copy_gbps, 4)},
+        "fwd_GBps": round(fb / (fwd_ms * 1e-3) / 1e9, 1),
+        "bwd_GBps": round(bb / (bwd_ms * 1e-3) / 1e9, 1),
+        "step_ms_min": round(min(step_t), 5),
+        "warm": {"ms_per_step": round(warm_ms, 5),
+                 "value": round((fb + bb) / (warm_ms * 1e-3) / 1e9, 2),
+                 "note": "K steps back to back, no flush"},
+        "ceiling": {"kernel": "streaming kernels with the step's access pattern on the same "
+                              "arrays (read 2 / write 1, read 3 / write 2), timed like the step",
+                    "GB/s": round(ceil_gbps, 1),
+                    "fwd_pattern_us": round(best[0] * 1e3, 2),
+                    "bwd_pattern_us": round(best[1] * 1e3, 2),
+                    "unroll": best[2],
+                    "value_frac": round(value / ceil_gbps, 4)},
         "roofline": {
             "bound": "hbm",
-            "kernel": f"{dom} scan ({names[bwd_algo if dom == 'backward' else fwd_algo]})",
+            "kernel": f"{dom} scan ({dom_algo})",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name, dom, dom_algo),
         },
     }
-    res["roofline"]["traffic"] = measured_traffic(wl.name, dom, names[bwd_algo if dom == "backward" else fwd_algo])
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp)
-    print(json.dumps(res), flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, cpu_budget)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="default",
+                    help="default: wide, long32, longseq, then masked (one line each, masked "
+                         "last); or one of " + ", ".join(WORKLOAD_TEXT))
+    ap.add_argument("--algo", default="auto")
+    ap.add_argument("--fwd-chunk", type=int, default=0)
+    ap.add_argument("--bwd-chunk", type=int, default=0)
+    ap.add_argument("--fwd-width", type=int, default=0)
+    ap.add_argument("--bwd-width", type=int, default=0)
+    ap.add_argument("--mode", default="train", choices=["train", "prefill", "decode"],
+                    help="train: forward + backward (the default line); prefill: the state-only "
+                         "forward (reads a and b, writes last); decode: one scan_step per token "
+                         "on the workload's [B, D] lanes")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run kernels of known traffic (a 1 GiB device copy and the "
+                         "read-2/write-1 streaming kernel on 3 x 256 MiB), the reference for "
+                         "HBM byte counters")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU; the scan is built and "
+                                   "measured on a single MI355X (run with --gpus 1)"}))
+        sys.exit(2)
+
+    import torch
+
+    import linear_recurrence_sequence_diag_amd as lr
+    import workloads as W
+
+    lr.library()  # fails loudly if the HIP library is not built
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+
+    if args.calibrate:
+        # Kernels of known size: their HBM byte counters (FETCH_SIZE,
+        # WRITE_SIZE) give the factors that turn counter readings into bytes.
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        x = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        y = torch.ones_like(x)
+        z = torch.empty_like(x)
+        ceil = StreamCeiling()
+        sh = torch.cuda.current_stream().cuda_stream
+        for _ in range(args.steps):
+            ceil.run(1, 4, [x, y], [z], x.numel() * 4, sh)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy and stream",
+                          "copy": {"bytes_read": 4 * n, "bytes_written": 4 * n},
+                          "stream_read2_write1": {"bytes_read": 2 * n, "bytes_written": n},
+                          "repetitions": args.steps}))
+        return
+
+    if args.workload in W.COMPLEX_WORKLOADS:
+        print(json.dumps(complex_line(args, W.COMPLEX_WORKLOADS[args.workload], lr, torch, W)),
+              flush=True)
+        return
+    if args.workload in W.SAMU_WORKLOADS:
+        print(json.dumps(samu_line(args, W.SAMU_WORKLOADS[args.workload], lr, torch, W)),
+              flush=True)
+        return
+    names = DEFAULT_WORKLOADS if args.workload == "default" else (args.workload,)
+    for i, name in enumerate(names):
+        final = i == len(names) - 1
+        print(json.dumps(train_line(args, name, lr, torch, W, 10.0 if final else 5.0)),
+              flush=True)
+        torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

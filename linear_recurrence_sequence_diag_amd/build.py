@@ -4,6 +4,11 @@ Every ``csrc/*.hip`` file is compiled by hipcc for gfx950 into an object and
 the objects are linked into ``liblrscan.so`` next to this file.  Only the
 symbols marked LRSCAN_API in ``include/lrscan.h`` are exported.
 
+``measure/stream_ceiling.hip`` is built the same way into
+``libstreamceil.so``: plain streaming kernels with the scan's access
+patterns, which only the benchmark loads (the achievable-bandwidth ceiling it
+reports beside the scan).
+
     python -m linear_recurrence_sequence_diag_amd.build
 """
 from __future__ import annotations
@@ -18,6 +23,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblrscan.so")
+MEASURE = os.path.join(HERE, "measure")
+CEILING_LIB = os.path.join(HERE, "libstreamceil.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 HIP_FLAGS = [
@@ -49,21 +56,28 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every HIP source and link liblrscan.so.  Always rebuilds."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    workers = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
-    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = True) -> str:
+    """Compile every HIP source and link liblrscan.so and libstreamceil.so.
+    Always rebuilds."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sources()
+    ceiling_src = os.path.join(MEASURE, "stream_ceiling.hip")
+    workers = min(len(srcs) + 1, max(1, min(16, os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(_compile, srcs + [ceiling_src]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], CEILING_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING_LIB}")
     return LIB
 
 

@@ -281,3 +281,37 @@ def test_caller_workspace_and_errors():
         with pytest.raises(lr.LRScanError):
             lr.scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), None, B, T, D, lr.BF16,
                            torch.cuda.current_stream().cuda_stream, small)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_plain_entry_points_on_data(dt):
+    """The two entry points the boundary is named by, scan_fwd and scan_bwd
+    (no options: the automatic choice), on a ragged shape with grad_last,
+    against the oracle element by element; and bitwise equal to scan_fwd_ex /
+    scan_bwd_ex with the same automatic choice."""
+    inp, h0, gl = W.random_inputs(3, 5000, 300, dt, seed=91, a_lo=0.5, a_hi=0.999,
+                                  with_state=True)
+    a, b, g = dev(inp.a, dt), dev(inp.b, dt), dev(inp.g, dt)
+    tgl = dev_f32(gl)
+    B, T, D = a.shape
+    code = lr.dtype_code(a.dtype)
+    sh = torch.cuda.current_stream().cuda_stream
+    out, ga, gb = torch.empty_like(a), torch.empty_like(a), torch.empty_like(a)
+    last = torch.empty((B, D), device="cuda", dtype=torch.float32)
+    assert lr.scan_fwd(a.data_ptr(), b.data_ptr(), out.data_ptr(), last.data_ptr(), B, T, D, code,
+                       sh) == 0
+    assert lr.scan_bwd(a.data_ptr(), out.data_ptr(), g.data_ptr(), tgl.data_ptr(), ga.data_ptr(),
+                       gb.data_ptr(), B, T, D, code, sh) == 0
+    torch.cuda.synchronize()
+    a64, b64, g64 = inp.f64("a"), inp.f64("b"), inp.f64("g")
+    h, hl = oracle.scan_fwd(a64, b64)
+    oga, ogb, _ = oracle.scan_bwd(a64, h, g64, grad_last=gl)
+    r = [check_close("out", host(out), h, dt), check_close("last", host(last), hl, "f32"),
+         check_close("grad_b", host(gb), ogb, dt),
+         check_grad_a(host(ga), oga, ogb, prev_state(h), dt)]
+    ex_out, ex_last = lr.scan(a, b)
+    ex_ga, ex_gb, _ = lr.scan_backward(a, ex_out, g, grad_last=tgl)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ex_out) and torch.equal(last, ex_last)
+    assert torch.equal(ga, ex_ga) and torch.equal(gb, ex_gb)
+    log(f"plain scan_fwd/scan_bwd {dt}: worst err/tol {max(r):.3f}")
