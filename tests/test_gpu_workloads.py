@@ -18,6 +18,19 @@ of tests/_gpu.py).  Logged beside each check: the worst err/tol, the number
 of grad_a elements outside the literal (unpropagated) bound, and the global
 metric max|err| / max|ref|.
 
+bf16 I/O adds the fp32 accumulation floor 4*u*M (u = 2^-24) to the bounds
+of out and grad_b.  M is the absolute accumulation of the recurrence at that
+element, the same scan run on the magnitudes of its results:
+M_t = |h_t| + a_t*M_{t-1} forward, |lambda_t| + a_{t+1}*M_{t+1} backward
+(fp64, by the oracle).  One fp32 rounding per step (the sequential form's
+single fma) leaves a first-order error of at most u*M; the tiled forms
+round a few times per step (summary, composition, replay), hence the factor
+4.  Without it a relative bound cannot hold where the state cancels to
+nearly zero: on longseq, sums of magnitude ~100 cancel to ~1e-5, and 2 of
+134M grad_b elements of the fused form (worst: exact 6.1e-5, error 1.13e-5,
+about 1.5 fp32 ulps of the running sums) fall outside 1e-5 + 1e-2*|ref|,
+where the per-lane walk itself reaches 0.996 of that bound.
+
 Also checked on every element: the final state against the last stored row;
 chunked against sequential (long32, within the fp32 bound, max |seq -
 chunked| logged); and on the masked workload the reset and padding
@@ -126,6 +139,9 @@ class Tally:
                                f"(row, t, d, got, ref) = {self.worst}")
 
 
+U32 = 2.0 ** -24  # fp32 unit roundoff
+
+
 def compare_with_oracle(name, path, inp, out, last, ga, gb):
     wl = inp.workload
     dt = wl.dtype
@@ -138,15 +154,23 @@ def compare_with_oracle(name, path, inp, out, last, ga, gb):
         h, hl = oracle.scan_fwd(a, b, threads=THREADS)
         oga, ogb, _ = oracle.scan_bwd(a, h, g, threads=THREADS)
         del b, g
-        tallies["out"].add(host(out[bi:bi + 1]), h, atol + rtol * np.abs(h), where=(bi,))
+        if dt == "bf16":  # the fp32 accumulation floor (module docstring)
+            fh = 4 * U32 * oracle.scan_fwd(a, np.abs(h), threads=THREADS)[0]
+            fl = 4 * U32 * oracle.scan_bwd(a, h, np.abs(ogb), threads=THREADS)[1]
+        else:
+            fh = fl = 0.0
+        tallies["out"].add(host(out[bi:bi + 1]), h, atol + rtol * np.abs(h) + fh, where=(bi,))
         tallies["last"].add(host(last[bi:bi + 1]), hl, 1e-5 + 1e-5 * np.abs(hl), where=(bi,))
-        tallies["grad_b"].add(host(gb[bi:bi + 1]), ogb, atol + rtol * np.abs(ogb), where=(bi,))
+        tallies["grad_b"].add(host(gb[bi:bi + 1]), ogb, atol + rtol * np.abs(ogb) + fl,
+                              where=(bi,))
         hp = prev_state(h)
+        fhp = prev_state(fh) if dt == "bf16" else 0.0
         del h, a
         tallies["grad_a"].add(host(ga[bi:bi + 1]), oga,
-                              atol * (1 + np.abs(ogb) + np.abs(hp)) + 2 * rtol * np.abs(oga),
+                              atol * (1 + np.abs(ogb) + np.abs(hp)) + 2 * rtol * np.abs(oga)
+                              + fl * np.abs(hp) + fhp * np.abs(ogb),
                               literal_tol=atol + rtol * np.abs(oga), where=(bi,))
-        del hp, oga, ogb
+        del hp, oga, ogb, fh, fl, fhp
     for t in tallies.values():
         log(f"{name} {path}: {t.report()}")
     for t in tallies.values():
@@ -184,7 +208,16 @@ def test_full_size_every_element(name, path):
         inner = pad.clone()
         inner[:, 0] = False
         prev = torch.roll(out, 1, dims=1)
-        assert torch.equal(out[inner], prev[inner])  # a padding step carries the state bit for bit
+        # a padding step carries the state: equal up to the bf16 rounding of two
+        # fp32 copies of the same state (a row that starts a thread's segment
+        # gets it from the composed tile maps, the row before it from the
+        # previous thread's replay); the oracle check below compares every
+        # padding element with the exact carried state
+        po, pp = out[inner].float(), prev[inner].float()
+        n_diff = int((po != pp).sum())
+        assert bool(((po - pp).abs() <= 1e-5 + 1e-2 * torch.maximum(po.abs(), pp.abs())).all())
+        log(f"masked {path}: {n_diff} of {po.numel()} padding outputs not bitwise equal to the "
+            f"row before (all within the bf16 bound)")
         # no adjoint crosses a reset: grad_a = lambda * h_prev there, and the
         # carry to the left is a_r * lambda_r = 0, so grad_b just left of a
         # reset is g there plus nothing from the right
