@@ -508,7 +508,8 @@ def inference_cpu_baseline(inp, mode, budget_s=8.0):
 
 class StreamCeiling:
     """Plain streaming kernels (libstreamceil.so, built beside liblrscan.so)
-    with the scan's access patterns: read 2 / write 1 and read 3 / write 2."""
+    with the scan's access patterns: read 2 / write 1 and read 3 / write 2,
+    non-temporal stores, each input loaded normally or non-temporally."""
 
     def __init__(self):
         import ctypes
@@ -520,15 +521,15 @@ class StreamCeiling:
                               "`python -m linear_recurrence_sequence_diag_amd.build`")
         self.lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
-        self.lib.stream_ceiling_run.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, P,
-                                                ctypes.c_size_t, P]
+        self.lib.stream_ceiling_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P,
+                                                P, P, ctypes.c_size_t, P]
         self.lib.stream_ceiling_run.restype = ctypes.c_int
 
-    def run(self, pattern, unroll, ins, outs, nbytes, stream):
+    def run(self, pattern, unroll, nt_mask, ins, outs, nbytes, stream):
         p = [t.data_ptr() for t in ins] + [None] * (3 - len(ins))
         q = [t.data_ptr() for t in outs] + [None] * (2 - len(outs))
-        rc = self.lib.stream_ceiling_run(pattern, unroll, p[0], p[1], p[2], q[0], q[1], nbytes,
-                                         stream)
+        rc = self.lib.stream_ceiling_run(pattern, unroll, nt_mask, p[0], p[1], p[2], q[0], q[1],
+                                         nbytes, stream)
         if rc != 0:
             raise RuntimeError(f"stream_ceiling_run failed ({rc})")
 
@@ -623,17 +624,21 @@ def train_line(args, name, lr, torch, W, cpu_budget):
     # achievable ceiling: streaming kernels with the step's access pattern on
     # the same arrays (forward: a, b -> out; backward: a, out, grad_out ->
     # grad_a, grad_b), timed like the step; the best of three unroll depths
+    # and three load policies (every input normal; the scan's policy: the
+    # forward's b non-temporal, everything the backward reads non-temporal;
+    # every input non-temporal)
     ceil = StreamCeiling()
     nb = a.numel() * a.element_size()
     best = None
-    for u in (2, 4, 8):
-        tf, tb = cold_times(torch, stream,
-                            [lambda: ceil.run(1, u, [a, b], [out], nb, sh),
-                             lambda: ceil.run(2, u, [a, out, g], [ga, gb], nb, sh)],
-                            args.steps, flush)
-        c = (sum(tf) / len(tf), sum(tb) / len(tb), u)
-        if best is None or c[0] + c[1] < best[0] + best[1]:
-            best = c
+    for u in (1, 2, 4):
+        for fm, bm in ((0, 0), (2, 7), (7, 7)):
+            tf, tb = cold_times(torch, stream,
+                                [lambda: ceil.run(1, u, fm, [a, b], [out], nb, sh),
+                                 lambda: ceil.run(2, u, bm, [a, out, g], [ga, gb], nb, sh)],
+                                args.steps, flush)
+            c = (sum(tf) / len(tf), sum(tb) / len(tb), u, fm, bm)
+            if best is None or c[0] + c[1] < best[0] + best[1]:
+                best = c
     ceil_gbps = (fb + bb) / ((best[0] + best[1]) * 1e-3) / 1e9
     del scrub, scrub_sum
 
@@ -695,6 +700,8 @@ def train_line(args, name, lr, torch, W, cpu_budget):
                     "fwd_pattern_us": round(best[0] * 1e3, 2),
                     "bwd_pattern_us": round(best[1] * 1e3, 2),
                     "unroll": best[2],
+                    "load_policy": {0: "normal", 2: "b non-temporal", 7: "non-temporal"}[best[3]]
+                                   + " / " + {0: "normal", 7: "non-temporal"}[best[4]],
                     "value_frac": round(value / ceil_gbps, 4)},
         "roofline": {
             "bound": "hbm",
@@ -764,7 +771,7 @@ def main():
         ceil = StreamCeiling()
         sh = torch.cuda.current_stream().cuda_stream
         for _ in range(args.steps):
-            ceil.run(1, 4, [x, y], [z], x.numel() * 4, sh)
+            ceil.run(1, 4, 0, [x, y], [z], x.numel() * 4, sh)
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "copy and stream",
                           "copy": {"bytes_read": 4 * n, "bytes_written": 4 * n},

@@ -160,8 +160,8 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
         const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
         ar[i] = load_vec<C::DT, ALIGNED>(par, off, g.nvalid, 1.0f);
         ai[i] = load_vec<C::DT, ALIGNED>(pai, off, g.nvalid, 0.0f);
-        br[i] = load_vec<C::DT, ALIGNED>(pbr, off, g.nvalid, 0.0f);
-        bi[i] = load_vec<C::DT, ALIGNED>(pbi, off, g.nvalid, 0.0f);
+        br[i] = load_vec<C::DT, ALIGNED, true>(pbr, off, g.nvalid, 0.0f);
+        bi[i] = load_vec<C::DT, ALIGNED, true>(pbi, off, g.nvalid, 0.0f);
     }
     if constexpr (RST) {
 #pragma unroll
@@ -316,10 +316,10 @@ void cx_fused_bwd_kernel(CxBwdArgs x) {
 #pragma unroll
     for (int i = NR - 1; i >= 0; --i) {  // last row first: the reverse summary's order
         const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
-        ar[i] = load_vec<C::DT, ALIGNED>(par, off, g.nvalid, 1.0f);
-        ai[i] = load_vec<C::DT, ALIGNED>(pai, off, g.nvalid, 0.0f);
-        gr[i] = load_vec<C::DT, ALIGNED>(pgr, off, g.nvalid, 0.0f);
-        gi[i] = load_vec<C::DT, ALIGNED>(pgi, off, g.nvalid, 0.0f);
+        ar[i] = load_vec<C::DT, ALIGNED, true>(par, off, g.nvalid, 1.0f);
+        ai[i] = load_vec<C::DT, ALIGNED, true>(pai, off, g.nvalid, 0.0f);
+        gr[i] = load_vec<C::DT, ALIGNED, true>(pgr, off, g.nvalid, 0.0f);
+        gi[i] = load_vec<C::DT, ALIGNED, true>(pgi, off, g.nvalid, 0.0f);
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the load order as written
     // the rows of `out` last: only the replay uses them
@@ -329,8 +329,8 @@ void cx_fused_bwd_kernel(CxBwdArgs x) {
         const int rc = row < d.T ? row : d.T - 1;
         const int hrw = rc >= 1 ? rc - 1 : 0;
         const uint32_t hoff = (uint32_t)(hrw - hrow0) * rowbytes + g.coff;
-        hr[i] = load_vec<C::DT, ALIGNED>(phr, hoff, g.nvalid, 0.0f);
-        hi[i] = load_vec<C::DT, ALIGNED>(phi, hoff, g.nvalid, 0.0f);
+        hr[i] = load_vec<C::DT, ALIGNED, true>(phr, hoff, g.nvalid, 0.0f);
+        hi[i] = load_vec<C::DT, ALIGNED, true>(phi, hoff, g.nvalid, 0.0f);
     }
     __builtin_amdgcn_sched_barrier(0);
     // at a segment start a_t is not used: transition 0, grad_a_t = 0

@@ -223,8 +223,8 @@ void fused_fwd_kernel(FwdArgs x) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
-        ra[i] = load_vec<C::DT, ALIGNED>(pa, off, g.nvalid, 1.0f);
-        rb[i] = load_vec<C::DT, ALIGNED>(pb, off, g.nvalid, 0.0f);
+        ra[i] = load_vec<C::DT, ALIGNED, false>(pa, off, g.nvalid, 1.0f);
+        rb[i] = load_vec<C::DT, ALIGNED, true>(pb, off, g.nvalid, 0.0f);
     }
     if constexpr (RST) {
         // a segment start drops the entering state: its transition becomes 0
@@ -380,8 +380,8 @@ void fused_bwd_kernel(BwdArgs x) {
 #pragma unroll
     for (int i = NR - 1; i >= 0; --i) {
         const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
-        ra[i] = load_vec<C::DT, ALIGNED>(pa, off, g.nvalid, 1.0f);
-        rg_[i] = load_vec<C::DT, ALIGNED>(pg, off, g.nvalid, 0.0f);
+        ra[i] = load_vec<C::DT, ALIGNED, true>(pa, off, g.nvalid, 1.0f);
+        rg_[i] = load_vec<C::DT, ALIGNED, true>(pg, off, g.nvalid, 0.0f);
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -390,7 +390,7 @@ void fused_bwd_kernel(BwdArgs x) {
         const int rc = row < d.T ? row : d.T - 1;
         const int hr = rc >= 1 ? rc - 1 : 0;
         const uint32_t hoff = (uint32_t)(hr - hrow0) * rowbytes + g.coff;
-        rh[i] = load_vec<C::DT, ALIGNED>(ph, hoff, g.nvalid, 0.0f);
+        rh[i] = load_vec<C::DT, ALIGNED, true>(ph, hoff, g.nvalid, 0.0f);
     }
     __builtin_amdgcn_sched_barrier(0);
     // at a segment start a_t is not used: its transition is 0 (no adjoint

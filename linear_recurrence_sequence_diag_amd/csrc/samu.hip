@@ -201,8 +201,8 @@ void samu_fwd_kernel(SamuFwdArgs x) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
-        br[i] = load_vec<C::DT, ALIGNED>(pbr, off, g.nvalid, 0.0f);
-        bi[i] = load_vec<C::DT, ALIGNED>(pbi, off, g.nvalid, 0.0f);
+        br[i] = load_vec<C::DT, ALIGNED, true>(pbr, off, g.nvalid, 0.0f);
+        bi[i] = load_vec<C::DT, ALIGNED, true>(pbi, off, g.nvalid, 0.0f);
     }
     // per-token and per-mode factors of this thread's rows and lanes (rows
     // past T and lanes past M read the last valid one; never used)
@@ -390,8 +390,8 @@ void samu_bwd_kernel(SamuBwdArgs x) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
-        gr[i] = load_vec<C::DT, ALIGNED>(pgr, off, g.nvalid, 0.0f);
-        gi[i] = load_vec<C::DT, ALIGNED>(pgi, off, g.nvalid, 0.0f);
+        gr[i] = load_vec<C::DT, ALIGNED, true>(pgr, off, g.nvalid, 0.0f);
+        gi[i] = load_vec<C::DT, ALIGNED, true>(pgi, off, g.nvalid, 0.0f);
     }
     // the rows of `out` last: only the replay uses them
 #pragma unroll
@@ -400,8 +400,8 @@ void samu_bwd_kernel(SamuBwdArgs x) {
         const int rc = row < d.T ? row : d.T - 1;
         const int hrw = rc >= 1 ? rc - 1 : 0;
         const uint32_t hoff = (uint32_t)(hrw - hrow0) * rowbytes + g.coff;
-        hr[i] = load_vec<C::DT, ALIGNED>(phr, hoff, g.nvalid, 0.0f);
-        hi[i] = load_vec<C::DT, ALIGNED>(phi, hoff, g.nvalid, 0.0f);
+        hr[i] = load_vec<C::DT, ALIGNED, true>(phr, hoff, g.nvalid, 0.0f);
+        hi[i] = load_vec<C::DT, ALIGNED, true>(phi, hoff, g.nvalid, 0.0f);
     }
     SamuTok tok[NR];
     uint32_t rbits = 0;
