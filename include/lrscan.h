@@ -69,9 +69,14 @@ enum {
     LRSCAN_ERR_WORKSPACE = -5, /* workspace given but smaller than scan_workspace_bytes() */
     LRSCAN_ERR_HIP = -6,       /* the HIP runtime reported an error (launch or allocation) */
     LRSCAN_ERR_ALGO = -7,      /* unknown algorithm */
-    LRSCAN_ERR_CAPTURE = -8    /* the stream is capturing a graph and its library workspace is
+    LRSCAN_ERR_CAPTURE = -8,   /* the stream is capturing a graph and its library workspace is
                                   missing or too small (see "Graph capture" above) */
+    LRSCAN_ERR_TOO_BIG = -9    /* scan_fwd_noalloc: the call needs more scratch than its static
+                                  buffer holds */
 };
+
+/* Bytes of the static device scratch of scan_fwd_noalloc (per device). */
+#define LRSCAN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
 
 /* algorithms */
 enum {
@@ -142,6 +147,26 @@ LRSCAN_API int scan_fwd_ex(const void* a, const void* b, void* out, float* last,
 LRSCAN_API int scan_bwd_ex(const void* a, const void* out, const void* grad_out,
                            const float* grad_last, void* grad_a, void* grad_b, int64_t B,
                            int64_t T, int64_t D, int dtype, void* stream, const lrscan_opts* opts);
+
+/*
+ * scan_fwd_noalloc: scan_fwd_ex that allocates nothing, for callers that
+ * cannot call hipMalloc (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and algorithm
+ * choice as scan_fwd_ex; the caller still passes every input and output.
+ * Scratch comes from a static device array of LRSCAN_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) that each device holds for the life of the process; the part a
+ * call uses is initialised by a kernel inside the call.
+ *   opts->workspace must be NULL (else LRSCAN_ERR_WORKSPACE).  A call that
+ *   needs more scratch than the array holds returns LRSCAN_ERR_TOO_BIG and
+ *   enqueues nothing (scan_workspace_bytes gives a shape's need; the per-lane
+ *   walk, LRSCAN_ALGO_SEQ, needs none).
+ *   Every call on a device shares that device's array: calls that overlap in
+ *   time on one device (on different streams, or from different threads
+ *   without ordering) race and give wrong results.
+ */
+LRSCAN_API int scan_fwd_noalloc(const void* a, const void* b, void* out, float* last, int64_t B,
+                                int64_t T, int64_t D, int dtype, void* stream,
+                                const lrscan_opts* opts);
 
 /*
  * scan_step: one time step of the recurrence on [B, D] lanes, for decoding

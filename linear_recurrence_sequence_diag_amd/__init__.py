@@ -26,7 +26,7 @@ ALGOS = {"auto": ALGO_AUTO, "seq": ALGO_SEQ, "chunked": ALGO_CHUNKED, "fused": A
 STATUS = {
     0: "LRSCAN_OK", -1: "LRSCAN_ERR_NULL", -2: "LRSCAN_ERR_DIM", -3: "LRSCAN_ERR_DTYPE",
     -4: "LRSCAN_ERR_CHUNK", -5: "LRSCAN_ERR_WORKSPACE", -6: "LRSCAN_ERR_HIP", -7: "LRSCAN_ERR_ALGO",
-    -8: "LRSCAN_ERR_CAPTURE",
+    -8: "LRSCAN_ERR_CAPTURE", -9: "LRSCAN_ERR_TOO_BIG",
 }
 
 
@@ -59,6 +59,7 @@ _SIGS = {
     "scan_bwd": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P], _INT),
     "scan_fwd_ex": ([_P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
     "scan_bwd_ex": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
+    "scan_fwd_noalloc": ([_P, _P, _P, _P, _I64, _I64, _I64, _INT, _P, ctypes.POINTER(Opts)], _INT),
     "scan_workspace_bytes": ([_I64, _I64, _I64, _INT, ctypes.POINTER(Opts)], ctypes.c_size_t),
     "scan_status_string": ([_INT], ctypes.c_char_p),
     "scan_step": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P], _INT),
@@ -137,6 +138,12 @@ def scan_bwd_ex(a, out, grad_out, grad_last, grad_a, grad_b, B, T, D, dtype, str
     return _check(library().scan_bwd_ex(a, out, grad_out, grad_last, grad_a, grad_b, B, T, D, dtype,
                                         stream, ctypes.byref(opts) if opts is not None else None),
                   "scan_bwd_ex")
+
+
+def scan_fwd_noalloc(a, b, out, last, B, T, D, dtype, stream, opts):
+    return _check(library().scan_fwd_noalloc(a, b, out, last, B, T, D, dtype, stream,
+                                             ctypes.byref(opts) if opts is not None else None),
+                  "scan_fwd_noalloc")
 
 
 def scan_step(a, b, state_in, reset, out, state_out, B, D, dtype, stream):

@@ -344,6 +344,33 @@ int run_fwd(const FwdCall& c, const Resolved& r, const Workspace& ws) {
 
 }  // namespace
 
+namespace lrscan {
+
+// A forward call whose scratch comes from a fixed buffer of `cap` bytes that
+// `acquire` supplies (only when the chosen algorithm needs scratch): no
+// allocation, and the buffer is initialised inside the call.
+int fwd_on_fixed_scratch(const void* a, const void* b, void* out, float* last, int64_t B,
+                         int64_t T, int64_t D, int dtype, void* stream, const lrscan_opts* opts,
+                         size_t cap, int (*acquire)(void**)) {
+    if (opts && opts->workspace) return LRSCAN_ERR_WORKSPACE;
+    const FwdCall c{a, b, out, last, Shape{B, T, D, dtype}, static_cast<hipStream_t>(stream), opts};
+    Resolved r;
+    int st = check_fwd(c, &r);
+    if (st != LRSCAN_OK) return st;
+    const size_t need = needed_bytes(c.s, r);
+    if (need > cap) return LRSCAN_ERR_TOO_BIG;
+    Workspace ws;
+    if (need > 0) {
+        st = acquire(&ws.ptr);
+        if (st != LRSCAN_OK) return st;
+        ws.bytes = need;
+        ws.init = true;  // nothing carries over from the previous user of the buffer
+    }
+    return run_fwd(c, r, ws);
+}
+
+}  // namespace lrscan
+
 extern "C" {
 
 LRSCAN_API const char* scan_status_string(int status) {
@@ -356,6 +383,9 @@ LRSCAN_API const char* scan_status_string(int status) {
         case LRSCAN_ERR_WORKSPACE: return "workspace smaller than scan_workspace_bytes() or not 256-byte aligned";
         case LRSCAN_ERR_HIP: return "the HIP runtime reported an error";
         case LRSCAN_ERR_ALGO: return "unknown algorithm";
+        case LRSCAN_ERR_TOO_BIG:
+            return "the call needs more scratch than the static buffer of scan_fwd_noalloc "
+                   "(LRSCAN_NOALLOC_SCRATCH_BYTES) holds";
         case LRSCAN_ERR_CAPTURE:
             return "the stream is capturing a graph and has no library workspace of this size yet "
                    "(make one eager call of at least this size on the stream first, or pass "

@@ -54,7 +54,7 @@ def test_binding_names_match_the_abi():
 
 def test_status_strings():
     lr = _lib()
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         s = lr.status_string(code)
         assert isinstance(s, str) and s and s != "unknown status"
     assert lr.status_string(-99) == "unknown status"
