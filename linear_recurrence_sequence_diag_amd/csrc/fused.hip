@@ -11,9 +11,13 @@
 //    seg = wave*8 + l/8, NR consecutive rows each.  Each instruction thus
 //    reads 8 full 128-byte lines, and every load of the tile is issued before
 //    the first is used.
-//  * Summary: each thread folds its NR rows into one affine map per lane;
-//    the 8 segments of a wavefront are scanned with an in-wavefront scan, the
-//    wavefronts through LDS, giving the tile's map (P, Q) per lane.
+//  * Summary: each thread folds its NR rows (its segment) into one affine
+//    map per lane and writes it to LDS.  One wavefront then folds the
+//    segments of each lane in order, giving the tile's map (P, Q) per lane,
+//    and leaves in LDS, in place of each segment's map, the composition of
+//    the segments before it (an exclusive prefix).  (Folding in LDS rather
+//    than scanning across the lanes of a wavefront keeps the registers free
+//    for the tile itself.)
 //  * Prefix: tiles of one lane block form a chain.  Tiles take tickets from
 //    an atomic counter in chain order (all tiles of chunk k before any tile of
 //    chunk k+1), publish (P, Q) as soon as the summary is done, then look back
@@ -31,8 +35,9 @@
 //    a tile that has polled long enough derives the maps it is missing from
 //    the inputs itself (bitwise the values their owners publish), so no wait
 //    is unbounded and no result depends on which path was taken.
-//  * Replay: each thread rescans its rows from registers, starting from the
-//    state entering its segment, and writes the outputs once.
+//  * Replay: each thread applies its segment's exclusive prefix to the
+//    carry entering the tile, then rescans its rows from registers and
+//    writes the outputs once.
 //
 // Published words are single 32- or 64-bit device-scope atomic stores;
 // every word starts as the all-ones pattern, which no published value takes,
@@ -108,12 +113,12 @@ struct BwdArgs {
 };
 
 // Map of tile j of series (bi, lane block) for lane `col`, derived from the
-// inputs in exactly the order the workgroup owning tile j computes it: NR
-// rows per thread, the in-wavefront scan over the RG row groups of each
-// wavefront, then the wavefronts in order.  Lanes past D are the identity.
+// inputs in exactly the order the workgroup owning tile j computes it: each
+// segment of NR rows folded from the identity, then the segments folded in
+// order.  Lanes past D are the identity.
 template <class C>
 __device__ Aff fwd_tile_map(const FwdArgs& x, int j, int bi, int col) {
-    constexpr int RG = C::RG, NR = C::NR;
+    constexpr int NR = C::NR, SEGS = C::WAVES * C::RG;
     Aff A = aff_identity();
     if (col >= x.d.D) return A;
     // wave-uniform row addresses, one 32-bit lane offset
@@ -122,37 +127,32 @@ __device__ Aff fwd_tile_map(const FwdArgs& x, int j, int bi, int col) {
     const char* b0 = static_cast<const char*>(x.b) + (size_t)bi * x.d.T * rowbytes;
     const uint32_t coff = (uint32_t)col * C::EB;
 #pragma unroll 1
-    for (int w = 0; w < C::WAVES; ++w) {
-        TreeFold<RG, Aff, AffThen> tree;
-#pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            Aff t = aff_identity();
-            const int r0 = j * C::CT + (w * RG + g) * NR;
+    for (int sg = 0; sg < SEGS; ++sg) {
+        Aff t = aff_identity();
+        const int r0 = j * C::CT + sg * NR;
 #pragma unroll 1
-            for (int i = 0; i < NR; ++i) {
-                const int r = r0 + i;
-                float at = 1.0f, bt = 0.0f;
-                if (r < x.d.T) {
-                    const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes);  // same tile in every lane
-                    at = Elem<C::DT>::load1(a0 + ro + coff, 0);
-                    bt = Elem<C::DT>::load1(b0 + ro + coff, 0);
-                    if (x.reset && x.reset[(size_t)bi * x.d.T + r]) at = 0.0f;
-                }
-                t.p = at * t.p;
-                t.q = fmaf(at, t.q, bt);
+        for (int i = 0; i < NR; ++i) {
+            const int r = r0 + i;
+            float at = 1.0f, bt = 0.0f;
+            if (r < x.d.T) {
+                const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes);  // same tile in every lane
+                at = Elem<C::DT>::load1(a0 + ro + coff, 0);
+                bt = Elem<C::DT>::load1(b0 + ro + coff, 0);
+                if (x.reset && x.reset[(size_t)bi * x.d.T + r]) at = 0.0f;
             }
-            tree.push(g, t);
+            t.p = at * t.p;
+            t.q = fmaf(at, t.q, bt);
         }
-        A = aff_then(A, tree.total());
+        A = aff_then(A, t);
     }
     return unpack_aff(pack_aff(A));
 }
 
-// Reverse-time counterpart: rows in decreasing order, row groups from the
-// last to the first, wavefronts from the last to the first.
+// Reverse-time counterpart: rows in decreasing order, segments from the last
+// to the first.
 template <class C>
 __device__ Aff bwd_tile_map(const BwdArgs& x, int j, int bi, int col) {
-    constexpr int RG = C::RG, NR = C::NR;
+    constexpr int NR = C::NR, SEGS = C::WAVES * C::RG;
     Aff A = aff_identity();
     if (col >= x.d.D) return A;
     const size_t rowbytes = (size_t)x.d.D * C::EB;
@@ -160,28 +160,23 @@ __device__ Aff bwd_tile_map(const BwdArgs& x, int j, int bi, int col) {
     const char* g0 = static_cast<const char*>(x.g) + (size_t)bi * x.d.T * rowbytes;
     const uint32_t coff = (uint32_t)col * C::EB;
 #pragma unroll 1
-    for (int w = C::WAVES - 1; w >= 0; --w) {
-        TreeFold<RG, Aff, AffThen> tree;
-#pragma unroll
-        for (int g = RG - 1; g >= 0; --g) {
-            Aff t = aff_identity();
-            const int r0 = j * C::CT + (w * RG + g) * NR;
+    for (int sg = SEGS - 1; sg >= 0; --sg) {
+        Aff t = aff_identity();
+        const int r0 = j * C::CT + sg * NR;
 #pragma unroll 1
-            for (int i = NR - 1; i >= 0; --i) {
-                const int r = r0 + i;
-                float at = 1.0f, gt = 0.0f;
-                if (r < x.d.T) {
-                    const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes);  // same tile in every lane
-                    at = Elem<C::DT>::load1(a0 + ro + coff, 0);
-                    gt = Elem<C::DT>::load1(g0 + ro + coff, 0);
-                    if (x.reset && x.reset[(size_t)bi * x.d.T + r]) at = 0.0f;
-                }
-                t.p = at * t.p;
-                t.q = at * (t.q + gt);
+        for (int i = NR - 1; i >= 0; --i) {
+            const int r = r0 + i;
+            float at = 1.0f, gt = 0.0f;
+            if (r < x.d.T) {
+                const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes);  // same tile in every lane
+                at = Elem<C::DT>::load1(a0 + ro + coff, 0);
+                gt = Elem<C::DT>::load1(g0 + ro + coff, 0);
+                if (x.reset && x.reset[(size_t)bi * x.d.T + r]) at = 0.0f;
             }
-            tree.push(RG - 1 - g, t);
+            t.p = at * t.p;
+            t.q = at * (t.q + gt);
         }
-        A = aff_then(A, tree.total());
+        A = aff_then(A, t);
     }
     return unpack_aff(pack_aff(A));
 }
@@ -194,10 +189,10 @@ __device__ Aff bwd_tile_map(const BwdArgs& x, int j, int bi, int col) {
 template <class C, bool ALIGNED, bool RST, bool OUT>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC_F)))
 void fused_fwd_kernel(FwdArgs x) {
-    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
-    __shared__ Aff s_excl[WAVES][V][kWave];
-    __shared__ Aff s_wtot[WAVES][W];
-    __shared__ float s_hin[W];
+    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, TPR = C::TPR;
+    constexpr int SEGS = C::WAVES * RG;
+    __shared__ Aff s_seg[SEGS][W];  // each segment's map, then the maps before it composed
+    __shared__ float s_hin[W];      // the state entering the tile, per lane
 
     const Dims d = x.d;
     const int tid = threadIdx.x;
@@ -232,6 +227,20 @@ void fused_fwd_kernel(FwdArgs x) {
         for (int i = 0; i < NR; ++i)
             if (rs[i]) ra[i] = RowVec<C::DT>::splat(0.0f);
     }
+    // rows past T (and every row of a thread whose lanes lie past D) become
+    // identity steps, once per row here rather than per element in the
+    // summary; a tile whose rows and lanes all exist (wave-uniform, and every
+    // tile when T and D are multiples of the tile) skips this
+    const bool full = g.trow0 + C::CT <= d.T && g.dcol0 + W <= d.D;
+    if (!full) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            if (i >= g.nrows) {
+                ra[i] = RowVec<C::DT>::splat(1.0f);
+                rb[i] = RowVec<C::DT>::splat(0.0f);
+            }
+        }
+    }
 
     // summary of this thread's rows, per lane (rows outer, so only one row
     // is widened to fp32 at a time), then the wavefront scan over its RG
@@ -241,29 +250,20 @@ void fused_fwd_kernel(FwdArgs x) {
     for (int j = 0; j < V; ++j) m[j] = aff_identity();
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        const bool ok = i < g.nrows;
 #pragma unroll
         for (int j = 0; j < V; ++j) {
-            const float at = ok ? ra[i].get(j) : 1.0f;
-            const float bt = ok ? rb[i].get(j) : 0.0f;
+            const float at = ra[i].get(j);
             m[j].p = at * m[j].p;
-            m[j].q = fmaf(at, m[j].q, bt);
+            m[j].q = fmaf(at, m[j].q, rb[i].get(j));
         }
     }
+    const int seg = wave * RG + rg;
+#pragma unroll
+    for (int j = 0; j < V; ++j) s_seg[seg][cg * V + j] = m[j];
     const uint32_t phase = tk.phase;
     const unsigned long long* pqs =
         reinterpret_cast<const unsigned long long*>(x.sc.region[phase] + x.sc.ctr_words);
     const uint32_t* hs = x.sc.region[phase] + x.sc.ctr_words + 2 * x.sc.entries;
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-        const Aff inc = wave_scan_up<TPR>(m[j]);
-        Aff ex;
-        ex.p = shfl_up_f(inc.p, TPR);
-        ex.q = shfl_up_f(inc.q, TPR);
-        if (rg == 0) ex = aff_identity();
-        s_excl[wave][j][l] = ex;
-        if (rg == RG - 1) s_wtot[wave][cg * V + j] = inc;
-    }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         opaque(ra[i]);
@@ -280,12 +280,16 @@ void fused_fwd_kernel(FwdArgs x) {
     }
     __syncthreads();
 
-    // tile map, publication, look-back: one column per thread
+    // exclusive prefixes and tile map, publication, look-back: one lane per thread
     if (tid < W) {
         const int c = tid;
         Aff A = aff_identity();
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) A = aff_then(A, s_wtot[w][c]);
+#pragma unroll 8
+        for (int sg = 0; sg < SEGS; ++sg) {
+            const Aff t = s_seg[sg][c];
+            s_seg[sg][c] = A;
+            A = aff_then(A, t);
+        }
         const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
         const bool more = g.k + 1 < d.NK;
         if (more) publish_u64(const_cast<unsigned long long*>(pqs) + o, pack_aff(A));
@@ -312,15 +316,10 @@ void fused_fwd_kernel(FwdArgs x) {
     // replay from registers
     float h[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-        const int col = cg * V + j;
-        float xv = s_hin[col];
-        for (int w = 0; w < wave; ++w) xv = aff_apply(s_wtot[w][col], xv);
-        h[j] = aff_apply(s_excl[wave][j][l], xv);
-    }
+    for (int j = 0; j < V; ++j) h[j] = aff_apply(s_seg[seg][cg * V + j], s_hin[cg * V + j]);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        if (i < g.nrows) {
+        if (full || i < g.nrows) {
             RowOut<C::DT> o;
 #pragma unroll
             for (int j = 0; j < V; ++j) {
@@ -344,10 +343,10 @@ void fused_fwd_kernel(FwdArgs x) {
 template <class C, bool ALIGNED, bool RST>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC_B)))
 void fused_bwd_kernel(BwdArgs x) {
-    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
-    __shared__ Aff s_excl[WAVES][V][kWave];
-    __shared__ Aff s_wtot[WAVES][W];
-    __shared__ float s_cin[W];
+    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, TPR = C::TPR;
+    constexpr int SEGS = C::WAVES * RG;
+    __shared__ Aff s_seg[SEGS][W];  // each segment's reverse map, then the maps after it composed
+    __shared__ float s_cin[W];      // the carry entering the tile from the right, per lane
 
     const Dims d = x.d;
     const int tid = threadIdx.x;
@@ -406,6 +405,18 @@ void fused_bwd_kernel(BwdArgs x) {
             }
         }
     }
+    // rows past T (and every row of a thread whose lanes lie past D) become
+    // identity steps (wave-uniform skip for a tile whose rows and lanes all exist)
+    const bool full = g.trow0 + C::CT <= d.T && g.dcol0 + W <= d.D;
+    if (!full) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            if (i >= g.nrows) {
+                ra[i] = RowVec<C::DT>::splat(1.0f);
+                rg_[i] = RowVec<C::DT>::splat(0.0f);
+            }
+        }
+    }
 
     // reverse summary: the map from the carry entering the segment on the
     // right to the carry a_s*lambda_s leaving its first row s
@@ -414,29 +425,20 @@ void fused_bwd_kernel(BwdArgs x) {
     for (int j = 0; j < V; ++j) m[j] = aff_identity();
 #pragma unroll
     for (int i = NR - 1; i >= 0; --i) {
-        const bool ok = i < g.nrows;
 #pragma unroll
         for (int j = 0; j < V; ++j) {
-            const float at = ok ? ra[i].get(j) : 1.0f;
-            const float gt = ok ? rg_[i].get(j) : 0.0f;
+            const float at = ra[i].get(j);
             m[j].p = at * m[j].p;
-            m[j].q = at * (m[j].q + gt);
+            m[j].q = at * (m[j].q + rg_[i].get(j));
         }
     }
+    const int seg = wave * RG + rg;
+#pragma unroll
+    for (int j = 0; j < V; ++j) s_seg[seg][cg * V + j] = m[j];
     const uint32_t phase = tk.phase;
     const unsigned long long* pqs =
         reinterpret_cast<const unsigned long long*>(x.sc.region[phase] + x.sc.ctr_words);
     const uint32_t* hs = x.sc.region[phase] + x.sc.ctr_words + 2 * x.sc.entries;
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-        const Aff inc = wave_scan_down<TPR>(m[j]);
-        Aff ex;
-        ex.p = shfl_down_f(inc.p, TPR);
-        ex.q = shfl_down_f(inc.q, TPR);
-        if (rg == RG - 1) ex = aff_identity();
-        s_excl[wave][j][l] = ex;
-        if (rg == 0) s_wtot[wave][cg * V + j] = inc;
-    }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         opaque(ra[i]);
@@ -454,8 +456,12 @@ void fused_bwd_kernel(BwdArgs x) {
     if (tid < W) {
         const int c = tid;
         Aff A = aff_identity();
-#pragma unroll
-        for (int w = WAVES - 1; w >= 0; --w) A = aff_then(A, s_wtot[w][c]);
+#pragma unroll 8
+        for (int sg = SEGS - 1; sg >= 0; --sg) {
+            const Aff t = s_seg[sg][c];
+            s_seg[sg][c] = A;
+            A = aff_then(A, t);
+        }
         const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
         const bool more = g.k > 0;
         if (more) publish_u64(const_cast<unsigned long long*>(pqs) + o, pack_aff(A));
@@ -480,17 +486,12 @@ void fused_bwd_kernel(BwdArgs x) {
     // after it (the carry itself for the first row processed)
     float lam[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-        const int col = cg * V + j;
-        float xv = s_cin[col];
-        for (int w = WAVES - 1; w > wave; --w) xv = aff_apply(s_wtot[w][col], xv);
-        lam[j] = aff_apply(s_excl[wave][j][l], xv);
-    }
+    for (int j = 0; j < V; ++j) lam[j] = aff_apply(s_seg[seg][cg * V + j], s_cin[cg * V + j]);
 #pragma unroll
     for (int i = NR - 1; i >= 0; --i) {
-        if (i < g.nrows) {
+        if (full || i < g.nrows) {
             const int row = g.row0 + i;
-            const bool after = i + 1 < NR && i + 1 < g.nrows;  // row t+1 is in this segment
+            const bool after = i + 1 < NR && (full || i + 1 < g.nrows);  // row t+1 is in this segment
             RowOut<C::DT> oa, ob;
 #pragma unroll
             for (int j = 0; j < V; ++j) {
