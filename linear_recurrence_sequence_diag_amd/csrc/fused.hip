@@ -616,14 +616,14 @@ bool fused_cfg_supported(const Shape& s, int dir, int width, int tile, bool alig
 }
 
 // Default tile shape, from measurements on MI355X (bf16 [8,2048,2560] and
-// [16,4096,2560], fp32 [4,8192,4096], bf16 [1,131072,1024]).  Forward:
-// 128-byte rows of 256 steps (with the early look-back reading, wider rows
-// were no faster, and slower on [8,2048,2560]); 512 steps for long chains
-// (T >= 4096) in bf16 ([16,4096,2560]: 197.6 -> 193.3 us) or when there are
-// fewer than 64 chains of 128-byte lane blocks, where consecutive tiles of a
-// chain start so close together that each waits on its predecessor: longer
-// tiles spread them out ([1,131072,1024]: 162 -> 158 us).  fp32 with many
-// chains stays at 256 ([4,8192,4096]: 277 against 290 us).  Backward:
+// [16,4096,2560], fp32 [4,8192,4096], bf16 [1,131072,1024]; kernel time with
+// the caches flushed before each step).  Forward: 128-byte rows of 256 steps
+// (wider rows and 512 steps were no faster: [16,4096,2560] 184.9 against
+// 190.3 us at 512 steps, [8,2048,2560] 54.2 against 58.7); 512 steps when
+// there are fewer than 64 chains of 128-byte lane blocks and long chains
+// (T >= 4096), where consecutive tiles of a chain start so close together
+// that each waits on its predecessor: longer tiles spread them out
+// ([1,131072,1024]: 152.4 -> 147.7 us).  Backward:
 // 256-byte rows of 128 steps when there are enough lane blocks to keep every
 // tile chain short (bf16 with at least 128 such blocks), else 128-byte rows,
 // which give long single-batch sequences 4x as many chains; fp32 was fastest
@@ -635,7 +635,7 @@ void fused_default_cfg(const Shape& s, int dir, bool aligned, int* width, int* t
     if (dir == 0) {
         const int64_t lanes8 = 8 * (s.dtype == DT_F32 ? Elem<DT_F32>::V : Elem<DT_BF16>::V);
         const int64_t chains8 = s.B * ((s.D + lanes8 - 1) / lanes8);
-        if (s.T >= 8 * 512 && (chains8 < 64 || s.dtype == DT_BF16)) *tile = 512;
+        if (s.T >= 8 * 512 && chains8 < 64) *tile = 512;
         return;
     }
     if (s.dtype == DT_BF16) {

@@ -109,7 +109,7 @@ def test_small_workload(algo, cf, cb, wf, wb):
     check_against_oracle(inp, run_pair(inp, algo, cf, cb, wf, wb))
 
 
-# the last two reach AUTO's 512-step forward tiles (long sequences: bf16, or few lane blocks)
+# the last two reach AUTO's 512-step forward tiles (long sequences with few lane blocks)
 SHAPES = [(1, 1, 1), (1, 2, 3), (2, 63, 7), (2, 64, 8), (1, 65, 9), (3, 257, 64), (2, 300, 65),
           (1, 1000, 100), (2, 513, 129), (1, 1100, 16), (2, 2049, 40), (3, 4099, 136),
           (1, 4097, 40)]
