@@ -15,9 +15,11 @@
 //  * the per-lane walk (one thread owns 16 bytes of each array, i.e. V
 //    complex lanes, and walks all T steps);
 //  * the single-launch tiled form of fused.hip with complex affine maps
-//    (P, Q complex): tickets, summary, deterministic look-back with bounded
-//    waiting, replay from registers.  A published entry is three 64-bit
-//    words (P, Q and the inclusive state H, each a (re, im) pair).
+//    (P, Q complex): tickets, summary (segment maps folded in LDS by one
+//    wavefront, which leaves each segment's exclusive prefix), deterministic
+//    look-back with bounded waiting, replay from registers.  A published
+//    entry is three 64-bit words (P, Q and the inclusive state H, each a
+//    (re, im) pair).
 // All complex products are spelled out with explicit fmas, identically on
 // every path that must agree bit for bit.
 #include <type_traits>
@@ -46,10 +48,11 @@ struct CxBwdArgs {
 
 
 // Map of tile j of series (bi, lane block) for lane `col`, derived from the
-// inputs in the owning workgroup's exact operation order.
+// inputs in the owning workgroup's exact operation order: each segment of NR
+// rows folded from the identity, then the segments folded in order.
 template <class C>
 __device__ CAff cx_fwd_tile_map(const CxFwdArgs& x, int j, int bi, int col) {
-    constexpr int RG = C::RG, NR = C::NR;
+    constexpr int NR = C::NR, SEGS = C::WAVES * C::RG;
     CAff A = caff_identity();
     if (col >= x.d.D) return A;
     const size_t rowbytes = (size_t)x.d.D * C::EB;
@@ -60,34 +63,31 @@ __device__ CAff cx_fwd_tile_map(const CxFwdArgs& x, int j, int bi, int col) {
     const char* bim = static_cast<const char*>(x.p.bi) + b0;
     const uint32_t coff = (uint32_t)col * C::EB;
 #pragma unroll 1
-    for (int w = 0; w < C::WAVES; ++w) {
-        TreeFold<RG, CAff, CAffThen> tree;
-#pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            CAff t = caff_identity();
-            const int r0 = j * C::CT + (w * RG + g) * NR;
+    for (int sg = 0; sg < SEGS; ++sg) {
+        CAff t = caff_identity();
+        const int r0 = j * C::CT + sg * NR;
 #pragma unroll 1
-            for (int i = 0; i < NR; ++i) {
-                const int r = r0 + i;
-                Cx at{1.0f, 0.0f}, bt{0.0f, 0.0f};
-                if (r < x.d.T) {
-                    const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes) + coff;
-                    at = load_cx<C::DT>(ar, ai, ro);
-                    bt = load_cx<C::DT>(br, bim, ro);
-                    if (x.p.reset && x.p.reset[(size_t)bi * x.d.T + r]) at = Cx{0.0f, 0.0f};
-                }
-                t = caff_then(t, fwd_step(at, bt));
+        for (int i = 0; i < NR; ++i) {
+            const int r = r0 + i;
+            Cx at{1.0f, 0.0f}, bt{0.0f, 0.0f};
+            if (r < x.d.T) {
+                const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes) + coff;
+                at = load_cx<C::DT>(ar, ai, ro);
+                bt = load_cx<C::DT>(br, bim, ro);
+                if (x.p.reset && x.p.reset[(size_t)bi * x.d.T + r]) at = Cx{0.0f, 0.0f};
             }
-            tree.push(g, t);
+            t = caff_then(t, fwd_step(at, bt));
         }
-        A = caff_then(A, tree.total());
+        A = caff_then(A, t);
     }
     return CAff{unpack_cx(pack_cx(A.p)), unpack_cx(pack_cx(A.q))};
 }
 
+// Reverse-time counterpart: rows in decreasing order, segments from the last
+// to the first.
 template <class C>
 __device__ CAff cx_bwd_tile_map(const CxBwdArgs& x, int j, int bi, int col) {
-    constexpr int RG = C::RG, NR = C::NR;
+    constexpr int NR = C::NR, SEGS = C::WAVES * C::RG;
     CAff A = caff_identity();
     if (col >= x.d.D) return A;
     const size_t rowbytes = (size_t)x.d.D * C::EB;
@@ -98,27 +98,22 @@ __device__ CAff cx_bwd_tile_map(const CxBwdArgs& x, int j, int bi, int col) {
     const char* gi = static_cast<const char*>(x.p.gi) + b0;
     const uint32_t coff = (uint32_t)col * C::EB;
 #pragma unroll 1
-    for (int w = C::WAVES - 1; w >= 0; --w) {
-        TreeFold<RG, CAff, CAffThen> tree;
-#pragma unroll
-        for (int g = RG - 1; g >= 0; --g) {
-            CAff t = caff_identity();
-            const int r0 = j * C::CT + (w * RG + g) * NR;
+    for (int sg = SEGS - 1; sg >= 0; --sg) {
+        CAff t = caff_identity();
+        const int r0 = j * C::CT + sg * NR;
 #pragma unroll 1
-            for (int i = NR - 1; i >= 0; --i) {
-                const int r = r0 + i;
-                Cx at{1.0f, 0.0f}, gt{0.0f, 0.0f};
-                if (r < x.d.T) {
-                    const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes) + coff;
-                    at = load_cx<C::DT>(ar, ai, ro);
-                    gt = load_cx<C::DT>(gr, gi, ro);
-                    if (x.p.reset && x.p.reset[(size_t)bi * x.d.T + r]) at = Cx{0.0f, 0.0f};
-                }
-                t = rev_fold(t, at, gt);
+        for (int i = NR - 1; i >= 0; --i) {
+            const int r = r0 + i;
+            Cx at{1.0f, 0.0f}, gt{0.0f, 0.0f};
+            if (r < x.d.T) {
+                const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes) + coff;
+                at = load_cx<C::DT>(ar, ai, ro);
+                gt = load_cx<C::DT>(gr, gi, ro);
+                if (x.p.reset && x.p.reset[(size_t)bi * x.d.T + r]) at = Cx{0.0f, 0.0f};
             }
-            tree.push(RG - 1 - g, t);
+            t = rev_fold(t, at, gt);
         }
-        A = caff_then(A, tree.total());
+        A = caff_then(A, t);
     }
     return CAff{unpack_cx(pack_cx(A.p)), unpack_cx(pack_cx(A.q))};
 }
@@ -130,10 +125,10 @@ __device__ CAff cx_bwd_tile_map(const CxBwdArgs& x, int j, int bi, int col) {
 template <class C, bool ALIGNED, bool RST, bool OUT>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void cx_fused_fwd_kernel(CxFwdArgs x) {
-    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
-    __shared__ CAff s_excl[WAVES][V][kWave];
-    __shared__ CAff s_wtot[WAVES][W];
-    __shared__ Cx s_hin[W];
+    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, TPR = C::TPR;
+    constexpr int SEGS = C::WAVES * RG;
+    __shared__ CAff s_seg[SEGS][W];  // each segment's map, then the maps before it composed
+    __shared__ Cx s_hin[W];          // the state entering the tile, per lane
 
     const Dims d = x.d;
     const int tid = threadIdx.x;
@@ -141,6 +136,7 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
     const int l = tid % kWave;
     const int rg = l / TPR;
     const int cg = l % TPR;
+    const int seg = wave * RG + rg;
     const Ticket tk = take_ticket(x.sc);
     const Geo g = tile_geo<C, false>(tk.ticket, d, wave, rg, cg);
     const uint32_t rowbytes = (uint32_t)d.D * C::EB;
@@ -171,23 +167,27 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
                 ai[i] = RowVec<C::DT>::splat(0.0f);
             }
     }
+    // rows past T (and every row of a thread whose lanes lie past D) become
+    // identity steps, once here (skipped by a tile whose rows and lanes all exist)
+    const bool full = g.trow0 + C::CT <= d.T && g.dcol0 + W <= d.D;
+    if (!full) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+            if (i >= g.nrows) {
+                ar[i] = RowVec<C::DT>::splat(1.0f);
+                ai[i] = RowVec<C::DT>::splat(0.0f);
+                br[i] = RowVec<C::DT>::splat(0.0f);
+                bi[i] = RowVec<C::DT>::splat(0.0f);
+            }
+    }
 
-    // summary of this thread's rows per lane, then the wavefront scan
+    // summary of this thread's rows per lane, into LDS
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         CAff m = caff_identity();
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const bool ok = i < g.nrows;
-            const Cx at = ok ? vget(ar[i], ai[i], j) : Cx{1.0f, 0.0f};
-            const Cx bt = ok ? vget(br[i], bi[i], j) : Cx{0.0f, 0.0f};
-            m = caff_then(m, fwd_step(at, bt));
-        }
-        const CAff inc = cwave_scan_up<TPR>(m);
-        CAff ex = cshfl_up<TPR>(inc);
-        if (rg == 0) ex = caff_identity();
-        s_excl[wave][j][l] = ex;
-        if (rg == RG - 1) s_wtot[wave][cg * V + j] = inc;
+        for (int i = 0; i < NR; ++i) m = caff_then(m, fwd_step(vget(ar[i], ai[i], j), vget(br[i], bi[i], j)));
+        s_seg[seg][cg * V + j] = m;
     }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -206,12 +206,17 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
     }
     __syncthreads();
 
+    // exclusive prefixes and tile map, publication, look-back: one lane per thread
     if (tid < W) {
         const int c = tid;
         const CxWords wd = cx_words(x.sc, tk.phase);
         CAff A = caff_identity();
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) A = caff_then(A, s_wtot[w][c]);
+#pragma unroll 4
+        for (int sg = 0; sg < SEGS; ++sg) {
+            const CAff t = s_seg[sg][c];
+            s_seg[sg][c] = A;
+            A = caff_then(A, t);
+        }
         const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
         const bool more = g.k + 1 < d.NK;
         if (more) {
@@ -243,15 +248,10 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
     char* poi = static_cast<char*>(x.p.out_i) + g.tbase;
     Cx h[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-        const int col = cg * V + j;
-        Cx xv = s_hin[col];
-        for (int w = 0; w < wave; ++w) xv = caff_apply(s_wtot[w][col], xv);
-        h[j] = caff_apply(s_excl[wave][j][l], xv);
-    }
+    for (int j = 0; j < V; ++j) h[j] = caff_apply(s_seg[seg][cg * V + j], s_hin[cg * V + j]);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        if (i < g.nrows) {
+        if (full || i < g.nrows) {
             RowOut<C::DT> orr, oii;
 #pragma unroll
             for (int j = 0; j < V; ++j) {
@@ -282,10 +282,10 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
 template <class C, bool ALIGNED, bool RST>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void cx_fused_bwd_kernel(CxBwdArgs x) {
-    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
-    __shared__ CAff s_excl[WAVES][V][kWave];
-    __shared__ CAff s_wtot[WAVES][W];
-    __shared__ Cx s_cin[W];
+    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, TPR = C::TPR;
+    constexpr int SEGS = C::WAVES * RG;
+    __shared__ CAff s_seg[SEGS][W];  // each segment's reverse map, then the maps after it composed
+    __shared__ Cx s_cin[W];          // the carry entering the tile from the right, per lane
 
     const Dims d = x.d;
     const int tid = threadIdx.x;
@@ -293,6 +293,7 @@ void cx_fused_bwd_kernel(CxBwdArgs x) {
     const int l = tid % kWave;
     const int rg = l / TPR;
     const int cg = l % TPR;
+    const int seg = wave * RG + rg;
     const Ticket tk = take_ticket(x.sc);
     const Geo g = tile_geo<C, true>(tk.ticket, d, wave, rg, cg);
     const uint32_t rowbytes = (uint32_t)d.D * C::EB;
@@ -346,24 +347,28 @@ void cx_fused_bwd_kernel(CxBwdArgs x) {
                 rbits |= 1u << i;
             }
     }
+    // rows past T (and every row of a thread whose lanes lie past D) become
+    // identity steps (skipped by a tile whose rows and lanes all exist)
+    const bool full = g.trow0 + C::CT <= d.T && g.dcol0 + W <= d.D;
+    if (!full) {
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+            if (i >= g.nrows) {
+                ar[i] = RowVec<C::DT>::splat(1.0f);
+                ai[i] = RowVec<C::DT>::splat(0.0f);
+                gr[i] = RowVec<C::DT>::splat(0.0f);
+                gi[i] = RowVec<C::DT>::splat(0.0f);
+            }
+    }
 
-    // reverse summary: the map from the carry entering on the right to the
-    // carry conj(a_s) lambda_s leaving the segment's first row s
+    // reverse summary, into LDS: the map from the carry entering on the right
+    // to the carry conj(a_s) lambda_s leaving the segment's first row s
 #pragma unroll
     for (int j = 0; j < V; ++j) {
         CAff m = caff_identity();
 #pragma unroll
-        for (int i = NR - 1; i >= 0; --i) {
-            const bool ok = i < g.nrows;
-            const Cx at = ok ? vget(ar[i], ai[i], j) : Cx{1.0f, 0.0f};
-            const Cx gt = ok ? vget(gr[i], gi[i], j) : Cx{0.0f, 0.0f};
-            m = rev_fold(m, at, gt);
-        }
-        const CAff inc = cwave_scan_down<TPR>(m);
-        CAff ex = cshfl_down_n(inc, TPR);
-        if (rg == RG - 1) ex = caff_identity();
-        s_excl[wave][j][l] = ex;
-        if (rg == 0) s_wtot[wave][cg * V + j] = inc;
+        for (int i = NR - 1; i >= 0; --i) m = rev_fold(m, vget(ar[i], ai[i], j), vget(gr[i], gi[i], j));
+        s_seg[seg][cg * V + j] = m;
     }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -386,8 +391,12 @@ void cx_fused_bwd_kernel(CxBwdArgs x) {
         const int c = tid;
         const CxWords wd = cx_words(x.sc, tk.phase);
         CAff A = caff_identity();
-#pragma unroll
-        for (int w = WAVES - 1; w >= 0; --w) A = caff_then(A, s_wtot[w][c]);
+#pragma unroll 4
+        for (int sg = SEGS - 1; sg >= 0; --sg) {
+            const CAff t = s_seg[sg][c];
+            s_seg[sg][c] = A;
+            A = caff_then(A, t);
+        }
         const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
         const bool more = g.k > 0;
         if (more) {
@@ -417,15 +426,10 @@ void cx_fused_bwd_kernel(CxBwdArgs x) {
     char* pgbi = static_cast<char*>(x.p.gbi) + g.tbase;
     Cx carry[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-        const int col = cg * V + j;
-        Cx xv = s_cin[col];
-        for (int w = WAVES - 1; w > wave; --w) xv = caff_apply(s_wtot[w][col], xv);
-        carry[j] = caff_apply(s_excl[wave][j][l], xv);
-    }
+    for (int j = 0; j < V; ++j) carry[j] = caff_apply(s_seg[seg][cg * V + j], s_cin[cg * V + j]);
 #pragma unroll
     for (int i = NR - 1; i >= 0; --i) {
-        if (i < g.nrows) {
+        if (full || i < g.nrows) {
             const int row = g.row0 + i;
             RowOut<C::DT> oar, oai, obr, obi;
 #pragma unroll

@@ -97,10 +97,12 @@ struct SamuBwdArgs {
     float *mode_nu, *mode_theta;  // [NK, B, M] partial sums over a tile's rows
 };
 
-// Derived tile maps for the look-back (same operation order as the owners).
+// Derived tile maps for the look-back, in the owners' operation order: each
+// segment of NR rows folded from the identity, then the segments folded in
+// order (forward) or in reverse order (backward).
 template <class C>
 __device__ CAff samu_fwd_tile_map(const SamuFwdArgs& x, int j, int bi, int col) {
-    constexpr int RG = C::RG, NR = C::NR;
+    constexpr int NR = C::NR, SEGS = C::WAVES * C::RG;
     CAff A = caff_identity();
     if (col >= x.d.D) return A;
     const SamuLane L = samu_lane(x.mode_tab, col);
@@ -110,35 +112,30 @@ __device__ CAff samu_fwd_tile_map(const SamuFwdArgs& x, int j, int bi, int col) 
     const char* bim = static_cast<const char*>(x.p.bi) + b0;
     const uint32_t coff = (uint32_t)col * C::EB;
 #pragma unroll 1
-    for (int w = 0; w < C::WAVES; ++w) {
-        TreeFold<RG, CAff, CAffThen> tree;
-#pragma unroll
-        for (int g = 0; g < RG; ++g) {
-            CAff t = caff_identity();
-            const int r0 = j * C::CT + (w * RG + g) * NR;
+    for (int sg = 0; sg < SEGS; ++sg) {
+        CAff t = caff_identity();
+        const int r0 = j * C::CT + sg * NR;
 #pragma unroll 1
-            for (int i = 0; i < NR; ++i) {
-                const int r = r0 + i;
-                Cx at{1.0f, 0.0f}, bt{0.0f, 0.0f};
-                if (r < x.d.T) {
-                    const size_t tok = (size_t)bi * x.d.T + r;
-                    const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes) + coff;
-                    at = samu_a(L, samu_tok(x.tok_tab, tok));
-                    bt = load_cx<C::DT>(br, bim, ro);
-                    if (x.p.reset && x.p.reset[tok]) at = Cx{0.0f, 0.0f};
-                }
-                t = caff_then(t, fwd_step(at, bt));
+        for (int i = 0; i < NR; ++i) {
+            const int r = r0 + i;
+            Cx at{1.0f, 0.0f}, bt{0.0f, 0.0f};
+            if (r < x.d.T) {
+                const size_t tok = (size_t)bi * x.d.T + r;
+                const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes) + coff;
+                at = samu_a(L, samu_tok(x.tok_tab, tok));
+                bt = load_cx<C::DT>(br, bim, ro);
+                if (x.p.reset && x.p.reset[tok]) at = Cx{0.0f, 0.0f};
             }
-            tree.push(g, t);
+            t = caff_then(t, fwd_step(at, bt));
         }
-        A = caff_then(A, tree.total());
+        A = caff_then(A, t);
     }
     return CAff{unpack_cx(pack_cx(A.p)), unpack_cx(pack_cx(A.q))};
 }
 
 template <class C>
 __device__ CAff samu_bwd_tile_map(const SamuBwdArgs& x, int j, int bi, int col) {
-    constexpr int RG = C::RG, NR = C::NR;
+    constexpr int NR = C::NR, SEGS = C::WAVES * C::RG;
     CAff A = caff_identity();
     if (col >= x.d.D) return A;
     const SamuLane L = samu_lane(x.mode_tab, col);
@@ -148,28 +145,23 @@ __device__ CAff samu_bwd_tile_map(const SamuBwdArgs& x, int j, int bi, int col) 
     const char* gi = static_cast<const char*>(x.p.gi) + b0;
     const uint32_t coff = (uint32_t)col * C::EB;
 #pragma unroll 1
-    for (int w = C::WAVES - 1; w >= 0; --w) {
-        TreeFold<RG, CAff, CAffThen> tree;
-#pragma unroll
-        for (int g = RG - 1; g >= 0; --g) {
-            CAff t = caff_identity();
-            const int r0 = j * C::CT + (w * RG + g) * NR;
+    for (int sg = SEGS - 1; sg >= 0; --sg) {
+        CAff t = caff_identity();
+        const int r0 = j * C::CT + sg * NR;
 #pragma unroll 1
-            for (int i = NR - 1; i >= 0; --i) {
-                const int r = r0 + i;
-                Cx at{1.0f, 0.0f}, gt{0.0f, 0.0f};
-                if (r < x.d.T) {
-                    const size_t tok = (size_t)bi * x.d.T + r;
-                    const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes) + coff;
-                    at = samu_a(L, samu_tok(x.tok_tab, tok));
-                    gt = load_cx<C::DT>(gr, gi, ro);
-                    if (x.p.reset && x.p.reset[tok]) at = Cx{0.0f, 0.0f};
-                }
-                t = rev_fold(t, at, gt);
+        for (int i = NR - 1; i >= 0; --i) {
+            const int r = r0 + i;
+            Cx at{1.0f, 0.0f}, gt{0.0f, 0.0f};
+            if (r < x.d.T) {
+                const size_t tok = (size_t)bi * x.d.T + r;
+                const size_t ro = (size_t)uniform64((int64_t)r * (int64_t)rowbytes) + coff;
+                at = samu_a(L, samu_tok(x.tok_tab, tok));
+                gt = load_cx<C::DT>(gr, gi, ro);
+                if (x.p.reset && x.p.reset[tok]) at = Cx{0.0f, 0.0f};
             }
-            tree.push(RG - 1 - g, t);
+            t = rev_fold(t, at, gt);
         }
-        A = caff_then(A, tree.total());
+        A = caff_then(A, t);
     }
     return CAff{unpack_cx(pack_cx(A.p)), unpack_cx(pack_cx(A.q))};
 }
@@ -180,10 +172,10 @@ __device__ CAff samu_bwd_tile_map(const SamuBwdArgs& x, int j, int bi, int col) 
 template <class C, bool ALIGNED, bool RST, bool OUT>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void samu_fwd_kernel(SamuFwdArgs x) {
-    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
-    __shared__ CAff s_excl[WAVES][V][kWave];
-    __shared__ CAff s_wtot[WAVES][W];
-    __shared__ Cx s_hin[W];
+    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, TPR = C::TPR;
+    constexpr int SEGS = C::WAVES * RG;
+    __shared__ CAff s_seg[SEGS][W];  // each segment's map, then the maps before it composed
+    __shared__ Cx s_hin[W];          // the state entering the tile, per lane
 
     const Dims d = x.d;
     const int tid = threadIdx.x;
@@ -191,6 +183,7 @@ void samu_fwd_kernel(SamuFwdArgs x) {
     const int l = tid % kWave;
     const int rg = l / TPR;
     const int cg = l % TPR;
+    const int seg = wave * RG + rg;
     const Ticket tk = take_ticket(x.sc);
     const Geo g = tile_geo<C, false>(tk.ticket, d, wave, rg, cg);
     const uint32_t rowbytes = (uint32_t)d.D * C::EB;
@@ -238,11 +231,7 @@ void samu_fwd_kernel(SamuFwdArgs x) {
             const Cx bt = ok ? vget(br[i], bi[i], j) : Cx{0.0f, 0.0f};
             m = caff_then(m, fwd_step(at, bt));
         }
-        const CAff inc = cwave_scan_up<TPR>(m);
-        CAff ex = cshfl_up<TPR>(inc);
-        if (rg == 0) ex = caff_identity();
-        s_excl[wave][j][l] = ex;
-        if (rg == RG - 1) s_wtot[wave][cg * V + j] = inc;
+        s_seg[seg][cg * V + j] = m;
     }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -263,8 +252,12 @@ void samu_fwd_kernel(SamuFwdArgs x) {
         const int c = tid;
         const CxWords wd = cx_words(x.sc, tk.phase);
         CAff A = caff_identity();
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) A = caff_then(A, s_wtot[w][c]);
+#pragma unroll 4
+        for (int sg = 0; sg < SEGS; ++sg) {
+            const CAff t = s_seg[sg][c];
+            s_seg[sg][c] = A;
+            A = caff_then(A, t);
+        }
         const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
         const bool more = g.k + 1 < d.NK;
         if (more) {
@@ -296,12 +289,7 @@ void samu_fwd_kernel(SamuFwdArgs x) {
     char* poi = static_cast<char*>(x.p.out_i) + g.tbase;
     Cx h[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-        const int col = cg * V + j;
-        Cx xv = s_hin[col];
-        for (int w = 0; w < wave; ++w) xv = caff_apply(s_wtot[w][col], xv);
-        h[j] = caff_apply(s_excl[wave][j][l], xv);
-    }
+    for (int j = 0; j < V; ++j) h[j] = caff_apply(s_seg[seg][cg * V + j], s_hin[cg * V + j]);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         if (i < g.nrows) {
@@ -365,9 +353,9 @@ template <class C, bool ALIGNED, bool RST>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void samu_bwd_kernel(SamuBwdArgs x) {
     constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
-    __shared__ CAff s_excl[WAVES][V][kWave];
-    __shared__ CAff s_wtot[WAVES][W];
-    __shared__ Cx s_cin[W];
+    constexpr int SEGS = WAVES * RG;
+    __shared__ CAff s_seg[SEGS][W];  // each segment's reverse map, then the maps after it composed
+    __shared__ Cx s_cin[W];          // the carry entering the tile from the right, per lane
     __shared__ float s_acc[2][WAVES][W];
 
     const Dims d = x.d;
@@ -376,6 +364,7 @@ void samu_bwd_kernel(SamuBwdArgs x) {
     const int l = tid % kWave;
     const int rg = l / TPR;
     const int cg = l % TPR;
+    const int seg = wave * RG + rg;
     const Ticket tk = take_ticket(x.sc);
     const Geo g = tile_geo<C, true>(tk.ticket, d, wave, rg, cg);
     const uint32_t rowbytes = (uint32_t)d.D * C::EB;
@@ -435,11 +424,7 @@ void samu_bwd_kernel(SamuBwdArgs x) {
             const Cx gt = ok ? vget(gr[i], gi[i], j) : Cx{0.0f, 0.0f};
             m = rev_fold(m, at, gt);
         }
-        const CAff inc = cwave_scan_down<TPR>(m);
-        CAff ex = cshfl_down_n(inc, TPR);
-        if (rg == RG - 1) ex = caff_identity();
-        s_excl[wave][j][l] = ex;
-        if (rg == 0) s_wtot[wave][cg * V + j] = inc;
+        s_seg[seg][cg * V + j] = m;
     }
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -460,8 +445,12 @@ void samu_bwd_kernel(SamuBwdArgs x) {
         const int c = tid;
         const CxWords wd = cx_words(x.sc, tk.phase);
         CAff A = caff_identity();
-#pragma unroll
-        for (int w = WAVES - 1; w >= 0; --w) A = caff_then(A, s_wtot[w][c]);
+#pragma unroll 4
+        for (int sg = SEGS - 1; sg >= 0; --sg) {
+            const CAff t = s_seg[sg][c];
+            s_seg[sg][c] = A;
+            A = caff_then(A, t);
+        }
         const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
         const bool more = g.k > 0;
         if (more) {
@@ -494,10 +483,7 @@ void samu_bwd_kernel(SamuBwdArgs x) {
     float acc[2 * V], tsum_[2 * NR];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        const int col = cg * V + j;
-        Cx xv = s_cin[col];
-        for (int w = WAVES - 1; w > wave; --w) xv = caff_apply(s_wtot[w][col], xv);
-        carry[j] = caff_apply(s_excl[wave][j][l], xv);
+        carry[j] = caff_apply(s_seg[seg][cg * V + j], s_cin[cg * V + j]);
         acc[2 * j] = 0.0f;
         acc[2 * j + 1] = 0.0f;
     }
