@@ -588,110 +588,97 @@ def reverse_chunk_replay(a, out, grad_out, future, chunk, h0=None):
     return ga, gb
 
 
-def _make_autograd():
+def _scan_function(run_forward, run_backward):
+    """A torch.autograd.Function over one pair of C entry points.
+
+    ``run_forward(reset, inputs)`` returns (outputs, kept): the outputs the
+    caller gets and the tensors the backward entry point reads (for every
+    scan here: the transition operands and the forward's ``out``, never
+    ``b``).  ``run_backward(reset, kept, grads)`` returns one gradient per
+    input.  Inputs and incoming gradients are made contiguous before they
+    reach the C ABI, which takes only contiguous [B, T, D] storage; the
+    segment mask is passed through and gets no gradient."""
     torch = _torch()
 
-    class DiagonalScan(torch.autograd.Function):
-        """out = scan(a, b); gradients from the reverse-time kernels."""
-
+    class ScanFunction(torch.autograd.Function):
         @staticmethod
-        def forward(ctx, a, b, reset):
-            a = a.contiguous()
-            b = b.contiguous()
-            out, _ = scan(a, b, with_last=False, reset=reset)
-            ctx.save_for_backward(a, out)
+        def forward(ctx, reset, *inputs):
+            outs, kept = run_forward(reset, [t.contiguous() for t in inputs])
+            ctx.save_for_backward(*kept)
             ctx.reset = reset
-            return out
+            return outs[0] if len(outs) == 1 else tuple(outs)
 
         @staticmethod
-        def backward(ctx, grad_out):
-            a, out = ctx.saved_tensors
-            ga, gb, _ = scan_backward(a, out, grad_out.contiguous(), reset=ctx.reset)
-            return ga, gb, None
+        def backward(ctx, *grads):
+            grads = [g.contiguous() for g in grads]
+            return (None, *run_backward(ctx.reset, ctx.saved_tensors, grads))
 
-    return DiagonalScan
-
-
-_autograd_cls = None
-_complex_autograd_cls = None
+    return ScanFunction
 
 
-def _make_complex_autograd():
-    torch = _torch()
-
-    class ComplexDiagonalScan(torch.autograd.Function):
-        """(out_r, out_i) = complex scan of (a, b); gradients from the reverse-time kernels."""
-
-        @staticmethod
-        def forward(ctx, ar, ai, br, bi, reset):
-            ar, ai, br, bi = (t.contiguous() for t in (ar, ai, br, bi))
-            out_r, out_i, _, _ = complex_scan(ar, ai, br, bi, with_last=False, reset=reset)
-            ctx.save_for_backward(ar, ai, out_r, out_i)
-            ctx.reset = reset
-            return out_r, out_i
-
-        @staticmethod
-        def backward(ctx, grad_out_r, grad_out_i):
-            ar, ai, out_r, out_i = ctx.saved_tensors
-            gar, gai, gbr, gbi, _ = complex_scan_backward(
-                ar, ai, out_r, out_i, grad_out_r.contiguous(), grad_out_i.contiguous(),
-                reset=ctx.reset)
-            return gar, gai, gbr, gbi, None
-
-    return ComplexDiagonalScan
+def _real_forward(reset, inputs):
+    a, b = inputs
+    out, _ = scan(a, b, with_last=False, reset=reset)
+    return [out], (a, out)
 
 
-def complex_diagonal_scan(ar, ai, br, bi, reset=None):
-    """Differentiable complex scan (torch autograd) on planar tensors; returns (out_r, out_i)."""
-    global _complex_autograd_cls
-    if _complex_autograd_cls is None:
-        _complex_autograd_cls = _make_complex_autograd()
-    return _complex_autograd_cls.apply(ar, ai, br, bi, reset)
+def _real_backward(reset, kept, grads):
+    a, out = kept
+    ga, gb, _ = scan_backward(a, out, grads[0], reset=reset)
+    return ga, gb
 
 
-_samu_autograd_cls = None
+def _complex_forward(reset, inputs):
+    ar, ai, br, bi = inputs
+    out_r, out_i, _, _ = complex_scan(ar, ai, br, bi, with_last=False, reset=reset)
+    return [out_r, out_i], (ar, ai, out_r, out_i)
 
 
-def _make_samu_autograd():
-    torch = _torch()
-
-    class SAMUScan(torch.autograd.Function):
-        """(out_r, out_i) of the fused-transition scan; the backward rebuilds the
-        transitions and returns gradients for eta, delta, nu_log, theta_log, br, bi."""
-
-        @staticmethod
-        def forward(ctx, eta, delta, nu_log, theta_log, br, bi, reset):
-            eta, delta, nu_log, theta_log, br, bi = (
-                t.contiguous() for t in (eta, delta, nu_log, theta_log, br, bi))
-            out_r, out_i, _, _ = samu_scan(eta, delta, nu_log, theta_log, br, bi,
-                                           with_last=False, reset=reset)
-            ctx.save_for_backward(eta, delta, nu_log, theta_log, out_r, out_i)
-            ctx.reset = reset
-            return out_r, out_i
-
-        @staticmethod
-        def backward(ctx, grad_out_r, grad_out_i):
-            eta, delta, nu_log, theta_log, out_r, out_i = ctx.saved_tensors
-            ge, gd, gn, gt, gbr, gbi, _ = samu_scan_backward(
-                eta, delta, nu_log, theta_log, out_r, out_i, grad_out_r.contiguous(),
-                grad_out_i.contiguous(), reset=ctx.reset)
-            return (ge.to(eta.dtype), gd.to(delta.dtype), gn, gt, gbr, gbi, None)
-
-    return SAMUScan
+def _complex_backward(reset, kept, grads):
+    ar, ai, out_r, out_i = kept
+    gar, gai, gbr, gbi, _ = complex_scan_backward(ar, ai, out_r, out_i, grads[0], grads[1],
+                                                  reset=reset)
+    return gar, gai, gbr, gbi
 
 
-def samu_diagonal_scan(eta, delta, nu_log, theta_log, br, bi, reset=None):
-    """Differentiable fused-transition scan (torch autograd); returns (out_r, out_i)."""
-    global _samu_autograd_cls
-    if _samu_autograd_cls is None:
-        _samu_autograd_cls = _make_samu_autograd()
-    return _samu_autograd_cls.apply(eta, delta, nu_log, theta_log, br, bi, reset)
+def _samu_forward(reset, inputs):
+    eta, delta, nu_log, theta_log, br, bi = inputs
+    out_r, out_i, _, _ = samu_scan(eta, delta, nu_log, theta_log, br, bi, with_last=False,
+                                   reset=reset)
+    return [out_r, out_i], (eta, delta, nu_log, theta_log, out_r, out_i)
+
+
+def _samu_backward(reset, kept, grads):
+    eta, delta, nu_log, theta_log, out_r, out_i = kept
+    ge, gd, gn, gt, gbr, gbi, _ = samu_scan_backward(eta, delta, nu_log, theta_log, out_r, out_i,
+                                                     grads[0], grads[1], reset=reset)
+    # the per-token gradients come back in fp32; the controls may be bf16
+    return ge.to(eta.dtype), gd.to(delta.dtype), gn, gt, gbr, gbi
+
+
+_functions = {}
+
+
+def _function(name):
+    if name not in _functions:
+        pair = {"real": (_real_forward, _real_backward),
+                "complex": (_complex_forward, _complex_backward),
+                "samu": (_samu_forward, _samu_backward)}[name]
+        _functions[name] = _scan_function(*pair)
+    return _functions[name]
 
 
 def diagonal_scan(a, b, reset=None):
     """Differentiable scan (torch autograd) returning every state; ``reset``
     ([B, T] bool/uint8, not differentiated) starts new segments."""
-    global _autograd_cls
-    if _autograd_cls is None:
-        _autograd_cls = _make_autograd()
-    return _autograd_cls.apply(a, b, reset)
+    return _function("real").apply(reset, a, b)
+
+
+def complex_diagonal_scan(ar, ai, br, bi, reset=None):
+    """Differentiable complex scan (torch autograd) on planar tensors; returns (out_r, out_i)."""
+    return _function("complex").apply(reset, ar, ai, br, bi)
+
+
+def samu_diagonal_scan(eta, delta, nu_log, theta_log, br, bi, reset=None):
+    """Differentiable fused-transition scan (torch autograd); returns (out_r, out_i)."""
+    return _function("samu").apply(reset, eta, delta, nu_log, theta_log, br, bi)

@@ -134,15 +134,30 @@ struct Resolved {
 // checked separately at launch time).
 bool shape_aligned(const Shape& s) { return (s.D * (s.dtype == LRSCAN_F32 ? 4 : 2)) % 16 == 0; }
 
-// The automatic choice: the single-launch fused form reads every input once
-// and was the fastest form on every measured shape; its tile shape comes from
-// fused_default_cfg.  The per-lane walk and the three-launch form are kept
-// for explicit requests.
+// The per-lane walk when the sequences are short and B*D alone fills the GPU
+// many times over: every tile of the fused form would be mostly idle rows,
+// while each lane's walk is a few steps of plain streaming.  Measured on
+// MI355X with 20M-42M lanes of T = 8 or 16: 5.3-5.9 TB/s against 0.4-3.4
+// for the best tile shape.  (At T = 32 the two are even; below about 1M
+// lanes the walk has too few threads in flight to be competitive.)
+bool prefer_seq(const Shape& s) { return s.T <= 16 && s.B * s.D >= ((int64_t)1 << 20); }
+
+// The automatic choice: the per-lane walk for short sequences over many
+// lanes (prefer_seq); otherwise the single-launch fused form, which reads
+// every input once and was the fastest form on every other measured shape,
+// with its tile shape from fused_default_cfg; the three-launch form past the
+// fused form's index limits.
 Resolved resolve(const Shape& s, int dir, const lrscan_opts* o, bool aligned) {
     Resolved r;
     r.algo = o ? o->algo : LRSCAN_ALGO_AUTO;
     r.chunk = o ? o->chunk : 0;
     r.width = o ? o->width : 0;
+    if (r.algo == LRSCAN_ALGO_AUTO && prefer_seq(s)) {
+        r.algo = LRSCAN_ALGO_SEQ;
+        r.chunk = 0;
+        r.width = 0;
+        return r;
+    }
     if (r.algo == LRSCAN_ALGO_AUTO) {
         int w = 0, t = 0;
         fused_default_cfg(s, dir, aligned, &w, &t);

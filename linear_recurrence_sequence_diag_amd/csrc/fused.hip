@@ -615,33 +615,55 @@ bool fused_cfg_supported(const Shape& s, int dir, int width, int tile, bool alig
     return true;
 }
 
-// Default tile shape, from measurements on MI355X (bf16 [8,2048,2560] and
-// [16,4096,2560], fp32 [4,8192,4096], bf16 [1,131072,1024]; kernel time with
-// the caches flushed before each step).  Forward: 128-byte rows of 256 steps
-// (wider rows and 512 steps were no faster: [16,4096,2560] 184.9 against
-// 190.3 us at 512 steps, [8,2048,2560] 54.2 against 58.7); 512 steps when
-// there are fewer than 64 chains of 128-byte lane blocks and long chains
-// (T >= 4096), where consecutive tiles of a chain start so close together
-// that each waits on its predecessor: longer tiles spread them out
-// ([1,131072,1024]: 152.4 -> 147.7 us).  Backward:
-// 256-byte rows of 128 steps when there are enough lane blocks to keep every
-// tile chain short (bf16 with at least 128 such blocks), else 128-byte rows,
-// which give long single-batch sequences 4x as many chains; fp32 was fastest
-// with 128-byte rows.
+// Default tile shape, from measurements on MI355X (kernel time with the caches
+// flushed before each launch; [B,T,D] bf16 and fp32 from [8,2048,2560] and
+// [16,4096,2560] to [1,131072,1024], and short sequences T = 8 .. 1024 at
+// about 340M elements).  A tile should not be much taller than the sequence:
+// its rows past T are idle threads.  Forward: 64 rows of 512-byte lane
+// blocks for T <= 64 ([4150,32,2560] bf16 5.0 against 1.6 TB/s at 256 rows),
+// 128 rows of 256-byte blocks for T <= 128 (5.9 against 4.7 TB/s), else 256
+// rows of 128-byte blocks, and 512 rows when there are fewer than 64 chains
+// of 128-byte lane blocks and T >= 4096, where consecutive tiles of a chain
+// start so close together that each waits on its predecessor ([1,131072,
+// 1024]: 152.4 -> 147.7 us).  Backward: 32 rows of 512-byte blocks for
+// T <= 32, 64 rows for T <= 64, 128 rows of 128-byte blocks for T <= 128,
+// 128 rows of 256-byte blocks for long bf16 sequences (T >= 1024) with at
+// least 128 such blocks ([16,4096,2560]: 277.7 against 283.0 us for 256 rows
+// of 128-byte blocks, [8,2048,2560] even), else 256 rows of 128-byte blocks
+// (T of 256..512 over many lane blocks: 5.8 against 5.2 TB/s).  A lane block
+// wider than the row (D smaller than the block) would leave lanes idle, so
+// the widths fall back to narrower rows.
 void fused_default_cfg(const Shape& s, int dir, bool aligned, int* width, int* tile) {
     *width = 8;
     *tile = 256;
     if (!aligned) return;
+    const int64_t row_bytes = s.D * (s.dtype == DT_F32 ? 4 : 2);
+    const auto fits = [&](int w) { return row_bytes >= (int64_t)w * 16; };
     if (dir == 0) {
-        const int64_t lanes8 = 8 * (s.dtype == DT_F32 ? Elem<DT_F32>::V : Elem<DT_BF16>::V);
-        const int64_t chains8 = s.B * ((s.D + lanes8 - 1) / lanes8);
-        if (s.T >= 8 * 512 && chains8 < 64) *tile = 512;
+        if (s.T <= 64 && fits(32)) {
+            *width = 32;
+            *tile = 64;
+        } else if (s.T <= 128 && fits(16)) {
+            *width = 16;
+            *tile = 128;
+        } else {
+            const int64_t lanes8 = 8 * (s.dtype == DT_F32 ? Elem<DT_F32>::V : Elem<DT_BF16>::V);
+            const int64_t chains8 = s.B * ((s.D + lanes8 - 1) / lanes8);
+            if (s.T >= 8 * 512 && chains8 < 64) *tile = 512;
+        }
         return;
     }
-    if (s.dtype == DT_BF16) {
+    if (s.T <= 32 && fits(32)) {
+        *width = 32;
+        *tile = 32;
+    } else if (s.T <= 64 && fits(32)) {
+        *width = 32;
+        *tile = 64;
+    } else if (s.T <= 128) {
+        *tile = 128;
+    } else if (s.dtype == DT_BF16 && s.T >= 1024 && fits(16)) {
         const int64_t lanes16 = 16 * Elem<DT_BF16>::V;
-        const int64_t blocks16 = s.B * ((s.D + lanes16 - 1) / lanes16);
-        if (blocks16 >= 128) {
+        if (s.B * ((s.D + lanes16 - 1) / lanes16) >= 128) {
             *width = 16;
             *tile = 128;
         }

@@ -145,13 +145,24 @@ def test_argument_errors_return_status_without_work():
 
 def test_workspace_sizes_and_auto_choice():
     lr = _lib()
-    # rows too long for the fused form's 32-bit in-tile offsets: AUTO takes the chunked form
     for dt in (lr.F32, lr.BF16):
         for direction in (0, 1):
-            algo, chunk, _ = lr.scan_auto_algo(1, 1, (1 << 22) + 5, dt, direction)
+            # rows too long for the fused form's 32-bit in-tile offsets: the chunked form
+            algo, chunk, _ = lr.scan_auto_algo(1, 32, 1 << 25, dt, direction)
             assert algo == lr.ALGO_CHUNKED and chunk > 0
+            # short sequences over millions of lanes: the per-lane walk
+            algo, chunk, _ = lr.scan_auto_algo(1, 1, (1 << 22) + 5, dt, direction)
+            assert algo == lr.ALGO_SEQ
+            algo, _, _ = lr.scan_auto_algo(16384, 16, 64, dt, direction)
+            assert algo == lr.ALGO_SEQ
+            # long sequences, and short ones over too few lanes for the walk: the fused form
             algo, _, _ = lr.scan_auto_algo(8, 2048, 2560, dt, direction)
             assert algo == lr.ALGO_FUSED
+            algo, _, _ = lr.scan_auto_algo(4, 16, 1024, dt, direction)
+            assert algo == lr.ALGO_FUSED
+            # a tile is not much taller than the sequence
+            _, tile, _ = lr.scan_auto_algo(4096, 32, 2560, dt, direction)
+            assert tile <= 64
     assert lr.scan_workspace_bytes(0, 8, 4, lr.F32) == 0
     o = lr.make_opts(algo="seq")
     assert lr.scan_workspace_bytes(2, 8, 4, lr.F32, o) == 0
