@@ -29,11 +29,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
 
-// Two floats -> two bf16 packed in one dword (lo in bits 0..15), RNE.
+// Two floats -> two bf16 packed in one dword (lo in bits 0..15), RNE.  As a
+// two-lane vector conversion this is one v_cvt_pk_bf16_f32 of both values
+// (two scalar conversions cost that instruction twice plus a shift and an or).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 l = (__bf16)lo;
-    __bf16 h = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {

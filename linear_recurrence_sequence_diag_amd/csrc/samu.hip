@@ -79,6 +79,12 @@ __device__ __forceinline__ Cx samu_a(const SamuLane& L, const SamuTok& k) {
     return samu_a_of(L, k, samu_x2(L, k));
 }
 
+// Make the compiler forget the factors after the summary, so that the
+// replay recomputes each transition instead of keeping the summary's copies
+// of all of them alive across the look-back.
+__device__ __forceinline__ void opaque(SamuTok& k) { asm volatile("" : "+v"(k.e), "+v"(k.cd), "+v"(k.sd)); }
+__device__ __forceinline__ void opaque(SamuLane& L) { asm volatile("" : "+v"(L.nu2), "+v"(L.ct), "+v"(L.st)); }
+
 struct SamuFwdArgs {
     SamuFwdPtrs p;
     const float4 *tok_tab, *mode_tab;
@@ -169,23 +175,28 @@ __device__ CAff samu_bwd_tile_map(const SamuBwdArgs& x, int j, int bi, int col) 
 // ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
-template <class C, bool ALIGNED, bool RST, bool OUT>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
-void samu_fwd_kernel(SamuFwdArgs x) {
-    constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, TPR = C::TPR;
-    constexpr int SEGS = C::WAVES * RG;
-    __shared__ CAff s_seg[SEGS][W];  // each segment's map, then the maps before it composed
-    __shared__ Cx s_hin[W];          // the state entering the tile, per lane
+// Distinct empty statements at the top of the two versions of a tile body:
+// without them the compiler hoists the identical start of both versions
+// above the branch, and the registers that the hoisted part keeps alive into
+// both made the pair spill where each version alone does not.
+template <bool FULL>
+__device__ __forceinline__ void tile_marker() {
+    if constexpr (FULL) asm volatile("; full tile");
+    else asm volatile("; partial tile");
+}
 
+// One tile of the forward.  FULL: every row and lane of the tile exists
+// (wave-uniform, and every tile when T and M are multiples of the tile), so
+// the tile runs without the per-element guards that rows past T and lanes
+// past M need.
+template <class C, bool ALIGNED, bool RST, bool OUT, bool FULL>
+__device__ __forceinline__ void samu_fwd_tile(const SamuFwdArgs& x, const Ticket& tk, const Geo& g,
+                                              int seg, int cg, CAff (&s_seg)[C::WAVES * C::RG][C::W],
+                                              Cx (&s_hin)[C::W]) {
+    constexpr int V = C::V, W = C::W, NR = C::NR, SEGS = C::WAVES * C::RG;
+    tile_marker<FULL>();
     const Dims d = x.d;
     const int tid = threadIdx.x;
-    const int wave = uniform((int)(threadIdx.x / kWave));
-    const int l = tid % kWave;
-    const int rg = l / TPR;
-    const int cg = l % TPR;
-    const int seg = wave * RG + rg;
-    const Ticket tk = take_ticket(x.sc);
-    const Geo g = tile_geo<C, false>(tk.ticket, d, wave, rg, cg);
     const uint32_t rowbytes = (uint32_t)d.D * C::EB;
     const char* pbr = static_cast<const char*>(x.p.br) + g.tbase;
     const char* pbi = static_cast<const char*>(x.p.bi) + g.tbase;
@@ -204,19 +215,19 @@ void samu_fwd_kernel(SamuFwdArgs x) {
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         const int row = g.row0 + i;
-        const size_t t = (size_t)g.bi * d.T + (row < d.T ? row : d.T - 1);
+        const size_t t = (size_t)g.bi * d.T + (FULL || row < d.T ? row : d.T - 1);
         tok[i] = samu_tok(x.tok_tab, t);
         if constexpr (RST) rbits |= (x.p.reset[t] ? 1u : 0u) << i;
     }
     SamuLane ln[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        const int m = g.d0 + j < d.D ? g.d0 + j : d.D - 1;
+        const int m = FULL || g.d0 + j < d.D ? g.d0 + j : d.D - 1;
         ln[j] = samu_lane(x.mode_tab, m);
     }
     // lanes past M step with the identity, as the derived maps assume
     auto trans = [&](int i, int j) -> Cx {
-        if (j >= g.nvalid) return Cx{1.0f, 0.0f};
+        if (!FULL && j >= g.nvalid) return Cx{1.0f, 0.0f};
         if (RST && ((rbits >> i) & 1u)) return Cx{0.0f, 0.0f};
         return samu_a(ln[j], tok[i]);
     };
@@ -226,7 +237,7 @@ void samu_fwd_kernel(SamuFwdArgs x) {
         CAff m = caff_identity();
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
-            const bool ok = i < g.nrows;
+            const bool ok = FULL || i < g.nrows;
             const Cx at = ok ? trans(i, j) : Cx{1.0f, 0.0f};
             const Cx bt = ok ? vget(br[i], bi[i], j) : Cx{0.0f, 0.0f};
             m = caff_then(m, fwd_step(at, bt));
@@ -237,7 +248,10 @@ void samu_fwd_kernel(SamuFwdArgs x) {
     for (int i = 0; i < NR; ++i) {
         opaque(br[i]);
         opaque(bi[i]);
+        opaque(tok[i]);
     }
+#pragma unroll
+    for (int j = 0; j < V; ++j) opaque(ln[j]);
     // early reading of the look-back window, issued once this thread's last
     // row has arrived
     EarlyWindow<ComplexLink, C::EW> early;
@@ -292,7 +306,7 @@ void samu_fwd_kernel(SamuFwdArgs x) {
     for (int j = 0; j < V; ++j) h[j] = caff_apply(s_seg[seg][cg * V + j], s_hin[cg * V + j]);
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        if (i < g.nrows) {
+        if (FULL || i < g.nrows) {
             RowOut<C::DT> orr, oii;
 #pragma unroll
             for (int j = 0; j < V; ++j) {
@@ -310,11 +324,33 @@ void samu_fwd_kernel(SamuFwdArgs x) {
     if (x.p.last_r && ends) {
 #pragma unroll
         for (int j = 0; j < V; ++j)
-            if (j < g.nvalid) {
+            if (FULL || j < g.nvalid) {
                 x.p.last_r[(size_t)g.bi * d.D + g.d0 + j] = h[j].r;
                 x.p.last_i[(size_t)g.bi * d.D + g.d0 + j] = h[j].i;
             }
     }
+}
+
+template <class C, bool ALIGNED, bool RST, bool OUT>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void samu_fwd_kernel(SamuFwdArgs x) {
+    constexpr int W = C::W, RG = C::RG, TPR = C::TPR;
+    constexpr int SEGS = C::WAVES * RG;
+    __shared__ CAff s_seg[SEGS][W];  // each segment's map, then the maps before it composed
+    __shared__ Cx s_hin[W];          // the state entering the tile, per lane
+
+    const int tid = threadIdx.x;
+    const int wave = uniform((int)(threadIdx.x / kWave));
+    const int l = tid % kWave;
+    const int rg = l / TPR;
+    const int cg = l % TPR;
+    const int seg = wave * RG + rg;
+    const Ticket tk = take_ticket(x.sc);
+    const Geo g = tile_geo<C, false>(tk.ticket, x.d, wave, rg, cg);
+    if (g.trow0 + C::CT <= x.d.T && g.dcol0 + W <= x.d.D)
+        samu_fwd_tile<C, ALIGNED, RST, OUT, true>(x, tk, g, seg, cg, s_seg, s_hin);
+    else
+        samu_fwd_tile<C, ALIGNED, RST, OUT, false>(x, tk, g, seg, cg, s_seg, s_hin);
 }
 
 // Transposing sum of N values per lane over the lanes {l ^ o}, o running
@@ -349,24 +385,19 @@ __device__ __forceinline__ void tsum(float* v, int lane) {
 // ---------------------------------------------------------------------------
 // reverse time
 // ---------------------------------------------------------------------------
+// One tile of the backward.  (Unlike the forward it has one body for all
+// tiles: a separate unguarded body for complete tiles raised its register
+// count past the budget and spilled.)
 template <class C, bool ALIGNED, bool RST>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
-void samu_bwd_kernel(SamuBwdArgs x) {
+__device__ __forceinline__ void samu_bwd_tile(const SamuBwdArgs& x, const Ticket& tk, const Geo& g,
+                                              int wave, int seg, int rg, int cg,
+                                              CAff (&s_seg)[C::WAVES * C::RG][C::W], Cx (&s_cin)[C::W],
+                                              float (&s_acc)[2][C::WAVES][C::W]) {
     constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
     constexpr int SEGS = WAVES * RG;
-    __shared__ CAff s_seg[SEGS][W];  // each segment's reverse map, then the maps after it composed
-    __shared__ Cx s_cin[W];          // the carry entering the tile from the right, per lane
-    __shared__ float s_acc[2][WAVES][W];
-
     const Dims d = x.d;
     const int tid = threadIdx.x;
-    const int wave = uniform((int)(threadIdx.x / kWave));
     const int l = tid % kWave;
-    const int rg = l / TPR;
-    const int cg = l % TPR;
-    const int seg = wave * RG + rg;
-    const Ticket tk = take_ticket(x.sc);
-    const Geo g = tile_geo<C, true>(tk.ticket, d, wave, rg, cg);
     const uint32_t rowbytes = (uint32_t)d.D * C::EB;
     const char* pgr = static_cast<const char*>(x.p.gr) + g.tbase;
     const char* pgi = static_cast<const char*>(x.p.gi) + g.tbase;
@@ -477,9 +508,12 @@ void samu_bwd_kernel(SamuBwdArgs x) {
     char* pgbr = static_cast<char*>(x.p.gbr) + g.tbase;
     char* pgbi = static_cast<char*>(x.p.gbi) + g.tbase;
     Cx carry[V];
-    // acc[2j], acc[2j+1]: this thread's sums over its rows of lane j's radial
-    // and phase terms (theta is applied once per tile and lane); tsum_[2i], [2i+1]: row i's sums over
-    // this thread's lanes of the radial and phase terms
+    // With w = conj(a) grad_a per element, the radial term is
+    // -nu e^eta Re(w) = -ln2 * nu2_j * e_t * Re(w) and the phase term Im(w).
+    // acc[2j], acc[2j+1]: this thread's sums over its rows of lane j's
+    // e_t Re(w) and Im(w) (the factor -ln2 nu2_j and theta are applied once
+    // per tile and lane); tsum_[2i], [2i+1]: row i's sums over this thread's
+    // lanes of nu2_j Re(w) and Im(w) (the factor -ln2 e_t once per row).
     float acc[2 * V], tsum_[2 * NR];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
@@ -498,13 +532,12 @@ void samu_bwd_kernel(SamuBwdArgs x) {
             float rsum = 0.0f, psum = 0.0f;
 #pragma unroll
             for (int j = 0; j < V; ++j) {
-                const float x2 = samu_x2(ln[j], tok[i]);
                 const Cx at = trans(i, j);
                 const Cx lam = cadd(vget(gr[i], gi[i], j), carry[j]);
                 Cx hp = vget(hr[i], hi[i], j);
-                if (row == 0) {
+                if (i == 0 && g.row0 == 0) {  // row 0: the state before it is h0, or 0
                     hp = Cx{0.0f, 0.0f};
-                    if (x.p.h0r && j < g.nvalid)
+                    if (x.p.h0r && (j < g.nvalid))
                         hp = Cx{x.p.h0r[(size_t)g.bi * d.D + g.d0 + j],
                                 x.p.h0i[(size_t)g.bi * d.D + g.d0 + j]};
                 }
@@ -514,12 +547,12 @@ void samu_bwd_kernel(SamuBwdArgs x) {
                 carry[j] = cmul(cconj(at), lam);
                 const Cx w = rs ? Cx{0.0f, 0.0f} : cmul(carry[j], cconj(hp));
                 const bool live = j < g.nvalid;
-                const float radial = live ? -(x2 * kLn2) * w.r : 0.0f;
-                const float phase = live ? w.i : 0.0f;
-                rsum += radial;
-                psum += phase;
-                acc[2 * j] += radial;
-                acc[2 * j + 1] += phase;
+                const float wr = live ? w.r : 0.0f;
+                const float wi = live ? w.i : 0.0f;
+                rsum = fmaf(ln[j].nu2, wr, rsum);
+                psum += wi;
+                acc[2 * j] = fmaf(tok[i].e, wr, acc[2 * j]);
+                acc[2 * j + 1] += wi;
                 obr.v[j] = lam.r;
                 obi.v[j] = lam.i;
             }
@@ -528,10 +561,12 @@ void samu_bwd_kernel(SamuBwdArgs x) {
                 store_vec<C::DT, ALIGNED>(pgbr, off, g.nvalid, obr);
                 store_vec<C::DT, ALIGNED>(pgbi, off, g.nvalid, obi);
             }
-            tsum_[2 * i] = rsum;
+            tsum_[2 * i] = rsum * -(tok[i].e * kLn2);
             tsum_[2 * i + 1] = psum;
         }
     }
+#pragma unroll
+    for (int j = 0; j < V; ++j) acc[2 * j] *= -(ln[j].nu2 * kLn2);
     // per-token partials over the row group's TPR lanes; value index 2i is
     // row i's radial sum, 2i + 1 its phase sum
     {
@@ -589,6 +624,26 @@ void samu_bwd_kernel(SamuBwdArgs x) {
             x.mode_theta[mp] = th * x.mode_tab[dl].y;  // d/dtheta_log = theta d/dtheta
         }
     }
+}
+
+template <class C, bool ALIGNED, bool RST>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void samu_bwd_kernel(SamuBwdArgs x) {
+    constexpr int W = C::W, RG = C::RG, WAVES = C::WAVES, TPR = C::TPR;
+    constexpr int SEGS = WAVES * RG;
+    __shared__ CAff s_seg[SEGS][W];  // each segment's reverse map, then the maps after it composed
+    __shared__ Cx s_cin[W];          // the carry entering the tile from the right, per lane
+    __shared__ float s_acc[2][WAVES][W];
+
+    const int tid = threadIdx.x;
+    const int wave = uniform((int)(threadIdx.x / kWave));
+    const int l = tid % kWave;
+    const int rg = l / TPR;
+    const int cg = l % TPR;
+    const int seg = wave * RG + rg;
+    const Ticket tk = take_ticket(x.sc);
+    const Geo g = tile_geo<C, true>(tk.ticket, x.d, wave, rg, cg);
+    samu_bwd_tile<C, ALIGNED, RST>(x, tk, g, wave, seg, rg, cg, s_seg, s_cin, s_acc);
 }
 
 // The second pass: dst[i] = sum_k src[k n + i] over k < count, for two arrays
