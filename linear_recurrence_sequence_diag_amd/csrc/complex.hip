@@ -280,7 +280,7 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
 // reverse time, tiled single launch
 // ---------------------------------------------------------------------------
 template <class C, bool ALIGNED, bool RST>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(3)))
 void cx_fused_bwd_kernel(CxBwdArgs x) {
     constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, TPR = C::TPR;
     constexpr int SEGS = C::WAVES * RG;
@@ -436,7 +436,7 @@ void cx_fused_bwd_kernel(CxBwdArgs x) {
             for (int j = 0; j < V; ++j) {
                 const Cx lam = cadd(vget(gr[i], gi[i], j), carry[j]);
                 Cx hp = vget(hr[i], hi[i], j);
-                if (row == 0 && !((rbits >> i) & 1u)) {
+                if (i == 0 && g.row0 == 0 && !((rbits >> i) & 1u)) {  // row 0: h0, or 0
                     hp = Cx{0.0f, 0.0f};
                     if (x.p.h0r && j < g.nvalid)
                         hp = Cx{x.p.h0r[(size_t)g.bi * d.D + g.d0 + j],
@@ -621,11 +621,15 @@ void dispatch2(bool al, bool rst, F&& f) {
 // rows per thread, wavefronts, look-back window>.  128 rows of 128-byte rows
 // per array; measured on MI355X (bf16 B8 T2048 M2560), 256-row tiles (8 rows
 // per thread, or 8 wavefronts) were no faster forward and 14-17% slower
-// backward, where six arrays of 8 rows no longer fit in registers.
+// backward, where six arrays of 8 rows no longer fit in registers.  The
+// backward looks back over 2 tiles, not 4: the window's words are what kept
+// it at 173 registers and 2 waves per SIMD; at 160 it runs 3 (155.6 ->
+// 145.5 us with the caches flushed; a window of 2 in the forward, at 3 or 4
+// waves, changed nothing measurable).
 template <int DT>
 using CxFwdCfg = Cfg<DT, 8, 4, 4, 4>;
 template <int DT>
-using CxBwdCfg = Cfg<DT, 8, 4, 4, 4>;
+using CxBwdCfg = Cfg<DT, 8, 4, 4, 2>;
 
 Layout cx_fwd_layout(const Shape& s) {
     return layout_of(s, CxFwdCfg<DT_F32>::TPR, CxFwdCfg<DT_F32>::CT);

@@ -498,7 +498,7 @@ void fused_bwd_kernel(BwdArgs x) {
                 const float an = (i + 1 < NR && after) ? ra[i + 1 < NR ? i + 1 : i].get(j) : 1.0f;
                 lam[j] = fmaf(an, lam[j], rg_[i].get(j));
                 float hp = rh[i].get(j);
-                if (row == 0 && !((rbits >> i) & 1u))
+                if (i == 0 && g.row0 == 0 && !((rbits >> i) & 1u))  // row 0: h0, or 0
                     hp = (x.h0 && j < g.nvalid) ? x.h0[(size_t)g.bi * d.D + g.d0 + j] : 0.0f;
                 ob.v[j] = lam[j];
                 oa.v[j] = lam[j] * hp;
