@@ -148,7 +148,7 @@ struct CxWords {
 };
 __device__ __forceinline__ CxWords cx_words(const Scratch& sc, uint32_t phase) {
     unsigned long long* base =
-        reinterpret_cast<unsigned long long*>(sc.region[phase] + sc.ctr_words);
+        reinterpret_cast<unsigned long long*>(sc.region[phase]);
     return CxWords{base, base + sc.entries, base + 2 * sc.entries};
 }
 

@@ -262,8 +262,8 @@ void fused_fwd_kernel(FwdArgs x) {
     for (int j = 0; j < V; ++j) s_seg[seg][cg * V + j] = m[j];
     const uint32_t phase = tk.phase;
     const unsigned long long* pqs =
-        reinterpret_cast<const unsigned long long*>(x.sc.region[phase] + x.sc.ctr_words);
-    const uint32_t* hs = x.sc.region[phase] + x.sc.ctr_words + 2 * x.sc.entries;
+        reinterpret_cast<const unsigned long long*>(x.sc.region[phase]);
+    const uint32_t* hs = x.sc.region[phase] + 2 * x.sc.entries;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         opaque(ra[i]);
@@ -437,8 +437,8 @@ void fused_bwd_kernel(BwdArgs x) {
     for (int j = 0; j < V; ++j) s_seg[seg][cg * V + j] = m[j];
     const uint32_t phase = tk.phase;
     const unsigned long long* pqs =
-        reinterpret_cast<const unsigned long long*>(x.sc.region[phase] + x.sc.ctr_words);
-    const uint32_t* hs = x.sc.region[phase] + x.sc.ctr_words + 2 * x.sc.entries;
+        reinterpret_cast<const unsigned long long*>(x.sc.region[phase]);
+    const uint32_t* hs = x.sc.region[phase] + 2 * x.sc.entries;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         opaque(ra[i]);

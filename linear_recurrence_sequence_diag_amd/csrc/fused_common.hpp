@@ -21,17 +21,14 @@ namespace {
 constexpr uint32_t kDefaultPolls = 1024;
 
 
-// Workspace of the fused form: a 256-byte header, then two regions of equal
-// size.  A region holds nC ticket counters (each in its own 128-byte line),
-// then the published tile maps (P, Q), then the published inclusive states H
-// (3 words per entry for a real scan, 6 for a complex one).  A
-// launch uses region `phase`, which is all-ones wherever it will write; it
-// clears the words the previous launch dirtied in the other region, counters
-// included.  The workgroup that takes the last ticket of the last counter to
-// run out records how many words this launch dirties, resets the other
-// phase's count of exhausted counters and flips the phase.  By then every
-// workgroup has read the phase, so back-to-back launches on one stream (or
-// replays of a captured graph) need no separate initialisation step.
+// Workspace of the fused form: a header, the ticket counters, then two
+// regions of equal size.  A region holds the published tile maps (P, Q), then
+// the published inclusive states H (3 words per entry for a real scan, 6 for
+// a complex one).  A launch uses region `phase`, which is all-ones wherever it
+// will write, and clears the words the previous launch dirtied in the other
+// region (the header records how many, per region), so back-to-back launches
+// on one stream (or replays of a captured graph) need no separate
+// initialisation step.
 //
 // Tickets.  Same-address atomics serialise (about 11.5 ns each on MI355X: one
 // counter for 2560 workgroups costs 30 us), so tickets come from nC counters,
@@ -43,36 +40,36 @@ constexpr uint32_t kDefaultPolls = 1024;
 // always drains.  Workgroups are spread over counters so that each counter is
 // fed from all XCDs and the counters advance together, which keeps the rows
 // in flight close to each other (this matters for DRAM locality).
+//
+// A counter is one 64-bit word: the launches it has served (its epoch) in
+// the high half, the tickets taken in the current launch in the low half, so
+// the one atomic increment that takes a ticket also says which region this
+// launch uses (the epoch's parity).  The taker of a counter's last ticket
+// moves it to the next epoch with its count back at zero, and also moves on
+// the counters this launch leaves unused, so that every counter's epoch
+// counts every launch on the workspace.  (Reading a separate phase word
+// before the increment cost a second round trip, about 1 us of the 2 us a
+// tile spent getting its ticket.)
 struct Header {
-    uint32_t phase;
-    uint32_t reserved;
-    unsigned long long dirty[2];  // words the last user of each region wrote
-    uint32_t pad[26];
-    uint32_t done[2];             // per phase: counters run out (all-ones: none)
+    unsigned long long dirty[2];  // words the last launch using each region wrote there
+    uint32_t pad[60];
 };
-static_assert(offsetof(Header, done) == 128, "the counter tally starts a new cache line");
+static_assert(sizeof(Header) == 256, "header size");
 
-constexpr int kCtrStride = 32;  // words between ticket counters (one 128-byte line each)
+constexpr int kCtrStride = 16;  // 64-bit words between ticket counters (one 128-byte line each)
 constexpr int kMaxCounters = 64;
+constexpr int kHeaderBytes = (int)sizeof(Header) + kMaxCounters * kCtrStride * 8;
 
 struct Scratch {
     Header* hdr;
+    unsigned long long* ctr;       // kMaxCounters counters, kCtrStride words apart
     uint32_t* region[2];
     unsigned long long entries;    // NK * nS * W published entries
     uint32_t words;                // 32-bit words each entry publishes (map + state)
-    unsigned long long ctr_words;  // nC * kCtrStride
     uint32_t total_tiles;
     uint32_t nC;                   // ticket counters (divides nS)
     uint32_t quota;                // tickets per counter = total_tiles / nC
 };
-
-constexpr int kHeaderBytes = 256;
-
-__device__ __forceinline__ void header_update(const Scratch& sc, uint32_t p) {
-    publish_u32(&sc.hdr->done[p ^ 1u], kEmpty);
-    publish_u64(&sc.hdr->dirty[p], sc.ctr_words + (unsigned long long)sc.words * sc.entries);
-    publish_u32(&sc.hdr->phase, p ^ 1u);
-}
 
 // ---------------------------------------------------------------------------
 // tile configuration
@@ -155,18 +152,32 @@ struct Ticket {
     unsigned long long nclear;
 };
 
+// Thread 0: the ticket, the region of this launch and the number of words to
+// clear, in one round trip (the header's two counts are read beside the
+// increment and the one for the other region kept).
 __device__ __forceinline__ Ticket take_ticket(const Scratch& sc) {
     __shared__ Ticket s_t;
     if (threadIdx.x == 0) {
-        const uint32_t p = peek_u32(&sc.hdr->phase);
         const uint32_t b = blockIdx.x;
         const uint32_t c = (b % sc.nC + b / sc.nC) % sc.nC;  // a permutation within each row of nC
-        const uint32_t i = atomicAdd(sc.region[p] + (size_t)c * kCtrStride, 1u) + 1u;
+        const unsigned long long d0 = peek_u64(&sc.hdr->dirty[0]);
+        const unsigned long long d1 = peek_u64(&sc.hdr->dirty[1]);
+        unsigned long long* w = sc.ctr + (size_t)c * kCtrStride;
+        const unsigned long long v = atomicAdd(w, 1ull);
+        const uint32_t i = (uint32_t)v;
+        const uint32_t p = (uint32_t)(v >> 32) & 1u;
         s_t.phase = p;
         s_t.ticket = i * sc.nC + c;
-        s_t.nclear = sc.hdr->dirty[p ^ 1u];
-        if (i == sc.quota - 1 && atomicAdd(&sc.hdr->done[p], 1u) + 1u == sc.nC - 1)
-            header_update(sc, p);
+        s_t.nclear = p ? d0 : d1;
+        if (i == sc.quota - 1) {
+            // the counter's last ticket of this launch: next epoch, count 0;
+            // the same for the counters this launch leaves unused
+            atomicAdd(w, (1ull << 32) - sc.quota);
+            for (uint32_t u = c + sc.nC; u < (uint32_t)kMaxCounters; u += sc.nC)
+                atomicAdd(sc.ctr + (size_t)u * kCtrStride, 1ull << 32);
+        }
+        if (i == 0 && c == 0)
+            publish_u64(&sc.hdr->dirty[p], (unsigned long long)sc.words * sc.entries);
     }
     __syncthreads();
     Ticket t;
@@ -390,15 +401,12 @@ struct TreeFold {
     __device__ __forceinline__ M total() const { return top; }
 };
 
-// Workspace initialisation: header (phase 0, both counters unused, nothing
-// dirty) and both regions all-ones.
+// Workspace initialisation: header and counters zero (nothing dirty, epoch
+// 0, no tickets taken) and both regions all-ones.
 __global__ void scratch_init_kernel(uint32_t* __restrict__ p, size_t words) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
-         i += (size_t)gridDim.x * blockDim.x) {
-        uint32_t v = kEmpty;
-        if (i < kHeaderBytes / 4) v = (i == 32 || i == 33) ? kEmpty : 0u;  // Header::done
-        p[i] = v;
-    }
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = i < (size_t)kHeaderBytes / 4 ? 0u : kEmpty;
 }
 
 struct Layout {
@@ -430,13 +438,9 @@ int counters_of(const Layout& L) {
     return c;
 }
 
-unsigned long long ctr_words_of(const Layout& L) {
-    return (unsigned long long)counters_of(L) * kCtrStride;
-}
-
 // Bytes of one region for `words` 32-bit words per published entry.
 size_t region_bytes_for(const Layout& L, int words) {
-    return ((ctr_words_of(L) + (unsigned long long)words * L.entries) * 4 + 255) / 256 * 256;
+    return ((unsigned long long)words * L.entries * 4 + 255) / 256 * 256;
 }
 
 // Region size implied by a workspace size (the same for every call on one buffer).
@@ -458,11 +462,11 @@ hipError_t prepare(void* ws, size_t ws_bytes, bool init, const Layout& L, int wo
         if (e != hipSuccess) return e;
     }
     sc->hdr = reinterpret_cast<Header*>(base);
+    sc->ctr = reinterpret_cast<unsigned long long*>(base + sizeof(Header));
     sc->region[0] = reinterpret_cast<uint32_t*>(base + kHeaderBytes);
     sc->region[1] = reinterpret_cast<uint32_t*>(base + kHeaderBytes + rb);
     sc->entries = L.entries;
     sc->words = (uint32_t)words;
-    sc->ctr_words = ctr_words_of(L);
     sc->total_tiles = (uint32_t)((unsigned long long)L.NK * L.nS);
     sc->nC = (uint32_t)counters_of(L);
     sc->quota = sc->total_tiles / sc->nC;
