@@ -413,16 +413,19 @@ __device__ __forceinline__ void samu_bwd_tile(const SamuBwdArgs& x, const Ticket
         gr[i] = load_vec<C::DT, ALIGNED, true>(pgr, off, g.nvalid, 0.0f);
         gi[i] = load_vec<C::DT, ALIGNED, true>(pgi, off, g.nvalid, 0.0f);
     }
-    // the rows of `out` last: only the replay uses them
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
+    // The rows of `out` last, as only the replay uses them; the later half
+    // now, the earlier half during the replay (the replay walks the rows
+    // from the last), so that the two halves never hold registers at once.
+    auto load_h = [&](int i, int z) {
         const int row = g.row0 + i;
         const int rc = row < d.T ? row : d.T - 1;
         const int hrw = rc >= 1 ? rc - 1 : 0;
-        const uint32_t hoff = (uint32_t)(hrw - hrow0) * rowbytes + g.coff;
+        const uint32_t hoff = (uint32_t)(hrw - hrow0) * rowbytes + g.coff + (uint32_t)z;
         hr[i] = load_vec<C::DT, ALIGNED, true>(phr, hoff, g.nvalid, 0.0f);
         hi[i] = load_vec<C::DT, ALIGNED, true>(phi, hoff, g.nvalid, 0.0f);
-    }
+    };
+#pragma unroll
+    for (int i = NR / 2; i < NR; ++i) load_h(i, 0);
     SamuTok tok[NR];
     uint32_t rbits = 0;
 #pragma unroll
@@ -525,6 +528,14 @@ __device__ __forceinline__ void samu_bwd_tile(const SamuBwdArgs& x, const Ticket
 #pragma unroll
     for (int i = NR - 1; i >= 0; --i) {
         const int row = g.row0 + i;
+        if (i == NR - 3) {
+            // the earlier half of `out`, once two rows have freed their
+            // registers (addressed with a zero that depends on the carry,
+            // so the loads cannot be issued sooner)
+            const int z = zero_after(carry[0].r);
+#pragma unroll
+            for (int r = 0; r < NR / 2; ++r) load_h(r, z);
+        }
         tsum_[2 * i] = 0.0f;
         tsum_[2 * i + 1] = 0.0f;
         if (row < d.T) {  // the same for every lane of a row group

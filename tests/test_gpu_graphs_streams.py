@@ -222,3 +222,33 @@ def test_captured_decode_loop(dt):
     _, last = lr.scan(a, b, algo="seq")
     torch.cuda.synchronize()
     assert torch.equal(last, eager_state)
+
+
+def test_one_workspace_across_shapes():
+    """One stream's library workspace serves calls whose tiles come from
+    different numbers of ticket counters (1, 2, 4 and 64 lane-block chains
+    per counter set) and different directions, one after another, twice
+    round: every result equals the same call made on a stream of its own,
+    bit for bit (each launch must find its region clean and leave the
+    counters and the other region's count right for the next one)."""
+    shapes = [(1, 3000, 64, "bf16"), (4, 1500, 1024, "bf16"), (3, 777, 200, "f32"),
+              (2, 5000, 130, "bf16"), (2, 2100, 96, "f32")]
+    data = []
+    for n, (B, T, D, dt) in enumerate(shapes):
+        r = W.random_inputs(B, T, D, dt, seed=200 + n, a_lo=0.5, a_hi=0.99)
+        data.append((dev(r.a, dt), dev(r.b, dt), dev(r.g, dt)))
+    refs = []
+    for x in data:
+        st = fresh_stream()
+        with torch.cuda.stream(st):
+            refs.append([t.clone() for t in real_step(*x)])
+        torch.cuda.synchronize()
+    shared = fresh_stream()
+    for rnd in range(2):
+        for n, x in enumerate(data):
+            with torch.cuda.stream(shared):
+                res = real_step(*x)
+            torch.cuda.synchronize()
+            for k, (u, v) in enumerate(zip(res, refs[n])):
+                assert torch.equal(u, v), f"round {rnd}, shape {shapes[n]}: output {k} differs"
+    log(f"one workspace, {len(shapes)} shapes x 2 rounds: bitwise equal to separate streams")
