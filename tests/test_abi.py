@@ -150,6 +150,14 @@ def test_workspace_sizes_and_auto_choice():
             # rows too long for the fused form's 32-bit in-tile offsets: the chunked form
             algo, chunk, _ = lr.scan_auto_algo(1, 32, 1 << 25, dt, direction)
             assert algo == lr.ALGO_CHUNKED and chunk > 0
+            # a fused grid of 2^32 work-items or more (2^24 tiles of 256 threads;
+            # 64 lanes are one 128-byte lane block in bf16, two in fp32): the
+            # chunked form, not a launch that would fail
+            edge = (1 << 16) if dt == lr.BF16 else (1 << 15)
+            algo, chunk, _ = lr.scan_auto_algo(edge, 1 << 16, 64, dt, direction)
+            assert algo == lr.ALGO_CHUNKED and chunk > 0
+            algo, _, _ = lr.scan_auto_algo(edge - 1, 1 << 16, 64, dt, direction)
+            assert algo == lr.ALGO_FUSED
             # short sequences over millions of lanes: the per-lane walk
             algo, chunk, _ = lr.scan_auto_algo(1, 1, (1 << 22) + 5, dt, direction)
             assert algo == lr.ALGO_SEQ
