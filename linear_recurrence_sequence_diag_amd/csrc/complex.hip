@@ -53,7 +53,7 @@ struct CxBwdArgs {
 template <class C>
 __device__ CAff cx_fwd_tile_map(const CxFwdArgs& x, int j, int bi, int col) {
     constexpr int NR = C::NR, SEGS = C::WAVES * C::RG;
-    CAff A = caff_identity();
+    CAff A = caff_identity(), Wv = caff_identity();
     if (col >= x.d.D) return A;
     const size_t rowbytes = (size_t)x.d.D * C::EB;
     const size_t b0 = (size_t)bi * x.d.T * rowbytes;
@@ -78,7 +78,11 @@ __device__ CAff cx_fwd_tile_map(const CxFwdArgs& x, int j, int bi, int col) {
             }
             t = caff_then(t, fwd_step(at, bt));
         }
-        A = caff_then(A, t);
+        Wv = caff_then(Wv, t);
+        if (sg % C::RG == C::RG - 1) {  // a wavefront's segments, then the wavefronts in order
+            A = caff_then(A, Wv);
+            Wv = caff_identity();
+        }
     }
     return CAff{unpack_cx(pack_cx(A.p)), unpack_cx(pack_cx(A.q))};
 }
@@ -127,7 +131,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void cx_fused_fwd_kernel(CxFwdArgs x) {
     constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, TPR = C::TPR;
     constexpr int SEGS = C::WAVES * RG;
-    __shared__ CAff s_seg[SEGS][W];  // each segment's map, then the maps before it composed
+    __shared__ CAff s_seg[SEGS][W];  // each segment's map, then its wavefront's maps before it composed
+    __shared__ CAff s_wav[C::WAVES][W];  // each wavefront's map, then the wavefronts' before it composed
     __shared__ Cx s_hin[W];          // the state entering the tile, per lane
 
     const Dims d = x.d;
@@ -189,6 +194,8 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
         for (int i = 0; i < NR; ++i) m = caff_then(m, fwd_step(vget(ar[i], ai[i], j), vget(br[i], bi[i], j)));
         s_seg[seg][cg * V + j] = m;
     }
+    fold_wave_segments<C, false, CAffThen>(s_seg, s_wav, seg / C::RG, (int)threadIdx.x % kWave,
+                                           caff_identity());
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         opaque(ar[i]);
@@ -211,10 +218,10 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
         const int c = tid;
         const CxWords wd = cx_words(x.sc, tk.phase);
         CAff A = caff_identity();
-#pragma unroll 4
-        for (int sg = 0; sg < SEGS; ++sg) {
-            const CAff t = s_seg[sg][c];
-            s_seg[sg][c] = A;
+#pragma unroll
+        for (int w = 0; w < C::WAVES; ++w) {
+            const CAff t = s_wav[w][c];
+            s_wav[w][c] = A;
             A = caff_then(A, t);
         }
         const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
@@ -248,7 +255,8 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
     char* poi = static_cast<char*>(x.p.out_i) + g.tbase;
     Cx h[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) h[j] = caff_apply(s_seg[seg][cg * V + j], s_hin[cg * V + j]);
+    for (int j = 0; j < V; ++j) h[j] = caff_apply(s_seg[seg][cg * V + j],
+                          caff_apply(s_wav[seg / C::RG][cg * V + j], s_hin[cg * V + j]));
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         if (full || i < g.nrows) {
@@ -622,10 +630,12 @@ void dispatch2(bool al, bool rst, F&& f) {
 // per array; measured on MI355X (bf16 B8 T2048 M2560), 256-row tiles (8 rows
 // per thread, or 8 wavefronts) were no faster forward and 14-17% slower
 // backward, where six arrays of 8 rows no longer fit in registers.  The
-// backward looks back over 2 tiles, not 4: the window's words are what kept
-// it at 173 registers and 2 waves per SIMD; at 160 it runs 3 (155.6 ->
-// 145.5 us with the caches flushed; a window of 2 in the forward, at 3 or 4
-// waves, changed nothing measurable).
+// backward folds its segments in one level (the forward's two levels,
+// wavefront segments first, raised it to 168 registers with 8 spilled:
+// 145.3 -> 152.7 us) and looks back over 2 tiles, not 4: the window's words
+// are what kept it at 173 registers and 2 waves per SIMD; at 160 it runs 3
+// (155.6 -> 145.5 us with the caches flushed; a window of 2 in the forward,
+// at 3 or 4 waves, changed nothing measurable).
 template <int DT>
 using CxFwdCfg = Cfg<DT, 8, 4, 4, 4>;
 template <int DT>

@@ -118,8 +118,8 @@ struct BwdArgs {
 // order.  Lanes past D are the identity.
 template <class C>
 __device__ Aff fwd_tile_map(const FwdArgs& x, int j, int bi, int col) {
-    constexpr int NR = C::NR, SEGS = C::WAVES * C::RG;
-    Aff A = aff_identity();
+    constexpr int NR = C::NR, RG = C::RG, SEGS = C::WAVES * C::RG;
+    Aff A = aff_identity(), Wv = aff_identity();
     if (col >= x.d.D) return A;
     // wave-uniform row addresses, one 32-bit lane offset
     const size_t rowbytes = (size_t)x.d.D * C::EB;
@@ -143,7 +143,11 @@ __device__ Aff fwd_tile_map(const FwdArgs& x, int j, int bi, int col) {
             t.p = at * t.p;
             t.q = fmaf(at, t.q, bt);
         }
-        A = aff_then(A, t);
+        Wv = aff_then(Wv, t);
+        if (sg % RG == RG - 1) {  // a wavefront's segments, then the wavefronts in order
+            A = aff_then(A, Wv);
+            Wv = aff_identity();
+        }
     }
     return unpack_aff(pack_aff(A));
 }
@@ -152,8 +156,8 @@ __device__ Aff fwd_tile_map(const FwdArgs& x, int j, int bi, int col) {
 // to the first.
 template <class C>
 __device__ Aff bwd_tile_map(const BwdArgs& x, int j, int bi, int col) {
-    constexpr int NR = C::NR, SEGS = C::WAVES * C::RG;
-    Aff A = aff_identity();
+    constexpr int NR = C::NR, RG = C::RG, SEGS = C::WAVES * C::RG;
+    Aff A = aff_identity(), Wv = aff_identity();
     if (col >= x.d.D) return A;
     const size_t rowbytes = (size_t)x.d.D * C::EB;
     const char* a0 = static_cast<const char*>(x.a) + (size_t)bi * x.d.T * rowbytes;
@@ -176,7 +180,11 @@ __device__ Aff bwd_tile_map(const BwdArgs& x, int j, int bi, int col) {
             t.p = at * t.p;
             t.q = at * (t.q + gt);
         }
-        A = aff_then(A, t);
+        Wv = aff_then(Wv, t);
+        if (sg % RG == 0) {  // a wavefront's segments (last first), then the wavefronts
+            A = aff_then(A, Wv);
+            Wv = aff_identity();
+        }
     }
     return unpack_aff(pack_aff(A));
 }
@@ -191,7 +199,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC_F)
 void fused_fwd_kernel(FwdArgs x) {
     constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, TPR = C::TPR;
     constexpr int SEGS = C::WAVES * RG;
-    __shared__ Aff s_seg[SEGS][W];  // each segment's map, then the maps before it composed
+    __shared__ Aff s_seg[SEGS][W];  // each segment's map, then its wavefront's maps before it composed
+    __shared__ Aff s_wav[C::WAVES][W];  // each wavefront's map, then the wavefronts' before it composed
     __shared__ float s_hin[W];      // the state entering the tile, per lane
 
     const Dims d = x.d;
@@ -260,6 +269,7 @@ void fused_fwd_kernel(FwdArgs x) {
     const int seg = wave * RG + rg;
 #pragma unroll
     for (int j = 0; j < V; ++j) s_seg[seg][cg * V + j] = m[j];
+    fold_wave_segments<C, false, AffThen>(s_seg, s_wav, wave, l, aff_identity());
     const uint32_t phase = tk.phase;
     const unsigned long long* pqs =
         reinterpret_cast<const unsigned long long*>(x.sc.region[phase]);
@@ -284,10 +294,10 @@ void fused_fwd_kernel(FwdArgs x) {
     if (tid < W) {
         const int c = tid;
         Aff A = aff_identity();
-#pragma unroll 8
-        for (int sg = 0; sg < SEGS; ++sg) {
-            const Aff t = s_seg[sg][c];
-            s_seg[sg][c] = A;
+#pragma unroll
+        for (int w = 0; w < C::WAVES; ++w) {
+            const Aff t = s_wav[w][c];
+            s_wav[w][c] = A;
             A = aff_then(A, t);
         }
         const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
@@ -316,7 +326,8 @@ void fused_fwd_kernel(FwdArgs x) {
     // replay from registers
     float h[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) h[j] = aff_apply(s_seg[seg][cg * V + j], s_hin[cg * V + j]);
+    for (int j = 0; j < V; ++j)
+        h[j] = aff_apply(s_seg[seg][cg * V + j], aff_apply(s_wav[wave][cg * V + j], s_hin[cg * V + j]));
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         if (full || i < g.nrows) {
@@ -345,7 +356,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC_B)
 void fused_bwd_kernel(BwdArgs x) {
     constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, TPR = C::TPR;
     constexpr int SEGS = C::WAVES * RG;
-    __shared__ Aff s_seg[SEGS][W];  // each segment's reverse map, then the maps after it composed
+    __shared__ Aff s_seg[SEGS][W];  // each segment's reverse map, then its wavefront's maps after it composed
+    __shared__ Aff s_wav[C::WAVES][W];  // each wavefront's reverse map, then the wavefronts' after it composed
     __shared__ float s_cin[W];      // the carry entering the tile from the right, per lane
 
     const Dims d = x.d;
@@ -435,6 +447,7 @@ void fused_bwd_kernel(BwdArgs x) {
     const int seg = wave * RG + rg;
 #pragma unroll
     for (int j = 0; j < V; ++j) s_seg[seg][cg * V + j] = m[j];
+    fold_wave_segments<C, true, AffThen>(s_seg, s_wav, wave, l, aff_identity());
     const uint32_t phase = tk.phase;
     const unsigned long long* pqs =
         reinterpret_cast<const unsigned long long*>(x.sc.region[phase]);
@@ -456,10 +469,10 @@ void fused_bwd_kernel(BwdArgs x) {
     if (tid < W) {
         const int c = tid;
         Aff A = aff_identity();
-#pragma unroll 8
-        for (int sg = SEGS - 1; sg >= 0; --sg) {
-            const Aff t = s_seg[sg][c];
-            s_seg[sg][c] = A;
+#pragma unroll
+        for (int w = C::WAVES - 1; w >= 0; --w) {
+            const Aff t = s_wav[w][c];
+            s_wav[w][c] = A;
             A = aff_then(A, t);
         }
         const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
@@ -486,7 +499,8 @@ void fused_bwd_kernel(BwdArgs x) {
     // after it (the carry itself for the first row processed)
     float lam[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) lam[j] = aff_apply(s_seg[seg][cg * V + j], s_cin[cg * V + j]);
+    for (int j = 0; j < V; ++j)
+        lam[j] = aff_apply(s_seg[seg][cg * V + j], aff_apply(s_wav[wave][cg * V + j], s_cin[cg * V + j]));
 #pragma unroll
     for (int i = NR - 1; i >= 0; --i) {
         if (full || i < g.nrows) {

@@ -401,6 +401,41 @@ struct TreeFold {
     __device__ __forceinline__ M total() const { return top; }
 };
 
+// First level of a tile's fold, per wavefront and lane, right after the
+// wavefront has written its segments' maps to s_seg: the wavefront's RG
+// segments are folded in order (REV: from the last), each replaced by the
+// composition of the wavefront's segments before it (an exclusive prefix),
+// and the total goes to s_wav.  All wavefronts do this at once; the
+// look-back wavefront then folds only the WAVES totals, which shortens the
+// serial fold before a tile's map is published from WAVES*RG steps to
+// RG + WAVES.  Lane c of a row is folded by lane c % 64 of the wavefront
+// (W / 64 lanes each, or one by each of the first W lanes when W < 64).
+// Then::then(e, l) is the composition "l after e".
+template <class C, bool REV, class Then, class M>
+__device__ __forceinline__ void fold_wave_segments(M (&s_seg)[C::WAVES * C::RG][C::W],
+                                                   M (&s_wav)[C::WAVES][C::W], int wave, int l,
+                                                   M identity) {
+    constexpr int RG = C::RG, W = C::W;
+    // the wavefront's own writes above, visible to all of its lanes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int q = 0; q < (W + kWave - 1) / kWave; ++q) {
+        const int c = q * kWave + l;
+        if (W < kWave && c >= W) break;
+        M A = identity;
+#pragma unroll
+        for (int r0 = 0; r0 < RG; ++r0) {
+            const int r = REV ? RG - 1 - r0 : r0;
+            const M t = s_seg[wave * RG + r][c];
+            s_seg[wave * RG + r][c] = A;
+            A = Then::then(A, t);
+        }
+        s_wav[wave][c] = A;
+    }
+}
+
 // Workspace initialisation: header and counters zero (nothing dirty, epoch
 // 0, no tickets taken) and both regions all-ones.
 __global__ void scratch_init_kernel(uint32_t* __restrict__ p, size_t words) {

@@ -109,7 +109,7 @@ struct SamuBwdArgs {
 template <class C>
 __device__ CAff samu_fwd_tile_map(const SamuFwdArgs& x, int j, int bi, int col) {
     constexpr int NR = C::NR, SEGS = C::WAVES * C::RG;
-    CAff A = caff_identity();
+    CAff A = caff_identity(), Wv = caff_identity();
     if (col >= x.d.D) return A;
     const SamuLane L = samu_lane(x.mode_tab, col);
     const size_t rowbytes = (size_t)x.d.D * C::EB;
@@ -134,7 +134,11 @@ __device__ CAff samu_fwd_tile_map(const SamuFwdArgs& x, int j, int bi, int col) 
             }
             t = caff_then(t, fwd_step(at, bt));
         }
-        A = caff_then(A, t);
+        Wv = caff_then(Wv, t);
+        if (sg % C::RG == C::RG - 1) {  // a wavefront's segments, then the wavefronts in order
+            A = caff_then(A, Wv);
+            Wv = caff_identity();
+        }
     }
     return CAff{unpack_cx(pack_cx(A.p)), unpack_cx(pack_cx(A.q))};
 }
@@ -142,7 +146,7 @@ __device__ CAff samu_fwd_tile_map(const SamuFwdArgs& x, int j, int bi, int col) 
 template <class C>
 __device__ CAff samu_bwd_tile_map(const SamuBwdArgs& x, int j, int bi, int col) {
     constexpr int NR = C::NR, SEGS = C::WAVES * C::RG;
-    CAff A = caff_identity();
+    CAff A = caff_identity(), Wv = caff_identity();
     if (col >= x.d.D) return A;
     const SamuLane L = samu_lane(x.mode_tab, col);
     const size_t rowbytes = (size_t)x.d.D * C::EB;
@@ -167,7 +171,11 @@ __device__ CAff samu_bwd_tile_map(const SamuBwdArgs& x, int j, int bi, int col) 
             }
             t = rev_fold(t, at, gt);
         }
-        A = caff_then(A, t);
+        Wv = caff_then(Wv, t);
+        if (sg % C::RG == 0) {  // a wavefront's segments (last first), then the wavefronts
+            A = caff_then(A, Wv);
+            Wv = caff_identity();
+        }
     }
     return CAff{unpack_cx(pack_cx(A.p)), unpack_cx(pack_cx(A.q))};
 }
@@ -192,7 +200,7 @@ __device__ __forceinline__ void tile_marker() {
 template <class C, bool ALIGNED, bool RST, bool OUT, bool FULL>
 __device__ __forceinline__ void samu_fwd_tile(const SamuFwdArgs& x, const Ticket& tk, const Geo& g,
                                               int seg, int cg, CAff (&s_seg)[C::WAVES * C::RG][C::W],
-                                              Cx (&s_hin)[C::W]) {
+                                              CAff (&s_wav)[C::WAVES][C::W], Cx (&s_hin)[C::W]) {
     constexpr int V = C::V, W = C::W, NR = C::NR, SEGS = C::WAVES * C::RG;
     tile_marker<FULL>();
     const Dims d = x.d;
@@ -244,6 +252,8 @@ __device__ __forceinline__ void samu_fwd_tile(const SamuFwdArgs& x, const Ticket
         }
         s_seg[seg][cg * V + j] = m;
     }
+    fold_wave_segments<C, false, CAffThen>(s_seg, s_wav, seg / C::RG, (int)threadIdx.x % kWave,
+                                           caff_identity());
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         opaque(br[i]);
@@ -266,10 +276,10 @@ __device__ __forceinline__ void samu_fwd_tile(const SamuFwdArgs& x, const Ticket
         const int c = tid;
         const CxWords wd = cx_words(x.sc, tk.phase);
         CAff A = caff_identity();
-#pragma unroll 4
-        for (int sg = 0; sg < SEGS; ++sg) {
-            const CAff t = s_seg[sg][c];
-            s_seg[sg][c] = A;
+#pragma unroll
+        for (int w = 0; w < C::WAVES; ++w) {
+            const CAff t = s_wav[w][c];
+            s_wav[w][c] = A;
             A = caff_then(A, t);
         }
         const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
@@ -303,7 +313,8 @@ __device__ __forceinline__ void samu_fwd_tile(const SamuFwdArgs& x, const Ticket
     char* poi = static_cast<char*>(x.p.out_i) + g.tbase;
     Cx h[V];
 #pragma unroll
-    for (int j = 0; j < V; ++j) h[j] = caff_apply(s_seg[seg][cg * V + j], s_hin[cg * V + j]);
+    for (int j = 0; j < V; ++j) h[j] = caff_apply(s_seg[seg][cg * V + j],
+                          caff_apply(s_wav[seg / C::RG][cg * V + j], s_hin[cg * V + j]));
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         if (FULL || i < g.nrows) {
@@ -336,7 +347,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void samu_fwd_kernel(SamuFwdArgs x) {
     constexpr int W = C::W, RG = C::RG, TPR = C::TPR;
     constexpr int SEGS = C::WAVES * RG;
-    __shared__ CAff s_seg[SEGS][W];  // each segment's map, then the maps before it composed
+    __shared__ CAff s_seg[SEGS][W];  // each segment's map, then its wavefront's maps before it composed
+    __shared__ CAff s_wav[C::WAVES][W];  // each wavefront's map, then the wavefronts' before it composed
     __shared__ Cx s_hin[W];          // the state entering the tile, per lane
 
     const int tid = threadIdx.x;
@@ -348,9 +360,9 @@ void samu_fwd_kernel(SamuFwdArgs x) {
     const Ticket tk = take_ticket(x.sc);
     const Geo g = tile_geo<C, false>(tk.ticket, x.d, wave, rg, cg);
     if (g.trow0 + C::CT <= x.d.T && g.dcol0 + W <= x.d.D)
-        samu_fwd_tile<C, ALIGNED, RST, OUT, true>(x, tk, g, seg, cg, s_seg, s_hin);
+        samu_fwd_tile<C, ALIGNED, RST, OUT, true>(x, tk, g, seg, cg, s_seg, s_wav, s_hin);
     else
-        samu_fwd_tile<C, ALIGNED, RST, OUT, false>(x, tk, g, seg, cg, s_seg, s_hin);
+        samu_fwd_tile<C, ALIGNED, RST, OUT, false>(x, tk, g, seg, cg, s_seg, s_wav, s_hin);
 }
 
 // Transposing sum of N values per lane over the lanes {l ^ o}, o running
@@ -391,7 +403,8 @@ __device__ __forceinline__ void tsum(float* v, int lane) {
 template <class C, bool ALIGNED, bool RST>
 __device__ __forceinline__ void samu_bwd_tile(const SamuBwdArgs& x, const Ticket& tk, const Geo& g,
                                               int wave, int seg, int rg, int cg,
-                                              CAff (&s_seg)[C::WAVES * C::RG][C::W], Cx (&s_cin)[C::W],
+                                              CAff (&s_seg)[C::WAVES * C::RG][C::W],
+                                              CAff (&s_wav)[C::WAVES][C::W], Cx (&s_cin)[C::W],
                                               float (&s_acc)[2][C::WAVES][C::W]) {
     constexpr int V = C::V, W = C::W, RG = C::RG, NR = C::NR, WAVES = C::WAVES, TPR = C::TPR;
     constexpr int SEGS = WAVES * RG;
@@ -460,6 +473,8 @@ __device__ __forceinline__ void samu_bwd_tile(const SamuBwdArgs& x, const Ticket
         }
         s_seg[seg][cg * V + j] = m;
     }
+    fold_wave_segments<C, true, CAffThen>(s_seg, s_wav, seg / C::RG, (int)threadIdx.x % kWave,
+                                          caff_identity());
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
         opaque(gr[i]);
@@ -479,10 +494,10 @@ __device__ __forceinline__ void samu_bwd_tile(const SamuBwdArgs& x, const Ticket
         const int c = tid;
         const CxWords wd = cx_words(x.sc, tk.phase);
         CAff A = caff_identity();
-#pragma unroll 4
-        for (int sg = SEGS - 1; sg >= 0; --sg) {
-            const CAff t = s_seg[sg][c];
-            s_seg[sg][c] = A;
+#pragma unroll
+        for (int w = C::WAVES - 1; w >= 0; --w) {
+            const CAff t = s_wav[w][c];
+            s_wav[w][c] = A;
             A = caff_then(A, t);
         }
         const size_t o = ((size_t)g.k * (size_t)d.nS + (size_t)g.s) * W + c;
@@ -520,7 +535,8 @@ __device__ __forceinline__ void samu_bwd_tile(const SamuBwdArgs& x, const Ticket
     float acc[2 * V], tsum_[2 * NR];
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-        carry[j] = caff_apply(s_seg[seg][cg * V + j], s_cin[cg * V + j]);
+        carry[j] = caff_apply(s_seg[seg][cg * V + j],
+                              caff_apply(s_wav[seg / C::RG][cg * V + j], s_cin[cg * V + j]));
         acc[2 * j] = 0.0f;
         acc[2 * j + 1] = 0.0f;
     }
@@ -642,7 +658,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void samu_bwd_kernel(SamuBwdArgs x) {
     constexpr int W = C::W, RG = C::RG, WAVES = C::WAVES, TPR = C::TPR;
     constexpr int SEGS = WAVES * RG;
-    __shared__ CAff s_seg[SEGS][W];  // each segment's reverse map, then the maps after it composed
+    __shared__ CAff s_seg[SEGS][W];  // each segment's reverse map, then its wavefront's maps after it composed
+    __shared__ CAff s_wav[C::WAVES][W];  // each wavefront's reverse map, then the wavefronts' after it composed
     __shared__ Cx s_cin[W];          // the carry entering the tile from the right, per lane
     __shared__ float s_acc[2][WAVES][W];
 
@@ -654,7 +671,7 @@ void samu_bwd_kernel(SamuBwdArgs x) {
     const int seg = wave * RG + rg;
     const Ticket tk = take_ticket(x.sc);
     const Geo g = tile_geo<C, true>(tk.ticket, x.d, wave, rg, cg);
-    samu_bwd_tile<C, ALIGNED, RST>(x, tk, g, wave, seg, rg, cg, s_seg, s_cin, s_acc);
+    samu_bwd_tile<C, ALIGNED, RST>(x, tk, g, wave, seg, rg, cg, s_seg, s_wav, s_cin, s_acc);
 }
 
 // The second pass: dst[i] = sum_k src[k n + i] over k < count, for two arrays
