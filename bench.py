@@ -101,6 +101,19 @@ def measured_traffic(workload, direction, algo, family="real"):
     return round(kib * 1024)
 
 
+def back_to_back_ms(torch, stream, fns, steps):
+    """Mean time (ms) of `steps` back-to-back runs of fns, by HIP events."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        for f in fns:
+            f()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def roofline(kernel, nbytes, ms, traffic=None):
     """The dominant kernel's HBM roofline entry: algorithmic bytes per launch
     over its average launch interval, against MI355X's 8 TB/s."""
@@ -214,15 +227,11 @@ def complex_line(args, wl, lr, torch, W):
         for f in step:
             f()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        for f in step:
-            f()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    if args.mode == "prefill":
+        ms = back_to_back_ms(torch, stream, step, args.steps)
+    else:
+        (fwd_ms, bwd_ms), ms, warm_ms = step_times(torch, stream, step, args.steps,
+                                                    cache_flush(torch))
     res = {"metric": f"complex {args.mode}: effective HBM GB/s",
            "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -232,20 +241,14 @@ def complex_line(args, wl, lr, torch, W):
                       "io_dtype": wl.dtype}}
     res["pct_of_peak"] = round(100 * res["value"] / HBM_PEAK_GBPS, 2)
     if args.mode != "prefill":
-        # per-direction averages over back-to-back launches
-        for name, f, nb in (("fwd", fwd, 6 * s * N + 8 * B * M), ("bwd", bwd, 10 * s * N)):
-            a0 = torch.cuda.Event(enable_timing=True)
-            a1 = torch.cuda.Event(enable_timing=True)
-            a0.record(stream)
-            for _ in range(args.steps):
-                f()
-            a1.record(stream)
-            torch.cuda.synchronize()
-            kms = a0.elapsed_time(a1) / args.steps
+        res["timing"] = COLD_TIMING
+        for name, kms, nb in (("fwd", fwd_ms, 6 * s * N + 8 * B * M), ("bwd", bwd_ms, 10 * s * N)):
             res[f"{name}_us"] = round(kms * 1e3, 2)
             res[f"{name}_GBps"] = round(nb / (kms * 1e-3) / 1e9, 1)
-        res["roofline"] = roofline("complex backward scan (fused)", 10 * s * N,
-                                   res["bwd_us"] * 1e-3,
+        res["warm"] = {"ms_per_step": round(warm_ms, 5),
+                       "value": round(nbytes / (warm_ms * 1e-3) / 1e9, 2),
+                       "note": "K steps back to back, no flush"}
+        res["roofline"] = roofline("complex backward scan (fused)", 10 * s * N, bwd_ms,
                                    measured_traffic(wl.name, "backward", "fused", "complex"))
     else:
         # no counter run covers the state-only kernel (it stores only `last`)
@@ -335,15 +338,11 @@ def samu_line(args, wl, lr, torch, W):
         for f in step:
             f()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        for f in step:
-            f()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    if args.mode == "prefill":
+        ms = back_to_back_ms(torch, stream, step, args.steps)
+    else:
+        (fwd_ms, bwd_ms), ms, warm_ms = step_times(torch, stream, step, args.steps,
+                                                    cache_flush(torch))
     res = {"metric": f"fused-transition {args.mode}: effective HBM GB/s",
            "value": round(nbytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -353,21 +352,16 @@ def samu_line(args, wl, lr, torch, W):
                       "io_dtype": wl.dtype}}
     res["pct_of_peak"] = round(100 * res["value"] / HBM_PEAK_GBPS, 2)
     if args.mode != "prefill":
-        for name, f, nb in (("fwd", fwd, fwd_bytes), ("bwd", bwd, bwd_bytes)):
-            a0 = torch.cuda.Event(enable_timing=True)
-            a1 = torch.cuda.Event(enable_timing=True)
-            a0.record(stream)
-            for _ in range(args.steps):
-                f()
-            a1.record(stream)
-            torch.cuda.synchronize()
-            kms = a0.elapsed_time(a1) / args.steps
+        res["timing"] = COLD_TIMING
+        for name, kms, nb in (("fwd", fwd_ms, fwd_bytes), ("bwd", bwd_ms, bwd_bytes)):
             res[f"{name}_us"] = round(kms * 1e3, 2)
             res[f"{name}_GBps"] = round(nb / (kms * 1e-3) / 1e9, 1)
+        res["warm"] = {"ms_per_step": round(warm_ms, 5),
+                       "value": round(nbytes / (warm_ms * 1e-3) / 1e9, 2),
+                       "note": "K steps back to back, no flush"}
         # the backward call is three launches (factor tables, the tiled
         # kernel, the fixed-order reduction); its interval is charged whole
-        res["roofline"] = roofline("fused-transition backward call (fused)", bwd_bytes,
-                                   res["bwd_us"] * 1e-3,
+        res["roofline"] = roofline("fused-transition backward call (fused)", bwd_bytes, bwd_ms,
                                    measured_traffic(wl.name, "backward", "fused", "samu"))
     else:
         res["roofline"] = roofline("fused-transition state-only forward call (fused)", nbytes, ms)
@@ -550,6 +544,36 @@ def cold_times(torch, stream, fns, steps, flush):
     return [[ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(steps)] for i in range(len(fns))]
 
 
+def cache_flush(torch):
+    """The cache flush: a 1 GiB read, four times the 256 MB Infinity Cache (a
+    read leaves clean lines, so the timed step pays no write-back for it)."""
+    scrub = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
+    scrub_sum = torch.empty((), device="cuda", dtype=torch.float32)
+    return lambda: torch.sum(scrub, dim=0, out=scrub_sum)
+
+
+def step_times(torch, stream, fns, steps, flush):
+    """The step timed as the real-scan lines time it: the mean of each call
+    over `steps` cold repetitions (caches flushed before each, HIP events
+    around each call), their sum, and the mean of `steps` back-to-back steps
+    (ms)."""
+    per = cold_times(torch, stream, fns, steps, flush)
+    means = [sum(t) / len(t) for t in per]
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(steps):
+        for f in fns:
+            f()
+    w1.record(stream)
+    torch.cuda.synchronize()
+    return means, sum(means), w0.elapsed_time(w1) / steps
+
+
+COLD_TIMING = ("mean over K steps, each with the Infinity Cache flushed before it "
+               "(a 1 GiB read outside the events)")
+
+
 DEFAULT_WORKLOADS = ("wide", "long32", "longseq", "masked")
 
 
@@ -585,13 +609,7 @@ def train_line(args, name, lr, torch, W, cpu_budget):
         lr.scan_bwd_ex(a.data_ptr(), out.data_ptr(), g.data_ptr(), None, ga.data_ptr(),
                        gb.data_ptr(), B, T, D, dt, sh, bo)
 
-    # the cache flush: a 1 GiB read, four times the 256 MB Infinity Cache (a
-    # read leaves clean lines, so the timed step pays no write-back for it)
-    scrub = torch.ones(1 << 28, device="cuda", dtype=torch.float32)
-    scrub_sum = torch.empty((), device="cuda", dtype=torch.float32)
-
-    def flush():
-        torch.sum(scrub, dim=0, out=scrub_sum)
+    flush = cache_flush(torch)
 
     for _ in range(args.warmup):
         fwd()
@@ -640,7 +658,7 @@ def train_line(args, name, lr, torch, W, cpu_budget):
             if best is None or c[0] + c[1] < best[0] + best[1]:
                 best = c
     ceil_gbps = (fb + bb) / ((best[0] + best[1]) * 1e-3) / 1e9
-    del scrub, scrub_sum
+    del flush
 
     fwd_algo, fwd_chunk, fwd_width = lr.scan_auto_algo(B, T, D, dt, 0)
     bwd_algo, bwd_chunk, bwd_width = lr.scan_auto_algo(B, T, D, dt, 1)
@@ -684,8 +702,7 @@ def train_line(args, name, lr, torch, W, cpu_budget):
         },
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "elements_per_s": round(wl.N / (ms_per_step * 1e-3), 1),
-        "timing": "mean over K steps, each with the Infinity Cache flushed before it "
-                  "(a 1 GiB read outside the events)",
+        "timing": COLD_TIMING,
         "fwd_us": round(fwd_ms * 1e3, 2),
         "bwd_us": round(bwd_ms * 1e3, 2),
         "fwd_GBps": round(fb / (fwd_ms * 1e-3) / 1e9, 1),
