@@ -61,44 +61,6 @@ __device__ __forceinline__ CAff rev_fold(CAff m, Cx a, Cx g) {
     return CAff{cmul(ac, m.p), cmul(ac, cadd(m.q, g))};
 }
 
-template <int STRIDE>
-__device__ __forceinline__ CAff cshfl_up(CAff m) {
-    return CAff{Cx{shfl_up_f(m.p.r, STRIDE), shfl_up_f(m.p.i, STRIDE)},
-                Cx{shfl_up_f(m.q.r, STRIDE), shfl_up_f(m.q.i, STRIDE)}};
-}
-__device__ __forceinline__ CAff cshfl_up_n(CAff m, int n) {
-    return CAff{Cx{shfl_up_f(m.p.r, n), shfl_up_f(m.p.i, n)},
-                Cx{shfl_up_f(m.q.r, n), shfl_up_f(m.q.i, n)}};
-}
-__device__ __forceinline__ CAff cshfl_down_n(CAff m, int n) {
-    return CAff{Cx{shfl_down_f(m.p.r, n), shfl_down_f(m.p.i, n)},
-                Cx{shfl_down_f(m.q.r, n), shfl_down_f(m.q.i, n)}};
-}
-
-// In-wavefront inclusive scans over the row-group index g = lane / STRIDE,
-// the same Hillis-Steele association as the real scans (device.hpp).
-template <int STRIDE>
-__device__ __forceinline__ CAff cwave_scan_up(CAff m) {
-    const int g = lane_id() / STRIDE;
-#pragma unroll
-    for (int s = 1; s < kWave / STRIDE; s <<= 1) {
-        const CAff e = cshfl_up_n(m, s * STRIDE);
-        if (g >= s) m = caff_then(e, m);
-    }
-    return m;
-}
-template <int STRIDE>
-__device__ __forceinline__ CAff cwave_scan_down(CAff m) {
-    constexpr int G = kWave / STRIDE;
-    const int g = lane_id() / STRIDE;
-#pragma unroll
-    for (int s = 1; s < G; s <<= 1) {
-        const CAff e = cshfl_down_n(m, s * STRIDE);
-        if (g + s < G) m = caff_then(e, m);
-    }
-    return m;
-}
-
 // ---------------------------------------------------------------------------
 // publication
 // ---------------------------------------------------------------------------

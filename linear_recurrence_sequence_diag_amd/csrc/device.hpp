@@ -273,7 +273,6 @@ __device__ __forceinline__ float aff_apply(Aff m, float h) { return fmaf(m.p, h,
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ float shfl_up_f(float x, int delta) { return __shfl_up(x, delta, kWave); }
-__device__ __forceinline__ float shfl_down_f(float x, int delta) { return __shfl_down(x, delta, kWave); }
 
 // Inclusive scan over the "group" index g = lane / STRIDE (groups of STRIDE
 // adjacent lanes, G = 64 / STRIDE groups), in increasing g: on return lane
@@ -291,22 +290,6 @@ __device__ __forceinline__ Aff wave_scan_up(Aff m) {
         e.p = shfl_up_f(m.p, s * STRIDE);
         e.q = shfl_up_f(m.q, s * STRIDE);
         if (g >= s) m = aff_then(e, m);
-    }
-    return m;
-}
-
-// Inclusive scan in decreasing g: lane g holds m_g after m_{g+1} after ... after m_{G-1}
-// (used by the reverse-time pass, whose carries flow from later rows to earlier ones).
-template <int STRIDE>
-__device__ __forceinline__ Aff wave_scan_down(Aff m) {
-    constexpr int G = kWave / STRIDE;
-    const int g = lane_id() / STRIDE;
-#pragma unroll
-    for (int s = 1; s < G; s <<= 1) {
-        Aff e;
-        e.p = shfl_down_f(m.p, s * STRIDE);
-        e.q = shfl_down_f(m.q, s * STRIDE);
-        if (g + s < G) m = aff_then(e, m);
     }
     return m;
 }

@@ -371,36 +371,6 @@ __device__ typename Link::S look_back(const Link& lk, int k, int NK, typename Li
     return x;
 }
 
-// Pairwise reduction, in a fixed association, of the RG maps a wavefront's
-// row groups produce, fed one at a time in scan order: for RG a power of two
-// this is the balanced tree that the in-wavefront Hillis-Steele scan forms
-// for its last group, so the total is bitwise the same.  Then::then(e, l) is
-// the composition "l after e".
-template <int RG, class M, class Then>
-struct TreeFold {
-    static constexpr int L = RG == 1 ? 1 : (RG == 2 ? 1 : (RG == 4 ? 2 : 3));  // pending levels
-    M st[L];
-    M top;
-    // g-th leaf (0-based): merge it with the pending left node of every level
-    // the leaf completes; the root lands in `top`
-    __device__ __forceinline__ void push(int g, M node) {
-        if (RG == 1) {
-            top = node;
-            return;
-        }
-#pragma unroll
-        for (int lvl = 0; lvl < L; ++lvl) {
-            if (((g >> lvl) & 1) == 0) {
-                st[lvl] = node;
-                return;
-            }
-            node = Then::then(st[lvl], node);
-        }
-        top = node;
-    }
-    __device__ __forceinline__ M total() const { return top; }
-};
-
 // First level of a tile's fold, per wavefront and lane, right after the
 // wavefront has written its segments' maps to s_seg: the wavefront's RG
 // segments are folded in order (REV: from the last), each replaced by the
