@@ -19,6 +19,11 @@ to back ("warm"), the forward and backward kernels' mean durations inside the
 timed steps (the dominant one's roofline), the achievable ceiling of plain
 streaming kernels with the step's access pattern on the same arrays, timed
 the same way, and the fp64 oracle's rate on a bounded sample on the host.
+
+    python bench.py --sweep lanes|short|tiles [--steps K]
+
+prints instead the measurements behind the automatic algorithm and tile
+choice, one JSON line per shape (see sweep_lines).
 """
 from __future__ import annotations
 
@@ -735,6 +740,149 @@ def train_line(args, name, lr, torch, W, cpu_budget):
     return res
 
 
+# Tile shapes (row width in 16-byte vectors, rows per tile) the fused form
+# is built for, per direction; the library rejects any other pair.
+FUSED_FWD_SHAPES = ((8, 256), (8, 512), (16, 128), (16, 256), (32, 32), (32, 64), (32, 128))
+FUSED_BWD_SHAPES = ((8, 256), (8, 128), (16, 128), (32, 64), (32, 32))
+
+SWEEP_LANES = ((8, 2048, 2560), (32, 2048, 2560), (128, 2048, 2560), (512, 512, 2560),
+               (2048, 128, 2560), (8192, 32, 2560))
+SWEEP_SHORT_T = (8, 16, 32, 64, 128, 256, 512, 1024)
+
+
+def sweep_lines(args, lr, torch, W):
+    """The measurements behind the automatic algorithm choice, one JSON line
+    per point; every time is the mean of `--steps` calls, each with the
+    Infinity Cache flushed before it (HIP events around the call).
+
+    lanes: the per-lane walk against the automatic choice as the number of
+      lanes B*D grows (D = 2560, bf16 and fp32).
+    short: every fused tile shape, the walk and the automatic choice on
+      short sequences at constant work (B*T*D*s ~ 680 MB over the three
+      forward arrays, T from 8 to 1024, D = 2560).
+    tiles: every fused tile shape and the automatic choice on the four large
+      workloads.
+    Inputs for lanes and short are drawn on the device (a ~ U(0.5, 0.9999),
+    b, g ~ N(0, 1)); tiles uses the workloads' own generators.  Rates are the
+    algorithmic bytes (forward 3*s*N + 4*B*D, backward 5*s*N) per second."""
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    flush = cache_flush(torch)
+    steps = max(1, args.steps)
+
+    def arrays(B, T, D, tdt, gen=None):
+        if gen is not None:
+            return gen
+        g0 = torch.Generator(device="cuda")
+        g0.manual_seed(0)
+        a = torch.empty(B, T, D, device="cuda").uniform_(0.5, 0.9999, generator=g0).to(tdt)
+        b = torch.randn(B, T, D, device="cuda", generator=g0).to(tdt)
+        g = torch.randn(B, T, D, device="cuda", generator=g0).to(tdt)
+        return a, b, g
+
+    def measure(B, T, D, dt, a, b, g, variants):
+        """variants: name -> (forward opts or None, backward opts or None)."""
+        out = torch.empty_like(a)
+        ga = torch.empty_like(a)
+        gb = torch.empty_like(a)
+        last = torch.empty((B, D), device="cuda", dtype=torch.float32)
+        s = a.element_size()
+        N = B * T * D
+        fb, bb = 3 * s * N + 4 * B * D, 5 * s * N
+        auto = lr.make_opts()
+        lr.scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(), last.data_ptr(), B, T, D, dt,
+                       sh, auto)
+        res = {}
+        for name, (fo, bo) in variants.items():
+            fns = []
+            if fo is not None:
+                fns.append(lambda fo=fo: lr.scan_fwd_ex(a.data_ptr(), b.data_ptr(), out.data_ptr(),
+                                                        last.data_ptr(), B, T, D, dt, sh, fo))
+            if bo is not None:
+                fns.append(lambda bo=bo: lr.scan_bwd_ex(a.data_ptr(), out.data_ptr(), g.data_ptr(),
+                                                        None, ga.data_ptr(), gb.data_ptr(), B, T,
+                                                        D, dt, sh, bo))
+            for f in fns:  # first call: workspace and code objects
+                f()
+            torch.cuda.synchronize()
+            per = cold_times(torch, stream, fns, steps, flush)
+            ms = [sum(t) / len(t) for t in per]
+            r = {}
+            k = 0
+            if fo is not None:
+                r["fwd_us"] = round(ms[k] * 1e3, 1)
+                r["fwd_gbps"] = round(fb / (ms[k] * 1e-3) / 1e9, 1)
+                k += 1
+            if bo is not None:
+                r["bwd_us"] = round(ms[k] * 1e3, 1)
+                r["bwd_gbps"] = round(bb / (ms[k] * 1e-3) / 1e9, 1)
+            res[name] = r
+        del out, ga, gb, last
+        return res
+
+    def best(res, key):
+        ranked = sorted((v[key], k) for k, v in res.items() if key in v)
+        return [k for _, k in ranked[::-1][:3]]
+
+    def shape_variants():
+        v = {"walk": (lr.make_opts(algo="seq"), lr.make_opts(algo="seq")),
+             "auto": (lr.make_opts(), lr.make_opts())}
+        fwd = set(FUSED_FWD_SHAPES)
+        bwd = set(FUSED_BWD_SHAPES)
+        for w, t in sorted(fwd | bwd):
+            v[f"w{w}x{t}"] = (lr.make_opts(algo="fused", width=w, chunk=t) if (w, t) in fwd else None,
+                              lr.make_opts(algo="fused", width=w, chunk=t) if (w, t) in bwd else None)
+        return v
+
+    dtypes = (("bf16", lr.BF16, torch.bfloat16), ("f32", lr.F32, torch.float32))
+    if args.sweep == "lanes":
+        for name, dt, tdt in dtypes:
+            for B, T, D in SWEEP_LANES:
+                a, b, g = arrays(B, T, D, tdt)
+                res = measure(B, T, D, dt, a, b, g,
+                              {"walk": (lr.make_opts(algo="seq"), lr.make_opts(algo="seq")),
+                               "auto": (lr.make_opts(), lr.make_opts())})
+                print(json.dumps({"sweep": "lanes", "dtype": name, "B": B, "T": T, "D": D,
+                                  "lanes": B * D, "steps": steps, **res}), flush=True)
+                del a, b, g
+                torch.cuda.empty_cache()
+    elif args.sweep == "short":
+        D = 2560
+        for name, dt, tdt in dtypes:
+            s = 2 if name == "bf16" else 4
+            for T in SWEEP_SHORT_T:
+                B = max(1, int(round(3.4e8 * 2 / s / (T * D))))
+                a, b, g = arrays(B, T, D, tdt)
+                res = measure(B, T, D, dt, a, b, g, shape_variants())
+                print(json.dumps({"sweep": "short", "dtype": name, "B": B, "T": T, "D": D,
+                                  "steps": steps, "best_fwd": best(res, "fwd_gbps"),
+                                  "best_bwd": best(res, "bwd_gbps"), **res}), flush=True)
+                del a, b, g
+                torch.cuda.empty_cache()
+    else:
+        for wname in DEFAULT_WORKLOADS:
+            wl = W.WORKLOADS[wname]
+            inp = W.generate(wl, seed=0)
+            dt = lr.F32 if wl.dtype == "f32" else lr.BF16
+
+            def dev(x):
+                if wl.dtype == "f32":
+                    return torch.from_numpy(x).cuda()
+                return torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+
+            a, b, g = dev(inp.a), dev(inp.b), dev(inp.g)
+            del inp
+            v = shape_variants()
+            del v["walk"]
+            res = measure(wl.B, wl.T, wl.D, dt, a, b, g, v)
+            print(json.dumps({"sweep": "tiles", "workload": wname, "B": wl.B, "T": wl.T,
+                              "D": wl.D, "dtype": wl.dtype, "steps": steps,
+                              "best_fwd": best(res, "fwd_gbps"), "best_bwd": best(res, "bwd_gbps"),
+                              **res}), flush=True)
+            del a, b, g
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -757,6 +905,11 @@ def main():
                     help="only run kernels of known traffic (a 1 GiB device copy and the "
                          "read-2/write-1 streaming kernel on 3 x 256 MiB), the reference for "
                          "HBM byte counters")
+    ap.add_argument("--sweep", choices=["lanes", "short", "tiles"],
+                    help="print the dispatch measurements instead of the step: the per-lane "
+                         "walk against the automatic choice over the number of lanes (lanes), "
+                         "every tile shape on short sequences (short) or on the large "
+                         "workloads (tiles); one JSON line per point")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -794,6 +947,10 @@ def main():
                           "copy": {"bytes_read": 4 * n, "bytes_written": 4 * n},
                           "stream_read2_write1": {"bytes_read": 2 * n, "bytes_written": n},
                           "repetitions": args.steps}))
+        return
+
+    if args.sweep:
+        sweep_lines(args, lr, torch, W)
         return
 
     if args.workload in W.COMPLEX_WORKLOADS:

@@ -80,9 +80,10 @@ enum {
 
 /* algorithms */
 enum {
-    LRSCAN_ALGO_AUTO = 0,    /* the library picks: FUSED with a measured tile shape, or CHUNKED
-                                (complex scan: SEQ) where a tile would exceed the fused form's
-                                32-bit in-tile offsets (rows of hundreds of MB) */
+    LRSCAN_ALGO_AUTO = 0,    /* the library picks: SEQ for sequences of at most 8 steps (bf16:
+                                16) over at least 2^20 lanes, else FUSED with a measured tile
+                                shape, or CHUNKED (complex scan: SEQ) where a tile would exceed
+                                the fused form's 32-bit in-tile offsets (rows of hundreds of MB) */
     LRSCAN_ALGO_SEQ = 1,     /* one thread walks all T steps of its lanes */
     LRSCAN_ALGO_CHUNKED = 2, /* three launches: chunk summary, chunk prefix, chunk replay */
     LRSCAN_ALGO_FUSED = 3    /* one launch: tile summary, look-back prefix, replay from registers */
@@ -95,7 +96,7 @@ typedef struct {
     int width;              /* FUSED only: threads of 16 bytes per tile row (8, 16 or 32; a
                                tile row is 128, 256 or 512 contiguous bytes); 0: default.
                                Supported (width, chunk): forward (8,256) (8,512) (16,128)
-                               (16,256) (32,64) (32,128); backward (8,256) (8,128) (16,128)
+                               (16,256) (32,32) (32,64) (32,128); backward (8,256) (8,128) (16,128)
                                (32,64) (32,32).  Rows that are not 16-byte aligned
                                (D * elem_bytes % 16 != 0 or an unaligned pointer) support
                                only (8,256). */

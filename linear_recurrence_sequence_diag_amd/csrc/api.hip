@@ -137,10 +137,16 @@ bool shape_aligned(const Shape& s) { return (s.D * (s.dtype == LRSCAN_F32 ? 4 : 
 // The per-lane walk when the sequences are short and B*D alone fills the GPU
 // many times over: every tile of the fused form would be mostly idle rows,
 // while each lane's walk is a few steps of plain streaming.  Measured on
-// MI355X with 20M-42M lanes of T = 8 or 16: 5.3-5.9 TB/s against 0.4-3.4
-// for the best tile shape.  (At T = 32 the two are even; below about 1M
-// lanes the walk has too few threads in flight to be competitive.)
-bool prefer_seq(const Shape& s) { return s.T <= 16 && s.B * s.D >= ((int64_t)1 << 20); }
+// MI355X with 10M-42M lanes (D = 2560): T = 8 5.6-5.8 TB/s against 3.4-3.6
+// for the best tile shape (32 rows of 512-byte lane blocks); bf16 T = 16
+// 5.3 against 3.7 (forward) and 4.9 (backward).  fp32 T = 16 is the other
+// way round (the tile 5.6 / 5.5 against 5.3 / 5.4), and from T = 32 the tile
+// wins for both types; below about 1M lanes the walk has too few threads in
+// flight to be competitive.
+bool prefer_seq(const Shape& s) {
+    return (s.T <= 8 || (s.T <= 16 && s.dtype == LRSCAN_BF16)) &&
+           s.B * s.D >= ((int64_t)1 << 20);
+}
 
 // The automatic choice: the per-lane walk for short sequences over many
 // lanes (prefer_seq); otherwise the single-launch fused form, which reads

@@ -538,7 +538,7 @@ struct TileCfg {
 };
 constexpr TileCfg kFwdCfgs[] = {
     {8, 256, 8, 4, 8}, {8, 512, 16, 4, 8}, {16, 128, 8, 4, 4},
-    {16, 256, 16, 4, 4}, {32, 64, 8, 4, 4}, {32, 128, 16, 4, 4},
+    {16, 256, 16, 4, 4}, {32, 32, 4, 4, 4}, {32, 64, 8, 4, 4}, {32, 128, 16, 4, 4},
 };
 constexpr TileCfg kBwdCfgs[] = {
     {8, 256, 8, 4, 8}, {8, 128, 4, 4, 8}, {16, 128, 8, 4, 4},
@@ -591,6 +591,7 @@ bool fwd_dispatch(const TileCfg& c, bool al, const FwdArgs& x, hipStream_t st) {
     else if (c.width == 8 && c.tile == 512) launch_fwd_cfg<DT, 8, 16, 4, 8, true>(x, st);
     else if (c.width == 16 && c.tile == 128) launch_fwd_cfg<DT, 16, 8, 4, 4, true>(x, st);
     else if (c.width == 16 && c.tile == 256) launch_fwd_cfg<DT, 16, 16, 4, 4, true>(x, st);
+    else if (c.width == 32 && c.tile == 32) launch_fwd_cfg<DT, 32, 4, 4, 4, true>(x, st);
     else if (c.width == 32 && c.tile == 64) launch_fwd_cfg<DT, 32, 8, 4, 4, true>(x, st);
     else if (c.width == 32 && c.tile == 128) launch_fwd_cfg<DT, 32, 16, 4, 4, true>(x, st);
     else return false;
@@ -633,11 +634,16 @@ bool fused_cfg_supported(const Shape& s, int dir, int width, int tile, bool alig
 // flushed before each launch; [B,T,D] bf16 and fp32 from [8,2048,2560] and
 // [16,4096,2560] to [1,131072,1024], and short sequences T = 8 .. 1024 at
 // about 340M elements).  A tile should not be much taller than the sequence:
-// its rows past T are idle threads.  Forward: 64 rows of 512-byte lane
-// blocks for T <= 64 ([4150,32,2560] bf16 5.0 against 1.6 TB/s at 256 rows),
-// 128 rows of 256-byte blocks for T <= 128 (5.9 against 4.7 TB/s), else 256
-// rows of 128-byte blocks, and 512 rows when there are fewer than 64 chains
-// of 128-byte lane blocks and T >= 4096, where consecutive tiles of a chain
+// its rows past T are idle threads.  Forward: 32 rows of 512-byte lane
+// blocks for T <= 32 ([4150,32,2560] bf16 5.5 against 4.7 TB/s at 64 rows
+// and 1.7 at 256), 64 rows for bf16 T <= 64, 128 rows of 256-byte blocks for
+// T <= 128 (bf16 T = 128: 6.0 against 4.9 TB/s at 64 rows; fp32 from T > 32:
+// [1038,64,2560] 6.0 against 5.9 TB/s at 64 rows of 512 bytes), else
+// 128-byte blocks: 512 rows for 256 < T <= 512, so that a chain is one tile with no
+// look-back and no mostly idle second tile ([461,288,2560] bf16 5.1 against
+// 4.5 TB/s at 256 rows, T = 512 5.6 against 5.5), else 256 rows, and 512 rows
+// when there are fewer than 64 chains of 128-byte lane blocks and T >= 4096,
+// where consecutive tiles of a chain
 // start so close together that each waits on its predecessor ([1,131072,
 // 1024]: 152.4 -> 147.7 us).  Backward: 32 rows of 512-byte blocks for
 // T <= 32, 64 rows for T <= 64, 128 rows of 128-byte blocks for T <= 128,
@@ -654,7 +660,10 @@ void fused_default_cfg(const Shape& s, int dir, bool aligned, int* width, int* t
     const int64_t row_bytes = s.D * (s.dtype == DT_F32 ? 4 : 2);
     const auto fits = [&](int w) { return row_bytes >= (int64_t)w * 16; };
     if (dir == 0) {
-        if (s.T <= 64 && fits(32)) {
+        if (s.T <= 32 && fits(32)) {
+            *width = 32;
+            *tile = 32;
+        } else if (s.T <= 64 && s.dtype == DT_BF16 && fits(32)) {
             *width = 32;
             *tile = 64;
         } else if (s.T <= 128 && fits(16)) {
@@ -663,7 +672,7 @@ void fused_default_cfg(const Shape& s, int dir, bool aligned, int* width, int* t
         } else {
             const int64_t lanes8 = 8 * (s.dtype == DT_F32 ? Elem<DT_F32>::V : Elem<DT_BF16>::V);
             const int64_t chains8 = s.B * ((s.D + lanes8 - 1) / lanes8);
-            if (s.T >= 8 * 512 && chains8 < 64) *tile = 512;
+            if ((s.T > 256 && s.T <= 512) || (s.T >= 8 * 512 && chains8 < 64)) *tile = 512;
         }
         return;
     }

@@ -161,16 +161,22 @@ def test_workspace_sizes_and_auto_choice():
             # short sequences over millions of lanes: the per-lane walk
             algo, chunk, _ = lr.scan_auto_algo(1, 1, (1 << 22) + 5, dt, direction)
             assert algo == lr.ALGO_SEQ
-            algo, _, _ = lr.scan_auto_algo(16384, 16, 64, dt, direction)
+            algo, _, _ = lr.scan_auto_algo(16384, 8, 64, dt, direction)
             assert algo == lr.ALGO_SEQ
+            algo, _, _ = lr.scan_auto_algo(16384, 16, 64, dt, direction)
+            assert algo == (lr.ALGO_SEQ if dt == lr.BF16 else lr.ALGO_FUSED)
             # long sequences, and short ones over too few lanes for the walk: the fused form
             algo, _, _ = lr.scan_auto_algo(8, 2048, 2560, dt, direction)
             assert algo == lr.ALGO_FUSED
             algo, _, _ = lr.scan_auto_algo(4, 16, 1024, dt, direction)
             assert algo == lr.ALGO_FUSED
-            # a tile is not much taller than the sequence
+            # a tile is no taller than a short sequence, and a forward chain of
+            # at most 512 steps is one tile
             _, tile, _ = lr.scan_auto_algo(4096, 32, 2560, dt, direction)
-            assert tile <= 64
+            assert tile == 32
+            if direction == 0:
+                _, tile, _ = lr.scan_auto_algo(256, 300, 2560, dt, direction)
+                assert tile == 512
     assert lr.scan_workspace_bytes(0, 8, 4, lr.F32) == 0
     o = lr.make_opts(algo="seq")
     assert lr.scan_workspace_bytes(2, 8, 4, lr.F32, o) == 0

@@ -23,6 +23,7 @@ ALGOS = [("seq", 0, 0, 0, 0), ("chunked", 16, 16, 0, 0), ("chunked", 64, 64, 0, 
          ("chunked", 256, 256, 0, 0), ("chunked", 1024, 1024, 0, 0),
          ("fused", 256, 256, 8, 8), ("fused", 512, 128, 8, 8), ("fused", 128, 128, 16, 16),
          ("fused", 256, 128, 16, 16), ("fused", 64, 64, 32, 32), ("fused", 128, 32, 32, 32),
+         ("fused", 32, 32, 32, 32),
          ("auto", 0, 0, 0, 0)]
 ALGO_IDS = [f"{a}{c}w{w}" if c else a for a, c, _, w, _ in ALGOS]
 
