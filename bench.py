@@ -713,6 +713,10 @@ def train_line(args, name, lr, torch, W, cpu_budget):
         "fwd_GBps": round(fb / (fwd_ms * 1e-3) / 1e9, 1),
         "bwd_GBps": round(bb / (bwd_ms * 1e-3) / 1e9, 1),
         "step_ms_min": round(min(step_t), 5),
+        "per_call_us": {"fwd_median": round(float(np.median(fwd_t)) * 1e3, 2),
+                        "fwd_min": round(min(fwd_t) * 1e3, 2),
+                        "bwd_median": round(float(np.median(bwd_t)) * 1e3, 2),
+                        "bwd_min": round(min(bwd_t) * 1e3, 2)},
         "warm": {"ms_per_step": round(warm_ms, 5),
                  "value": round((fb + bb) / (warm_ms * 1e-3) / 1e9, 2),
                  "note": "K steps back to back, no flush"},

@@ -110,10 +110,13 @@ def test_small_workload(algo, cf, cb, wf, wb):
     check_against_oracle(inp, run_pair(inp, algo, cf, cb, wf, wb))
 
 
-# the last two reach AUTO's 512-step forward tiles (long sequences with few lane blocks)
-SHAPES = [(1, 1, 1), (1, 2, 3), (2, 63, 7), (2, 64, 8), (1, 65, 9), (3, 257, 64), (2, 300, 65),
-          (1, 1000, 100), (2, 513, 129), (1, 1100, 16), (2, 2049, 40), (3, 4099, 136),
-          (1, 4097, 40)]
+# AUTO's tile shapes: (2, 20, 304) and (3, 33, 520) its short-sequence tiles
+# with 512-byte rows (rows past T and lanes past D in every tile), (3, 257, 64)
+# a forward chain of one 512-row tile, the last two its 512-row forward tiles
+# for long sequences with few lane blocks
+SHAPES = [(1, 1, 1), (1, 2, 3), (2, 63, 7), (2, 64, 8), (1, 65, 9), (2, 20, 304), (3, 33, 520),
+          (3, 257, 64), (2, 300, 65), (1, 1000, 100), (2, 513, 129), (1, 1100, 16),
+          (2, 2049, 40), (3, 4099, 136), (1, 4097, 40)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
