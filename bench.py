@@ -73,14 +73,29 @@ KERNEL_SOURCES = {
 }
 
 
-def kernel_sources_sha256(family="real"):
-    """Hash of one kernel family's sources."""
+def code_only(text):
+    """C++ source with its comments removed and its whitespace collapsed, so
+    that a change to a comment is not a change to the kernel (the sources
+    hold no string literal with a comment marker in it)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_sources_sha256(family="real", read=None):
+    """Hash of one kernel family's sources, comments and layout left out.
+    `read(name)` returns a source file's text (default: the working tree)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_recurrence_sequence_diag_amd", "csrc")
     for f in KERNEL_SOURCES[family]:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        if read is None:
+            with open(os.path.join(csrc, f)) as fh:
+                text = fh.read()
+        else:
+            text = read(f)
+        h.update(code_only(text).encode())
     return h.hexdigest()
 
 

@@ -634,25 +634,29 @@ bool fused_cfg_supported(const Shape& s, int dir, int width, int tile, bool alig
 // flushed before each launch; [B,T,D] bf16 and fp32 from [8,2048,2560] and
 // [16,4096,2560] to [1,131072,1024], and short sequences T = 8 .. 1024 at
 // about 340M elements).  A tile should not be much taller than the sequence:
-// its rows past T are idle threads.  Forward: 32 rows of 512-byte lane
-// blocks for T <= 32 ([4150,32,2560] bf16 5.5 against 4.7 TB/s at 64 rows
-// and 1.7 at 256), 64 rows for bf16 T <= 64, 128 rows of 256-byte blocks for
-// T <= 128 (bf16 T = 128: 6.0 against 4.9 TB/s at 64 rows; fp32 from T > 32:
-// [1038,64,2560] 6.0 against 5.9 TB/s at 64 rows of 512 bytes), else
-// 128-byte blocks: 512 rows for 256 < T <= 512, so that a chain is one tile with no
-// look-back and no mostly idle second tile ([461,288,2560] bf16 5.1 against
-// 4.5 TB/s at 256 rows, T = 512 5.6 against 5.5), else 256 rows, and 512 rows
-// when there are fewer than 64 chains of 128-byte lane blocks and T >= 4096,
-// where consecutive tiles of a chain
+// its rows past T are idle threads.
+//
+// Forward: 32 rows of 512-byte lane blocks for T <= 32 ([4150,32,2560] bf16
+// 5.5 against 4.7 TB/s at 64 rows and 1.7 at 256); 64 rows of them for bf16
+// T <= 64; 128 rows of 256-byte blocks for T <= 128 (bf16 T = 128: 6.0
+// against 4.9 TB/s at 64 rows of 512 bytes) and for fp32 T <= 64 ([1038,64,
+// 2560]: 6.0 against 5.9); else 128-byte blocks: 512 rows for 256 < T <= 512,
+// so that a chain is one tile with no look-back and no mostly idle second
+// tile ([461,288,2560] bf16 5.1 against 4.5 TB/s at 256 rows, T = 512 5.6
+// against 5.5), 512 rows also when there are fewer than 64 chains of
+// 128-byte lane blocks and T >= 4096, where consecutive tiles of a chain
 // start so close together that each waits on its predecessor ([1,131072,
-// 1024]: 152.4 -> 147.7 us).  Backward: 32 rows of 512-byte blocks for
-// T <= 32, 64 rows for T <= 64, 128 rows of 128-byte blocks for T <= 128,
-// 128 rows of 256-byte blocks for long bf16 sequences (T >= 1024) with at
-// least 128 such blocks ([16,4096,2560]: 277.7 against 283.0 us for 256 rows
-// of 128-byte blocks, [8,2048,2560] even), else 256 rows of 128-byte blocks
-// (T of 256..512 over many lane blocks: 5.8 against 5.2 TB/s).  A lane block
-// wider than the row (D smaller than the block) would leave lanes idle, so
-// the widths fall back to narrower rows.
+// 1024]: 152.4 -> 147.7 us), else 256 rows.
+//
+// Backward: 32 rows of 512-byte blocks for T <= 32, 64 rows for T <= 64, 128
+// rows of 128-byte blocks for T <= 128, 128 rows of 256-byte blocks for long
+// bf16 sequences (T >= 1024) with at least 128 such blocks ([16,4096,2560]:
+// 277.7 against 283.0 us for 256 rows of 128-byte blocks, [8,2048,2560]
+// even), else 256 rows of 128-byte blocks (T of 256..512 over many lane
+// blocks: 5.8 against 5.2 TB/s).
+//
+// A lane block wider than the row (D smaller than the block) would leave
+// lanes idle, so the widths fall back to narrower rows.
 void fused_default_cfg(const Shape& s, int dir, bool aligned, int* width, int* tile) {
     *width = 8;
     *tile = 256;
