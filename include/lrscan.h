@@ -83,7 +83,9 @@ enum {
     LRSCAN_ALGO_AUTO = 0,    /* the library picks: SEQ for sequences of at most 8 steps (bf16:
                                 16) over at least 2^20 lanes, else FUSED with a measured tile
                                 shape, or CHUNKED (complex scan: SEQ) where a tile would exceed
-                                the fused form's 32-bit in-tile offsets (rows of hundreds of MB) */
+                                the fused form's 32-bit in-tile offsets (rows of hundreds of MB).
+                                Complex scan: SEQ for T <= 16, and from 2^18 lanes for T <= 32
+                                (bf16 forward: T <= 64), else FUSED */
     LRSCAN_ALGO_SEQ = 1,     /* one thread walks all T steps of its lanes */
     LRSCAN_ALGO_CHUNKED = 2, /* three launches: chunk summary, chunk prefix, chunk replay */
     LRSCAN_ALGO_FUSED = 3    /* one launch: tile summary, look-back prefix, replay from registers */

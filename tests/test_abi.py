@@ -107,6 +107,11 @@ def test_argument_errors_return_status_without_work():
                                 2, 8, 4, lr.BF16, None, None) == -1
     assert lr.scan_complex_workspace_bytes(2, 1000, 64, lr.F32) > 0
     assert lr.scan_complex_workspace_bytes(2, 1000, 64, lr.F32, lr.make_opts(algo="seq")) == 0
+    # AUTO: short complex sequences walk per lane in both directions (no
+    # scratch); a bf16 64-step sequence over 1.3M lanes walks forward only
+    assert lr.scan_complex_workspace_bytes(4096, 8, 64, lr.F32) == 0
+    assert lr.scan_complex_workspace_bytes(512, 32, 2560, lr.BF16) == 0
+    assert lr.scan_complex_workspace_bytes(512, 64, 2560, lr.BF16) > 0
     # fused-transition scan: controls required, pairs whole, AUTO/FUSED only
     assert lib.scan_samu_fwd(None, *([fake] * 7), None, None, None, None, 2, 8, 4, lr.F32, None,
                              None) == -1

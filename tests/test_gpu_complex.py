@@ -87,7 +87,8 @@ def state_pair(B, M, seed):
     return (z.real.astype(np.float32) + 1j * z.imag.astype(np.float32))
 
 
-SHAPES = [(2, 300, 72), (3, 1000, 130), (1, 4096, 256), (2, 333, 13), (1, 1, 1), (2, 129, 1)]
+SHAPES = [(2, 300, 72), (3, 1000, 130), (1, 4096, 256), (2, 333, 13), (1, 1, 1), (2, 129, 1),
+          (300, 12, 1024), (140, 40, 2048)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -101,7 +102,7 @@ def test_complex_against_oracle(B, T, M, dt):
     for m in (None, mask):
         h, hl = oracle.complex_fwd(a, b, h0=h0, reset=m)
         oga, ogb, ogh0 = oracle.complex_bwd(a, h, g, h0=h0, grad_last=gl, reset=m)
-        for algo in ("seq", "fused"):
+        for algo in ("seq", "fused", "auto"):
             res = run(inp, algo, h0=h0, gl=gl, mask=m)
             out, last = chost(res[0], res[1]), chost(res[2], res[3])
             ga, gb = chost(res[4], res[5]), chost(res[6], res[7])
