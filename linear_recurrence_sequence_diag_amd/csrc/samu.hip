@@ -429,6 +429,7 @@ __device__ __forceinline__ void samu_bwd_tile(const SamuBwdArgs& x, const Ticket
     // The rows of `out` last, as only the replay uses them; the later half
     // now, the earlier half during the replay (the replay walks the rows
     // from the last), so that the two halves never hold registers at once.
+    // With fewer than 4 rows per thread every row is loaded now.
     auto load_h = [&](int i, int z) {
         const int row = g.row0 + i;
         const int rc = row < d.T ? row : d.T - 1;
@@ -437,8 +438,9 @@ __device__ __forceinline__ void samu_bwd_tile(const SamuBwdArgs& x, const Ticket
         hr[i] = load_vec<C::DT, ALIGNED, true>(phr, hoff, g.nvalid, 0.0f);
         hi[i] = load_vec<C::DT, ALIGNED, true>(phi, hoff, g.nvalid, 0.0f);
     };
+    constexpr int kHLate = NR >= 4 ? NR / 2 : 0;  // rows of `out` loaded during the replay
 #pragma unroll
-    for (int i = NR / 2; i < NR; ++i) load_h(i, 0);
+    for (int i = kHLate; i < NR; ++i) load_h(i, 0);
     SamuTok tok[NR];
     uint32_t rbits = 0;
 #pragma unroll
@@ -544,13 +546,13 @@ __device__ __forceinline__ void samu_bwd_tile(const SamuBwdArgs& x, const Ticket
 #pragma unroll
     for (int i = NR - 1; i >= 0; --i) {
         const int row = g.row0 + i;
-        if (i == NR - 3) {
+        if (kHLate > 0 && i == NR - 3) {
             // the earlier half of `out`, once two rows have freed their
             // registers (addressed with a zero that depends on the carry,
             // so the loads cannot be issued sooner)
             const int z = zero_after(carry[0].r);
 #pragma unroll
-            for (int r = 0; r < NR / 2; ++r) load_h(r, z);
+            for (int r = 0; r < kHLate; ++r) load_h(r, z);
         }
         tsum_[2 * i] = 0.0f;
         tsum_[2 * i + 1] = 0.0f;
@@ -726,24 +728,88 @@ void dispatch2(bool al, bool rst, F&& f) {
     else f(std::false_type{}, std::false_type{});
 }
 
-// Tile shapes of the two directions: Cfg<type, threads of 16 bytes per row,
-// rows per thread, wavefronts, look-back window>.  256 rows of 128-byte rows
-// per array: measured on MI355X (bf16 B8 T2048 M2560) against 128 rows and
+// Tile shapes: Cfg<type, threads of 16 bytes per row, rows per thread,
+// wavefronts, look-back window>.  Long sequences: 256 rows of 128-byte rows
+// per array; measured on MI355X (bf16 B8 T2048 M2560) against 128 rows and
 // 256-byte rows (8 or 4 rows per thread, 4 or 8 wavefronts), this shape was
 // the fastest in both directions; the tile's fixed costs (ticket, look-back,
 // barriers) dominate smaller tiles, whose bytes per tile are fewer than the
 // real scan's because the transitions are not read.  The backward looks back
 // over 2 tiles: with a window of 4 its registers spilled (144.7 -> 142.6 us).
+// Short sequences: a tile no taller than the sequence, with wider rows to
+// keep the bytes per tile up, as in the real scan -- 32 rows of 512-byte rows
+// for T <= 32, 64 of them for T <= 64, 128 rows of 256-byte rows for
+// T <= 128 (a 256-row tile over an 8-step sequence is 97% idle rows).
+enum SamuShape { kSamuLong = 0, kSamuT32 = 1, kSamuT64 = 2, kSamuT128 = 3, kSamuT8 = 4, kSamuT16 = 5 };
+template <int DT, int SH>
+struct SamuShapeCfg;
 template <int DT>
-using SamuFwdCfg = Cfg<DT, 8, 8, 4, 4>;
+struct SamuShapeCfg<DT, kSamuLong> {
+    using Fwd = Cfg<DT, 8, 8, 4, 4>;
+    using Bwd = Cfg<DT, 8, 8, 4, 2>;
+};
 template <int DT>
-using SamuBwdCfg = Cfg<DT, 8, 8, 4, 2>;
+struct SamuShapeCfg<DT, kSamuT8> {
+    using Fwd = Cfg<DT, 32, 1, 4, 4>;
+    using Bwd = Cfg<DT, 32, 1, 4, 2>;
+};
+template <int DT>
+struct SamuShapeCfg<DT, kSamuT16> {
+    using Fwd = Cfg<DT, 32, 2, 4, 4>;
+    using Bwd = Cfg<DT, 32, 2, 4, 2>;
+};
+template <int DT>
+struct SamuShapeCfg<DT, kSamuT32> {
+    using Fwd = Cfg<DT, 32, 4, 4, 4>;
+    using Bwd = Cfg<DT, 32, 4, 4, 2>;
+};
+template <int DT>
+struct SamuShapeCfg<DT, kSamuT64> {
+    using Fwd = Cfg<DT, 32, 8, 4, 4>;
+    using Bwd = Cfg<DT, 32, 8, 4, 2>;
+};
+template <int DT>
+struct SamuShapeCfg<DT, kSamuT128> {
+    using Fwd = Cfg<DT, 16, 8, 4, 4>;
+    using Bwd = Cfg<DT, 16, 8, 4, 2>;
+};
 
-Layout samu_fwd_layout(const Shape& s) {
-    return layout_of(s, SamuFwdCfg<DT_F32>::TPR, SamuFwdCfg<DT_F32>::CT);
+// The shape for a problem (the same in both directions, so that the
+// workspace and the partial sums are sized from the shape alone).  A row of
+// lanes narrower than a wide tile row keeps the long shape.
+int samu_shape(const Shape& s) {
+    const int64_t row_bytes = s.D * (s.dtype == DT_F32 ? 4 : 2);
+    if (s.T <= 8 && row_bytes >= 512) return kSamuT8;
+    if (s.T <= 16 && row_bytes >= 512) return kSamuT16;
+    if (s.T <= 32 && row_bytes >= 512) return kSamuT32;
+    if (s.T <= 64 && row_bytes >= 512) return kSamuT64;
+    if (s.T <= 128 && row_bytes >= 256) return kSamuT128;
+    return kSamuLong;
 }
-Layout samu_bwd_layout(const Shape& s) {
-    return layout_of(s, SamuBwdCfg<DT_F32>::TPR, SamuBwdCfg<DT_F32>::CT);
+// tiles of the shape: threads of 16 bytes per row and rows per tile
+void samu_tile(int sh, int* tpr, int* ct) {
+    switch (sh) {
+        case kSamuT8: *tpr = 32; *ct = 8; return;
+        case kSamuT16: *tpr = 32; *ct = 16; return;
+        case kSamuT32: *tpr = 32; *ct = 32; return;
+        case kSamuT64: *tpr = 32; *ct = 64; return;
+        case kSamuT128: *tpr = 16; *ct = 128; return;
+        default: *tpr = 8; *ct = 256; return;
+    }
+}
+static_assert(SamuShapeCfg<DT_F32, kSamuT8>::Fwd::CT == 8 &&
+                  SamuShapeCfg<DT_F32, kSamuT16>::Fwd::CT == 16 &&
+                  SamuShapeCfg<DT_F32, kSamuT32>::Fwd::CT == 32 &&
+                  SamuShapeCfg<DT_F32, kSamuT64>::Fwd::CT == 64 &&
+                  SamuShapeCfg<DT_F32, kSamuT128>::Fwd::CT == 128 &&
+                  SamuShapeCfg<DT_F32, kSamuLong>::Fwd::CT == 256,
+              "tile heights");
+
+// Both directions use the same rows per tile and row width.
+Layout samu_layout(const Shape& s) {
+    int tpr = 0, ct = 0;
+    samu_tile(samu_shape(s), &tpr, &ct);
+    return layout_of(s, tpr, ct);
 }
 
 // The auxiliary buffer: the mode table [M] and token table [B*T] (float4
@@ -753,7 +819,7 @@ struct AuxLayout {
 };
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 AuxLayout aux_layout(const Shape& s) {
-    const Layout L = samu_bwd_layout(s);
+    const Layout L = samu_layout(s);
     const size_t tokens = (size_t)s.B * s.T;
     AuxLayout a;
     a.mode = 0;
@@ -777,11 +843,10 @@ hipError_t samu_factors(const Shape& s, const void* eta, const void* delta, cons
     return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, class C>
 hipError_t samu_fwd_t(const Shape& s, const SamuFwdPtrs& p, void* ws, size_t ws_bytes, bool init,
                       void* auxp, int polls, hipStream_t st) {
-    using C = SamuFwdCfg<DT>;
-    const Layout L = samu_fwd_layout(s);
+    const Layout L = samu_layout(s);
     char* aux = static_cast<char*>(auxp);
     const AuxLayout a = aux_layout(s);
     SamuFwdArgs x;
@@ -806,11 +871,10 @@ hipError_t samu_fwd_t(const Shape& s, const SamuFwdPtrs& p, void* ws, size_t ws_
     return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, class C>
 hipError_t samu_bwd_t(const Shape& s, const SamuBwdPtrs& p, void* ws, size_t ws_bytes, bool init,
                       void* auxp, int polls, hipStream_t st) {
-    using C = SamuBwdCfg<DT>;
-    const Layout L = samu_bwd_layout(s);
+    const Layout L = samu_layout(s);
     char* aux = static_cast<char*>(auxp);
     const AuxLayout a = aux_layout(s);
     SamuBwdArgs x;
@@ -854,27 +918,78 @@ hipError_t samu_bwd_t(const Shape& s, const SamuBwdPtrs& p, void* ws, size_t ws_
 }  // namespace
 
 bool samu_supported(const Shape& s) {
-    return tiled_layout_ok(s, SamuFwdCfg<DT_F32>::CT, SamuFwdCfg<DT_F32>::NT, samu_fwd_layout(s)) &&
-           tiled_layout_ok(s, SamuBwdCfg<DT_F32>::CT, SamuBwdCfg<DT_F32>::NT, samu_bwd_layout(s));
+    int tpr = 0, ct = 0;
+    samu_tile(samu_shape(s), &tpr, &ct);
+    return tiled_layout_ok(s, ct, 4 * kWave, samu_layout(s));
 }
 
 size_t samu_scratch_bytes(const Shape& s) {
-    return kHeaderBytes + 2 * std::max(region_bytes_for(samu_fwd_layout(s), kComplexWords),
-                                       region_bytes_for(samu_bwd_layout(s), kComplexWords));
+    return kHeaderBytes + 2 * region_bytes_for(samu_layout(s), kComplexWords);
 }
 
 size_t samu_aux_bytes(const Shape& s) { return aux_layout(s).total; }
 
+namespace {
+template <int DT>
+hipError_t samu_fwd_shape(const Shape& s, const SamuFwdPtrs& p, void* ws, size_t ws_bytes,
+                          bool init, void* aux, int polls, hipStream_t st) {
+    switch (samu_shape(s)) {
+        case kSamuT8:
+            return samu_fwd_t<DT, typename SamuShapeCfg<DT, kSamuT8>::Fwd>(s, p, ws, ws_bytes,
+                                                                           init, aux, polls, st);
+        case kSamuT16:
+            return samu_fwd_t<DT, typename SamuShapeCfg<DT, kSamuT16>::Fwd>(s, p, ws, ws_bytes,
+                                                                            init, aux, polls, st);
+        case kSamuT32:
+            return samu_fwd_t<DT, typename SamuShapeCfg<DT, kSamuT32>::Fwd>(s, p, ws, ws_bytes,
+                                                                            init, aux, polls, st);
+        case kSamuT64:
+            return samu_fwd_t<DT, typename SamuShapeCfg<DT, kSamuT64>::Fwd>(s, p, ws, ws_bytes,
+                                                                            init, aux, polls, st);
+        case kSamuT128:
+            return samu_fwd_t<DT, typename SamuShapeCfg<DT, kSamuT128>::Fwd>(s, p, ws, ws_bytes,
+                                                                             init, aux, polls, st);
+        default:
+            return samu_fwd_t<DT, typename SamuShapeCfg<DT, kSamuLong>::Fwd>(s, p, ws, ws_bytes,
+                                                                             init, aux, polls, st);
+    }
+}
+template <int DT>
+hipError_t samu_bwd_shape(const Shape& s, const SamuBwdPtrs& p, void* ws, size_t ws_bytes,
+                          bool init, void* aux, int polls, hipStream_t st) {
+    switch (samu_shape(s)) {
+        case kSamuT8:
+            return samu_bwd_t<DT, typename SamuShapeCfg<DT, kSamuT8>::Bwd>(s, p, ws, ws_bytes,
+                                                                           init, aux, polls, st);
+        case kSamuT16:
+            return samu_bwd_t<DT, typename SamuShapeCfg<DT, kSamuT16>::Bwd>(s, p, ws, ws_bytes,
+                                                                            init, aux, polls, st);
+        case kSamuT32:
+            return samu_bwd_t<DT, typename SamuShapeCfg<DT, kSamuT32>::Bwd>(s, p, ws, ws_bytes,
+                                                                            init, aux, polls, st);
+        case kSamuT64:
+            return samu_bwd_t<DT, typename SamuShapeCfg<DT, kSamuT64>::Bwd>(s, p, ws, ws_bytes,
+                                                                            init, aux, polls, st);
+        case kSamuT128:
+            return samu_bwd_t<DT, typename SamuShapeCfg<DT, kSamuT128>::Bwd>(s, p, ws, ws_bytes,
+                                                                             init, aux, polls, st);
+        default:
+            return samu_bwd_t<DT, typename SamuShapeCfg<DT, kSamuLong>::Bwd>(s, p, ws, ws_bytes,
+                                                                             init, aux, polls, st);
+    }
+}
+}  // namespace
+
 hipError_t launch_samu_fwd(const Shape& s, const SamuFwdPtrs& p, void* ws, size_t ws_bytes,
                            bool init, void* aux, int polls, hipStream_t st) {
-    return s.dtype == DT_F32 ? samu_fwd_t<DT_F32>(s, p, ws, ws_bytes, init, aux, polls, st)
-                             : samu_fwd_t<DT_BF16>(s, p, ws, ws_bytes, init, aux, polls, st);
+    return s.dtype == DT_F32 ? samu_fwd_shape<DT_F32>(s, p, ws, ws_bytes, init, aux, polls, st)
+                             : samu_fwd_shape<DT_BF16>(s, p, ws, ws_bytes, init, aux, polls, st);
 }
 
 hipError_t launch_samu_bwd(const Shape& s, const SamuBwdPtrs& p, void* ws, size_t ws_bytes,
                            bool init, void* aux, int polls, hipStream_t st) {
-    return s.dtype == DT_F32 ? samu_bwd_t<DT_F32>(s, p, ws, ws_bytes, init, aux, polls, st)
-                             : samu_bwd_t<DT_BF16>(s, p, ws, ws_bytes, init, aux, polls, st);
+    return s.dtype == DT_F32 ? samu_bwd_shape<DT_F32>(s, p, ws, ws_bytes, init, aux, polls, st)
+                             : samu_bwd_shape<DT_BF16>(s, p, ws, ws_bytes, init, aux, polls, st);
 }
 
 }  // namespace lrscan

@@ -166,7 +166,11 @@ def check_all(tag, res, bd, rows=slice(None), check_params=True):
         check(f"{tag} grad_theta_log", host(res["gt"]), bd.gt, bd.tol_gt)
 
 
-SHAPES = [(2, 300, 72), (3, 1000, 130), (1, 4096, 256), (2, 333, 13), (1, 1, 1), (2, 129, 1)]
+# the last five run the short-sequence tiles: 8, 16, 32 and 64 rows of
+# 512-byte rows (rows of 300 bf16 values are not 16-byte aligned) and 128 rows
+# of 256-byte rows
+SHAPES = [(2, 300, 72), (3, 1000, 130), (1, 4096, 256), (2, 333, 13), (1, 1, 1), (2, 129, 1),
+          (64, 7, 512), (30, 13, 300), (40, 20, 300), (9, 50, 520), (5, 100, 200)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
