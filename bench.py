@@ -20,7 +20,7 @@ timed steps (the dominant one's roofline), the achievable ceiling of plain
 streaming kernels with the step's access pattern on the same arrays, timed
 the same way, and the fp64 oracle's rate on a bounded sample on the host.
 
-    python bench.py --sweep lanes|short|tiles [--steps K]
+    python bench.py --sweep lanes|short|tiles|complex|samu [--steps K]
 
 prints instead the measurements behind the automatic algorithm and tile
 choice, one JSON line per shape (see sweep_lines).
@@ -902,6 +902,105 @@ def sweep_lines(args, lr, torch, W):
             torch.cuda.empty_cache()
 
 
+SWEEP_FAMILY_T = (8, 16, 32, 64, 128, 256, 1024)
+SWEEP_COMPLEX_LANES = ((8, 8), (8, 32), (8, 128), (8, 512), (32, 8), (32, 32), (32, 128),
+                       (32, 512), (64, 8), (64, 32), (64, 128), (64, 512))
+
+
+def family_sweep_lines(args, lr, torch):
+    """Short sequences of the complex and fused-transition scans, one JSON
+    line per point (M = 2560, per-call HIP events with the Infinity Cache
+    flushed before each call, the mean of `--steps` calls).
+
+    complex: the tiled form (algo fused), the per-lane walk (seq) and the
+      automatic choice, at constant work (B*T*M ~ 100M complex elements in
+      bf16, 50M in fp32; T from 8 to 1024) and over the number of lanes B*M
+      for T = 8, 32, 64 (B = 8 ... 512).
+    samu: the automatic choice (its tiles) at constant work (B*T*M ~ 84M
+      bf16 elements, T from 8 to 1024).
+    Inputs are drawn on the device (a, b, grad_out ~ N(0, 0.5^2) per part for
+    the complex scan; eta ~ N(0, 0.5^2), delta ~ N(0, 0.1^2), nu ~ U(0.005,
+    0.5), theta ~ U(0.001, 3) for the fused-transition scan).  Rates are the
+    interface bytes per second: complex forward 6*s*N + 8*B*M, backward
+    10*s*N; fused-transition forward 4*s*N, backward 6*s*N."""
+    import ctypes
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    flush = cache_flush(torch)
+    steps = max(1, args.steps)
+    L = lr.library()
+    M = 2560
+
+    def P(t):
+        return t.data_ptr()
+
+    def rate(nbytes, times):
+        return round(nbytes / (sum(times) / len(times) * 1e-3) / 1e9, 1)
+
+    def timed(f, bw, fb, bb):
+        assert f() == 0 and bw() == 0
+        torch.cuda.synchronize()
+        tf, tb = cold_times(torch, stream, [f, bw], steps, flush)
+        return {"fwd_gbps": rate(fb, tf), "bwd_gbps": rate(bb, tb),
+                "fwd_us": round(sum(tf) / len(tf) * 1e3, 1),
+                "bwd_us": round(sum(tb) / len(tb) * 1e3, 1)}
+
+    dtypes = (("bf16", lr.BF16, torch.bfloat16, 2), ("f32", lr.F32, torch.float32, 4))
+    if args.sweep == "complex":
+        points = [(name, dt, tdt, s, T, max(1, int(round(2.0e8 * 2 / s / (T * M)))))
+                  for name, dt, tdt, s in dtypes for T in SWEEP_FAMILY_T]
+        points += [(name, dt, tdt, s, T, B) for name, dt, tdt, s in dtypes
+                   for T, B in SWEEP_COMPLEX_LANES]
+        for name, dt, tdt, s, T, B in points:
+            ar, ai, br, bi, gr, gi = (torch.randn(B, T, M, device="cuda").mul_(0.5).to(tdt)
+                                      for _ in range(6))
+            o = [torch.empty_like(ar) for _ in range(6)]
+            last = [torch.empty(B, M, device="cuda") for _ in range(2)]
+            N = B * T * M
+            res = {}
+            for algo in ("fused", "seq", "auto"):
+                op = lr.make_opts(algo=algo)
+                f = lambda op=op: L.scan_complex_fwd(
+                    P(ar), P(ai), P(br), P(bi), P(o[0]), P(o[1]), P(last[0]), P(last[1]), None,
+                    None, B, T, M, dt, sh, ctypes.byref(op))
+                bw = lambda op=op: L.scan_complex_bwd(
+                    P(ar), P(ai), P(o[0]), P(o[1]), P(gr), P(gi), None, None, None, None, P(o[2]),
+                    P(o[3]), P(o[4]), P(o[5]), None, None, B, T, M, dt, sh, ctypes.byref(op))
+                res["walk" if algo == "seq" else ("tile" if algo == "fused" else "auto")] = timed(
+                    f, bw, 6 * s * N + 8 * B * M, 10 * s * N)
+            print(json.dumps({"sweep": "complex", "dtype": name, "B": B, "T": T, "M": M,
+                              "lanes": B * M, "steps": steps, **res}), flush=True)
+            del ar, ai, br, bi, gr, gi, o, last
+            torch.cuda.empty_cache()
+        return
+    for name, dt, tdt, s in dtypes[:1]:
+        for T in SWEEP_FAMILY_T:
+            B = max(1, int(round(1.68e8 * 2 / s / (T * M))))
+            eta = torch.randn(B, T, device="cuda").mul_(0.5).to(tdt)
+            delta = torch.randn(B, T, device="cuda").mul_(0.1).to(tdt)
+            nu = torch.empty(M, device="cuda").uniform_(0.005, 0.5).log_()
+            th = torch.empty(M, device="cuda").uniform_(0.001, 3.0).log_()
+            br, bi, gr, gi = (torch.randn(B, T, M, device="cuda").mul_(0.3).to(tdt)
+                              for _ in range(4))
+            o = [torch.empty_like(br) for _ in range(4)]
+            last = [torch.empty(B, M, device="cuda") for _ in range(2)]
+            grads = [torch.empty(B, T, device="cuda"), torch.empty(B, T, device="cuda"),
+                     torch.empty(M, device="cuda"), torch.empty(M, device="cuda")]
+            ctl = (P(eta), P(delta), P(nu), P(th))
+            op = lr.make_opts()
+            f = lambda: L.scan_samu_fwd(*ctl, P(br), P(bi), P(o[0]), P(o[1]), P(last[0]),
+                                        P(last[1]), None, None, B, T, M, dt, sh, ctypes.byref(op))
+            bw = lambda: L.scan_samu_bwd(*ctl, P(o[0]), P(o[1]), P(gr), P(gi), None, None, None,
+                                         None, *(P(x) for x in grads), P(o[2]), P(o[3]), None,
+                                         None, B, T, M, dt, sh, ctypes.byref(op))
+            N = B * T * M
+            res = timed(f, bw, 4 * s * N, 6 * s * N)
+            print(json.dumps({"sweep": "samu", "dtype": name, "B": B, "T": T, "M": M,
+                              "steps": steps, "auto": res}), flush=True)
+            del eta, delta, br, bi, gr, gi, o, last, grads
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -924,11 +1023,13 @@ def main():
                     help="only run kernels of known traffic (a 1 GiB device copy and the "
                          "read-2/write-1 streaming kernel on 3 x 256 MiB), the reference for "
                          "HBM byte counters")
-    ap.add_argument("--sweep", choices=["lanes", "short", "tiles"],
+    ap.add_argument("--sweep", choices=["lanes", "short", "tiles", "complex", "samu"],
                     help="print the dispatch measurements instead of the step: the per-lane "
                          "walk against the automatic choice over the number of lanes (lanes), "
                          "every tile shape on short sequences (short) or on the large "
-                         "workloads (tiles); one JSON line per point")
+                         "workloads (tiles), the complex scan's tiles against its walk on short "
+                         "sequences (complex), the fused-transition scan on short sequences "
+                         "(samu); one JSON line per point")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -968,6 +1069,9 @@ def main():
                           "repetitions": args.steps}))
         return
 
+    if args.sweep in ("complex", "samu"):
+        family_sweep_lines(args, lr, torch)
+        return
     if args.sweep:
         sweep_lines(args, lr, torch, W)
         return
