@@ -148,11 +148,35 @@ bool prefer_seq(const Shape& s) {
            s.B * s.D >= ((int64_t)1 << 20);
 }
 
+// The three-launch form for long sequences over one or two 128-byte lane
+// blocks in all: the fused form's tiles then form one or two chains, whose
+// states advance by one look-back window per publication round trip, while
+// the three-launch form summarises every chunk in parallel once there are
+// thousands of chunks.  Measured on MI355X (caches flushed, forward /
+// backward TB/s, fused -> chunks of 256 / of 1024 rows): one chain, bf16
+// D = 64: T = 256K 1.0 / 1.0 -> 0.8 / 0.4 (fused ahead), T = 1M 1.2 / 1.0 ->
+// 1.9 / 1.3, T = 4M 1.2 / 1.0 -> 1.8 / 1.9 and 2.5 / 1.3, T = 8M 1.2 / 1.0 ->
+// 1.6 / 1.9 and 2.6 / 2.4; two chains, bf16 D = 128: T = 1M 2.4 / 2.0 ->
+// 2.5 / 2.1, T = 2M 2.4 / 2.1 -> 2.3 / 2.6 and 2.8 / 1.4; fp32 D = 64: T = 2M
+// 2.4 / 2.1 -> 2.3 / 2.7 and 2.8 / 1.5.  From four chains the fused form is
+// ahead (bf16 D = 256, T = 1M: 4.4 / 3.9 against 2.6 / 2.6).  Returns the
+// chunk length, or 0 for the other forms.
+int prefer_chunked(const Shape& s, int dir) {
+    if (s.T < ((int64_t)1 << 20)) return 0;
+    const int64_t eb = s.dtype == LRSCAN_F32 ? 4 : 2;
+    const int64_t chains = s.B * ((s.D * eb + 127) / 128);
+    if (chains > 2) return 0;
+    if (dir == 1) return s.T >= ((int64_t)1 << 23) ? 1024 : 256;
+    if (chains == 1) return s.T >= ((int64_t)1 << 22) ? 1024 : 256;
+    return s.T >= ((int64_t)1 << 21) ? 1024 : 0;
+}
+
 // The automatic choice: the per-lane walk for short sequences over many
-// lanes (prefer_seq); otherwise the single-launch fused form, which reads
-// every input once and was the fastest form on every other measured shape,
-// with its tile shape from fused_default_cfg; the three-launch form past the
-// fused form's index limits.
+// lanes (prefer_seq); the three-launch form for long sequences over one or
+// two lane blocks (prefer_chunked); otherwise the single-launch fused form,
+// which reads every input once and was the fastest form on every other
+// measured shape, with its tile shape from fused_default_cfg; the
+// three-launch form past the fused form's index limits.
 Resolved resolve(const Shape& s, int dir, const lrscan_opts* o, bool aligned) {
     Resolved r;
     r.algo = o ? o->algo : LRSCAN_ALGO_AUTO;
@@ -161,6 +185,12 @@ Resolved resolve(const Shape& s, int dir, const lrscan_opts* o, bool aligned) {
     if (r.algo == LRSCAN_ALGO_AUTO && prefer_seq(s)) {
         r.algo = LRSCAN_ALGO_SEQ;
         r.chunk = 0;
+        r.width = 0;
+        return r;
+    }
+    if (r.algo == LRSCAN_ALGO_AUTO && prefer_chunked(s, dir) > 0) {
+        r.algo = LRSCAN_ALGO_CHUNKED;
+        r.chunk = prefer_chunked(s, dir);
         r.width = 0;
         return r;
     }

@@ -170,6 +170,20 @@ def test_workspace_sizes_and_auto_choice():
             assert algo == lr.ALGO_SEQ
             algo, _, _ = lr.scan_auto_algo(16384, 16, 64, dt, direction)
             assert algo == (lr.ALGO_SEQ if dt == lr.BF16 else lr.ALGO_FUSED)
+            # sequences of a million steps or more over one or two 128-byte
+            # lane blocks in all: the three-launch form, with longer chunks
+            # for longer sequences; shorter ones, and more blocks: fused
+            one = 64 if dt == lr.BF16 else 32
+            algo, chunk, _ = lr.scan_auto_algo(1, 1 << 20, one, dt, direction)
+            assert algo == lr.ALGO_CHUNKED and chunk == 256
+            algo, chunk, _ = lr.scan_auto_algo(1, 1 << 23, one, dt, direction)
+            assert algo == lr.ALGO_CHUNKED and chunk == 1024
+            algo, _, _ = lr.scan_auto_algo(1, (1 << 20) - 1, one, dt, direction)
+            assert algo == lr.ALGO_FUSED
+            algo, chunk, _ = lr.scan_auto_algo(1, 1 << 20, 2 * one, dt, direction)
+            assert algo == (lr.ALGO_FUSED if direction == 0 else lr.ALGO_CHUNKED)
+            algo, _, _ = lr.scan_auto_algo(1, 1 << 23, 4 * one, dt, direction)
+            assert algo == lr.ALGO_FUSED
             # long sequences, and short ones over too few lanes for the walk: the fused form
             algo, _, _ = lr.scan_auto_algo(8, 2048, 2560, dt, direction)
             assert algo == lr.ALGO_FUSED

@@ -27,9 +27,11 @@ def _need_gpu():
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("B,T,D", [(1, (1 << 20) + 3, 1), (1, (1 << 18) + 7, 8), (2, 100003, 3)],
                          ids=["T1M_D1", "T256k_D8", "B2_T100k_D3"])
-@pytest.mark.parametrize("algo,chunk", [("auto", 0), ("chunked", 1024), ("seq", 0)],
-                         ids=["auto", "chunked1024", "seq"])
+@pytest.mark.parametrize("algo,chunk", [("auto", 0), ("fused", 0), ("chunked", 1024), ("seq", 0)],
+                         ids=["auto", "fused", "chunked1024", "seq"])
 def test_long_single_chain(B, T, D, dt, algo, chunk):
+    # AUTO takes the three-launch form on the million-step one-block chain;
+    # the fused form is run explicitly for its chained look-backs
     inp = W.random_inputs(B, T, D, dt, seed=51, a_lo=0.5, a_hi=0.99)
     res = run_pair(inp, algo, chunk, chunk)
     check_against_oracle(inp, res)
