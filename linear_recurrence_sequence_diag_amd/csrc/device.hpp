@@ -112,6 +112,7 @@ struct RowVec {
 // write-back.  (Measured on MI355X: the backward on [8,2048,2560] bf16 went
 // from 94 to 78 us; every other form gained 0-14%.)
 typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void store16_nt(void* p, uint4 v) {
     const u32x4_nt w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4_nt*>(p));
@@ -133,9 +134,72 @@ struct RowOut {
     }
 };
 
-// Load V lanes starting at element offset `off` (lane d0 of a row).
-// ALIGNED: the whole vector is in range and 16-byte aligned.
-// Otherwise `nvalid` (0..V) lanes are loaded one by one and the rest are `fill`.
+// ---- rows that are not 16-byte aligned -------------------------------------
+// A thread's 16 bytes [p, p + 16) then straddle two aligned blocks, sh = p mod
+// 16 bytes (a multiple of the element size) into the first.  Reading them as
+// one or two aligned 16-byte loads and shifting keeps the access pattern of
+// aligned rows (element-wise accesses, eight 2-byte loads per bf16 vector,
+// ran the scan about ten times slower).
+
+// d[k + q] for q = 0..3, with no indexing of registers by a variable.
+__device__ __forceinline__ uint32_t dword_at(const uint32_t (&d)[8], uint32_t q, int k) {
+    return q == 0 ? d[k] : q == 1 ? d[k + 1] : q == 2 ? d[k + 2] : d[k + 3];
+}
+
+// The 16 bytes that start `sh` (0..15) bytes into the 32 bytes lo, hi.
+__device__ __forceinline__ uint4 bytes16_at(uint4 lo, uint4 hi, uint32_t sh) {
+    const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    const uint32_t q = sh >> 2, r = sh & 3u;
+    uint32_t e[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) e[k] = dword_at(d, q, k);
+    // alignbyte(hi, lo, r): bytes r .. r + 3 of the 64-bit value hi:lo
+    return make_uint4(__builtin_amdgcn_alignbyte(e[1], e[0], r),
+                      __builtin_amdgcn_alignbyte(e[2], e[1], r),
+                      __builtin_amdgcn_alignbyte(e[3], e[2], r),
+                      __builtin_amdgcn_alignbyte(e[4], e[3], r));
+}
+
+// Load a vector at an address that need not be 16-byte aligned: the aligned
+// block holding its first byte and, when lanes of the vector lie in it, the
+// next block (each block read holds bytes of the vector, so no read reaches
+// past memory the vector lies in; otherwise the first block is read twice),
+// then shifted into place.  Lanes from `nvalid` on are `fill`.  No branches:
+// the same code serves complete vectors and a row's last, partial one.
+template <int DT>
+__device__ __forceinline__ RowVec<DT> load_vec_unaligned(const char* p, int nvalid, float fill) {
+    constexpr int S = Elem<DT>::bytes;
+    const uintptr_t ua = reinterpret_cast<uintptr_t>(p);
+    const uint32_t sh = (uint32_t)(ua & 15u);
+    const uint4* blk = reinterpret_cast<const uint4*>(ua - sh);
+    const bool straddles = (uint32_t)(nvalid * S) > 16u - sh;
+    const uint4 lo = blk[0];
+    const uint4 hi = blk[straddles ? 1 : 0];
+    const uint4 w = bytes16_at(lo, hi, sh);
+    // keep the bits of lanes below nvalid, `fill` elsewhere
+    const uint4 f = RowVec<DT>::splat(fill).w;
+    uint32_t m[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if constexpr (DT == DT_F32) {
+            m[q] = q < nvalid ? 0xffffffffu : 0u;
+        } else {
+            m[q] = (2 * q < nvalid ? 0x0000ffffu : 0u) | (2 * q + 1 < nvalid ? 0xffff0000u : 0u);
+        }
+    }
+    RowVec<DT> r;
+    r.w = make_uint4((w.x & m[0]) | (f.x & ~m[0]), (w.y & m[1]) | (f.y & ~m[1]),
+                     (w.z & m[2]) | (f.z & ~m[2]), (w.w & m[3]) | (f.w & ~m[3]));
+    return r;
+}
+
+// Load V lanes starting at element offset `off` (lane d0 of a row), for the
+// per-lane walk and the three-launch form.  ALIGNED: the whole vector is in
+// range and 16-byte aligned.  Otherwise `nvalid` (0..V) lanes are read one
+// by one and the rest are `fill`: these kernels keep many rows of loads in
+// flight per thread, and the two-block reads of load_vec_unaligned would
+// double the registers that takes (measured: the walk's backward at 256
+// VGPRs and one wave per SIMD, 0.3x as fast over few lanes).
 template <int DT, bool ALIGNED>
 __device__ __forceinline__ RowVec<DT> load_row(const void* base, size_t off, int nvalid, float fill) {
     if constexpr (ALIGNED) {
@@ -174,6 +238,108 @@ __device__ __forceinline__ void store_row(void* base, size_t off, int nvalid, co
     }
 }
 
+// Dword q (0..3) of r, q not known at compile time.
+__device__ __forceinline__ uint32_t dword_of(uint4 r, uint32_t q) {
+    return q == 0 ? r.x : q == 1 ? r.y : q == 2 ? r.z : r.w;
+}
+
+// Store bytes [o0, o1) of a 16-byte block image `img` at the aligned block
+// `blk`, as at most three naturally aligned pieces; o0 and o1 are even, and
+// either o0 == 0 or o1 == 16.
+__device__ __forceinline__ void store_block_part(char* blk, uint4 img, uint32_t o0, uint32_t o1) {
+    if (o1 == 16) {  // a head: pieces of 2, 4, then 8 bytes up to the block's end
+        uint32_t o = o0;
+        if (o & 2u) {
+            __builtin_nontemporal_store((uint16_t)(dword_of(img, o >> 2) >> 16),
+                                        reinterpret_cast<uint16_t*>(blk + o));
+            o += 2;
+        }
+        if (o & 4u) {
+            __builtin_nontemporal_store(dword_of(img, o >> 2), reinterpret_cast<uint32_t*>(blk + o));
+            o += 4;
+        }
+        if (o & 8u) {
+            const u32x2_nt v = {img.z, img.w};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2_nt*>(blk + 8));
+        }
+    } else {  // a tail: pieces of 8, 4, then 2 bytes from the block's start
+        uint32_t o = 0;
+        if (o1 & 8u) {
+            const u32x2_nt v = {img.x, img.y};
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x2_nt*>(blk));
+            o = 8;
+        }
+        if (o1 & 4u) {
+            __builtin_nontemporal_store(dword_of(img, o >> 2), reinterpret_cast<uint32_t*>(blk + o));
+            o += 4;
+        }
+        if (o1 & 2u)
+            __builtin_nontemporal_store((uint16_t)dword_of(img, o >> 2),
+                                        reinterpret_cast<uint16_t*>(blk + o));
+    }
+}
+
+// Store a vector at an address that need not be 16-byte aligned.  Threads
+// in consecutive lanes that hold consecutive vectors of one row share the
+// aligned blocks between them: a block holds the tail of one thread's
+// vector and the head of the next one's, and the later thread writes the
+// whole block (the earlier one's tail through a lane shuffle) when both parts
+// are there.  `prev_adj` / `next_adj`: the thread in the previous / next lane
+// holds the previous / next vector of this row and stores it in this same
+// call.  A part of a block shared with any other writer is written in at most
+// three naturally aligned pieces (element by element for a vector that
+// reaches past the row's end).  `rem` is the number of lanes from this
+// thread's first to the end of the row (nvalid = min(rem, V)).
+template <int DT>
+__device__ __forceinline__ void store_vec_unaligned(char* p, int nvalid, const RowOut<DT>& o,
+                                                    bool prev_adj, bool next_adj, int rem) {
+    constexpr int V = Elem<DT>::V, S = Elem<DT>::bytes;
+    const uint4 w = o.pack();
+    // the previous lane's packed vector (used only when prev_adj)
+    const uint4 wp = make_uint4(__shfl_up(w.x, 1, kWave), __shfl_up(w.y, 1, kWave),
+                                __shfl_up(w.z, 1, kWave), __shfl_up(w.w, 1, kWave));
+    if (nvalid <= 0) return;
+    const uintptr_t ua = reinterpret_cast<uintptr_t>(p);
+    const uint32_t sh = (uint32_t)(ua & 15u);
+    if (sh == 0 && nvalid == V) {
+        store16_nt(p, w);
+        return;
+    }
+    const int k = (int)(16u - sh) / S;  // this vector's elements in its first block
+    const int nv_next = rem - V < 0 ? 0 : (rem - V > V ? V : rem - V);
+    // the block holding this vector's head is written whole by this thread
+    // when the previous lane's vector is adjacent (then it is complete, as
+    // this one has lanes) and this vector's head is complete; this vector's
+    // tail goes with the next lane's block when that thread writes it
+    const bool mine = sh != 0 && prev_adj && nvalid >= k;
+    const bool next_takes = sh != 0 && next_adj && nvalid == V && nv_next >= k;
+    char* blk = reinterpret_cast<char*>(ua - sh);
+    if (nvalid == V) {
+        if (mine) store16_nt(blk, bytes16_at(wp, w, 16u - sh));
+        // w rotated so that its bytes sit at their offsets in the two blocks:
+        // the head at sh .. 15 of the first, the tail at 0 .. sh - 1 of the second
+        const uint4 rot = bytes16_at(w, w, 16u - sh);
+        if (!mine) store_block_part(blk, rot, sh, 16);
+        if (!next_takes) store_block_part(blk + 16, rot, 0, sh);
+        return;
+    }
+    const uint32_t words[4] = {w.x, w.y, w.z, w.w};
+    const int h1 = mine ? 0 : (nvalid < k ? nvalid : k);  // head elements stored one by one
+    const int t0 = next_takes ? nvalid : k;                // tail elements from t0 on
+    if (mine) store16_nt(blk, bytes16_at(wp, w, 16u - sh));
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        if (j < nvalid && (j < h1 || j >= t0)) {
+            if constexpr (DT == DT_F32) {
+                __builtin_nontemporal_store(words[j], reinterpret_cast<uint32_t*>(p) + j);
+            } else {
+                const uint16_t h = (uint16_t)(words[j >> 1] >> ((j & 1) * 16));
+                __builtin_nontemporal_store(h, reinterpret_cast<uint16_t*>(p) + j);
+            }
+        }
+    }
+}
+
 // Row vectors addressed as (wave-uniform row pointer) + (per-lane byte offset),
 // so the compiler can keep the pointer in SGPRs and one 32-bit offset per lane
 // in a VGPR for every row of a tile.
@@ -202,17 +368,22 @@ __device__ __forceinline__ RowVec<DT> load_vec(const char* row, uint32_t lane_of
         }
         return r;
     } else {
-        return load_row<DT, false>(row + lane_off, 0, nvalid, fill);
+        return load_vec_unaligned<DT>(row + lane_off, nvalid, fill);
     }
 }
 
-template <int DT, bool ALIGNED>
+// The store of one thread's vector of a tile row: `cg` is the thread's place
+// in its row group of TPR threads, `rem` the lanes from its first to the end
+// of the row (used when rows are not aligned).
+template <int DT, bool ALIGNED, int TPR>
 __device__ __forceinline__ void store_vec(char* row, uint32_t lane_off, int nvalid,
-                                          const RowOut<DT>& o) {
+                                          const RowOut<DT>& o, int cg, int rem) {
     if constexpr (ALIGNED) {
         store16_nt(row + lane_off, o.pack());
     } else {
-        store_row<DT, false>(row + lane_off, 0, nvalid, o);
+        // the TPR threads of a row group (consecutive lanes, cg = 0 .. TPR - 1)
+        // hold consecutive vectors of one tile row
+        store_vec_unaligned<DT>(row + lane_off, nvalid, o, cg > 0, cg + 1 < TPR, rem);
     }
 }
 

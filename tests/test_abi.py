@@ -189,6 +189,14 @@ def test_workspace_sizes_and_auto_choice():
             assert algo == lr.ALGO_FUSED
             algo, _, _ = lr.scan_auto_algo(4, 16, 1024, dt, direction)
             assert algo == lr.ALGO_FUSED
+            # rows that are not 16-byte aligned: the walk up to 64 steps from
+            # 2^18 lanes (fp32: 128 steps), as their only tile is 256 rows tall
+            algo, _, _ = lr.scan_auto_algo(4096, 64, 2559, dt, direction)
+            assert algo == lr.ALGO_SEQ
+            algo, _, _ = lr.scan_auto_algo(4096, 64, 2560, dt, direction)
+            assert algo == lr.ALGO_FUSED
+            algo, _, _ = lr.scan_auto_algo(4096, 128, 2559, dt, direction)
+            assert algo == (lr.ALGO_SEQ if dt == lr.F32 else lr.ALGO_FUSED)
             # a tile is no taller than a short sequence, and a forward chain of
             # at most 512 steps is one tile
             _, tile, _ = lr.scan_auto_algo(4096, 32, 2560, dt, direction)
