@@ -22,15 +22,20 @@ constexpr int kSeqU = 8;  // rows in flight per buffer
 // A walk's store of its vector of one row.  Rows that are not 16-byte
 // aligned share aligned blocks between neighbouring lanes, which hold
 // neighbouring vectors of a row unless a row starts between them (or a
-// wavefront does).
+// wavefront does); over many lanes the walk writes those blocks whole
+// (store_vec_unaligned), over few lanes, where each thread's latency bounds
+// the walk, element by element (measured on MI355X, bf16 D = 2559: [4096, 8]
+// 0.91 / 0.77 -> 1.6 / 1.4 TB/s with shared blocks, while [8, 2048] fell
+// from 50 to 34 GB/s).
 struct WalkNbrs {
-    bool prev, next;
+    bool prev, next, share;
     int rem;  // lanes from this thread's first to the end of its row
 };
-__device__ __forceinline__ WalkNbrs walk_nbrs(int64_t vidx, int64_t vpr, int64_t rem) {
+__device__ __forceinline__ WalkNbrs walk_nbrs(int64_t vidx, int64_t vpr, int64_t rem,
+                                              int64_t lanes) {
     const int lane = (int)(threadIdx.x % kWave);
     return WalkNbrs{lane > 0 && vidx > 0, lane + 1 < kWave && vidx + 1 < vpr,
-                    (int)(rem < 64 ? rem : 64)};
+                    lanes >= ((int64_t)1 << 18), (int)(rem < 64 ? rem : 64)};
 }
 template <int DT, bool ALIGNED>
 __device__ __forceinline__ void walk_store(void* base, size_t off, int nvalid, const RowOut<DT>& o,
@@ -38,8 +43,11 @@ __device__ __forceinline__ void walk_store(void* base, size_t off, int nvalid, c
     if constexpr (ALIGNED) {
         store_row<DT, true>(base, off, nvalid, o);
     } else {
-        store_vec_unaligned<DT>(reinterpret_cast<char*>(base) + off * Elem<DT>::bytes, nvalid, o,
-                                nb.prev, nb.next, nb.rem);
+        if (nb.share)
+            store_vec_unaligned<DT>(reinterpret_cast<char*>(base) + off * Elem<DT>::bytes, nvalid,
+                                    o, nb.prev, nb.next, nb.rem);
+        else
+            store_row<DT, false>(base, off, nvalid, o);
     }
 }
 
@@ -59,7 +67,7 @@ __global__ __launch_bounds__(kSeqBlock) void seq_fwd_kernel(const void* __restri
     if (bi >= B) return;
     const int64_t d0 = (gid - bi * vpr) * V;
     const int nvalid = (int)((D - d0) < V ? (D - d0) : V);
-    const WalkNbrs nbrs = walk_nbrs(gid - bi * vpr, vpr, D - d0);
+    const WalkNbrs nbrs = walk_nbrs(gid - bi * vpr, vpr, D - d0, B * D);
     const size_t base = (size_t)bi * (size_t)T * (size_t)D + (size_t)d0;
 
     float h[V];
@@ -129,7 +137,7 @@ __global__ __launch_bounds__(kSeqBlock) void seq_bwd_kernel(
     if (bi >= B) return;
     const int64_t d0 = (gid - bi * vpr) * V;
     const int nvalid = (int)((D - d0) < V ? (D - d0) : V);
-    const WalkNbrs nbrs = walk_nbrs(gid - bi * vpr, vpr, D - d0);
+    const WalkNbrs nbrs = walk_nbrs(gid - bi * vpr, vpr, D - d0, B * D);
     const size_t base = (size_t)bi * (size_t)T * (size_t)D + (size_t)d0;
 
     float carry[V], hinit[V];

@@ -39,6 +39,22 @@ def test_long_single_chain(B, T, D, dt, algo, chunk):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("algo", ["auto", "seq", "fused"])
+def test_many_lanes_unaligned_rows(dt, algo):
+    """Rows that are not 16-byte aligned over 300K lanes and a few steps: the
+    walk writes blocks shared between neighbouring lanes (and wavefronts and
+    batch rows end mid-block), the tiles write blocks shared across their
+    row groups; every element against the oracle, with h0 and grad_last."""
+    B, T, D = 300, 5, 1001
+    inp = W.random_inputs(B, T, D, dt, seed=59, a_lo=0.5, a_hi=0.99)
+    rng = np.random.default_rng(60)
+    h0 = rng.standard_normal((B, D)).astype(np.float32)
+    gl = rng.standard_normal((B, D)).astype(np.float32)
+    check_against_oracle(inp, run_pair(inp, algo, 0, 0, h0=h0, gl=gl), h0=h0, gl=gl)
+    log(f"{algo} {dt} B{B} T{T} D{D}: within tolerance")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("algo,chunk", [("auto", 0), ("chunked", 16), ("seq", 0)],
                          ids=["auto", "chunked16", "seq"])
 def test_single_step_many_lanes(dt, algo, chunk):
