@@ -916,8 +916,9 @@ def family_sweep_lines(args, lr, torch):
       automatic choice, at constant work (B*T*M ~ 100M complex elements in
       bf16, 50M in fp32; T from 8 to 1024) and over the number of lanes B*M
       for T = 8, 32, 64 (B = 8 ... 512).
-    samu: the automatic choice (its tiles) at constant work (B*T*M ~ 84M
-      bf16 elements, T from 8 to 1024).
+    samu: the fused-transition scan's tiles, its per-lane walk and the
+      automatic choice at constant work (B*T*M ~ 84M bf16 elements, 42M
+      fp32; T from 8 to 1024).
     Inputs are drawn on the device (a, b, grad_out ~ N(0, 0.5^2) per part for
     the complex scan; eta ~ N(0, 0.5^2), delta ~ N(0, 0.1^2), nu ~ U(0.005,
     0.5), theta ~ U(0.001, 3) for the fused-transition scan).  Rates are the
@@ -973,7 +974,7 @@ def family_sweep_lines(args, lr, torch):
             del ar, ai, br, bi, gr, gi, o, last
             torch.cuda.empty_cache()
         return
-    for name, dt, tdt, s in dtypes[:1]:
+    for name, dt, tdt, s in dtypes:
         for T in SWEEP_FAMILY_T:
             B = max(1, int(round(1.68e8 * 2 / s / (T * M))))
             eta = torch.randn(B, T, device="cuda").mul_(0.5).to(tdt)
@@ -987,16 +988,21 @@ def family_sweep_lines(args, lr, torch):
             grads = [torch.empty(B, T, device="cuda"), torch.empty(B, T, device="cuda"),
                      torch.empty(M, device="cuda"), torch.empty(M, device="cuda")]
             ctl = (P(eta), P(delta), P(nu), P(th))
-            op = lr.make_opts()
-            f = lambda: L.scan_samu_fwd(*ctl, P(br), P(bi), P(o[0]), P(o[1]), P(last[0]),
-                                        P(last[1]), None, None, B, T, M, dt, sh, ctypes.byref(op))
-            bw = lambda: L.scan_samu_bwd(*ctl, P(o[0]), P(o[1]), P(gr), P(gi), None, None, None,
-                                         None, *(P(x) for x in grads), P(o[2]), P(o[3]), None,
-                                         None, B, T, M, dt, sh, ctypes.byref(op))
             N = B * T * M
-            res = timed(f, bw, 4 * s * N, 6 * s * N)
+            res = {}
+            for algo in ("fused", "seq", "auto"):
+                op = lr.make_opts(algo=algo)
+                f = lambda op=op: L.scan_samu_fwd(*ctl, P(br), P(bi), P(o[0]), P(o[1]),
+                                                  P(last[0]), P(last[1]), None, None, B, T, M,
+                                                  dt, sh, ctypes.byref(op))
+                bw = lambda op=op: L.scan_samu_bwd(*ctl, P(o[0]), P(o[1]), P(gr), P(gi), None,
+                                                   None, None, None, *(P(x) for x in grads),
+                                                   P(o[2]), P(o[3]), None, None, B, T, M, dt, sh,
+                                                   ctypes.byref(op))
+                res["walk" if algo == "seq" else ("tile" if algo == "fused" else "auto")] = timed(
+                    f, bw, 4 * s * N, 6 * s * N)
             print(json.dumps({"sweep": "samu", "dtype": name, "B": B, "T": T, "M": M,
-                              "steps": steps, "auto": res}), flush=True)
+                              "lanes": B * M, "steps": steps, **res}), flush=True)
             del eta, delta, br, bi, gr, gi, o, last, grads
             torch.cuda.empty_cache()
 
@@ -1028,8 +1034,8 @@ def main():
                          "walk against the automatic choice over the number of lanes (lanes), "
                          "every tile shape on short sequences (short) or on the large "
                          "workloads (tiles), the complex scan's tiles against its walk on short "
-                         "sequences (complex), the fused-transition scan on short sequences "
-                         "(samu); one JSON line per point")
+                         "sequences (complex), the fused-transition scan's tiles against its walk "
+                         "on short sequences (samu); one JSON line per point")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

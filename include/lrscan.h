@@ -247,10 +247,12 @@ LRSCAN_API size_t scan_complex_workspace_bytes(int64_t B, int64_t T, int64_t M, 
  * a fixed order (results do not depend on scheduling).  At a reset step
  * (opts->reset) the transition is 0 and contributes nothing to the four
  * parameter gradients.
- * opts: algo AUTO or FUSED only (else LRSCAN_ERR_ALGO) with chunk and width
- * 0: the tile shapes are the library's (else LRSCAN_ERR_CHUNK); workspace,
- * polls and reset as for the real scan.  A caller workspace must hold
- * scan_samu_workspace_bytes(); its contents are overwritten by every call.
+ * opts: algo AUTO, FUSED or SEQ (a per-lane walk; CHUNKED returns
+ * LRSCAN_ERR_ALGO) with chunk and width 0: the tile shapes are the library's
+ * (else LRSCAN_ERR_CHUNK); AUTO walks sequences of at most 16 steps (bf16:
+ * 64) over at least 2^18 lanes and tiles the rest; workspace, polls and reset as for the
+ * real scan.  A caller workspace must hold scan_samu_workspace_bytes() (the
+ * same for every algorithm); its contents are overwritten by every call.
  * ------------------------------------------------------------------------ */
 /*   eta, delta, nu_log, theta_log, br, bi read.  out_r, out_i written (NULL
  *   pair: state-only forward, then last is required).  last_r, last_i written

@@ -469,7 +469,7 @@ def _check_controls(eta, delta, nu_log, theta_log, ref):
 
 
 def samu_scan(eta, delta, nu_log, theta_log, br, bi, h0=None, with_last=True, with_out=True,
-              polls=0, reset=None, workspace=None):
+              polls=0, reset=None, workspace=None, algo="auto"):
     """Fused-transition complex scan: a_t = exp(-e^nu_log e^eta) exp(i (e^theta_log + delta))
     is rebuilt in the kernel; h_t = a_t h_{t-1} + b_t on planar [B, T, M] b.
     Returns (out_r, out_i, last_r, last_i); parts not asked for are None."""
@@ -492,13 +492,14 @@ def samu_scan(eta, delta, nu_log, theta_log, br, bi, h0=None, with_last=True, wi
         scan_samu_fwd(eta.data_ptr(), delta.data_ptr(), nu_log.data_ptr(), theta_log.data_ptr(),
                       br.data_ptr(), bi.data_ptr(), _ptr(out_r), _ptr(out_i), _ptr(last_r),
                       _ptr(last_i), _ptr(h0r), _ptr(h0i), B, T, M, dtype_code(br.dtype),
-                      _stream(br), make_opts(polls=polls, reset=reset, workspace=workspace))
+                      _stream(br), make_opts(algo=algo, polls=polls, reset=reset,
+                                             workspace=workspace))
     return out_r, out_i, last_r, last_i
 
 
 def samu_scan_backward(eta, delta, nu_log, theta_log, out_r, out_i, grad_out_r, grad_out_i,
                        grad_last=None, h0=None, need_grad_h0=False, polls=0, reset=None,
-                       workspace=None):
+                       workspace=None, algo="auto"):
     """Adjoint of samu_scan for L = sum Re(conj(g) out) + Re(conj(grad_last) last).
     Returns (grad_eta [B,T], grad_delta [B,T], grad_nu_log [M], grad_theta_log [M]
     (all float32), grad_br, grad_bi, (grad_h0_r, grad_h0_i) or None)."""
@@ -528,7 +529,7 @@ def samu_scan_backward(eta, delta, nu_log, theta_log, out_r, out_i, grad_out_r, 
                       grad_out_i.data_ptr(), _ptr(glr), _ptr(gli), _ptr(h0r), _ptr(h0i),
                       ge.data_ptr(), gd.data_ptr(), gn.data_ptr(), gt.data_ptr(), gbr.data_ptr(),
                       gbi.data_ptr(), _ptr(gh0r), _ptr(gh0i), B, T, M, dtype_code(out_r.dtype),
-                      _stream(out_r), make_opts(polls=polls, reset=reset, workspace=workspace))
+                      _stream(out_r), make_opts(algo=algo, polls=polls, reset=reset, workspace=workspace))
     return ge, gd, gn, gt, gbr, gbi, gh0
 
 

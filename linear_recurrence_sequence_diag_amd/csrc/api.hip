@@ -337,12 +337,26 @@ int complex_workspace(const Shape& s, int algo, const lrscan_opts* o, hipStream_
 
 // ---- fused-transition scan helpers ----
 
-// AUTO or FUSED with the library's tile shapes (chunk and width 0); other
-// algorithms are not provided.
-int samu_algo(const lrscan_opts* o) {
+// The per-lane walk of the fused-transition scan for short sequences over
+// at least 2^18 lanes, where even tiles as short as the sequence spend much
+// of their time on fixed costs.  Measured on MI355X (M = 2560, B*T*M fixed,
+// caches flushed, forward / backward TB/s, tiles against walk): bf16 T = 8
+// 1.2 / 1.1 against 3.9 / 2.9, T = 32 3.5 / 3.0 against 4.6 / 4.1, T = 64
+// 4.3 / 3.9 against 4.5 / 4.2; fp32 T = 16 4.6 / 4.1 against 5.1 / 4.4,
+// T = 32 5.1 / 4.8 against 4.8 / 4.5.
+bool samu_prefer_seq(const Shape& s) {
+    if (s.B * s.D < ((int64_t)1 << 18)) return false;
+    return s.T <= 16 || (s.dtype == LRSCAN_BF16 && s.T <= 64);
+}
+
+// AUTO (SEQ for short sequences, else FUSED), FUSED with the library's tile
+// shapes (chunk and width 0) or SEQ; CHUNKED is not provided.
+int samu_algo(const Shape& s, const lrscan_opts* o, int* algo) {
     const int a = o ? o->algo : LRSCAN_ALGO_AUTO;
-    if (a != LRSCAN_ALGO_AUTO && a != LRSCAN_ALGO_FUSED) return LRSCAN_ERR_ALGO;
+    if (a != LRSCAN_ALGO_AUTO && a != LRSCAN_ALGO_FUSED && a != LRSCAN_ALGO_SEQ)
+        return LRSCAN_ERR_ALGO;
     if (o && (o->chunk != 0 || o->width != 0)) return LRSCAN_ERR_CHUNK;
+    *algo = a == LRSCAN_ALGO_AUTO ? (samu_prefer_seq(s) ? LRSCAN_ALGO_SEQ : LRSCAN_ALGO_FUSED) : a;
     return LRSCAN_OK;
 }
 
@@ -672,9 +686,10 @@ LRSCAN_API int scan_samu_fwd(const void* eta, const void* delta, const float* nu
     if (!out_r && !last_r) return LRSCAN_ERR_NULL;
     if (!dims_ok(B, T, M)) return LRSCAN_ERR_DIM;
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
-    int st = samu_algo(opts);
-    if (st != LRSCAN_OK) return st;
     const Shape s{B, T, M, dtype};
+    int algo = 0;
+    int st = samu_algo(s, opts, &algo);
+    if (st != LRSCAN_OK) return st;
     const SamuFwdPtrs p{eta,    delta,  nu_log, theta_log, br,   bi,  out_r,
                         out_i,  last_r, last_i, h0_r,      h0_i, opts ? opts->reset : nullptr};
     hipStream_t hs = static_cast<hipStream_t>(stream);
@@ -682,6 +697,8 @@ LRSCAN_API int scan_samu_fwd(const void* eta, const void* delta, const float* nu
     void* aux = nullptr;
     st = samu_workspace(s, opts, hs, &ws, &aux);
     if (st != LRSCAN_OK) return st;
+    // the walk leaves the fused scratch untouched (not initialised by it)
+    if (algo == LRSCAN_ALGO_SEQ) return hip_status(launch_samu_seq_fwd(s, p, aux, hs));
     return fused_status(
         launch_samu_fwd(s, p, ws.ptr, ws.bytes, ws.init, aux, opts ? opts->polls : 0, hs),
         ws, hs);
@@ -704,9 +721,10 @@ LRSCAN_API int scan_samu_bwd(const void* eta, const void* delta, const float* nu
         return LRSCAN_ERR_NULL;
     if (!dims_ok(B, T, M)) return LRSCAN_ERR_DIM;
     if (!dtype_ok(dtype)) return LRSCAN_ERR_DTYPE;
-    int st = samu_algo(opts);
-    if (st != LRSCAN_OK) return st;
     const Shape s{B, T, M, dtype};
+    int algo = 0;
+    int st = samu_algo(s, opts, &algo);
+    if (st != LRSCAN_OK) return st;
     SamuBwdPtrs p;
     p.eta = eta;
     p.delta = delta;
@@ -734,6 +752,7 @@ LRSCAN_API int scan_samu_bwd(const void* eta, const void* delta, const float* nu
     void* aux = nullptr;
     st = samu_workspace(s, opts, hs, &ws, &aux);
     if (st != LRSCAN_OK) return st;
+    if (algo == LRSCAN_ALGO_SEQ) return hip_status(launch_samu_seq_bwd(s, p, aux, hs));
     return fused_status(
         launch_samu_bwd(s, p, ws.ptr, ws.bytes, ws.init, aux, opts ? opts->polls : 0, hs),
         ws, hs);
@@ -741,8 +760,12 @@ LRSCAN_API int scan_samu_bwd(const void* eta, const void* delta, const float* nu
 
 LRSCAN_API size_t scan_samu_workspace_bytes(int64_t B, int64_t T, int64_t M, int dtype,
                                             const lrscan_opts* opts) {
-    if (!dims_ok(B, T, M) || !dtype_ok(dtype) || samu_algo(opts) != LRSCAN_OK) return 0;
+    if (!dims_ok(B, T, M) || !dtype_ok(dtype)) return 0;
     const Shape s{B, T, M, dtype};
+    int algo = 0;
+    if (samu_algo(s, opts, &algo) != LRSCAN_OK) return 0;
+    // the walk uses the same buffer (its tables and partial sums in the part
+    // after the fused scratch), so the need is the same for every algorithm
     return samu_supported(s) ? samu_need(s) : 0;
 }
 

@@ -134,5 +134,8 @@ hipError_t launch_samu_fwd(const Shape& s, const SamuFwdPtrs& p, void* ws, size_
                            bool init, void* aux, int polls, hipStream_t st);
 hipError_t launch_samu_bwd(const Shape& s, const SamuBwdPtrs& p, void* ws, size_t ws_bytes,
                            bool init, void* aux, int polls, hipStream_t st);
+// The per-lane walk of the same scan (no fused scratch; `aux` as above).
+hipError_t launch_samu_seq_fwd(const Shape& s, const SamuFwdPtrs& p, void* aux, hipStream_t st);
+hipError_t launch_samu_seq_bwd(const Shape& s, const SamuBwdPtrs& p, void* aux, hipStream_t st);
 
 }  // namespace lrscan

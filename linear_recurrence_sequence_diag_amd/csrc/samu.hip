@@ -728,6 +728,199 @@ void dispatch2(bool al, bool rst, F&& f) {
     else f(std::false_type{}, std::false_type{});
 }
 
+// ---------------------------------------------------------------------------
+// per-lane walk
+// ---------------------------------------------------------------------------
+// One thread per (batch row, 16-byte vector of modes) walks all T steps with
+// each transition rebuilt in registers, as the complex scan's walk does with
+// stored ones: for sequences too short for the tiles' fixed costs.  In the
+// backward a row's vectors are padded to whole wavefronts (`tpr` threads per
+// row, a multiple of 64), so that a wavefront sums each token's radial and
+// phase terms over its lanes with butterfly shuffles and writes one partial
+// per (wavefront of the row, token); each thread keeps its modes' sums over
+// the row's tokens and writes one partial per (row, mode).  The reduction
+// kernel adds the partials as for the tiles.
+constexpr int kSamuSeqBlock = 256;
+constexpr int kSamuSeqU = 4;  // rows loaded ahead
+
+template <int DT, bool ALIGNED, bool RST>
+__global__ __launch_bounds__(kSamuSeqBlock) void samu_seq_fwd_kernel(
+    SamuFwdPtrs p, const float4* __restrict__ tok_tab, const float4* __restrict__ mode_tab,
+    int64_t B, int64_t T, int64_t M, int64_t vpr) {
+    constexpr int V = Elem<DT>::V;
+    constexpr int U = kSamuSeqU;
+    const int64_t gid = (int64_t)blockIdx.x * kSamuSeqBlock + threadIdx.x;
+    const int64_t b = gid / vpr;
+    if (b >= B) return;
+    const int64_t d0 = (gid - b * vpr) * V;
+    const int nvalid = (int)((M - d0) < V ? (M - d0) : V);
+    const size_t base = (size_t)b * (size_t)T * (size_t)M + (size_t)d0;
+    SamuLane ln[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) ln[j] = samu_lane(mode_tab, d0 + j < M ? (int)(d0 + j) : (int)(M - 1));
+    Cx h[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+        h[j] = (p.h0r && j < nvalid) ? Cx{p.h0r[b * M + d0 + j], p.h0i[b * M + d0 + j]}
+                                     : Cx{0.0f, 0.0f};
+    for (int64_t t0 = 0; t0 < T; t0 += U) {
+        RowVec<DT> vr[U], vi[U];
+        SamuTok tk[U];
+        uint32_t rr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (t0 + u < T) {
+                const size_t e = base + (size_t)(t0 + u) * M;
+                vr[u] = load_row<DT, ALIGNED>(p.br, e, nvalid, 0.0f);
+                vi[u] = load_row<DT, ALIGNED>(p.bi, e, nvalid, 0.0f);
+                tk[u] = samu_tok(tok_tab, (size_t)b * T + t0 + u);
+                if (RST) rr[u] = p.reset[(size_t)b * T + t0 + u];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (t0 + u < T) {
+                RowOut<DT> orr, oii;
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    const Cx at = (RST && rr[u]) ? Cx{0.0f, 0.0f} : samu_a(ln[j], tk[u]);
+                    h[j] = cfma(at, h[j], vget(vr[u], vi[u], j));
+                    orr.v[j] = h[j].r;
+                    oii.v[j] = h[j].i;
+                }
+                if (p.out_r) {
+                    const size_t e = base + (size_t)(t0 + u) * M;
+                    store_row<DT, ALIGNED>(p.out_r, e, nvalid, orr);
+                    store_row<DT, ALIGNED>(p.out_i, e, nvalid, oii);
+                }
+            }
+        }
+    }
+    if (p.last_r) {
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+            if (j < nvalid) {
+                p.last_r[b * M + d0 + j] = h[j].r;
+                p.last_i[b * M + d0 + j] = h[j].i;
+            }
+    }
+}
+
+struct SamuSeqParts {
+    float *tok_eta, *tok_delta;   // [tpr / 64, B*T]
+    float *mode_nu, *mode_theta;  // [B, M]
+};
+
+template <int DT, bool ALIGNED, bool RST>
+__global__ __launch_bounds__(kSamuSeqBlock) void samu_seq_bwd_kernel(
+    SamuBwdPtrs p, const float4* __restrict__ tok_tab, const float4* __restrict__ mode_tab,
+    SamuSeqParts q, int64_t B, int64_t T, int64_t M, int64_t tpr) {
+    constexpr int V = Elem<DT>::V;
+    constexpr int U = kSamuSeqU;
+    const int64_t gid = (int64_t)blockIdx.x * kSamuSeqBlock + threadIdx.x;
+    const int64_t b = gid / tpr;
+    if (b >= B) return;  // whole wavefronts: tpr and the block are multiples of 64
+    const int64_t col = gid - b * tpr;
+    const int64_t d0 = col * V;
+    const int nvalid = d0 >= M ? 0 : (int)((M - d0) < V ? (M - d0) : V);
+    const int wrow = (int)(col / kWave);
+    const int lane = (int)(threadIdx.x % kWave);
+    const size_t tokens = (size_t)B * T;
+    // padding threads (past M) read the row's first vector; their terms are 0
+    const size_t base = (size_t)b * (size_t)T * (size_t)M + (size_t)(nvalid > 0 ? d0 : 0);
+    SamuLane ln[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) ln[j] = samu_lane(mode_tab, d0 + j < M ? (int)(d0 + j) : (int)(M - 1));
+    Cx carry[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+        carry[j] = (p.glr && j < nvalid) ? Cx{p.glr[b * M + d0 + j], p.gli[b * M + d0 + j]}
+                                         : Cx{0.0f, 0.0f};
+    // acc[2j], acc[2j+1]: lane j's sums over the row's tokens of e_t Re(w) and Im(w)
+    float acc[2 * V];
+#pragma unroll
+    for (int k = 0; k < 2 * V; ++k) acc[k] = 0.0f;
+    for (int64_t top = T - 1; top >= 0; top -= U) {
+        RowVec<DT> gr[U], gi[U], hr[U], hi[U];
+        SamuTok tk[U];
+        uint32_t rr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = top - u;
+            if (t >= 0) {
+                const size_t e = base + (size_t)t * M;
+                gr[u] = load_row<DT, ALIGNED>(p.gr, e, nvalid, 0.0f);
+                gi[u] = load_row<DT, ALIGNED>(p.gi, e, nvalid, 0.0f);
+                if (t >= 1) {
+                    hr[u] = load_row<DT, ALIGNED>(p.hr, e - M, nvalid, 0.0f);
+                    hi[u] = load_row<DT, ALIGNED>(p.hi, e - M, nvalid, 0.0f);
+                }
+                tk[u] = samu_tok(tok_tab, (size_t)b * T + t);
+                if (RST) rr[u] = p.reset[(size_t)b * T + t];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = top - u;
+            if (t >= 0) {
+                const bool rs = RST && rr[u];
+                RowOut<DT> obr, obi;
+                float rsum = 0.0f, psum = 0.0f;
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    const Cx at = rs ? Cx{0.0f, 0.0f} : samu_a(ln[j], tk[u]);
+                    const Cx lam = cadd(vget(gr[u], gi[u], j), carry[j]);
+                    Cx hp{0.0f, 0.0f};
+                    if (t >= 1)
+                        hp = vget(hr[u], hi[u], j);
+                    else if (p.h0r && j < nvalid)
+                        hp = Cx{p.h0r[b * M + d0 + j], p.h0i[b * M + d0 + j]};
+                    // w = conj(a) grad_a = conj(a) lambda conj(h_{t-1}): the new
+                    // carry conj(a) lambda times conj(h_{t-1})
+                    carry[j] = cmul(cconj(at), lam);
+                    const Cx w = rs ? Cx{0.0f, 0.0f} : cmul(carry[j], cconj(hp));
+                    const bool live = j < nvalid;
+                    const float wr = live ? w.r : 0.0f;
+                    const float wi = live ? w.i : 0.0f;
+                    rsum = fmaf(ln[j].nu2, wr, rsum);
+                    psum += wi;
+                    acc[2 * j] = fmaf(tk[u].e, wr, acc[2 * j]);
+                    acc[2 * j + 1] += wi;
+                    obr.v[j] = lam.r;
+                    obi.v[j] = lam.i;
+                }
+                if (nvalid > 0) {
+                    const size_t e = base + (size_t)t * M;
+                    store_row<DT, ALIGNED>(p.gbr, e, nvalid, obr);
+                    store_row<DT, ALIGNED>(p.gbi, e, nvalid, obi);
+                }
+                // the token's sums over this wavefront's lanes, in a fixed order
+#pragma unroll
+                for (int o = kWave / 2; o >= 1; o >>= 1) {
+                    rsum += __shfl_xor(rsum, o, kWave);
+                    psum += __shfl_xor(psum, o, kWave);
+                }
+                if (lane == 0) {
+                    const size_t tp = (size_t)wrow * tokens + (size_t)b * T + t;
+                    q.tok_eta[tp] = rsum * -(tk[u].e * kLn2);
+                    q.tok_delta[tp] = psum;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+        if (j < nvalid) {
+            if (p.gh0r) {
+                p.gh0r[b * M + d0 + j] = carry[j].r;
+                p.gh0i[b * M + d0 + j] = carry[j].i;
+            }
+            const size_t mp = (size_t)b * M + d0 + j;
+            q.mode_nu[mp] = acc[2 * j] * -(ln[j].nu2 * kLn2);
+            q.mode_theta[mp] = acc[2 * j + 1] * ln[j].th;  // d/dtheta_log = theta d/dtheta
+        }
+}
+
 // Tile shapes: Cfg<type, threads of 16 bytes per row, rows per thread,
 // wavefronts, look-back window>.  Long sequences: 256 rows of 128-byte rows
 // per array; measured on MI355X (bf16 B8 T2048 M2560) against 128 rows and
@@ -915,6 +1108,71 @@ hipError_t samu_bwd_t(const Shape& s, const SamuBwdPtrs& p, void* ws, size_t ws_
     return hipGetLastError();
 }
 
+template <int DT>
+hipError_t samu_seq_fwd_t(const Shape& s, const SamuFwdPtrs& p, void* auxp, hipStream_t st) {
+    char* aux = static_cast<char*>(auxp);
+    const AuxLayout a = aux_layout(s);
+    hipError_t e = samu_factors<DT>(s, p.eta, p.delta, p.nu_log, p.theta_log, aux, st);
+    if (e != hipSuccess) return e;
+    const float4* mode_tab = reinterpret_cast<const float4*>(aux + a.mode);
+    const float4* tok_tab = reinterpret_cast<const float4*>(aux + a.tok);
+    const int64_t vpr = (s.D + Elem<DT>::V - 1) / Elem<DT>::V;
+    const int64_t blocks = (s.B * vpr + kSamuSeqBlock - 1) / kSamuSeqBlock;
+    if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const void* ptrs[4] = {p.br, p.bi, p.out_r, p.out_i};
+    const bool al = rows_aligned(s, ptrs, 4);
+    dispatch2(al, p.reset != nullptr, [&](auto AL, auto RS) {
+        hipLaunchKernelGGL((samu_seq_fwd_kernel<DT, decltype(AL)::value, decltype(RS)::value>),
+                           dim3((unsigned)blocks), dim3(kSamuSeqBlock), 0, st, p, tok_tab,
+                           mode_tab, s.B, s.T, s.D, vpr);
+    });
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t samu_seq_bwd_t(const Shape& s, const SamuBwdPtrs& p, void* auxp, hipStream_t st) {
+    char* aux = static_cast<char*>(auxp);
+    const AuxLayout a = aux_layout(s);
+    hipError_t e = samu_factors<DT>(s, p.eta, p.delta, p.nu_log, p.theta_log, aux, st);
+    if (e != hipSuccess) return e;
+    const float4* mode_tab = reinterpret_cast<const float4*>(aux + a.mode);
+    const float4* tok_tab = reinterpret_cast<const float4*>(aux + a.tok);
+    const int64_t vpr = (s.D + Elem<DT>::V - 1) / Elem<DT>::V;
+    const int64_t tpr = (vpr + kWave - 1) / kWave * kWave;  // a row's threads, whole wavefronts
+    const int64_t nww = tpr / kWave;
+    // the partial sums fit where the tiles keep theirs: at most as many
+    // per-token slots (wavefronts of 64 vectors against tile rows of at most
+    // 32) and per-mode slots (B against tiles * B)
+    const Layout L = samu_layout(s);
+    if (nww > L.nW) return hipErrorInvalidValue;
+    const int64_t blocks = (s.B * tpr + kSamuSeqBlock - 1) / kSamuSeqBlock;
+    if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const size_t tokens = (size_t)s.B * s.T;
+    SamuSeqParts q;
+    q.tok_eta = reinterpret_cast<float*>(aux + a.tok_part);
+    q.tok_delta = q.tok_eta + tokens * nww;
+    q.mode_nu = reinterpret_cast<float*>(aux + a.mode_part);
+    q.mode_theta = q.mode_nu + (size_t)s.B * s.D;
+    const void* ptrs[6] = {p.hr, p.hi, p.gr, p.gi, p.gbr, p.gbi};
+    const bool al = rows_aligned(s, ptrs, 6);
+    dispatch2(al, p.reset != nullptr, [&](auto AL, auto RS) {
+        hipLaunchKernelGGL((samu_seq_bwd_kernel<DT, decltype(AL)::value, decltype(RS)::value>),
+                           dim3((unsigned)blocks), dim3(kSamuSeqBlock), 0, st, p, tok_tab,
+                           mode_tab, q, s.B, s.T, s.D, tpr);
+    });
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // grad_eta / grad_delta: a token's partials over the row's wavefronts;
+    // grad_nu_log / grad_theta_log: a mode's partials over the batch rows
+    const SumJob jt{q.tok_eta, q.tok_delta, p.grad_eta, p.grad_delta, (int64_t)tokens, nww};
+    const SumJob jm{q.mode_nu, q.mode_theta, p.grad_nu_log, p.grad_theta_log, s.D, s.B};
+    const unsigned bt = (unsigned)((tokens + kSumLanes - 1) / kSumLanes);
+    const unsigned bm = (unsigned)((s.D + kSumLanes - 1) / kSumLanes);
+    hipLaunchKernelGGL(samu_reduce_kernel, dim3(bt + bm), dim3(kSumLanes * kSumSlices), 0, st, jt,
+                       jm, bt);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool samu_supported(const Shape& s) {
@@ -990,6 +1248,16 @@ hipError_t launch_samu_bwd(const Shape& s, const SamuBwdPtrs& p, void* ws, size_
                            bool init, void* aux, int polls, hipStream_t st) {
     return s.dtype == DT_F32 ? samu_bwd_shape<DT_F32>(s, p, ws, ws_bytes, init, aux, polls, st)
                              : samu_bwd_shape<DT_BF16>(s, p, ws, ws_bytes, init, aux, polls, st);
+}
+
+hipError_t launch_samu_seq_fwd(const Shape& s, const SamuFwdPtrs& p, void* aux, hipStream_t st) {
+    return s.dtype == DT_F32 ? samu_seq_fwd_t<DT_F32>(s, p, aux, st)
+                             : samu_seq_fwd_t<DT_BF16>(s, p, aux, st);
+}
+
+hipError_t launch_samu_seq_bwd(const Shape& s, const SamuBwdPtrs& p, void* aux, hipStream_t st) {
+    return s.dtype == DT_F32 ? samu_seq_bwd_t<DT_F32>(s, p, aux, st)
+                             : samu_seq_bwd_t<DT_BF16>(s, p, aux, st);
 }
 
 }  // namespace lrscan

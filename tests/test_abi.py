@@ -120,10 +120,10 @@ def test_argument_errors_return_status_without_work():
     assert lib.scan_samu_fwd(*([fake] * 8), None, None, None, None, 2, 8, 0, lr.F32, None,
                              None) == -2
     assert lib.scan_samu_fwd(*([fake] * 8), None, None, None, None, 2, 8, 4, 3, None, None) == -3
-    for algo, code in (("seq", -7), ("chunked", -7)):
-        o = lr.make_opts(algo=algo)
-        assert lib.scan_samu_fwd(*([fake] * 8), None, None, None, None, 2, 8, 4, lr.F32, None,
-                                 ctypes.byref(o)) == code
+    # no three-launch form for the fused-transition scan (rejected before any work)
+    o = lr.make_opts(algo="chunked")
+    assert lib.scan_samu_fwd(*([fake] * 8), None, None, None, None, 2, 8, 4, lr.F32, None,
+                             ctypes.byref(o)) == -7
     o = lr.make_opts(algo="fused", chunk=64)
     assert lib.scan_samu_bwd(*([fake] * 8), None, None, None, None, None, None, None, None,
                              fake, fake, None, None, 2, 8, 4, lr.BF16, None,
@@ -134,7 +134,9 @@ def test_argument_errors_return_status_without_work():
                              None, fake, None, None, 2, 8, 4, lr.BF16, None, None) == -1
     assert lr.scan_samu_workspace_bytes(2, 1000, 64, lr.F32) > lr.scan_complex_workspace_bytes(
         2, 1000, 64, lr.F32)
-    assert lr.scan_samu_workspace_bytes(2, 1000, 64, lr.F32, lr.make_opts(algo="seq")) == 0
+    # the walk uses the same buffer as the tiles (tables and partial sums)
+    assert lr.scan_samu_workspace_bytes(2, 1000, 64, lr.F32, lr.make_opts(algo="seq")) == \
+        lr.scan_samu_workspace_bytes(2, 1000, 64, lr.F32)
     o = lr.make_opts()
     o.workspace = fake
     o.workspace_bytes = 16

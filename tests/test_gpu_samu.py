@@ -56,17 +56,18 @@ def sdev(inp):
                 gr=dev(inp.gr, dt), gi=dev(inp.gi, dt))
 
 
-def run(inp, h0=None, gl=None, mask=None, polls=0, need_grad_h0=True, workspace=None):
+def run(inp, h0=None, gl=None, mask=None, polls=0, need_grad_h0=True, workspace=None,
+        algo="auto"):
     t = sdev(inp)
     th0 = None if h0 is None else (dev_f32(h0.real), dev_f32(h0.imag))
     tgl = None if gl is None else (dev_f32(gl.real), dev_f32(gl.imag))
     tm = None if mask is None else torch.from_numpy(mask.astype(np.uint8)).cuda()
     ctl = (t["eta"], t["delta"], t["nu_log"], t["theta_log"])
     out_r, out_i, last_r, last_i = lr.samu_scan(*ctl, t["br"], t["bi"], h0=th0, polls=polls,
-                                                reset=tm, workspace=workspace)
+                                                reset=tm, workspace=workspace, algo=algo)
     ge, gd, gn, gt, gbr, gbi, gh0 = lr.samu_scan_backward(
         *ctl, out_r, out_i, t["gr"], t["gi"], grad_last=tgl, h0=th0, polls=polls, reset=tm,
-        need_grad_h0=need_grad_h0, workspace=workspace)
+        need_grad_h0=need_grad_h0, workspace=workspace, algo=algo)
     torch.cuda.synchronize()
     return dict(out_r=out_r, out_i=out_i, last_r=last_r, last_i=last_i, ge=ge, gd=gd, gn=gn,
                 gt=gt, gbr=gbr, gbi=gbi, gh0=gh0)
@@ -166,11 +167,13 @@ def check_all(tag, res, bd, rows=slice(None), check_params=True):
         check(f"{tag} grad_theta_log", host(res["gt"]), bd.gt, bd.tol_gt)
 
 
-# the last five run the short-sequence tiles: 8, 16, 32 and 64 rows of
-# 512-byte rows (rows of 300 bf16 values are not 16-byte aligned) and 128 rows
-# of 256-byte rows
+# (64, 7, 512) ... (5, 100, 200) run the short-sequence tiles: 8, 16, 32 and
+# 64 rows of 512-byte rows (rows of 300 bf16 values are not 16-byte aligned)
+# and 128 rows of 256-byte rows; (520, 6, 520) is walked by AUTO (270K lanes),
+# a row's second wavefront mostly padding
 SHAPES = [(2, 300, 72), (3, 1000, 130), (1, 4096, 256), (2, 333, 13), (1, 1, 1), (2, 129, 1),
-          (64, 7, 512), (30, 13, 300), (40, 20, 300), (9, 50, 520), (5, 100, 200)]
+          (64, 7, 512), (30, 13, 300), (40, 20, 300), (9, 50, 520), (5, 100, 200),
+          (520, 6, 520)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -184,12 +187,14 @@ def test_samu_against_oracle(B, T, M, dt):
     b, g = inp.c128("b"), inp.c128("g")
     for m in (None, mask):
         bd = Bounds(eta, delta, nu_log, theta_log, b, g, dt, h0=h0, gl=gl, mask=m)
-        res = run(inp, h0=h0, gl=gl, mask=m)
-        tag = f"{dt} B{B}T{T}M{M}{'+reset' if m is not None else ''}"
-        check_all(tag, res, bd)
-        if m is not None:
-            assert np.all(host(res["ge"])[m] == 0) and np.all(host(res["gd"])[m] == 0), tag
-    log(f"samu {dt} B{B} T{T} M{M}: within the derived bounds, with and without resets")
+        for algo in ("fused", "seq", "auto"):
+            res = run(inp, h0=h0, gl=gl, mask=m, algo=algo)
+            tag = f"{dt} B{B}T{T}M{M}{'+reset' if m is not None else ''} {algo}"
+            check_all(tag, res, bd)
+            if m is not None:
+                assert np.all(host(res["ge"])[m] == 0) and np.all(host(res["gd"])[m] == 0), tag
+    log(f"samu {dt} B{B} T{T} M{M}: tiles, walk and AUTO within the derived bounds, with and "
+        f"without resets")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
