@@ -177,7 +177,9 @@ def test_workspace_sizes_and_auto_choice():
             # for longer sequences; shorter ones, and more blocks: fused
             one = 64 if dt == lr.BF16 else 32
             algo, chunk, _ = lr.scan_auto_algo(1, 1 << 20, one, dt, direction)
-            assert algo == lr.ALGO_CHUNKED and chunk == 256
+            assert algo == lr.ALGO_CHUNKED and chunk == (256 if direction == 0 else 128)
+            algo, chunk, _ = lr.scan_auto_algo(1, 1 << 22, one, dt, direction)
+            assert algo == lr.ALGO_CHUNKED and chunk == (1024 if direction == 0 else 512)
             algo, chunk, _ = lr.scan_auto_algo(1, 1 << 23, one, dt, direction)
             assert algo == lr.ALGO_CHUNKED and chunk == 1024
             algo, _, _ = lr.scan_auto_algo(1, (1 << 20) - 1, one, dt, direction)
