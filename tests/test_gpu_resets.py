@@ -40,7 +40,9 @@ def oracle_ref(inp, h0, gl, mask):
     return h, hl, oga, ogb, ogh0
 
 
-SHAPES = [(2, 1000, 72), (3, 777, 130), (1, 4096, 256), (4, 300, 4096)]
+# (2, 10317, 64): two chains of 41 tiles, so the backward's window of 16
+# predecessors is crossed twice under resets
+SHAPES = [(2, 1000, 72), (3, 777, 130), (1, 4096, 256), (4, 300, 4096), (2, 10317, 64)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -81,8 +83,8 @@ def test_reset_mask_every_algorithm(B, T, D, dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_reset_derivation_is_bitwise_identical(dt):
-    B, T, D = 2, 4096, 256
+@pytest.mark.parametrize("B,T,D", [(2, 4096, 256), (1, 10317, 64)], ids=["B2T4096D256", "B1T10317D64"])
+def test_reset_derivation_is_bitwise_identical(B, T, D, dt):
     inp, h0, gl = W.random_inputs(B, T, D, dt, seed=12, a_lo=0.9, with_state=True)
     mask = reset_mask(B, T, 13, p=0.01)
     a, b, g = dev(inp.a, dt), dev(inp.b, dt), dev(inp.g, dt)
