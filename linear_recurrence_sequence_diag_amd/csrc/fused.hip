@@ -654,11 +654,12 @@ bool fused_cfg_supported(const Shape& s, int dir, int width, int tile, bool alig
 // 1024]: 152.4 -> 147.7 us), else 256 rows.
 //
 // Backward: 32 rows of 512-byte blocks for T <= 32, 64 rows for T <= 64, 128
-// rows of 128-byte blocks for T <= 128, 128 rows of 256-byte blocks for long
-// bf16 sequences (T >= 1024) with at least 128 such blocks ([16,4096,2560]:
-// 277.7 against 283.0 us for 256 rows of 128-byte blocks, [8,2048,2560]
-// even), else 256 rows of 128-byte blocks (T of 256..512 over many lane
-// blocks: 5.8 against 5.2 TB/s).
+// rows of 128-byte blocks for T <= 128, else 256 rows of 128-byte blocks (T
+// of 256..512 over many lane blocks: 5.8 against 5.2 TB/s).  128 rows of
+// 256-byte blocks are within 3% of it either way on [8,2048,2560] and
+// [16,4096,2560] bf16 (which one leads changes from one GPU to another), but
+// 20% slower on [16,2048,4096] and 5-8% on [8,2048,8192], [32,2048,2048]
+// and [64,1024,1024] (13% faster only on [16,4096,2048]).
 //
 // A lane block wider than the row (D smaller than the block) would leave
 // lanes idle, so the widths fall back to narrower rows.
@@ -693,12 +694,6 @@ void fused_default_cfg(const Shape& s, int dir, bool aligned, int* width, int* t
         *tile = 64;
     } else if (s.T <= 128) {
         *tile = 128;
-    } else if (s.dtype == DT_BF16 && s.T >= 1024 && fits(16)) {
-        const int64_t lanes16 = 16 * Elem<DT_BF16>::V;
-        if (s.B * ((s.D + lanes16 - 1) / lanes16) >= 128) {
-            *width = 16;
-            *tile = 128;
-        }
     }
 }
 

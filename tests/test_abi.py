@@ -188,9 +188,10 @@ def test_workspace_sizes_and_auto_choice():
             assert algo == (lr.ALGO_FUSED if direction == 0 else lr.ALGO_CHUNKED)
             algo, _, _ = lr.scan_auto_algo(1, 1 << 23, 4 * one, dt, direction)
             assert algo == lr.ALGO_FUSED
-            # long sequences, and short ones over too few lanes for the walk: the fused form
-            algo, _, _ = lr.scan_auto_algo(8, 2048, 2560, dt, direction)
-            assert algo == lr.ALGO_FUSED
+            # long sequences, and short ones over too few lanes for the walk: the
+            # fused form, 256 rows of 128-byte lane blocks
+            algo, tile, width = lr.scan_auto_algo(8, 2048, 2560, dt, direction)
+            assert (algo, tile, width) == (lr.ALGO_FUSED, 256, 8)
             algo, _, _ = lr.scan_auto_algo(4, 16, 1024, dt, direction)
             assert algo == lr.ALGO_FUSED
             # rows that are not 16-byte aligned: the walk up to 64 steps from
