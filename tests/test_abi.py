@@ -66,6 +66,11 @@ def test_argument_errors_return_status_without_work():
     fake = 0x10000  # never dereferenced: validation fails first
     assert lib.scan_fwd(None, fake, fake, None, 2, 8, 4, lr.F32, None) == -1
     assert lib.scan_fwd(fake, fake, fake, None, 0, 8, 4, lr.F32, None) == -2
+    # empty inputs in any dimension are argument errors
+    assert lib.scan_fwd(fake, fake, fake, None, 2, 0, 4, lr.F32, None) == -2
+    assert lib.scan_fwd(fake, fake, fake, None, 2, 8, 0, lr.BF16, None) == -2
+    assert lib.scan_bwd(fake, fake, fake, None, fake, fake, 2, 0, 4, lr.F32, None) == -2
+    assert lib.scan_bwd(fake, fake, fake, None, fake, fake, 0, 8, 4, lr.BF16, None) == -2
     assert lib.scan_fwd(fake, fake, fake, None, 2, -1, 4, lr.F32, None) == -2
     assert lib.scan_fwd(fake, fake, fake, None, 2, 8, 4, 7, None) == -3
     assert lib.scan_bwd(fake, fake, None, None, fake, fake, 2, 8, 4, lr.F32, None) == -1
