@@ -269,8 +269,8 @@ void cx_fused_fwd_kernel(CxFwdArgs x) {
             }
             if constexpr (OUT) {
                 const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
-                store_vec<C::DT, ALIGNED, C::TPR>(por, off, g.nvalid, orr, cg, d.D - g.d0);
-                store_vec<C::DT, ALIGNED, C::TPR>(poi, off, g.nvalid, oii, cg, d.D - g.d0);
+                store_vec<C::DT, ALIGNED>(por, off, g.nvalid, orr);
+                store_vec<C::DT, ALIGNED>(poi, off, g.nvalid, oii);
             }
         }
     }
@@ -458,10 +458,10 @@ void cx_fused_bwd_kernel(CxBwdArgs x) {
                 carry[j] = cmul(cconj(vget(ar[i], ai[i], j)), lam);
             }
             const uint32_t off = row_off(g, row, d.T, rowbytes);
-            store_vec<C::DT, ALIGNED, C::TPR>(pgar, off, g.nvalid, oar, cg, d.D - g.d0);
-            store_vec<C::DT, ALIGNED, C::TPR>(pgai, off, g.nvalid, oai, cg, d.D - g.d0);
-            store_vec<C::DT, ALIGNED, C::TPR>(pgbr, off, g.nvalid, obr, cg, d.D - g.d0);
-            store_vec<C::DT, ALIGNED, C::TPR>(pgbi, off, g.nvalid, obi, cg, d.D - g.d0);
+            store_vec<C::DT, ALIGNED>(pgar, off, g.nvalid, oar);
+            store_vec<C::DT, ALIGNED>(pgai, off, g.nvalid, oai);
+            store_vec<C::DT, ALIGNED>(pgbr, off, g.nvalid, obr);
+            store_vec<C::DT, ALIGNED>(pgbi, off, g.nvalid, obi);
         }
     }
     if (x.p.gh0r && g.nrows > 0 && g.row0 == 0) {

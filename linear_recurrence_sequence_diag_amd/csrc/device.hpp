@@ -112,7 +112,6 @@ struct RowVec {
 // write-back.  (Measured on MI355X: the backward on [8,2048,2560] bf16 went
 // from 94 to 78 us; every other form gained 0-14%.)
 typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void store16_nt(void* p, uint4 v) {
     const u32x4_nt w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4_nt*>(p));
@@ -160,15 +159,34 @@ __device__ __forceinline__ uint4 bytes16_at(uint4 lo, uint4 hi, uint32_t sh) {
                       __builtin_amdgcn_alignbyte(e[4], e[3], r));
 }
 
-// Load a vector at an address that need not be 16-byte aligned: the aligned
-// block holding its first byte and, when lanes of the vector lie in it, the
-// next block (each block read holds bytes of the vector, so no read reaches
-// past memory the vector lies in; otherwise the first block is read twice),
-// then shifted into place.  Lanes from `nvalid` on are `fill`.  No branches:
-// the same code serves complete vectors and a row's last, partial one.
+// 16 bytes at an address aligned only to the element size.  The compiler
+// emits one 16-byte global access for it (gfx950 code objects for the HSA
+// runtime run with unaligned accesses enabled); the hardware splits it at the
+// cache-line boundaries.  It touches exactly those 16 bytes.  Measured on
+// MI355X against per-block accesses with the neighbouring lanes' blocks
+// shared (bf16 [8,2048,2559], forward / backward): 2117 / 1889 -> 2857 / 3016
+// GB/s, the same bits out.
+__device__ __forceinline__ uint4 load16_any(const void* p) {
+    uint4 v;
+    __builtin_memcpy(&v, p, 16);
+    return v;
+}
+__device__ __forceinline__ void store16_any(void* p, uint4 v) { __builtin_memcpy(p, &v, 16); }
+
+// Load a vector at an address that need not be 16-byte aligned.  A complete
+// vector is one 16-byte access.  A row's last, partial vector reads the
+// aligned block holding its first byte and, when lanes of the vector lie in
+// it, the next block (each block read holds bytes of the vector, so no read
+// reaches past memory the vector lies in; otherwise the first block is read
+// twice), then shifted into place.  Lanes from `nvalid` on are `fill`.
 template <int DT>
 __device__ __forceinline__ RowVec<DT> load_vec_unaligned(const char* p, int nvalid, float fill) {
     constexpr int S = Elem<DT>::bytes;
+    if (nvalid == Elem<DT>::V) {
+        RowVec<DT> r;
+        r.w = load16_any(p);
+        return r;
+    }
     const uintptr_t ua = reinterpret_cast<uintptr_t>(p);
     const uint32_t sh = (uint32_t)(ua & 15u);
     const uint4* blk = reinterpret_cast<const uint4*>(ua - sh);
@@ -195,11 +213,11 @@ __device__ __forceinline__ RowVec<DT> load_vec_unaligned(const char* p, int nval
 
 // Load V lanes starting at element offset `off` (lane d0 of a row), for the
 // per-lane walk and the three-launch form.  ALIGNED: the whole vector is in
-// range and 16-byte aligned.  Otherwise `nvalid` (0..V) lanes are read one
-// by one and the rest are `fill`: these kernels keep many rows of loads in
-// flight per thread, and the two-block reads of load_vec_unaligned would
-// double the registers that takes (measured: the walk's backward at 256
-// VGPRs and one wave per SIMD, 0.3x as fast over few lanes).
+// range and 16-byte aligned.  Otherwise a complete vector is one 16-byte
+// access at its own address, and a partial one (`nvalid` < V lanes) is read
+// lane by lane, the rest `fill` (these kernels keep many rows of loads in
+// flight per thread, and the two-block reads of a partial vector would
+// double the registers that takes).
 template <int DT, bool ALIGNED>
 __device__ __forceinline__ RowVec<DT> load_row(const void* base, size_t off, int nvalid, float fill) {
     if constexpr (ALIGNED) {
@@ -207,6 +225,11 @@ __device__ __forceinline__ RowVec<DT> load_row(const void* base, size_t off, int
         r.w = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + off * Elem<DT>::bytes);
         return r;
     } else {
+        if (nvalid == RowVec<DT>::V) {
+            RowVec<DT> r;
+            r.w = load16_any(reinterpret_cast<const char*>(base) + off * Elem<DT>::bytes);
+            return r;
+        }
         RowVec<DT> r = RowVec<DT>::splat(fill);
         uint32_t ws[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
         const typename Elem<DT>::raw* p = reinterpret_cast<const typename Elem<DT>::raw*>(base) + off;
@@ -231,6 +254,8 @@ template <int DT, bool ALIGNED>
 __device__ __forceinline__ void store_row(void* base, size_t off, int nvalid, const RowOut<DT>& o) {
     if constexpr (ALIGNED) {
         store16_nt(reinterpret_cast<char*>(base) + off * Elem<DT>::bytes, o.pack());
+    } else if (nvalid == RowOut<DT>::V) {
+        store16_any(reinterpret_cast<char*>(base) + off * Elem<DT>::bytes, o.pack());
     } else {
 #pragma unroll
         for (int j = 0; j < RowOut<DT>::V; ++j)
@@ -238,111 +263,21 @@ __device__ __forceinline__ void store_row(void* base, size_t off, int nvalid, co
     }
 }
 
-// Unaligned outputs are stored through the caches (write-back), not
-// non-temporally: a 128-byte line there is written partly by each of two
-// neighbouring tiles, and the caches merge the two parts before the line
-// reaches memory (measured on MI355X, bf16 [8,2048,2559]: forward / backward
-// 1443 / 1199 -> 2107 / 1878 GB/s).
-__device__ __forceinline__ void store16_wb(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
-
-// Dword q (0..3) of r, q not known at compile time.
-__device__ __forceinline__ uint32_t dword_of(uint4 r, uint32_t q) {
-    return q == 0 ? r.x : q == 1 ? r.y : q == 2 ? r.z : r.w;
-}
-
-// Store bytes [o0, o1) of a 16-byte block image `img` at the aligned block
-// `blk`, as at most three naturally aligned pieces; o0 and o1 are even, and
-// either o0 == 0 or o1 == 16.
-__device__ __forceinline__ void store_block_part(char* blk, uint4 img, uint32_t o0, uint32_t o1) {
-    if (o1 == 16) {  // a head: pieces of 2, 4, then 8 bytes up to the block's end
-        uint32_t o = o0;
-        if (o & 2u) {
-            *reinterpret_cast<uint16_t*>(blk + o) = (uint16_t)(dword_of(img, o >> 2) >> 16);
-            o += 2;
-        }
-        if (o & 4u) {
-            *reinterpret_cast<uint32_t*>(blk + o) = dword_of(img, o >> 2);
-            o += 4;
-        }
-        if (o & 8u) {
-            const u32x2_t v = {img.z, img.w};
-            *reinterpret_cast<u32x2_t*>(blk + 8) = v;
-        }
-    } else {  // a tail: pieces of 8, 4, then 2 bytes from the block's start
-        uint32_t o = 0;
-        if (o1 & 8u) {
-            const u32x2_t v = {img.x, img.y};
-            *reinterpret_cast<u32x2_t*>(blk) = v;
-            o = 8;
-        }
-        if (o1 & 4u) {
-            *reinterpret_cast<uint32_t*>(blk + o) = dword_of(img, o >> 2);
-            o += 4;
-        }
-        if (o1 & 2u)
-            *reinterpret_cast<uint16_t*>(blk + o) = (uint16_t)dword_of(img, o >> 2);
-    }
-}
-
-// Store a vector at an address that need not be 16-byte aligned.  Threads
-// in consecutive lanes that hold consecutive vectors of one row share the
-// aligned blocks between them: a block holds the tail of one thread's
-// vector and the head of the next one's, and the later thread writes the
-// whole block (the earlier one's tail through a lane shuffle) when both parts
-// are there.  `prev_adj` / `next_adj`: the thread in the previous / next lane
-// holds the previous / next vector of this row and stores it in this same
-// call.  A part of a block shared with any other writer is written in at most
-// three naturally aligned pieces (element by element for a vector that
-// reaches past the row's end).  `rem` is the number of lanes from this
-// thread's first to the end of the row (nvalid = min(rem, V)).
+// Store a vector at an address that need not be 16-byte aligned: a complete
+// vector is one 16-byte store at its own address, through the caches (a
+// 128-byte line of such a row is written partly by each of two neighbouring
+// tiles, and the caches merge the parts before the line reaches memory); a
+// row's last, partial vector is written lane by lane.  Each thread writes
+// exactly its own lanes.
 template <int DT>
-__device__ __forceinline__ void store_vec_unaligned(char* p, int nvalid, const RowOut<DT>& o,
-                                                    bool prev_adj, bool next_adj, int rem) {
-    constexpr int V = Elem<DT>::V, S = Elem<DT>::bytes;
-    const uint4 w = o.pack();
-    // the previous lane's packed vector (used only when prev_adj)
-    const uint4 wp = make_uint4(__shfl_up(w.x, 1, kWave), __shfl_up(w.y, 1, kWave),
-                                __shfl_up(w.z, 1, kWave), __shfl_up(w.w, 1, kWave));
-    if (nvalid <= 0) return;
-    const uintptr_t ua = reinterpret_cast<uintptr_t>(p);
-    const uint32_t sh = (uint32_t)(ua & 15u);
-    if (sh == 0 && nvalid == V) {
-        store16_wb(p, w);
+__device__ __forceinline__ void store_vec_unaligned(char* p, int nvalid, const RowOut<DT>& o) {
+    if (nvalid == Elem<DT>::V) {
+        store16_any(p, o.pack());
         return;
     }
-    const int k = (int)(16u - sh) / S;  // this vector's elements in its first block
-    const int nv_next = rem - V < 0 ? 0 : (rem - V > V ? V : rem - V);
-    // the block holding this vector's head is written whole by this thread
-    // when the previous lane's vector is adjacent (then it is complete, as
-    // this one has lanes) and this vector's head is complete; this vector's
-    // tail goes with the next lane's block when that thread writes it
-    const bool mine = sh != 0 && prev_adj && nvalid >= k;
-    const bool next_takes = sh != 0 && next_adj && nvalid == V && nv_next >= k;
-    char* blk = reinterpret_cast<char*>(ua - sh);
-    if (nvalid == V) {
-        if (mine) store16_wb(blk, bytes16_at(wp, w, 16u - sh));
-        // w rotated so that its bytes sit at their offsets in the two blocks:
-        // the head at sh .. 15 of the first, the tail at 0 .. sh - 1 of the second
-        const uint4 rot = bytes16_at(w, w, 16u - sh);
-        if (!mine) store_block_part(blk, rot, sh, 16);
-        if (!next_takes) store_block_part(blk + 16, rot, 0, sh);
-        return;
-    }
-    const uint32_t words[4] = {w.x, w.y, w.z, w.w};
-    const int h1 = mine ? 0 : (nvalid < k ? nvalid : k);  // head elements stored one by one
-    const int t0 = next_takes ? nvalid : k;                // tail elements from t0 on
-    if (mine) store16_wb(blk, bytes16_at(wp, w, 16u - sh));
 #pragma unroll
-    for (int j = 0; j < V; ++j) {
-        if (j < nvalid && (j < h1 || j >= t0)) {
-            if constexpr (DT == DT_F32) {
-                reinterpret_cast<uint32_t*>(p)[j] = words[j];
-            } else {
-                const uint16_t h = (uint16_t)(words[j >> 1] >> ((j & 1) * 16));
-                reinterpret_cast<uint16_t*>(p)[j] = h;
-            }
-        }
-    }
+    for (int j = 0; j < Elem<DT>::V; ++j)
+        if (j < nvalid) Elem<DT>::store1(p, j, o.v[j]);
 }
 
 // Row vectors addressed as (wave-uniform row pointer) + (per-lane byte offset),
@@ -377,19 +312,14 @@ __device__ __forceinline__ RowVec<DT> load_vec(const char* row, uint32_t lane_of
     }
 }
 
-// The store of one thread's vector of a tile row: `cg` is the thread's place
-// in its row group of TPR threads, `rem` the lanes from its first to the end
-// of the row (used when rows are not aligned).
-template <int DT, bool ALIGNED, int TPR>
+// The store of one thread's vector of a tile row (`nvalid` lanes of it exist).
+template <int DT, bool ALIGNED>
 __device__ __forceinline__ void store_vec(char* row, uint32_t lane_off, int nvalid,
-                                          const RowOut<DT>& o, int cg, int rem) {
-    if constexpr (ALIGNED) {
+                                          const RowOut<DT>& o) {
+    if constexpr (ALIGNED)
         store16_nt(row + lane_off, o.pack());
-    } else {
-        // the TPR threads of a row group (consecutive lanes, cg = 0 .. TPR - 1)
-        // hold consecutive vectors of one tile row
-        store_vec_unaligned<DT>(row + lane_off, nvalid, o, cg > 0, cg + 1 < TPR, rem);
-    }
+    else
+        store_vec_unaligned<DT>(row + lane_off, nvalid, o);
 }
 
 // Make the compiler forget what it knows about a register-resident row, so it

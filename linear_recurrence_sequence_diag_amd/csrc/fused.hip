@@ -338,7 +338,7 @@ void fused_fwd_kernel(FwdArgs x) {
                 o.v[j] = h[j];
             }
             if constexpr (OUT)
-                store_vec<C::DT, ALIGNED, C::TPR>(po, row_off(g, g.row0 + i, d.T, rowbytes), g.nvalid, o, cg, d.D - g.d0);
+                store_vec<C::DT, ALIGNED>(po, row_off(g, g.row0 + i, d.T, rowbytes), g.nvalid, o);
         }
     }
     if (x.last && ends) {
@@ -518,8 +518,8 @@ void fused_bwd_kernel(BwdArgs x) {
                 oa.v[j] = lam[j] * hp;
             }
             const uint32_t off = row_off(g, row, d.T, rowbytes);
-            store_vec<C::DT, ALIGNED, C::TPR>(pga, off, g.nvalid, oa, cg, d.D - g.d0);
-            store_vec<C::DT, ALIGNED, C::TPR>(pgb, off, g.nvalid, ob, cg, d.D - g.d0);
+            store_vec<C::DT, ALIGNED>(pga, off, g.nvalid, oa);
+            store_vec<C::DT, ALIGNED>(pgb, off, g.nvalid, ob);
         }
     }
     if (x.grad_h0 && g.nrows > 0 && g.row0 == 0) {

@@ -327,8 +327,8 @@ __device__ __forceinline__ void samu_fwd_tile(const SamuFwdArgs& x, const Ticket
             }
             if constexpr (OUT) {
                 const uint32_t off = row_off(g, g.row0 + i, d.T, rowbytes);
-                store_vec<C::DT, ALIGNED, C::TPR>(por, off, g.nvalid, orr, cg, d.D - g.d0);
-                store_vec<C::DT, ALIGNED, C::TPR>(poi, off, g.nvalid, oii, cg, d.D - g.d0);
+                store_vec<C::DT, ALIGNED>(por, off, g.nvalid, orr);
+                store_vec<C::DT, ALIGNED>(poi, off, g.nvalid, oii);
             }
         }
     }
@@ -587,8 +587,8 @@ __device__ __forceinline__ void samu_bwd_tile(const SamuBwdArgs& x, const Ticket
             }
             if (g.nvalid > 0) {
                 const uint32_t off = row_off(g, row, d.T, rowbytes);
-                store_vec<C::DT, ALIGNED, C::TPR>(pgbr, off, g.nvalid, obr, cg, d.D - g.d0);
-                store_vec<C::DT, ALIGNED, C::TPR>(pgbi, off, g.nvalid, obi, cg, d.D - g.d0);
+                store_vec<C::DT, ALIGNED>(pgbr, off, g.nvalid, obr);
+                store_vec<C::DT, ALIGNED>(pgbi, off, g.nvalid, obi);
             }
             tsum_[2 * i] = rsum * -(tok[i].e * kLn2);
             tsum_[2 * i + 1] = psum;

@@ -19,38 +19,6 @@ constexpr int kSeqU = 8;  // rows in flight per buffer
 
 // RST: `reset` ([B, T] bytes) marks segment starts, where the step's
 // transition is taken as 0 (the entering state is dropped).
-// A walk's store of its vector of one row.  Rows that are not 16-byte
-// aligned share aligned blocks between neighbouring lanes, which hold
-// neighbouring vectors of a row unless a row starts between them (or a
-// wavefront does); over many lanes the walk writes those blocks whole
-// (store_vec_unaligned), over few lanes, where each thread's latency bounds
-// the walk, element by element (measured on MI355X, bf16 D = 2559: [4096, 8]
-// 0.91 / 0.77 -> 1.6 / 1.4 TB/s with shared blocks, while [8, 2048] fell
-// from 50 to 34 GB/s).
-struct WalkNbrs {
-    bool prev, next, share;
-    int rem;  // lanes from this thread's first to the end of its row
-};
-__device__ __forceinline__ WalkNbrs walk_nbrs(int64_t vidx, int64_t vpr, int64_t rem,
-                                              int64_t lanes) {
-    const int lane = (int)(threadIdx.x % kWave);
-    return WalkNbrs{lane > 0 && vidx > 0, lane + 1 < kWave && vidx + 1 < vpr,
-                    lanes >= ((int64_t)1 << 18), (int)(rem < 64 ? rem : 64)};
-}
-template <int DT, bool ALIGNED>
-__device__ __forceinline__ void walk_store(void* base, size_t off, int nvalid, const RowOut<DT>& o,
-                                           const WalkNbrs& nb) {
-    if constexpr (ALIGNED) {
-        store_row<DT, true>(base, off, nvalid, o);
-    } else {
-        if (nb.share)
-            store_vec_unaligned<DT>(reinterpret_cast<char*>(base) + off * Elem<DT>::bytes, nvalid,
-                                    o, nb.prev, nb.next, nb.rem);
-        else
-            store_row<DT, false>(base, off, nvalid, o);
-    }
-}
-
 template <int DT, bool ALIGNED, bool RST>
 __global__ __launch_bounds__(kSeqBlock) void seq_fwd_kernel(const void* __restrict__ a,
                                                             const void* __restrict__ b,
@@ -67,7 +35,6 @@ __global__ __launch_bounds__(kSeqBlock) void seq_fwd_kernel(const void* __restri
     if (bi >= B) return;
     const int64_t d0 = (gid - bi * vpr) * V;
     const int nvalid = (int)((D - d0) < V ? (D - d0) : V);
-    const WalkNbrs nbrs = walk_nbrs(gid - bi * vpr, vpr, D - d0, B * D);
     const size_t base = (size_t)bi * (size_t)T * (size_t)D + (size_t)d0;
 
     float h[V];
@@ -105,7 +72,7 @@ __global__ __launch_bounds__(kSeqBlock) void seq_fwd_kernel(const void* __restri
                     h[j] = fmaf(at, h[j], cb[u].get(j));
                     o.v[j] = h[j];
                 }
-                if (out) walk_store<DT, ALIGNED>(out, base + (size_t)(t0 + u) * D, nvalid, o, nbrs);
+                if (out) store_row<DT, ALIGNED>(out, base + (size_t)(t0 + u) * D, nvalid, o);
             }
         }
 #pragma unroll
@@ -137,7 +104,6 @@ __global__ __launch_bounds__(kSeqBlock) void seq_bwd_kernel(
     if (bi >= B) return;
     const int64_t d0 = (gid - bi * vpr) * V;
     const int nvalid = (int)((D - d0) < V ? (D - d0) : V);
-    const WalkNbrs nbrs = walk_nbrs(gid - bi * vpr, vpr, D - d0, B * D);
     const size_t base = (size_t)bi * (size_t)T * (size_t)D + (size_t)d0;
 
     float carry[V], hinit[V];
@@ -187,8 +153,8 @@ __global__ __launch_bounds__(kSeqBlock) void seq_bwd_kernel(
                     const float at = rs ? 0.0f : ca[u].get(j);
                     carry[j] = (u == U - 1 || t == 0) ? at * lam : lam;
                 }
-                walk_store<DT, ALIGNED>(grad_a, base + (size_t)t * D, nvalid, oa, nbrs);
-                walk_store<DT, ALIGNED>(grad_b, base + (size_t)t * D, nvalid, ob, nbrs);
+                store_row<DT, ALIGNED>(grad_a, base + (size_t)t * D, nvalid, oa);
+                store_row<DT, ALIGNED>(grad_b, base + (size_t)t * D, nvalid, ob);
             }
         }
 #pragma unroll
