@@ -4,8 +4,8 @@
 //    rounded to nearest even on store (bf16 via the gfx950 packed convert);
 //  * 16-byte row vectors: one thread owns V = 16 / sizeof(elem) adjacent lanes
 //    of a [B, T, D] row (4 fp32 or 8 bf16), loaded and stored with one
-//    dwordx4 access when the row is 16-byte aligned, element by element
-//    otherwise;
+//    dwordx4 access (at an address aligned only to the element size when the
+//    row is not 16-byte aligned; a row's last, partial vector lane by lane);
 //  * the affine map h -> p*h + q that summarises a run of steps, and its
 //    composition "later after earlier" (associative, not commutative; page
 //    "triton_training_scan.py", the affine prefix kernels that compose the
@@ -135,10 +135,10 @@ struct RowOut {
 
 // ---- rows that are not 16-byte aligned -------------------------------------
 // A thread's 16 bytes [p, p + 16) then straddle two aligned blocks, sh = p mod
-// 16 bytes (a multiple of the element size) into the first.  Reading them as
-// one or two aligned 16-byte loads and shifting keeps the access pattern of
-// aligned rows (element-wise accesses, eight 2-byte loads per bf16 vector,
-// ran the scan about ten times slower).
+// 16 bytes (a multiple of the element size) into the first.  A row's last,
+// partial vector is read as one or two aligned 16-byte loads and shifted, so
+// that no read leaves the bytes of the row (element-wise accesses, eight
+// 2-byte loads per bf16 vector, ran the scan about ten times slower).
 
 // d[k + q] for q = 0..3, with no indexing of registers by a variable.
 __device__ __forceinline__ uint32_t dword_at(const uint32_t (&d)[8], uint32_t q, int k) {

@@ -579,7 +579,8 @@ void launch_bwd_cfg(const BwdArgs& x, hipStream_t st) {
 }
 
 // Unaligned rows (D * elem_bytes not a multiple of 16, or unaligned pointers)
-// use element-wise accesses and only the narrowest configuration.
+// use 16-byte accesses at element-aligned addresses and only the narrowest
+// configuration.
 template <int DT>
 bool fwd_dispatch(const TileCfg& c, bool al, const FwdArgs& x, hipStream_t st) {
     if (!al) {
