@@ -579,13 +579,15 @@ void launch_bwd_cfg(const BwdArgs& x, hipStream_t st) {
 }
 
 // Unaligned rows (D * elem_bytes not a multiple of 16, or unaligned pointers)
-// use 16-byte accesses at element-aligned addresses and only the narrowest
-// configuration.
+// use 16-byte accesses at element-aligned addresses, in the shapes
+// unaligned_cfg accepts.
 template <int DT>
 bool fwd_dispatch(const TileCfg& c, bool al, const FwdArgs& x, hipStream_t st) {
     if (!al) {
-        if (c.width != 8 || c.tile != 256) return false;
-        launch_fwd_cfg<DT, 8, 8, 4, 8, false>(x, st);
+        if (c.width == 8 && c.tile == 256) launch_fwd_cfg<DT, 8, 8, 4, 8, false>(x, st);
+        else if (c.width == 16 && c.tile == 128) launch_fwd_cfg<DT, 16, 8, 4, 4, false>(x, st);
+        else if (c.width == 32 && c.tile == 64) launch_fwd_cfg<DT, 32, 8, 4, 4, false>(x, st);
+        else return false;
         return true;
     }
     if (c.width == 8 && c.tile == 256) launch_fwd_cfg<DT, 8, 8, 4, 8, true>(x, st);
@@ -602,8 +604,11 @@ bool fwd_dispatch(const TileCfg& c, bool al, const FwdArgs& x, hipStream_t st) {
 template <int DT>
 bool bwd_dispatch(const TileCfg& c, bool al, const BwdArgs& x, hipStream_t st) {
     if (!al) {
-        if (c.width != 8 || c.tile != 256) return false;
-        launch_bwd_cfg<DT, 8, 8, 4, 8, false>(x, st);
+        if (c.width == 8 && c.tile == 256) launch_bwd_cfg<DT, 8, 8, 4, 8, false>(x, st);
+        else if (c.width == 8 && c.tile == 128) launch_bwd_cfg<DT, 8, 4, 4, 8, false>(x, st);
+        else if (c.width == 16 && c.tile == 128) launch_bwd_cfg<DT, 16, 8, 4, 4, false>(x, st);
+        else if (c.width == 32 && c.tile == 64) launch_bwd_cfg<DT, 32, 8, 4, 4, false>(x, st);
+        else return false;
         return true;
     }
     // At most eight chains: a look-back window of 16 tiles.  The backward
@@ -620,11 +625,18 @@ bool bwd_dispatch(const TileCfg& c, bool al, const BwdArgs& x, hipStream_t st) {
     return true;
 }
 
+// Tile shapes for rows that are not 16-byte aligned: 128-byte rows x 256 (x
+// 128 backward), 256-byte rows x 128 and 512-byte rows x 64.
+bool unaligned_cfg(int dir, int width, int tile) {
+    return (width == 8 && tile == 256) || (width == 16 && tile == 128) ||
+           (width == 32 && tile == 64) || (dir == 1 && width == 8 && tile == 128);
+}
+
 }  // namespace
 
 bool fused_cfg_supported(const Shape& s, int dir, int width, int tile, bool aligned) {
     if (!find_cfg(dir, width, tile)) return false;
-    if (!aligned && (width != 8 || tile != 256)) return false;
+    if (!aligned && !unaligned_cfg(dir, width, tile)) return false;
     // 32-bit row offsets inside a tile, 32-bit lane and row indices, 32-bit tickets
     const int64_t eb = s.dtype == DT_F32 ? 4 : 2;
     if ((int64_t)(tile + 1) * s.D * eb >= ((int64_t)1 << 31)) return false;
@@ -662,14 +674,26 @@ bool fused_cfg_supported(const Shape& s, int dir, int width, int tile, bool alig
 // 20% slower on [16,2048,4096] and 5-8% on [8,2048,8192], [32,2048,2048]
 // and [64,1024,1024] (13% faster only on [16,4096,2048]).
 //
+// Rows that are not 16-byte aligned: 128 rows of 256-byte blocks when there
+// are at least 128 chains of them (fewer shared 128-byte lines between tiles:
+// bf16 [8,2048,2559] 2.8 / 2.9 -> 3.2 / 3.4 TB/s forward / backward, fp32
+// [2,4096,4097] 3.1 / 3.2 -> 3.4 / 4.0), else 256 rows of 128-byte blocks
+// (few chains: [1,131072,1023] bf16 3.1 / 3.1 against 2.2 / 3.0).
+//
 // A lane block wider than the row (D smaller than the block) would leave
 // lanes idle, so the widths fall back to narrower rows.
 void fused_default_cfg(const Shape& s, int dir, bool aligned, int* width, int* tile) {
     *width = 8;
     *tile = 256;
-    if (!aligned) return;
     const int64_t row_bytes = s.D * (s.dtype == DT_F32 ? 4 : 2);
     const auto fits = [&](int w) { return row_bytes >= (int64_t)w * 16; };
+    if (!aligned) {
+        if (fits(16) && s.B * ((row_bytes + 255) / 256) >= 128) {
+            *width = 16;
+            *tile = 128;
+        }
+        return;
+    }
     if (dir == 0) {
         if (s.T <= 32 && fits(32)) {
             *width = 32;

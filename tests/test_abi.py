@@ -81,7 +81,8 @@ def test_argument_errors_return_status_without_work():
     o = lr.make_opts(algo="fused", chunk=100)
     assert lib.scan_bwd_ex(fake, fake, fake, None, fake, fake, 2, 8, 4, lr.BF16, None,
                            ctypes.byref(o)) == -4
-    o = lr.make_opts(algo="fused", chunk=64, width=32)  # wide tiles need aligned rows (D=3)
+    # 512-byte rows x 128 need 16-byte aligned rows (D=3 is not)
+    o = lr.make_opts(algo="fused", chunk=128, width=32)
     assert lib.scan_fwd_ex(fake, fake, fake, None, 2, 8, 3, lr.BF16, None, ctypes.byref(o)) == -4
     o = lr.make_opts(algo=9)
     assert lib.scan_fwd_ex(fake, fake, fake, None, 2, 8, 4, lr.F32, None, ctypes.byref(o)) == -7
@@ -207,6 +208,11 @@ def test_workspace_sizes_and_auto_choice():
             assert algo == lr.ALGO_FUSED
             algo, _, _ = lr.scan_auto_algo(4096, 128, 2559, dt, direction)
             assert algo == (lr.ALGO_SEQ if dt == lr.F32 else lr.ALGO_FUSED)
+            # unaligned rows over many 256-byte lane blocks: 256-byte rows x 128
+            algo, tile, width = lr.scan_auto_algo(8, 2048, 2559, dt, direction)
+            assert (algo, tile, width) == (lr.ALGO_FUSED, 128, 16)
+            algo, tile, width = lr.scan_auto_algo(1, 131072, 1023, dt, direction)
+            assert (algo, tile, width) == (lr.ALGO_FUSED, 256, 8)
             # a tile is no taller than a short sequence, and a forward chain of
             # at most 512 steps is one tile
             _, tile, _ = lr.scan_auto_algo(4096, 32, 2560, dt, direction)
