@@ -676,9 +676,11 @@ bool fused_cfg_supported(const Shape& s, int dir, int width, int tile, bool alig
 //
 // Rows that are not 16-byte aligned: 128 rows of 256-byte blocks when there
 // are at least 128 chains of them (fewer shared 128-byte lines between tiles:
-// bf16 [8,2048,2559] 2.8 / 2.9 -> 3.2 / 3.4 TB/s forward / backward, fp32
-// [2,4096,4097] 3.1 / 3.2 -> 3.4 / 4.0), else 256 rows of 128-byte blocks
-// (few chains: [1,131072,1023] bf16 3.1 / 3.1 against 2.2 / 3.0).
+// bf16 [8,2048,2559] 2.8 / 2.9 -> 3.2 / 3.4 TB/s forward / backward), for
+// fp32 64 rows of 512-byte blocks ([2,4096,4097] 3.1 / 3.2 -> 3.8 / 4.2,
+// against 3.4 / 4.0 at 256 bytes; bf16 is 4-6% slower at 512 bytes), else
+// 256 rows of 128-byte blocks (few chains: [1,131072,1023] bf16 3.1 / 3.1
+// against 2.2 / 3.0 at 256 bytes).
 //
 // A lane block wider than the row (D smaller than the block) would leave
 // lanes idle, so the widths fall back to narrower rows.
@@ -689,8 +691,9 @@ void fused_default_cfg(const Shape& s, int dir, bool aligned, int* width, int* t
     const auto fits = [&](int w) { return row_bytes >= (int64_t)w * 16; };
     if (!aligned) {
         if (fits(16) && s.B * ((row_bytes + 255) / 256) >= 128) {
-            *width = 16;
-            *tile = 128;
+            const bool w32 = s.dtype == DT_F32 && fits(32);
+            *width = w32 ? 32 : 16;
+            *tile = w32 ? 64 : 128;
         }
         return;
     }
