@@ -156,9 +156,17 @@ bool prefer_seq(const Shape& s) {
 // / 1.1, T = 128 1.4 / 1.0 against 0.95 / 0.98; fp32 T = 64 0.84 / 0.62
 // against 2.6 / 2.6, T = 128 1.5 / 1.1 against 2.4 / 2.4, T = 256 2.0 / 1.5
 // against 1.6 / 1.5.
+//
+// With 16-byte accesses at element-aligned addresses and 64-row tiles of
+// 512-byte blocks for sequences of at most 64 steps, the tiles took bf16 T =
+// 64 (3.7 / 3.7 against 2.2 / 2.2 for the walk, [692, 64, 2559]) and tie at
+// T = 32 (2.5 / 2.6 against 2.5 / 2.4); the fp32 walk still leads up to 128
+// steps (T = 128: 4.1 / 3.9 against 4.1 / 3.7).  Rows too short for 512-byte
+// blocks keep the walk up to 64 steps.
 bool prefer_seq_unaligned(const Shape& s) {
     if (s.B * s.D < ((int64_t)1 << 18)) return false;
-    return s.T <= 64 || (s.dtype == LRSCAN_F32 && s.T <= 128);
+    if (s.dtype == LRSCAN_F32) return s.T <= 128;
+    return s.T <= 32 || (s.T <= 64 && s.D * 2 < 512);
 }
 
 // The three-launch form for long sequences over one or two 128-byte lane

@@ -200,9 +200,15 @@ def test_workspace_sizes_and_auto_choice():
             assert (algo, tile, width) == (lr.ALGO_FUSED, 256, 8)
             algo, _, _ = lr.scan_auto_algo(4, 16, 1024, dt, direction)
             assert algo == lr.ALGO_FUSED
-            # rows that are not 16-byte aligned: the walk up to 64 steps from
-            # 2^18 lanes (fp32: 128 steps), as their only tile is 256 rows tall
-            algo, _, _ = lr.scan_auto_algo(4096, 64, 2559, dt, direction)
+            # rows that are not 16-byte aligned: the walk from 2^18 lanes up to
+            # 32 steps (fp32: 128; bf16 rows shorter than 512 bytes: 64)
+            algo, _, _ = lr.scan_auto_algo(4096, 32, 2559, dt, direction)
+            assert algo == lr.ALGO_SEQ
+            # bf16 from 33 steps: 512-byte rows x 64 (rows of at least 512 bytes)
+            algo, tile, width = lr.scan_auto_algo(4096, 64, 2559, dt, direction)
+            assert (algo, tile, width) == ((lr.ALGO_SEQ, 0, 0) if dt == lr.F32
+                                           else (lr.ALGO_FUSED, 64, 32))
+            algo, _, _ = lr.scan_auto_algo(4096, 64, 201, dt, direction)
             assert algo == lr.ALGO_SEQ
             algo, _, _ = lr.scan_auto_algo(4096, 64, 2560, dt, direction)
             assert algo == lr.ALGO_FUSED
