@@ -81,7 +81,10 @@ enum {
 /* algorithms */
 enum {
     LRSCAN_ALGO_AUTO = 0,    /* the library picks: SEQ for sequences of at most 8 steps (bf16:
-                                16) over at least 2^20 lanes, else FUSED with a measured tile
+                                16) over at least 2^20 lanes (rows that are not 16-byte
+                                aligned: at most 32 steps, fp32 128, over at least 2^18
+                                lanes), CHUNKED for sequences of at least 2^20 steps over
+                                one or two 128-byte lane blocks in all, else FUSED with a measured tile
                                 shape, or CHUNKED (complex scan: SEQ) where a tile would exceed
                                 the fused form's 32-bit in-tile offsets (rows of hundreds of MB).
                                 Complex scan: SEQ for T <= 16, and from 2^18 lanes for T <= 32
@@ -101,7 +104,7 @@ typedef struct {
                                (16,256) (32,32) (32,64) (32,128); backward (8,256) (8,128) (16,128)
                                (32,64) (32,32).  Rows that are not 16-byte aligned
                                (D * elem_bytes % 16 != 0 or an unaligned pointer) support
-                               only (8,256). */
+                               (8,256) (16,128) (32,64), and backward (8,128). */
     void* workspace;        /* device scratch, or NULL for the library's own per-stream cache */
     size_t workspace_bytes; /* size of `workspace` */
     const float* h0;        /* [B, D] initial state, or NULL for zero (forward and backward) */
